@@ -1,0 +1,210 @@
+"""CPU oracle for the speculative-decoding output side -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps the plain C oracle in
+``ref.c`` (double precision, single thread) with ctypes and numpy; it shares
+no code with the HIP library and never imports it.
+
+Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
+  philox / u24      pinned: published known-answer blocks + ATen's Philox engine
+  bias / softmax    pinned: numpy matmul, scipy softmax, W2 = 0 reduction
+  propose           pinned: brute-force inverse CDF, chi-square at V = 16
+  verify            pinned: chi-square of emitted tokens vs p_t, closed forms
+                    for P(accept), E[n_acc], special cases
+  confidence        pinned: V = 2 closed form, identical rows, TV identity
+  schedule          pinned: exhaustive enumeration of allocations
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "ref.c")
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = False) -> str:
+    """Compile ref.c into liboracle.so with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < max(os.path.getmtime(_SRC),
+                                               os.path.getmtime(os.path.join(_HERE, "ref.h"))):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, u64, f32 = ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
+        L.ref_philox4x32_10.argtypes = [P, P, P]
+        L.ref_draw.argtypes = [u64, u64, i32, i32, P]
+        L.ref_u24.argtypes = [ctypes.c_uint32]
+        L.ref_u24.restype = ctypes.c_double
+        L.ref_bias.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32, P]
+        L.ref_inverse_cdf.argtypes = [P, ctypes.c_int, ctypes.c_double, P]
+        L.ref_inverse_cdf.restype = i32
+        L.ref_argmax.argtypes = [P, ctypes.c_int, P]
+        L.ref_argmax.restype = i32
+        L.ref_markov_propose.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, f32, ctypes.c_int, u64, u64,
+                                         P, P, P, P, P, P]
+        L.ref_verify.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, f32, ctypes.c_int, u64, u64, P,
+                                 P, P, P, P, P, P, P, P, P]
+        L.ref_confidence.argtypes = [P, P, P, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, f32, P, P]
+        L.ref_schedule.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P, P, P,
+                                   P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _weights(W1, W2):
+    """Return (W1, W2, dtype code): float32 arrays, or bf16 given as uint16 bits."""
+    if W1.dtype == np.uint16:
+        return _c(W1, np.uint16), _c(W2, np.uint16), BF16
+    return _c(W1, np.float32), _c(W2, np.float32), F32
+
+
+def philox(ctr, key):
+    out = np.zeros(4, np.uint32)
+    lib().ref_philox4x32_10(_p(_c(ctr, np.uint32)), _p(_c(key, np.uint32)), _p(out))
+    return out
+
+
+def draw(seed, rnd, req, k):
+    out = np.zeros(4, np.uint32)
+    lib().ref_draw(seed, rnd, req, k, _p(out))
+    return out
+
+
+def u24(w):
+    return lib().ref_u24(int(w))
+
+
+def bias(W1, W2, xprev):
+    W1, W2, dt = _weights(W1, W2)
+    V, r = W2.shape
+    out = np.zeros(V, np.float64)
+    lib().ref_bias(_p(W1), _p(W2), dt, r, V, int(xprev), _p(out))
+    return out
+
+
+def inverse_cdf(w, u):
+    w = _c(w, np.float64)
+    m = np.zeros(1, np.float64)
+    v = lib().ref_inverse_cdf(_p(w), w.size, float(u), _p(m))
+    return int(v), float(m[0])
+
+
+def argmax(z):
+    z = _c(z, np.float64)
+    m = np.zeros(1, np.float64)
+    v = lib().ref_argmax(_p(z), z.size, _p(m))
+    return int(v), float(m[0])
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def markov_propose(U, W1, W2, x0, T, greedy, seed, rnd, req_ids=None, x_cond=None):
+    """Returns dict with x [R,g], pd_x [R,g], pd_stats [R,g,2], margin [R,g]."""
+    U = _c(U, np.float32)
+    R, g, V = U.shape
+    W1, W2, dt = _weights(W1, W2)
+    r = W2.shape[1]
+    x0 = _c(x0, np.int32)
+    req_ids = _c(req_ids, np.int32)
+    x_cond = _c(x_cond, np.int32)
+    out = dict(x=np.zeros((R, g), np.int32), pd_x=np.zeros((R, g)),
+               pd_stats=np.zeros((R, g, 2)), margin=np.zeros((R, g)))
+    st = lib().ref_markov_propose(_p(U), _p(W1), _p(W2), dt, _p(x0), R, g, r, V, float(T),
+                                  int(bool(greedy)), seed, rnd, _p(req_ids), _p(x_cond),
+                                  _p(out["x"]), _p(out["pd_x"]), _p(out["pd_stats"]),
+                                  _p(out["margin"]))
+    if st != 0:
+        raise OracleError("ref_markov_propose rejected its arguments")
+    return out
+
+
+def verify(U, W1, W2, x0, x, Lt, T, greedy, seed, rnd, ell=None, req_ids=None):
+    """Returns dict with n_acc, y, pt_x, pd_x, c_star and per-position instrumentation."""
+    U = _c(U, np.float32)
+    R, g, V = U.shape
+    Lt = _c(Lt, np.float32)
+    assert Lt.shape == (R, g + 1, V)
+    W1, W2, dt = _weights(W1, W2)
+    r = W2.shape[1]
+    x0, x = _c(x0, np.int32), _c(x, np.int32)
+    ell, req_ids = _c(ell, np.int32), _c(req_ids, np.int32)
+    o = dict(n_acc=np.zeros(R, np.int32), y=np.zeros((R, g + 1), np.int32),
+             pt_x=np.zeros((R, g)), pd_x=np.zeros((R, g)), c_star=np.zeros((R, g)),
+             acc=np.zeros((R, g), np.int32), acc_margin=np.zeros((R, g)),
+             y_alt=np.zeros((R, g + 1), np.int32), y_margin=np.zeros((R, g + 1)))
+    st = lib().ref_verify(_p(U), _p(W1), _p(W2), dt, _p(x0), _p(x), _p(Lt), _p(ell), R, g, r, V,
+                          float(T), int(bool(greedy)), seed, rnd, _p(req_ids),
+                          _p(o["n_acc"]), _p(o["y"]), _p(o["pt_x"]), _p(o["pd_x"]),
+                          _p(o["c_star"]), _p(o["acc"]), _p(o["acc_margin"]), _p(o["y_alt"]),
+                          _p(o["y_margin"]))
+    if st != 0:
+        raise OracleError("ref_verify rejected its arguments")
+    return o
+
+
+def confidence(U, W1, W2, x0, x, Lt, T):
+    U = _c(U, np.float32)
+    R, g, V = U.shape
+    Lt = _c(Lt, np.float32)
+    W1, W2, dt = _weights(W1, W2)
+    r = W2.shape[1]
+    x0, x = _c(x0, np.int32), _c(x, np.int32)
+    c = np.zeros((R, g))
+    a = np.zeros((R, g))
+    st = lib().ref_confidence(_p(U), _p(W1), _p(W2), dt, _p(x0), _p(x), _p(Lt), R, g, r, V,
+                              float(T), _p(c), _p(a))
+    if st != 0:
+        raise OracleError("ref_confidence rejected its arguments")
+    return c, a
+
+
+def schedule(c, sps):
+    c = _c(c, np.float32)
+    R, g = c.shape
+    sps = _c(sps, np.float32)
+    ell = np.zeros(R, np.int32)
+    a = np.zeros((R, g))
+    K = np.zeros(1, np.int32)
+    th = np.zeros(1)
+    tm = np.zeros(1)
+    gap = np.zeros(1)
+    st = lib().ref_schedule(_p(c), R, g, _p(sps), sps.size, _p(ell), _p(a), _p(K), _p(th),
+                            _p(tm), _p(gap))
+    if st != 0:
+        raise OracleError("ref_schedule rejected its arguments")
+    return dict(ell=ell, a=a, K_star=int(K[0]), theta_star=float(th[0]),
+                theta_margin=float(tm[0]), a_gap=float(gap[0]))

@@ -1,0 +1,123 @@
+/*
+ * ref.h -- CPU oracle for the output side of one speculative-decoding step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this code: only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no source with the HIP
+ * library (no headers, helpers, constants or generated tables).
+ *
+ * Everything is plain single-threaded C in double precision, loops in
+ * ascending index order, written from the equations of the DSpark blog page
+ * ("[DeepSeek-6] DSpark", xutianle.me):
+ *   - draft distribution p_k = softmax(U_k + B_k)           (section 3, eq. for p_k)
+ *   - Markov bias B(x_{k-1}, .) = W1[x_{k-1}] W2             (section 4, eq. for B)
+ *   - confidence label c*_k = 1 - 1/2 ||p_d - p_t||_1         (section 5, eq. for c*)
+ *   - survival a_{r,j} = prod_{i<=j} c_{r,i}                   (section 6, eq. for a)
+ *   - batch B = sum_r (1 + l_r), tau = sum_r (1 + sum_j a_rj),
+ *     Theta = tau * SPS(B), sort-greedy over a                  (section 6, eqs. + text)
+ * and the standard lossless rejection rule the page relies on (section 3 says
+ * the exact per-position draft probability is what rejection sampling needs;
+ * the section 1 diagram keeps the longest accepted prefix and adds one bonus
+ * token from the target).  The verify window [bonus, d_1..d_gamma] giving gamma+1 target rows
+ * follows the SGLang walk-through page ("DeepSeek-V4 MTP/NextN ...", section 3).
+ *
+ * Readings taken where the pages are silent (each is also listed in the design
+ * notes): temperature T divides both logit sets; uniforms come from
+ * Philox4x32-10 with key = seed, counter = (k, request, round_lo, round_hi),
+ * word 0 = draft sample, word 1 = accept test, word 2 = residual / bonus draw,
+ * u = (w >> 8) * 2^-24; the inverse CDF picks the smallest v whose running
+ * sum exceeds u * total; argmax ties go to the lowest index.
+ *
+ * Layouts (row-major, all sizes in elements):
+ *   U   [R, gamma, V]   fp32 base logits
+ *   Lt  [R, gamma+1, V] fp32 target logits (row k-1 checks x_k, row l_r is the bonus row)
+ *   W1  [V, r]          embedding of the previous token (fp32 or bf16 bits)
+ *   W2  [V, r]          weight of the bias-free projection r -> V (out x in
+ *                       storage), so B[v] = sum_i W1[x, i] * W2[v, i]; this is
+ *                       the transpose of the r x V matrix in the page's formula.
+ */
+#ifndef SPEC_ORACLE_REF_H
+#define SPEC_ORACLE_REF_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { REF_F32 = 0, REF_BF16 = 1 };
+
+/* Philox4x32-10 block (Salmon et al., SC'11): 10 rounds, bumping the key by
+ * the Weyl constants between rounds. */
+void ref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+/* The four words for (seed, round, request id, position k). */
+void ref_draw(uint64_t seed, uint64_t round, int32_t req, int32_t k, uint32_t out[4]);
+/* 24-bit uniform in [0, 1 - 2^-24]. */
+double ref_u24(uint32_t w);
+
+/* B[v] = sum_i W1[xprev, i] * W2[v, i], accumulated in double, i ascending. */
+void ref_bias(const void* W1, const void* W2, int w_dtype, int r, int V,
+              int32_t xprev, double* B);
+/* Inverse CDF on non-negative weights w[0..V): smallest v with
+ * sum_{i<=v} w_i > u * sum_i w_i; if rounding leaves none, the largest v with
+ * w_v > 0.  *margin = min(F(v) - u, u - F(v-1)) on the normalised CDF. */
+int32_t ref_inverse_cdf(const double* w, int V, double u, double* margin);
+/* Lowest index of the maximum of z[0..V); *margin = top1 - top2 (0 on ties). */
+int32_t ref_argmax(const double* z, int V, double* margin);
+
+/* Markov-head proposal over gamma positions.
+ *   req_ids  : Philox request index of each row (NULL -> 0..R-1)
+ *   x_cond   : NULL for free running; else [R,gamma] tokens whose prefix
+ *              conditions each position (conditioned mode)
+ * Outputs (all [R,gamma], stats [R,gamma,2]):
+ *   x       : drafted tokens
+ *   pd_x    : p_d(x_k)
+ *   pd_stats: (M, S) with M = max_v (U+B)(v), S = sum_v exp(((U+B)(v) - M)/T)
+ *   margin  : decision margin (CDF margin when sampled, top1-top2 logit when greedy)
+ * Returns 0, or -1 on a bad argument or an out-of-range token id. */
+int ref_markov_propose(const float* U, const void* W1, const void* W2, int w_dtype,
+                       const int32_t* x0, int R, int gamma, int r, int V, float T,
+                       int greedy, uint64_t seed, uint64_t round,
+                       const int32_t* req_ids, const int32_t* x_cond,
+                       int32_t* x, double* pd_x, double* pd_stats, double* margin);
+
+/* Lossless verification of the drafts x against the target rows Lt.
+ *   ell      : verified length per request (NULL -> gamma for every request)
+ * Outputs:
+ *   n_acc    [R]          accepted drafts (bonus excluded)
+ *   y        [R,gamma+1]  x_1..x_{n_acc}, then the correction/bonus token, then -1
+ *   pt_x, pd_x, c_star [R,gamma]   per verified position (NaN past ell)
+ * Per-position instrumentation for the conditioned comparison (any may be NULL):
+ *   acc      [R,gamma]    accept decision at k (1/0; -1 past ell)
+ *   acc_margin [R,gamma]  |u - min(1, p_t/p_d)| (greedy: top1-top2 of the target row)
+ *   y_alt    [R,gamma+1]  token drawn if k were the first rejection (index k-1),
+ *                         and the bonus draw at index ell
+ *   y_margin [R,gamma+1]  decision margin of each y_alt draw
+ * Returns 0 or -1. */
+int ref_verify(const float* U, const void* W1, const void* W2, int w_dtype,
+               const int32_t* x0, const int32_t* x, const float* Lt, const int32_t* ell,
+               int R, int gamma, int r, int V, float T, int greedy,
+               uint64_t seed, uint64_t round, const int32_t* req_ids,
+               int32_t* n_acc, int32_t* y, double* pt_x, double* pd_x, double* c_star,
+               int32_t* acc, double* acc_margin, int32_t* y_alt, double* y_margin);
+
+/* Confidence labels c*_{r,k} for every drafted position, and their running
+ * products a*_{r,j} = prod_{i<=j} c*_{r,i}. */
+int ref_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
+                   const int32_t* x0, const int32_t* x, const float* Lt,
+                   int R, int gamma, int r, int V, float T,
+                   double* c_star, double* a_star);
+
+/* Hardware-aware prefix scheduler.
+ *   c   [R,gamma] confidences in [0,1];  sps[B-1] = SPS(B) for B = 1..B_max
+ * Outputs: ell [R], a [R,gamma] (may be NULL), *K_star, *theta_star,
+ *   *theta_margin = (Theta(K*) - max_{K != K*} Theta(K)) / Theta(K*)  (may be NULL)
+ *   *a_gap = relative gap between the K*-th and (K*+1)-th sorted a (may be NULL)
+ * Returns 0, or -1 on a bad argument (c outside [0,1], B_max < R, ...). */
+int ref_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
+                 int32_t* ell, double* a, int32_t* K_star, double* theta_star,
+                 double* theta_margin, double* a_gap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
