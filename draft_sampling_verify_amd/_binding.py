@@ -1,0 +1,270 @@
+"""ctypes binding of libspec (include/spec.h): argument marshalling only.
+
+Every function has the C entry point's name and takes torch tensors on the
+GPU (PyTorch supplies device memory and the stream); outputs that are not
+passed in are allocated with torch.empty.  All computation happens in the
+HIP kernels of libspec.so; if the library is missing this module raises
+instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspec.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH, SPEC_EDEVICE, SPEC_EUNSUPPORTED = range(7)
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE = range(4)
+SPEC_DEV_BAD_TOKEN, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_CONFIDENCE = 1, 2, 4
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
+
+
+_lib = None
+
+P, I, F, U64, SZ, D = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64,
+                       ctypes.c_size_t, ctypes.c_double)
+
+_SIGS = {
+    "spec_workspace_bytes": ([I, I, I, I, I, I], SZ),
+    "spec_workspace_init": ([P, SZ, P], I),
+    "spec_device_status": ([P, P, I, P], I),
+    "spec_markov_propose": ([P, P, P, I, P, I, I, I, I, F, I, U64, U64, P, P, P, P, SZ, P], I),
+    "spec_verify": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
+    "spec_confidence": ([P, P, P, I, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P], I),
+    "spec_schedule": ([P, I, I, P, I, P, P, P, P, P, SZ, P], I),
+    "spec_status_str": ([I], ctypes.c_char_p),
+    "spec_profile_enable": ([I], I),
+    "spec_profile_reset": ([], I),
+    "spec_profile_read": ([ctypes.c_char_p, P, P], I),
+    "spec_profile_names": ([ctypes.c_char_p, I], I),
+}
+
+
+def lib():
+    """The loaded libspec.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libspec.so is not built (run draft_sampling_verify_amd.build.build()); "
+                              "there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().spec_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SPEC_OK:
+        raise SpecError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t, shape, dtype, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError("%s must be %s %s, got %s %s" % (name, tuple(shape), dtype, tuple(t.shape), t.dtype))
+
+
+def _draft_shapes(U, W1, W2, x0):
+    if U.dim() != 3 or U.dtype != torch.float32:
+        raise ValueError("U must be float32 [R, gamma, V]")
+    R, gamma, V = U.shape
+    if W2.dim() != 2 or W2.shape[0] != V:
+        raise ValueError("W2 must be [V, r]")
+    r = W2.shape[1]
+    _need(W1, (V, r), W2.dtype, "W1")
+    _need(x0, (R,), torch.int32, "x0")
+    return R, gamma, V, r
+
+
+def _wdtype(W):
+    if W.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if W.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError("weights must be torch.bfloat16 or torch.float32")
+
+
+def spec_workspace_bytes(op, R, gamma, r, V, B_max=0) -> int:
+    return int(lib().spec_workspace_bytes(op, R, gamma, r, V, B_max))
+
+
+class Workspace:
+    """A device workspace (uint8 tensor) large enough for the given sizes of
+    every operation, with its status word zeroed."""
+
+    def __init__(self, R, gamma, r, V, B_max=0, device=None):
+        need = max(spec_workspace_bytes(op, R, gamma, r, V, max(B_max, R))
+                   for op in (SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE))
+        if need == 0:
+            raise SpecError(SPEC_EINVAL, "Workspace")
+        self.tensor = torch.empty(need, dtype=torch.uint8, device=device or "cuda")
+        spec_workspace_init(self)
+
+    @property
+    def nbytes(self):
+        return self.tensor.numel()
+
+    def ptr(self):
+        return ctypes.c_void_p(self.tensor.data_ptr())
+
+
+def _ws(ws, R, gamma, r, V, device):
+    if ws is None:
+        ws = Workspace(R, gamma, r, V, device=device)
+    return ws
+
+
+def spec_workspace_init(ws: Workspace, stream=None):
+    _check(lib().spec_workspace_init(ws.ptr(), ws.nbytes, _stream(stream)), "spec_workspace_init")
+
+
+def spec_device_status(ws: Workspace, stream=None, clear=False) -> int:
+    flags = ctypes.c_int(0)
+    st = lib().spec_device_status(ws.ptr(), _stream(stream), int(bool(clear)), ctypes.byref(flags))
+    if st not in (SPEC_OK, SPEC_EDEVICE):
+        raise SpecError(st, "spec_device_status")
+    return flags.value
+
+
+def spec_markov_propose(U, W1, W2, x0, T, greedy=False, seed=1, round=0, x=None, pd_x=None,
+                        pd_stats=None, ws=None, stream=None):
+    R, gamma, V, r = _draft_shapes(U, W1, W2, x0)
+    dev = U.device
+    _need(x, (R, gamma), torch.int32, "x")
+    _need(pd_x, (R, gamma), torch.float32, "pd_x")
+    _need(pd_stats, (R, gamma, 2), torch.float32, "pd_stats")
+    x = torch.empty((R, gamma), dtype=torch.int32, device=dev) if x is None else x
+    pd_x = torch.empty((R, gamma), dtype=torch.float32, device=dev) if pd_x is None else pd_x
+    pd_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev) if pd_stats is None else pd_stats
+    ws = _ws(ws, R, gamma, r, V, dev)
+    st = lib().spec_markov_propose(_ptr(U), _ptr(W1), _ptr(W2), _wdtype(W2), _ptr(x0), R, gamma, r, V,
+                                   float(T), int(bool(greedy)), int(seed), int(round), _ptr(x), _ptr(pd_x),
+                                   _ptr(pd_stats), ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "spec_markov_propose")
+    return x, pd_x, pd_stats
+
+
+def spec_verify(U, W1, W2, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=0, ell=None,
+                n_acc=None, y=None, pt_x=None, c_star=None, want_pt_x=True, want_c_star=True,
+                ws=None, stream=None):
+    R, gamma, V, r = _draft_shapes(U, W1, W2, x0)
+    dev = U.device
+    _need(x, (R, gamma), torch.int32, "x")
+    _need(pd_stats, (R, gamma, 2), torch.float32, "pd_stats")
+    _need(Lt, (R, gamma + 1, V), torch.float32, "Lt")
+    _need(ell, (R,), torch.int32, "ell")
+    _need(n_acc, (R,), torch.int32, "n_acc")
+    _need(y, (R, gamma + 1), torch.int32, "y")
+    _need(pt_x, (R, gamma), torch.float32, "pt_x")
+    _need(c_star, (R, gamma), torch.float32, "c_star")
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    y = torch.empty((R, gamma + 1), dtype=torch.int32, device=dev) if y is None else y
+    if pt_x is None and want_pt_x:
+        pt_x = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    if c_star is None and want_c_star:
+        c_star = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    ws = _ws(ws, R, gamma, r, V, dev)
+    st = lib().spec_verify(_ptr(U), _ptr(W1), _ptr(W2), _wdtype(W2), _ptr(x0), _ptr(x), _ptr(pd_stats),
+                           _ptr(Lt), _ptr(ell), R, gamma, r, V, float(T), int(bool(greedy)), int(seed),
+                           int(round), _ptr(n_acc), _ptr(y), _ptr(pt_x), _ptr(c_star), ws.ptr(), ws.nbytes,
+                           _stream(stream))
+    _check(st, "spec_verify")
+    return n_acc, y, pt_x, c_star
+
+
+def spec_confidence(U, W1, W2, x0, x, Lt, T, pd_stats=None, c_star=None, a_star=None, want_a_star=True,
+                    ws=None, stream=None):
+    R, gamma, V, r = _draft_shapes(U, W1, W2, x0)
+    dev = U.device
+    _need(x, (R, gamma), torch.int32, "x")
+    _need(pd_stats, (R, gamma, 2), torch.float32, "pd_stats")
+    _need(Lt, (R, gamma + 1, V), torch.float32, "Lt")
+    _need(c_star, (R, gamma), torch.float32, "c_star")
+    _need(a_star, (R, gamma), torch.float64, "a_star")
+    c_star = torch.empty((R, gamma), dtype=torch.float32, device=dev) if c_star is None else c_star
+    if a_star is None and want_a_star:
+        a_star = torch.empty((R, gamma), dtype=torch.float64, device=dev)
+    ws = _ws(ws, R, gamma, r, V, dev)
+    st = lib().spec_confidence(_ptr(U), _ptr(W1), _ptr(W2), _wdtype(W2), _ptr(x0), _ptr(x), _ptr(pd_stats),
+                               _ptr(Lt), R, gamma, r, V, float(T), _ptr(c_star), _ptr(a_star), ws.ptr(),
+                               ws.nbytes, _stream(stream))
+    _check(st, "spec_confidence")
+    return c_star, a_star
+
+
+def spec_schedule(c, sps, ell=None, a=None, K_star=None, theta_star=None, want_a=True, ws=None,
+                  stream=None):
+    if c.dim() != 2 or c.dtype != torch.float32:
+        raise ValueError("c must be float32 [R, gamma]")
+    R, gamma = c.shape
+    if sps.dim() != 1 or sps.dtype != torch.float32:
+        raise ValueError("sps must be float32 [B_max]")
+    dev = c.device
+    _need(ell, (R,), torch.int32, "ell")
+    _need(a, (R, gamma), torch.float64, "a")
+    ell = torch.empty(R, dtype=torch.int32, device=dev) if ell is None else ell
+    if a is None and want_a:
+        a = torch.empty((R, gamma), dtype=torch.float64, device=dev)
+    K_star = torch.empty(1, dtype=torch.int32, device=dev) if K_star is None else K_star
+    theta_star = torch.empty(1, dtype=torch.float64, device=dev) if theta_star is None else theta_star
+    if ws is None:
+        ws = Workspace(R, gamma, 16, 1, B_max=sps.numel(), device=dev)
+    st = lib().spec_schedule(_ptr(c), R, gamma, _ptr(sps), sps.numel(), _ptr(ell), _ptr(a), _ptr(K_star),
+                             _ptr(theta_star), ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "spec_schedule")
+    return ell, a, K_star, theta_star
+
+
+def spec_profile_enable(on=True):
+    _check(lib().spec_profile_enable(int(bool(on))), "spec_profile_enable")
+
+
+def spec_profile_reset():
+    _check(lib().spec_profile_reset(), "spec_profile_reset")
+
+
+def spec_profile_read(kernel: str):
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().spec_profile_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)), "spec_profile_read")
+    return n.value, ms.value
+
+
+def spec_profile_names():
+    need = lib().spec_profile_names(None, 0)
+    buf = ctypes.create_string_buffer(need + 1)
+    lib().spec_profile_names(buf, need + 1)
+    return [s for s in buf.value.decode().split(",") if s]

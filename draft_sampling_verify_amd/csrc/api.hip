@@ -1,0 +1,269 @@
+// api.hip -- extern "C" entry points of libspec (declared in include/spec.h):
+// host-side argument validation, workspace carving and launch sequencing.
+// Nothing here allocates device memory; every check happens before the
+// first enqueue.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/spec.h"
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+using spec::DraftArgs;
+
+constexpr int MAX_R = 65536;
+constexpr int MAX_GAMMA = 64;
+constexpr int MAX_V = 1 << 24;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_draft(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, int R,
+                int gamma, int r, int V, float T)
+{
+    if (w_dtype != SPEC_F32 && w_dtype != SPEC_BF16) return SPEC_EDTYPE;
+    if (R < 0 || gamma < 1 || V < 1 || r < 16 || (r % 16) != 0) return SPEC_EINVAL;
+    if (!(T > 0.0f) || isinf(T)) return SPEC_EINVAL;
+    if (R > MAX_R || gamma > MAX_GAMMA || V > MAX_V || r > 512) return SPEC_EUNSUPPORTED;
+    if (w_dtype == SPEC_F32 && r > 256) return SPEC_EUNSUPPORTED;
+    if ((double)R * (gamma + 1) * (double)V >= 1099511627776.0) return SPEC_EUNSUPPORTED;
+    if (R > 0 && (!U || !W1 || !W2 || !x0)) return SPEC_EINVAL;
+    if (R > 0 && (!aligned16(U) || !aligned16(W1) || !aligned16(W2))) return SPEC_EINVAL;
+    return SPEC_OK;
+}
+
+DraftArgs make_args(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0,
+                    const int32_t* x, int R, int gamma, int r, int V, float T, int greedy, uint64_t seed,
+                    uint64_t round, void* ws)
+{
+    DraftArgs a{};
+    a.U = U; a.W1 = W1; a.W2 = W2; a.w_dtype = w_dtype; a.x0 = x0; a.x = x;
+    a.R = R; a.gamma = gamma; a.r = r; a.V = V;
+    // c = log2(e) / T rounded once to fp32; every exponential is 2^((z - m) c)
+    a.c = (float)(1.4426950408889634 / (double)T);
+    a.greedy = greedy != 0;
+    a.seed = seed; a.round = round;
+    a.status = reinterpret_cast<uint32_t*>(ws);
+    return a;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH; }
+
+__global__ void k_zero_words(uint32_t* p, int n)
+{
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+// ---- profiling records
+struct ProfRecord {
+    std::string name;
+    hipEvent_t start, stop;
+};
+bool g_prof_on = false;
+std::vector<ProfRecord> g_records;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_event_pool;
+size_t g_pool_used = 0;
+
+}  // namespace
+
+namespace spec {
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s)
+{
+    if (!g_prof_on) return;
+    if (g_pool_used == g_event_pool.size()) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return;
+        if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return; }
+        g_event_pool.emplace_back(a, b);
+    }
+    auto ev = g_event_pool[g_pool_used++];
+    if (hipEventRecord(ev.first, s) != hipSuccess) return;
+    g_records.push_back(ProfRecord{name, ev.first, ev.second});
+    slot = (int)g_records.size() - 1;
+}
+
+ProfScope::~ProfScope()
+{
+    if (slot >= 0) hipEventRecord(g_records[slot].stop, stream);
+}
+
+}  // namespace spec
+
+extern "C" {
+
+size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
+{
+    size_t bytes = 0;
+    switch (op) {
+    case SPEC_OP_PROPOSE:
+        if (check_draft(nullptr, nullptr, nullptr, SPEC_BF16, nullptr, 0, gamma, r, V, 1.0f) != SPEC_OK || R < 0 ||
+            R > MAX_R)
+            return 0;
+        spec::carve_propose(nullptr, R, V, &bytes);
+        return bytes;
+    case SPEC_OP_VERIFY:
+    case SPEC_OP_CONFIDENCE:
+        if (check_draft(nullptr, nullptr, nullptr, SPEC_BF16, nullptr, 0, gamma, r, V, 1.0f) != SPEC_OK || R < 0 ||
+            R > MAX_R)
+            return 0;
+        spec::carve_verify(nullptr, R, gamma, V, op == SPEC_OP_CONFIDENCE, &bytes);
+        return bytes;
+    case SPEC_OP_SCHEDULE:
+        if (R < 1 || gamma < 1 || (long)R * gamma > spec::SCHED_MAX_ENTRIES || B_max < R) return 0;
+        return spec::WS_HEADER;
+    default:
+        return 0;
+    }
+}
+
+int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    if (!ws || ws_bytes < spec::WS_HEADER) return SPEC_EWORKSPACE;
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint32_t*)ws, 64);
+    return launch_status(hipGetLastError());
+}
+
+int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags)
+{
+    if (!ws || !flags) return SPEC_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, ws, sizeof word, hipMemcpyDeviceToHost, s) != hipSuccess) return SPEC_ELAUNCH;
+    if (hipStreamSynchronize(s) != hipSuccess) return SPEC_ELAUNCH;
+    *flags = (int)word;
+    if (clear) {
+        hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, (uint32_t*)ws, 1);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    }
+    return word ? SPEC_EDEVICE : SPEC_OK;
+}
+
+int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, int R,
+                        int gamma, int r, int V, float T, int greedy, uint64_t seed, uint64_t round, int32_t* x,
+                        float* pd_x, float* pd_stats, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
+    if (st != SPEC_OK) return st;
+    if (R > 0 && (!x || !pd_x || !pd_stats)) return SPEC_EINVAL;
+    size_t need = 0;
+    spec::carve_propose(nullptr, R, V, &need);
+    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_OK;
+    const spec::ProposeWs w = spec::carve_propose(ws, R, V, nullptr);
+    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, greedy, seed, round, ws);
+    return launch_status(spec::launch_propose(a, x, pd_x, pd_stats, w, (hipStream_t)stream));
+}
+
+int spec_verify(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, const int32_t* x,
+                const float* pd_stats, const float* Lt, const int32_t* ell, int R, int gamma, int r, int V, float T,
+                int greedy, uint64_t seed, uint64_t round, int32_t* n_acc, int32_t* y, float* pt_x, float* c_star,
+                void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
+    if (st != SPEC_OK) return st;
+    if (R > 0 && (!x || !pd_stats || !Lt || !n_acc || !y)) return SPEC_EINVAL;
+    if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
+    size_t need = 0;
+    spec::carve_verify(nullptr, R, gamma, V, false, &need);
+    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_OK;
+    const spec::VerifyWs w = spec::carve_verify(ws, R, gamma, V, false, nullptr);
+    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, greedy, seed, round, ws);
+    int32_t* counts = reinterpret_cast<spec::WsHeader*>(ws)->counts;
+    return launch_status(
+        spec::launch_verify(a, pd_stats, Lt, ell, n_acc, y, pt_x, c_star, w, counts, (hipStream_t)stream));
+}
+
+int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0,
+                    const int32_t* x, const float* pd_stats, const float* Lt, int R, int gamma, int r, int V,
+                    float T, float* c_star, double* a_star, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
+    if (st != SPEC_OK) return st;
+    if (R > 0 && (!x || !Lt || !c_star)) return SPEC_EINVAL;
+    if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
+    size_t need = 0;
+    spec::carve_verify(nullptr, R, gamma, V, true, &need);
+    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_OK;
+    const spec::VerifyWs w = spec::carve_verify(ws, R, gamma, V, true, nullptr);
+    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, 0, 0, 0, ws);
+    return launch_status(spec::launch_confidence(a, pd_stats, Lt, c_star, a_star, w, (hipStream_t)stream));
+}
+
+int spec_schedule(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* ell, double* a,
+                  int32_t* K_star, double* theta_star, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    if (R < 1 || gamma < 1 || B_max < R) return SPEC_EINVAL;
+    if ((long)R * gamma > spec::SCHED_MAX_ENTRIES) return SPEC_EUNSUPPORTED;
+    if (!c || !sps || !ell || !K_star || !theta_star) return SPEC_EINVAL;
+    if (!ws || ws_bytes < spec::WS_HEADER) return SPEC_EWORKSPACE;
+    return launch_status(spec::launch_schedule(c, R, gamma, sps, B_max, ell, a, K_star, theta_star,
+                                               reinterpret_cast<uint32_t*>(ws), (hipStream_t)stream));
+}
+
+const char* spec_status_str(int status)
+{
+    switch (status) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument";
+    case SPEC_EDTYPE: return "unknown weight dtype";
+    case SPEC_EWORKSPACE: return "workspace missing or too small";
+    case SPEC_ELAUNCH: return "HIP launch error";
+    case SPEC_EDEVICE: return "a kernel saw invalid device data (token, length or confidence)";
+    case SPEC_EUNSUPPORTED: return "size outside the supported limits";
+    default: return "unknown status";
+    }
+}
+
+int spec_profile_enable(int on)
+{
+    g_prof_on = on != 0;
+    return SPEC_OK;
+}
+
+int spec_profile_reset(void)
+{
+    g_records.clear();
+    g_pool_used = 0;
+    return SPEC_OK;
+}
+
+int spec_profile_read(const char* kernel, int* launches, double* total_ms)
+{
+    if (!kernel || !launches || !total_ms) return SPEC_EINVAL;
+    int n = 0;
+    double tot = 0.0;
+    for (const ProfRecord& rec : g_records) {
+        if (rec.name != kernel) continue;
+        if (hipEventSynchronize(rec.stop) != hipSuccess) return SPEC_ELAUNCH;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, rec.start, rec.stop) != hipSuccess) return SPEC_ELAUNCH;
+        tot += ms;
+        ++n;
+    }
+    *launches = n;
+    *total_ms = tot;
+    return SPEC_OK;
+}
+
+int spec_profile_names(char* buf, int buf_len)
+{
+    std::string all;
+    for (const ProfRecord& rec : g_records) {
+        const std::string key = "," + rec.name + ",";
+        if (("," + all + ",").find(key) == std::string::npos) all += (all.empty() ? "" : ",") + rec.name;
+    }
+    if (buf && buf_len > 0) {
+        strncpy(buf, all.c_str(), (size_t)buf_len - 1);
+        buf[buf_len - 1] = '\0';
+    }
+    return (int)all.size() + 1;
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// internal.h -- host-side interfaces between the C-ABI layer (api.cpp) and
+// the kernel launchers (propose.hip, verify.hip, schedule.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spec {
+
+constexpr int GRAN_IDS = 128;  // same as GRAN in common.h (host copy)
+
+inline int n_granules(int V) { return (V + GRAN_IDS - 1) / GRAN_IDS; }
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace header: status word and device-side counts.
+struct WsHeader {
+    uint32_t status;     // SPEC_DEV_* bits (sticky)
+    uint32_t pad0[3];
+    int32_t counts[4];   // [0] verified rows K, [1] target rows K + R
+};
+constexpr size_t WS_HEADER = 256;
+
+// Carves a workspace into regions; with base == nullptr it only measures.
+struct Carver {
+    char* base;
+    size_t off;
+    explicit Carver(void* b) : base((char*)b), off(WS_HEADER) {}
+    template <typename T>
+    T* take(size_t count)
+    {
+        T* p = base ? (T*)(base + off) : nullptr;
+        off += align256(count * sizeof(T));
+        return p;
+    }
+};
+
+// Regions used by verify and confidence.
+struct VerifyWs {
+    float2* tgran;   // [TR, n_gran] per-granule (max, sum) of target rows
+    int32_t* tgidx;  // [TR, n_gran] per-granule argmax
+    float2* trow;    // [TR] merged (M_t, S_t)
+    int32_t* targ;   // [TR] row argmax
+    float2* vpart;   // [VR, n_gran] per-granule (TV mass, residual mass)
+    int4* vmap;      // [VR] verified row -> (request, k, target row, 0)
+    int2* tmap;      // [TR] target row -> (request, row within request)
+    int32_t* voff;   // [R] first verified row of each request
+    int32_t* toff;   // [R] first target row of each request
+    float2* dgran;   // confidence only: [VR, n_gran] draft per-granule stats
+    int32_t* dgidx;  // confidence only
+    float2* drow;    // confidence only: [VR] draft (M, S)
+};
+
+inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence, size_t* bytes)
+{
+    const size_t ng = (size_t)n_granules(V);
+    const size_t VR = (size_t)R * gamma;
+    const size_t TR = confidence ? VR : (size_t)R * (gamma + 1);
+    Carver c(ws);
+    VerifyWs w{};
+    w.tgran = c.take<float2>(TR * ng);
+    w.tgidx = c.take<int32_t>(TR * ng);
+    w.trow = c.take<float2>(TR);
+    w.targ = c.take<int32_t>(TR);
+    w.vpart = c.take<float2>(VR * ng);
+    w.vmap = c.take<int4>(VR);
+    w.tmap = c.take<int2>(TR);
+    w.voff = c.take<int32_t>(R);
+    w.toff = c.take<int32_t>(R);
+    if (confidence) {
+        w.dgran = c.take<float2>(VR * ng);
+        w.dgidx = c.take<int32_t>(VR * ng);
+        w.drow = c.take<float2>(VR);
+    }
+    if (bytes) *bytes = c.off;
+    return w;
+}
+
+struct ProposeWs {
+    float2* gstat;   // [R, n_gran]
+    int32_t* gidx;   // [R, n_gran]
+};
+
+inline ProposeWs carve_propose(void* ws, int R, int V, size_t* bytes)
+{
+    const size_t ng = (size_t)n_granules(V);
+    Carver c(ws);
+    ProposeWs w{};
+    w.gstat = c.take<float2>((size_t)R * ng);
+    w.gidx = c.take<int32_t>((size_t)R * ng);
+    if (bytes) *bytes = c.off;
+    return w;
+}
+
+// Arguments common to the draft-side kernels.
+struct DraftArgs {
+    const float* U;
+    const void* W1;
+    const void* W2;
+    int w_dtype;       // 0 fp32, 1 bf16
+    const int32_t* x0;
+    const int32_t* x;  // drafts (propose: output being filled; verify: input)
+    int R, gamma, r, V;
+    float c;           // log2(e) / T, rounded to fp32
+    int greedy;
+    uint64_t seed, round;
+    uint32_t* status;
+};
+
+// propose.hip
+hipError_t launch_propose(const DraftArgs& a, int32_t* x_out, float* pd_x, float* pd_stats,
+                          const ProposeWs& w, hipStream_t s);
+// Draft (max, sum) per granule and per row for all R*gamma drafted rows
+// (confidence without supplied statistics).
+hipError_t launch_draft_row_stats(const DraftArgs& a, const VerifyWs& w, hipStream_t s);
+
+// verify.hip
+hipError_t launch_verify(const DraftArgs& a, const float* pd_stats, const float* Lt,
+                         const int32_t* ell, int32_t* n_acc, int32_t* y, float* pt_x,
+                         float* c_star, const VerifyWs& w, int32_t* counts, hipStream_t s);
+hipError_t launch_confidence(const DraftArgs& a, const float* pd_stats, const float* Lt,
+                             float* c_star, double* a_star, const VerifyWs& w, hipStream_t s);
+
+// schedule.hip
+hipError_t launch_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
+                           int32_t* ell, double* a, int32_t* K_star, double* theta_star,
+                           uint32_t* status, hipStream_t s);
+constexpr int SCHED_MAX_ENTRIES = 8192;
+
+// Profiling hooks (api.cpp): bracket one kernel launch on stream s.
+struct ProfScope {
+    ProfScope(const char* name, hipStream_t s);
+    ~ProfScope();
+    int slot;
+    hipStream_t stream;
+};
+
+}  // namespace spec

@@ -1,0 +1,174 @@
+// schedule.hip -- hardware-aware prefix scheduler (DSpark blog page, section 6).
+//
+// One workgroup of 1024 threads does the whole problem in LDS (R*gamma <=
+// 8192 entries):
+//   1. a_{r,j} = prod_{i<=j} c_{r,i} in fp64, left to right, per request;
+//   2. bitonic sort of (a, r*gamma + j - 1) into the order a descending,
+//      then request, then position ascending;
+//   3. fp64 prefix sums P_K of the sorted a;
+//   4. Theta(K) = (R + P_K) * SPS(R + K) for K = 0..min(R*gamma, B_max - R),
+//      K* = the smallest maximiser;
+//   5. l_r = number of request-r entries among the first K*.
+// Because a does not increase along j, the first K entries of that order
+// are prefix-closed per request and carry the largest expected accepted
+// mass among all allocations of K drafts; scanning every K is exact.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace spec {
+
+constexpr int SCHED_THREADS = 1024;
+
+__device__ inline bool sched_before(double ka, int ia, double kb, int ib)
+{
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+__global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int R, int gamma,
+                                                            const float* sps, int B_max, int32_t* ell,
+                                                            double* a_out, int32_t* K_star,
+                                                            double* theta_star, uint32_t* status)
+{
+    __shared__ double key[SCHED_MAX_ENTRIES];
+    __shared__ int idx[SCHED_MAX_ENTRIES];
+    __shared__ int cnt[SCHED_MAX_ENTRIES];
+    __shared__ double wsum[SCHED_THREADS / WAVE];
+    __shared__ double best_th[SCHED_THREADS / WAVE];
+    __shared__ int best_k[SCHED_THREADS / WAVE];
+    __shared__ int bad;
+
+    const int t = threadIdx.x;
+    const int lane = t & (WAVE - 1), w = t / WAVE;
+    const int n = R * gamma;
+    int N = 1;
+    while (N < n) N <<= 1;
+    if (t == 0) bad = 0;
+    __syncthreads();
+
+    // 1. survival products
+    for (int r = t; r < R; r += SCHED_THREADS) {
+        double run = 1.0;
+        for (int j = 0; j < gamma; ++j) {
+            const int o = r * gamma + j;
+            const float cv = c[o];
+            if (!(cv >= 0.0f && cv <= 1.0f)) bad = 1;
+            run *= (double)cv;
+            key[o] = run;
+            idx[o] = o;
+            if (a_out) a_out[o] = run;
+        }
+        cnt[r] = 0;
+    }
+    for (int i = n + t; i < N; i += SCHED_THREADS) {
+        key[i] = -1.0;  // sorts after every real entry (a >= 0)
+        idx[i] = i;
+    }
+    __syncthreads();
+    if (bad) {
+        if (t == 0) {
+            raise_flag(status, 4u);
+            *K_star = -1;
+            *theta_star = NAN;
+        }
+        for (int r = t; r < R; r += SCHED_THREADS) ell[r] = -1;
+        return;
+    }
+
+    // 2. bitonic sort into "before" order
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < N; i += SCHED_THREADS) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const double ki = key[i], kl = key[l];
+                    const int ii = idx[i], il = idx[l];
+                    const bool up = (i & k) == 0;
+                    const bool swap = up ? sched_before(kl, il, ki, ii) : sched_before(ki, ii, kl, il);
+                    if (swap) {
+                        key[i] = kl; key[l] = ki;
+                        idx[i] = il; idx[l] = ii;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 3. inclusive prefix sums over the first n sorted values, in place;
+    //    each thread owns a contiguous run of `per` entries
+    const int per = (n + SCHED_THREADS - 1) / SCHED_THREADS;
+    const int i0 = min(t * per, n), i1 = min(i0 + per, n);
+    double local = 0.0;
+    for (int i = i0; i < i1; ++i) local += key[i];
+    // block exclusive scan of `local` (fp64)
+    double incl = local;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const double v = __shfl_up(incl, o, WAVE);
+        if (lane >= o) incl += v;
+    }
+    double ex = __shfl_up(incl, 1, WAVE);
+    if (lane == 0) ex = 0.0;
+    if (lane == WAVE - 1) wsum[w] = incl;
+    __syncthreads();
+    double before = 0.0;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    double run = before + ex;
+
+    // 4. Theta(K) and its argmax (smallest K on ties)
+    const int Kmax = min(n, B_max - R);
+    double bth = -INFINITY;
+    int bk = 0x7fffffff;
+    if (t == 0) {
+        bth = (double)R * (double)sps[R - 1];
+        bk = 0;
+    }
+    for (int i = i0; i < i1; ++i) {
+        run += key[i];
+        const int K = i + 1;
+        if (K <= Kmax) {
+            const double th = ((double)R + run) * (double)sps[R + K - 1];
+            if (th > bth) { bth = th; bk = K; }
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        const double ot = __shfl_xor(bth, o, WAVE);
+        const int ok = __shfl_xor(bk, o, WAVE);
+        if (ot > bth || (ot == bth && ok < bk)) { bth = ot; bk = ok; }
+    }
+    if (lane == 0) {
+        best_th[w] = bth;
+        best_k[w] = bk;
+    }
+    __syncthreads();
+    double th_star = best_th[0];
+    int k_star = best_k[0];
+    for (int i = 1; i < SCHED_THREADS / WAVE; ++i)
+        if (best_th[i] > th_star || (best_th[i] == th_star && best_k[i] < k_star)) {
+            th_star = best_th[i];
+            k_star = best_k[i];
+        }
+
+    // 5. per-request counts among the first K*
+    for (int i = t; i < k_star; i += SCHED_THREADS) atomicAdd(&cnt[idx[i] / gamma], 1);
+    __syncthreads();
+    for (int r = t; r < R; r += SCHED_THREADS) ell[r] = cnt[r];
+    if (t == 0) {
+        *K_star = k_star;
+        *theta_star = th_star;
+    }
+}
+
+hipError_t launch_schedule(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* ell,
+                           double* a, int32_t* K_star, double* theta_star, uint32_t* status, hipStream_t s)
+{
+    {
+        ProfScope ps("schedule", s);
+        hipLaunchKernelGGL(k_schedule, dim3(1), dim3(SCHED_THREADS), 0, s, c, R, gamma, sps, B_max, ell, a,
+                           K_star, theta_star, status);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace spec

@@ -1,0 +1,189 @@
+/*
+ * spec.h -- C ABI of libspec: the vocabulary-sized output side of one
+ * speculative-decoding step on an MI355X (gfx950) GPU.
+ *
+ * Four operations, in the notation of the DSpark blog page ("[DeepSeek-6]
+ * DSpark", xutianle.me) and the SGLang MTP/NextN walk-through page
+ * ("DeepSeek-V4 MTP/NextN ...", akiyangdev):
+ *   spec_markov_propose  draft x_1..x_gamma from p_k = softmax((U_k + B_k)/T),
+ *                        B_k = W1[x_{k-1}] W2            (DSpark sections 3-4)
+ *   spec_verify          lossless verification against target logits: accept,
+ *                        residual resample, bonus token  (DSpark section 1
+ *                        diagram; the verify window of gamma+1 target rows,
+ *                        SGLang page section 3), with the confidence label
+ *                        c* fused in                       (DSpark section 5)
+ *   spec_confidence      c*_k = 1 - 1/2 ||p_d - p_t||_1 and a*_j = prod c*_i
+ *                                                          (DSpark sections 5-6)
+ *   spec_schedule        per-request verify lengths l_r maximising
+ *                        Theta = tau * SPS(B), B = sum_r (1 + l_r),
+ *                        tau = sum_r (1 + sum_{j<=l_r} a_{r,j}) (DSpark section 6)
+ *
+ * Conventions shared by every entry point
+ *   Memory      Every pointer argument is DEVICE memory unless its comment says
+ *               host.  The caller allocates and frees everything, including
+ *               the workspace; the library never allocates, frees or retains
+ *               caller memory and keeps no per-call state outside `ws`.
+ *   Layout      Row-major, vocabulary index fastest.  U [R,gamma,V] and
+ *               Lt [R,gamma+1,V] are fp32.  W1 and W2 are [V,r]: W1 row x is
+ *               the embedding of token x; W2 row v holds the weights of output
+ *               v of the bias-free projection r -> V, so
+ *               B_k[v] = sum_i W1[x_{k-1}, i] * W2[v, i]  (the transpose of the
+ *               r x V matrix in the page's formula, i.e. the usual storage of
+ *               a linear layer's weight).  Target row k-1 of a request checks
+ *               draft x_k; target row l_r gives the bonus token.
+ *   Alignment   U, Lt, W1, W2 must be 16-byte aligned; r % 16 == 0.
+ *   Asynchrony  Calls only validate on the host and enqueue kernels on
+ *               `stream` (a hipStream_t; NULL = the null stream).  Outputs are
+ *               valid once the caller synchronises that stream.
+ *   Randomness  Every uniform is Philox4x32-10 with key = seed and counter =
+ *               (k, request, round_lo, round_hi); word 0 draws x_k, word 1 is
+ *               the accept test at k, word 2 the residual draw at k or the
+ *               bonus draw at k = l_r + 1; u = (w >> 8) * 2^-24.  Sampling is
+ *               by inverse CDF in vocabulary order (smallest v whose running
+ *               sum exceeds u * total), so results are a pure function of
+ *               (inputs, seed, round).
+ *   Greedy      greedy != 0 replaces every draw by the lowest-index argmax of
+ *               the same logits (draft: U+B; accept iff x_k equals the target
+ *               argmax).  Probabilities and c* are still reported at T.
+ *   Errors      Return SPEC_OK or an error code.  All argument checks happen
+ *               on the host before anything is enqueued; nothing is coerced.
+ *               Token ids, lengths and confidences that live in device memory
+ *               are checked by the kernels: the request's outputs become -1 /
+ *               NaN and a bit is OR-ed into the workspace status word, read by
+ *               spec_device_status().
+ *   Threads     Calls with distinct workspaces may run concurrently.
+ */
+#ifndef SPEC_H
+#define SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* spec_stream_t; /* identical to hipStream_t */
+
+enum spec_status {
+    SPEC_OK = 0,
+    SPEC_EINVAL = 1,      /* bad scalar, NULL required pointer, misalignment    */
+    SPEC_EDTYPE = 2,      /* unknown weight dtype                               */
+    SPEC_EWORKSPACE = 3,  /* ws NULL or smaller than spec_workspace_bytes()     */
+    SPEC_ELAUNCH = 4,     /* the HIP runtime reported an error at launch        */
+    SPEC_EDEVICE = 5,     /* spec_device_status(): a kernel saw bad device data */
+    SPEC_EUNSUPPORTED = 6 /* size beyond what the kernels handle (see limits)   */
+};
+
+enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+enum spec_op { SPEC_OP_PROPOSE = 0, SPEC_OP_VERIFY = 1, SPEC_OP_CONFIDENCE = 2, SPEC_OP_SCHEDULE = 3 };
+
+/* Bits of the device status word. */
+enum spec_device_flag {
+    SPEC_DEV_BAD_TOKEN = 1,       /* an anchor or draft id outside [0, V)          */
+    SPEC_DEV_BAD_LENGTH = 2,      /* an l_r outside [0, gamma]                     */
+    SPEC_DEV_BAD_CONFIDENCE = 4   /* a confidence outside [0, 1] (or NaN)          */
+};
+
+/* Limits: 1 <= R <= 65536, 1 <= gamma <= 64, 16 <= r <= 512 (r % 16 == 0;
+ * r <= 256 for SPEC_F32 weights), 1 <= V <= 2^24, R*(gamma+1)*V < 2^40;
+ * spec_schedule: R*gamma <= 8192. */
+
+/* Bytes of workspace `op` needs for these sizes (B_max only for schedule).
+ * Returns 0 for sizes the entry point would reject. */
+size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max);
+
+/* Zero the status word of a freshly allocated workspace (enqueued on stream). */
+int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Synchronise `stream`, then return the status word of `ws` in *flags (host
+ * pointer; SPEC_DEV_* bits, sticky across calls).  clear != 0 zeroes it.
+ * Returns SPEC_OK, or SPEC_EDEVICE when a bit is set. */
+int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags);
+
+/* Draft gamma tokens per request with the Markov head (DSpark sections 3-4):
+ *   x_0 = x0[r];  for k = 1..gamma:
+ *     z_k = U[r,k-1,:] + W1[x_{k-1}] W2^T        (raw draft logits)
+ *     p_k = softmax(z_k / T);  x_k ~ p_k (word 0), or argmax z_k if greedy
+ * In:  U [R,gamma,V] fp32; W1, W2 [V,r] (w_dtype); x0 [R] int32.
+ * Out: x [R,gamma] int32; pd_x [R,gamma] fp32 = p_k(x_k);
+ *      pd_stats [R,gamma,2] fp32 = (M, S) with M = max_v z_k(v) and
+ *      S = sum_v exp((z_k(v) - M)/T), so p_k(v) = exp((z_k(v)-M)/T)/S.
+ * The gamma positions run serially on the device; nothing returns to the
+ * host in between. */
+int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dtype,
+                        const int32_t* x0, int R, int gamma, int r, int V, float T,
+                        int greedy, uint64_t seed, uint64_t round,
+                        int32_t* x, float* pd_x, float* pd_stats,
+                        void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Verify drafts against target logits (standard lossless rule):
+ *   for k = 1..l_r: accept x_k iff u1 < p_t,k(x_k) / p_k(x_k) (greedy: iff
+ *   x_k == argmax Lt[r,k-1,:]); at the first rejection emit a draw from
+ *   normalize(max(0, p_t,k - p_k)) (word 2 at k; p_t,k if that mass is 0;
+ *   greedy: the target argmax); after l_r accepts emit the bonus draw from
+ *   p_t,l_r+1 (word 2 at k = l_r + 1).  p_t,k = softmax(Lt[r,k-1,:] / T).
+ * In:  U, W1, W2, x0 as for propose; x [R,gamma] drafts; pd_stats from
+ *      propose for the same drafts; Lt [R,gamma+1,V] fp32;
+ *      ell [R] int32 verify lengths in [0,gamma], or NULL = gamma for all.
+ * Out: n_acc [R] int32 accepted drafts (bonus excluded);
+ *      y [R,gamma+1] int32 = x_1..x_{n_acc}, correction or bonus, then -1;
+ *      pt_x [R,gamma] fp32 = p_t,k(x_k) (optional, NULL to skip);
+ *      c_star [R,gamma] fp32 = 1 - 1/2 ||p_k - p_t,k||_1 clamped to [0,1]
+ *      (optional; NULL skips the full-row sweep of accepted positions).
+ * Entries past l_r are NaN (pt_x, c_star). */
+int spec_verify(const float* U, const void* W1, const void* W2, int w_dtype,
+                const int32_t* x0, const int32_t* x, const float* pd_stats,
+                const float* Lt, const int32_t* ell,
+                int R, int gamma, int r, int V, float T, int greedy,
+                uint64_t seed, uint64_t round,
+                int32_t* n_acc, int32_t* y, float* pt_x, float* c_star,
+                void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Confidence labels of every drafted position (DSpark section 5) and their
+ * running products (section 6):
+ *   c_star [R,gamma] fp32 = clamp(1 - 1/2 ||p_k - p_t,k||_1, 0, 1)
+ *   a_star [R,gamma] fp64 = prod_{i<=k} c*_i, left to right (optional).
+ * pd_stats may be NULL (the draft normalisers are then recomputed). */
+int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
+                    const int32_t* x0, const int32_t* x, const float* pd_stats,
+                    const float* Lt, int R, int gamma, int r, int V, float T,
+                    float* c_star, double* a_star,
+                    void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Hardware-aware prefix scheduler (DSpark section 6):
+ *   a_{r,j} = prod_{i<=j} c_{r,i} in fp64, left to right;
+ *   rank all (a, r, j) by a descending, then r, then j ascending;
+ *   P_K = sum of the first K;  Theta(K) = (R + P_K) * SPS(R + K) for
+ *   K = 0..min(R*gamma, B_max - R);  K* = smallest maximiser;
+ *   l_r = number of request-r entries among the first K*.
+ * Ranking by a is prefix-safe because a does not increase along j, and the
+ * top-K set maximises tau for each batch size, so this is the exact optimum.
+ * In:  c [R,gamma] fp32 confidences in [0,1]; sps [B_max] fp32 with
+ *      sps[B-1] = SPS(B).  B_max >= R.
+ * Out: ell [R] int32; a [R,gamma] fp64 (optional); K_star [1] int32;
+ *      theta_star [1] fp64. */
+int spec_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
+                  int32_t* ell, double* a, int32_t* K_star, double* theta_star,
+                  void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Name of a status code (static string). */
+const char* spec_status_str(int status);
+
+/* Kernel timing.  spec_profile_enable(1) makes every later launch on every
+ * stream record HIP events around itself (not thread-safe; for benchmarks).
+ * spec_profile_read() synchronises the recorded events and returns, for the
+ * kernel named `kernel`, the number of launches and their total duration in
+ * milliseconds since the last reset.  spec_profile_reset() drops the records. */
+int spec_profile_enable(int on);
+int spec_profile_reset(void);
+int spec_profile_read(const char* kernel, int* launches, double* total_ms);
+/* Names of kernels with records, separated by ',' into buf (host); returns the
+ * length needed. */
+int spec_profile_names(char* buf, int buf_len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_H */

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases span several 128-id granules, ragged vocabularies (V % 128 != 0,
+V % 4 != 0), ragged request counts (R % 32 != 0), rank padding, fp32 and bf16
+weights, and degenerate sizes; the measured workloads run at full size, with
+the oracle checking every request (c2) or sampled requests (c3, c4, c5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Config
+import draft_sampling_verify_amd as spec
+from parity import (MARGIN, PROB_TOL, check_propose, check_verify, log, np_, run_propose, run_verify,
+                    to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": workloads.CONFIGS["tiny"],
+    "tiny_T07": workloads.CONFIGS["tiny"].replace(name="tiny_T07", T=0.7),
+    "ragged_bf16": Config("ragged_bf16", 11, 37, 3, 1000, 32, True, 0.8, 2.0, 0.05, 0.5),
+    "odd_vocab": Config("odd_vocab", 12, 5, 2, 1001, 48, True, 1.0, 2.0, 0.1, 0.7),
+    "rank512": Config("rank512", 13, 3, 2, 2048, 512, True, 1.0, 2.0, 0.05, 0.5),
+    "fp32_r256": Config("fp32_r256", 14, 6, 3, 3000, 256, False, 1.0, 2.0, 0.05, 0.5),
+    "tiny_vocab": Config("tiny_vocab", 15, 9, 5, 7, 16, True, 1.0, 1.0, 0.3, 0.5),
+    "one_token": Config("one_token", 16, 2, 3, 1, 16, True, 1.0, 1.0, 0.3, 0.5),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    spec.lib()
+
+
+@pytest.mark.parametrize("greedy", [False, True], ids=["sampled", "greedy"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_propose_verify_confidence(name, greedy):
+    cfg = SMALL[name]
+    log("case", name, "greedy" if greedy else "sampled", "R=%d g=%d V=%d r=%d" % (cfg.R, cfg.gamma, cfg.V, cfg.r))
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    x, pdx, pds = run_propose(t, cfg, greedy, ws=ws)
+    st = check_propose(d, np_(x), np_(pdx), np_(pds), greedy)
+    log("  propose", st)
+    n_acc, y, pt_x, c_star = run_verify(t, cfg, x, pds, greedy, ws=ws)
+    sv = check_verify(d, np_(x), None, np_(n_acc), np_(y), np_(pt_x), np_(c_star), greedy)
+    log("  verify", sv)
+    # scheduled (ragged) lengths, including 0 and gamma
+    rng = np.random.default_rng(cfg.index)
+    ell = rng.integers(0, cfg.gamma + 1, cfg.R).astype(np.int32)
+    ell[0] = 0
+    ell[-1] = cfg.gamma
+    n2, y2, p2, c2 = run_verify(t, cfg, x, pds, greedy, ell=torch.from_numpy(ell).cuda(), ws=ws)
+    sv2 = check_verify(d, np_(x), ell, np_(n2), np_(y2), np_(p2), np_(c2), greedy)
+    log("  verify ragged", sv2)
+    # confidence, with and without the propose statistics
+    oc, oa = oracle.confidence(d["U"], d["W1"], d["W2"], d["x0"], np_(x), d["Lt"], np.float32(cfg.T))
+    for stats in (pds, None):
+        cs, a = spec.spec_confidence(t["U"], t["W1"], t["W2"], t["x0"], x, t["Lt"], cfg.T, pd_stats=stats, ws=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(np_(cs), oc, rtol=0, atol=PROB_TOL)
+        np.testing.assert_allclose(np_(a), oa, rtol=0, atol=PROB_TOL * cfg.gamma)
+    assert spec.spec_device_status(ws) == 0
+
+
+def test_determinism_and_round_dependence():
+    cfg = SMALL["ragged_bf16"]
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    a = [np_(v) for v in run_propose(t, cfg, False, rnd=3, ws=ws)]
+    b = [np_(v) for v in run_propose(t, cfg, False, rnd=3, ws=ws)]
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    c = np_(run_propose(t, cfg, False, rnd=4, ws=ws)[0])
+    assert (c != a[0]).any()
+    st = check_propose(d, c, *[np_(v) for v in run_propose(t, cfg, False, rnd=4, ws=ws)[1:]], False, rnd=4)
+    log("  round 4", st)
+    xs = torch.from_numpy(a[0]).cuda()
+    pds = torch.from_numpy(a[2]).cuda()
+    v1 = [np_(v) for v in run_verify(t, cfg, xs, pds, False, rnd=3, ws=ws)]
+    v2 = [np_(v) for v in run_verify(t, cfg, xs, pds, False, rnd=3, ws=ws)]
+    for u, v in zip(v1, v2):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_invalid_tokens_flag_and_blank_outputs():
+    cfg = SMALL["tiny"]
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    x0 = t["x0"].clone()
+    x0[1] = cfg.V        # out of range anchor
+    x, pdx, pds = spec.spec_markov_propose(t["U"], t["W1"], t["W2"], x0, 1.0, False, 1, 0, ws=ws)
+    torch.cuda.synchronize()
+    assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_TOKEN
+    assert (np_(x)[1] == -1).all() and np.isnan(np_(pdx)[1]).all()
+    ok = [0, 2, 3]
+    dd = workloads.make(cfg, requests=ok)
+    check_propose(dd, np_(x)[ok], np_(pdx)[ok], np_(pds)[ok], False)
+    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2"], x0, x, pds, t["Lt"], 1.0, False,
+                                              1, 0, ws=ws)
+    torch.cuda.synchronize()
+    assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_TOKEN
+    assert np_(n_acc)[1] == -1 and (np_(y)[1] == -1).all()
+    bad_ell = torch.tensor([1, 2, cfg.gamma + 1, 0], dtype=torch.int32, device="cuda")
+    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2"], t["x0"], x.clone().fill_(0),
+                                              pds, t["Lt"], 1.0, False, 1, 0, ell=bad_ell, ws=ws)
+    torch.cuda.synchronize()
+    assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_LENGTH
+    assert np_(n_acc)[2] == -1
+    assert spec.spec_device_status(ws) == 0
+
+
+def test_empty_batch_is_a_no_op():
+    e = torch.empty((0, 4, 1024), device="cuda")
+    W = torch.zeros((1024, 16), device="cuda")
+    x0 = torch.empty(0, dtype=torch.int32, device="cuda")
+    x, pdx, pds = spec.spec_markov_propose(e, W, W, x0, 1.0, ws=spec.Workspace(1, 4, 16, 1024))
+    assert x.shape == (0, 4)
+
+
+def _chi2_case(V=16, r=16, rounds=16, R=65536, seed=21):
+    rng = np.random.default_rng(seed)
+    u = (rng.standard_normal((2, V)) * 1.5).astype(np.float32)
+    lt = (u + rng.standard_normal((2, V)) * 0.8).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * 0.5).astype(np.float32)
+    W2 = (rng.standard_normal((V, r)) * 0.5).astype(np.float32)
+    U = torch.from_numpy(u[:1]).cuda().expand(R, 1, V).contiguous()
+    Lt = torch.from_numpy(lt).cuda().expand(R, 2, V).contiguous()
+    tW1, tW2 = torch.from_numpy(W1).cuda(), torch.from_numpy(W2).cuda()
+    x0 = torch.full((R,), 2, dtype=torch.int32, device="cuda")
+    ws = spec.Workspace(R, 1, r, V)
+    first, acc1 = [], []
+    for rnd in range(rounds):
+        x, pdx, pds = spec.spec_markov_propose(U, tW1, tW2, x0, 1.0, False, 1, rnd, ws=ws)
+        n_acc, y, _, c_star = spec.spec_verify(U, tW1, tW2, x0, x, pds, Lt, 1.0, False, 1, rnd, ws=ws)
+        first.append(np_(y)[:, 0])
+        acc1.append(np_(n_acc) >= 1)
+    from scipy import special
+    p_d = special.softmax(u[0].astype(np.float64) + W2.astype(np.float64) @ W1[2].astype(np.float64))
+    p_t = special.softmax(lt[0].astype(np.float64))
+    return np.concatenate(first), np.concatenate(acc1), p_d, p_t, np_(c_star)[0, 0]
+
+
+def test_emitted_tokens_follow_target_chi_square():
+    """2^20 verify calls' first emitted token at V = 16 must follow p_t (chi-square)."""
+    from scipy import stats
+    tok, acc, p_d, p_t, c1 = _chi2_case()
+    n = tok.size
+    counts = np.bincount(tok, minlength=p_t.size)
+    pv = stats.chisquare(counts, p_t * n).pvalue
+    log("  chi-square p-value", pv)
+    assert pv > 1e-4
+    c_exact = np.minimum(p_d, p_t).sum()
+    assert abs(c1 - c_exact) < PROB_TOL
+    se = np.sqrt(c_exact * (1 - c_exact) / n)
+    assert abs(acc.mean() - c_exact) < 5 * se
+
+
+# ------------------------------------------------------- measured workloads
+
+def _sample(R):
+    return sorted(set([0, 1, R // 2, R - 1]))
+
+
+@pytest.mark.parametrize("greedy", [False, True], ids=["sampled", "greedy"])
+def test_c2_full(greedy):
+    cfg = workloads.CONFIGS["c2"]
+    log("case c2 full", "greedy" if greedy else "sampled")
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    x, pdx, pds = run_propose(t, cfg, greedy, ws=ws)
+    log("  propose", check_propose(d, np_(x), np_(pdx), np_(pds), greedy))
+    n_acc, y, pt_x, c_star = run_verify(t, cfg, x, pds, greedy, ws=ws)
+    log("  verify", check_verify(d, np_(x), None, np_(n_acc), np_(y), np_(pt_x), np_(c_star), greedy))
+
+
+@pytest.mark.parametrize("name,greedy", [("c3", False), ("c5", False), ("c5", True)])
+def test_large_sampled_requests(name, greedy):
+    cfg = workloads.CONFIGS[name]
+    log("case", name, "greedy" if greedy else "sampled")
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    x, pdx, pds = run_propose(t, cfg, greedy, ws=ws)
+    n_acc, y, pt_x, c_star = run_verify(t, cfg, x, pds, greedy, ws=ws)
+    req = _sample(cfg.R)
+    sub = workloads.make(cfg, requests=req)
+    del d
+    log("  propose", check_propose(sub, np_(x)[req], np_(pdx)[req], np_(pds)[req], greedy))
+    log("  verify", check_verify(sub, np_(x)[req], None, np_(n_acc)[req], np_(y)[req], np_(pt_x)[req],
+                                 np_(c_star)[req], greedy))
+    # every request: structural invariants
+    xa, na, ya = np_(x), np_(n_acc), np_(y)
+    assert ((xa >= 0) & (xa < cfg.V)).all()
+    assert ((na >= 0) & (na <= cfg.gamma)).all()
+    for i in range(cfg.R):
+        assert (ya[i, :na[i]] == xa[i, :na[i]]).all() and (ya[i, na[i] + 1:] == -1).all()
+        assert 0 <= ya[i, na[i]] < cfg.V
+
+
+def test_c4_pipeline():
+    """propose -> confidence (c* of the drafted rows) -> schedule(c) -> verify(l)."""
+    cfg = workloads.CONFIGS["c4"]
+    log("case c4 pipeline")
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V, B_max=cfg.sps_len)
+    x, pdx, pds = run_propose(t, cfg, False, ws=ws)
+    c_star, a_star = spec.spec_confidence(t["U"], t["W1"], t["W2"], t["x0"], x, t["Lt"], cfg.T, pd_stats=pds,
+                                          ws=ws)
+    ell, a, K, th = spec.spec_schedule(t["c"], t["sps"], ws=ws)
+    n_acc, y, pt_x, cv = run_verify(t, cfg, x, pds, False, ell=ell, ws=ws)
+    os_ = oracle.schedule(d["c"], d["sps"])
+    log("  schedule K*", int(np_(K)[0]), "oracle", os_["K_star"], "theta margin", os_["theta_margin"])
+    assert os_["theta_margin"] > MARGIN
+    np.testing.assert_array_equal(np_(ell), os_["ell"])
+    assert int(np_(K)[0]) == os_["K_star"]
+    assert float(np_(th)[0]) == pytest.approx(os_["theta_star"], rel=1e-12)
+    np.testing.assert_array_equal(np_(a), os_["a"])           # same fp64 products, same order
+    req = _sample(cfg.R)
+    sub = workloads.make(cfg, requests=req)
+    del d
+    log("  propose", check_propose(sub, np_(x)[req], np_(pdx)[req], np_(pds)[req], False))
+    oc, oa = oracle.confidence(sub["U"], sub["W1"], sub["W2"], sub["x0"], np_(x)[req], sub["Lt"],
+                               np.float32(cfg.T))
+    np.testing.assert_allclose(np_(c_star)[req], oc, rtol=0, atol=PROB_TOL)
+    ell_np = np_(ell)
+    log("  verify", check_verify(sub, np_(x)[req], ell_np[req], np_(n_acc)[req], np_(y)[req],
+                                 np_(pt_x)[req], np_(cv)[req], False))
+    # the verify c* equals the confidence c* on verified positions
+    for i in range(cfg.R):
+        np.testing.assert_allclose(np_(cv)[i, :ell_np[i]], np_(c_star)[i, :ell_np[i]], rtol=0, atol=1e-6)
