@@ -1,0 +1,247 @@
+"""Benchmark: verified draft tokens/s of one speculative-decoding output step
+(Markov-head propose + lossless verify with the fused confidence label) on
+one MI355X, and its fraction of the HBM roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+Workload (default c2): R=32 requests, gamma=7, V=129280, r=256, bf16
+Markov weights, fp32 base/target logits, sampled, T=1, every position
+verified.  Inputs are seeded synthetic data resident in HBM before timing.
+A step is one spec_markov_propose + one spec_verify (c* and p_t(x_k)
+included) with round = step index.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft tokens/s (propose+verify) at V=129280, gamma=7; % HBM roofline"
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "draft_tile": ["draft_sampling_verify_amd/csrc/propose.hip", "draft_sampling_verify_amd/csrc/common.h"],
+    "propose_pick": ["draft_sampling_verify_amd/csrc/propose.hip", "draft_sampling_verify_amd/csrc/common.h"],
+    "target_tile": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
+    "row_merge": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
+    "verify_sweep": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
+    "verify_resolve": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(kernel: str, cfg, K: int) -> float:
+    """Compulsory HBM bytes of ONE launch of `kernel` (what it must read and
+    write for its own job, each distinct byte once).  K = verified rows."""
+    R, g, V, r = cfg.R, cfg.gamma, cfg.V, cfg.r
+    wb = 2 if cfg.bf16 else 4
+    ng = (V + 127) // 128
+    if kernel == "draft_tile":      # one position: U_k rows, W2, W1 rows; (max, sum) partials out
+        return 4.0 * R * V + wb * r * V + wb * R * r + 8.0 * R * ng
+    if kernel == "target_tile":     # every target row once; (max, sum, argmax) partials out
+        return (R + K) * (4.0 * V + 12.0 * ng)
+    if kernel == "verify_sweep":    # U and target rows of every verified row, W2, W1 rows; partials out
+        return K * (8.0 * V + wb * r + 8.0 * ng) + wb * r * V
+    if kernel == "propose_pick":    # partials of every request + one granule rescan
+        return R * (8.0 * ng + 128 * (4.0 + wb * r) + 16.0)
+    if kernel == "row_merge":
+        return (R + K) * (8.0 * ng + 12.0)
+    if kernel == "verify_resolve":
+        return R * (8.0 * ng * (g + 2) + 128 * (8.0 + wb * r))
+    return float("nan")
+
+
+def step_algorithmic_bytes(cfg, K: int) -> float:
+    """Whole-step compulsory bytes: every input byte once (W2 once per call)."""
+    R, g, V, r = cfg.R, cfg.gamma, cfg.V, cfg.r
+    wb = 2 if cfg.bf16 else 4
+    propose = 4.0 * R * g * V + wb * r * V + wb * R * g * r + 16.0 * R * g
+    verify = 4.0 * K * V + 4.0 * (R + K) * V + wb * r * V + wb * K * r + 16.0 * R * (g + 1)
+    return propose + verify
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel's sources changed since."""
+    path = os.path.join(PROFILE_DIR, "pmc_%s_%s.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"source_sha256:\s*([0-9a-f]+)", text)
+    m_t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_h or not m_t or m_h.group(1) != kernel_source_hash(kernel):
+        return None
+    return float(m_t.group(1))
+
+
+def cpu_baseline(cfg, seconds_target=12.0):
+    """The oracle (single-threaded C, fp64) on a bounded sample of requests
+    of the same workload: propose + verify with c*, timed on the host."""
+    import oracle
+    import workloads
+    oracle.build()
+    per_req = None
+    done, t_total, reqs = 0, 0.0, []
+    rid = 0
+    while t_total < seconds_target and rid < cfg.R:
+        d = workloads.make(cfg, requests=[rid])
+        t0 = time.perf_counter()
+        p = oracle.markov_propose(d["U"], d["W1"], d["W2"], d["x0"], np.float32(cfg.T), False, 1, 0,
+                                  req_ids=d["req_ids"])
+        oracle.verify(d["U"], d["W1"], d["W2"], d["x0"], p["x"], d["Lt"], np.float32(cfg.T), False, 1, 0,
+                      req_ids=d["req_ids"])
+        t_total += time.perf_counter() - t0
+        reqs.append(rid)
+        done += cfg.gamma
+        rid += 1
+    return {"value": done / t_total, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of %d requests of workload %s (propose + verify with c*), %.1f s single-threaded"
+                      % (len(reqs), cfg.R, cfg.name, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run warmup + timed steps only (for rocprofv3), print the JSON line")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requests would shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import draft_sampling_verify_amd as spec
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    spec.lib()
+    cfg = workloads.CONFIGS[args.workload]
+    d = workloads.make(cfg)
+    dev = torch.device("cuda:0")
+    U = torch.from_numpy(d["U"]).to(dev)
+    Lt = torch.from_numpy(d["Lt"]).to(dev)
+    if cfg.bf16:
+        W1 = torch.from_numpy(d["W1"].view(np.int16)).to(dev).view(torch.bfloat16)
+        W2 = torch.from_numpy(d["W2"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        W1, W2 = torch.from_numpy(d["W1"]).to(dev), torch.from_numpy(d["W2"]).to(dev)
+    x0 = torch.from_numpy(d["x0"]).to(dev)
+    R, g, V = cfg.R, cfg.gamma, cfg.V
+    x = torch.empty((R, g), dtype=torch.int32, device=dev)
+    pd_x = torch.empty((R, g), dtype=torch.float32, device=dev)
+    pd_stats = torch.empty((R, g, 2), dtype=torch.float32, device=dev)
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev)
+    y = torch.empty((R, g + 1), dtype=torch.int32, device=dev)
+    pt_x = torch.empty((R, g), dtype=torch.float32, device=dev)
+    c_star = torch.empty((R, g), dtype=torch.float32, device=dev)
+    ws = spec.Workspace(R, g, cfg.r, V, device=dev)
+    stream = torch.cuda.current_stream()
+    del d
+
+    def step(i):
+        spec.spec_markov_propose(U, W1, W2, x0, cfg.T, False, 1, i, x=x, pd_x=pd_x, pd_stats=pd_stats,
+                                 ws=ws, stream=stream)
+        spec.spec_verify(U, W1, W2, x0, x, pd_stats, Lt, cfg.T, False, 1, i, n_acc=n_acc, y=y, pt_x=pt_x,
+                         c_star=c_star, ws=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, plain launches
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # same K steps again with HIP events around every kernel (on its stream)
+    spec.spec_profile_reset()
+    spec.spec_profile_enable(True)
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed_prof = time.perf_counter() - t1
+    spec.spec_profile_enable(False)
+    kernels = {}
+    for name in spec.spec_profile_names():
+        n, ms = spec.spec_profile_read(name)
+        kernels[name] = {"launches_per_step": n / args.steps, "avg_us": 1000.0 * ms / n,
+                         "us_per_step": 1000.0 * ms / args.steps}
+    spec.spec_profile_reset()
+    acc = float(n_acc.float().mean())
+    cmean = float(c_star.float().mean())
+    flags = spec.spec_device_status(ws)
+
+    K = R * g
+    ms_step = 1000.0 * elapsed / args.steps
+    value = K * args.steps / elapsed
+    dom = max(kernels, key=lambda k: kernels[k]["us_per_step"])
+    per_launch = algorithmic_bytes(dom, cfg, K)
+    achieved = per_launch / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+    traffic = read_traffic(dom, cfg.name)
+    step_bytes = step_algorithmic_bytes(cfg, K)
+    for k, v in kernels.items():
+        b = algorithmic_bytes(k, cfg, K)
+        v["algorithmic_GBs"] = round(b / (v["avg_us"] * 1e-6) / 1e9, 1)
+        v["avg_us"] = round(v["avg_us"], 2)
+        v["us_per_step"] = round(v["us_per_step"], 2)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "%s: R=%d, gamma=%d, V=%d, r=%d, %s Markov weights, fp32 logits, "
+                               "sampled, T=%g, all positions verified" %
+                               (cfg.name, R, g, V, cfg.r, "bf16" if cfg.bf16 else "fp32", cfg.T),
+                   "R": R, "gamma": g, "V": V, "r": cfg.r, "verified_per_step": K},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": per_launch},
+        "hbm_roofline_frac_step": round(step_bytes / (PEAK_HBM_GBS * 1e9) / (elapsed / args.steps), 4),
+        "step_algorithmic_bytes": step_bytes,
+        "ms_per_step_with_kernel_events": round(1000.0 * elapsed_prof / args.steps, 4),
+        "kernels": kernels,
+        "mean_n_acc": round(acc, 4),
+        "mean_c_star": round(cmean, 4),
+        "device_status": flags,
+    }
+    if not args.no_cpu_baseline and not args.profile_only:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
