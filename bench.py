@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + timed steps only (for rocprofv3), print the JSON line")
+    ap.add_argument("--calib-copy-mb", type=int, default=512,
+                    help="size of the device-to-device copy timed as the achievable-bandwidth reference")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -149,6 +151,8 @@ def main():
     else:
         W1, W2 = torch.from_numpy(d["W1"]).to(dev), torch.from_numpy(d["W2"]).to(dev)
     x0 = torch.from_numpy(d["x0"]).to(dev)
+    W2p = spec.spec_pack_w2(W2)          # once per weight, outside the timed region
+    del W2
     R, g, V = cfg.R, cfg.gamma, cfg.V
     x = torch.empty((R, g), dtype=torch.int32, device=dev)
     pd_x = torch.empty((R, g), dtype=torch.float32, device=dev)
@@ -162,9 +166,9 @@ def main():
     del d
 
     def step(i):
-        spec.spec_markov_propose(U, W1, W2, x0, cfg.T, False, 1, i, x=x, pd_x=pd_x, pd_stats=pd_stats,
+        spec.spec_markov_propose(U, W1, W2p, x0, cfg.T, False, 1, i, x=x, pd_x=pd_x, pd_stats=pd_stats,
                                  ws=ws, stream=stream)
-        spec.spec_verify(U, W1, W2, x0, x, pd_stats, Lt, cfg.T, False, 1, i, n_acc=n_acc, y=y, pt_x=pt_x,
+        spec.spec_verify(U, W1, W2p, x0, x, pd_stats, Lt, cfg.T, False, 1, i, n_acc=n_acc, y=y, pt_x=pt_x,
                          c_star=c_star, ws=ws, stream=stream)
 
     for i in range(args.warmup):
@@ -193,6 +197,22 @@ def main():
         kernels[name] = {"launches_per_step": n / args.steps, "avg_us": 1000.0 * ms / n,
                          "us_per_step": 1000.0 * ms / args.steps}
     spec.spec_profile_reset()
+    # achievable-bandwidth reference: a plain device copy of known size
+    copy_gbs = None
+    if args.calib_copy_mb > 0:
+        nb = args.calib_copy_mb << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2.0 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
     acc = float(n_acc.float().mean())
     cmean = float(c_star.float().mean())
     flags = spec.spec_device_status(ws)
@@ -231,6 +251,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": per_launch},
         "hbm_roofline_frac_step": round(step_bytes / (PEAK_HBM_GBS * 1e9) / (elapsed / args.steps), 4),
+        "device_copy_GBs": None if copy_gbs is None else round(copy_gbs, 1),
         "step_algorithmic_bytes": step_bytes,
         "ms_per_step_with_kernel_events": round(1000.0 * elapsed_prof / args.steps, 4),
         "kernels": kernels,

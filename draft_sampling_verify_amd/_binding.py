@@ -36,6 +36,8 @@ P, I, F, U64, SZ, D = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_u
 _SIGS = {
     "spec_workspace_bytes": ([I, I, I, I, I, I], SZ),
     "spec_workspace_init": ([P, SZ, P], I),
+    "spec_packed_w2_bytes": ([I, I, I], SZ),
+    "spec_pack_w2": ([P, I, I, I, P, P], I),
     "spec_device_status": ([P, P, I, P], I),
     "spec_markov_propose": ([P, P, P, I, P, I, I, I, I, F, I, U64, U64, P, P, P, P, SZ, P], I),
     "spec_verify": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
@@ -97,14 +99,16 @@ def _need(t, shape, dtype, name):
         raise ValueError("%s must be %s %s, got %s %s" % (name, tuple(shape), dtype, tuple(t.shape), t.dtype))
 
 
-def _draft_shapes(U, W1, W2, x0):
+def _draft_shapes(U, W1, W2p, x0):
     if U.dim() != 3 or U.dtype != torch.float32:
         raise ValueError("U must be float32 [R, gamma, V]")
     R, gamma, V = U.shape
-    if W2.dim() != 2 or W2.shape[0] != V:
-        raise ValueError("W2 must be [V, r]")
-    r = W2.shape[1]
-    _need(W1, (V, r), W2.dtype, "W1")
+    if W1.dim() != 2 or W1.shape[0] != V:
+        raise ValueError("W1 must be [V, r]")
+    r = W1.shape[1]
+    nbytes = spec_packed_w2_bytes(_wdtype(W1), r, V)
+    if W2p.dtype != torch.uint8 or W2p.dim() != 1 or W2p.numel() != nbytes:
+        raise ValueError("W2p must be the uint8 tensor of %d bytes returned by spec_pack_w2" % nbytes)
     _need(x0, (R,), torch.int32, "x0")
     return R, gamma, V, r
 
@@ -115,6 +119,26 @@ def _wdtype(W):
     if W.dtype == torch.float32:
         return SPEC_F32
     raise TypeError("weights must be torch.bfloat16 or torch.float32")
+
+
+def spec_packed_w2_bytes(w_dtype, r, V) -> int:
+    return int(lib().spec_packed_w2_bytes(w_dtype, r, V))
+
+
+def spec_pack_w2(W2, out=None, stream=None):
+    """Rearrange W2 [V, r] (bf16 or fp32) into the streamed layout; returns a
+    uint8 tensor (do this once per weight)."""
+    if W2.dim() != 2:
+        raise ValueError("W2 must be [V, r]")
+    V, r = W2.shape
+    dt = _wdtype(W2)
+    nbytes = spec_packed_w2_bytes(dt, r, V)
+    if nbytes == 0:
+        raise SpecError(SPEC_EINVAL, "spec_pack_w2")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=W2.device) if out is None else out
+    _need(out, (nbytes,), torch.uint8, "out")
+    _check(lib().spec_pack_w2(_ptr(W2), dt, r, V, _ptr(out), _stream(stream)), "spec_pack_w2")
+    return out
 
 
 def spec_workspace_bytes(op, R, gamma, r, V, B_max=0) -> int:
@@ -159,9 +183,9 @@ def spec_device_status(ws: Workspace, stream=None, clear=False) -> int:
     return flags.value
 
 
-def spec_markov_propose(U, W1, W2, x0, T, greedy=False, seed=1, round=0, x=None, pd_x=None,
+def spec_markov_propose(U, W1, W2p, x0, T, greedy=False, seed=1, round=0, x=None, pd_x=None,
                         pd_stats=None, ws=None, stream=None):
-    R, gamma, V, r = _draft_shapes(U, W1, W2, x0)
+    R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
     dev = U.device
     _need(x, (R, gamma), torch.int32, "x")
     _need(pd_x, (R, gamma), torch.float32, "pd_x")
@@ -170,17 +194,17 @@ def spec_markov_propose(U, W1, W2, x0, T, greedy=False, seed=1, round=0, x=None,
     pd_x = torch.empty((R, gamma), dtype=torch.float32, device=dev) if pd_x is None else pd_x
     pd_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev) if pd_stats is None else pd_stats
     ws = _ws(ws, R, gamma, r, V, dev)
-    st = lib().spec_markov_propose(_ptr(U), _ptr(W1), _ptr(W2), _wdtype(W2), _ptr(x0), R, gamma, r, V,
+    st = lib().spec_markov_propose(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), R, gamma, r, V,
                                    float(T), int(bool(greedy)), int(seed), int(round), _ptr(x), _ptr(pd_x),
                                    _ptr(pd_stats), ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_markov_propose")
     return x, pd_x, pd_stats
 
 
-def spec_verify(U, W1, W2, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=0, ell=None,
+def spec_verify(U, W1, W2p, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=0, ell=None,
                 n_acc=None, y=None, pt_x=None, c_star=None, want_pt_x=True, want_c_star=True,
                 ws=None, stream=None):
-    R, gamma, V, r = _draft_shapes(U, W1, W2, x0)
+    R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
     dev = U.device
     _need(x, (R, gamma), torch.int32, "x")
     _need(pd_stats, (R, gamma, 2), torch.float32, "pd_stats")
@@ -197,7 +221,7 @@ def spec_verify(U, W1, W2, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=0
     if c_star is None and want_c_star:
         c_star = torch.empty((R, gamma), dtype=torch.float32, device=dev)
     ws = _ws(ws, R, gamma, r, V, dev)
-    st = lib().spec_verify(_ptr(U), _ptr(W1), _ptr(W2), _wdtype(W2), _ptr(x0), _ptr(x), _ptr(pd_stats),
+    st = lib().spec_verify(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(x), _ptr(pd_stats),
                            _ptr(Lt), _ptr(ell), R, gamma, r, V, float(T), int(bool(greedy)), int(seed),
                            int(round), _ptr(n_acc), _ptr(y), _ptr(pt_x), _ptr(c_star), ws.ptr(), ws.nbytes,
                            _stream(stream))
@@ -205,9 +229,9 @@ def spec_verify(U, W1, W2, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=0
     return n_acc, y, pt_x, c_star
 
 
-def spec_confidence(U, W1, W2, x0, x, Lt, T, pd_stats=None, c_star=None, a_star=None, want_a_star=True,
+def spec_confidence(U, W1, W2p, x0, x, Lt, T, pd_stats=None, c_star=None, a_star=None, want_a_star=True,
                     ws=None, stream=None):
-    R, gamma, V, r = _draft_shapes(U, W1, W2, x0)
+    R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
     dev = U.device
     _need(x, (R, gamma), torch.int32, "x")
     _need(pd_stats, (R, gamma, 2), torch.float32, "pd_stats")
@@ -218,7 +242,7 @@ def spec_confidence(U, W1, W2, x0, x, Lt, T, pd_stats=None, c_star=None, a_star=
     if a_star is None and want_a_star:
         a_star = torch.empty((R, gamma), dtype=torch.float64, device=dev)
     ws = _ws(ws, R, gamma, r, V, dev)
-    st = lib().spec_confidence(_ptr(U), _ptr(W1), _ptr(W2), _wdtype(W2), _ptr(x0), _ptr(x), _ptr(pd_stats),
+    st = lib().spec_confidence(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(x), _ptr(pd_stats),
                                _ptr(Lt), R, gamma, r, V, float(T), _ptr(c_star), _ptr(a_star), ws.ptr(),
                                ws.nbytes, _stream(stream))
     _check(st, "spec_confidence")

@@ -53,10 +53,12 @@ DraftArgs make_args(const float* U, const void* W1, const void* W2, int w_dtype,
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH; }
 
-__global__ void k_zero_words(uint32_t* p, int n)
+__global__ void k_zero_words(uint32_t* p, size_t n)
 {
-    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
+
 
 // ---- profiling records
 struct ProfRecord {
@@ -77,8 +79,12 @@ ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s)
     if (!g_prof_on) return;
     if (g_pool_used == g_event_pool.size()) {
         hipEvent_t a, b;
-        if (hipEventCreate(&a) != hipSuccess) return;
-        if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return; }
+        // no system-scope fence: the events only timestamp work on this device
+        if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return;
+        if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
+            hipEventDestroy(a);
+            return;
+        }
         g_event_pool.emplace_back(a, b);
     }
     auto ev = g_event_pool[g_pool_used++];
@@ -124,8 +130,23 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
 int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream)
 {
     if (!ws || ws_bytes < spec::WS_HEADER) return SPEC_EWORKSPACE;
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint32_t*)ws, 64);
+    hipLaunchKernelGGL(k_zero_words, dim3(256), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ws,
+                       spec::WS_HEADER / 4);
     return launch_status(hipGetLastError());
+}
+
+size_t spec_packed_w2_bytes(int w_dtype, int r, int V)
+{
+    if (check_draft(nullptr, nullptr, nullptr, w_dtype, nullptr, 0, 1, r, V, 1.0f) != SPEC_OK) return 0;
+    return spec::packed_w2_bytes(w_dtype, r, V);
+}
+
+int spec_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, spec_stream_t stream)
+{
+    int st = check_draft(nullptr, nullptr, nullptr, w_dtype, nullptr, 0, 1, r, V, 1.0f);
+    if (st != SPEC_OK) return st;
+    if (!W2 || !W2p || !aligned16(W2) || !aligned16(W2p)) return SPEC_EINVAL;
+    return launch_status(spec::launch_pack_w2(W2, w_dtype, r, V, W2p, (hipStream_t)stream));
 }
 
 int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags)
@@ -137,7 +158,7 @@ int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags)
     if (hipStreamSynchronize(s) != hipSuccess) return SPEC_ELAUNCH;
     *flags = (int)word;
     if (clear) {
-        hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, (uint32_t*)ws, 1);
+        hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, (uint32_t*)ws, (size_t)1);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     }
     return word ? SPEC_EDEVICE : SPEC_OK;
@@ -193,7 +214,8 @@ int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
     if (R == 0) return SPEC_OK;
     const spec::VerifyWs w = spec::carve_verify(ws, R, gamma, V, true, nullptr);
     DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, 0, 0, 0, ws);
-    return launch_status(spec::launch_confidence(a, pd_stats, Lt, c_star, a_star, w, (hipStream_t)stream));
+    return launch_status(
+        spec::launch_confidence(a, pd_stats, Lt, c_star, a_star, w, (hipStream_t)stream));
 }
 
 int spec_schedule(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* ell, double* a,

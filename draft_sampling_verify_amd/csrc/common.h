@@ -187,25 +187,29 @@ __device__ inline int block_min(int v, int* sm)
 // granule's 128 weights.  Threads of a 256-wide block own contiguous
 // granule ranges [g0, g1).
 
-// Thread-local sum of its granule masses and the block-wide exclusive scan.
+// One wave; lane l owns the contiguous granule range [g0, g1).  Returns the
+// lane's exclusive prefix of the granule masses and the wave total.
 template <typename WF>
-__device__ inline void granule_scan(WF wf, int g0, int g1, float* smf, float& tsum, float& excl,
-                                    float& total)
+__device__ inline void wave_granule_scan(WF wf, int g0, int g1, float& excl, float& total)
 {
-    tsum = 0.0f;
+    const int lane = threadIdx.x & (WAVE - 1);
+    float tsum = 0.0f;
     for (int g = g0; g < g1; ++g) tsum += wf(g);
-    excl = block_excl_scan(tsum, smf, total);
+    const float incl = wave_incl_scan(tsum);
+    excl = __shfl_up(incl, 1, WAVE);
+    if (lane == 0) excl = 0.0f;
+    total = __shfl(incl, WAVE - 1, WAVE);
 }
 
-// First granule whose running sum exceeds target.  Every thread re-runs its
+// First granule of positive mass whose running sum exceeds target.  Every lane re-runs its
 // own running sum from its exclusive prefix and claims if it crosses; the
-// lowest claiming thread wins (prefix pieces computed by different threads
-// may disagree in the last bit).  Returns the granule (same in every thread)
-// and the running sum before it, or -1 if no partial sum exceeds target;
-// then the last granule with positive mass is returned in *fallback_g.
+// lowest claiming lane wins (prefix pieces of different lanes may disagree
+// in the last bit).  Returns the granule and the running sum before it,
+// identical in every lane; if no partial sum exceeds target (rounding),
+// returns the last granule with positive mass and sets fallback.
 template <typename WF>
-__device__ inline int granule_find(WF wf, int g0, int g1, float excl, float target, float* smf,
-                                   int* smi, float& before, int& fallback_g)
+__device__ inline int wave_granule_find(WF wf, int g0, int g1, float excl, float target, float& before,
+                                        bool& fallback)
 {
     float run = excl, prev = excl;
     int pick = -1, lastpos = -1;
@@ -215,21 +219,20 @@ __device__ inline int granule_find(WF wf, int g0, int g1, float excl, float targ
         if (pick < 0) {
             prev = run;
             run += wg;
-            if (run > target) pick = g;
+            if (run > target && wg > 0.0f) pick = g;
         }
     }
-    const int first = block_min(pick >= 0 ? (int)threadIdx.x : 0x7fffffff, smi);
-    if ((int)threadIdx.x == first) {
-        smi[4] = pick;
-        smf[4] = prev;
+    const unsigned long long hit = __ballot(pick >= 0);
+    if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        fallback = false;
+        before = __shfl(prev, L, WAVE);
+        return __shfl(pick, L, WAVE);
     }
-    fallback_g = -block_min(-lastpos, smi);
-    if (first == 0x7fffffff && threadIdx.x == 0) smi[4] = -1;
-    __syncthreads();
-    const int gstar = smi[4];
-    before = smf[4];
-    __syncthreads();
-    return gstar;
+    fallback = true;
+    before = 0.0f;
+    const int lp = -wave_min(-lastpos);
+    return lp < 0 ? 0 : lp;
 }
 
 // Inside one granule, run by a single full wave: lane l holds the weights of
@@ -246,12 +249,16 @@ __device__ inline int granule_pick(float ea, float eb, float before, float targe
     if (lane == 0) ex = 0.0f;
     const float ca = (before + ex) + ea;
     const float cb = ca + eb;
-    const unsigned long long hit = __ballot(!fallback && (ca > target || cb > target));
+    // only an id of positive weight can be the first to pass the target
+    // (the running sums of neighbouring lanes are rounded differently)
+    const bool ha = ca > target && ea > 0.0f, hb = cb > target && eb > 0.0f;
+    const unsigned long long hit = __ballot(!fallback && (ha || hb));
     if (hit) {
         const int L = __ffsll((long long)hit) - 1;
-        const float la = __shfl(ca, L, WAVE), lea = __shfl(ea, L, WAVE), leb = __shfl(eb, L, WAVE);
-        e_out = la > target ? lea : leb;
-        return la > target ? 2 * L : 2 * L + 1;
+        const bool la = __shfl((int)ha, L, WAVE) != 0;
+        const float lea = __shfl(ea, L, WAVE), leb = __shfl(eb, L, WAVE);
+        e_out = la ? lea : leb;
+        return la ? 2 * L : 2 * L + 1;
     }
     const unsigned long long nz = __ballot(ea > 0.0f || eb > 0.0f);
     const int L = nz ? 63 - __clzll((long long)nz) : 0;
@@ -275,47 +282,89 @@ __device__ inline int xcd_logical(int bid, int n)
 
 // ------------------------------------------------------- MFMA bias tile
 //
-// One wave computes D[m][n] = sum_i W2[col0 + m, i] * W1[tok_n, i] for the
-// 32 vocabulary ids col0..col0+31 (m) and 32 rows (n), i.e. the Markov bias
-// of 32 rows at 32 ids, with v_mfma_f32_32x32x16_bf16 (bf16 weights) or
-// v_mfma_f32_32x32x2_f32 (fp32 weights).  Operand lane layout (lane l,
-// h = l >> 5): A holds W2 row col0 + (l & 31), k-slice 8h..8h+7 of each
-// 16-wide k-step; B holds W1 row tok_{l & 31}, same k-slice.  Result lane l
-// holds column n = l & 31 (the row of the block) and 16 ids
-// col0 + 8*(j>>2) + 4h + (j&3), j = 0..15.
+// The Markov bias of 32 rows at 32 vocabulary ids is one wave's
+//   D[m][n] = sum_i W2[32b + m, i] * W1[tok_n, i]
+// on v_mfma_f32_32x32x16_bf16 (bf16 weights) or v_mfma_f32_32x32x2_f32
+// (fp32 weights): m runs over the ids of column block b, n over the rows.
 //
-// The W2 operand depends only on the granule and is kept in registers while
-// a workgroup walks over several row blocks.
+// A operand (W2) comes from the packed layout written by k_pack_w2: for
+// column block b and k-step s the 64 lanes' operands are one contiguous
+// 1 KB (bf16) chunk, lane l = n + 32h holding W2[32b + n][16s + 8h .. +7],
+// so every load instruction is fully coalesced.  For fp32 weights a chunk
+// holds four k-steps of 2: lane l holds W2[32b + n][8t + 2q + h], q = 0..3.
+// The A operand of a wave stays in registers while its workgroup walks
+// over row blocks.
+//
+// B operand (W1 rows of the 32 row tokens) is staged once per row block in
+// LDS (row stride RS elements, padded so the 32 rows fall on distinct
+// banks), lane l = n + 32h reading row n, k-slice 8h..8h+7 of each step.
+//
+// Result lane l = n + 32h holds row n and the 16 ids
+// 32b + 8*(j>>2) + 4h + (j&3), j = 0..15.
 
 template <typename WT, int KS>
-struct W2Operand;
+struct TileOps;
 
 template <int KS>
-struct W2Operand<bf16w, KS> {
-    uint4 a[KS];  // KS k-steps of 16; 8 bf16 per lane per step
-    __device__ inline void load(const bf16w* W2, int r, int V, int col, int h)
+struct TileOps<bf16w, KS> {
+    static constexpr int ELEM = 2;
+    static constexpr int RS = 16 * KS + 8;  // LDS row stride (elements) of the staged W1 rows
+    uint4 a[KS];
+    // ks = r / 16 real k-steps (<= KS); the rest multiply zeros
+    __device__ inline void load_a(const void* W2p, int ks, int b, bool valid, int lane)
     {
-        const int ks = r >> 4;
+        const uint4* P = reinterpret_cast<const uint4*>(W2p) + (size_t)b * ks * WAVE + lane;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (s < ks && col < V)
-                a[s] = *reinterpret_cast<const uint4*>(W2 + (size_t)col * r + 16 * s + 8 * h);
-            else
-                a[s] = make_uint4(0, 0, 0, 0);
-        }
+        for (int s = 0; s < KS; ++s) a[s] = (valid && s < ks) ? P[(size_t)s * WAVE] : make_uint4(0, 0, 0, 0);
     }
-    // tok < 0 -> zero row
-    __device__ inline f32x16 mul(const bf16w* W1, int r, int tok, int h) const
+    __device__ inline f32x16 mfma(const void* sB, int ks, int lane) const
     {
-        const int ks = r >> 4;
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(sB) + (lane & 31) * RS + 8 * (lane >> 5);
         f32x16 acc = {};
-        const bf16w* row = W1 + (size_t)(tok < 0 ? 0 : tok) * r + 8 * h;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if (s < ks) {
-                uint4 b = tok >= 0 ? *reinterpret_cast<const uint4*>(row + 16 * s) : make_uint4(0, 0, 0, 0);
+                const uint4 bv = *reinterpret_cast<const uint4*>(B + 16 * s);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
-                                                              __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+                                                              __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
+    // B operand held in registers: lane l = n + 32h keeps W1[tok, 16s+8h..+7]
+    // of its own row token (tok < 0: zeros).  Used by the single-row rescans.
+    struct BRow {
+        uint4 b[KS];
+        __device__ inline void load(const bf16w* W1, int r, int tok, int ks, int lane)
+        {
+            const uint4* row = reinterpret_cast<const uint4*>(W1 + (size_t)(tok < 0 ? 0 : tok) * r) + (lane >> 5);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) b[s] = (tok >= 0 && s < ks) ? row[2 * s] : make_uint4(0, 0, 0, 0);
+        }
+    };
+    __device__ inline f32x16 mfma_row(const BRow& br, int ks) const
+    {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s < ks)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                              __builtin_bit_cast(bf16x8, br.b[s]), acc, 0, 0, 0);
+        }
+        return acc;
+    }
+    // B operand straight from global memory (one row per lane; used by the
+    // single-row rescans, which must see the same bits as the staged path)
+    __device__ inline f32x16 mfma_global(const bf16w* W1, int r, int tok, int ks, int lane) const
+    {
+        const uint4* row = reinterpret_cast<const uint4*>(W1 + (size_t)(tok < 0 ? 0 : tok) * r) + (lane >> 5);
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s < ks) {
+                const uint4 bv = tok >= 0 ? row[2 * s] : make_uint4(0, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                              __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
             }
         }
         return acc;
@@ -323,49 +372,194 @@ struct W2Operand<bf16w, KS> {
 };
 
 template <int KS>
-struct W2Operand<float, KS> {
-    float a[KS];  // KS k-steps of 2; one fp32 per lane per step
-    __device__ inline void load(const float* W2, int r, int V, int col, int h)
+struct TileOps<float, KS> {
+    static constexpr int ELEM = 4;
+    static constexpr int RS = 8 * KS + 4;  // KS groups of four 2-wide k-steps
+    float4 a[KS];
+    __device__ inline void load_a(const void* W2p, int ks, int b, bool valid, int lane)
     {
-        const int ks = r >> 1;
+        const float4* P = reinterpret_cast<const float4*>(W2p) + (size_t)b * ks * WAVE + lane;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            a[s] = (s < ks && col < V) ? W2[(size_t)col * r + 2 * s + h] : 0.0f;
+        for (int t = 0; t < KS; ++t) a[t] = (valid && t < ks) ? P[(size_t)t * WAVE] : make_float4(0, 0, 0, 0);
     }
-    __device__ inline f32x16 mul(const float* W1, int r, int tok, int h) const
+    __device__ inline f32x16 mfma(const void* sB, int ks, int lane) const
     {
-        const int ks = r >> 1;
+        const float* B = reinterpret_cast<const float*>(sB) + (lane & 31) * RS + (lane >> 5);
         f32x16 acc = {};
-        const float* row = W1 + (size_t)(tok < 0 ? 0 : tok) * r + h;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (s < ks) {
-                float b = tok >= 0 ? row[2 * s] : 0.0f;
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b, acc, 0, 0, 0);
+        for (int t = 0; t < KS; ++t) {
+            if (t < ks) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].x, B[8 * t + 0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].y, B[8 * t + 2], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, B[8 * t + 4], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, B[8 * t + 6], acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
+    struct BRow {
+        float4 b[KS];  // W1[tok, 8t + 2q + h], q = 0..3
+        __device__ inline void load(const float* W1, int r, int tok, int ks, int lane)
+        {
+            const float* row = W1 + (size_t)(tok < 0 ? 0 : tok) * r + (lane >> 5);
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+                b[t] = (tok >= 0 && t < ks) ? make_float4(row[8 * t], row[8 * t + 2], row[8 * t + 4], row[8 * t + 6])
+                                            : make_float4(0, 0, 0, 0);
+        }
+    };
+    __device__ inline f32x16 mfma_row(const BRow& br, int ks) const
+    {
+        f32x16 acc = {};
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            if (t < ks) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].x, br.b[t].x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].y, br.b[t].y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, br.b[t].z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, br.b[t].w, acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
+    __device__ inline f32x16 mfma_global(const float* W1, int r, int tok, int ks, int lane) const
+    {
+        const float* row = W1 + (size_t)(tok < 0 ? 0 : tok) * r + (lane >> 5);
+        f32x16 acc = {};
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            if (t < ks) {
+                const float b0 = tok >= 0 ? row[8 * t + 0] : 0.0f, b1 = tok >= 0 ? row[8 * t + 2] : 0.0f;
+                const float b2 = tok >= 0 ? row[8 * t + 4] : 0.0f, b3 = tok >= 0 ? row[8 * t + 6] : 0.0f;
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].x, b0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].y, b1, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, b2, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, b3, acc, 0, 0, 0);
             }
         }
         return acc;
     }
 };
 
-// id of accumulator j held by a lane of half h, relative to the wave's col0
-__device__ inline int acc_col(int j, int h) { return 8 * (j >> 2) + 4 * h + (j & 3); }
+// k-steps (bf16) or groups of four k-steps (fp32) for rank r
+template <typename WT> __host__ __device__ inline int k_steps(int r);
+template <> __host__ __device__ inline int k_steps<bf16w>(int r) { return r / 16; }
+template <> __host__ __device__ inline int k_steps<float>(int r) { return r / 8; }
 
-// Load 16 fp32 values row[col0 + acc_col(j, h)] (ids >= V -> -inf).
-// vec4: the row base is 16-byte aligned and V % 4 == 0.
-__device__ inline void load_row16(const float* row, int col0, int h, int V, bool vec4, float (&v)[16])
+// Stage the W1 rows of the 32 tokens tok[0..31] (LDS; -1 = zero row) into
+// sB[32][RS]; all threads of the block take part.
+template <typename WT, int RS>
+__device__ inline void stage_w1(void* sB, const WT* W1, const int* tok, int r)
+{
+    constexpr int ELEM = (int)sizeof(WT);
+    const int per_row = r * ELEM / 16;  // uint4 per row
+    for (int idx = threadIdx.x; idx < 32 * per_row; idx += TILE_THREADS) {
+        const int row = idx / per_row, c = idx - row * per_row;
+        const int tk = tok[row];
+        const uint4 v = tk >= 0 ? reinterpret_cast<const uint4*>(W1 + (size_t)tk * r)[c] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sB) + (size_t)row * RS * ELEM + 16 * c) = v;
+    }
+}
+
+// LDS tile of the block's results: 32 rows x 128 ids (+4 floats padding).
+constexpr int ZS = GRAN + 4;
+
+// Wave w stores its 32x32 result into sZ[n][32w + ...].
+__device__ inline void store_tile(float* sZ, const f32x16& acc, int w, int lane)
+{
+    const int n = lane & 31, h = lane >> 5;
+    float* row = sZ + n * ZS + 32 * w + 4 * h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(row + 8 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+}
+
+// Load the 16 values a lane of half h holds in the MFMA result layout,
+// row[c0 + 8*(j>>2) + 4h + (j&3)] for j = 0..15 (ids >= V read as -inf).
+__device__ inline void load_acc16(const float* row, int c0, int h, int V, bool vec4, float (&v)[16])
 {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int c = col0 + 8 * q + 4 * h;
+        const int c = c0 + 8 * q + 4 * h;
         if (vec4 && c + 3 < V) {
-            float4 t = *reinterpret_cast<const float4*>(row + c);
+            const float4 t = *reinterpret_cast<const float4*>(row + c);
             v[4 * q + 0] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[4 * q + e] = (c + e < V) ? row[c + e] : -INFINITY;
         }
     }
+}
+
+// Load 16 consecutive fp32 values row[c0 .. c0+15]; ids >= V read as -inf.
+// Fully in-bounds aligned segments take four unconditional 16-byte loads.
+__device__ inline void load16(const float* row, int c0, int V, bool vec4, float (&v)[16])
+{
+    if (vec4 && c0 + 15 < V) {
+        const float4* p4 = reinterpret_cast<const float4*>(row + c0);
+        const float4 a = p4[0], b = p4[1], c = p4[2], d = p4[3];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        v[8] = c.x; v[9] = c.y; v[10] = c.z; v[11] = c.w;
+        v[12] = d.x; v[13] = d.y; v[14] = d.z; v[15] = d.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = (c0 + e < V) ? row[c0 + e] : -INFINITY;
+    }
+}
+
+// Reductions across the 8 lanes that share an epilogue row, on DPP (no LDS
+// round trip): quad_perm swaps lanes 1<->0, 3<->2 (xor 1) and 2,3<->0,1
+// (xor 2); row_half_mirror pairs lane i with 7-i, joining the two quads.
+// Every lane of the group ends with the same result.
+template <int CTRL>
+__device__ inline float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141;
+
+__device__ inline float oct_max(float v)
+{
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    return fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+}
+__device__ inline float oct_sum(float v)
+{
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    return v + dpp_f<DPP_HALF_MIRROR>(v);
+}
+__device__ inline void oct_argmax(float& v, int& i)
+{
+    argmax_merge(v, i, dpp_f<DPP_XOR1>(v), dpp_i<DPP_XOR1>(i));
+    argmax_merge(v, i, dpp_f<DPP_XOR2>(v), dpp_i<DPP_XOR2>(i));
+    argmax_merge(v, i, dpp_f<DPP_HALF_MIRROR>(v), dpp_i<DPP_HALF_MIRROR>(i));
+}
+
+// Instantiations of the rank-dependent kernels: bf16 weights use r/16 k-steps
+// (4, 8, 16 or 32 held; fewer real steps multiply zeros), fp32 weights r/8
+// groups of four k-steps (2, 8 or 32 held).
+template <template <typename, int> class F, typename... Args>
+inline hipError_t dispatch_ks(int w_dtype, int r, Args&&... args)
+{
+    if (w_dtype == 1) {
+        const int ks = r / 16;
+        if (ks <= 4) return F<bf16w, 4>::run(args...);
+        if (ks <= 8) return F<bf16w, 8>::run(args...);
+        if (ks <= 16) return F<bf16w, 16>::run(args...);
+        return F<bf16w, 32>::run(args...);
+    }
+    const int ks = r / 8;
+    if (ks <= 2) return F<float, 2>::run(args...);
+    if (ks <= 8) return F<float, 8>::run(args...);
+    return F<float, 32>::run(args...);
 }
 
 }  // namespace spec

@@ -43,6 +43,7 @@ struct VerifyWs {
     float2* trow;    // [TR] merged (M_t, S_t)
     int32_t* targ;   // [TR] row argmax
     float2* vpart;   // [VR, n_gran] per-granule (TV mass, residual mass)
+    float* vbias;    // [VR] Markov bias at the drafted id of each verified row
     int4* vmap;      // [VR] verified row -> (request, k, target row, 0)
     int2* tmap;      // [TR] target row -> (request, row within request)
     int32_t* voff;   // [R] first verified row of each request
@@ -64,6 +65,7 @@ inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence,
     w.trow = c.take<float2>(TR);
     w.targ = c.take<int32_t>(TR);
     w.vpart = c.take<float2>(VR * ng);
+    w.vbias = c.take<float>(VR);
     w.vmap = c.take<int4>(VR);
     w.tmap = c.take<int2>(TR);
     w.voff = c.take<int32_t>(R);
@@ -97,7 +99,7 @@ inline ProposeWs carve_propose(void* ws, int R, int V, size_t* bytes)
 struct DraftArgs {
     const float* U;
     const void* W1;
-    const void* W2;
+    const void* W2;    // packed layout (spec_pack_w2)
     int w_dtype;       // 0 fp32, 1 bf16
     const int32_t* x0;
     const int32_t* x;  // drafts (propose: output being filled; verify: input)
@@ -109,6 +111,11 @@ struct DraftArgs {
 };
 
 // propose.hip
+hipError_t launch_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, hipStream_t s);
+inline size_t packed_w2_bytes(int w_dtype, int r, int V)
+{
+    return (size_t)((V + 31) / 32) * 32 * (size_t)r * (w_dtype == 1 ? 2 : 4);
+}
 hipError_t launch_propose(const DraftArgs& a, int32_t* x_out, float* pd_x, float* pd_stats,
                           const ProposeWs& w, hipStream_t s);
 // Draft (max, sum) per granule and per row for all R*gamma drafted rows

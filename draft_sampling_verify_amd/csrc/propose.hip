@@ -2,25 +2,77 @@
 // for k = 1..gamma, z_k = U_k + W1[x_{k-1}] W2^T, x_k ~ softmax(z_k / T).
 //
 // Per position two kernels run back to back on the caller's stream:
-//   k_draft_tile   grid over (granule, chunk of 32-row blocks): the bias of
-//                  32 rows at 128 ids per workgroup on MFMA (W2 operand held
-//                  in registers across the row blocks of the chunk), plus
-//                  U, and per (row, granule) max / sum of 2^((z-max)c) /
-//                  argmax -- one streaming pass over U_k and W2.
-//   k_propose_pick one workgroup per request: merge the granule partials,
-//                  draw the Philox uniform, find the granule where the
-//                  running sum crosses u*S, recompute that granule's 128
-//                  logits with the same tile code and pick the id.
+//   k_draft_tile   one workgroup per (128-id granule, chunk of 32-row
+//                  blocks): the bias of 32 rows x 128 ids on MFMA (W2
+//                  operand stationary in registers, W1 rows staged in LDS),
+//                  transposed through LDS so that every thread owns 16
+//                  consecutive ids of one row; adds U_k (coalesced 64-byte
+//                  loads) and writes per (row, granule) the max, the sum of
+//                  2^((z - max) c) and (greedy) the argmax.
+//   k_propose_pick one wave per request: merge the granule partials, draw
+//                  the Philox uniform, find the granule where the running
+//                  sum crosses u * S, recompute that granule's 128 logits
+//                  with the same MFMA operands and pick the id.
 // x_k stays on the device and feeds the next position's W1 gather.
 #include "common.h"
 #include "internal.h"
 
 namespace spec {
 
+// ------------------------------------------------------------ W2 packing
+
+__global__ void k_pack_w2_bf16(const uint16_t* W2, int r, int V, int ks, uint4* out, size_t total)
+{
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const int l = (int)(idx % WAVE);
+    const size_t bs = idx / WAVE;
+    const int s = (int)(bs % ks);
+    const int b = (int)(bs / ks);
+    const int v = 32 * b + (l & 31), h = l >> 5;
+    out[idx] = v < V ? *reinterpret_cast<const uint4*>(W2 + (size_t)v * r + 16 * s + 8 * h) : make_uint4(0, 0, 0, 0);
+}
+
+__global__ void k_pack_w2_f32(const float* W2, int r, int V, int ks, float4* out, size_t total)
+{
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const int l = (int)(idx % WAVE);
+    const size_t bt = idx / WAVE;
+    const int tq = (int)(bt % ks);
+    const int b = (int)(bt / ks);
+    const int v = 32 * b + (l & 31), h = l >> 5;
+    float4 o = make_float4(0, 0, 0, 0);
+    if (v < V) {
+        const float* row = W2 + (size_t)v * r + 8 * tq + h;
+        o = make_float4(row[0], row[2], row[4], row[6]);
+    }
+    out[idx] = o;
+}
+
+hipError_t launch_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, hipStream_t s)
+{
+    const int nblk = (V + 31) / 32;
+    if (w_dtype == 1) {
+        const int ks = r / 16;
+        const size_t total = (size_t)nblk * ks * WAVE;
+        hipLaunchKernelGGL(k_pack_w2_bf16, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                           (const uint16_t*)W2, r, V, ks, (uint4*)W2p, total);
+    } else {
+        const int ks = r / 8;
+        const size_t total = (size_t)nblk * ks * WAVE;
+        hipLaunchKernelGGL(k_pack_w2_f32, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                           (const float*)W2, r, V, ks, (float4*)W2p, total);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ draft tile
+
 struct TileArgs {
     const float* U;
     const void* W1;
-    const void* W2;
+    const void* W2p;
     const int32_t* x0;
     const int32_t* x;  // drafts; row (req, kk) reads x[req*gamma + kk - 1] when kk > 0
     int R, gamma, r, V;
@@ -50,94 +102,100 @@ __device__ inline void draft_row(const TileArgs& p, int row, int& req, int& kk, 
 }
 
 template <typename WT, int KS, bool GREEDY>
-__global__ __launch_bounds__(TILE_THREADS) void k_draft_tile(TileArgs p)
+__global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 {
+    using Ops = TileOps<WT, KS>;
     const int nlog = p.n_gran * p.n_chunks;
     const int lid = xcd_logical(blockIdx.x, nlog);
     if (lid >= nlog) return;
     const int g = lid / p.n_chunks, chunk = lid - g * p.n_chunks;
-    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-    const int h = lane >> 5, n = lane & 31;
-    const int col0 = g * GRAN + 32 * w;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const int ks = k_steps<WT>(p.r);
+    const int nblk = (p.V + 31) / 32;
 
-    W2Operand<WT, KS> A;
-    A.load(reinterpret_cast<const WT*>(p.W2), p.r, p.V, col0 + n, h);
+    Ops A;
+    A.load_a(p.W2p, ks, 4 * g + w, 4 * g + w < nblk, lane);
 
-    __shared__ float sm_m[4][32], sm_s[4][32];
-    __shared__ int sm_i[4][32];
+    __shared__ __align__(16) char sB[32 * Ops::RS * Ops::ELEM];
+    __shared__ __align__(16) float sZ[32 * ZS];
+    __shared__ int s_tok[32];
 
+    const int er = t >> 3, ec = (t & 7) * 16;  // epilogue: row er, ids ec..ec+15 of the granule
+    const int cbase = g * GRAN + ec;
     for (int b = 0; b < p.bpc; ++b) {
         const int rb = chunk * p.bpc + b;
         if (rb * BLOCK_ROWS >= p.nrows) break;
-        const int row = rb * BLOCK_ROWS + n;
-        int req = 0, kk = 0, tok = -1;
-        bool valid = row < p.nrows;
-        if (valid) {
-            draft_row(p, row, req, kk, tok);
-            if (tok < 0 || tok >= p.V) {
-                if (g == 0 && w == 0 && h == 0) raise_flag(p.status, 1u);
-                tok = -1;
-                valid = false;
-            }
-        }
-        const f32x16 acc = A.mul(reinterpret_cast<const WT*>(p.W1), p.r, tok, h);
+        // the epilogue row's U segment does not depend on the tokens: issue it first
+        const int erow = rb * BLOCK_ROWS + er;
         float z[16];
-        if (valid) {
-            load_row16(p.U + ((size_t)req * p.gamma + kk) * p.V, col0, h, p.V, p.vec4, z);
+        if (erow < p.nrows) {
+            const int ereq = p.kfix >= 0 ? erow : erow / p.gamma;
+            const int ekk = p.kfix >= 0 ? p.kfix : erow - ereq * p.gamma;
+            load16(p.U + ((size_t)ereq * p.gamma + ekk) * p.V, cbase, p.V, p.vec4, z);
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) z[j] = -INFINITY;
         }
+        if (t < 32) {
+            const int row = rb * BLOCK_ROWS + t;
+            int req = -1, kk = 0, tok = -1;
+            if (row < p.nrows) {
+                draft_row(p, row, req, kk, tok);
+                if (tok < 0 || tok >= p.V) {
+                    if (g == 0) raise_flag(p.status, 1u);
+                    tok = -1;
+                }
+            }
+            s_tok[t] = tok;
+        }
+        __syncthreads();
+        stage_w1<WT, Ops::RS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
+        __syncthreads();
+        store_tile(sZ, A.mfma(sB, ks, lane), w, lane);
+        __syncthreads();
+        const bool valid = erow < p.nrows && s_tok[er] >= 0;
+
+        const float* zr = sZ + er * ZS + ec;
         float m = -INFINITY, bv = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            z[j] = z[j] + acc[j];
-            m = fmaxf(m, z[j]);
-            if (GREEDY && z[j] > bv) { bv = z[j]; bi = col0 + acc_col(j, h); }
+        for (int q = 0; q < 4; ++q) {
+            const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
+            z[4 * q + 0] = z[4 * q + 0] + bq.x;
+            z[4 * q + 1] = z[4 * q + 1] + bq.y;
+            z[4 * q + 2] = z[4 * q + 2] + bq.z;
+            z[4 * q + 3] = z[4 * q + 3] + bq.w;
         }
-        m = fmaxf(m, shfl_xor(m, 32));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            m = fmaxf(m, z[j]);
+            if (GREEDY && z[j] > bv) { bv = z[j]; bi = cbase + j; }
+        }
+        m = oct_max(m);
         const float ms = safe_ref(m);
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) s += softw(z[j], ms, p.c);
-        s += shfl_xor(s, 32);
-        if (GREEDY) argmax_merge(bv, bi, shfl_xor(bv, 32), shfl_xor(bi, 32));
-        if (h == 0) {
-            sm_m[w][n] = m;
-            sm_s[w][n] = s;
-            sm_i[w][n] = bi;
+        s = oct_sum(s);
+        if (GREEDY) oct_argmax(bv, bi);
+        if ((t & 7) == 0 && valid) {
+            const size_t o = (size_t)erow * p.n_gran + g;
+            p.gstat[o] = make_float2(m, s);
+            if (GREEDY) p.gidx[o] = bi;
         }
-        __syncthreads();
-        if (threadIdx.x < 32 && valid) {
-            float M = sm_m[0][n];
-#pragma unroll
-            for (int i = 1; i < 4; ++i) M = fmaxf(M, sm_m[i][n]);
-            const float Ms = safe_ref(M);
-            float S = 0.0f;
-            int idx = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                S += sm_s[i][n] * softw(sm_m[i][n], Ms, p.c);
-                if (GREEDY && idx == 0x7fffffff && sm_m[i][n] == M) idx = sm_i[i][n];
-            }
-            const size_t o = (size_t)row * p.n_gran + g;
-            p.gstat[o] = make_float2(M, S);
-            if (GREEDY) p.gidx[o] = idx;
-        }
-        __syncthreads();
     }
 }
+
+// ------------------------------------------------------------ pick
 
 struct PickArgs {
     const float* U;
     const void* W1;
-    const void* W2;
+    const void* W2p;
     const int32_t* x0;
     int32_t* x;  // [R, gamma]; position k is written, k-1 is read
     int R, gamma, r, V;
     float c;
-    int vec4;
     int k;       // 1-based position
     int n_gran;
     uint64_t seed, round;
@@ -147,14 +205,40 @@ struct PickArgs {
     float* pd_stats;
 };
 
+// One workgroup of four waves per request.  Everything that does not depend
+// on the drawn granule is loaded first (the previous token, this request's
+// W1 row, its granule partials); every wave then merges the partials and
+// locates the granule (identical results), wave w recomputes column block w
+// of that granule on MFMA with U added, and wave 0 picks the id.
+constexpr int PICK_CACHE = 32;  // granule partials held in registers per lane
+
 template <typename WT, int KS, bool GREEDY>
 __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
 {
     const int q = blockIdx.x;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const int n = lane & 31, h = lane >> 5;
     const size_t o = (size_t)q * p.gamma + (p.k - 1);
+    const int ks = k_steps<WT>(p.r);
+    const int nblk = (p.V + 31) / 32;
+    __shared__ float zrow[GRAN];
+
+    // independent loads first
+    const float2* gs = p.gstat + (size_t)q * p.n_gran;
+    const int per = (p.n_gran + WAVE - 1) / WAVE;
+    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
+    float2 gc[PICK_CACHE];
+#pragma unroll
+    for (int i = 0; i < PICK_CACHE; ++i) gc[i] = (g0 + i < g1) ? gs[g0 + i] : make_float2(-INFINITY, 0.0f);
     const int tok = p.k == 1 ? p.x0[q] : p.x[(size_t)q * p.gamma + p.k - 2];
-    if (tok < 0 || tok >= p.V) {
+    const bool ok = tok >= 0 && tok < p.V;
+    // B operand: only this request's W1 row (column n == q's slot); a matrix
+    // core output element depends only on its own row and column operands
+    const int nq = q & (BLOCK_ROWS - 1);
+    TileOps<WT, KS> A;
+    typename TileOps<WT, KS>::BRow brow;
+    brow.load(reinterpret_cast<const WT*>(p.W1), p.r, (ok && n == nq) ? tok : -1, ks, lane);
+    if (!ok) {
         if (t == 0) {
             p.x[o] = -1;
             p.pd_x[o] = NAN;
@@ -163,28 +247,34 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         }
         return;
     }
-    __shared__ float smf[8];
-    __shared__ int smi[8];
-    __shared__ float zrow[GRAN];
-
-    // merge the granule partials: M = max, w_g = S_g 2^((M_g - M) c)
-    const float2* gs = p.gstat + (size_t)q * p.n_gran;
-    const int per = (p.n_gran + TILE_THREADS - 1) / TILE_THREADS;
-    const int g0 = min(t * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
+    // merge the granule partials: M = max, w_g = S_g 2^((M_g - M) c); the
+    // first PICK_CACHE granules of each lane come from registers
     float m = -INFINITY;
-    for (int g = g0; g < g1; ++g) m = fmaxf(m, gs[g].x);
-    const float M = block_max(m, smf);
+#pragma unroll
+    for (int i = 0; i < PICK_CACHE; ++i) m = fmaxf(m, gc[i].x);
+    for (int g = g0 + PICK_CACHE; g < g1; ++g) m = fmaxf(m, gs[g].x);
+    const float M = wave_max(m);
     const float c = p.c;
-    auto wf = [&](int g) { const float2 v = gs[g]; return v.y * softw(v.x, M, c); };
-    float tsum, excl, S;
-    granule_scan(wf, g0, g1, smf, tsum, excl, S);
+    float wv[PICK_CACHE];
+    float tsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PICK_CACHE; ++i) {
+        wv[i] = gc[i].y * softw(gc[i].x, M, c);  // padding: 0 * 0
+        tsum += wv[i];
+    }
+    for (int g = g0 + PICK_CACHE; g < g1; ++g) tsum += gs[g].y * softw(gs[g].x, M, c);
+    const float incl = wave_incl_scan(tsum);
+    float excl = __shfl_up(incl, 1, WAVE);
+    if (lane == 0) excl = 0.0f;
+    const float S = __shfl(incl, WAVE - 1, WAVE);
 
     if (GREEDY) {
+        if (w != 0) return;
         int cand = 0x7fffffff;
         for (int g = g0; g < g1; ++g)
             if (gs[g].x == M) { cand = p.gidx[(size_t)q * p.n_gran + g]; break; }
-        const int best = block_min(cand, smi);
-        if (t == 0) {
+        const int best = wave_min(cand);
+        if (lane == 0) {
             p.x[o] = best;
             p.pd_x[o] = 1.0f / S;
             p.pd_stats[2 * o] = M;
@@ -195,56 +285,77 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
 
     const float u = u24f(philox((uint32_t)p.k, (uint32_t)q, p.round, p.seed).w[0]);
     const float target = u * S;
-    float before;
-    int gfb;
-    int gstar = granule_find(wf, g0, g1, excl, target, smf, smi, before, gfb);
-    const bool fallback = gstar < 0;
-    if (fallback) gstar = gfb < 0 ? 0 : gfb;
-
-    // Recompute the 128 logits of granule gstar for q's row block with the
-    // same tile code as k_draft_tile (bit-identical z).
-    const int lane = t & (WAVE - 1), w = t / WAVE, h = lane >> 5, n = lane & 31;
-    const int col0 = gstar * GRAN + 32 * w;
-    W2Operand<WT, KS> A;
-    A.load(reinterpret_cast<const WT*>(p.W2), p.r, p.V, col0 + n, h);
-    const int rr = (q / BLOCK_ROWS) * BLOCK_ROWS + n;
-    int tk = -1;
-    if (rr < p.R) {
-        tk = p.k == 1 ? p.x0[rr] : p.x[(size_t)rr * p.gamma + p.k - 2];
-        if (tk < 0 || tk >= p.V) tk = -1;
-    }
-    const f32x16 acc = A.mul(reinterpret_cast<const WT*>(p.W1), p.r, tk, h);
-    if (n == (q & (BLOCK_ROWS - 1))) {
-        float z[16];
-        load_row16(p.U + ((size_t)q * p.gamma + (p.k - 1)) * p.V, col0, h, p.V, p.vec4, z);
+    // first granule of positive mass whose running sum exceeds target
+    float run = excl, prev = excl;
+    int pick = -1, lastpos = -1;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) zrow[32 * w + acc_col(j, h)] = z[j] + acc[j];
+    for (int i = 0; i < PICK_CACHE; ++i) {
+        if (wv[i] > 0.0f) lastpos = g0 + i;
+        if (pick < 0) {
+            prev = run;
+            run += wv[i];
+            if (run > target && wv[i] > 0.0f) pick = g0 + i;
+        }
+    }
+    for (int g = g0 + PICK_CACHE; g < g1; ++g) {
+        const float wg = gs[g].y * softw(gs[g].x, M, c);
+        if (wg > 0.0f) lastpos = g;
+        if (pick < 0) {
+            prev = run;
+            run += wg;
+            if (run > target && wg > 0.0f) pick = g;
+        }
+    }
+    const unsigned long long hit = __ballot(pick >= 0);
+    bool fallback;
+    float before;
+    int gstar;
+    if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        fallback = false;
+        before = __shfl(prev, L, WAVE);
+        gstar = __shfl(pick, L, WAVE);
+    } else {
+        fallback = true;
+        before = 0.0f;
+        const int lp = -wave_min(-lastpos);
+        gstar = lp < 0 ? 0 : lp;
+    }
+
+    // column block w of granule gstar for q's row (same operands as the tile)
+    const int b = 4 * gstar + w;
+    float uv[16];
+    load_acc16(p.U + ((size_t)q * p.gamma + (p.k - 1)) * p.V, gstar * GRAN + 32 * w, h, p.V, (p.V % 4) == 0, uv);
+    A.load_a(p.W2p, ks, b, b < nblk, lane);
+    const f32x16 acc = A.mfma_row(brow, ks);
+    if (n == nq) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] = softw(uv[j] + acc[j], M, c);
     }
     __syncthreads();
-    if (w == 0) {
-        float e;
-        const int col = granule_pick(softw(zrow[2 * lane], M, c), softw(zrow[2 * lane + 1], M, c),
-                                     before, target, fallback, e);
-        if (lane == 0) {
-            p.x[o] = gstar * GRAN + col;
-            p.pd_x[o] = e / S;
-            p.pd_stats[2 * o] = M;
-            p.pd_stats[2 * o + 1] = S;
-        }
+    if (w != 0) return;
+    float e;
+    const int col = granule_pick(zrow[2 * lane], zrow[2 * lane + 1], before, target, fallback, e);
+    if (lane == 0) {
+        p.x[o] = gstar * GRAN + col;
+        p.pd_x[o] = e / S;
+        p.pd_stats[2 * o] = M;
+        p.pd_stats[2 * o + 1] = S;
     }
 }
 
 // ------------------------------------------------------------ launchers
 
-static int rows_per_chunk_blocks(int nrows, int n_gran)
+// Workgroups cover one granule and `bpc` consecutive 32-row blocks; the row
+// blocks are split into just enough chunks to give ~1024 workgroups.
+static void tile_grid(int nrows, int n_gran, int& bpc, int& n_chunks)
 {
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
-    long work = (long)n_rb * n_gran;
-    int bpc = (int)(work / 2048);
-    if (bpc < 1) bpc = 1;
-    if (bpc > 4) bpc = 4;
-    if (bpc > n_rb) bpc = n_rb;
-    return bpc;
+    n_chunks = (1024 + n_gran - 1) / n_gran;
+    if (n_chunks > n_rb) n_chunks = n_rb;
+    if (n_chunks < 1) n_chunks = 1;
+    bpc = (n_rb + n_chunks - 1) / n_chunks;
+    n_chunks = (n_rb + bpc - 1) / bpc;
 }
 
 template <typename WT, int KS>
@@ -252,20 +363,18 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
                                const ProposeWs& ws, hipStream_t s)
 {
     const int n_gran = n_granules(a.V);
-    const int n_rb = (a.R + BLOCK_ROWS - 1) / BLOCK_ROWS;
-    const int bpc = rows_per_chunk_blocks(a.R, n_gran);
-    const int n_chunks = (n_rb + bpc - 1) / bpc;
     TileArgs t{};
-    t.U = a.U; t.W1 = a.W1; t.W2 = a.W2; t.x0 = a.x0; t.x = x_out;
+    t.U = a.U; t.W1 = a.W1; t.W2p = a.W2; t.x0 = a.x0; t.x = x_out;
     t.R = a.R; t.gamma = a.gamma; t.r = a.r; t.V = a.V; t.c = a.c; t.vec4 = (a.V % 4) == 0;
-    t.nrows = a.R; t.n_gran = n_gran; t.n_chunks = n_chunks; t.bpc = bpc;
+    t.nrows = a.R; t.n_gran = n_gran;
+    tile_grid(a.R, n_gran, t.bpc, t.n_chunks);
     t.gstat = ws.gstat; t.gidx = ws.gidx; t.status = a.status;
     PickArgs pk{};
-    pk.U = a.U; pk.W1 = a.W1; pk.W2 = a.W2; pk.x0 = a.x0; pk.x = x_out;
-    pk.R = a.R; pk.gamma = a.gamma; pk.r = a.r; pk.V = a.V; pk.c = a.c; pk.vec4 = t.vec4;
+    pk.U = a.U; pk.W1 = a.W1; pk.W2p = a.W2; pk.x0 = a.x0; pk.x = x_out;
+    pk.R = a.R; pk.gamma = a.gamma; pk.r = a.r; pk.V = a.V; pk.c = a.c;
     pk.n_gran = n_gran; pk.seed = a.seed; pk.round = a.round;
     pk.gstat = ws.gstat; pk.gidx = ws.gidx; pk.pd_x = pd_x; pk.pd_stats = pd_stats;
-    const int grid = xcd_grid(n_gran * n_chunks);
+    const int grid = xcd_grid(n_gran * t.n_chunks);
     for (int k = 1; k <= a.gamma; ++k) {
         t.kfix = k - 1;
         pk.k = k;
@@ -291,8 +400,7 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
     return hipSuccess;
 }
 
-// Per-(row, granule) draft statistics and per-row (M, S) for every (req, kk)
-// row; used by spec_confidence when no propose statistics are supplied.
+// One wave per row: merge granule partials into the row's (M, S).
 __global__ __launch_bounds__(TILE_THREADS) void k_merge_rows(const float2* gstat, int nrows, int n_gran,
                                                              float c, float2* rows)
 {
@@ -310,22 +418,22 @@ __global__ __launch_bounds__(TILE_THREADS) void k_merge_rows(const float2* gstat
     if (lane == 0) rows[row] = make_float2(M, S);
 }
 
+// Draft (M, S) of every (req, kk) row, for spec_confidence without supplied
+// propose statistics.
 template <typename WT, int KS>
 static hipError_t row_stats_impl(const DraftArgs& a, const VerifyWs& ws, hipStream_t s)
 {
     const int n_gran = n_granules(a.V);
     const int nrows = a.R * a.gamma;
-    const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
-    const int bpc = rows_per_chunk_blocks(nrows, n_gran);
-    const int n_chunks = (n_rb + bpc - 1) / bpc;
     TileArgs t{};
-    t.U = a.U; t.W1 = a.W1; t.W2 = a.W2; t.x0 = a.x0; t.x = a.x;
+    t.U = a.U; t.W1 = a.W1; t.W2p = a.W2; t.x0 = a.x0; t.x = a.x;
     t.R = a.R; t.gamma = a.gamma; t.r = a.r; t.V = a.V; t.c = a.c; t.vec4 = (a.V % 4) == 0;
-    t.kfix = -1; t.nrows = nrows; t.n_gran = n_gran; t.n_chunks = n_chunks; t.bpc = bpc;
+    t.kfix = -1; t.nrows = nrows; t.n_gran = n_gran;
+    tile_grid(nrows, n_gran, t.bpc, t.n_chunks);
     t.gstat = ws.dgran; t.gidx = ws.dgidx; t.status = a.status;
     {
         ProfScope ps("draft_tile", s);
-        hipLaunchKernelGGL((k_draft_tile<WT, KS, false>), dim3(xcd_grid(n_gran * n_chunks)),
+        hipLaunchKernelGGL((k_draft_tile<WT, KS, false>), dim3(xcd_grid(n_gran * t.n_chunks)),
                            dim3(TILE_THREADS), 0, s, t);
     }
     hipError_t e = hipGetLastError();
@@ -336,23 +444,6 @@ static hipError_t row_stats_impl(const DraftArgs& a, const VerifyWs& ws, hipStre
                            (const float2*)ws.dgran, nrows, n_gran, a.c, ws.drow);
     }
     return hipGetLastError();
-}
-
-// Dispatch on weight dtype and the padded number of k-steps.
-template <template <typename, int> class F, typename... Args>
-static hipError_t dispatch_ks(int w_dtype, int r, Args&&... args)
-{
-    if (w_dtype == 1) {
-        const int ks = r / 16;
-        if (ks <= 4) return F<bf16w, 4>::run(args...);
-        if (ks <= 8) return F<bf16w, 8>::run(args...);
-        if (ks <= 16) return F<bf16w, 16>::run(args...);
-        return F<bf16w, 32>::run(args...);
-    }
-    const int ks = r / 2;
-    if (ks <= 8) return F<float, 8>::run(args...);
-    if (ks <= 32) return F<float, 32>::run(args...);
-    return F<float, 128>::run(args...);
 }
 
 template <typename WT, int KS>

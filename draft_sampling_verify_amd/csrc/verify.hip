@@ -9,10 +9,10 @@
 // Kernels, in launch order:
 //   k_plan            (only with scheduled lengths) row maps for the ragged
 //                     verified rows: flattened, no padding.
-//   k_target_tile     per (target row, granule): max, sum of 2^((L-max)c),
-//                     argmax -- first streaming pass over the target rows.
-//   k_row_merge       per target row: (M_t, S_t) and argmax.
-//   k_verify_sweep    per (verified row, granule): recompute the Markov bias
+//   k_target_rows     one workgroup per target row: max, sum of 2^((L-max)c)
+//                     and argmax per granule, and the row's (M_t, S_t,
+//                     argmax) -- first streaming pass over the target rows.
+//   k_verify_sweep    per (granule, verified rows): recompute the Markov bias
 //                     on MFMA, p_d and p_t, and the granule's TV mass
 //                     sum |p_t - p_d| and residual mass sum max(0, p_t - p_d)
 //                     -- second pass over the target rows plus U and W2.
@@ -86,83 +86,106 @@ struct TargetArgs {
     int R, gamma, V, P;  // P: target rows per request in the implicit map
     float c;
     int vec4;
-    int n_gran, n_gchunks, max_rows;
+    int n_gran, max_rows;
     const int2* tmap;        // NULL = implicit
     const int32_t* counts;   // counts[1] = rows when tmap != NULL
     float2* tgran;
     int32_t* tgidx;
+    float2* trow;
+    int32_t* targ;
 };
 
-// One workgroup: one target row x 32 granules; each 32-lane half handles one
-// granule per step with float4 loads.
-__global__ __launch_bounds__(TILE_THREADS) void k_target_tile(TargetArgs p)
+// One workgroup (512 threads) per target row streams the whole row, 8192
+// ids per step (next step's loads issued before this step's arithmetic).
+// Each 8-lane group reduces one 128-id granule per step (16 consecutive ids
+// per lane, DPP reductions) and writes its (max, sum of 2^((L-max)c),
+// argmax); a running (max, sum, argmax) per group then folds into the row's
+// (M_t, S_t, argmax) at the end, so no separate merge pass is needed.
+constexpr int TROW_THREADS = 512;
+constexpr int TROW_GRANS = TROW_THREADS / 8;  // granules per step
+
+__global__ __launch_bounds__(TROW_THREADS) void k_target_rows(TargetArgs p)
 {
-    const int row = blockIdx.x / p.n_gchunks, gc = blockIdx.x - row * p.n_gchunks;
+    const int row = blockIdx.x;
     const int nrows = p.tmap ? p.counts[1] : p.max_rows;
     if (row >= nrows) return;
     const int2 ti = trow_info(p.tmap, row, p.P);
     const float* L = p.Lt + ((size_t)ti.x * (p.gamma + 1) + ti.y) * p.V;
-    const int hw = threadIdx.x >> 5, li = threadIdx.x & 31;
+    const int t = threadIdx.x, gi = t >> 3, l8 = t & 7;
+    const int steps = (p.n_gran + TROW_GRANS - 1) / TROW_GRANS;
+    float rm = -INFINITY, rs = 0.0f;
+    int rbi = 0x7fffffff;
+    float cur[16], nxt[16];
+    load16(L, gi * GRAN + 16 * l8, p.V, p.vec4, cur);
+    for (int st = 0; st < steps; ++st) {
+        if (st + 1 < steps) load16(L, ((st + 1) * TROW_GRANS + gi) * GRAN + 16 * l8, p.V, p.vec4, nxt);
+        const int g = st * TROW_GRANS + gi;
+        const int c0 = g * GRAN + 16 * l8;
+        float m = -INFINITY, bv = -INFINITY;
+        int bi = 0x7fffffff;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int g = gc * 32 + it * 8 + hw;
-        if (g >= p.n_gran) break;  // uniform within the half
-        const int c0 = g * GRAN + 4 * li;
-        float v[4];
-        if (p.vec4 && c0 + 3 < p.V) {
-            const float4 t4 = *reinterpret_cast<const float4*>(L + c0);
-            v[0] = t4.x; v[1] = t4.y; v[2] = t4.z; v[3] = t4.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = c0 + e < p.V ? L[c0 + e] : -INFINITY;
+        for (int j = 0; j < 16; ++j) {
+            m = fmaxf(m, cur[j]);
+            if (cur[j] > bv) { bv = cur[j]; bi = c0 + j; }
         }
-        float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-        float bv = v[0];
-        int bi = c0;
-#pragma unroll
-        for (int e = 1; e < 4; ++e)
-            if (v[e] > bv) { bv = v[e]; bi = c0 + e; }
-        m = half_max(m);
+        m = oct_max(m);
         const float ms = safe_ref(m);
-        float s = softw(v[0], ms, p.c) + softw(v[1], ms, p.c) + softw(v[2], ms, p.c) + softw(v[3], ms, p.c);
-        s = half_sum(s);
+        float sm = 0.0f;
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) argmax_merge(bv, bi, shfl_xor(bv, o), shfl_xor(bi, o));
-        if (li == 0) {
-            const size_t o = (size_t)row * p.n_gran + g;
-            p.tgran[o] = make_float2(m, s);
-            p.tgidx[o] = bi;
+        for (int j = 0; j < 16; ++j) sm += softw(cur[j], ms, p.c);
+        sm = oct_sum(sm);
+        oct_argmax(bv, bi);
+        if (g < p.n_gran) {
+            if (l8 == 0) {
+                const size_t o = (size_t)row * p.n_gran + g;
+                p.tgran[o] = make_float2(m, sm);
+                p.tgidx[o] = bi;
+            }
+            // fold into the group's running row statistics (granules ascend)
+            if (m > rm) {
+                rs = rs * softw(rm, m, p.c) + sm;
+                rm = m;
+                rbi = bi;
+            } else {
+                rs += sm * softw(m, safe_ref(rm), p.c);
+            }
+        }
+        if (st + 1 < steps) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
         }
     }
-}
-
-// One wave per row: merge granule partials into (M, S) and the argmax.
-__global__ __launch_bounds__(TILE_THREADS) void k_row_merge(const float2* gran, const int32_t* gidx,
-                                                            int max_rows, const int32_t* count,
-                                                            int n_gran, float c, float2* rows,
-                                                            int32_t* argm)
-{
-    const int row = blockIdx.x * (TILE_THREADS / WAVE) + threadIdx.x / WAVE;
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int nrows = count ? *count : max_rows;
-    if (row >= nrows) return;
-    const float2* gs = gran + (size_t)row * n_gran;
-    float m = -INFINITY;
-    for (int g = lane; g < n_gran; g += WAVE) m = fmaxf(m, gs[g].x);
-    const float M = wave_max(m);
-    const float Ms = safe_ref(M);
-    float s = 0.0f;
-    int best = 0x7fffffff;
-    for (int g = lane; g < n_gran; g += WAVE) {
-        const float2 v = gs[g];
-        s += v.y * softw(v.x, Ms, c);
-        if (best == 0x7fffffff && v.x == M) best = gidx[(size_t)row * n_gran + g];
+    // merge the 64 groups: lanes 0, 8, ..., 56 of each wave, then the waves
+    __shared__ float s_m[TROW_THREADS / WAVE], s_s[TROW_THREADS / WAVE];
+    __shared__ int s_i[TROW_THREADS / WAVE];
+#pragma unroll
+    for (int o = 8; o < WAVE; o <<= 1) {
+        const float m2 = shfl_xor(rm, o), s2 = shfl_xor(rs, o);
+        const int i2 = shfl_xor(rbi, o);
+        const float M = fmaxf(rm, m2), Ms = safe_ref(M);
+        rs = rs * softw(rm, Ms, p.c) + s2 * softw(m2, Ms, p.c);
+        if (m2 > rm || (m2 == rm && i2 < rbi)) rbi = i2;
+        rm = M;
     }
-    const float S = wave_sum(s);
-    best = wave_min(best);
-    if (lane == 0) {
-        rows[row] = make_float2(M, S);
-        if (argm) argm[row] = best;
+    const int w = t / WAVE;
+    if ((t & (WAVE - 1)) == 0) {
+        s_m[w] = rm;
+        s_s[w] = rs;
+        s_i[w] = rbi;
+    }
+    __syncthreads();
+    if (t == 0) {
+        float M = s_m[0];
+        for (int i = 1; i < TROW_THREADS / WAVE; ++i) M = fmaxf(M, s_m[i]);
+        const float Ms = safe_ref(M);
+        float S = 0.0f;
+        int best = 0x7fffffff;
+        for (int i = 0; i < TROW_THREADS / WAVE; ++i) {
+            S += s_s[i] * softw(s_m[i], Ms, p.c);
+            if (s_m[i] == M && s_i[i] < best) best = s_i[i];
+        }
+        p.trow[row] = make_float2(M, S);
+        p.targ[row] = best;
     }
 }
 
@@ -171,7 +194,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_row_merge(const float2* gran, 
 struct SweepArgs {
     const float* U;
     const void* W1;
-    const void* W2;
+    const void* W2p;
     const int32_t* x0;
     const int32_t* x;
     const float* dstats;  // [R*gamma, 2] draft (M, S) (propose output layout)
@@ -183,101 +206,114 @@ struct SweepArgs {
     const int4* vmap;
     const int32_t* counts;
     const float2* trow;
-    float2* vpart;
+    float2* vpart;        // [rows, n_gran] (TV mass, residual mass)
+    float* vbias;         // [rows] Markov bias at the drafted id x_k
 };
 
-// Per-element weights of one verified row at the 16 ids a lane holds:
-// p_d from the draft logits z_d = U + bias, p_t from the target logits.
+// Verified row f: where its data lives and the normalisers of p_d and p_t.
 struct RowCtx {
-    bool valid;
-    int req, k, trow, tok;
+    int req, k, trow, xk;  // req = -1: no such row
     float Md, iSd, Mt, iSt;
 };
 
-__device__ inline RowCtx sweep_row(const SweepArgs& p, int f, int nrows)
+__device__ inline RowCtx row_ctx(const SweepArgs& p, int f, int nrows)
 {
     RowCtx rc{};
-    rc.valid = f < nrows;
-    rc.tok = -1;
-    if (!rc.valid) return rc;
+    rc.req = -1;
+    if (f >= nrows) return rc;
     const int4 vi = vrow_info(p.vmap, f, p.gamma, p.P);
-    rc.req = vi.x; rc.k = vi.y; rc.trow = vi.z;
-    rc.tok = rc.k == 1 ? p.x0[rc.req] : p.x[(size_t)rc.req * p.gamma + rc.k - 2];
-    const int xk = p.x[(size_t)rc.req * p.gamma + rc.k - 1];
-    if (rc.tok < 0 || rc.tok >= p.V || xk < 0 || xk >= p.V) {
-        rc.valid = false;
-        rc.tok = -1;
-        return rc;
-    }
-    const size_t so = (size_t)rc.req * p.gamma + rc.k - 1;
+    rc.req = vi.x;
+    rc.k = vi.y;
+    rc.trow = vi.z;
+    rc.xk = p.x[(size_t)vi.x * p.gamma + vi.y - 1];
+    const size_t so = (size_t)vi.x * p.gamma + vi.y - 1;
     rc.Md = p.dstats[2 * so];
     rc.iSd = 1.0f / p.dstats[2 * so + 1];
-    const float2 ts = p.trow[rc.trow];
+    const float2 ts = p.trow[vi.z];
     rc.Mt = ts.x;
     rc.iSt = 1.0f / ts.y;
     return rc;
 }
 
-// p_d and p_t at the 16 ids (col0 + acc_col(j, h)) for a valid row.
-__device__ inline void sweep_probs(const SweepArgs& p, const RowCtx& rc, const f32x16& acc, int col0,
-                                   int h, float (&pd)[16], float (&pt)[16])
+// Token whose W1 row biases verified row f (x_{k-1}), or -1 when the row does
+// not exist or its tokens are out of range.
+__device__ inline int row_tok(const SweepArgs& p, int f, int nrows)
 {
-    float zd[16], zt[16];
-    load_row16(p.U + ((size_t)rc.req * p.gamma + rc.k - 1) * p.V, col0, h, p.V, p.vec4, zd);
-    load_row16(p.Lt + ((size_t)rc.req * (p.gamma + 1) + rc.k - 1) * p.V, col0, h, p.V, p.vec4, zt);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        pd[j] = softw(zd[j] + acc[j], rc.Md, p.c) * rc.iSd;
-        pt[j] = softw(zt[j], rc.Mt, p.c) * rc.iSt;
-    }
+    if (f >= nrows) return -1;
+    const int4 vi = vrow_info(p.vmap, f, p.gamma, p.P);
+    const int tok = vi.y == 1 ? p.x0[vi.x] : p.x[(size_t)vi.x * p.gamma + vi.y - 2];
+    const int xk = p.x[(size_t)vi.x * p.gamma + vi.y - 1];
+    return (tok < 0 || tok >= p.V || xk < 0 || xk >= p.V) ? -1 : tok;
+}
+
+// Residual weight max(0, p_t - p_d) of one id; the sweep and the resolve's
+// rescan both use this expression.
+__device__ inline float resid(float zu, float bias, float zt, const RowCtx& rc, float c, float& d)
+{
+    const float pd = softw(zu + bias, rc.Md, c) * rc.iSd;
+    const float pt = softw(zt, rc.Mt, c) * rc.iSt;
+    d = pt - pd;
+    return fmaxf(d, 0.0f);
 }
 
 template <typename WT, int KS>
-__global__ __launch_bounds__(TILE_THREADS) void k_verify_sweep(SweepArgs p)
+__global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
 {
+    using Ops = TileOps<WT, KS>;
     const int nlog = p.n_gran * p.n_chunks;
     const int lid = xcd_logical(blockIdx.x, nlog);
     if (lid >= nlog) return;
     const int g = lid / p.n_chunks, chunk = lid - g * p.n_chunks;
     const int nrows = p.vmap ? p.counts[0] : p.max_rows;
-    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-    const int h = lane >> 5, n = lane & 31;
-    const int col0 = g * GRAN + 32 * w;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const int ks = k_steps<WT>(p.r);
+    const int nblk = (p.V + 31) / 32;
 
-    W2Operand<WT, KS> A;
-    A.load(reinterpret_cast<const WT*>(p.W2), p.r, p.V, col0 + n, h);
-    __shared__ float sm_tv[4][32], sm_res[4][32];
+    Ops A;
+    A.load_a(p.W2p, ks, 4 * g + w, 4 * g + w < nblk, lane);
 
+    __shared__ __align__(16) char sB[32 * Ops::RS * Ops::ELEM];
+    __shared__ __align__(16) float sZ[32 * ZS];
+    __shared__ int s_tok[32];
+
+    const int er = t >> 3, ec = (t & 7) * 16;
+    const int cbase = g * GRAN + ec;
     for (int b = 0; b < p.bpc; ++b) {
         const int rb = chunk * p.bpc + b;
         if (rb * BLOCK_ROWS >= nrows) break;
-        const int f = rb * BLOCK_ROWS + n;
-        const RowCtx rc = sweep_row(p, f, nrows);
-        const f32x16 acc = A.mul(reinterpret_cast<const WT*>(p.W1), p.r, rc.tok, h);
-        float tv = 0.0f, res = 0.0f;
-        if (rc.valid) {
-            float pd[16], pt[16];
-            sweep_probs(p, rc, acc, col0, h, pd, pt);
+        // the epilogue row's data do not depend on the tokens: issue them first
+        const int f = rb * BLOCK_ROWS + er;
+        const RowCtx rc = row_ctx(p, f, nrows);
+        float zu[16], zt[16];
+        if (rc.req >= 0) {
+            load16(p.U + ((size_t)rc.req * p.gamma + rc.k - 1) * p.V, cbase, p.V, p.vec4, zu);
+            load16(p.Lt + ((size_t)rc.req * (p.gamma + 1) + rc.k - 1) * p.V, cbase, p.V, p.vec4, zt);
+        }
+        if (t < 32) s_tok[t] = row_tok(p, rb * BLOCK_ROWS + t, nrows);
+        __syncthreads();
+        stage_w1<WT, Ops::RS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
+        __syncthreads();
+        store_tile(sZ, A.mfma(sB, ks, lane), w, lane);
+        __syncthreads();
+        if (rc.req >= 0 && s_tok[er] >= 0) {
+            const float* zr = sZ + er * ZS + ec;
+            float tv = 0.0f, res = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float d = pt[j] - pd[j];
-                tv += fabsf(d);
-                res += fmaxf(d, 0.0f);
+            for (int q = 0; q < 4; ++q) {
+                const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
+                const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float d;
+                    res += resid(zu[4 * q + e], bb[e], zt[4 * q + e], rc, p.c, d);
+                    tv += fabsf(d);
+                }
             }
+            tv = oct_sum(tv);
+            res = oct_sum(res);
+            if ((t & 7) == 0) p.vpart[(size_t)f * p.n_gran + g] = make_float2(tv, res);
+            if (rc.xk >= cbase && rc.xk < cbase + 16) p.vbias[f] = zr[rc.xk - cbase];
         }
-        tv += shfl_xor(tv, 32);
-        res += shfl_xor(res, 32);
-        if (h == 0) {
-            sm_tv[w][n] = tv;
-            sm_res[w][n] = res;
-        }
-        __syncthreads();
-        if (threadIdx.x < 32 && rc.valid) {
-            const float T4 = ((sm_tv[0][n] + sm_tv[1][n]) + sm_tv[2][n]) + sm_tv[3][n];
-            const float R4 = ((sm_res[0][n] + sm_res[1][n]) + sm_res[2][n]) + sm_res[3][n];
-            p.vpart[(size_t)f * p.n_gran + g] = make_float2(T4, R4);
-        }
-        __syncthreads();
     }
 }
 
@@ -298,50 +334,38 @@ struct ResolveArgs {
     uint32_t* status;
 };
 
-__device__ inline double weight_d(const float* W, size_t i) { return (double)W[i]; }
-__device__ inline double weight_d(const bf16w* W, size_t i)
-{
-    return (double)__uint_as_float((uint32_t)W[i].bits << 16);
-}
-
 // Draw from target row `trow` (data row (req, kk) of Lt) by inverse CDF with
 // uniform u: granule masses from the first pass, then one granule rescan.
-__device__ inline int draw_target_row(const ResolveArgs& a, int trow, int req, int kk, float u,
-                                      float* smf, int* smi)
+// One wave.
+__device__ inline int draw_target_row(const ResolveArgs& a, int trow, int req, int kk, float u)
 {
     const SweepArgs& p = a.s;
+    const int lane = threadIdx.x & (WAVE - 1);
     const float2* gs = a.tgran + (size_t)trow * p.n_gran;
-    const int t = threadIdx.x;
-    const int per = (p.n_gran + TILE_THREADS - 1) / TILE_THREADS;
-    const int g0 = min(t * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
-    float m = -INFINITY;
-    for (int g = g0; g < g1; ++g) m = fmaxf(m, gs[g].x);
-    const float M = block_max(m, smf);
+    const float M = p.trow[trow].x;
     const float c = p.c;
+    const int per = (p.n_gran + WAVE - 1) / WAVE;
+    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
     auto wf = [&](int g) { const float2 v = gs[g]; return v.y * softw(v.x, M, c); };
-    float tsum, excl, S;
-    granule_scan(wf, g0, g1, smf, tsum, excl, S);
+    float excl, S;
+    wave_granule_scan(wf, g0, g1, excl, S);
     const float target = u * S;
     float before;
-    int gfb;
-    int gstar = granule_find(wf, g0, g1, excl, target, smf, smi, before, gfb);
-    const bool fallback = gstar < 0;
-    if (fallback) gstar = gfb < 0 ? 0 : gfb;
-    int pick = 0;
-    if (t < WAVE) {
-        const float* L = p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V;
-        const int ca = gstar * GRAN + 2 * t, cb = ca + 1;
-        const float za = ca < p.V ? L[ca] : -INFINITY, zb = cb < p.V ? L[cb] : -INFINITY;
-        float e;
-        pick = gstar * GRAN + granule_pick(softw(za, M, c), softw(zb, M, c), before, target, fallback, e);
-        if (t == 0) smi[5] = pick;
-    }
-    __syncthreads();
-    pick = smi[5];
-    __syncthreads();
-    return pick;
+    bool fallback;
+    const int gstar = wave_granule_find(wf, g0, g1, excl, target, before, fallback);
+    const float* L = p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V;
+    const int ca = gstar * GRAN + 2 * lane, cb = ca + 1;
+    const float za = ca < p.V ? L[ca] : -INFINITY, zb = cb < p.V ? L[cb] : -INFINITY;
+    float e;
+    return gstar * GRAN + granule_pick(softw(za, M, c), softw(zb, M, c), before, target, fallback, e);
 }
 
+// One workgroup of four waves per request.
+// Phase 1 does everything that does not depend on which position is rejected
+// first, in parallel: the accept test of every verified position (one thread
+// each, fp64 on the drafted id), c* of every position and the residual
+// granule search of every position (one wave each), and the bonus draw.
+// Phase 2 rescans one granule of the first rejected position's residual.
 template <typename WT, int KS, bool GREEDY>
 __global__ __launch_bounds__(TILE_THREADS) void k_verify_resolve(ResolveArgs a)
 {
@@ -349,22 +373,95 @@ __global__ __launch_bounds__(TILE_THREADS) void k_verify_resolve(ResolveArgs a)
     const int r = blockIdx.x, t = threadIdx.x;
     const int lane = t & (WAVE - 1), w = t / WAVE;
     const int G = p.gamma;
-    __shared__ float smf[8];
-    __shared__ int smi[8];
-    __shared__ float rowbuf[GRAN];
+    __shared__ int s_acc[64];
+    __shared__ int s_g[65];        // granule of the residual draw at k (index k-1)
+    __shared__ float s_before[65];
+    __shared__ int s_fb[65];
+    __shared__ float s_Z[65];
+    __shared__ int s_bonus;
+    __shared__ int s_y;
+    __shared__ float zrow[GRAN];
 
     const int Lr = a.ell ? a.ell[r] : G;
     const bool bad_len = Lr < 0 || Lr > G;
-    bool bad_tok = false;
-    if (!bad_len) {
-        if (t == 0) bad_tok = p.x0[r] < 0 || p.x0[r] >= p.V;
-        if (t < Lr) {
-            const int xv = p.x[(size_t)r * G + t];
-            bad_tok = bad_tok || xv < 0 || xv >= p.V;
+    const int L = bad_len ? 0 : Lr;
+    const int voff = a.voff ? a.voff[r] : r * G;
+    const int toff = a.toff ? a.toff[r] : r * p.P;
+    const int x0r = p.x0[r];
+    bool bad = bad_len || x0r < 0 || x0r >= p.V;
+
+    // ---- phase 1a: accept tests, one thread per verified position
+    if (t < L) {
+        const int xk = p.x[(size_t)r * G + t];
+        if (xk < 0 || xk >= p.V) {
+            bad = true;
+        } else {
+            const int tr = toff + t;
+            const float2 ts = p.trow[tr];
+            const double zt = (double)p.Lt[((size_t)r * (G + 1) + t) * p.V + xk];
+            const double pt = exp2((zt - (double)ts.x) * (double)p.c) / (double)ts.y;
+            int acc;
+            if (GREEDY) {
+                acc = xk == a.targ[tr];
+            } else {
+                // p_d(x) from U, the bias the sweep recorded at x and propose's (M, S)
+                const size_t so = (size_t)r * G + t;
+                const double zd = (double)p.U[so * p.V + xk] + (double)p.vbias[voff + t];
+                const double pd = exp2((zd - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
+                double ratio;
+                if (pd > 0.0) ratio = pt / pd;
+                else ratio = pt > 0.0 ? INFINITY : 0.0;
+                const double u1 = u24d(philox((uint32_t)(t + 1), (uint32_t)r, a.round, a.seed).w[1]);
+                acc = u1 < ratio;
+            }
+            s_acc[t] = acc;
+            if (a.pt_x) a.pt_x[(size_t)r * G + t] = (float)pt;
+        }
+    } else if (t < G) {
+        if (a.pt_x) a.pt_x[(size_t)r * G + t] = NAN;
+        if (a.c_star) a.c_star[(size_t)r * G + t] = NAN;
+    }
+    // ---- phase 1b: per position, one wave: c* and the residual granule search
+    const int per = (p.n_gran + WAVE - 1) / WAVE;
+    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
+    for (int k = w + 1; k <= L; k += TILE_THREADS / WAVE) {
+        const float2* vp = p.vpart + (size_t)(voff + k - 1) * p.n_gran;
+        if (a.c_star) {
+            float sm = 0.0f;
+            for (int g = g0; g < g1; ++g) sm += vp[g].x;
+            sm = wave_sum(sm);
+            if (lane == 0) a.c_star[(size_t)r * G + k - 1] = fminf(fmaxf(1.0f - 0.5f * sm, 0.0f), 1.0f);
+        }
+        if (!GREEDY) {
+            auto wf = [&](int g) { return vp[g].y; };
+            float excl, Z;
+            wave_granule_scan(wf, g0, g1, excl, Z);
+            const float u2 = u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[2]);
+            float before = 0.0f;
+            bool fallback = true;
+            int gs = 0;
+            if (Z > 0.0f) gs = wave_granule_find(wf, g0, g1, excl, u2 * Z, before, fallback);
+            if (lane == 0) {
+                s_g[k - 1] = gs;
+                s_before[k - 1] = before;
+                s_fb[k - 1] = fallback;
+                s_Z[k - 1] = Z;
+            }
         }
     }
-    bad_tok = __syncthreads_or(bad_tok);
-    if (bad_len || bad_tok) {
+    // ---- phase 1c: the bonus draw after a full accept (wave L % 4)
+    if (w == L % (TILE_THREADS / WAVE)) {
+        int yb;
+        if (GREEDY) {
+            yb = a.targ[toff + L];
+        } else {
+            const float u2 = u24f(philox((uint32_t)(L + 1), (uint32_t)r, a.round, a.seed).w[2]);
+            yb = draw_target_row(a, toff + L, r, L, u2);
+        }
+        if (lane == 0) s_bonus = yb;
+    }
+    bad = __syncthreads_or(bad);
+    if (bad) {
         if (t == 0) raise_flag(a.status, bad_len ? 2u : 1u);
         if (t == 0) a.n_acc[r] = -1;
         if (t <= G) a.y[(size_t)r * (G + 1) + t] = -1;
@@ -374,123 +471,68 @@ __global__ __launch_bounds__(TILE_THREADS) void k_verify_resolve(ResolveArgs a)
         }
         return;
     }
-    const int voff = a.voff ? a.voff[r] : r * G;
-    const int toff = a.toff ? a.toff[r] : r * p.P;
+    int kstar = 0;
+    for (int k = 1; k <= L; ++k)
+        if (!s_acc[k - 1]) { kstar = k; break; }
+    const int nacc = kstar ? kstar - 1 : L;
 
-    // ---- accept tests, one thread per verified position (fp64 on one id)
-    bool acc_k = true;
-    if (t < Lr) {
-        const int xk = p.x[(size_t)r * G + t];
-        const int tr = toff + t;
-        const float2 ts = p.trow[tr];
-        const double zt = (double)p.Lt[((size_t)r * (G + 1) + t) * p.V + xk];
-        const double pt = exp2((zt - (double)ts.x) * (double)p.c) / (double)ts.y;
-        if (a.pt_x) a.pt_x[(size_t)r * G + t] = (float)pt;
-        if (GREEDY) {
-            acc_k = xk == a.targ[tr];
-        } else {
-            const int xp = t == 0 ? p.x0[r] : p.x[(size_t)r * G + t - 1];
-            const WT* W1 = reinterpret_cast<const WT*>(p.W1);
-            const WT* W2 = reinterpret_cast<const WT*>(p.W2);
-            double b = 0.0;
-            for (int i = 0; i < p.r; ++i)
-                b += weight_d(W1, (size_t)xp * p.r + i) * weight_d(W2, (size_t)xk * p.r + i);
-            const size_t so = (size_t)r * G + t;
-            const double zd = (double)p.U[so * p.V + xk] + b;
-            const double pd = exp2((zd - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
-            double ratio;
-            if (pd > 0.0) ratio = pt / pd;
-            else ratio = pt > 0.0 ? INFINITY : 0.0;
-            const double u1 = u24d(philox((uint32_t)(t + 1), (uint32_t)r, a.round, a.seed).w[1]);
-            acc_k = u1 < ratio;
-        }
-    } else if (t < G) {
-        if (a.pt_x) a.pt_x[(size_t)r * G + t] = NAN;
-    }
-    const int kstar = block_min((t < Lr && !acc_k) ? t + 1 : 0x7fffffff, smi);
-    const int nacc = kstar == 0x7fffffff ? Lr : kstar - 1;
-
-    // ---- c* for every verified position: 1 - 1/2 sum over granules of TV mass
-    if (a.c_star) {
-        for (int k = w + 1; k <= Lr; k += TILE_THREADS / WAVE) {
-            const float2* vp = p.vpart + (size_t)(voff + k - 1) * p.n_gran;
-            float s = 0.0f;
-            for (int g = lane; g < p.n_gran; g += WAVE) s += vp[g].x;
-            s = wave_sum(s);
-            if (lane == 0) {
-                float cs = 1.0f - 0.5f * s;
-                cs = fminf(fmaxf(cs, 0.0f), 1.0f);
-                a.c_star[(size_t)r * G + k - 1] = cs;
-            }
-        }
-        if (t >= Lr && t < G) a.c_star[(size_t)r * G + t] = NAN;
-    }
-
-    // ---- emitted token
-    int ytok;
-    if (kstar != 0x7fffffff) {
-        const int tr = toff + kstar - 1;
-        if (GREEDY) {
-            ytok = a.targ[tr];
-        } else {
-            const float u2 = u24f(philox((uint32_t)kstar, (uint32_t)r, a.round, a.seed).w[2]);
-            const int f = voff + kstar - 1;
-            const float2* vp = p.vpart + (size_t)f * p.n_gran;
-            const int per = (p.n_gran + TILE_THREADS - 1) / TILE_THREADS;
-            const int g0 = min(t * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
-            auto wf = [&](int g) { return vp[g].y; };
-            float tsum, excl, Z;
-            granule_scan(wf, g0, g1, smf, tsum, excl, Z);
-            if (Z > 0.0f) {
-                const float target = u2 * Z;
-                float before;
-                int gfb;
-                int gstar = granule_find(wf, g0, g1, excl, target, smf, smi, before, gfb);
-                const bool fallback = gstar < 0;
-                if (fallback) gstar = gfb < 0 ? 0 : gfb;
-                // recompute the residual weights of row f in granule gstar with
-                // the sweep's tile code
-                const int h = lane >> 5, n = lane & 31;
-                const int col0 = gstar * GRAN + 32 * w;
-                W2Operand<WT, KS> A;
-                A.load(reinterpret_cast<const WT*>(p.W2), p.r, p.V, col0 + n, h);
-                const int nrows = p.vmap ? p.counts[0] : p.max_rows;
-                const int fr = (f / BLOCK_ROWS) * BLOCK_ROWS + n;
-                const RowCtx rc = sweep_row(p, fr, nrows);
-                const f32x16 acc = A.mul(reinterpret_cast<const WT*>(p.W1), p.r, rc.tok, h);
-                if (fr == f) {
-                    float pd[16], pt[16];
-                    sweep_probs(p, rc, acc, col0, h, pd, pt);
+    // ---- phase 2: the emitted token
+    if (!kstar) {
+        if (t == 0) s_y = s_bonus;
+    } else if (GREEDY) {
+        if (t == 0) s_y = a.targ[toff + kstar - 1];
+    } else if (s_Z[kstar - 1] > 0.0f) {
+        // wave w recomputes column block w of granule gstar for row f: the
+        // W2 block, the W1 row of x_{k*-1}, U and the target row
+        const int f = voff + kstar - 1;
+        const int gstar = s_g[kstar - 1];
+        const int nrows = p.vmap ? p.counts[0] : p.max_rows;
+        const int n = lane & 31, h = lane >> 5;
+        const int nf = f & (BLOCK_ROWS - 1);
+        const int ks = k_steps<WT>(p.r);
+        const int b = 4 * gstar + w;
+        const int c0 = gstar * GRAN + 32 * w;
+        const bool v4 = (p.V % 4) == 0;
+        const int xp = kstar == 1 ? x0r : p.x[(size_t)r * G + kstar - 2];
+        typename TileOps<WT, KS>::BRow brow;
+        brow.load(reinterpret_cast<const WT*>(p.W1), p.r, n == nf ? xp : -1, ks, lane);
+        float uu[16], ll[16];
+        load_acc16(p.U + ((size_t)r * G + kstar - 1) * p.V, c0, h, p.V, v4, uu);
+        load_acc16(p.Lt + ((size_t)r * (G + 1) + kstar - 1) * p.V, c0, h, p.V, v4, ll);
+        const RowCtx rc = row_ctx(p, f, nrows);
+        TileOps<WT, KS> A;
+        A.load_a(p.W2p, ks, b, b < (p.V + 31) / 32, lane);
+        const f32x16 acc = A.mfma_row(brow, ks);
+        if (n == nf) {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) rowbuf[32 * w + acc_col(j, h)] = fmaxf(pt[j] - pd[j], 0.0f);
-                }
-                __syncthreads();
-                if (w == 0) {
-                    float e;
-                    const int col = granule_pick(rowbuf[2 * lane], rowbuf[2 * lane + 1], before, target,
-                                                 fallback, e);
-                    if (lane == 0) smi[6] = gstar * GRAN + col;
-                }
-                __syncthreads();
-                ytok = smi[6];
-            } else {
-                ytok = draw_target_row(a, tr, r, kstar - 1, u2, smf, smi);
+            for (int j = 0; j < 16; ++j) {
+                const int col = c0 + 8 * (j >> 2) + 4 * h + (j & 3);
+                float d;
+                zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] =
+                    col < p.V ? resid(uu[j], acc[j], ll[j], rc, p.c, d) : 0.0f;
             }
         }
-    } else {
-        const int tr = toff + Lr;
-        if (GREEDY) {
-            ytok = a.targ[tr];
-        } else {
-            const float u2 = u24f(philox((uint32_t)(Lr + 1), (uint32_t)r, a.round, a.seed).w[2]);
-            ytok = draw_target_row(a, tr, r, Lr, u2, smf, smi);
+        __syncthreads();
+        if (w == 0) {
+            float e;
+            const int y = gstar * GRAN + granule_pick(zrow[2 * lane], zrow[2 * lane + 1], s_before[kstar - 1],
+                                                      s_Z[kstar - 1] * u24f(philox((uint32_t)kstar, (uint32_t)r,
+                                                                                   a.round, a.seed).w[2]),
+                                                      s_fb[kstar - 1], e);
+            if (lane == 0) s_y = y;
         }
+    } else if (w == 0) {
+        // no residual mass (p_t == p_d in fp32): draw from p_t itself
+        const float u2 = u24f(philox((uint32_t)kstar, (uint32_t)r, a.round, a.seed).w[2]);
+        const int y = draw_target_row(a, toff + kstar - 1, r, kstar - 1, u2);
+        if (lane == 0) s_y = y;
     }
+    __syncthreads();
     if (t == 0) a.n_acc[r] = nacc;
     if (t <= G) {
         int v = -1;
         if (t < nacc) v = p.x[(size_t)r * G + t];
-        else if (t == nacc) v = ytok;
+        else if (t == nacc) v = s_y;
         a.y[(size_t)r * (G + 1) + t] = v;
     }
 }
@@ -534,32 +576,30 @@ __global__ __launch_bounds__(TILE_THREADS) void k_conf_finalize(const float2* vp
 
 // ------------------------------------------------------------ launchers
 
-static int chunk_blocks(int nrows, int n_gran)
+static void sweep_grid(int nrows, int n_gran, int& bpc, int& n_chunks)
 {
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
-    long work = (long)n_rb * n_gran;
-    int bpc = (int)(work / 2048);
-    if (bpc < 1) bpc = 1;
-    if (bpc > 4) bpc = 4;
-    if (bpc > n_rb) bpc = n_rb;
-    return bpc;
+    n_chunks = (1024 + n_gran - 1) / n_gran;
+    if (n_chunks > n_rb) n_chunks = n_rb;
+    if (n_chunks < 1) n_chunks = 1;
+    bpc = (n_rb + n_chunks - 1) / n_chunks;
+    n_chunks = (n_rb + bpc - 1) / bpc;
 }
 
 static SweepArgs make_sweep(const DraftArgs& a, const float* dstats, const float* Lt, int P,
                             const VerifyWs& w, const int32_t* counts, bool maps)
 {
     SweepArgs s{};
-    s.U = a.U; s.W1 = a.W1; s.W2 = a.W2; s.x0 = a.x0; s.x = a.x; s.dstats = dstats; s.Lt = Lt;
+    s.U = a.U; s.W1 = a.W1; s.W2p = a.W2; s.x0 = a.x0; s.x = a.x; s.dstats = dstats; s.Lt = Lt;
     s.R = a.R; s.gamma = a.gamma; s.r = a.r; s.V = a.V; s.P = P; s.c = a.c; s.vec4 = (a.V % 4) == 0;
     s.n_gran = n_granules(a.V);
     s.max_rows = a.R * a.gamma;
-    s.bpc = chunk_blocks(s.max_rows, s.n_gran);
-    const int n_rb = (s.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS;
-    s.n_chunks = (n_rb + s.bpc - 1) / s.bpc;
+    sweep_grid(s.max_rows, s.n_gran, s.bpc, s.n_chunks);
     s.vmap = maps ? w.vmap : nullptr;
     s.counts = counts;
     s.trow = w.trow;
     s.vpart = w.vpart;
+    s.vbias = w.vbias;
     return s;
 }
 
@@ -569,22 +609,13 @@ static hipError_t target_pass(const DraftArgs& a, const float* Lt, int P, int ma
     TargetArgs t{};
     t.Lt = Lt; t.R = a.R; t.gamma = a.gamma; t.V = a.V; t.P = P; t.c = a.c; t.vec4 = (a.V % 4) == 0;
     t.n_gran = n_granules(a.V);
-    t.n_gchunks = (t.n_gran + 31) / 32;
     t.max_rows = max_rows;
     t.tmap = maps ? w.tmap : nullptr;
     t.counts = counts;
-    t.tgran = w.tgran; t.tgidx = w.tgidx;
+    t.tgran = w.tgran; t.tgidx = w.tgidx; t.trow = w.trow; t.targ = w.targ;
     {
-        ProfScope ps("target_tile", s);
-        hipLaunchKernelGGL(k_target_tile, dim3(max_rows * t.n_gchunks), dim3(TILE_THREADS), 0, s, t);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    {
-        ProfScope ps("row_merge", s);
-        hipLaunchKernelGGL(k_row_merge, dim3((max_rows + 3) / 4), dim3(TILE_THREADS), 0, s,
-                           (const float2*)w.tgran, (const int32_t*)w.tgidx, max_rows,
-                           maps ? counts + 1 : (const int32_t*)nullptr, t.n_gran, a.c, w.trow, w.targ);
+        ProfScope ps("target_rows", s);
+        hipLaunchKernelGGL(k_target_rows, dim3(max_rows), dim3(TROW_THREADS), 0, s, t);
     }
     return hipGetLastError();
 }
@@ -682,33 +713,17 @@ struct ConfF {
     }
 };
 
-template <template <typename, int> class F, typename... Args>
-static hipError_t dispatch_ks_v(int w_dtype, int r, Args&&... args)
-{
-    if (w_dtype == 1) {
-        const int ks = r / 16;
-        if (ks <= 4) return F<bf16w, 4>::run(args...);
-        if (ks <= 8) return F<bf16w, 8>::run(args...);
-        if (ks <= 16) return F<bf16w, 16>::run(args...);
-        return F<bf16w, 32>::run(args...);
-    }
-    const int ks = r / 2;
-    if (ks <= 8) return F<float, 8>::run(args...);
-    if (ks <= 32) return F<float, 32>::run(args...);
-    return F<float, 128>::run(args...);
-}
-
 hipError_t launch_verify(const DraftArgs& a, const float* pd_stats, const float* Lt, const int32_t* ell,
                          int32_t* n_acc, int32_t* y, float* pt_x, float* c_star, const VerifyWs& w,
                          int32_t* counts, hipStream_t s)
 {
-    return dispatch_ks_v<VerifyF>(a.w_dtype, a.r, a, pd_stats, Lt, ell, n_acc, y, pt_x, c_star, w, counts, s);
+    return dispatch_ks<VerifyF>(a.w_dtype, a.r, a, pd_stats, Lt, ell, n_acc, y, pt_x, c_star, w, counts, s);
 }
 
 hipError_t launch_confidence(const DraftArgs& a, const float* pd_stats, const float* Lt, float* c_star,
                              double* a_star, const VerifyWs& w, hipStream_t s)
 {
-    return dispatch_ks_v<ConfF>(a.w_dtype, a.r, a, pd_stats, Lt, c_star, a_star, w, s);
+    return dispatch_ks<ConfF>(a.w_dtype, a.r, a, pd_stats, Lt, c_star, a_star, w, s);
 }
 
 }  // namespace spec

@@ -29,9 +29,11 @@
  *               v of the bias-free projection r -> V, so
  *               B_k[v] = sum_i W1[x_{k-1}, i] * W2[v, i]  (the transpose of the
  *               r x V matrix in the page's formula, i.e. the usual storage of
- *               a linear layer's weight).  Target row k-1 of a request checks
- *               draft x_k; target row l_r gives the bonus token.
- *   Alignment   U, Lt, W1, W2 must be 16-byte aligned; r % 16 == 0.
+ *               a linear layer's weight).  The hot-path calls take W2 after
+ *               spec_pack_w2 has rearranged it once (W2p): the same values in
+ *               the order the kernels stream them.  Target row k-1 of a
+ *               request checks draft x_k; target row l_r gives the bonus token.
+ *   Alignment   U, Lt, W1, W2, W2p must be 16-byte aligned; r % 16 == 0.
  *   Asynchrony  Calls only validate on the host and enqueue kernels on
  *               `stream` (a hipStream_t; NULL = the null stream).  Outputs are
  *               valid once the caller synchronises that stream.
@@ -94,8 +96,21 @@ enum spec_device_flag {
  * Returns 0 for sizes the entry point would reject. */
 size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max);
 
-/* Zero the status word of a freshly allocated workspace (enqueued on stream). */
+/* Zero the status word of a freshly allocated workspace (enqueued on
+ * stream).  Call once after allocating a workspace. */
 int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Bytes of the packed W2 for these sizes (0 if rejected). */
+size_t spec_packed_w2_bytes(int w_dtype, int r, int V);
+
+/* Rearrange W2 [V,r] (w_dtype) into W2p, the layout the kernels stream: the
+ * vocabulary is cut into blocks of 32 ids; within a block, for each step of
+ * the rank dimension (16 for bf16, 8 for fp32), the 64 lanes' matrix-core
+ * operands are contiguous (lane n + 32h holds row 32b + n, rank slice h of
+ * the step), so every load is one coalesced 1 KB chunk.  Ids past V are
+ * zero.  Run once per weight (e.g. at model load); W2p is caller-owned,
+ * spec_packed_w2_bytes() long.  Enqueued on stream. */
+int spec_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, spec_stream_t stream);
 
 /* Synchronise `stream`, then return the status word of `ws` in *flags (host
  * pointer; SPEC_DEV_* bits, sticky across calls).  clear != 0 zeroes it.
@@ -106,13 +121,14 @@ int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags);
  *   x_0 = x0[r];  for k = 1..gamma:
  *     z_k = U[r,k-1,:] + W1[x_{k-1}] W2^T        (raw draft logits)
  *     p_k = softmax(z_k / T);  x_k ~ p_k (word 0), or argmax z_k if greedy
- * In:  U [R,gamma,V] fp32; W1, W2 [V,r] (w_dtype); x0 [R] int32.
+ * In:  U [R,gamma,V] fp32; W1 [V,r] (w_dtype); W2p = spec_pack_w2(W2);
+ *      x0 [R] int32.
  * Out: x [R,gamma] int32; pd_x [R,gamma] fp32 = p_k(x_k);
  *      pd_stats [R,gamma,2] fp32 = (M, S) with M = max_v z_k(v) and
  *      S = sum_v exp((z_k(v) - M)/T), so p_k(v) = exp((z_k(v)-M)/T)/S.
  * The gamma positions run serially on the device; nothing returns to the
  * host in between. */
-int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dtype,
+int spec_markov_propose(const float* U, const void* W1, const void* W2p, int w_dtype,
                         const int32_t* x0, int R, int gamma, int r, int V, float T,
                         int greedy, uint64_t seed, uint64_t round,
                         int32_t* x, float* pd_x, float* pd_stats,
@@ -124,7 +140,7 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dt
  *   normalize(max(0, p_t,k - p_k)) (word 2 at k; p_t,k if that mass is 0;
  *   greedy: the target argmax); after l_r accepts emit the bonus draw from
  *   p_t,l_r+1 (word 2 at k = l_r + 1).  p_t,k = softmax(Lt[r,k-1,:] / T).
- * In:  U, W1, W2, x0 as for propose; x [R,gamma] drafts; pd_stats from
+ * In:  U, W1, W2p, x0 as for propose; x [R,gamma] drafts; pd_stats from
  *      propose for the same drafts; Lt [R,gamma+1,V] fp32;
  *      ell [R] int32 verify lengths in [0,gamma], or NULL = gamma for all.
  * Out: n_acc [R] int32 accepted drafts (bonus excluded);
@@ -133,7 +149,7 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dt
  *      c_star [R,gamma] fp32 = 1 - 1/2 ||p_k - p_t,k||_1 clamped to [0,1]
  *      (optional; NULL skips the full-row sweep of accepted positions).
  * Entries past l_r are NaN (pt_x, c_star). */
-int spec_verify(const float* U, const void* W1, const void* W2, int w_dtype,
+int spec_verify(const float* U, const void* W1, const void* W2p, int w_dtype,
                 const int32_t* x0, const int32_t* x, const float* pd_stats,
                 const float* Lt, const int32_t* ell,
                 int R, int gamma, int r, int V, float T, int greedy,
@@ -146,7 +162,7 @@ int spec_verify(const float* U, const void* W1, const void* W2, int w_dtype,
  *   c_star [R,gamma] fp32 = clamp(1 - 1/2 ||p_k - p_t,k||_1, 0, 1)
  *   a_star [R,gamma] fp64 = prod_{i<=k} c*_i, left to right (optional).
  * pd_stats may be NULL (the draft normalisers are then recomputed). */
-int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
+int spec_confidence(const float* U, const void* W1, const void* W2p, int w_dtype,
                     const int32_t* x0, const int32_t* x, const float* pd_stats,
                     const float* Lt, int R, int gamma, int r, int V, float T,
                     float* c_star, double* a_star,

@@ -34,6 +34,7 @@ def to_dev(d):
             t[k] = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
         else:
             t[k] = torch.from_numpy(w).cuda()
+    t["W2p"] = spec.spec_pack_w2(t["W2"])
     t["x0"] = torch.from_numpy(d["x0"]).cuda()
     if "c" in d:
         t["c"] = torch.from_numpy(d["c"]).cuda()
@@ -125,14 +126,14 @@ def check_verify(d, x, ell, n_acc, y, pt_x, c_star, greedy, seed=1, rnd=0):
 
 
 def run_propose(t, cfg, greedy, seed=1, rnd=0, ws=None):
-    x, pdx, pds = spec.spec_markov_propose(t["U"], t["W1"], t["W2"], t["x0"], cfg.T, greedy, seed, rnd,
+    x, pdx, pds = spec.spec_markov_propose(t["U"], t["W1"], t["W2p"], t["x0"], cfg.T, greedy, seed, rnd,
                                            ws=ws)
     torch.cuda.synchronize()
     return x, pdx, pds
 
 
 def run_verify(t, cfg, x, pds, greedy, ell=None, seed=1, rnd=0, ws=None):
-    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2"], t["x0"], x, pds, t["Lt"], cfg.T,
+    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2p"], t["x0"], x, pds, t["Lt"], cfg.T,
                                               greedy, seed, rnd, ell=ell, ws=ws)
     torch.cuda.synchronize()
     return n_acc, y, pt_x, c_star

@@ -103,6 +103,19 @@ def test_propose_validation(L):
     assert _propose(L, R=0, U=None, W1=None, W2=None, x0=None, x=None, pdx=None, pds=None) == d.SPEC_OK
 
 
+def test_pack_validation(L):
+    import draft_sampling_verify_amd as d
+    assert L.spec_packed_w2_bytes(1, 256, 129280) == 129280 * 256 * 2
+    assert L.spec_packed_w2_bytes(1, 16, 1001) == 32 * 32 * 16 * 2      # padded to 32-id blocks
+    assert L.spec_packed_w2_bytes(0, 16, 5) == 32 * 16 * 4
+    assert L.spec_packed_w2_bytes(1, 24, 100) == 0
+    assert L.spec_packed_w2_bytes(3, 16, 100) == 0
+    assert L.spec_pack_w2(FAKE, 1, 16, 100, None, None) == d.SPEC_EINVAL
+    assert L.spec_pack_w2(FAKE, 1, 16, 100, ctypes.c_void_p(4100), None) == d.SPEC_EINVAL
+    assert L.spec_pack_w2(FAKE, 4, 16, 100, FAKE, None) == d.SPEC_EDTYPE
+    assert L.spec_pack_w2(FAKE, 1, 16, 0, FAKE, None) == d.SPEC_EINVAL
+
+
 def test_verify_confidence_schedule_validation(L):
     import draft_sampling_verify_amd as d
     F = FAKE

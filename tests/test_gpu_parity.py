@@ -62,7 +62,7 @@ def test_small_propose_verify_confidence(name, greedy):
     # confidence, with and without the propose statistics
     oc, oa = oracle.confidence(d["U"], d["W1"], d["W2"], d["x0"], np_(x), d["Lt"], np.float32(cfg.T))
     for stats in (pds, None):
-        cs, a = spec.spec_confidence(t["U"], t["W1"], t["W2"], t["x0"], x, t["Lt"], cfg.T, pd_stats=stats, ws=ws)
+        cs, a = spec.spec_confidence(t["U"], t["W1"], t["W2p"], t["x0"], x, t["Lt"], cfg.T, pd_stats=stats, ws=ws)
         torch.cuda.synchronize()
         np.testing.assert_allclose(np_(cs), oc, rtol=0, atol=PROB_TOL)
         np.testing.assert_allclose(np_(a), oa, rtol=0, atol=PROB_TOL * cfg.gamma)
@@ -97,20 +97,20 @@ def test_invalid_tokens_flag_and_blank_outputs():
     ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
     x0 = t["x0"].clone()
     x0[1] = cfg.V        # out of range anchor
-    x, pdx, pds = spec.spec_markov_propose(t["U"], t["W1"], t["W2"], x0, 1.0, False, 1, 0, ws=ws)
+    x, pdx, pds = spec.spec_markov_propose(t["U"], t["W1"], t["W2p"], x0, 1.0, False, 1, 0, ws=ws)
     torch.cuda.synchronize()
     assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_TOKEN
     assert (np_(x)[1] == -1).all() and np.isnan(np_(pdx)[1]).all()
     ok = [0, 2, 3]
     dd = workloads.make(cfg, requests=ok)
     check_propose(dd, np_(x)[ok], np_(pdx)[ok], np_(pds)[ok], False)
-    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2"], x0, x, pds, t["Lt"], 1.0, False,
+    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2p"], x0, x, pds, t["Lt"], 1.0, False,
                                               1, 0, ws=ws)
     torch.cuda.synchronize()
     assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_TOKEN
     assert np_(n_acc)[1] == -1 and (np_(y)[1] == -1).all()
     bad_ell = torch.tensor([1, 2, cfg.gamma + 1, 0], dtype=torch.int32, device="cuda")
-    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2"], t["x0"], x.clone().fill_(0),
+    n_acc, y, pt_x, c_star = spec.spec_verify(t["U"], t["W1"], t["W2p"], t["x0"], x.clone().fill_(0),
                                               pds, t["Lt"], 1.0, False, 1, 0, ell=bad_ell, ws=ws)
     torch.cuda.synchronize()
     assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_LENGTH
@@ -122,7 +122,8 @@ def test_empty_batch_is_a_no_op():
     e = torch.empty((0, 4, 1024), device="cuda")
     W = torch.zeros((1024, 16), device="cuda")
     x0 = torch.empty(0, dtype=torch.int32, device="cuda")
-    x, pdx, pds = spec.spec_markov_propose(e, W, W, x0, 1.0, ws=spec.Workspace(1, 4, 16, 1024))
+    Wp = spec.spec_pack_w2(W)
+    x, pdx, pds = spec.spec_markov_propose(e, W, Wp, x0, 1.0, ws=spec.Workspace(1, 4, 16, 1024))
     assert x.shape == (0, 4)
 
 
@@ -134,7 +135,7 @@ def _chi2_case(V=16, r=16, rounds=16, R=65536, seed=21):
     W2 = (rng.standard_normal((V, r)) * 0.5).astype(np.float32)
     U = torch.from_numpy(u[:1]).cuda().expand(R, 1, V).contiguous()
     Lt = torch.from_numpy(lt).cuda().expand(R, 2, V).contiguous()
-    tW1, tW2 = torch.from_numpy(W1).cuda(), torch.from_numpy(W2).cuda()
+    tW1, tW2 = torch.from_numpy(W1).cuda(), spec.spec_pack_w2(torch.from_numpy(W2).cuda())
     x0 = torch.full((R,), 2, dtype=torch.int32, device="cuda")
     ws = spec.Workspace(R, 1, r, V)
     first, acc1 = [], []
@@ -215,7 +216,7 @@ def test_c4_pipeline():
     t = to_dev(d)
     ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V, B_max=cfg.sps_len)
     x, pdx, pds = run_propose(t, cfg, False, ws=ws)
-    c_star, a_star = spec.spec_confidence(t["U"], t["W1"], t["W2"], t["x0"], x, t["Lt"], cfg.T, pd_stats=pds,
+    c_star, a_star = spec.spec_confidence(t["U"], t["W1"], t["W2p"], t["x0"], x, t["Lt"], cfg.T, pd_stats=pds,
                                           ws=ws)
     ell, a, K, th = spec.spec_schedule(t["c"], t["sps"], ws=ws)
     n_acc, y, pt_x, cv = run_verify(t, cfg, x, pds, False, ell=ell, ws=ws)
@@ -239,3 +240,27 @@ def test_c4_pipeline():
     # the verify c* equals the confidence c* on verified positions
     for i in range(cfg.R):
         np.testing.assert_allclose(np_(cv)[i, :ell_np[i]], np_(c_star)[i, :ell_np[i]], rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("bf16,r,V", [(True, 256, 1000), (True, 16, 33), (True, 512, 64),
+                                      (False, 256, 70), (False, 16, 5)])
+def test_pack_w2_layout(bf16, r, V):
+    """The packed W2 equals a numpy re-derivation of the documented layout."""
+    rng = np.random.default_rng(r + V)
+    W = rng.standard_normal((V, r)).astype(np.float32)
+    nblk = (V + 31) // 32
+    Wpad = np.zeros((nblk * 32, r), np.float32)
+    if bf16:
+        bits = workloads.to_bf16_bits(W)
+        Wt = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        Wpad[:V] = workloads.bf16_bits_to_f32(bits)
+        got = workloads.bf16_bits_to_f32(np_(spec.spec_pack_w2(Wt)).view(np.uint16))
+        got = got.reshape(nblk, r // 16, 2, 32, 8)            # block, k-step, half, row, element
+        want = Wpad.reshape(nblk, 32, r // 16, 2, 8).transpose(0, 2, 3, 1, 4)
+    else:
+        Wt = torch.from_numpy(W).cuda()
+        Wpad[:V] = W
+        got = np_(spec.spec_pack_w2(Wt)).view(np.float32).reshape(nblk, r // 8, 2, 32, 4)
+        # group t, half h, row n, component q  <-  W[32b + n, 8t + 2q + h]
+        want = Wpad.reshape(nblk, 32, r // 8, 4, 2).transpose(0, 2, 4, 1, 3)
+    np.testing.assert_array_equal(got, want)
