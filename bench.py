@@ -28,13 +28,16 @@ sys.path.insert(0, ROOT)
 METRIC = "verified draft tokens/s (propose+verify) at V=129280, gamma=7; % HBM roofline"
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+_PROPOSE = ["draft_sampling_verify_amd/csrc/propose.hip", "draft_sampling_verify_amd/csrc/common.h"]
+_VERIFY = ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"]
 KERNEL_SOURCES = {
-    "draft_tile": ["draft_sampling_verify_amd/csrc/propose.hip", "draft_sampling_verify_amd/csrc/common.h"],
-    "propose_pick": ["draft_sampling_verify_amd/csrc/propose.hip", "draft_sampling_verify_amd/csrc/common.h"],
-    "target_tile": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
-    "row_merge": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
-    "verify_sweep": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
-    "verify_resolve": ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"],
+    "propose_fused": _PROPOSE,
+    "clear_flags": _PROPOSE,
+    "draft_tile": _PROPOSE,
+    "propose_pick": _PROPOSE,
+    "target_rows": _VERIFY,
+    "verify_sweep": _VERIFY,
+    "verify_resolve": _VERIFY,
 }
 
 
@@ -52,16 +55,18 @@ def algorithmic_bytes(kernel: str, cfg, K: int) -> float:
     R, g, V, r = cfg.R, cfg.gamma, cfg.V, cfg.r
     wb = 2 if cfg.bf16 else 4
     ng = (V + 127) // 128
+    if kernel == "propose_fused":   # all positions: U rows, W2 once, W1 rows; x, p_d(x), (M, S) out
+        return 4.0 * R * g * V + wb * r * V + wb * R * g * r + 16.0 * R * g
+    if kernel == "clear_flags":
+        return 4.0 * (ng + R + 1)
     if kernel == "draft_tile":      # one position: U_k rows, W2, W1 rows; (max, sum) partials out
         return 4.0 * R * V + wb * r * V + wb * R * r + 8.0 * R * ng
-    if kernel == "target_tile":     # every target row once; (max, sum, argmax) partials out
+    if kernel == "target_rows":     # every target row once; (max, sum, argmax) partials out
         return (R + K) * (4.0 * V + 12.0 * ng)
     if kernel == "verify_sweep":    # U and target rows of every verified row, W2, W1 rows; partials out
         return K * (8.0 * V + wb * r + 8.0 * ng) + wb * r * V
     if kernel == "propose_pick":    # partials of every request + one granule rescan
         return R * (8.0 * ng + 128 * (4.0 + wb * r) + 16.0)
-    if kernel == "row_merge":
-        return (R + K) * (8.0 * ng + 12.0)
     if kernel == "verify_resolve":
         return R * (8.0 * ng * (g + 2) + 128 * (8.0 + wb * r))
     return float("nan")
@@ -124,6 +129,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + timed steps only (for rocprofv3), print the JSON line")
+    ap.add_argument("--propose-path", choices=["auto", "per_position"], default="auto",
+                    help="auto: the fused single-launch propose where it fits; per_position: two kernels "
+                         "per draft position")
     ap.add_argument("--calib-copy-mb", type=int, default=512,
                     help="size of the device-to-device copy timed as the achievable-bandwidth reference")
     args = ap.parse_args()
@@ -140,6 +148,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     spec.lib()
+    spec.spec_set_propose_fused(args.propose_path == "auto")
     cfg = workloads.CONFIGS[args.workload]
     d = workloads.make(cfg)
     dev = torch.device("cuda:0")
@@ -246,7 +255,8 @@ def main():
         "config": {"workload": "%s: R=%d, gamma=%d, V=%d, r=%d, %s Markov weights, fp32 logits, "
                                "sampled, T=%g, all positions verified" %
                                (cfg.name, R, g, V, cfg.r, "bf16" if cfg.bf16 else "fp32", cfg.T),
-                   "R": R, "gamma": g, "V": V, "r": cfg.r, "verified_per_step": K},
+                   "R": R, "gamma": g, "V": V, "r": cfg.r, "verified_per_step": K,
+                   "propose": "fused" if "propose_fused" in kernels else "per_position"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": per_launch},

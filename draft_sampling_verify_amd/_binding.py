@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libspec.so")
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH, SPEC_EDEVICE, SPEC_EUNSUPPORTED = range(7)
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE = range(4)
-SPEC_DEV_BAD_TOKEN, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_CONFIDENCE = 1, 2, 4
+SPEC_DEV_BAD_TOKEN, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_CONFIDENCE, SPEC_DEV_WAIT_FAILED = 1, 2, 4, 8
 
 
 class SpecError(RuntimeError):
@@ -44,6 +44,7 @@ _SIGS = {
     "spec_confidence": ([P, P, P, I, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P], I),
     "spec_schedule": ([P, I, I, P, I, P, P, P, P, P, SZ, P], I),
     "spec_status_str": ([I], ctypes.c_char_p),
+    "spec_set_propose_fused": ([I], I),
     "spec_profile_enable": ([I], I),
     "spec_profile_reset": ([], I),
     "spec_profile_read": ([ctypes.c_char_p, P, P], I),
@@ -270,6 +271,12 @@ def spec_schedule(c, sps, ell=None, a=None, K_star=None, theta_star=None, want_a
                              _ptr(theta_star), ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_schedule")
     return ell, a, K_star, theta_star
+
+
+def spec_set_propose_fused(enable: bool) -> bool:
+    """Process-wide: allow (True, the default) or forbid the fused propose
+    launch; returns the previous setting."""
+    return bool(lib().spec_set_propose_fused(int(bool(enable))))
 
 
 def spec_profile_enable(on=True):

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -74,6 +75,12 @@ size_t g_pool_used = 0;
 
 namespace spec {
 
+namespace {
+std::atomic<int> g_fused{1};
+}
+int set_propose_fused(int enable) { return g_fused.exchange(enable ? 1 : 0); }
+int propose_fused_enabled() { return g_fused.load(); }
+
 ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s)
 {
     if (!g_prof_on) return;
@@ -126,6 +133,8 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
         return 0;
     }
 }
+
+int spec_set_propose_fused(int enable) { return spec::set_propose_fused(enable); }
 
 int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream)
 {

@@ -14,6 +14,7 @@ namespace spec {
 
 constexpr int WAVE = 64;
 constexpr int GRAN = 128;       // vocabulary ids per granule
+constexpr int ZS_ = GRAN + 4;   // row stride (floats) of the 32 x 128 LDS result tile
 constexpr int BLOCK_ROWS = 32;  // rows per MFMA block (one 32x32 output tile)
 constexpr int TILE_THREADS = 256;
 
@@ -56,6 +57,73 @@ __device__ inline u32x4 philox(uint32_t k, uint32_t req, uint64_t round, uint64_
 // 24-bit uniform in [0, 1 - 2^-24]; exact in fp32 and fp64.
 __device__ inline float u24f(uint32_t w) { return (float)(w >> 8) * (1.0f / 16777216.0f); }
 __device__ inline double u24d(uint32_t w) { return (double)(w >> 8) * (1.0 / 16777216.0); }
+
+// ------------------------------------------- exchange between workgroups
+//
+// Values one workgroup of a running kernel hands to another go through
+// agent-scope atomic stores and loads.  On gfx950 these carry the sc1 cache
+// policy: stores write through to the device coherence point and loads do
+// not hit stale lines in the per-XCD L2, so no L2 writeback or invalidate is
+// needed.  A producer issues its data stores, waits until they are
+// acknowledged (stores_done), and only then stores the flag the consumer
+// polls; the consumer reads the data after it has seen the flag.
+
+__device__ inline void st_dev(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(int32_t* p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev2(float* p, float a, float b)  // p 8-byte aligned
+{
+    const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t ld_dev(const uint64_t* p)
+{
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t ld_dev(const uint32_t* p)
+{
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int32_t ld_dev(const int32_t* p)
+{
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float2 ld_dev2(const float* p)  // p 8-byte aligned
+{
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+// Hide a uniform value from loop-invariant code motion, so that addresses
+// derived from it are recomputed where they are used instead of being kept
+// live (or spilled) across a long loop body.
+template <typename T>
+__device__ inline T* opaque(T* p)
+{
+    asm volatile("" : "+s"(p));
+    return p;
+}
+__device__ inline int opaque(int v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+__device__ inline int opaque_v(int v)  // per-lane value
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ inline void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ------------------------------------------------------------- arithmetic
 
@@ -331,6 +399,18 @@ struct TileOps<bf16w, KS> {
         }
         return acc;
     }
+    // all KS k-steps (r == 16 KS), accumulating onto acc
+    __device__ inline f32x16 mfma_acc(const void* sB, int lane, f32x16 acc) const
+    {
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(sB) + (lane & 31) * RS + 8 * (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 bv = *reinterpret_cast<const uint4*>(B + 16 * s);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+        }
+        return acc;
+    }
     // B operand held in registers: lane l = n + 32h keeps W1[tok, 16s+8h..+7]
     // of its own row token (tok < 0: zeros).  Used by the single-row rescans.
     struct BRow {
@@ -394,6 +474,19 @@ struct TileOps<float, KS> {
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, B[8 * t + 4], acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, B[8 * t + 6], acc, 0, 0, 0);
             }
+        }
+        return acc;
+    }
+    // all KS groups (r == 8 KS), accumulating onto acc
+    __device__ inline f32x16 mfma_acc(const void* sB, int lane, f32x16 acc) const
+    {
+        const float* B = reinterpret_cast<const float*>(sB) + (lane & 31) * RS + (lane >> 5);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].x, B[8 * t + 0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].y, B[8 * t + 2], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, B[8 * t + 4], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, B[8 * t + 6], acc, 0, 0, 0);
         }
         return acc;
     }
@@ -461,8 +554,55 @@ __device__ inline void stage_w1(void* sB, const WT* W1, const int* tok, int r)
     }
 }
 
+// stage_w1 for r that fills the k-steps exactly (2 KS uint4 per row): every
+// thread issues all of its loads before its first LDS write, so the gather
+// costs one memory round trip.
+template <typename WT, int RS, int KS>
+__device__ inline void stage_w1_exact(void* sB, const WT* W1, const int* tok)
+{
+    constexpr int ELEM = (int)sizeof(WT);
+    constexpr int PER_ROW = 2 * KS;                  // uint4 per W1 row
+    constexpr int R_ELEMS = PER_ROW * 16 / ELEM;     // r
+    constexpr int TOTAL = 32 * PER_ROW;
+    constexpr int NPT = (TOTAL + TILE_THREADS - 1) / TILE_THREADS;
+    // indices recomputed here from an opaque thread id: nothing of this
+    // survives between calls (register pressure in the callers' loops)
+    const int t0 = opaque_v(threadIdx.x);
+    uint4 v[NPT];
+    uint32_t keep[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        int idx = t0 + i * TILE_THREADS;
+        if (TOTAL % TILE_THREADS != 0) idx = min(idx, TOTAL - 1);  // duplicates store the same value
+        const int tk = tok[idx / PER_ROW];
+        keep[i] = tk >= 0 ? ~0u : 0u;
+        // unconditional load (row 0 for a missing token), masked to zero below
+        v[i] = reinterpret_cast<const uint4*>(W1 + (size_t)(tk >= 0 ? tk : 0) * R_ELEMS)[idx % PER_ROW];
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        int idx = t0 + i * TILE_THREADS;
+        if (TOTAL % TILE_THREADS != 0) idx = min(idx, TOTAL - 1);
+        const uint4 m = make_uint4(v[i].x & keep[i], v[i].y & keep[i], v[i].z & keep[i], v[i].w & keep[i]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sB) + (size_t)(idx / PER_ROW) * RS * ELEM +
+                                  16 * (idx % PER_ROW)) = m;
+    }
+}
+
+// Read back what store_tile wrote for this lane (its own 16 entries).
+__device__ inline void load_tile_own(const float* sZ, f32x16& acc, int w, int lane)
+{
+    const int n = lane & 31, h = lane >> 5;
+    const float* row = sZ + n * ZS_ + 32 * w + 4 * h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(row + 8 * q);
+        acc[4 * q] = v.x; acc[4 * q + 1] = v.y; acc[4 * q + 2] = v.z; acc[4 * q + 3] = v.w;
+    }
+}
+
 // LDS tile of the block's results: 32 rows x 128 ids (+4 floats padding).
-constexpr int ZS = GRAN + 4;
+constexpr int ZS = ZS_;
 
 // Wave w stores its 32x32 result into sZ[n][32w + ...].
 __device__ inline void store_tile(float* sZ, const f32x16& acc, int w, int lane)

@@ -17,7 +17,9 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Workspace header: status word and device-side counts.
 struct WsHeader {
     uint32_t status;     // SPEC_DEV_* bits (sticky)
-    uint32_t pad0[3];
+    uint32_t epoch;      // fused propose calls made with this workspace
+    uint32_t abort;      // epoch of a fused propose that gave up waiting
+    uint32_t pad0;
     int32_t counts[4];   // [0] verified rows K, [1] target rows K + R
 };
 constexpr size_t WS_HEADER = 256;
@@ -79,9 +81,18 @@ inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence,
     return w;
 }
 
+// The fused propose (one cooperative launch for all positions) handles one
+// block of up to 32 requests; its hand-over words are kept in this many
+// copies (every workgroup polls them).
+constexpr int FUSED_MAX_R = 32;
+constexpr int FUSED_TOKEN_COPIES = 8;
+constexpr int FUSED_PART_WORDS = 3;  // per (request, granule): max, sum, argmax
+
 struct ProposeWs {
-    float2* gstat;   // [R, n_gran]
-    int32_t* gidx;   // [R, n_gran]
+    float2* gstat;    // [R, n_gran] per-position kernels
+    int32_t* gidx;    // [R, n_gran]
+    uint64_t* part;   // [R, n_gran, FUSED_PART_WORDS] fused: tagged partials (R <= FUSED_MAX_R), else null
+    uint64_t* words;  // [FUSED_TOKEN_COPIES, 32] fused: tagged token words
 };
 
 inline ProposeWs carve_propose(void* ws, int R, int V, size_t* bytes)
@@ -91,9 +102,18 @@ inline ProposeWs carve_propose(void* ws, int R, int V, size_t* bytes)
     ProposeWs w{};
     w.gstat = c.take<float2>((size_t)R * ng);
     w.gidx = c.take<int32_t>((size_t)R * ng);
+    if (R <= FUSED_MAX_R) {
+        w.part = c.take<uint64_t>((size_t)R * ng * FUSED_PART_WORDS);
+        w.words = c.take<uint64_t>((size_t)FUSED_TOKEN_COPIES * 32);
+    }
     if (bytes) *bytes = c.off;
     return w;
 }
+
+// Process-wide switch: 0 keeps the propose on the per-position kernels even
+// where the fused launch fits (returns the previous value).
+int set_propose_fused(int enable);
+int propose_fused_enabled();
 
 // Arguments common to the draft-side kernels.
 struct DraftArgs {

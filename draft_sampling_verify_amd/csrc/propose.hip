@@ -14,6 +14,8 @@
 //                  sum crosses u * S, recompute that granule's 128 logits
 //                  with the same MFMA operands and pick the id.
 // x_k stays on the device and feeds the next position's W1 gather.
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -149,11 +151,12 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
             s_tok[t] = tok;
         }
         __syncthreads();
+        // read before the next block may overwrite s_tok (two barriers ahead)
+        const bool valid = erow < p.nrows && s_tok[er] >= 0;
         stage_w1<WT, Ops::RS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
         __syncthreads();
         store_tile(sZ, A.mfma(sB, ks, lane), w, lane);
         __syncthreads();
-        const bool valid = erow < p.nrows && s_tok[er] >= 0;
 
         const float* zr = sZ + er * ZS + ec;
         float m = -INFINITY, bv = -INFINITY;
@@ -344,6 +347,354 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
     }
 }
 
+// ------------------------------------------------------------ fused propose
+//
+// All gamma positions in one cooperative launch, for one block of up to 32
+// requests, when one workgroup per granule fits on the chip at once.
+// Workgroup g keeps the W2 columns of granule g in registers for the whole
+// call (W2 is read from HBM once instead of once per position) and, per
+// position k:
+//   tile  z = U_k + W1[x_{k-1}] W2^T for its 128 ids and every request on
+//         MFMA, then per request the granule's (max, sum of weights) or
+//         (max, argmax), stored with a tag naming (call, k);
+//   pick  for request q = g (and g + n_gran, ...): poll q's partials of all
+//         granules until every tag reads k (the values arrive with the
+//         poll), merge, draw, recompute the chosen granule on MFMA with the
+//         tile's own operands (bit-identical logits) and pick the id; the
+//         token goes out as a tagged word, which the next tile phase polls.
+// Hand-over values use agent-scope atomic stores and loads (common.h).
+// Tags carry a per-workspace call counter, so nothing needs clearing
+// between calls; every wait is bounded.
+
+struct FusedArgs {
+    TileArgs t;            // nrows = R <= 32, rows are requests
+    uint64_t seed, round;
+    int32_t* x;            // [R, gamma]
+    float* pd_x;           // [R, gamma]
+    float* pd_stats;       // [R, gamma, 2]
+    uint64_t* part;        // [R, n_gran, FUSED_PART_WORDS] tagged partials: max, sum, argmax
+    uint64_t* words;       // [FUSED_TOKEN_COPIES, 32] tagged token words
+    uint32_t* epoch;       // calls so far on this workspace
+    uint32_t* abort_flag;  // abort_word(epoch) of a call that gave up waiting
+};
+
+constexpr int SPIN_LIMIT = 1 << 20;     // polls before a wait is declared failed
+constexpr uint32_t DEV_WAIT_FAILED = 8u;
+constexpr int FUSED_PER = 4;            // granules per thread in the merge: n_gran <= 1024
+
+// Tag of (call, position): the fixed high byte keeps it apart from any float
+// or id that other calls leave in the workspace.
+__device__ inline uint32_t call_tag(uint32_t epoch, int k)
+{
+    return 0x5A000000u | ((epoch & 0xFFFFu) << 7) | (uint32_t)k;
+}
+// What a call that gives up leaves in the abort word: never 0 (the value of
+// a fresh workspace) and distinct for every epoch below 2^31.
+__device__ inline uint32_t abort_word(uint32_t epoch) { return epoch | 0x80000000u; }
+__device__ inline uint64_t tagged(uint32_t v, uint32_t tag) { return (uint64_t)v | ((uint64_t)tag << 32); }
+__device__ inline uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
+
+// End of one poll of a bounded wait (whole block): true when the wait has
+// failed (timeout, or another workgroup of this call gave up), after
+// raising the status bit and the abort word.
+__device__ inline bool poll_failed(int spin, bool aborted, uint32_t epoch, uint32_t* abort_flag, uint32_t* status)
+{
+    if (__syncthreads_or(threadIdx.x == 0 && (aborted || spin >= SPIN_LIMIT))) {
+        if (threadIdx.x == 0) {
+            st_dev(abort_flag, abort_word(epoch));
+            raise_flag(status, DEV_WAIT_FAILED);
+        }
+        return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    return false;
+}
+
+template <typename WT, int KS, bool GREEDY>
+__global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
+{
+    using Ops = TileOps<WT, KS>;
+    const TileArgs& p = f.t;
+    const int g = blockIdx.x;
+    const int NG = p.n_gran;
+    const int R = p.nrows;
+    constexpr int ks = KS;  // launched only when r fills the k-steps exactly
+    const int nblk = (p.V + 31) / 32;
+    const uint32_t epoch = ld_dev(f.epoch) & 0x7FFFFFFFu;
+
+    Ops A;
+    A.load_a(p.W2p, ks, 4 * g + (int)threadIdx.x / WAVE, 4 * g + (int)threadIdx.x / WAVE < nblk,
+             threadIdx.x & (WAVE - 1));
+
+    __shared__ __align__(16) char sB[32 * Ops::RS * Ops::ELEM];
+    __shared__ __align__(16) float sZ[32 * ZS];
+    __shared__ int s_tok[32];
+    __shared__ float s_red[TILE_THREADS / WAVE];
+    __shared__ int s_ired[TILE_THREADS / WAVE];
+    __shared__ int s_gstar;
+    __shared__ float s_before;
+    __shared__ float zrow[GRAN];
+    __shared__ int s_prev[FUSED_MAX_R];  // previous token of each request this workgroup picks
+
+    for (int j = threadIdx.x; g + j * NG < R; j += TILE_THREADS) {
+        const int a = p.x0[g + j * NG];
+        s_prev[j] = a >= 0 && a < p.V ? a : -1;
+    }
+    // U is parked in the LDS result tile, in the matrix-core output layout,
+    // until the MFMA starts from it; no registers hold it meanwhile
+    auto load_u = [&](int k, float (&ua)[16]) {
+        const int tt = opaque_v(threadIdx.x);
+        const int row = tt & 31;
+        if (row < R) {
+            load_acc16(p.U + ((size_t)row * p.gamma + (k - 1)) * p.V, g * GRAN + 32 * (tt / WAVE), (tt >> 5) & 1,
+                       p.V, p.vec4 != 0, ua);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) ua[j] = -INFINITY;
+        }
+    };
+    auto park_u = [&](const float (&ua)[16]) {
+        const int tt = opaque_v(threadIdx.x);
+        f32x16 u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) u[j] = ua[j];
+        store_tile(sZ, u, tt / WAVE, tt & (WAVE - 1));
+    };
+    {
+        float ua[16];
+        load_u(1, ua);
+        park_u(ua);
+    }
+
+    bool failed = false;
+    for (int k = 1; k <= p.gamma && !failed; ++k) {
+        // thread-derived indices are recomputed per position rather than
+        // kept live across the loop (register pressure)
+        const int t = opaque_v(threadIdx.x), lane = t & (WAVE - 1), w = t / WAVE;
+        const int n = lane & 31, h = lane >> 5;
+        const int er = t >> 3, ec = (t & 7) * 16;
+        const int cbase = g * GRAN + ec;
+        const uint32_t tag = call_tag(epoch, k);
+
+        // ---------------- tile phase
+        int tok = -1;
+        if (k == 1) {
+            if (t < R) tok = p.x0[t];
+        } else {
+            // the previous position's tokens of all requests
+            const uint64_t* wd = opaque(f.words) + (size_t)(g % FUSED_TOKEN_COPIES) * 32;
+            const uint32_t want = call_tag(epoch, k - 1);
+            for (int spin = 0;; ++spin) {
+                bool ok = true;
+                if (t < R) {
+                    const uint64_t v = ld_dev(wd + t);
+                    ok = tag_of(v) == want;
+                    tok = (int)(uint32_t)v;
+                }
+                const bool ab = t == 0 && ld_dev(f.abort_flag) == abort_word(epoch);
+                if (__syncthreads_and(ok)) break;
+                if (poll_failed(spin, ab, epoch, f.abort_flag, p.status)) {
+                    failed = true;
+                    break;
+                }
+            }
+            if (failed) break;
+        }
+        if (t < 32) {
+            if (t >= R) {
+                tok = -1;
+            } else if (tok < 0 || tok >= p.V) {
+                if (g == 0) raise_flag(p.status, 1u);
+                tok = -1;
+            }
+            s_tok[t] = tok;
+        }
+        __syncthreads();
+        const bool valid = er < R && s_tok[er] >= 0;
+        stage_w1_exact<WT, Ops::RS, KS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok);
+        __syncthreads();
+        {
+            f32x16 acc;
+            load_tile_own(sZ, acc, w, lane);
+            store_tile(sZ, A.mfma_acc(sB, lane, acc), w, lane);
+        }
+        __syncthreads();
+        {
+            const float* zr = sZ + er * ZS + ec;
+            float z[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(zr + 4 * q);
+                z[4 * q] = v.x; z[4 * q + 1] = v.y; z[4 * q + 2] = v.z; z[4 * q + 3] = v.w;
+            }
+            float m = -INFINITY, bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                m = fmaxf(m, z[j]);
+                if (GREEDY && z[j] > bv) { bv = z[j]; bi = cbase + j; }
+            }
+            m = oct_max(m);
+            const float ms = safe_ref(m);
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s += softw(z[j], ms, p.c);
+            s = oct_sum(s);
+            if (GREEDY) oct_argmax(bv, bi);
+            if ((t & 7) == 0 && valid) {
+                uint64_t* slot = f.part + ((size_t)er * NG + g) * FUSED_PART_WORDS;
+                st_dev(slot, tagged(__float_as_uint(m), tag));
+                st_dev(slot + 1, tagged(__float_as_uint(s), tag));
+                if (GREEDY) st_dev(slot + 2, tagged((uint32_t)bi, tag));
+            }
+        }
+        __syncthreads();          // the tile's reads are complete
+        if (k < p.gamma) {
+            float ua[16];
+            load_u(k + 1, ua);
+            park_u(ua);
+        }
+
+        // ---------------- pick phase (W2 registers are free here: reloaded below)
+        if (g < R) {
+            int j = 0;
+            for (int q = g; q < R; q += NG, ++j) {
+                const size_t o = (size_t)q * p.gamma + (k - 1);
+                int xk = -1;
+                float pdx = NAN, sM = NAN, sS = NAN;
+                if (s_prev[j] >= 0) {
+                    // q's partials of every granule, polled until all carry this position
+                    const int g0 = min(t * FUSED_PER, NG), g1 = min(g0 + FUSED_PER, NG);
+                    const uint64_t* row = opaque(f.part) + (size_t)q * NG * FUSED_PART_WORDS;
+                    float gm[FUSED_PER], gs[FUSED_PER];
+                    uint32_t gi[FUSED_PER];
+                    for (int spin = 0;; ++spin) {
+                        bool ok = true;
+#pragma unroll
+                        for (int i = 0; i < FUSED_PER; ++i) {
+                            gm[i] = -INFINITY;
+                            gs[i] = 0.0f;
+                            gi[i] = 0u;
+                            if (g0 + i < g1) {
+                                const uint64_t* sl = row + (size_t)(g0 + i) * FUSED_PART_WORDS;
+                                const uint64_t a0 = ld_dev(sl), a1 = ld_dev(sl + 1);
+                                const uint64_t a2 = GREEDY ? ld_dev(sl + 2) : tagged(0u, tag);
+                                ok &= tag_of(a0) == tag && tag_of(a1) == tag && tag_of(a2) == tag;
+                                gm[i] = __uint_as_float((uint32_t)a0);
+                                gs[i] = __uint_as_float((uint32_t)a1);
+                                gi[i] = (uint32_t)a2;
+                            }
+                        }
+                        const bool ab = t == 0 && ld_dev(f.abort_flag) == abort_word(epoch);
+                        if (__syncthreads_and(ok)) break;
+                        if (poll_failed(spin, ab, epoch, f.abort_flag, p.status)) {
+                            failed = true;
+                            break;
+                        }
+                    }
+                    if (failed) break;
+                    float mloc = -INFINITY;
+#pragma unroll
+                    for (int i = 0; i < FUSED_PER; ++i) mloc = fmaxf(mloc, gm[i]);
+                    const float M = block_max(mloc, s_red);
+                    float wv[FUSED_PER], tsum = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < FUSED_PER; ++i) {
+                        wv[i] = gs[i] * softw(gm[i], M, p.c);  // padding: 0 * 0
+                        tsum += wv[i];
+                    }
+                    float S;
+                    const float excl = block_excl_scan(tsum, s_red, S);
+                    if (GREEDY) {
+                        int cand = 0x7fffffff;
+#pragma unroll
+                        for (int i = FUSED_PER - 1; i >= 0; --i)
+                            if (g0 + i < g1 && gm[i] == M) cand = (int)gi[i];
+                        xk = block_min(cand, s_ired);
+                        sM = M;
+                    } else {
+                        sM = M;
+                        sS = S;
+                        const float target = u24f(philox((uint32_t)k, (uint32_t)q, f.round, f.seed).w[0]) * S;
+                        // first granule of positive mass whose running sum exceeds target
+                        float run = excl, prev = excl;
+                        int pick = -1, lastpos = -1;
+#pragma unroll
+                        for (int i = 0; i < FUSED_PER; ++i) {
+                            if (wv[i] > 0.0f) lastpos = g0 + i;
+                            if (pick < 0) {
+                                prev = run;
+                                run += wv[i];
+                                if (run > target && wv[i] > 0.0f) pick = g0 + i;
+                            }
+                        }
+                        const int first = block_min(pick >= 0 ? t : 0x7fffffff, s_ired);
+                        const int lastp = -block_min(-lastpos, s_ired);
+                        if (t == first) {
+                            s_gstar = pick;
+                            s_before = prev;
+                        }
+                        __syncthreads();
+                        const bool fallback = first == 0x7fffffff;
+                        const int gstar = fallback ? max(lastp, 0) : s_gstar;
+                        const float before = fallback ? 0.0f : s_before;
+                        // granule gstar for q with the tile's own operands: W2
+                        // block, U_k as the starting accumulator, and sB, which
+                        // still holds this position's W1 rows (column q)
+                        {
+                            Ops A2;
+                            A2.load_a(p.W2p, ks, 4 * gstar + w, 4 * gstar + w < nblk, lane);
+                            float uq[16];
+                            load_acc16(p.U + ((size_t)q * p.gamma + (k - 1)) * p.V, gstar * GRAN + 32 * w, h, p.V,
+                                       p.vec4 != 0, uq);
+                            f32x16 acc;
+#pragma unroll
+                            for (int jj = 0; jj < 16; ++jj) acc[jj] = uq[jj];
+                            acc = A2.mfma_acc(sB, lane, acc);
+                            if (n == (q & 31)) {
+#pragma unroll
+                                for (int jj = 0; jj < 16; ++jj)
+                                    zrow[32 * w + 8 * (jj >> 2) + 4 * h + (jj & 3)] = softw(acc[jj], M, p.c);
+                            }
+                        }
+                        __syncthreads();
+                        if (w == 0) {
+                            float e;
+                            const int col = granule_pick(zrow[2 * lane], zrow[2 * lane + 1], before, target,
+                                                         fallback, e);
+                            xk = gstar * GRAN + col;
+                            pdx = e / S;
+                        }
+                    }
+                    if (GREEDY) {
+                        sS = S;
+                        pdx = 1.0f / S;
+                    }
+                }
+                // wave 0 publishes the token (copies in lanes 0..7) and
+                // records the outputs
+                if (w == 0) {
+                    if (lane < FUSED_TOKEN_COPIES) st_dev(f.words + (size_t)lane * 32 + q, tagged((uint32_t)xk, tag));
+                    if (lane == 0) {
+                        f.x[o] = xk;
+                        f.pd_x[o] = pdx;
+                        f.pd_stats[2 * o] = sM;
+                        f.pd_stats[2 * o + 1] = sS;
+                        s_prev[j] = xk;
+                    }
+                }
+                __syncthreads();
+            }
+            // unconditional, so that the W2 registers are provably free
+            // during the picks (32 workgroups re-read 64 KB each)
+            if (!GREEDY) A.load_a(p.W2p, ks, 4 * g + w, 4 * g + w < nblk, lane);
+        }
+    }
+    // the call counter advances once every workgroup has read it: workgroup
+    // 0's last pick needed the partials of all of them
+    if (g == 0 && threadIdx.x == 0) st_dev(f.epoch, (epoch + 1) & 0x7FFFFFFFu);
+}
+
 // ------------------------------------------------------------ launchers
 
 // Workgroups cover one granule and `bpc` consecutive 32-row blocks; the row
@@ -356,6 +707,48 @@ static void tile_grid(int nrows, int n_gran, int& bpc, int& n_chunks)
     if (n_chunks < 1) n_chunks = 1;
     bpc = (n_rb + n_chunks - 1) / n_chunks;
     n_chunks = (n_rb + bpc - 1) / bpc;
+}
+
+// Workgroups of k_propose_fused the current device holds at once (0 if it
+// cannot launch cooperatively); cached per device.
+template <typename WT, int KS, bool GREEDY>
+static int fused_capacity()
+{
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV];  // capacity + 1; 0 = not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int coop = 0, cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_propose_fused<WT, KS, GREEDY>, TILE_THREADS,
+                                                         0) != hipSuccess)
+            per_cu = 0;
+        v = (coop ? per_cu * cus : 0) + 1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v - 1;
+}
+
+template <typename WT, int KS, bool GREEDY>
+static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* x_out, float* pd_x,
+                                float* pd_stats, const ProposeWs& ws, hipStream_t s)
+{
+    FusedArgs f{};
+    f.t = t;
+    f.seed = a.seed; f.round = a.round;
+    f.x = x_out; f.pd_x = pd_x; f.pd_stats = pd_stats;
+    f.part = ws.part;
+    f.words = ws.words;
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(a.status);
+    f.epoch = &hdr->epoch;
+    f.abort_flag = &hdr->abort;
+    void* args[] = {&f};
+    ProfScope ps("propose_fused", s);
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_propose_fused<WT, KS, GREEDY>),
+                                      dim3(t.n_gran), dim3(TILE_THREADS), args, 0, s);
 }
 
 template <typename WT, int KS>
@@ -374,6 +767,16 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
     pk.R = a.R; pk.gamma = a.gamma; pk.r = a.r; pk.V = a.V; pk.c = a.c;
     pk.n_gran = n_gran; pk.seed = a.seed; pk.round = a.round;
     pk.gstat = ws.gstat; pk.gidx = ws.gidx; pk.pd_x = pd_x; pk.pd_stats = pd_stats;
+    if (ws.part && propose_fused_enabled() && n_gran <= FUSED_PER * TILE_THREADS && k_steps<WT>(a.r) == KS) {
+        const bool fits = a.greedy ? n_gran <= fused_capacity<WT, KS, true>()
+                                   : n_gran <= fused_capacity<WT, KS, false>();
+        if (fits) {
+            t.n_chunks = 1;
+            t.bpc = (a.R + BLOCK_ROWS - 1) / BLOCK_ROWS;
+            return a.greedy ? propose_fused<WT, KS, true>(a, t, x_out, pd_x, pd_stats, ws, s)
+                            : propose_fused<WT, KS, false>(a, t, x_out, pd_x, pd_stats, ws, s);
+        }
+    }
     const int grid = xcd_grid(n_gran * t.n_chunks);
     for (int k = 1; k <= a.gamma; ++k) {
         t.kfix = k - 1;

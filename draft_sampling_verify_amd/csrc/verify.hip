@@ -291,11 +291,13 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
         }
         if (t < 32) s_tok[t] = row_tok(p, rb * BLOCK_ROWS + t, nrows);
         __syncthreads();
+        // read before the next block may overwrite s_tok (two barriers ahead)
+        const bool valid = rc.req >= 0 && s_tok[er] >= 0;
         stage_w1<WT, Ops::RS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
         __syncthreads();
         store_tile(sZ, A.mfma(sB, ks, lane), w, lane);
         __syncthreads();
-        if (rc.req >= 0 && s_tok[er] >= 0) {
+        if (valid) {
             const float* zr = sZ + er * ZS + ec;
             float tv = 0.0f, res = 0.0f;
 #pragma unroll

@@ -85,7 +85,11 @@ enum spec_op { SPEC_OP_PROPOSE = 0, SPEC_OP_VERIFY = 1, SPEC_OP_CONFIDENCE = 2, 
 enum spec_device_flag {
     SPEC_DEV_BAD_TOKEN = 1,       /* an anchor or draft id outside [0, V)          */
     SPEC_DEV_BAD_LENGTH = 2,      /* an l_r outside [0, gamma]                     */
-    SPEC_DEV_BAD_CONFIDENCE = 4   /* a confidence outside [0, 1] (or NaN)          */
+    SPEC_DEV_BAD_CONFIDENCE = 4,  /* a confidence outside [0, 1] (or NaN)          */
+    SPEC_DEV_WAIT_FAILED = 8      /* the fused propose gave up waiting for another
+                                     workgroup (the GPU was shared and not all of
+                                     its workgroups ran at once); outputs of that
+                                     call are undefined                          */
 };
 
 /* Limits: 1 <= R <= 65536, 1 <= gamma <= 64, 16 <= r <= 512 (r % 16 == 0;
@@ -133,6 +137,19 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2p, int w_d
                         int greedy, uint64_t seed, uint64_t round,
                         int32_t* x, float* pd_x, float* pd_stats,
                         void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Propose runs in one of two ways, with the same results up to fp32
+ * summation order.  Fused: one cooperative launch for all gamma positions;
+ * each workgroup keeps the W2 columns of one 128-id granule in registers for
+ * the whole call, so W2 is read from HBM once.  It is taken when every
+ * granule's workgroup fits on the device at once, r fills the matrix-core
+ * k-steps exactly (r = 64, 128, 256 or 512 for bf16; 16, 64 or 256 for
+ * fp32), R <= 64 and the switch below is on.  Otherwise: two kernels per
+ * position (partials, then the pick), W2 streamed once per position.
+ * spec_set_propose_fused(0) forces the per-position kernels for every later
+ * call in the process (1 restores the default); returns the previous value.
+ * Not synchronised with calls running in other threads. */
+int spec_set_propose_fused(int enable);
 
 /* Verify drafts against target logits (standard lossless rule):
  *   for k = 1..l_r: accept x_k iff u1 < p_t,k(x_k) / p_k(x_k) (greedy: iff

@@ -27,7 +27,19 @@ SMALL = {
     "fp32_r256": Config("fp32_r256", 14, 6, 3, 3000, 256, False, 1.0, 2.0, 0.05, 0.5),
     "tiny_vocab": Config("tiny_vocab", 15, 9, 5, 7, 16, True, 1.0, 1.0, 0.3, 0.5),
     "one_token": Config("one_token", 16, 2, 3, 1, 16, True, 1.0, 1.0, 0.3, 0.5),
+    # shapes the fused (single cooperative launch) propose takes: r fills the
+    # k-steps, R <= 32; a ragged request count; more requests than granules
+    "fused_r256": Config("fused_r256", 17, 29, 7, 5000, 256, True, 1.0, 3.0, 0.02, 1.0),
+    "fused_many_req": Config("fused_many_req", 18, 30, 4, 300, 64, True, 1.0, 2.0, 0.1, 0.7),
 }
+
+
+@pytest.fixture(params=[True, False], ids=["fused", "per_position"])
+def propose_path(request):
+    """Run the test with the fused propose allowed, then forbidden."""
+    prev = spec.spec_set_propose_fused(request.param)
+    yield request.param
+    spec.spec_set_propose_fused(prev)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -69,8 +81,9 @@ def test_small_propose_verify_confidence(name, greedy):
     assert spec.spec_device_status(ws) == 0
 
 
-def test_determinism_and_round_dependence():
-    cfg = SMALL["ragged_bf16"]
+@pytest.mark.parametrize("name", ["ragged_bf16", "fused_r256"])
+def test_determinism_and_round_dependence(name, propose_path):
+    cfg = SMALL[name]
     d = workloads.make(cfg)
     t = to_dev(d)
     ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
@@ -90,7 +103,7 @@ def test_determinism_and_round_dependence():
         np.testing.assert_array_equal(u, v)
 
 
-def test_invalid_tokens_flag_and_blank_outputs():
+def test_invalid_tokens_flag_and_blank_outputs(propose_path):
     cfg = SMALL["tiny"]
     d = workloads.make(cfg)
     t = to_dev(d)
@@ -116,6 +129,33 @@ def test_invalid_tokens_flag_and_blank_outputs():
     assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_LENGTH
     assert np_(n_acc)[2] == -1
     assert spec.spec_device_status(ws) == 0
+
+
+@pytest.mark.parametrize("name", ["fused_r256", "fused_many_req", "tiny"])
+def test_propose_paths_agree_with_oracle(name):
+    """Both ways of running the propose match the oracle on the same inputs;
+    their token streams agree except where a decision is within the margin."""
+    cfg = SMALL[name]
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    outs = {}
+    prev = spec.spec_set_propose_fused(True)
+    try:
+        for fused in (True, False):
+            spec.spec_set_propose_fused(fused)
+            for greedy in (False, True):
+                x, pdx, pds = run_propose(t, cfg, greedy, ws=ws)
+                st = check_propose(d, np_(x), np_(pdx), np_(pds), greedy)
+                log("  %s %s" % ("fused" if fused else "per_position", "greedy" if greedy else "sampled"), st)
+                outs[fused, greedy] = np_(x)
+    finally:
+        spec.spec_set_propose_fused(prev)
+    assert spec.spec_device_status(ws) == 0
+    for greedy in (False, True):
+        same = (outs[True, greedy] == outs[False, greedy]).mean()
+        log("  token agreement between paths", "greedy" if greedy else "sampled", same)
+        assert same > 0.9
 
 
 def test_empty_batch_is_a_no_op():
