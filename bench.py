@@ -42,10 +42,16 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of the kernel's sources with comments and blank lines removed
+    (a comment edit does not invalidate a counter measurement)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES.get(kernel, []):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

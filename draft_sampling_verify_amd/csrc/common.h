@@ -399,6 +399,34 @@ struct TileOps<bf16w, KS> {
         }
         return acc;
     }
+    // the ks real k-steps, accumulating onto acc
+    __device__ inline f32x16 mfma_acc_n(const void* sB, int ks, int lane, f32x16 acc) const
+    {
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(sB) + (lane & 31) * RS + 8 * (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s < ks) {
+                const uint4 bv = *reinterpret_cast<const uint4*>(B + 16 * s);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                              __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
+    // B operand from global memory, accumulating onto acc (single-row rescans)
+    __device__ inline f32x16 mfma_global_acc(const bf16w* W1, int r, int tok, int ks, int lane, f32x16 acc) const
+    {
+        const uint4* row = reinterpret_cast<const uint4*>(W1 + (size_t)(tok < 0 ? 0 : tok) * r) + (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s < ks) {
+                const uint4 bv = tok >= 0 ? row[2 * s] : make_uint4(0, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                              __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
     // all KS k-steps (r == 16 KS), accumulating onto acc
     __device__ inline f32x16 mfma_acc(const void* sB, int lane, f32x16 acc) const
     {
@@ -425,6 +453,16 @@ struct TileOps<bf16w, KS> {
     __device__ inline f32x16 mfma_row(const BRow& br, int ks) const
     {
         f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s < ks)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                              __builtin_bit_cast(bf16x8, br.b[s]), acc, 0, 0, 0);
+        }
+        return acc;
+    }
+    __device__ inline f32x16 mfma_row_acc(const BRow& br, int ks, f32x16 acc) const
+    {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if (s < ks)
@@ -477,6 +515,37 @@ struct TileOps<float, KS> {
         }
         return acc;
     }
+    // the ks real groups, accumulating onto acc
+    __device__ inline f32x16 mfma_acc_n(const void* sB, int ks, int lane, f32x16 acc) const
+    {
+        const float* B = reinterpret_cast<const float*>(sB) + (lane & 31) * RS + (lane >> 5);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            if (t < ks) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].x, B[8 * t + 0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].y, B[8 * t + 2], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, B[8 * t + 4], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, B[8 * t + 6], acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
+    __device__ inline f32x16 mfma_global_acc(const float* W1, int r, int tok, int ks, int lane, f32x16 acc) const
+    {
+        const float* row = W1 + (size_t)(tok < 0 ? 0 : tok) * r + (lane >> 5);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            if (t < ks) {
+                const float b0 = tok >= 0 ? row[8 * t + 0] : 0.0f, b1 = tok >= 0 ? row[8 * t + 2] : 0.0f;
+                const float b2 = tok >= 0 ? row[8 * t + 4] : 0.0f, b3 = tok >= 0 ? row[8 * t + 6] : 0.0f;
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].x, b0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].y, b1, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, b2, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, b3, acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
     // all KS groups (r == 8 KS), accumulating onto acc
     __device__ inline f32x16 mfma_acc(const void* sB, int lane, f32x16 acc) const
     {
@@ -515,6 +584,19 @@ struct TileOps<float, KS> {
         }
         return acc;
     }
+    __device__ inline f32x16 mfma_row_acc(const BRow& br, int ks, f32x16 acc) const
+    {
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            if (t < ks) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].x, br.b[t].x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].y, br.b[t].y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].z, br.b[t].z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t].w, br.b[t].w, acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
     __device__ inline f32x16 mfma_global(const float* W1, int r, int tok, int ks, int lane) const
     {
         const float* row = W1 + (size_t)(tok < 0 ? 0 : tok) * r + (lane >> 5);
@@ -540,17 +622,34 @@ template <> __host__ __device__ inline int k_steps<bf16w>(int r) { return r / 16
 template <> __host__ __device__ inline int k_steps<float>(int r) { return r / 8; }
 
 // Stage the W1 rows of the 32 tokens tok[0..31] (LDS; -1 = zero row) into
-// sB[32][RS]; all threads of the block take part.
-template <typename WT, int RS>
+// sB[32][RS]; all threads of the block take part.  KS bounds the row length
+// (r <= 16 KS bf16 or 8 KS fp32 elements, 2 KS uint4); every thread issues
+// all of its loads before its first LDS write, so the gather costs one
+// memory round trip.
+template <typename WT, int RS, int KS>
 __device__ inline void stage_w1(void* sB, const WT* W1, const int* tok, int r)
 {
     constexpr int ELEM = (int)sizeof(WT);
+    constexpr int NPT = (32 * 2 * KS + TILE_THREADS - 1) / TILE_THREADS;
     const int per_row = r * ELEM / 16;  // uint4 per row
-    for (int idx = threadIdx.x; idx < 32 * per_row; idx += TILE_THREADS) {
+    const int total = 32 * per_row;
+    const int t0 = opaque_v(threadIdx.x);
+    uint4 v[NPT];
+    uint32_t keep[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int idx = min(t0 + i * TILE_THREADS, total - 1);  // duplicates store the same value
         const int row = idx / per_row, c = idx - row * per_row;
         const int tk = tok[row];
-        const uint4 v = tk >= 0 ? reinterpret_cast<const uint4*>(W1 + (size_t)tk * r)[c] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sB) + (size_t)row * RS * ELEM + 16 * c) = v;
+        keep[i] = tk >= 0 ? ~0u : 0u;
+        v[i] = reinterpret_cast<const uint4*>(W1 + (size_t)(tk >= 0 ? tk : 0) * r)[c];
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int idx = min(t0 + i * TILE_THREADS, total - 1);
+        const int row = idx / per_row, c = idx - row * per_row;
+        const uint4 m = make_uint4(v[i].x & keep[i], v[i].y & keep[i], v[i].z & keep[i], v[i].w & keep[i]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sB) + (size_t)row * RS * ELEM + 16 * c) = m;
     }
 }
 

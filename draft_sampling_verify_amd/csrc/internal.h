@@ -85,13 +85,13 @@ inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence,
 // block of up to 32 requests; its hand-over words are kept in this many
 // copies (every workgroup polls them).
 constexpr int FUSED_MAX_R = 32;
-constexpr int FUSED_TOKEN_COPIES = 8;
+constexpr int FUSED_TOKEN_COPIES = 64;
 constexpr int FUSED_PART_WORDS = 3;  // per (request, granule): max, sum, argmax
 
 struct ProposeWs {
     float2* gstat;    // [R, n_gran] per-position kernels
     int32_t* gidx;    // [R, n_gran]
-    uint64_t* part;   // [R, n_gran, FUSED_PART_WORDS] fused: tagged partials (R <= FUSED_MAX_R), else null
+    uint64_t* part;   // [FUSED_PART_WORDS][R][n_gran] fused: tagged partials (R <= FUSED_MAX_R), else null
     uint64_t* words;  // [FUSED_TOKEN_COPIES, 32] fused: tagged token words
 };
 

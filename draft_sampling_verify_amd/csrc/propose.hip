@@ -1,7 +1,10 @@
 // propose.hip -- Markov-head drafting (DSpark blog page, sections 3-4):
 // for k = 1..gamma, z_k = U_k + W1[x_{k-1}] W2^T, x_k ~ softmax(z_k / T).
 //
-// Per position two kernels run back to back on the caller's stream:
+// Up to 32 requests whose shapes allow it run in one launch
+// (k_propose_fused, below: W2 stays in registers for all positions).
+// Otherwise, per position two kernels run back to back on the caller's
+// stream:
 //   k_draft_tile   one workgroup per (128-id granule, chunk of 32-row
 //                  blocks): the bias of 32 rows x 128 ids on MFMA (W2
 //                  operand stationary in registers, W1 rows staged in LDS),
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
         __syncthreads();
         // read before the next block may overwrite s_tok (two barriers ahead)
         const bool valid = erow < p.nrows && s_tok[er] >= 0;
-        stage_w1<WT, Ops::RS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
+        stage_w1<WT, Ops::RS, KS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
         __syncthreads();
         store_tile(sZ, A.mfma(sB, ks, lane), w, lane);
         __syncthreads();
@@ -349,8 +352,8 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
 
 // ------------------------------------------------------------ fused propose
 //
-// All gamma positions in one cooperative launch, for one block of up to 32
-// requests, when one workgroup per granule fits on the chip at once.
+// All gamma positions in one launch, for one block of up to 32 requests,
+// when one workgroup per granule fits on the chip at once.
 // Workgroup g keeps the W2 columns of granule g in registers for the whole
 // call (W2 is read from HBM once instead of once per position) and, per
 // position k:
@@ -372,13 +375,14 @@ struct FusedArgs {
     int32_t* x;            // [R, gamma]
     float* pd_x;           // [R, gamma]
     float* pd_stats;       // [R, gamma, 2]
-    uint64_t* part;        // [R, n_gran, FUSED_PART_WORDS] tagged partials: max, sum, argmax
+    uint64_t* part;        // [FUSED_PART_WORDS][R][n_gran] tagged partials: max, sum, argmax
     uint64_t* words;       // [FUSED_TOKEN_COPIES, 32] tagged token words
     uint32_t* epoch;       // calls so far on this workspace
     uint32_t* abort_flag;  // abort_word(epoch) of a call that gave up waiting
 };
 
 constexpr int SPIN_LIMIT = 1 << 20;     // polls before a wait is declared failed
+constexpr int ABORT_EVERY = 32;         // polls between looks at the (single, shared) abort word
 constexpr uint32_t DEV_WAIT_FAILED = 8u;
 constexpr int FUSED_PER = 4;            // granules per thread in the merge: n_gran <= 1024
 
@@ -397,6 +401,7 @@ __device__ inline uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 // End of one poll of a bounded wait (whole block): true when the wait has
 // failed (timeout, or another workgroup of this call gave up), after
 // raising the status bit and the abort word.
+template <int SLEEP>
 __device__ inline bool poll_failed(int spin, bool aborted, uint32_t epoch, uint32_t* abort_flag, uint32_t* status)
 {
     if (__syncthreads_or(threadIdx.x == 0 && (aborted || spin >= SPIN_LIMIT))) {
@@ -406,9 +411,11 @@ __device__ inline bool poll_failed(int spin, bool aborted, uint32_t epoch, uint3
         }
         return true;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(SLEEP);
     return false;
 }
+// Whether this poll also reads the abort word (thread 0, every ABORT_EVERY polls).
+__device__ inline bool look_abort(int spin) { return threadIdx.x == 0 && spin % ABORT_EVERY == ABORT_EVERY - 1; }
 
 template <typename WT, int KS, bool GREEDY>
 __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
@@ -435,6 +442,7 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
     __shared__ float s_before;
     __shared__ float zrow[GRAN];
     __shared__ int s_prev[FUSED_MAX_R];  // previous token of each request this workgroup picks
+    __shared__ float s_round[TILE_THREADS / WAVE][FUSED_PER];
 
     for (int j = threadIdx.x; g + j * NG < R; j += TILE_THREADS) {
         const int a = p.x0[g + j * NG];
@@ -491,9 +499,9 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                     ok = tag_of(v) == want;
                     tok = (int)(uint32_t)v;
                 }
-                const bool ab = t == 0 && ld_dev(f.abort_flag) == abort_word(epoch);
+                const bool ab = look_abort(spin) && ld_dev(f.abort_flag) == abort_word(epoch);
                 if (__syncthreads_and(ok)) break;
-                if (poll_failed(spin, ab, epoch, f.abort_flag, p.status)) {
+                if (poll_failed<2>(spin, ab, epoch, f.abort_flag, p.status)) {
                     failed = true;
                     break;
                 }
@@ -542,17 +550,40 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
             s = oct_sum(s);
             if (GREEDY) oct_argmax(bv, bi);
             if ((t & 7) == 0 && valid) {
-                uint64_t* slot = f.part + ((size_t)er * NG + g) * FUSED_PART_WORDS;
-                st_dev(slot, tagged(__float_as_uint(m), tag));
-                st_dev(slot + 1, tagged(__float_as_uint(s), tag));
-                if (GREEDY) st_dev(slot + 2, tagged((uint32_t)bi, tag));
+                // partials as three arrays [R][n_gran] (max, sum, argmax), so
+                // that a poll reads them granule-contiguous
+                const size_t o = (size_t)er * NG + g, plane = (size_t)R * NG;
+                st_dev(f.part + o, tagged(__float_as_uint(m), tag));
+                st_dev(f.part + plane + o, tagged(__float_as_uint(s), tag));
+                if (GREEDY) st_dev(f.part + 2 * plane + o, tagged((uint32_t)bi, tag));
             }
         }
         __syncthreads();          // the tile's reads are complete
         if (k < p.gamma) {
-            float ua[16];
-            load_u(k + 1, ua);
-            park_u(ua);
+            // the next position's U, parked while the other workgroups finish,
+            // in four waited chunks: spread out, the 16 MB of all workgroups
+            // do not queue ahead of the small hand-over loads
+            const int tt = opaque_v(threadIdx.x);
+            const int row = tt & 31, ww = tt / WAVE, hh = (tt >> 5) & 1;
+            const float* urow = p.U + ((size_t)(row < R ? row : 0) * p.gamma + k) * p.V;
+            float* dst = sZ + row * ZS + 32 * ww + 4 * hh;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = g * GRAN + 32 * ww + 8 * q + 4 * hh;
+                float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                if (row < R) {
+                    if (p.vec4 && c + 3 < p.V) {
+                        v = *reinterpret_cast<const float4*>(urow + c);
+                    } else {
+                        v.x = c < p.V ? urow[c] : -INFINITY;
+                        v.y = c + 1 < p.V ? urow[c + 1] : -INFINITY;
+                        v.z = c + 2 < p.V ? urow[c + 2] : -INFINITY;
+                        v.w = c + 3 < p.V ? urow[c + 3] : -INFINITY;
+                    }
+                }
+                *reinterpret_cast<float4*>(dst + 8 * q) = v;
+                stores_done();
+            }
         }
 
         // ---------------- pick phase (W2 registers are free here: reloaded below)
@@ -563,31 +594,32 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                 int xk = -1;
                 float pdx = NAN, sM = NAN, sS = NAN;
                 if (s_prev[j] >= 0) {
-                    // q's partials of every granule, polled until all carry this position
-                    const int g0 = min(t * FUSED_PER, NG), g1 = min(g0 + FUSED_PER, NG);
-                    const uint64_t* row = opaque(f.part) + (size_t)q * NG * FUSED_PART_WORDS;
+                    // q's partials of every granule, polled until all carry
+                    // this position; thread t reads granules t + 256 i
+                    const size_t plane = (size_t)R * NG;
+                    const uint64_t* rm = opaque(f.part) + (size_t)q * NG;
                     float gm[FUSED_PER], gs[FUSED_PER];
                     uint32_t gi[FUSED_PER];
                     for (int spin = 0;; ++spin) {
                         bool ok = true;
 #pragma unroll
                         for (int i = 0; i < FUSED_PER; ++i) {
+                            const int gg = t + i * TILE_THREADS;
                             gm[i] = -INFINITY;
                             gs[i] = 0.0f;
                             gi[i] = 0u;
-                            if (g0 + i < g1) {
-                                const uint64_t* sl = row + (size_t)(g0 + i) * FUSED_PART_WORDS;
-                                const uint64_t a0 = ld_dev(sl), a1 = ld_dev(sl + 1);
-                                const uint64_t a2 = GREEDY ? ld_dev(sl + 2) : tagged(0u, tag);
+                            if (gg < NG) {
+                                const uint64_t a0 = ld_dev(rm + gg), a1 = ld_dev(rm + plane + gg);
+                                const uint64_t a2 = GREEDY ? ld_dev(rm + 2 * plane + gg) : tagged(0u, tag);
                                 ok &= tag_of(a0) == tag && tag_of(a1) == tag && tag_of(a2) == tag;
                                 gm[i] = __uint_as_float((uint32_t)a0);
                                 gs[i] = __uint_as_float((uint32_t)a1);
                                 gi[i] = (uint32_t)a2;
                             }
                         }
-                        const bool ab = t == 0 && ld_dev(f.abort_flag) == abort_word(epoch);
+                        const bool ab = look_abort(spin) && ld_dev(f.abort_flag) == abort_word(epoch);
                         if (__syncthreads_and(ok)) break;
-                        if (poll_failed(spin, ab, epoch, f.abort_flag, p.status)) {
+                        if (poll_failed<1>(spin, ab, epoch, f.abort_flag, p.status)) {
                             failed = true;
                             break;
                         }
@@ -597,42 +629,64 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
 #pragma unroll
                     for (int i = 0; i < FUSED_PER; ++i) mloc = fmaxf(mloc, gm[i]);
                     const float M = block_max(mloc, s_red);
-                    float wv[FUSED_PER], tsum = 0.0f;
+                    // weights; per-round totals (round i = granules 256 i ..
+                    // 256 i + 255, in thread order) through LDS
+                    float wv[FUSED_PER];
 #pragma unroll
                     for (int i = 0; i < FUSED_PER; ++i) {
                         wv[i] = gs[i] * softw(gm[i], M, p.c);  // padding: 0 * 0
-                        tsum += wv[i];
+                        const float rs = wave_sum(wv[i]);
+                        if (lane == 0) s_round[w][i] = rs;
                     }
-                    float S;
-                    const float excl = block_excl_scan(tsum, s_red, S);
+                    __syncthreads();
+                    float tot[FUSED_PER], S = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < FUSED_PER; ++i) {
+                        tot[i] = 0.0f;
+#pragma unroll
+                        for (int v = 0; v < TILE_THREADS / WAVE; ++v) tot[i] += s_round[v][i];
+                        S += tot[i];
+                    }
+                    sM = M;
+                    sS = S;
                     if (GREEDY) {
                         int cand = 0x7fffffff;
 #pragma unroll
                         for (int i = FUSED_PER - 1; i >= 0; --i)
-                            if (g0 + i < g1 && gm[i] == M) cand = (int)gi[i];
+                            if (t + i * TILE_THREADS < NG && gm[i] == M) cand = (int)gi[i];
                         xk = block_min(cand, s_ired);
-                        sM = M;
+                        pdx = 1.0f / S;
                     } else {
-                        sM = M;
-                        sS = S;
                         const float target = u24f(philox((uint32_t)k, (uint32_t)q, f.round, f.seed).w[0]) * S;
-                        // first granule of positive mass whose running sum exceeds target
-                        float run = excl, prev = excl;
-                        int pick = -1, lastpos = -1;
+                        // the round where the running sum first exceeds target
+                        float pre = 0.0f;
+                        int rstar = -1;
+                        float rbase = 0.0f;
 #pragma unroll
                         for (int i = 0; i < FUSED_PER; ++i) {
-                            if (wv[i] > 0.0f) lastpos = g0 + i;
-                            if (pick < 0) {
-                                prev = run;
-                                run += wv[i];
-                                if (run > target && wv[i] > 0.0f) pick = g0 + i;
+                            if (rstar < 0 && tot[i] > 0.0f && pre + tot[i] > target) {
+                                rstar = i;
+                                rbase = pre;
                             }
+                            pre += tot[i];
                         }
-                        const int first = block_min(pick >= 0 ? t : 0x7fffffff, s_ired);
+                        // inside it, the first granule of positive mass crossing target
+                        float wr = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < FUSED_PER; ++i)
+                            if (i == rstar) wr = wv[i];
+                        float rtot;
+                        const float excl = rbase + block_excl_scan(wr, s_red, rtot);
+                        const bool hit = rstar >= 0 && wr > 0.0f && excl + wr > target;
+                        const int first = block_min(hit ? t : 0x7fffffff, s_ired);
+                        int lastpos = -1;
+#pragma unroll
+                        for (int i = 0; i < FUSED_PER; ++i)
+                            if (wv[i] > 0.0f) lastpos = t + i * TILE_THREADS;
                         const int lastp = -block_min(-lastpos, s_ired);
                         if (t == first) {
-                            s_gstar = pick;
-                            s_before = prev;
+                            s_gstar = t + rstar * TILE_THREADS;
+                            s_before = excl;
                         }
                         __syncthreads();
                         const bool fallback = first == 0x7fffffff;
@@ -665,10 +719,6 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                             xk = gstar * GRAN + col;
                             pdx = e / S;
                         }
-                    }
-                    if (GREEDY) {
-                        sS = S;
-                        pdx = 1.0f / S;
                     }
                 }
                 // wave 0 publishes the token (copies in lanes 0..7) and
@@ -709,8 +759,8 @@ static void tile_grid(int nrows, int n_gran, int& bpc, int& n_chunks)
     n_chunks = (n_rb + bpc - 1) / bpc;
 }
 
-// Workgroups of k_propose_fused the current device holds at once (0 if it
-// cannot launch cooperatively); cached per device.
+// Workgroups of k_propose_fused the current device holds at once; cached
+// per device.
 template <typename WT, int KS, bool GREEDY>
 static int fused_capacity()
 {
@@ -720,13 +770,12 @@ static int fused_capacity()
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return 0;
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v == 0) {
-        int coop = 0, cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
+        int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_propose_fused<WT, KS, GREEDY>, TILE_THREADS,
                                                          0) != hipSuccess)
             per_cu = 0;
-        v = (coop ? per_cu * cus : 0) + 1;
+        v = per_cu * cus + 1;
         cache[dev].store(v, std::memory_order_relaxed);
     }
     return v - 1;
@@ -745,10 +794,13 @@ static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* 
     WsHeader* hdr = reinterpret_cast<WsHeader*>(a.status);
     f.epoch = &hdr->epoch;
     f.abort_flag = &hdr->abort;
-    void* args[] = {&f};
+    // A plain launch: the grid is no larger than what the device holds at
+    // once (fused_capacity), so on an otherwise free device every workgroup
+    // becomes resident; waits are bounded in any case.  (A cooperative launch
+    // gives the same guarantee formally but costs ~17 us per call here.)
     ProfScope ps("propose_fused", s);
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_propose_fused<WT, KS, GREEDY>),
-                                      dim3(t.n_gran), dim3(TILE_THREADS), args, 0, s);
+    hipLaunchKernelGGL((k_propose_fused<WT, KS, GREEDY>), dim3(t.n_gran), dim3(TILE_THREADS), 0, s, f);
+    return hipGetLastError();
 }
 
 template <typename WT, int KS>

@@ -293,7 +293,7 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
         __syncthreads();
         // read before the next block may overwrite s_tok (two barriers ahead)
         const bool valid = rc.req >= 0 && s_tok[er] >= 0;
-        stage_w1<WT, Ops::RS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
+        stage_w1<WT, Ops::RS, KS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
         __syncthreads();
         store_tile(sZ, A.mfma(sB, ks, lane), w, lane);
         __syncthreads();

@@ -87,9 +87,10 @@ enum spec_device_flag {
     SPEC_DEV_BAD_LENGTH = 2,      /* an l_r outside [0, gamma]                     */
     SPEC_DEV_BAD_CONFIDENCE = 4,  /* a confidence outside [0, 1] (or NaN)          */
     SPEC_DEV_WAIT_FAILED = 8      /* the fused propose gave up waiting for another
-                                     workgroup (the GPU was shared and not all of
-                                     its workgroups ran at once); outputs of that
-                                     call are undefined                          */
+                                     of its workgroups (not all of them could run
+                                     at once: e.g. two fused calls on different
+                                     streams of one GPU); that call's outputs are
+                                     undefined                                    */
 };
 
 /* Limits: 1 <= R <= 65536, 1 <= gamma <= 64, 16 <= r <= 512 (r % 16 == 0;
@@ -138,14 +139,19 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2p, int w_d
                         int32_t* x, float* pd_x, float* pd_stats,
                         void* ws, size_t ws_bytes, spec_stream_t stream);
 
-/* Propose runs in one of two ways, with the same results up to fp32
- * summation order.  Fused: one cooperative launch for all gamma positions;
- * each workgroup keeps the W2 columns of one 128-id granule in registers for
- * the whole call, so W2 is read from HBM once.  It is taken when every
- * granule's workgroup fits on the device at once, r fills the matrix-core
- * k-steps exactly (r = 64, 128, 256 or 512 for bf16; 16, 64 or 256 for
- * fp32), R <= 64 and the switch below is on.  Otherwise: two kernels per
- * position (partials, then the pick), W2 streamed once per position.
+/* Propose runs in one of two ways; tokens agree except at decisions within
+ * fp32 rounding of a boundary (the logits are computed with the same
+ * operands, the sums in a different order).  Fused: one launch for all gamma
+ * positions; each workgroup keeps the W2 columns of one 128-id granule in
+ * registers for the whole call, so W2 is read from HBM once, and workgroups
+ * hand partials and tokens to each other through device memory.  It is taken
+ * when every granule's workgroup fits on the device at once, r fills the
+ * matrix-core k-steps exactly (r = 64, 128, 256 or 512 for bf16; 16, 64 or
+ * 256 for fp32), R <= 32 and the switch below is on.  Concurrent fused calls
+ * on different streams of one GPU can starve each other of workgroup slots
+ * and end with SPEC_DEV_WAIT_FAILED (after about a second); issue them on one
+ * stream.  Otherwise: two kernels per position (partials, then the pick), W2
+ * streamed once per position.
  * spec_set_propose_fused(0) forces the per-position kernels for every later
  * call in the process (1 restores the default); returns the previous value.
  * Not synchronised with calls running in other threads. */

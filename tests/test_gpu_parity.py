@@ -27,7 +27,7 @@ SMALL = {
     "fp32_r256": Config("fp32_r256", 14, 6, 3, 3000, 256, False, 1.0, 2.0, 0.05, 0.5),
     "tiny_vocab": Config("tiny_vocab", 15, 9, 5, 7, 16, True, 1.0, 1.0, 0.3, 0.5),
     "one_token": Config("one_token", 16, 2, 3, 1, 16, True, 1.0, 1.0, 0.3, 0.5),
-    # shapes the fused (single cooperative launch) propose takes: r fills the
+    # shapes the fused (single launch) propose takes: r fills the
     # k-steps, R <= 32; a ragged request count; more requests than granules
     "fused_r256": Config("fused_r256", 17, 29, 7, 5000, 256, True, 1.0, 3.0, 0.02, 1.0),
     "fused_many_req": Config("fused_many_req", 18, 30, 4, 300, 64, True, 1.0, 2.0, 0.1, 0.7),
