@@ -303,6 +303,61 @@ __device__ inline int wave_granule_find(WF wf, int g0, int g1, float excl, float
     return lp < 0 ? 0 : lp;
 }
 
+// Register-cached inverse CDF over at most 64 NR granule masses, one wave.
+// Lane l holds w[i] = mass of granule l + 64 i (0 past the end): the caller
+// loads all of them at once (coalesced, one memory round trip).  Round i
+// covers granules 64 i .. 64 i + 63 in lane order, so the rounds in order
+// are the granules in vocabulary order.  Returns the first granule of
+// positive mass whose running sum exceeds u * total, the running sum before
+// it and the total, identical in every lane; if rounding leaves none, the
+// last granule with positive mass (fallback set).
+template <int NR>
+__device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& total, float& before, bool& fallback)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    float T[NR];
+    float Z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        T[i] = wave_sum(w[i]);
+        Z += T[i];
+    }
+    total = Z;
+    const float target = u * Z;
+    float pre = 0.0f, rbase = 0.0f;
+    int rstar = -1;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        if (rstar < 0 && T[i] > 0.0f && pre + T[i] > target) {
+            rstar = i;
+            rbase = pre;
+        }
+        pre += T[i];
+    }
+    float wr = 0.0f;
+    int lastpos = -1;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        if (i == rstar) wr = w[i];
+        if (w[i] > 0.0f) lastpos = lane + WAVE * i;
+    }
+    const float incl = wave_incl_scan(wr);
+    float ex = __shfl_up(incl, 1, WAVE);
+    if (lane == 0) ex = 0.0f;
+    const float run0 = rbase + ex;
+    const unsigned long long hit = __ballot(rstar >= 0 && wr > 0.0f && run0 + wr > target);
+    if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        fallback = false;
+        before = __shfl(run0, L, WAVE);
+        return L + WAVE * rstar;
+    }
+    fallback = true;
+    before = 0.0f;
+    const int lp = -wave_min(-lastpos);
+    return lp < 0 ? 0 : lp;
+}
+
 // Inside one granule, run by a single full wave: lane l holds the weights of
 // ids 2l and 2l+1 of the granule.  Picks the first id whose running sum
 // (from `before`) exceeds target; if none (rounding, or `fallback`), the

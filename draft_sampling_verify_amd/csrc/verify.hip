@@ -101,7 +101,7 @@ struct TargetArgs {
 // per lane, DPP reductions) and writes its (max, sum of 2^((L-max)c),
 // argmax); a running (max, sum, argmax) per group then folds into the row's
 // (M_t, S_t, argmax) at the end, so no separate merge pass is needed.
-constexpr int TROW_THREADS = 512;
+constexpr int TROW_THREADS = 1024;
 constexpr int TROW_GRANS = TROW_THREADS / 8;  // granules per step
 
 __global__ __launch_bounds__(TROW_THREADS) void k_target_rows(TargetArgs p)
@@ -336,6 +336,62 @@ struct ResolveArgs {
     uint32_t* status;
 };
 
+// One wave, over the granule records of one verified row: the total TV mass
+// (for c*) and the residual draw with uniform u.  Lane l reads granules
+// l + 64 i, all at once; rows of more than 64 NR granules take the looped
+// scan instead.
+template <int NR>
+__device__ inline int resid_pick_cached(const float2* vp, int n, float u, float& Z, float& before, bool& fallback,
+                                        float& tv)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    float w[NR];
+    float tl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int g = lane + WAVE * i;
+        const float2 v = g < n ? vp[g] : make_float2(0.0f, 0.0f);
+        w[i] = v.y;
+        tl += v.x;
+    }
+    tv = wave_sum(tl);
+    return wave_rounds_pick(w, u, Z, before, fallback);
+}
+
+__device__ inline int resid_pick(const float2* vp, int n, float u, float& Z, float& before, bool& fallback,
+                                 float& tv)
+{
+    if (n <= 16 * WAVE) return resid_pick_cached<16>(vp, n, u, Z, before, fallback, tv);
+    if (n <= 32 * WAVE) return resid_pick_cached<32>(vp, n, u, Z, before, fallback, tv);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int per = (n + WAVE - 1) / WAVE;
+    const int g0 = min(lane * per, n), g1 = min(g0 + per, n);
+    float sm = 0.0f;
+    for (int g = g0; g < g1; ++g) sm += vp[g].x;
+    tv = wave_sum(sm);
+    auto wf = [&](int g) { return vp[g].y; };
+    float excl;
+    wave_granule_scan(wf, g0, g1, excl, Z);
+    before = 0.0f;
+    fallback = true;
+    return Z > 0.0f ? wave_granule_find(wf, g0, g1, excl, u * Z, before, fallback) : 0;
+}
+
+template <int NR>
+__device__ inline int target_pick_cached(const float2* gs, int n, float M, float c, float u, float& S, float& before,
+                                         bool& fallback)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    float w[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int g = lane + WAVE * i;
+        const float2 v = g < n ? gs[g] : make_float2(-INFINITY, 0.0f);
+        w[i] = v.y * softw(v.x, M, c);  // past the end: 0 * 0
+    }
+    return wave_rounds_pick(w, u, S, before, fallback);
+}
+
 // Draw from target row `trow` (data row (req, kk) of Lt) by inverse CDF with
 // uniform u: granule masses from the first pass, then one granule rescan.
 // One wave.
@@ -346,15 +402,23 @@ __device__ inline int draw_target_row(const ResolveArgs& a, int trow, int req, i
     const float2* gs = a.tgran + (size_t)trow * p.n_gran;
     const float M = p.trow[trow].x;
     const float c = p.c;
-    const int per = (p.n_gran + WAVE - 1) / WAVE;
-    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
-    auto wf = [&](int g) { const float2 v = gs[g]; return v.y * softw(v.x, M, c); };
-    float excl, S;
-    wave_granule_scan(wf, g0, g1, excl, S);
-    const float target = u * S;
-    float before;
+    const int n = p.n_gran;
+    float S, before;
     bool fallback;
-    const int gstar = wave_granule_find(wf, g0, g1, excl, target, before, fallback);
+    int gstar;
+    if (n <= 16 * WAVE) {
+        gstar = target_pick_cached<16>(gs, n, M, c, u, S, before, fallback);
+    } else if (n <= 32 * WAVE) {
+        gstar = target_pick_cached<32>(gs, n, M, c, u, S, before, fallback);
+    } else {
+        const int per = (n + WAVE - 1) / WAVE;
+        const int g0 = min(lane * per, n), g1 = min(g0 + per, n);
+        auto wf = [&](int g) { const float2 v = gs[g]; return v.y * softw(v.x, M, c); };
+        float excl;
+        wave_granule_scan(wf, g0, g1, excl, S);
+        gstar = wave_granule_find(wf, g0, g1, excl, u * S, before, fallback);
+    }
+    const float target = u * S;
     const float* L = p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V;
     const int ca = gstar * GRAN + 2 * lane, cb = ca + 1;
     const float za = ca < p.V ? L[ca] : -INFINITY, zb = cb < p.V ? L[cb] : -INFINITY;
@@ -362,14 +426,18 @@ __device__ inline int draw_target_row(const ResolveArgs& a, int trow, int req, i
     return gstar * GRAN + granule_pick(softw(za, M, c), softw(zb, M, c), before, target, fallback, e);
 }
 
-// One workgroup of four waves per request.
+// One workgroup of eight waves per request.
 // Phase 1 does everything that does not depend on which position is rejected
 // first, in parallel: the accept test of every verified position (one thread
 // each, fp64 on the drafted id), c* of every position and the residual
 // granule search of every position (one wave each), and the bonus draw.
-// Phase 2 rescans one granule of the first rejected position's residual.
+// Phase 2 rescans one granule of the first rejected position's residual
+// (waves 0-3, one 32-id column block each).
+constexpr int RES_THREADS = 512;
+constexpr int RES_WAVES = RES_THREADS / WAVE;
+
 template <typename WT, int KS, bool GREEDY>
-__global__ __launch_bounds__(TILE_THREADS) void k_verify_resolve(ResolveArgs a)
+__global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
 {
     const SweepArgs& p = a.s;
     const int r = blockIdx.x, t = threadIdx.x;
@@ -424,35 +492,22 @@ __global__ __launch_bounds__(TILE_THREADS) void k_verify_resolve(ResolveArgs a)
         if (a.c_star) a.c_star[(size_t)r * G + t] = NAN;
     }
     // ---- phase 1b: per position, one wave: c* and the residual granule search
-    const int per = (p.n_gran + WAVE - 1) / WAVE;
-    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
-    for (int k = w + 1; k <= L; k += TILE_THREADS / WAVE) {
+    for (int k = w + 1; k <= L; k += RES_WAVES) {
         const float2* vp = p.vpart + (size_t)(voff + k - 1) * p.n_gran;
-        if (a.c_star) {
-            float sm = 0.0f;
-            for (int g = g0; g < g1; ++g) sm += vp[g].x;
-            sm = wave_sum(sm);
-            if (lane == 0) a.c_star[(size_t)r * G + k - 1] = fminf(fmaxf(1.0f - 0.5f * sm, 0.0f), 1.0f);
-        }
-        if (!GREEDY) {
-            auto wf = [&](int g) { return vp[g].y; };
-            float excl, Z;
-            wave_granule_scan(wf, g0, g1, excl, Z);
-            const float u2 = u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[2]);
-            float before = 0.0f;
-            bool fallback = true;
-            int gs = 0;
-            if (Z > 0.0f) gs = wave_granule_find(wf, g0, g1, excl, u2 * Z, before, fallback);
-            if (lane == 0) {
-                s_g[k - 1] = gs;
-                s_before[k - 1] = before;
-                s_fb[k - 1] = fallback;
-                s_Z[k - 1] = Z;
-            }
+        const float u2 = u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[2]);
+        float Z, before, tv;
+        bool fallback;
+        const int gs = resid_pick(vp, p.n_gran, u2, Z, before, fallback, tv);
+        if (lane == 0) {
+            if (a.c_star) a.c_star[(size_t)r * G + k - 1] = fminf(fmaxf(1.0f - 0.5f * tv, 0.0f), 1.0f);
+            s_g[k - 1] = Z > 0.0f ? gs : 0;
+            s_before[k - 1] = Z > 0.0f ? before : 0.0f;
+            s_fb[k - 1] = Z > 0.0f ? fallback : true;
+            s_Z[k - 1] = Z;
         }
     }
-    // ---- phase 1c: the bonus draw after a full accept (wave L % 4)
-    if (w == L % (TILE_THREADS / WAVE)) {
+    // ---- phase 1c: the bonus draw after a full accept (wave L % 8)
+    if (w == L % RES_WAVES) {
         int yb;
         if (GREEDY) {
             yb = a.targ[toff + L];
@@ -484,34 +539,36 @@ __global__ __launch_bounds__(TILE_THREADS) void k_verify_resolve(ResolveArgs a)
     } else if (GREEDY) {
         if (t == 0) s_y = a.targ[toff + kstar - 1];
     } else if (s_Z[kstar - 1] > 0.0f) {
-        // wave w recomputes column block w of granule gstar for row f: the
+        // waves 0-3 recompute column block w of granule gstar for row f: the
         // W2 block, the W1 row of x_{k*-1}, U and the target row
-        const int f = voff + kstar - 1;
         const int gstar = s_g[kstar - 1];
-        const int nrows = p.vmap ? p.counts[0] : p.max_rows;
-        const int n = lane & 31, h = lane >> 5;
-        const int nf = f & (BLOCK_ROWS - 1);
-        const int ks = k_steps<WT>(p.r);
-        const int b = 4 * gstar + w;
-        const int c0 = gstar * GRAN + 32 * w;
-        const bool v4 = (p.V % 4) == 0;
-        const int xp = kstar == 1 ? x0r : p.x[(size_t)r * G + kstar - 2];
-        typename TileOps<WT, KS>::BRow brow;
-        brow.load(reinterpret_cast<const WT*>(p.W1), p.r, n == nf ? xp : -1, ks, lane);
-        float uu[16], ll[16];
-        load_acc16(p.U + ((size_t)r * G + kstar - 1) * p.V, c0, h, p.V, v4, uu);
-        load_acc16(p.Lt + ((size_t)r * (G + 1) + kstar - 1) * p.V, c0, h, p.V, v4, ll);
-        const RowCtx rc = row_ctx(p, f, nrows);
-        TileOps<WT, KS> A;
-        A.load_a(p.W2p, ks, b, b < (p.V + 31) / 32, lane);
-        const f32x16 acc = A.mfma_row(brow, ks);
-        if (n == nf) {
+        if (w < 4) {
+            const int f = voff + kstar - 1;
+            const int nrows = p.vmap ? p.counts[0] : p.max_rows;
+            const int n = lane & 31, h = lane >> 5;
+            const int nf = f & (BLOCK_ROWS - 1);
+            const int ks = k_steps<WT>(p.r);
+            const int b = 4 * gstar + w;
+            const int c0 = gstar * GRAN + 32 * w;
+            const bool v4 = (p.V % 4) == 0;
+            const int xp = kstar == 1 ? x0r : p.x[(size_t)r * G + kstar - 2];
+            typename TileOps<WT, KS>::BRow brow;
+            brow.load(reinterpret_cast<const WT*>(p.W1), p.r, n == nf ? xp : -1, ks, lane);
+            float uu[16], ll[16];
+            load_acc16(p.U + ((size_t)r * G + kstar - 1) * p.V, c0, h, p.V, v4, uu);
+            load_acc16(p.Lt + ((size_t)r * (G + 1) + kstar - 1) * p.V, c0, h, p.V, v4, ll);
+            const RowCtx rc = row_ctx(p, f, nrows);
+            TileOps<WT, KS> A;
+            A.load_a(p.W2p, ks, b, b < (p.V + 31) / 32, lane);
+            const f32x16 acc = A.mfma_row(brow, ks);
+            if (n == nf) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int col = c0 + 8 * (j >> 2) + 4 * h + (j & 3);
-                float d;
-                zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] =
-                    col < p.V ? resid(uu[j], acc[j], ll[j], rc, p.c, d) : 0.0f;
+                for (int j = 0; j < 16; ++j) {
+                    const int col = c0 + 8 * (j >> 2) + 4 * h + (j & 3);
+                    float d;
+                    zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] =
+                        col < p.V ? resid(uu[j], acc[j], ll[j], rc, p.c, d) : 0.0f;
+                }
             }
         }
         __syncthreads();
@@ -659,9 +716,9 @@ static hipError_t verify_impl(const DraftArgs& a, const float* pd_stats, const f
     {
         ProfScope ps("verify_resolve", s);
         if (a.greedy)
-            hipLaunchKernelGGL((k_verify_resolve<WT, KS, true>), dim3(a.R), dim3(TILE_THREADS), 0, s, ra);
+            hipLaunchKernelGGL((k_verify_resolve<WT, KS, true>), dim3(a.R), dim3(RES_THREADS), 0, s, ra);
         else
-            hipLaunchKernelGGL((k_verify_resolve<WT, KS, false>), dim3(a.R), dim3(TILE_THREADS), 0, s, ra);
+            hipLaunchKernelGGL((k_verify_resolve<WT, KS, false>), dim3(a.R), dim3(RES_THREADS), 0, s, ra);
     }
     return hipGetLastError();
 }
