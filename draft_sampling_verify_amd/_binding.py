@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libspec.so")
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH, SPEC_EDEVICE, SPEC_EUNSUPPORTED = range(7)
 SPEC_F32, SPEC_BF16 = 0, 1
-SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE = range(4)
+SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE, SPEC_OP_ROUNDS = range(5)
 SPEC_DEV_BAD_TOKEN, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_CONFIDENCE, SPEC_DEV_WAIT_FAILED = 1, 2, 4, 8
 
 
@@ -43,6 +43,7 @@ _SIGS = {
     "spec_verify": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
     "spec_confidence": ([P, P, P, I, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P], I),
     "spec_schedule": ([P, I, I, P, I, P, P, P, P, P, SZ, P], I),
+    "spec_decode_rounds": ([P, P, P, I, P, P, I, I, I, I, F, I, U64, U64, I, P, P, P, P, P, P, SZ, P], I),
     "spec_status_str": ([I], ctypes.c_char_p),
     "spec_set_propose_fused": ([I], I),
     "spec_profile_enable": ([I], I),
@@ -152,7 +153,7 @@ class Workspace:
 
     def __init__(self, R, gamma, r, V, B_max=0, device=None):
         need = max(spec_workspace_bytes(op, R, gamma, r, V, max(B_max, R))
-                   for op in (SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE))
+                   for op in (SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_ROUNDS))
         if need == 0:
             raise SpecError(SPEC_EINVAL, "Workspace")
         self.tensor = torch.empty(need, dtype=torch.uint8, device=device or "cuda")
@@ -228,6 +229,35 @@ def spec_verify(U, W1, W2p, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=
                            _stream(stream))
     _check(st, "spec_verify")
     return n_acc, y, pt_x, c_star
+
+
+def spec_decode_rounds(U, W1, W2p, x0, Lt, T, n_rounds, greedy=False, seed=1, round0=0, want_c_star=False,
+                       anchors=None, x=None, n_acc=None, y=None, c_star=None, ws=None, stream=None):
+    """n_rounds propose + verify rounds on the device, each round's anchors
+    being the previous round's last emitted tokens.  Returns (anchors
+    [n+1, R], x [n, R, gamma], n_acc [n, R], y [n, R, gamma+1], c_star or
+    None)."""
+    R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
+    dev = U.device
+    n = int(n_rounds)
+    _need(Lt, (R, gamma + 1, V), torch.float32, "Lt")
+    _need(anchors, (n + 1, R), torch.int32, "anchors")
+    _need(x, (n, R, gamma), torch.int32, "x")
+    _need(n_acc, (n, R), torch.int32, "n_acc")
+    _need(y, (n, R, gamma + 1), torch.int32, "y")
+    _need(c_star, (n, R, gamma), torch.float32, "c_star")
+    anchors = torch.empty((n + 1, R), dtype=torch.int32, device=dev) if anchors is None else anchors
+    x = torch.empty((n, R, gamma), dtype=torch.int32, device=dev) if x is None else x
+    n_acc = torch.empty((n, R), dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    y = torch.empty((n, R, gamma + 1), dtype=torch.int32, device=dev) if y is None else y
+    if c_star is None and want_c_star:
+        c_star = torch.empty((n, R, gamma), dtype=torch.float32, device=dev)
+    ws = _ws(ws, R, gamma, r, V, dev)
+    st = lib().spec_decode_rounds(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(Lt), R, gamma, r, V,
+                                  float(T), int(bool(greedy)), int(seed), int(round0), n, _ptr(anchors), _ptr(x),
+                                  _ptr(n_acc), _ptr(y), _ptr(c_star), ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "spec_decode_rounds")
+    return anchors, x, n_acc, y, c_star
 
 
 def spec_confidence(U, W1, W2p, x0, x, Lt, T, pd_stats=None, c_star=None, a_star=None, want_a_star=True,

@@ -54,6 +54,28 @@ DraftArgs make_args(const float* U, const void* W1, const void* W2, int w_dtype,
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH; }
 
+// spec_decode_rounds keeps each round's p_d(x) and (M, S) after the larger of
+// the propose and verify regions (verify reads what propose wrote).
+size_t rounds_scratch_offset(size_t propose_bytes, size_t verify_bytes)
+{
+    return spec::align256(propose_bytes > verify_bytes ? propose_bytes : verify_bytes);
+}
+
+__global__ void k_copy_words(const int32_t* src, int32_t* dst, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
+// Next anchor of every request: the token it emitted last.
+__global__ void k_next_anchor(const int32_t* n_acc, const int32_t* y, int R, int gamma, int32_t* next)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= R) return;
+    const int n = n_acc[i];
+    next[i] = (n >= 0 && n <= gamma) ? y[(size_t)i * (gamma + 1) + n] : -1;
+}
+
 __global__ void k_zero_words(uint32_t* p, size_t n)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -126,6 +148,13 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
             return 0;
         spec::carve_verify(nullptr, R, gamma, V, op == SPEC_OP_CONFIDENCE, &bytes);
         return bytes;
+    case SPEC_OP_ROUNDS: {
+        const size_t pb = spec_workspace_bytes(SPEC_OP_PROPOSE, R, gamma, r, V, B_max);
+        const size_t vb = spec_workspace_bytes(SPEC_OP_VERIFY, R, gamma, r, V, B_max);
+        if (!pb || !vb) return 0;
+        return rounds_scratch_offset(pb, vb) + spec::align256((size_t)R * gamma * 4) +
+               spec::align256((size_t)R * gamma * 8);
+    }
     case SPEC_OP_SCHEDULE:
         if (R < 1 || gamma < 1 || (long)R * gamma > spec::SCHED_MAX_ENTRIES || B_max < R) return 0;
         return spec::WS_HEADER;
@@ -225,6 +254,46 @@ int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
     DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, 0, 0, 0, ws);
     return launch_status(
         spec::launch_confidence(a, pd_stats, Lt, c_star, a_star, w, (hipStream_t)stream));
+}
+
+int spec_decode_rounds(const float* U, const void* W1, const void* W2p, int w_dtype, const int32_t* x0,
+                       const float* Lt, int R, int gamma, int r, int V, float T, int greedy, uint64_t seed,
+                       uint64_t round0, int n_rounds, int32_t* anchors, int32_t* x, int32_t* n_acc, int32_t* y,
+                       float* c_star, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    int st = check_draft(U, W1, W2p, w_dtype, x0, R, gamma, r, V, T);
+    if (st != SPEC_OK) return st;
+    if (n_rounds < 1) return SPEC_EINVAL;
+    if (R > 0 && (!Lt || !anchors || !x || !n_acc || !y)) return SPEC_EINVAL;
+    if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
+    const size_t need = spec_workspace_bytes(SPEC_OP_ROUNDS, R, gamma, r, V, 0);
+    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_OK;
+    const size_t off = rounds_scratch_offset(spec_workspace_bytes(SPEC_OP_PROPOSE, R, gamma, r, V, 0),
+                                             spec_workspace_bytes(SPEC_OP_VERIFY, R, gamma, r, V, 0));
+    float* pd_x = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+    float* pd_stats = reinterpret_cast<float*>(static_cast<char*>(ws) + off + spec::align256((size_t)R * gamma * 4));
+    hipStream_t s = (hipStream_t)stream;
+    const int nb = (R + 255) / 256;
+    hipLaunchKernelGGL(k_copy_words, dim3(nb), dim3(256), 0, s, x0, anchors, R);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    for (int i = 0; i < n_rounds; ++i) {
+        const int32_t* a_i = anchors + (size_t)i * R;
+        int32_t* x_i = x + (size_t)i * R * gamma;
+        int32_t* n_i = n_acc + (size_t)i * R;
+        int32_t* y_i = y + (size_t)i * R * (gamma + 1);
+        float* c_i = c_star ? c_star + (size_t)i * R * gamma : nullptr;
+        st = spec_markov_propose(U, W1, W2p, w_dtype, a_i, R, gamma, r, V, T, greedy, seed, round0 + i, x_i, pd_x,
+                                 pd_stats, ws, ws_bytes, stream);
+        if (st != SPEC_OK) return st;
+        st = spec_verify(U, W1, W2p, w_dtype, a_i, x_i, pd_stats, Lt, nullptr, R, gamma, r, V, T, greedy, seed,
+                         round0 + i, n_i, y_i, nullptr, c_i, ws, ws_bytes, stream);
+        if (st != SPEC_OK) return st;
+        hipLaunchKernelGGL(k_next_anchor, dim3(nb), dim3(256), 0, s, n_i, y_i, R, gamma,
+                           anchors + (size_t)(i + 1) * R);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    }
+    return SPEC_OK;
 }
 
 int spec_schedule(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* ell, double* a,

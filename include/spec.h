@@ -79,7 +79,13 @@ enum spec_status {
 
 enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
 
-enum spec_op { SPEC_OP_PROPOSE = 0, SPEC_OP_VERIFY = 1, SPEC_OP_CONFIDENCE = 2, SPEC_OP_SCHEDULE = 3 };
+enum spec_op {
+    SPEC_OP_PROPOSE = 0,
+    SPEC_OP_VERIFY = 1,
+    SPEC_OP_CONFIDENCE = 2,
+    SPEC_OP_SCHEDULE = 3,
+    SPEC_OP_ROUNDS = 4  /* spec_decode_rounds */
+};
 
 /* Bits of the device status word. */
 enum spec_device_flag {
@@ -156,6 +162,30 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2p, int w_d
  * call in the process (1 restores the default); returns the previous value.
  * Not synchronised with calls running in other threads. */
 int spec_set_propose_fused(int enable);
+
+/* Several speculative rounds back to back on the device: the loop around
+ * one step.  Round i (Philox round round0 + i) drafts gamma tokens from the
+ * anchors a_i (spec_markov_propose), verifies all of them (spec_verify,
+ * every position, c* optional), and the next anchor of each request is the
+ * token it emitted last, y_i[r][n_acc_i[r]]: the correction after a
+ * rejection or the bonus after a full accept (the bonus token is the next
+ * round's first prediction position; DSpark section 1 cycle, section 3
+ * anchor).  U and Lt are the same every round (they stand in for the
+ * per-round backbone and target logits).  Nothing returns to the host
+ * between rounds and the enqueued work contains no synchronisation, host
+ * copy or memset, so the whole sequence can be captured in a HIP graph.
+ * In:  U, W1, W2p, w_dtype, Lt, sizes, T, greedy, seed as for the two calls;
+ *      x0 [R] the first anchors; n_rounds >= 1.
+ * Out: anchors [n_rounds + 1, R] (anchors[0] = x0; -1 after an invalid
+ *      token); x [n_rounds, R, gamma]; n_acc [n_rounds, R];
+ *      y [n_rounds, R, gamma + 1]; c_star [n_rounds, R, gamma] or NULL.
+ * ws: spec_workspace_bytes(SPEC_OP_ROUNDS, ...) bytes (it also holds each
+ * round's p_d(x) and (M, S)). */
+int spec_decode_rounds(const float* U, const void* W1, const void* W2p, int w_dtype,
+                       const int32_t* x0, const float* Lt, int R, int gamma, int r, int V,
+                       float T, int greedy, uint64_t seed, uint64_t round0, int n_rounds,
+                       int32_t* anchors, int32_t* x, int32_t* n_acc, int32_t* y, float* c_star,
+                       void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Verify drafts against target logits (standard lossless rule):
  *   for k = 1..l_r: accept x_k iff u1 < p_t,k(x_k) / p_k(x_k) (greedy: iff

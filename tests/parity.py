@@ -83,6 +83,8 @@ def check_propose(d, x, pd_x, pd_stats, greedy, seed=1, rnd=0):
         u = oracle.u24(int(oracle.draw(seed, rnd, int(d["req_ids"][i]), int(k) + 1)[0]))
         assert near_boundary(p, int(x[i, k]), u), (i, k)
     ok = ~mism
+    if pd_x is None:                 # tokens only (callers that keep no probabilities)
+        return dict(decisions=int(x.size), excluded=int(mism.sum()), low_margin=int(low.sum()))
     np.testing.assert_allclose(pd_x[ok], o["pd_x"][ok], rtol=0, atol=PROB_TOL)
     M, S = pd_stats[..., 0], pd_stats[..., 1]
     np.testing.assert_allclose(M[ok], o["pd_stats"][..., 0][ok], rtol=0,

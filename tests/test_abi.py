@@ -138,6 +138,23 @@ def test_verify_confidence_schedule_validation(L):
     assert L.spec_schedule(*s5) == d.SPEC_EINVAL                           # ell required
 
 
+def test_decode_rounds_validation(L):
+    import draft_sampling_verify_amd as d
+    F = FAKE
+    need = d.spec_workspace_bytes(d.SPEC_OP_ROUNDS, 4, 4, 16, 1024)
+    assert need > max(d.spec_workspace_bytes(d.SPEC_OP_PROPOSE, 4, 4, 16, 1024),
+                      d.spec_workspace_bytes(d.SPEC_OP_VERIFY, 4, 4, 16, 1024))
+    args = [F, F, F, 1, F, F, 4, 4, 16, 1024, 1.0, 0, 1, 0, 3, F, F, F, F, None, F, need, None]
+    a0 = list(args); a0[14] = 0
+    assert L.spec_decode_rounds(*a0) == d.SPEC_EINVAL                       # n_rounds
+    a1 = list(args); a1[21] = need - 1
+    assert L.spec_decode_rounds(*a1) == d.SPEC_EWORKSPACE
+    a2 = list(args); a2[15] = None
+    assert L.spec_decode_rounds(*a2) == d.SPEC_EINVAL                       # anchors required
+    a3 = list(args); a3[5] = ctypes.c_void_p(4100)
+    assert L.spec_decode_rounds(*a3) == d.SPEC_EINVAL                       # Lt misaligned
+
+
 def test_binding_rejects_bad_shapes_without_a_gpu():
     import torch
     import draft_sampling_verify_amd as d
