@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--propose-path", choices=["auto", "per_position"], default="auto",
                     help="auto: the fused single-launch propose where it fits; per_position: two kernels "
                          "per draft position")
+    ap.add_argument("--rounds", type=int, default=8,
+                    help="rounds of the multi-round loop measured after the main steps (0 = skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=512,
                     help="size of the device-to-device copy timed as the achievable-bandwidth reference")
     args = ap.parse_args()
@@ -228,6 +230,54 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = 2.0 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del src, dst
+    # the multi-round loop: n rounds of propose + verify (c* included), each
+    # round anchored on the previous round's last emitted tokens, eager and
+    # replayed from one captured HIP graph
+    multi = None
+    if args.rounds > 0 and not args.profile_only:
+        n = args.rounds
+        rb = dict(anchors=torch.empty((n + 1, R), dtype=torch.int32, device=dev),
+                  x=torch.empty((n, R, g), dtype=torch.int32, device=dev),
+                  n_acc=torch.empty((n, R), dtype=torch.int32, device=dev),
+                  y=torch.empty((n, R, g + 1), dtype=torch.int32, device=dev),
+                  c_star=torch.empty((n, R, g), dtype=torch.float32, device=dev))
+
+        def rounds(i, strm):
+            spec.spec_decode_rounds(U, W1, W2p, x0, Lt, cfg.T, n, False, 1, 1000 + i * n, ws=ws, stream=strm, **rb)
+
+        reps = max(3, args.steps // (2 * n))
+        rounds(0, stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            rounds(i, stream)
+        torch.cuda.synchronize()
+        eager_s = (time.perf_counter() - t0) / reps
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            rounds(0, side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            rounds(0, torch.cuda.current_stream())
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_s = (time.perf_counter() - t0) / reps
+        emitted = float((rb["n_acc"].float() + 1.0).sum())
+        multi = {"rounds": n, "repetitions": reps,
+                 "ms_per_round_eager": round(1000.0 * eager_s / n, 4),
+                 "ms_per_round_graph": round(1000.0 * graph_s / n, 4),
+                 "verified_draft_tokens_per_s_graph": round(R * g * n / graph_s, 1),
+                 "emitted_tokens_per_round": round(emitted / n, 2),
+                 "emitted_tokens_per_s_graph": round(emitted / graph_s, 1)}
+        del graph
+
     acc = float(n_acc.float().mean())
     cmean = float(c_star.float().mean())
     flags = spec.spec_device_status(ws)
@@ -271,6 +321,7 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "ms_per_step_with_kernel_events": round(1000.0 * elapsed_prof / args.steps, 4),
         "kernels": kernels,
+        "multi_round": multi,
         "mean_n_acc": round(acc, 4),
         "mean_c_star": round(cmean, 4),
         "device_status": flags,
