@@ -46,6 +46,7 @@ _SIGS = {
     "spec_decode_rounds": ([P, P, P, I, P, P, I, I, I, I, F, I, U64, U64, I, P, P, P, P, P, P, SZ, P], I),
     "spec_status_str": ([I], ctypes.c_char_p),
     "spec_set_propose_fused": ([I], I),
+    "spec_set_verify_lds": ([I], I),
     "spec_profile_enable": ([I], I),
     "spec_profile_reset": ([], I),
     "spec_profile_read": ([ctypes.c_char_p, P, P], I),
@@ -307,6 +308,14 @@ def spec_set_propose_fused(enable: bool) -> bool:
     """Process-wide: allow (True, the default) or forbid the fused propose
     launch; returns the previous setting."""
     return bool(lib().spec_set_propose_fused(int(bool(enable))))
+
+
+def spec_set_verify_lds(enable: bool) -> bool:
+    """Process-wide: allow (True, the default) or forbid the pipelined
+    verify sweep (W1 rows gathered straight into LDS by half of each
+    workgroup, U and target rows streamed by the other half); returns the
+    previous setting."""
+    return bool(lib().spec_set_verify_lds(int(bool(enable))))
 
 
 def spec_profile_enable(on=True):

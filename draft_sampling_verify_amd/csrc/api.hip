@@ -102,6 +102,11 @@ std::atomic<int> g_fused{1};
 }
 int set_propose_fused(int enable) { return g_fused.exchange(enable ? 1 : 0); }
 int propose_fused_enabled() { return g_fused.load(); }
+namespace {
+std::atomic<int> g_sweep_lds{1};
+}
+int set_sweep_lds(int enable) { return g_sweep_lds.exchange(enable ? 1 : 0); }
+int sweep_lds_enabled() { return g_sweep_lds.load(); }
 
 ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s)
 {
@@ -164,6 +169,7 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
 }
 
 int spec_set_propose_fused(int enable) { return spec::set_propose_fused(enable); }
+int spec_set_verify_lds(int enable) { return spec::set_sweep_lds(enable); }
 
 int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream)
 {

@@ -681,31 +681,51 @@ template <> __host__ __device__ inline int k_steps<float>(int r) { return r / 8;
 // (r <= 16 KS bf16 or 8 KS fp32 elements, 2 KS uint4); every thread issues
 // all of its loads before its first LDS write, so the gather costs one
 // memory round trip.
+// The gather in two halves, so that a caller can issue other loads between
+// them: issue() starts every W1 load of this thread, commit() writes them to
+// LDS (and so waits for them, but not for loads issued after issue()).
+template <typename WT, int RS, int KS>
+struct W1Gather {
+    static constexpr int ELEM = (int)sizeof(WT);
+    static constexpr int NPT = (32 * 2 * KS + TILE_THREADS - 1) / TILE_THREADS;
+    uint4 v[NPT];
+    uint32_t keep[NPT];
+
+    __device__ inline void issue(const WT* W1, const int* tok, int r)
+    {
+        const int per_row = r * ELEM / 16;  // uint4 per row
+        const int total = 32 * per_row;
+        const int t0 = opaque_v(threadIdx.x);
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int idx = min(t0 + i * TILE_THREADS, total - 1);  // duplicates store the same value
+            const int row = idx / per_row, c = idx - row * per_row;
+            const int tk = tok[row];
+            keep[i] = tk >= 0 ? ~0u : 0u;
+            v[i] = reinterpret_cast<const uint4*>(W1 + (size_t)(tk >= 0 ? tk : 0) * r)[c];
+        }
+    }
+    __device__ inline void commit(void* sB, int r) const
+    {
+        const int per_row = r * ELEM / 16;
+        const int total = 32 * per_row;
+        const int t0 = opaque_v(threadIdx.x);
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int idx = min(t0 + i * TILE_THREADS, total - 1);
+            const int row = idx / per_row, c = idx - row * per_row;
+            const uint4 m = make_uint4(v[i].x & keep[i], v[i].y & keep[i], v[i].z & keep[i], v[i].w & keep[i]);
+            *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sB) + (size_t)row * RS * ELEM + 16 * c) = m;
+        }
+    }
+};
+
 template <typename WT, int RS, int KS>
 __device__ inline void stage_w1(void* sB, const WT* W1, const int* tok, int r)
 {
-    constexpr int ELEM = (int)sizeof(WT);
-    constexpr int NPT = (32 * 2 * KS + TILE_THREADS - 1) / TILE_THREADS;
-    const int per_row = r * ELEM / 16;  // uint4 per row
-    const int total = 32 * per_row;
-    const int t0 = opaque_v(threadIdx.x);
-    uint4 v[NPT];
-    uint32_t keep[NPT];
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const int idx = min(t0 + i * TILE_THREADS, total - 1);  // duplicates store the same value
-        const int row = idx / per_row, c = idx - row * per_row;
-        const int tk = tok[row];
-        keep[i] = tk >= 0 ? ~0u : 0u;
-        v[i] = reinterpret_cast<const uint4*>(W1 + (size_t)(tk >= 0 ? tk : 0) * r)[c];
-    }
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const int idx = min(t0 + i * TILE_THREADS, total - 1);
-        const int row = idx / per_row, c = idx - row * per_row;
-        const uint4 m = make_uint4(v[i].x & keep[i], v[i].y & keep[i], v[i].z & keep[i], v[i].w & keep[i]);
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sB) + (size_t)row * RS * ELEM + 16 * c) = m;
-    }
+    W1Gather<WT, RS, KS> gw;
+    gw.issue(W1, tok, r);
+    gw.commit(sB, r);
 }
 
 // stage_w1 for r that fills the k-steps exactly (2 KS uint4 per row): every
@@ -800,6 +820,49 @@ __device__ inline void load16(const float* row, int c0, int V, bool vec4, float 
 #pragma unroll
         for (int e = 0; e < 16; ++e) v[e] = (c0 + e < V) ? row[c0 + e] : -INFINITY;
     }
+}
+
+// load16 without branches (the compiler then counts this thread's loads
+// exactly, so a later wait on an earlier load does not also wait for these):
+// indices clamped into the row, ids past V replaced by -inf.  c0 is a
+// multiple of 16; VEC4 requires V % 4 == 0.
+// The loads of load16_flat without the masking: ids past V hold whatever the
+// clamped load returned, and the caller masks them where it uses them (so
+// that nothing touches the loaded registers before then).
+template <bool VEC4>
+__device__ inline void load16_raw(const float* row, int c0, int V, float (&v)[16])
+{
+    if constexpr (VEC4) {
+        const float4* p4 = reinterpret_cast<const float4*>(row);
+        const int q0 = c0 >> 2, qmax = (V >> 2) - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 a = p4[min(q0 + j, qmax)];
+            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = row[min(c0 + e, V - 1)];
+    }
+}
+
+template <bool VEC4>
+__device__ inline void load16_flat(const float* row, int c0, int V, float (&v)[16])
+{
+    if constexpr (VEC4) {
+        const float4* p4 = reinterpret_cast<const float4*>(row);
+        const int q0 = c0 >> 2, qmax = (V >> 2) - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 a = p4[min(q0 + j, qmax)];
+            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = row[min(c0 + e, V - 1)];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = c0 + e < V ? v[e] : -INFINITY;
 }
 
 // Reductions across the 8 lanes that share an epilogue row, on DPP (no LDS

@@ -114,6 +114,10 @@ inline ProposeWs carve_propose(void* ws, int R, int V, size_t* bytes)
 // where the fused launch fits (returns the previous value).
 int set_propose_fused(int enable);
 int propose_fused_enabled();
+// Process-wide switch: 0 keeps the verify sweep on the register-staged
+// kernel even where the pipelined direct-to-LDS one applies.
+int set_sweep_lds(int enable);
+int sweep_lds_enabled();
 
 // Arguments common to the draft-side kernels.
 struct DraftArgs {

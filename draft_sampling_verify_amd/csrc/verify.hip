@@ -22,6 +22,8 @@
 //                     granule rescan.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -256,7 +258,88 @@ __device__ inline float resid(float zu, float bias, float zt, const RowCtx& rc, 
     return fmaxf(d, 0.0f);
 }
 
-template <typename WT, int KS>
+// What a verified row's epilogue needs, as loaded (no arithmetic on the
+// loaded values, so that the loads can be issued one block ahead without the
+// compiler waiting for them at once).  Rows past the end load row 0's data
+// and carry ok = false.  MAPS: the row map is in memory (scheduled lengths),
+// else implicit.
+struct RowRaw {
+    int4 vi;
+    int xk;
+    float md, sd;
+    float2 ts;
+    bool ok;
+};
+
+template <bool MAPS>
+__device__ inline int4 vrow_at(const SweepArgs& p, int f)
+{
+    if constexpr (MAPS) return p.vmap[f];
+    const int r = f / p.gamma, kk = f - r * p.gamma;
+    return make_int4(r, kk + 1, r * p.P + kk, 0);
+}
+
+template <bool MAPS>
+__device__ inline RowRaw row_raw(const SweepArgs& p, int f, int nrows)
+{
+    RowRaw w;
+    w.ok = f < nrows;
+    w.vi = vrow_at<MAPS>(p, w.ok ? f : 0);
+    const size_t so = (size_t)w.vi.x * p.gamma + w.vi.y - 1;
+    w.xk = p.x[so];
+    w.md = p.dstats[2 * so];
+    w.sd = p.dstats[2 * so + 1];
+    w.ts = p.trow[w.vi.z];
+    return w;
+}
+
+// The same RowCtx as row_ctx() computes.
+__device__ inline RowCtx row_finish(const RowRaw& w)
+{
+    RowCtx rc;
+    rc.req = w.ok ? w.vi.x : -1;
+    rc.k = w.vi.y;
+    rc.trow = w.vi.z;
+    rc.xk = w.xk;
+    rc.Md = w.md;
+    rc.iSd = 1.0f / w.sd;
+    rc.Mt = w.ts.x;
+    rc.iSt = 1.0f / w.ts.y;
+    return rc;
+}
+
+// The two tokens row_tok() checks, as loaded: (x_{k-1}, x_k); (-1, -1) past
+// the end.  Both loads are unconditional (x_{k-1} of position 1 is x0).
+template <bool MAPS>
+__device__ inline int2 tok_raw(const SweepArgs& p, int f, int nrows)
+{
+    const bool ok = f < nrows;
+    const int4 vi = vrow_at<MAPS>(p, ok ? f : 0);
+    const size_t so = (size_t)vi.x * p.gamma + vi.y - 1;
+    const int* src = vi.y == 1 ? p.x0 + vi.x : p.x + (so - 1);
+    // masked with an opaque value rather than a select, so that the compiler
+    // does not move the loads under a branch
+    const int om = opaque_v(ok ? 0 : -1);
+    return make_int2(*src | om, p.x[so] | om);
+}
+
+__device__ inline int tok_check(int2 tx, int V)
+{
+    return (tx.x < 0 || tx.x >= V || tx.y < 0 || tx.y >= V) ? -1 : tx.x;
+}
+
+// One workgroup per (granule, chunk of 32-row blocks); W2's 128 x r slice of
+// the granule stays in registers (the MFMA A operand) for the whole chunk.
+// Per block: W1 rows of the 32 tokens are gathered into LDS, the 32 x 128
+// bias tile is computed on MFMA into LDS, and each 8-lane group combines one
+// row's bias with its U and target logits.  The loads are ordered so that
+// the dependent chain (tokens -> W1 rows -> MFMA) never waits for the
+// streamed U and target rows: right after the W1 gather is issued come this
+// block's U and target loads and then the next block's tokens and row
+// context, so the LDS write of W1 waits for W1 alone and the rest stays in
+// flight through the MFMA.  (Loads are counted in issue order, so this needs
+// straight-line code: no branch around any of these loads.)
+template <typename WT, int KS, bool VEC4, bool MAPS>
 __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
 {
     using Ops = TileOps<WT, KS>;
@@ -264,7 +347,10 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
     const int lid = xcd_logical(blockIdx.x, nlog);
     if (lid >= nlog) return;
     const int g = lid / p.n_chunks, chunk = lid - g * p.n_chunks;
-    const int nrows = p.vmap ? p.counts[0] : p.max_rows;
+    const int nrows = MAPS ? p.counts[0] : p.max_rows;
+    const int rb0 = chunk * p.bpc;
+    const int nb = min(p.bpc, (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS - rb0);
+    if (nb <= 0) return;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const int ks = k_steps<WT>(p.r);
     const int nblk = (p.V + 31) / 32;
@@ -278,22 +364,25 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
 
     const int er = t >> 3, ec = (t & 7) * 16;
     const int cbase = g * GRAN + ec;
-    for (int b = 0; b < p.bpc; ++b) {
-        const int rb = chunk * p.bpc + b;
-        if (rb * BLOCK_ROWS >= nrows) break;
-        // the epilogue row's data do not depend on the tokens: issue them first
-        const int f = rb * BLOCK_ROWS + er;
-        const RowCtx rc = row_ctx(p, f, nrows);
-        float zu[16], zt[16];
-        if (rc.req >= 0) {
-            load16(p.U + ((size_t)rc.req * p.gamma + rc.k - 1) * p.V, cbase, p.V, p.vec4, zu);
-            load16(p.Lt + ((size_t)rc.req * (p.gamma + 1) + rc.k - 1) * p.V, cbase, p.V, p.vec4, zt);
-        }
-        if (t < 32) s_tok[t] = row_tok(p, rb * BLOCK_ROWS + t, nrows);
+    // every lane loads a token pair (lanes 32-63 repeat 0-31): no branch
+    int2 tx = tok_raw<MAPS>(p, rb0 * BLOCK_ROWS + (t & 31), nrows);
+    RowRaw rw = row_raw<MAPS>(p, rb0 * BLOCK_ROWS + er, nrows);
+    for (int b = 0; b < nb; ++b) {
+        const int f = (rb0 + b) * BLOCK_ROWS + er;
+        if (t < 32) s_tok[t] = tok_check(tx, p.V);
+        const RowCtx rc = row_finish(rw);
+        const int req = rw.vi.x, kk = rw.vi.y;  // row 0's data when the row is past the end
+        // s_tok written; the previous block's epilogue is done with sZ
         __syncthreads();
-        // read before the next block may overwrite s_tok (two barriers ahead)
         const bool valid = rc.req >= 0 && s_tok[er] >= 0;
-        stage_w1<WT, Ops::RS, KS>(sB, reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
+        W1Gather<WT, Ops::RS, KS> gw;
+        gw.issue(reinterpret_cast<const WT*>(p.W1), s_tok, p.r);
+        float zu[16], zt[16];
+        load16_flat<VEC4>(p.U + ((size_t)req * p.gamma + kk - 1) * p.V, cbase, p.V, zu);
+        load16_flat<VEC4>(p.Lt + ((size_t)req * (p.gamma + 1) + kk - 1) * p.V, cbase, p.V, zt);
+        tx = tok_raw<MAPS>(p, (rb0 + b + 1) * BLOCK_ROWS + (t & 31), nrows);
+        rw = row_raw<MAPS>(p, f + BLOCK_ROWS, nrows);
+        gw.commit(sB, p.r);
         __syncthreads();
         store_tile(sZ, A.mfma(sB, ks, lane), w, lane);
         __syncthreads();
@@ -317,6 +406,255 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
             if (rc.xk >= cbase && rc.xk < cbase + 16) p.vbias[f] = zr[rc.xk - cbase];
         }
     }
+}
+
+// The sweep for bf16 weights whose W1 rows fill the k-steps exactly (r =
+// 128, 256, 512).  The W1 rows of a block are gathered by direct
+// global-to-LDS loads (no registers involved) one block ahead, into the
+// other half of a double-buffered tile, so the gather of block b+1 is in
+// flight during block b's MFMA and epilogue.  A direct load writes 16 bytes
+// per lane at consecutive LDS addresses from a per-wave base, so each load
+// moves one W1 row with half a wave (32 lanes x 16 bytes = 512 bytes at
+// r = 256; longer rows take several loads) and the tile keeps the padded row
+// stride of TileOps (RS elements), which spreads the rows of an operand read
+// over the LDS banks.
+template <int KS>
+struct LdsW1 {
+    using Ops = TileOps<bf16w, KS>;
+    static constexpr int ROW = 32 * KS;                   // bytes per W1 row
+    static constexpr int STRIDE = Ops::RS * Ops::ELEM;    // bytes per LDS row
+    static constexpr int BYTES = 32 * STRIDE;             // one 32-row tile
+    static constexpr int PARTS = ROW / 512;               // 512-byte loads per row
+    static constexpr int PER_WAVE = 32 * PARTS / 4;       // loads per wave per tile
+    static_assert(ROW % 512 == 0 || ROW == 256, "W1 rows of 256, 512 or 1024 bytes");
+
+    // Gather W1[tok[n]] for the 32 rows into buf (tok < 0: row 0, whose
+    // values the caller ignores).  Load j of the workgroup moves part j %
+    // PARTS of row j / PARTS.  At r = 128 (256-byte rows) the half wave
+    // covers two rows: lanes 16-31 write the second row at the padded
+    // stride's offset, which a single contiguous load cannot do, so there
+    // each load takes one row with a quarter wave instead.
+    __device__ static inline void gather(__attribute__((address_space(3))) char* buf, const bf16w* W1,
+                                         const int* tok, int w, int lane)
+    {
+        if constexpr (ROW == 256) {
+            // 8 loads per wave, lanes 0-15 active: 16 x 16 bytes = one row
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 8 * w + i;
+                const int tk = tok[row];
+                if (lane < 16) {
+                    const uint4* src = reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * 16 + lane;
+                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE, 16, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const int j = w * PER_WAVE + i;
+                const int row = j / PARTS, part = j % PARTS;
+                const int tk = tok[row];
+                if (lane < 32) {
+                    const uint4* src =
+                        reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * (2 * KS) + 32 * part + lane;
+                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE + 512 * part, 16, 0, 0);
+                }
+            }
+        }
+    }
+};
+
+// Direct load of one 32-bit value per active lane: lane l of the calling
+// wave writes dst[l] (the callers keep lanes 32-63 inactive).
+__device__ inline void dma32(const void* src, __attribute__((address_space(3))) void* dst)
+{
+    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+// The direct-to-LDS sweep, for the implicit row map (every position of every
+// request verified), with the work of a block split between two groups of
+// four waves that run one stage apart:
+//   MFMA waves (0-3)      hold W2's granule slice (the A operand) and, in
+//                         stage s, gather block s+1's W1 rows into LDS,
+//                         compute block s's 32 x 128 bias tile into LDS and
+//                         store block s-2's results;
+//   epilogue waves (4-7)  hold U and target rows of two blocks in registers
+//                         and, in stage s, finish block s-1 (p_d, p_t, the
+//                         TV and residual masses, the bias at x_k) into LDS
+//                         while block s's rows are in flight, then issue
+//                         block s+1's loads.
+// One barrier per stage.  The epilogue waves issue nothing but their own
+// row loads, so each of their waits is for the older block only and the
+// newer one stays in flight across the barrier; the MFMA waves wait for all
+// of theirs before it.  Per-row values go through LDS by direct loads, one
+// stage ahead: the raw row context (x_k, the draft's (M, S), the target's
+// (M, S)) and, two blocks ahead, the token pairs from which the W1 rows are
+// chosen.
+template <int KS, bool VEC4>
+__global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepArgs p)
+{
+    using Ops = TileOps<bf16w, KS>;
+    using SW = LdsW1<KS>;
+    typedef __attribute__((address_space(3))) char lchar;
+    const int nlog = p.n_gran * p.n_chunks;
+    const int lid = xcd_logical(blockIdx.x, nlog);
+    if (lid >= nlog) return;
+    const int g = lid / p.n_chunks, chunk = lid - g * p.n_chunks;
+    const int nrows = p.max_rows;
+    const int rb0 = chunk * p.bpc;
+    const int nb = min(p.bpc, (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS - rb0);
+    if (nb <= 0) return;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
+
+    // buffers of even and odd blocks
+    __shared__ __align__(16) char sB0[SW::BYTES], sB1[SW::BYTES];  // W1 tiles
+    __shared__ __align__(16) float sZ0[32 * ZS], sZ1[32 * ZS];     // bias tiles
+    __shared__ int s_tok[4][32];                                    // checked tokens, block b in b & 3
+    __shared__ int s_tr[2][2][32];                                  // raw (x_{k-1}, x_k)
+    __shared__ int s_xk[2][32];                                     // raw x_k
+    __shared__ float s_cf[2][4][32];                                // raw M_d, S_d, M_t, S_t
+    __shared__ float2 s_part[2][32];                                // results: (TV, residual) mass
+    __shared__ float s_bx[2][32];                                   // results: bias at x_k
+    __shared__ int s_has[2][32];                                    // x_k in this granule
+    __shared__ int s_ok[2][32];                                     // row exists, tokens valid
+    auto L = [](void* q) { return (lchar*)q; };
+    auto rel_row = [&](int b, int i) { return (rb0 + b) * BLOCK_ROWS + i; };
+
+    // blocks 0 and 1: tokens (plain loads, needed at once); block 2: raw
+    // tokens by direct loads.  Rows past the end load row 0's values and are
+    // masked where used.
+    if (t < 64) {
+        const int q = rel_row(t >> 5, t & 31);
+        s_tok[t >> 5][t & 31] = q < nrows ? tok_check(tok_raw<false>(p, q, nrows), p.V) : -1;
+    }
+    auto load_tokens = [&](int b, int (*tr)[32]) __attribute__((always_inline)) {
+        const int q = rel_row(b, lane), qc = q < nrows ? q : 0;
+        const int r = qc / p.gamma, kk = qc - r * p.gamma;
+        dma32(kk == 0 ? p.x0 + r : p.x + (qc - 1), L(tr[0]));
+        dma32(p.x + qc, L(tr[1]));
+    };
+    if (t < 32) load_tokens(2, s_tr[0]);
+    // stage s computes block s's tile (s < nb), finishes block s-1 and
+    // stores block s-2's results: stages 0..nb+1, rounded up to an even
+    // count (the loops below take stages in pairs)
+    const int n_stages = (nb + 3) & ~1;
+
+    if (w < 4) {
+        // ------------------------------------------------ MFMA waves
+        // the A operand, in flight with the token loads
+        Ops A;
+        A.load_a(p.W2p, KS, 4 * g + w, 4 * g + w < (p.V + 31) / 32, lane);
+        stores_done();
+        __syncthreads();
+        SW::gather(L(sB0), W1, s_tok[0], w, lane);
+        stores_done();
+        __syncthreads();
+        auto load_ctx = [&](int b) __attribute__((always_inline)) {
+            const int q = rel_row(b, lane), qc = q < nrows ? q : 0;
+            const int r = qc / p.gamma, kk = qc - r * p.gamma;
+            // target row (r, kk) of the first pass: P rows per request
+            const float* ts = reinterpret_cast<const float*>(p.trow) + 2 * ((size_t)r * p.P + kk);
+            dma32(p.x + qc, L(s_xk[b & 1]));
+            dma32(p.dstats + 2 * (size_t)qc, L(s_cf[b & 1][0]));
+            dma32(p.dstats + 2 * (size_t)qc + 1, L(s_cf[b & 1][1]));
+            dma32(ts, L(s_cf[b & 1][2]));
+            dma32(ts + 1, L(s_cf[b & 1][3]));
+        };
+        // stage s; bcur/zcur hold block s, bnxt block s+1 (fixed per call, so
+        // the compiler can tell the MFMA's LDS reads from the direct loads in
+        // flight and does not wait for them)
+        auto stage = [&](char* bcur, char* bnxt, float* zcur, int s) __attribute__((always_inline)) {
+            if (t < 32) {
+                // block s+2's tokens (raw values landed last stage)
+                const int q = rel_row(s + 2, t);
+                s_tok[(s + 2) & 3][t] =
+                    q < nrows ? tok_check(make_int2(s_tr[s & 1][0][t], s_tr[s & 1][1][t]), p.V) : -1;
+            } else if (w == 2 && lane < 32 && s >= 2 && s - 2 < nb) {
+                // block s-2's results (finished last stage)
+                // (s_tok of block s-2 is being overwritten by wave 0 now)
+                const int e = s - 2, f = rel_row(e, lane);
+                if (s_ok[e & 1][lane]) {
+                    p.vpart[(size_t)f * p.n_gran + g] = s_part[e & 1][lane];
+                    if (s_has[e & 1][lane]) p.vbias[f] = s_bx[e & 1][lane];
+                }
+            }
+            if (s + 1 < nb) SW::gather(L(bnxt), W1, s_tok[(s + 1) & 3], w, lane);
+            if (t < 32) load_tokens(s + 3, s_tr[(s + 1) & 1]);
+            else if (w == 1 && lane < 32) load_ctx(s);
+            if (s < nb) store_tile(zcur, A.mfma_acc(bcur, lane, f32x16{}), w, lane);
+            stores_done();
+            __syncthreads();
+        };
+        for (int s = 0; s < n_stages; s += 2) {
+            stage(sB0, sB1, sZ0, s);
+            stage(sB1, sB0, sZ1, s + 1);
+        }
+    } else {
+        // ---------------------------------------------- epilogue waves
+        const int te = t - TILE_THREADS;
+        const int er = te >> 3, ec = (te & 7) * 16;
+        const int cbase = g * GRAN + ec;
+        // issue block b's U and target rows (b past the last block: the last
+        // block again, so the code stays free of branches around loads)
+        auto issue = [&](int b, float (&zu)[16], float (&zt)[16]) __attribute__((always_inline)) {
+            const int f = rel_row(min(b, nb - 1), er), fc = f < nrows ? f : 0;
+            const int req = fc / p.gamma, kk = fc - req * p.gamma;
+            load16_raw<VEC4>(p.U + (size_t)fc * p.V, cbase, p.V, zu);
+            load16_raw<VEC4>(p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V, cbase, p.V, zt);
+        };
+        float zuA[16], ztA[16], zuB[16], ztB[16];  // blocks of even / odd index
+        issue(0, zuA, ztA);
+        __syncthreads();
+        __syncthreads();
+        // stage s: finish block s-1 (rows in zu/zt, tile in zprev) into LDS,
+        // then refill zu/zt with block s+1
+        auto stage = [&](float (&zu)[16], float (&zt)[16], const float* zprev, int s) __attribute__((always_inline)) {
+            const int e = s - 1;
+            const bool ok = rel_row(e, er) < nrows && s_tok[e & 3][er] >= 0;
+            if (s >= 1 && s <= nb && (te & 7) == 0) s_ok[e & 1][er] = ok;
+            if (s >= 1 && s <= nb && ok) {
+                RowCtx rc;
+                rc.req = 0;
+                rc.xk = s_xk[e & 1][er];
+                rc.Md = s_cf[e & 1][0][er];
+                rc.iSd = 1.0f / s_cf[e & 1][1][er];
+                rc.Mt = s_cf[e & 1][2][er];
+                rc.iSt = 1.0f / s_cf[e & 1][3][er];
+                const float* zr = zprev + er * ZS + ec;
+                float tv = 0.0f, res = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
+                    const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        // ids past V as -inf (weight 0 on both sides)
+                        const bool in = cbase + 4 * q + k < p.V;
+                        float d;
+                        res += resid(in ? zu[4 * q + k] : -INFINITY, bb[k], in ? zt[4 * q + k] : -INFINITY, rc, p.c,
+                                     d);
+                        tv += fabsf(d);
+                    }
+                }
+                tv = oct_sum(tv);
+                res = oct_sum(res);
+                if ((te & 7) == 0) {
+                    s_part[e & 1][er] = make_float2(tv, res);
+                    s_has[e & 1][er] = rc.xk >= g * GRAN && rc.xk < g * GRAN + GRAN;
+                }
+                if (rc.xk >= cbase && rc.xk < cbase + 16) s_bx[e & 1][er] = zr[rc.xk - cbase];
+            }
+            issue(s + 1, zu, zt);
+            __syncthreads();
+        };
+        for (int s = 0; s < n_stages; s += 2) {
+            stage(zuB, ztB, sZ1, s);
+            stage(zuA, ztA, sZ0, s + 1);
+        }
+    }
+    // direct loads still in flight (blocks past this chunk) land before exit
+    stores_done();
 }
 
 // ------------------------------------------------------------- resolve
@@ -635,10 +973,13 @@ __global__ __launch_bounds__(TILE_THREADS) void k_conf_finalize(const float2* vp
 
 // ------------------------------------------------------------ launchers
 
-static void sweep_grid(int nrows, int n_gran, int& bpc, int& n_chunks)
+// Workgroups cover one granule and `bpc` consecutive 32-row blocks; the row
+// blocks are split into just enough chunks to give about `target`
+// workgroups.
+static void sweep_grid(int nrows, int n_gran, int& bpc, int& n_chunks, int target = 1024)
 {
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
-    n_chunks = (1024 + n_gran - 1) / n_gran;
+    n_chunks = (target + n_gran - 1) / n_gran;
     if (n_chunks > n_rb) n_chunks = n_rb;
     if (n_chunks < 1) n_chunks = 1;
     bpc = (n_rb + n_chunks - 1) / n_chunks;
@@ -679,6 +1020,49 @@ static hipError_t target_pass(const DraftArgs& a, const float* Lt, int P, int ma
     return hipGetLastError();
 }
 
+// Workgroups of k_verify_sweep_ws the current device holds at once (two
+// per CU: LDS and registers), cached per device.
+static int sweep_ws_target()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = 2 * cus;
+    }
+    return cached[dev];
+}
+
+template <typename WT, int KS>
+static void launch_sweep(const SweepArgs& sw, hipStream_t s)
+{
+    const dim3 grid(xcd_grid(sw.n_gran * sw.n_chunks));
+    const dim3 blk(TILE_THREADS);
+    if constexpr (std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16 || KS == 32)) {
+        if (sw.r == 16 * KS && !sw.vmap && sweep_lds_enabled()) {
+            // as many workgroups as fit at once, with the longest chunks
+            // that give that many (the pipeline fills and drains once per
+            // workgroup)
+            SweepArgs sw2 = sw;
+            sweep_grid(sw.max_rows, sw.n_gran, sw2.bpc, sw2.n_chunks, sweep_ws_target());
+            const dim3 grid2(xcd_grid(sw2.n_gran * sw2.n_chunks)), blk2(2 * TILE_THREADS);
+            if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), grid2, blk2, 0, s, sw2);
+            else hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), grid2, blk2, 0, s, sw2);
+            return;
+        }
+    }
+    if (sw.vmap) {
+        if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep<WT, KS, true, true>), grid, blk, 0, s, sw);
+        else hipLaunchKernelGGL((k_verify_sweep<WT, KS, false, true>), grid, blk, 0, s, sw);
+    } else {
+        if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep<WT, KS, true, false>), grid, blk, 0, s, sw);
+        else hipLaunchKernelGGL((k_verify_sweep<WT, KS, false, false>), grid, blk, 0, s, sw);
+    }
+}
+
 template <typename WT, int KS>
 static hipError_t verify_impl(const DraftArgs& a, const float* pd_stats, const float* Lt,
                               const int32_t* ell, int32_t* n_acc, int32_t* y, float* pt_x,
@@ -699,8 +1083,7 @@ static hipError_t verify_impl(const DraftArgs& a, const float* pd_stats, const f
     SweepArgs sw = make_sweep(a, pd_stats, Lt, P, w, counts, maps);
     {
         ProfScope ps("verify_sweep", s);
-        hipLaunchKernelGGL((k_verify_sweep<WT, KS>), dim3(xcd_grid(sw.n_gran * sw.n_chunks)),
-                           dim3(TILE_THREADS), 0, s, sw);
+        launch_sweep<WT, KS>(sw, s);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -740,8 +1123,7 @@ static hipError_t confidence_impl(const DraftArgs& a, const float* pd_stats, con
     SweepArgs sw = make_sweep(a, dstats, Lt, P, w, nullptr, false);
     {
         ProfScope ps("verify_sweep", s);
-        hipLaunchKernelGGL((k_verify_sweep<WT, KS>), dim3(xcd_grid(sw.n_gran * sw.n_chunks)),
-                           dim3(TILE_THREADS), 0, s, sw);
+        launch_sweep<WT, KS>(sw, s);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

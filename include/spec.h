@@ -163,6 +163,20 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2p, int w_d
  * Not synchronised with calls running in other threads. */
 int spec_set_propose_fused(int enable);
 
+/* The verify sweep (and spec_confidence's) recomputes the Markov bias of
+ * every verified row in 32-row blocks.  For bf16 weights with r = 128, 256
+ * or 512 and every position verified (ell == NULL, and always in
+ * spec_confidence) it runs as a software pipeline: half of each workgroup
+ * gathers W1 rows straight into on-chip memory one block ahead and computes
+ * the bias tiles on the matrix cores, the other half streams U and target
+ * rows two blocks ahead and finishes each block.  Otherwise the W1 rows are
+ * staged through registers and one workgroup does each block start to end.
+ * Both compute the same products in the same order (identical results).
+ * spec_set_verify_lds(0) forces the staged kernel for every later call in
+ * the process (1 restores the default); returns the previous value.  Not
+ * synchronised with calls running in other threads. */
+int spec_set_verify_lds(int enable);
+
 /* Several speculative rounds back to back on the device: the loop around
  * one step.  Round i (Philox round round0 + i) drafts gamma tokens from the
  * anchors a_i (spec_markov_propose), verifies all of them (spec_verify,

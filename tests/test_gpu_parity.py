@@ -31,6 +31,11 @@ SMALL = {
     # k-steps, R <= 32; a ragged request count; more requests than granules
     "fused_r256": Config("fused_r256", 17, 29, 7, 5000, 256, True, 1.0, 3.0, 0.02, 1.0),
     "fused_many_req": Config("fused_many_req", 18, 30, 4, 300, 64, True, 1.0, 2.0, 0.1, 0.7),
+    # the verify sweep that gathers W1 straight into LDS (bf16, r = 128 /
+    # 256 / 512): V % 4 != 0 with a ragged last block; several 32-row blocks
+    # per workgroup (its double-buffered gather)
+    "lds_r128_odd": Config("lds_r128_odd", 19, 37, 3, 1001, 128, True, 1.0, 2.0, 0.05, 0.5),
+    "lds_multi": Config("lds_multi", 20, 40, 7, 40000, 256, True, 1.0, 3.0, 0.02, 1.0),
 }
 
 
@@ -156,6 +161,44 @@ def test_propose_paths_agree_with_oracle(name):
         same = (outs[True, greedy] == outs[False, greedy]).mean()
         log("  token agreement between paths", "greedy" if greedy else "sampled", same)
         assert same > 0.9
+
+
+@pytest.mark.parametrize("name", ["lds_multi", "rank512", "lds_r128_odd"])
+def test_verify_sweep_paths_identical(name):
+    """The sweep that gathers W1 rows straight into LDS and the one that
+    stages them through registers compute the same products in the same
+    order: verify (fixed and scheduled lengths, sampled and greedy) and
+    confidence outputs are bit-identical, and match the oracle."""
+    cfg = SMALL[name]
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    x, pdx, pds = run_propose(t, cfg, False, ws=ws)
+    rng = np.random.default_rng(cfg.index + 100)
+    ell = rng.integers(0, cfg.gamma + 1, cfg.R).astype(np.int32)
+    ell_d = torch.from_numpy(ell).cuda()
+    outs = {}
+    prev = spec.spec_set_verify_lds(True)
+    try:
+        for lds in (True, False):
+            spec.spec_set_verify_lds(lds)
+            for greedy in (False, True):
+                for lens in (None, ell):
+                    res = run_verify(t, cfg, x, pds, greedy, ell=None if lens is None else ell_d, ws=ws)
+                    res = [np_(v) for v in res]
+                    st = check_verify(d, np_(x), lens, *res, greedy)
+                    log("  %s %s %s" % ("lds" if lds else "staged", "greedy" if greedy else "sampled",
+                                        "fixed" if lens is None else "scheduled"), st)
+                    outs[lds, greedy, lens is None] = res
+            cs, a = spec.spec_confidence(t["U"], t["W1"], t["W2p"], t["x0"], x, t["Lt"], cfg.T, pd_stats=pds, ws=ws)
+            torch.cuda.synchronize()
+            outs[lds, "conf"] = [np_(cs), np_(a)]
+    finally:
+        spec.spec_set_verify_lds(prev)
+    assert spec.spec_device_status(ws) == 0
+    for key in [k for k in outs if k[0]]:
+        for got, want in zip(outs[key], outs[(False,) + key[1:]]):
+            np.testing.assert_array_equal(got, want)
 
 
 def test_empty_batch_is_a_no_op():
