@@ -22,6 +22,7 @@
 //                     granule rescan.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -472,23 +473,27 @@ __device__ inline void dma32(const void* src, __attribute__((address_space(3))) 
 }
 
 // The direct-to-LDS sweep, for the implicit row map (every position of every
-// request verified), with the work of a block split between two groups of
-// four waves that run one stage apart:
+// request verified).  The work is a sequence of units, unit u = (granule
+// u / n_rb, 32-row block u % n_rb); each workgroup takes a contiguous run of
+// units (runs differ in length by at most one), so the pipeline below fills
+// and drains once per workgroup and W2 is reloaded only where the run
+// crosses into the next granule.  The work of a unit is split between two
+// groups of four waves that run one stage apart:
 //   MFMA waves (0-3)      hold W2's granule slice (the A operand) and, in
-//                         stage s, gather block s+1's W1 rows into LDS,
-//                         compute block s's 32 x 128 bias tile into LDS and
-//                         store block s-2's results;
-//   epilogue waves (4-7)  hold U and target rows of two blocks in registers
-//                         and, in stage s, finish block s-1 (p_d, p_t, the
-//                         TV and residual masses, the bias at x_k) into LDS
-//                         while block s's rows are in flight, then issue
-//                         block s+1's loads.
+//                         stage s, gather unit s+1's W1 rows into LDS,
+//                         compute unit s's 32 x 128 bias tile into LDS and
+//                         store unit s-2's results;
+//   epilogue waves (4-7)  hold U and target rows of two units in registers
+//                         and, in stage s, finish unit s-1 (p_d, p_t, the TV
+//                         and residual masses, the bias at x_k) into LDS
+//                         while unit s's rows are in flight, then issue
+//                         unit s+1's loads.
 // One barrier per stage.  The epilogue waves issue nothing but their own
-// row loads, so each of their waits is for the older block only and the
+// row loads, so each of their waits is for the older unit only and the
 // newer one stays in flight across the barrier; the MFMA waves wait for all
 // of theirs before it.  Per-row values go through LDS by direct loads, one
 // stage ahead: the raw row context (x_k, the draft's (M, S), the target's
-// (M, S)) and, two blocks ahead, the token pairs from which the W1 rows are
+// (M, S)) and, two units ahead, the token pairs from which the W1 rows are
 // chosen.
 template <int KS, bool VEC4>
 __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepArgs p)
@@ -496,21 +501,23 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
     using Ops = TileOps<bf16w, KS>;
     using SW = LdsW1<KS>;
     typedef __attribute__((address_space(3))) char lchar;
-    const int nlog = p.n_gran * p.n_chunks;
-    const int lid = xcd_logical(blockIdx.x, nlog);
-    if (lid >= nlog) return;
-    const int g = lid / p.n_chunks, chunk = lid - g * p.n_chunks;
     const int nrows = p.max_rows;
-    const int rb0 = chunk * p.bpc;
-    const int nb = min(p.bpc, (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS - rb0);
-    if (nb <= 0) return;
+    const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
+    const long NU = (long)p.n_gran * n_rb;
+    const int u0 = (int)((long)blockIdx.x * NU / gridDim.x);
+    const int nu = (int)((long)(blockIdx.x + 1) * NU / gridDim.x) - u0;
+    if (nu <= 0) return;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
+    // unit j of this run (j may pass the run's end: only tokens and row
+    // context are loaded for such units, and they are never used)
+    auto ugran = [&](int j) { return (u0 + j) / n_rb; };
+    auto urow = [&](int j, int i) { return ((u0 + j) % n_rb) * BLOCK_ROWS + i; };
 
-    // buffers of even and odd blocks
+    // buffers of even and odd units
     __shared__ __align__(16) char sB0[SW::BYTES], sB1[SW::BYTES];  // W1 tiles
     __shared__ __align__(16) float sZ0[32 * ZS], sZ1[32 * ZS];     // bias tiles
-    __shared__ int s_tok[4][32];                                    // checked tokens, block b in b & 3
+    __shared__ int s_tok[4][32];                                    // checked tokens, unit j in j & 3
     __shared__ int s_tr[2][2][32];                                  // raw (x_{k-1}, x_k)
     __shared__ int s_xk[2][32];                                     // raw x_k
     __shared__ float s_cf[2][4][32];                                // raw M_d, S_d, M_t, S_t
@@ -519,70 +526,80 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
     __shared__ int s_has[2][32];                                    // x_k in this granule
     __shared__ int s_ok[2][32];                                     // row exists, tokens valid
     auto L = [](void* q) { return (lchar*)q; };
-    auto rel_row = [&](int b, int i) { return (rb0 + b) * BLOCK_ROWS + i; };
 
-    // blocks 0 and 1: tokens (plain loads, needed at once); block 2: raw
+    // units 0 and 1: tokens (plain loads, needed at once); unit 2: raw
     // tokens by direct loads.  Rows past the end load row 0's values and are
     // masked where used.
     if (t < 64) {
-        const int q = rel_row(t >> 5, t & 31);
+        const int q = urow(t >> 5, t & 31);
         s_tok[t >> 5][t & 31] = q < nrows ? tok_check(tok_raw<false>(p, q, nrows), p.V) : -1;
     }
-    auto load_tokens = [&](int b, int (*tr)[32]) __attribute__((always_inline)) {
-        const int q = rel_row(b, lane), qc = q < nrows ? q : 0;
+    auto load_tokens = [&](int j, int (*tr)[32]) __attribute__((always_inline)) {
+        const int q = urow(j, lane), qc = q < nrows ? q : 0;
         const int r = qc / p.gamma, kk = qc - r * p.gamma;
         dma32(kk == 0 ? p.x0 + r : p.x + (qc - 1), L(tr[0]));
         dma32(p.x + qc, L(tr[1]));
     };
     if (t < 32) load_tokens(2, s_tr[0]);
-    // stage s computes block s's tile (s < nb), finishes block s-1 and
-    // stores block s-2's results: stages 0..nb+1, rounded up to an even
-    // count (the loops below take stages in pairs)
-    const int n_stages = (nb + 3) & ~1;
+    // stage s computes unit s's tile (s < nu), finishes unit s-1 and stores
+    // unit s-2's results: stages 0..nu+1, rounded up to an even count (the
+    // loops below take stages in pairs)
+    const int n_stages = (nu + 3) & ~1;
 
     if (w < 4) {
         // ------------------------------------------------ MFMA waves
-        // the A operand, in flight with the token loads
+        const int nblk = (p.V + 31) / 32;
+        // the A operand of unit 0's granule, in flight with the token loads
+        int ga = ugran(0);
         Ops A;
-        A.load_a(p.W2p, KS, 4 * g + w, 4 * g + w < (p.V + 31) / 32, lane);
+        A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
         stores_done();
         __syncthreads();
         SW::gather(L(sB0), W1, s_tok[0], w, lane);
         stores_done();
         __syncthreads();
-        auto load_ctx = [&](int b) __attribute__((always_inline)) {
-            const int q = rel_row(b, lane), qc = q < nrows ? q : 0;
+        auto load_ctx = [&](int j) __attribute__((always_inline)) {
+            const int q = urow(j, lane), qc = q < nrows ? q : 0;
             const int r = qc / p.gamma, kk = qc - r * p.gamma;
             // target row (r, kk) of the first pass: P rows per request
             const float* ts = reinterpret_cast<const float*>(p.trow) + 2 * ((size_t)r * p.P + kk);
-            dma32(p.x + qc, L(s_xk[b & 1]));
-            dma32(p.dstats + 2 * (size_t)qc, L(s_cf[b & 1][0]));
-            dma32(p.dstats + 2 * (size_t)qc + 1, L(s_cf[b & 1][1]));
-            dma32(ts, L(s_cf[b & 1][2]));
-            dma32(ts + 1, L(s_cf[b & 1][3]));
+            dma32(p.x + qc, L(s_xk[j & 1]));
+            dma32(p.dstats + 2 * (size_t)qc, L(s_cf[j & 1][0]));
+            dma32(p.dstats + 2 * (size_t)qc + 1, L(s_cf[j & 1][1]));
+            dma32(ts, L(s_cf[j & 1][2]));
+            dma32(ts + 1, L(s_cf[j & 1][3]));
         };
-        // stage s; bcur/zcur hold block s, bnxt block s+1 (fixed per call, so
+        // stage s; bcur/zcur hold unit s, bnxt unit s+1 (fixed per call, so
         // the compiler can tell the MFMA's LDS reads from the direct loads in
         // flight and does not wait for them)
         auto stage = [&](char* bcur, char* bnxt, float* zcur, int s) __attribute__((always_inline)) {
             if (t < 32) {
-                // block s+2's tokens (raw values landed last stage)
-                const int q = rel_row(s + 2, t);
+                // unit s+2's tokens (raw values landed last stage)
+                const int q = urow(s + 2, t);
                 s_tok[(s + 2) & 3][t] =
                     q < nrows ? tok_check(make_int2(s_tr[s & 1][0][t], s_tr[s & 1][1][t]), p.V) : -1;
-            } else if (w == 2 && lane < 32 && s >= 2 && s - 2 < nb) {
-                // block s-2's results (finished last stage)
-                // (s_tok of block s-2 is being overwritten by wave 0 now)
-                const int e = s - 2, f = rel_row(e, lane);
+            } else if (w == 2 && lane < 32 && s >= 2 && s - 2 < nu) {
+                // unit s-2's results (finished last stage; its s_tok entry is
+                // being overwritten by wave 0 now)
+                const int e = s - 2, f = urow(e, lane);
                 if (s_ok[e & 1][lane]) {
-                    p.vpart[(size_t)f * p.n_gran + g] = s_part[e & 1][lane];
+                    p.vpart[(size_t)f * p.n_gran + ugran(e)] = s_part[e & 1][lane];
                     if (s_has[e & 1][lane]) p.vbias[f] = s_bx[e & 1][lane];
                 }
             }
-            if (s + 1 < nb) SW::gather(L(bnxt), W1, s_tok[(s + 1) & 3], w, lane);
+            if (s + 1 < nu) SW::gather(L(bnxt), W1, s_tok[(s + 1) & 3], w, lane);
             if (t < 32) load_tokens(s + 3, s_tr[(s + 1) & 1]);
             else if (w == 1 && lane < 32) load_ctx(s);
-            if (s < nb) store_tile(zcur, A.mfma_acc(bcur, lane, f32x16{}), w, lane);
+            if (s < nu) {
+                store_tile(zcur, A.mfma_acc(bcur, lane, f32x16{}), w, lane);
+                // the next unit in another granule: its W2 slice, in flight
+                // until the barrier
+                const int gn = ugran(s + 1);
+                if (s + 1 < nu && gn != ga) {
+                    ga = gn;
+                    A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
+                }
+            }
             stores_done();
             __syncthreads();
         };
@@ -594,26 +611,30 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
         // ---------------------------------------------- epilogue waves
         const int te = t - TILE_THREADS;
         const int er = te >> 3, ec = (te & 7) * 16;
-        const int cbase = g * GRAN + ec;
-        // issue block b's U and target rows (b past the last block: the last
-        // block again, so the code stays free of branches around loads)
-        auto issue = [&](int b, float (&zu)[16], float (&zt)[16]) __attribute__((always_inline)) {
-            const int f = rel_row(min(b, nb - 1), er), fc = f < nrows ? f : 0;
+        // issue unit j's U and target rows (j past the run: its last unit
+        // again, so the code stays free of branches around loads)
+        auto issue = [&](int j, float (&zu)[16], float (&zt)[16]) __attribute__((always_inline)) {
+            const int jj = min(j, nu - 1);
+            const int f = urow(jj, er), fc = f < nrows ? f : 0;
             const int req = fc / p.gamma, kk = fc - req * p.gamma;
+            const int cbase = ugran(jj) * GRAN + ec;
             load16_raw<VEC4>(p.U + (size_t)fc * p.V, cbase, p.V, zu);
             load16_raw<VEC4>(p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V, cbase, p.V, zt);
         };
-        float zuA[16], ztA[16], zuB[16], ztB[16];  // blocks of even / odd index
+        float zuA[16], ztA[16], zuB[16], ztB[16];  // units of even / odd index
+        // (the first barrier before the loads: the wait before it covers the
+        // prologue's direct loads, and so any load issued ahead of it)
+        __syncthreads();
         issue(0, zuA, ztA);
         __syncthreads();
-        __syncthreads();
-        // stage s: finish block s-1 (rows in zu/zt, tile in zprev) into LDS,
-        // then refill zu/zt with block s+1
+        // stage s: finish unit s-1 (rows in zu/zt, tile in zprev) into LDS,
+        // then refill zu/zt with unit s+1
         auto stage = [&](float (&zu)[16], float (&zt)[16], const float* zprev, int s) __attribute__((always_inline)) {
             const int e = s - 1;
-            const bool ok = rel_row(e, er) < nrows && s_tok[e & 3][er] >= 0;
-            if (s >= 1 && s <= nb && (te & 7) == 0) s_ok[e & 1][er] = ok;
-            if (s >= 1 && s <= nb && ok) {
+            const int ge = ugran(e), cbase = ge * GRAN + ec;
+            const bool ok = urow(e, er) < nrows && s_tok[e & 3][er] >= 0;
+            if (s >= 1 && s <= nu && (te & 7) == 0) s_ok[e & 1][er] = ok;
+            if (s >= 1 && s <= nu && ok) {
                 RowCtx rc;
                 rc.req = 0;
                 rc.xk = s_xk[e & 1][er];
@@ -641,7 +662,7 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
                 res = oct_sum(res);
                 if ((te & 7) == 0) {
                     s_part[e & 1][er] = make_float2(tv, res);
-                    s_has[e & 1][er] = rc.xk >= g * GRAN && rc.xk < g * GRAN + GRAN;
+                    s_has[e & 1][er] = rc.xk >= ge * GRAN && rc.xk < ge * GRAN + GRAN;
                 }
                 if (rc.xk >= cbase && rc.xk < cbase + 16) s_bx[e & 1][er] = zr[rc.xk - cbase];
             }
@@ -653,7 +674,7 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
             stage(zuA, ztA, sZ0, s + 1);
         }
     }
-    // direct loads still in flight (blocks past this chunk) land before exit
+    // direct loads still in flight (units past this run) land before exit
     stores_done();
 }
 
@@ -1043,14 +1064,11 @@ static void launch_sweep(const SweepArgs& sw, hipStream_t s)
     const dim3 blk(TILE_THREADS);
     if constexpr (std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16 || KS == 32)) {
         if (sw.r == 16 * KS && !sw.vmap && sweep_lds_enabled()) {
-            // as many workgroups as fit at once, with the longest chunks
-            // that give that many (the pipeline fills and drains once per
-            // workgroup)
-            SweepArgs sw2 = sw;
-            sweep_grid(sw.max_rows, sw.n_gran, sw2.bpc, sw2.n_chunks, sweep_ws_target());
-            const dim3 grid2(xcd_grid(sw2.n_gran * sw2.n_chunks)), blk2(2 * TILE_THREADS);
-            if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), grid2, blk2, 0, s, sw2);
-            else hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), grid2, blk2, 0, s, sw2);
+            // as many workgroups as fit at once, each with one run of units
+            const long units = (long)sw.n_gran * ((sw.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
+            const dim3 grid2((unsigned)std::min<long>(sweep_ws_target(), units)), blk2(2 * TILE_THREADS);
+            if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), grid2, blk2, 0, s, sw);
+            else hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), grid2, blk2, 0, s, sw);
             return;
         }
     }
