@@ -125,6 +125,15 @@ __device__ inline int opaque_v(int v)  // per-lane value
 // Wait until every memory operation this wave issued has completed.
 __device__ inline void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Direct global-to-LDS loads: active lane l of the calling wave writes its
+// 4 (dma32) or 16 (dma16) bytes at dst + 4 l or dst + 16 l; dst is the same
+// for the whole wave.  They count as loads of the issuing wave (a wait for
+// its loads covers them); other waves see the data after that wait and a
+// barrier.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ inline void dma32(const void* src, lds_void* dst) { __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0); }
+__device__ inline void dma16(const void* src, lds_void* dst) { __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0); }
+
 // ------------------------------------------------------------- arithmetic
 
 // exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.

@@ -465,13 +465,6 @@ struct LdsW1 {
     }
 };
 
-// Direct load of one 32-bit value per active lane: lane l of the calling
-// wave writes dst[l] (the callers keep lanes 32-63 inactive).
-__device__ inline void dma32(const void* src, __attribute__((address_space(3))) void* dst)
-{
-    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
-}
-
 // The direct-to-LDS sweep, for the implicit row map (every position of every
 // request verified).  The work is a sequence of units, unit u = (granule
 // u / n_rb, 32-row block u % n_rb); each workgroup takes a contiguous run of
