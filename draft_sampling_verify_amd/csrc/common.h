@@ -174,6 +174,12 @@ __device__ inline int wave_min(int v)
     for (int o = 32; o > 0; o >>= 1) v = min(v, shfl_xor(v, o));
     return v;
 }
+__device__ inline int wave_max_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, shfl_xor(v, o));
+    return v;
+}
 // reductions inside each 32-lane half of the wave
 __device__ inline float half_max(float v)
 {

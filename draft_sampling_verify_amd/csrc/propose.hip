@@ -438,11 +438,11 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
     __shared__ int s_tok[32];
     __shared__ float s_red[TILE_THREADS / WAVE];
     __shared__ int s_ired[TILE_THREADS / WAVE];
-    __shared__ int s_gstar;
-    __shared__ float s_before;
+    __shared__ float s_wtot[TILE_THREADS / WAVE];
+    __shared__ int s_cand[TILE_THREADS / WAVE], s_last[TILE_THREADS / WAVE];
+    __shared__ float s_cbefore[TILE_THREADS / WAVE];
     __shared__ float zrow[GRAN];
     __shared__ int s_prev[FUSED_MAX_R];  // previous token of each request this workgroup picks
-    __shared__ float s_round[TILE_THREADS / WAVE][FUSED_PER];
 
     for (int j = threadIdx.x; g + j * NG < R; j += TILE_THREADS) {
         const int a = p.x0[g + j * NG];
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                 float pdx = NAN, sM = NAN, sS = NAN;
                 if (s_prev[j] >= 0) {
                     // q's partials of every granule, polled until all carry
-                    // this position; thread t reads granules t + 256 i
+                    // this position; thread t reads granules 4t .. 4t+3
                     const size_t plane = (size_t)R * NG;
                     const uint64_t* rm = opaque(f.part) + (size_t)q * NG;
                     float gm[FUSED_PER], gs[FUSED_PER];
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                         bool ok = true;
 #pragma unroll
                         for (int i = 0; i < FUSED_PER; ++i) {
-                            const int gg = t + i * TILE_THREADS;
+                            const int gg = FUSED_PER * t + i;
                             gm[i] = -INFINITY;
                             gs[i] = 0.0f;
                             gi[i] = 0u;
@@ -625,73 +625,97 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                         }
                     }
                     if (failed) break;
+                    // three barriers: the maximum M; the wave totals of the
+                    // weights (a running sum in granule order: lanes, then
+                    // waves); the first granule whose running sum passes the
+                    // target
                     float mloc = -INFINITY;
 #pragma unroll
                     for (int i = 0; i < FUSED_PER; ++i) mloc = fmaxf(mloc, gm[i]);
-                    const float M = block_max(mloc, s_red);
-                    // weights; per-round totals (round i = granules 256 i ..
-                    // 256 i + 255, in thread order) through LDS
-                    float wv[FUSED_PER];
+                    mloc = wave_max(mloc);
+                    if (lane == 0) s_red[w] = mloc;
+                    __syncthreads();
+                    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+                    float wv[FUSED_PER], tsum = 0.0f;
 #pragma unroll
                     for (int i = 0; i < FUSED_PER; ++i) {
                         wv[i] = gs[i] * softw(gm[i], M, p.c);  // padding: 0 * 0
-                        const float rs = wave_sum(wv[i]);
-                        if (lane == 0) s_round[w][i] = rs;
+                        tsum += wv[i];
+                    }
+                    const float incl = wave_incl_scan(tsum);
+                    float exl = __shfl_up(incl, 1, WAVE);
+                    if (lane == 0) exl = 0.0f;
+                    if (lane == WAVE - 1) s_wtot[w] = incl;
+                    if (GREEDY) {
+                        int cand = 0x7fffffff;
+#pragma unroll
+                        for (int i = 0; i < FUSED_PER; ++i)
+                            if (FUSED_PER * t + i < NG && gm[i] == M) cand = min(cand, (int)gi[i]);
+                        cand = wave_min(cand);
+                        if (lane == 0) s_ired[w] = cand;
                     }
                     __syncthreads();
-                    float tot[FUSED_PER], S = 0.0f;
+                    float S = 0.0f, woff = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < FUSED_PER; ++i) {
-                        tot[i] = 0.0f;
-#pragma unroll
-                        for (int v = 0; v < TILE_THREADS / WAVE; ++v) tot[i] += s_round[v][i];
-                        S += tot[i];
+                    for (int v = 0; v < TILE_THREADS / WAVE; ++v) {
+                        if (v == w) woff = S;
+                        S += s_wtot[v];
                     }
                     sM = M;
                     sS = S;
                     if (GREEDY) {
-                        int cand = 0x7fffffff;
-#pragma unroll
-                        for (int i = FUSED_PER - 1; i >= 0; --i)
-                            if (t + i * TILE_THREADS < NG && gm[i] == M) cand = (int)gi[i];
-                        xk = block_min(cand, s_ired);
+                        xk = min(min(s_ired[0], s_ired[1]), min(s_ired[2], s_ired[3]));
                         pdx = 1.0f / S;
                     } else {
                         const float target = u24f(philox((uint32_t)k, (uint32_t)q, f.round, f.seed).w[0]) * S;
-                        // the round where the running sum first exceeds target
-                        float pre = 0.0f;
-                        int rstar = -1;
-                        float rbase = 0.0f;
+                        // this thread's share of the running sum is
+                        // [woff + exl, woff + incl): consecutive shares meet
+                        // exactly, so at most one thread holds the target
+                        const float lo = woff + exl, hi = woff + incl;
+                        const bool hit = tsum > 0.0f && lo <= target && target < hi;
+                        int ig = -1, ilast = -1;
+                        float c = lo, cbefore = lo;
 #pragma unroll
                         for (int i = 0; i < FUSED_PER; ++i) {
-                            if (rstar < 0 && tot[i] > 0.0f && pre + tot[i] > target) {
-                                rstar = i;
-                                rbase = pre;
+                            if (wv[i] > 0.0f) {
+                                if (ig < 0 && c + wv[i] > target) {
+                                    ig = i;
+                                    cbefore = c;
+                                }
+                                ilast = i;
                             }
-                            pre += tot[i];
+                            c += wv[i];
                         }
-                        // inside it, the first granule of positive mass crossing target
-                        float wr = 0.0f;
+                        if (hit && ig < 0) {  // the share's own sum rounded below the target
+                            ig = ilast;
+                            float c2 = lo;
 #pragma unroll
-                        for (int i = 0; i < FUSED_PER; ++i)
-                            if (i == rstar) wr = wv[i];
-                        float rtot;
-                        const float excl = rbase + block_excl_scan(wr, s_red, rtot);
-                        const bool hit = rstar >= 0 && wr > 0.0f && excl + wr > target;
-                        const int first = block_min(hit ? t : 0x7fffffff, s_ired);
-                        int lastpos = -1;
-#pragma unroll
-                        for (int i = 0; i < FUSED_PER; ++i)
-                            if (wv[i] > 0.0f) lastpos = t + i * TILE_THREADS;
-                        const int lastp = -block_min(-lastpos, s_ired);
-                        if (t == first) {
-                            s_gstar = t + rstar * TILE_THREADS;
-                            s_before = excl;
+                            for (int i = 0; i < FUSED_PER; ++i)
+                                if (i < ilast) c2 += wv[i];
+                            cbefore = c2;
                         }
+                        const unsigned long long hits = __ballot(hit);
+                        const int lastpos = wave_max_int(ilast >= 0 ? FUSED_PER * t + ilast : -1);
+                        if (hits) {
+                            if (lane == __ffsll((long long)hits) - 1) {
+                                s_cand[w] = FUSED_PER * t + ig;
+                                s_cbefore[w] = cbefore;
+                            }
+                        } else if (lane == 0) {
+                            s_cand[w] = -1;
+                        }
+                        if (lane == 0) s_last[w] = lastpos;
                         __syncthreads();
-                        const bool fallback = first == 0x7fffffff;
-                        const int gstar = fallback ? max(lastp, 0) : s_gstar;
-                        const float before = fallback ? 0.0f : s_before;
+                        int gstar = -1;
+                        float before = 0.0f;
+#pragma unroll
+                        for (int v = TILE_THREADS / WAVE - 1; v >= 0; --v)
+                            if (s_cand[v] >= 0) {
+                                gstar = s_cand[v];
+                                before = s_cbefore[v];
+                            }
+                        const bool fallback = gstar < 0;
+                        if (fallback) gstar = max(max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])), 0);
                         // granule gstar for q with the tile's own operands: W2
                         // block, U_k as the starting accumulator, and sB, which
                         // still holds this position's W1 rows (column q)
