@@ -23,6 +23,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1034,20 +1035,27 @@ static hipError_t target_pass(const DraftArgs& a, const float* Lt, int P, int ma
     return hipGetLastError();
 }
 
-// Workgroups of k_verify_sweep_ws the current device holds at once (two
-// per CU: LDS and registers), cached per device.
-static int sweep_ws_target()
+// Workgroups of k_verify_sweep_ws<KS, VEC4> the current device holds at once
+// (the occupancy API's figure times the CUs), cached per device.
+template <int KS, bool VEC4>
+static int sweep_ws_slots()
 {
-    static int cached[64] = {};
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV];  // slots + 1; 0 = not yet known
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-    if (!cached[dev]) {
-        int cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        cached[dev] = 2 * cus;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_verify_sweep_ws<KS, VEC4>, 2 * TILE_THREADS,
+                                                         0) != hipSuccess || per_cu <= 0)
+            per_cu = 1;
+        v = per_cu * cus + 1;
+        cache[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v - 1;
 }
 
 template <typename WT, int KS>
@@ -1059,9 +1067,14 @@ static void launch_sweep(const SweepArgs& sw, hipStream_t s)
         if (sw.r == 16 * KS && !sw.vmap && sweep_lds_enabled()) {
             // as many workgroups as fit at once, each with one run of units
             const long units = (long)sw.n_gran * ((sw.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
-            const dim3 grid2((unsigned)std::min<long>(sweep_ws_target(), units)), blk2(2 * TILE_THREADS);
-            if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), grid2, blk2, 0, s, sw);
-            else hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), grid2, blk2, 0, s, sw);
+            const dim3 blk2(2 * TILE_THREADS);
+            if (sw.vec4) {
+                const dim3 grid2((unsigned)std::min<long>(sweep_ws_slots<KS, true>(), units));
+                hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), grid2, blk2, 0, s, sw);
+            } else {
+                const dim3 grid2((unsigned)std::min<long>(sweep_ws_slots<KS, false>(), units));
+                hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), grid2, blk2, 0, s, sw);
+            }
             return;
         }
     }
