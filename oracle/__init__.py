@@ -13,6 +13,8 @@ Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
                     for P(accept), E[n_acc], special cases
   confidence        pinned: V = 2 closed form, identical rows, TV identity
   schedule          pinned: exhaustive enumeration of allocations
+  schedule_async    pinned: enumeration of fixed-size allocations (top-K is
+                    the best), the two-step history ring, nesting in K
 """
 from __future__ import annotations
 
@@ -71,6 +73,8 @@ def lib():
                                      ctypes.c_int, ctypes.c_int, f32, P, P]
         L.ref_schedule.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P, P, P,
                                    P, P]
+        L.ref_schedule_async.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P, P, P, P,
+                                         P, P]
         _lib = L
     return _lib
 
@@ -208,3 +212,26 @@ def schedule(c, sps):
         raise OracleError("ref_schedule rejected its arguments")
     return dict(ell=ell, a=a, K_star=int(K[0]), theta_star=float(th[0]),
                 theta_margin=float(tm[0]), a_gap=float(gap[0]))
+
+
+def schedule_async(c, sps, K_hist):
+    """The production scheduler step (ref_schedule_async): K from the ring
+    K_hist = [K* two calls ago, K* one call ago] (negative: none yet),
+    ranking by the current confidences.  Returns the outputs and the
+    advanced ring."""
+    c = _c(c, np.float32)
+    R, g = c.shape
+    sps = _c(sps, np.float32)
+    hist = np.array(K_hist, np.int32)
+    ell = np.zeros(R, np.int32)
+    a = np.zeros((R, g))
+    Ku = np.zeros(1, np.int32)
+    K = np.zeros(1, np.int32)
+    th = np.zeros(1)
+    tm = np.zeros(1)
+    st = lib().ref_schedule_async(_p(c), R, g, _p(sps), sps.size, _p(hist), _p(ell), _p(a), _p(Ku), _p(K),
+                                  _p(th), _p(tm))
+    if st != 0:
+        raise OracleError("ref_schedule_async rejected its arguments")
+    return dict(ell=ell, a=a, K_used=int(Ku[0]), K_star=int(K[0]), theta_star=float(th[0]),
+                theta_margin=float(tm[0]), K_hist=hist)

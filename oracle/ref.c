@@ -472,3 +472,40 @@ int ref_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
     free(P);
     return 0;
 }
+
+/* The asynchronous variant: K from the history ring, ranking from the
+ * current survival products (both orders as in ref_schedule). */
+int ref_schedule_async(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* K_hist,
+                       int32_t* ell, double* a, int32_t* K_used, int32_t* K_star, double* theta_star,
+                       double* theta_margin)
+{
+    if (!K_hist || !K_used) return -1;
+    /* the current optimum (also validates the arguments) */
+    if (ref_schedule(c, R, gamma, sps, B_max, ell, a, K_star, theta_star, theta_margin, NULL) != 0) return -1;
+    size_t n = (size_t)R * (size_t)gamma;
+    long K = K_hist[0] >= 0 ? (long)K_hist[0] : (long)*K_star;
+    if (K > (long)n) K = (long)n;
+    /* rank the current products again and count the first K */
+    ref_entry* e = (ref_entry*)malloc(sizeof(ref_entry) * n);
+    if (!e) return -1;
+    for (int r = 0; r < R; ++r) {
+        double run = 1.0;
+        for (int j = 1; j <= gamma; ++j) {
+            size_t o = (size_t)r * gamma + (size_t)(j - 1);
+            run *= (double)c[o];
+            e[o].a = run;
+            e[o].r = r;
+            e[o].j = j;
+        }
+    }
+    qsort(e, n, sizeof(ref_entry), entry_cmp);
+    for (int r = 0; r < R; ++r)
+        ell[r] = 0;
+    for (long i = 0; i < K; ++i)
+        ell[e[i].r] += 1;
+    *K_used = (int32_t)K;
+    K_hist[0] = K_hist[1];
+    K_hist[1] = *K_star;
+    free(e);
+    return 0;
+}

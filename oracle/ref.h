@@ -117,6 +117,23 @@ int ref_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
                  int32_t* ell, double* a, int32_t* K_star, double* theta_star,
                  double* theta_margin, double* a_gap);
 
+/* Production (asynchronous) variant of the scheduler (DSpark blog page,
+ * section 7): the candidates are ranked by the current confidences, while
+ * the number verified, K, is the scheduler's optimum from two calls earlier
+ * (a dynamic top-K; the capacity comes from history, so the choice does not
+ * look at the current tokens).
+ *   K_hist [2] in/out: K* of the two previous calls, oldest first; a
+ *   negative entry means "none yet", and the current call's own optimum is
+ *   used instead.  On return K_hist = {K_hist[1], K*} (the ring advanced).
+ * Outputs: ell [R] = counts per request among the first K_used entries of
+ * the ranking (a descending, then request, then position); a [R,gamma]
+ * (may be NULL); *K_used = min(K, R*gamma); *K_star, *theta_star,
+ * *theta_margin as ref_schedule for the current confidences.
+ * Returns 0, or -1 on a bad argument. */
+int ref_schedule_async(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* K_hist,
+                       int32_t* ell, double* a, int32_t* K_used, int32_t* K_star, double* theta_star,
+                       double* theta_margin);
+
 #ifdef __cplusplus
 }
 #endif
