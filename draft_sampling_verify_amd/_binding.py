@@ -43,6 +43,7 @@ _SIGS = {
     "spec_verify": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
     "spec_confidence": ([P, P, P, I, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P], I),
     "spec_schedule": ([P, I, I, P, I, P, P, P, P, P, SZ, P], I),
+    "spec_schedule_async": ([P, I, I, P, I, P, P, P, P, P, P, P, SZ, P], I),
     "spec_decode_rounds": ([P, P, P, I, P, P, I, I, I, I, F, I, U64, U64, I, P, P, P, P, P, P, SZ, P], I),
     "spec_status_str": ([I], ctypes.c_char_p),
     "spec_set_propose_fused": ([I], I),
@@ -302,6 +303,35 @@ def spec_schedule(c, sps, ell=None, a=None, K_star=None, theta_star=None, want_a
                              _ptr(theta_star), ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_schedule")
     return ell, a, K_star, theta_star
+
+
+def spec_schedule_async(c, sps, K_hist, ell=None, a=None, K_used=None, K_star=None, theta_star=None, want_a=True,
+                        ws=None, stream=None):
+    """The production scheduler step.  K_hist: int32 [2] device tensor (the
+    K* of the previous two calls, oldest first, -1 = none), updated in place.
+    Returns (ell, a, K_used, K_star, theta_star)."""
+    if c.dim() != 2 or c.dtype != torch.float32:
+        raise ValueError("c must be float32 [R, gamma]")
+    R, gamma = c.shape
+    if sps.dim() != 1 or sps.dtype != torch.float32:
+        raise ValueError("sps must be float32 [B_max]")
+    dev = c.device
+    _need(K_hist, (2,), torch.int32, "K_hist")
+    _need(ell, (R,), torch.int32, "ell")
+    _need(a, (R, gamma), torch.float64, "a")
+    ell = torch.empty(R, dtype=torch.int32, device=dev) if ell is None else ell
+    if a is None and want_a:
+        a = torch.empty((R, gamma), dtype=torch.float64, device=dev)
+    K_used = torch.empty(1, dtype=torch.int32, device=dev) if K_used is None else K_used
+    K_star = torch.empty(1, dtype=torch.int32, device=dev) if K_star is None else K_star
+    theta_star = torch.empty(1, dtype=torch.float64, device=dev) if theta_star is None else theta_star
+    if ws is None:
+        ws = Workspace(R, gamma, 16, 1, B_max=sps.numel(), device=dev)
+    st = lib().spec_schedule_async(_ptr(c), R, gamma, _ptr(sps), sps.numel(), _ptr(K_hist), _ptr(ell), _ptr(a),
+                                   _ptr(K_used), _ptr(K_star), _ptr(theta_star), ws.ptr(), ws.nbytes,
+                                   _stream(stream))
+    _check(st, "spec_schedule_async")
+    return ell, a, K_used, K_star, theta_star
 
 
 def spec_set_propose_fused(enable: bool) -> bool:

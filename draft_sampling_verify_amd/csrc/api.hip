@@ -309,8 +309,20 @@ int spec_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
     if ((long)R * gamma > spec::SCHED_MAX_ENTRIES) return SPEC_EUNSUPPORTED;
     if (!c || !sps || !ell || !K_star || !theta_star) return SPEC_EINVAL;
     if (!ws || ws_bytes < spec::WS_HEADER) return SPEC_EWORKSPACE;
-    return launch_status(spec::launch_schedule(c, R, gamma, sps, B_max, ell, a, K_star, theta_star,
-                                               reinterpret_cast<uint32_t*>(ws), (hipStream_t)stream));
+    return launch_status(spec::launch_schedule(c, R, gamma, sps, B_max, ell, a, K_star, theta_star, nullptr,
+                                               nullptr, reinterpret_cast<uint32_t*>(ws), (hipStream_t)stream));
+}
+
+int spec_schedule_async(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* K_hist,
+                        int32_t* ell, double* a, int32_t* K_used, int32_t* K_star, double* theta_star, void* ws,
+                        size_t ws_bytes, spec_stream_t stream)
+{
+    if (R < 1 || gamma < 1 || B_max < R) return SPEC_EINVAL;
+    if ((long)R * gamma > spec::SCHED_MAX_ENTRIES) return SPEC_EUNSUPPORTED;
+    if (!c || !sps || !K_hist || !ell || !K_used || !K_star || !theta_star) return SPEC_EINVAL;
+    if (!ws || ws_bytes < spec::WS_HEADER) return SPEC_EWORKSPACE;
+    return launch_status(spec::launch_schedule(c, R, gamma, sps, B_max, ell, a, K_star, theta_star, K_hist,
+                                               K_used, reinterpret_cast<uint32_t*>(ws), (hipStream_t)stream));
 }
 
 const char* spec_status_str(int status)

@@ -156,7 +156,7 @@ hipError_t launch_confidence(const DraftArgs& a, const float* pd_stats, const fl
 // schedule.hip
 hipError_t launch_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
                            int32_t* ell, double* a, int32_t* K_star, double* theta_star,
-                           uint32_t* status, hipStream_t s);
+                           int32_t* K_hist, int32_t* K_used, uint32_t* status, hipStream_t s);
 constexpr int SCHED_MAX_ENTRIES = 8192;
 
 // Profiling hooks (api.cpp): bracket one kernel launch on stream s.

@@ -1,4 +1,6 @@
-// schedule.hip -- hardware-aware prefix scheduler (DSpark blog page, section 6).
+// schedule.hip -- hardware-aware prefix scheduler (DSpark blog page, section 6)
+// and its production step with a two-call lag on the verified count
+// (section 7).
 //
 // One workgroup of 1024 threads does the whole problem in LDS (R*gamma <=
 // 8192 entries):
@@ -26,10 +28,15 @@ __device__ inline bool sched_before(double ka, int ia, double kb, int ib)
     return ka > kb || (ka == kb && ia < ib);
 }
 
+// K_hist == NULL: the synchronous scheduler (l from the first K* entries).
+// Otherwise the production step: l from the first K entries, K = K_hist[0]
+// (the optimum two calls earlier; negative: none, use K*), capped at
+// R*gamma; K_used = K, and the ring advances to {K_hist[1], K*}.
 __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int R, int gamma,
                                                             const float* sps, int B_max, int32_t* ell,
                                                             double* a_out, int32_t* K_star,
-                                                            double* theta_star, uint32_t* status)
+                                                            double* theta_star, int32_t* K_hist,
+                                                            int32_t* K_used, uint32_t* status)
 {
     __shared__ double key[SCHED_MAX_ENTRIES];
     __shared__ int idx[SCHED_MAX_ENTRIES];
@@ -71,6 +78,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int 
             raise_flag(status, 4u);
             *K_star = -1;
             *theta_star = NAN;
+            if (K_used) *K_used = -1;  // the ring is left as it was
         }
         for (int r = t; r < R; r += SCHED_THREADS) ell[r] = -1;
         return;
@@ -150,23 +158,35 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int 
             k_star = best_k[i];
         }
 
-    // 5. per-request counts among the first K*
-    for (int i = t; i < k_star; i += SCHED_THREADS) atomicAdd(&cnt[idx[i] / gamma], 1);
+    // 5. per-request counts among the first K* (production step: the first
+    //    K of the history)
+    int k_use = k_star;
+    if (K_hist) {
+        const int h = K_hist[0];
+        k_use = h >= 0 ? min(h, n) : k_star;
+    }
+    for (int i = t; i < k_use; i += SCHED_THREADS) atomicAdd(&cnt[idx[i] / gamma], 1);
     __syncthreads();
     for (int r = t; r < R; r += SCHED_THREADS) ell[r] = cnt[r];
     if (t == 0) {
         *K_star = k_star;
         *theta_star = th_star;
+        if (K_hist) {
+            *K_used = k_use;
+            K_hist[0] = K_hist[1];
+            K_hist[1] = k_star;
+        }
     }
 }
 
 hipError_t launch_schedule(const float* c, int R, int gamma, const float* sps, int B_max, int32_t* ell,
-                           double* a, int32_t* K_star, double* theta_star, uint32_t* status, hipStream_t s)
+                           double* a, int32_t* K_star, double* theta_star, int32_t* K_hist, int32_t* K_used,
+                           uint32_t* status, hipStream_t s)
 {
     {
         ProfScope ps("schedule", s);
         hipLaunchKernelGGL(k_schedule, dim3(1), dim3(SCHED_THREADS), 0, s, c, R, gamma, sps, B_max, ell, a,
-                           K_star, theta_star, status);
+                           K_star, theta_star, K_hist, K_used, status);
     }
     return hipGetLastError();
 }

@@ -17,6 +17,9 @@
  *   spec_schedule        per-request verify lengths l_r maximising
  *                        Theta = tau * SPS(B), B = sum_r (1 + l_r),
  *                        tau = sum_r (1 + sum_{j<=l_r} a_{r,j}) (DSpark section 6)
+ *   spec_schedule_async  the production step: the same ranking, with the
+ *                        verified count taken from the optimum two calls
+ *                        earlier (a dynamic top-K)          (DSpark section 7)
  *
  * Conventions shared by every entry point
  *   Memory      Every pointer argument is DEVICE memory unless its comment says
@@ -250,6 +253,27 @@ int spec_confidence(const float* U, const void* W1, const void* W2p, int w_dtype
 int spec_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
                   int32_t* ell, double* a, int32_t* K_star, double* theta_star,
                   void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Production step of the scheduler (DSpark section 7): the candidates are
+ * ranked by the current confidences exactly as in spec_schedule, but the
+ * number verified is the optimum K* that the scheduler found two calls
+ * earlier -- a dynamic top-K whose size comes from history, so it is known
+ * a step ahead (graph replay) and does not depend on the current tokens.
+ *   K_hist [2] int32, device, in/out: K* of the previous two calls, oldest
+ *     first; a negative entry means "none yet" (the current K* is used).
+ *     The call reads K_hist[0] and leaves {K_hist[1], K*} (initialise both
+ *     to -1; one ring per decode loop; calls on one ring must be ordered).
+ *   K_used [1] int32 = min(K_hist[0], R*gamma), or K* when K_hist[0] < 0.
+ *   ell [R] = number of request-r entries among the first K_used of the
+ *     ranking (a descending, then request, then position).
+ *   a, K_star, theta_star: as spec_schedule, for the current confidences.
+ * A confidence outside [0,1] raises SPEC_DEV_BAD_CONFIDENCE, writes -1 to
+ * ell, K_used and K_star and leaves K_hist unchanged.  Limits as
+ * spec_schedule. */
+int spec_schedule_async(const float* c, int R, int gamma, const float* sps, int B_max,
+                        int32_t* K_hist, int32_t* ell, double* a, int32_t* K_used,
+                        int32_t* K_star, double* theta_star,
+                        void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Name of a status code (static string). */
 const char* spec_status_str(int status);

@@ -75,3 +75,89 @@ def test_bad_confidence_sets_flag():
     ell, a, K, th = _run(c, np.ones(6, np.float32), ws)
     assert K == -1 and (ell == -1).all()
     assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_CONFIDENCE
+
+
+def _sawtooth(R, g, rng):
+    """The decreasing sawtooth SPS table of the scheduler-heavy workload."""
+    B = np.arange(1, R * (g + 1) + 1)
+    eps = rng.uniform(-1, 1, int(np.ceil(B[-1] / 64)) + 1)
+    step = np.ceil(B / 64).astype(int)
+    return (1000.0 * (1 + 0.08 * eps[step]) / (20 + 0.25 * step + 0.001 * B)).astype(np.float32)
+
+
+@pytest.mark.parametrize("R,g", [(5, 6), (64, 8), (512, 16)])
+def test_async_sequence_matches_oracle(R, g):
+    """The production step over a sequence of calls on one device ring: the
+    count verified at step t is the optimum of step t-2, the ranking is the
+    current one; ell, K_used, K_star, a and the ring match the oracle."""
+    rng = np.random.default_rng(R + g)
+    sps = _sawtooth(R, g, rng)
+    sps_d = torch.from_numpy(sps).cuda()
+    ring = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    oring = [-1, -1]
+    ws = spec.Workspace(R, g, 16, 1, B_max=sps.size)
+    excluded = 0
+    for t in range(10):
+        c = (1 / (1 + np.exp(-rng.normal(1.5, 1.0, (R, g))))).astype(np.float32)
+        ell, a, Ku, Ks, th = spec.spec_schedule_async(torch.from_numpy(c).cuda(), sps_d, ring, ws=ws)
+        torch.cuda.synchronize()
+        o = oracle.schedule_async(c, sps, oring)
+        np.testing.assert_array_equal(np_(a), o["a"])
+        assert int(np_(Ku)[0]) == o["K_used"]
+        np.testing.assert_array_equal(np_(ell), o["ell"])
+        if o["theta_margin"] >= MARGIN:
+            assert int(np_(Ks)[0]) == o["K_star"]
+        else:
+            excluded += 1
+        oring = list(np_(ring))        # follow the device ring (equal unless excluded)
+        assert oring[0] == (o["K_hist"][0])
+    log("  async steps excluded (theta margin < 1e-6):", excluded)
+    assert spec.spec_device_status(ws) == 0
+
+
+def test_async_graph_replay():
+    """One captured production step, replayed with new confidences copied
+    into its input between replays: every replay equals the oracle step."""
+    R, g = 64, 8
+    rng = np.random.default_rng(123)
+    sps = _sawtooth(R, g, rng)
+    sps_d = torch.from_numpy(sps).cuda()
+    c_d = torch.zeros((R, g), dtype=torch.float32, device="cuda")
+    ring = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    ws = spec.Workspace(R, g, 16, 1, B_max=sps.size)
+    outs = [torch.empty(R, dtype=torch.int32, device="cuda"), torch.empty((R, g), dtype=torch.float64, device="cuda"),
+            torch.empty(1, dtype=torch.int32, device="cuda"), torch.empty(1, dtype=torch.int32, device="cuda"),
+            torch.empty(1, dtype=torch.float64, device="cuda")]
+    c_d.fill_(0.5)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):  # warm-up outside the capture
+        spec.spec_schedule_async(c_d, sps_d, ring, *outs, ws=ws, stream=s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        spec.spec_schedule_async(c_d, sps_d, ring, *outs, ws=ws, stream=s)
+    ring.fill_(-1)
+    torch.cuda.synchronize()
+    oring = [-1, -1]
+    for t in range(8):
+        c = (1 / (1 + np.exp(-rng.normal(1.5, 1.0, (R, g))))).astype(np.float32)
+        c_d.copy_(torch.from_numpy(c))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o = oracle.schedule_async(c, sps, oring)
+        np.testing.assert_array_equal(np_(outs[0]), o["ell"])
+        assert int(np_(outs[2])[0]) == o["K_used"]
+        oring = list(np_(ring))
+    assert spec.spec_device_status(ws) == 0
+
+
+def test_async_bad_confidence_keeps_ring():
+    ws = spec.Workspace(2, 2, 16, 16)
+    ring = torch.tensor([3, 4], dtype=torch.int32, device="cuda")
+    c = torch.tensor([[0.5, float("nan")], [0.2, 0.1]], dtype=torch.float32, device="cuda")
+    ell, a, Ku, Ks, th = spec.spec_schedule_async(c, torch.ones(6, device="cuda"), ring, ws=ws)
+    torch.cuda.synchronize()
+    assert int(np_(Ku)[0]) == -1 and int(np_(Ks)[0]) == -1 and (np_(ell) == -1).all()
+    np.testing.assert_array_equal(np_(ring), [3, 4])
+    assert spec.spec_device_status(ws, clear=True) & spec.SPEC_DEV_BAD_CONFIDENCE
