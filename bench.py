@@ -278,6 +278,34 @@ def main():
                  "emitted_tokens_per_s_graph": round(emitted / graph_s, 1)}
         del graph
 
+    # the prefix scheduler at the scheduler-heavy shape (R = 512, gamma = 16,
+    # sawtooth SPS over B = 1..8704), synchronous and production step
+    sched = None
+    if not args.profile_only:
+        c4 = workloads.CONFIGS["c4"]
+        cs = torch.from_numpy(workloads.confidences(c4)).to(dev)
+        sps4 = torch.from_numpy(workloads.sawtooth_sps(c4)).to(dev)
+        sws = spec.Workspace(c4.R, c4.gamma, 16, 1, B_max=sps4.numel(), device=dev)
+        ring = torch.full((2,), -1, dtype=torch.int32, device=dev)
+        so = spec.spec_schedule(cs, sps4, ws=sws, stream=stream)
+        ao = spec.spec_schedule_async(cs, sps4, ring, ws=sws, stream=stream)
+        times = {}
+        for name, fn in (("sync", lambda: spec.spec_schedule(cs, sps4, *so, ws=sws, stream=stream)),
+                         ("async", lambda: spec.spec_schedule_async(cs, sps4, ring, *ao, ws=sws, stream=stream))):
+            for _ in range(3):
+                fn()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(50):
+                fn()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            times[name] = a0.elapsed_time(a1) * 1e3 / 50
+        sched = {"workload": "c4 shape: R=512, gamma=16 (8192 candidates), sawtooth SPS over B=1..8704",
+                 "us_per_call_sync": round(times["sync"], 2), "us_per_call_async": round(times["async"], 2),
+                 "K_star": int(so[2].item()), "K_used_async": int(ao[2].item())}
+        del sws
+
     acc = float(n_acc.float().mean())
     cmean = float(c_star.float().mean())
     flags = spec.spec_device_status(ws)
@@ -322,6 +350,7 @@ def main():
         "ms_per_step_with_kernel_events": round(1000.0 * elapsed_prof / args.steps, 4),
         "kernels": kernels,
         "multi_round": multi,
+        "scheduler": sched,
         "mean_n_acc": round(acc, 4),
         "mean_c_star": round(cmean, 4),
         "device_status": flags,

@@ -5,8 +5,9 @@
 // One workgroup of 1024 threads does the whole problem in LDS (R*gamma <=
 // 8192 entries):
 //   1. a_{r,j} = prod_{i<=j} c_{r,i} in fp64, left to right, per request;
-//   2. bitonic sort of (a, r*gamma + j - 1) into the order a descending,
-//      then request, then position ascending;
+//   2. the R per-request runs (already in order, a not increasing along j)
+//      merged pairwise into the order a descending, then request, then
+//      position ascending (log2 R merge levels);
 //   3. fp64 prefix sums P_K of the sorted a;
 //   4. Theta(K) = (R + P_K) * SPS(R + K) for K = 0..min(R*gamma, B_max - R),
 //      K* = the smallest maximiser;
@@ -23,11 +24,6 @@ namespace spec {
 
 constexpr int SCHED_THREADS = 1024;
 
-__device__ inline bool sched_before(double ka, int ia, double kb, int ib)
-{
-    return ka > kb || (ka == kb && ia < ib);
-}
-
 // K_hist == NULL: the synchronous scheduler (l from the first K* entries).
 // Otherwise the production step: l from the first K entries, K = K_hist[0]
 // (the optimum two calls earlier; negative: none, use K*), capped at
@@ -38,9 +34,11 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int 
                                                             double* theta_star, int32_t* K_hist,
                                                             int32_t* K_used, uint32_t* status)
 {
-    __shared__ double key[SCHED_MAX_ENTRIES];
-    __shared__ int idx[SCHED_MAX_ENTRIES];
-    __shared__ int cnt[SCHED_MAX_ENTRIES];
+    // survival products by entry (o = r*gamma + j - 1), and the ranking as a
+    // permutation of entries, ping-ponged between two index buffers while
+    // the runs are merged; the spare buffer holds the per-request counts
+    __shared__ double sa[SCHED_MAX_ENTRIES];
+    __shared__ int ibuf[2][SCHED_MAX_ENTRIES];
     __shared__ double wsum[SCHED_THREADS / WAVE];
     __shared__ double best_th[SCHED_THREADS / WAVE];
     __shared__ int best_k[SCHED_THREADS / WAVE];
@@ -49,30 +47,31 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int 
     const int t = threadIdx.x;
     const int lane = t & (WAVE - 1), w = t / WAVE;
     const int n = R * gamma;
-    int N = 1;
-    while (N < n) N <<= 1;
     if (t == 0) bad = 0;
     __syncthreads();
 
-    // 1. survival products
+    // 1. survival products; each request's run is already in ranking order
+    //    (a does not increase along j: a factor in [0,1] cannot round above
+    //    the running product, and ties keep j ascending).  The confidences
+    //    are first read coalesced into sa, then multiplied along each row.
+    for (int o = t; o < n; o += SCHED_THREADS) {
+        const float cv = c[o];
+        if (!(cv >= 0.0f && cv <= 1.0f)) bad = 1;
+        sa[o] = (double)cv;
+        ibuf[0][o] = o;
+    }
+    __syncthreads();
     for (int r = t; r < R; r += SCHED_THREADS) {
         double run = 1.0;
         for (int j = 0; j < gamma; ++j) {
             const int o = r * gamma + j;
-            const float cv = c[o];
-            if (!(cv >= 0.0f && cv <= 1.0f)) bad = 1;
-            run *= (double)cv;
-            key[o] = run;
-            idx[o] = o;
-            if (a_out) a_out[o] = run;
+            run *= sa[o];
+            sa[o] = run;
         }
-        cnt[r] = 0;
-    }
-    for (int i = n + t; i < N; i += SCHED_THREADS) {
-        key[i] = -1.0;  // sorts after every real entry (a >= 0)
-        idx[i] = i;
     }
     __syncthreads();
+    if (a_out)
+        for (int o = t; o < n; o += SCHED_THREADS) a_out[o] = sa[o];
     if (bad) {
         if (t == 0) {
             raise_flag(status, 4u);
@@ -84,32 +83,48 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int 
         return;
     }
 
-    // 2. bitonic sort into "before" order
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = t; i < N; i += SCHED_THREADS) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const double ki = key[i], kl = key[l];
-                    const int ii = idx[i], il = idx[l];
-                    const bool up = (i & k) == 0;
-                    const bool swap = up ? sched_before(kl, il, ki, ii) : sched_before(ki, ii, kl, il);
-                    if (swap) {
-                        key[i] = kl; key[l] = ki;
-                        idx[i] = il; idx[l] = ii;
-                    }
+    // 2. merge runs pairwise, gamma -> 2 gamma -> ... -> n, into the order
+    //    a descending, then entry (request, position) ascending.  Each thread
+    //    writes a contiguous chunk of the output; where a chunk starts (or a
+    //    new pair of runs begins) its split between the two runs is found by
+    //    binary search on the merge path.
+    auto ranks_first = [&](int x, int y) { return sa[x] > sa[y] || (sa[x] == sa[y] && x < y); };
+    const int per = (n + SCHED_THREADS - 1) / SCHED_THREADS;
+    int cur = 0;
+    for (int run = gamma; run < n; run *= 2, cur ^= 1) {
+        const int* src = ibuf[cur];
+        int* dst = ibuf[cur ^ 1];
+        const int p0 = min(t * per, n), p1 = min(p0 + per, n);
+        int i = 0, j = 0, base = -1, la = 0, lb = 0;
+        for (int p = p0; p < p1; ++p) {
+            const int pb = p - p % (2 * run);
+            if (pb != base) {
+                base = pb;
+                la = min(run, n - base);
+                lb = min(run, n - base - la);
+                const int q = p - base;
+                int lo = max(0, q - lb), hi = min(q, la);
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (ranks_first(src[base + mid], src[base + la + q - mid - 1])) lo = mid + 1;
+                    else hi = mid;
                 }
+                i = lo;
+                j = q - lo;
             }
-            __syncthreads();
+            const bool take_a = j >= lb || (i < la && ranks_first(src[base + i], src[base + la + j]));
+            dst[p] = take_a ? src[base + i++] : src[base + la + j++];
         }
+        __syncthreads();
     }
+    const int* idx = ibuf[cur];
+    int* cnt = ibuf[cur ^ 1];
 
     // 3. inclusive prefix sums over the first n sorted values, in place;
     //    each thread owns a contiguous run of `per` entries
-    const int per = (n + SCHED_THREADS - 1) / SCHED_THREADS;
     const int i0 = min(t * per, n), i1 = min(i0 + per, n);
     double local = 0.0;
-    for (int i = i0; i < i1; ++i) local += key[i];
+    for (int i = i0; i < i1; ++i) local += sa[idx[i]];
     // block exclusive scan of `local` (fp64)
     double incl = local;
     for (int o = 1; o < WAVE; o <<= 1) {
@@ -133,7 +148,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int 
         bk = 0;
     }
     for (int i = i0; i < i1; ++i) {
-        run += key[i];
+        run += sa[idx[i]];
         const int K = i + 1;
         if (K <= Kmax) {
             const double th = ((double)R + run) * (double)sps[R + K - 1];
@@ -165,6 +180,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* c, int 
         const int h = K_hist[0];
         k_use = h >= 0 ? min(h, n) : k_star;
     }
+    for (int r = t; r < R; r += SCHED_THREADS) cnt[r] = 0;
+    __syncthreads();
     for (int i = t; i < k_use; i += SCHED_THREADS) atomicAdd(&cnt[idx[i] / gamma], 1);
     __syncthreads();
     for (int r = t; r < R; r += SCHED_THREADS) ell[r] = cnt[r];
