@@ -15,6 +15,9 @@ Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
   schedule          pinned: exhaustive enumeration of allocations
   schedule_async    pinned: enumeration of fixed-size allocations (top-K is
                     the best), the two-step history ring, nesting in K
+  draft_loss        pinned: scipy log-softmax cross-entropy, identical rows
+                    (l1 = 0, c* = 1), l1 = 2(1 - c*) against confidence,
+                    finite differences of dq, closed form at V = 2
 """
 from __future__ import annotations
 
@@ -75,6 +78,8 @@ def lib():
                                    P, P]
         L.ref_schedule_async.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P, P, P, P,
                                          P, P]
+        L.ref_draft_loss.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, f32, f32, f32, f32, P, P, P]
         _lib = L
     return _lib
 
@@ -194,6 +199,27 @@ def confidence(U, W1, W2, x0, x, Lt, T):
     if st != 0:
         raise OracleError("ref_confidence rejected its arguments")
     return c, a
+
+
+def draft_loss(U, W1, W2, x0, y, Lt, q, T, alphas=(0.1, 0.9, 1.0)):
+    """Training-side loss (ref_draft_loss): returns dict(loss, terms [R,g,3]
+    = (ce, l1, bce), dq [R,g])."""
+    W1, W2, dt = _weights(W1, W2)
+    U = _c(U, np.float32)
+    R, g, V = U.shape
+    r = W1.shape[1]
+    x0 = _c(x0, np.int32)
+    y = _c(y, np.int32)
+    Lt = _c(Lt, np.float32)
+    q = _c(q, np.float32)
+    loss = np.zeros(1)
+    terms = np.zeros((R, g, 3))
+    dq = np.zeros((R, g))
+    st = lib().ref_draft_loss(_p(U), _p(W1), _p(W2), dt, _p(x0), _p(y), _p(Lt), _p(q), R, g, r, V, float(T),
+                              float(alphas[0]), float(alphas[1]), float(alphas[2]), _p(loss), _p(terms), _p(dq))
+    if st != 0:
+        raise OracleError("ref_draft_loss rejected its arguments")
+    return dict(loss=float(loss[0]), terms=terms, dq=dq)
 
 
 def schedule(c, sps):

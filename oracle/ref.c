@@ -386,6 +386,77 @@ int ref_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
     return status;
 }
 
+/* ------------------------------------------------------------ training loss */
+
+/* Training-side loss over the drafted positions (DSpark page, section 9, the
+ * weighted sum of a cross-entropy, an L1/TV and a confidence term with
+ * position weights; the coefficients of DeepSpec's configuration, section 8,
+ * are the caller's alphas).  Teacher-forced: the bias of position k uses the
+ * label y_{k-1} (y_0 = the anchor).  Per position (r, k):
+ *   ce  = -log p_d(y_k)
+ *   l1  = sum_v |p_d(v) - p_t(v)|               (twice the TV distance)
+ *   c*  = clamp(1 - l1 / 2, 0, 1)                 (section 5)
+ *   bce = BCE-with-logits(q, c*) = max(q, 0) - q c* + log(1 + exp(-|q|))
+ *   w_k = exp(-(k - 1) / gamma)
+ * loss = sum_{r,k} w_k (a_ce ce + a_tv l1 + a_conf bce) / sum_{r,k} w_k, and
+ * dq = d loss / d q = w_k a_conf (sigmoid(q) - c*) / sum w (c* is a label). */
+int ref_draft_loss(const float* U, const void* W1, const void* W2, int w_dtype,
+                   const int32_t* x0, const int32_t* y, const float* Lt, const float* q,
+                   int R, int gamma, int r, int V, float T, float a_ce, float a_tv, float a_conf,
+                   double* loss, double* terms, double* dq)
+{
+    if (bad_common(U, W1, W2, w_dtype, x0, R, gamma, r, V, T) || !y || !Lt || !q || !loss)
+        return -1;
+    const double Td = (double)T;
+    double* z = (double*)malloc(sizeof(double) * (size_t)V);
+    double* pd = (double*)malloc(sizeof(double) * (size_t)V);
+    double* lt = (double*)malloc(sizeof(double) * (size_t)V);
+    double* pt = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!z || !pd || !lt || !pt) {
+        free(z); free(pd); free(lt); free(pt);
+        return -1;
+    }
+    int status = 0;
+    double wsum = 0.0, total = 0.0;
+    for (int k = 1; k <= gamma; ++k)
+        wsum += (double)R * exp(-(double)(k - 1) / (double)gamma);
+    for (int row = 0; row < R && status == 0; ++row) {
+        int32_t yprev = x0[row];
+        for (int k = 1; k <= gamma; ++k) {
+            size_t o = (size_t)row * gamma + (size_t)(k - 1);
+            const int32_t yk = y[o];
+            if (yprev < 0 || yprev >= V || yk < 0 || yk >= V) { status = -1; break; }
+            draft_logits(U, W1, W2, w_dtype, row, k, gamma, r, V, yprev, z);
+            softmax_T(z, V, Td, pd, NULL, NULL);
+            const float* lrow = Lt + ((size_t)row * (gamma + 1) + (size_t)(k - 1)) * (size_t)V;
+            for (int v = 0; v < V; ++v)
+                lt[v] = (double)lrow[v];
+            softmax_T(lt, V, Td, pt, NULL, NULL);
+            double l1 = 0.0;
+            for (int v = 0; v < V; ++v)
+                l1 += fabs(pd[v] - pt[v]);
+            double cs = 1.0 - 0.5 * l1;
+            if (cs < 0.0) cs = 0.0;
+            if (cs > 1.0) cs = 1.0;
+            const double ce = -log(pd[yk]);
+            const double qv = (double)q[o];
+            const double bce = (qv > 0.0 ? qv : 0.0) - qv * cs + log1p(exp(-fabs(qv)));
+            const double wk = exp(-(double)(k - 1) / (double)gamma);
+            total += wk * ((double)a_ce * ce + (double)a_tv * l1 + (double)a_conf * bce);
+            if (terms) {
+                terms[3 * o] = ce;
+                terms[3 * o + 1] = l1;
+                terms[3 * o + 2] = bce;
+            }
+            if (dq) dq[o] = wk * (double)a_conf * (1.0 / (1.0 + exp(-qv)) - cs) / wsum;
+            yprev = yk;
+        }
+    }
+    *loss = total / wsum;
+    free(z); free(pd); free(lt); free(pt);
+    return status;
+}
+
 /* ---------------------------------------------------------------- schedule */
 
 typedef struct {

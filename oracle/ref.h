@@ -107,6 +107,19 @@ int ref_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
                    int R, int gamma, int r, int V, float T,
                    double* c_star, double* a_star);
 
+/* Training-side loss over the drafted positions (DSpark section 9),
+ * teacher-forced on the labels y [R,gamma] (the bias of position k uses
+ * y_{k-1}, y_0 = x0); q [R,gamma] confidence logits.  Per position
+ * ce = -log p_d(y_k), l1 = ||p_d - p_t||_1, bce = BCE-with-logits(q, c*),
+ * weights w_k = exp(-(k-1)/gamma):
+ *   *loss = sum w_k (a_ce ce + a_tv l1 + a_conf bce) / sum w_k
+ * Optional: terms [R,gamma,3] = (ce, l1, bce); dq [R,gamma] = d loss / dq.
+ * Returns 0, or -1 on a bad argument or token. */
+int ref_draft_loss(const float* U, const void* W1, const void* W2, int w_dtype,
+                   const int32_t* x0, const int32_t* y, const float* Lt, const float* q,
+                   int R, int gamma, int r, int V, float T, float a_ce, float a_tv, float a_conf,
+                   double* loss, double* terms, double* dq);
+
 /* Hardware-aware prefix scheduler.
  *   c   [R,gamma] confidences in [0,1];  sps[B-1] = SPS(B) for B = 1..B_max
  * Outputs: ell [R], a [R,gamma] (may be NULL), *K_star, *theta_star,
