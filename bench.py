@@ -306,6 +306,33 @@ def main():
                  "K_star": int(so[2].item()), "K_used_async": int(ao[2].item())}
         del sws
 
+    # the training-side loss over the same rows (teacher-forced on seeded
+    # labels): draft row statistics, target row statistics, the sweep, the
+    # terms and their weighted mean
+    loss_info = None
+    if not args.profile_only:
+        yl = torch.from_numpy(workloads.loss_labels(cfg)).to(dev)
+        ql = torch.from_numpy(workloads.confidence_logits(cfg)).to(dev)
+        lo = spec.spec_draft_loss(U, W1, W2p, x0, yl, Lt, ql, cfg.T, ws=ws, stream=stream)
+        for _ in range(3):
+            spec.spec_draft_loss(U, W1, W2p, x0, yl, Lt, ql, cfg.T, loss=lo[0], terms=lo[1], dq=lo[2], ws=ws,
+                                 stream=stream)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nl = max(10, args.steps // 4)
+        a0.record(stream)
+        for _ in range(nl):
+            spec.spec_draft_loss(U, W1, W2p, x0, yl, Lt, ql, cfg.T, loss=lo[0], terms=lo[1], dq=lo[2], ws=ws,
+                                 stream=stream)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) * 1e3 / nl
+        lb = 2.0 * R * g * V * 4 + V * cfg.r * (2 if cfg.bf16 else 4)   # U, g target rows, W2 once
+        loss_info = {"workload": "%s shape, uniform labels, q ~ N(0, 1.5^2), coefficients (0.1, 0.9, 1.0)" % cfg.name,
+                     "us_per_call": round(us, 2), "positions_per_s": round(R * g / (us * 1e-6), 1),
+                     "algorithmic_bytes": lb, "algorithmic_GBs": round(lb / (us * 1e-6) / 1e9, 1),
+                     "loss": round(float(lo[0].item()), 6)}
+        del yl, ql, lo
+
     acc = float(n_acc.float().mean())
     cmean = float(c_star.float().mean())
     flags = spec.spec_device_status(ws)
@@ -351,6 +378,7 @@ def main():
         "kernels": kernels,
         "multi_round": multi,
         "scheduler": sched,
+        "training_loss": loss_info,
         "mean_n_acc": round(acc, 4),
         "mean_c_star": round(cmean, 4),
         "device_status": flags,

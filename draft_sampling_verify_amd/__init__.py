@@ -7,8 +7,8 @@ include/spec.h); this package is its thin ctypes binding.  See
 from ._binding import (  # noqa: F401
     LIB_PATH, SPEC_BF16, SPEC_DEV_BAD_CONFIDENCE, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_TOKEN,
     SPEC_DEV_WAIT_FAILED, SPEC_EDEVICE, SPEC_EDTYPE, SPEC_EINVAL, SPEC_ELAUNCH, SPEC_EUNSUPPORTED,
-    SPEC_EWORKSPACE, SPEC_F32, SPEC_OK, SPEC_OP_CONFIDENCE, SPEC_OP_PROPOSE, SPEC_OP_ROUNDS,
-    SPEC_OP_SCHEDULE, SPEC_OP_VERIFY, SpecError, Workspace, lib, spec_confidence, spec_decode_rounds,
+    SPEC_EWORKSPACE, SPEC_F32, SPEC_OK, SPEC_OP_CONFIDENCE, SPEC_OP_LOSS, SPEC_OP_PROPOSE,
+    SPEC_OP_ROUNDS, SPEC_OP_SCHEDULE, SPEC_OP_VERIFY, SpecError, Workspace, lib, spec_confidence, spec_decode_rounds, spec_draft_loss,
     spec_device_status, spec_markov_propose, spec_pack_w2, spec_packed_w2_bytes, spec_profile_enable,
     spec_profile_names, spec_profile_read, spec_profile_reset, spec_schedule, spec_schedule_async,
     spec_set_propose_fused,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libspec.so")
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH, SPEC_EDEVICE, SPEC_EUNSUPPORTED = range(7)
 SPEC_F32, SPEC_BF16 = 0, 1
-SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE, SPEC_OP_ROUNDS = range(5)
+SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE, SPEC_OP_ROUNDS, SPEC_OP_LOSS = range(6)
 SPEC_DEV_BAD_TOKEN, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_CONFIDENCE, SPEC_DEV_WAIT_FAILED = 1, 2, 4, 8
 
 
@@ -44,6 +44,7 @@ _SIGS = {
     "spec_confidence": ([P, P, P, I, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P], I),
     "spec_schedule": ([P, I, I, P, I, P, P, P, P, P, SZ, P], I),
     "spec_schedule_async": ([P, I, I, P, I, P, P, P, P, P, P, P, SZ, P], I),
+    "spec_draft_loss": ([P, P, P, I, P, P, P, P, I, I, I, I, F, F, F, F, P, P, P, P, SZ, P], I),
     "spec_decode_rounds": ([P, P, P, I, P, P, I, I, I, I, F, I, U64, U64, I, P, P, P, P, P, P, SZ, P], I),
     "spec_status_str": ([I], ctypes.c_char_p),
     "spec_set_propose_fused": ([I], I),
@@ -155,7 +156,7 @@ class Workspace:
 
     def __init__(self, R, gamma, r, V, B_max=0, device=None):
         need = max(spec_workspace_bytes(op, R, gamma, r, V, max(B_max, R))
-                   for op in (SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_ROUNDS))
+                   for op in (SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_ROUNDS, SPEC_OP_LOSS))
         if need == 0:
             raise SpecError(SPEC_EINVAL, "Workspace")
         self.tensor = torch.empty(need, dtype=torch.uint8, device=device or "cuda")
@@ -280,6 +281,32 @@ def spec_confidence(U, W1, W2p, x0, x, Lt, T, pd_stats=None, c_star=None, a_star
                                ws.nbytes, _stream(stream))
     _check(st, "spec_confidence")
     return c_star, a_star
+
+
+def spec_draft_loss(U, W1, W2p, x0, y, Lt, q, T, alphas=(0.1, 0.9, 1.0), loss=None, terms=None, dq=None,
+                    want_terms=True, want_dq=True, ws=None, stream=None):
+    """Training-side loss over the drafted positions, teacher-forced on the
+    labels y.  Returns (loss [1] fp64, terms [R,gamma,3] fp32 or None,
+    dq [R,gamma] fp32 or None)."""
+    R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
+    dev = U.device
+    _need(y, (R, gamma), torch.int32, "y")
+    _need(Lt, (R, gamma + 1, V), torch.float32, "Lt")
+    _need(q, (R, gamma), torch.float32, "q")
+    _need(loss, (1,), torch.float64, "loss")
+    _need(terms, (R, gamma, 3), torch.float32, "terms")
+    _need(dq, (R, gamma), torch.float32, "dq")
+    loss = torch.empty(1, dtype=torch.float64, device=dev) if loss is None else loss
+    if terms is None and want_terms:
+        terms = torch.empty((R, gamma, 3), dtype=torch.float32, device=dev)
+    if dq is None and want_dq:
+        dq = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    ws = _ws(ws, R, gamma, r, V, dev)
+    st = lib().spec_draft_loss(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(y), _ptr(Lt), _ptr(q), R,
+                               gamma, r, V, float(T), float(alphas[0]), float(alphas[1]), float(alphas[2]),
+                               _ptr(loss), _ptr(terms), _ptr(dq), ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "spec_draft_loss")
+    return loss, terms, dq
 
 
 def spec_schedule(c, sps, ell=None, a=None, K_star=None, theta_star=None, want_a=True, ws=None,

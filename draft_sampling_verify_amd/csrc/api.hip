@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -160,6 +161,12 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
         return rounds_scratch_offset(pb, vb) + spec::align256((size_t)R * gamma * 4) +
                spec::align256((size_t)R * gamma * 8);
     }
+    case SPEC_OP_LOSS:
+        if (check_draft(nullptr, nullptr, nullptr, SPEC_BF16, nullptr, 0, gamma, r, V, 1.0f) != SPEC_OK || R < 0 ||
+            R > MAX_R)
+            return 0;
+        spec::carve_verify(nullptr, R, gamma, V, true, &bytes, true);
+        return bytes;
     case SPEC_OP_SCHEDULE:
         if (R < 1 || gamma < 1 || (long)R * gamma > spec::SCHED_MAX_ENTRIES || B_max < R) return 0;
         return spec::WS_HEADER;
@@ -260,6 +267,29 @@ int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
     DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, 0, 0, 0, ws);
     return launch_status(
         spec::launch_confidence(a, pd_stats, Lt, c_star, a_star, w, (hipStream_t)stream));
+}
+
+int spec_draft_loss(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0,
+                    const int32_t* y, const float* Lt, const float* q, int R, int gamma, int r, int V, float T,
+                    float a_ce, float a_tv, float a_conf, double* loss, float* terms, float* dq, void* ws,
+                    size_t ws_bytes, spec_stream_t stream)
+{
+    int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
+    if (st != SPEC_OK) return st;
+    if (!loss || !std::isfinite(a_ce) || !std::isfinite(a_tv) || !std::isfinite(a_conf)) return SPEC_EINVAL;
+    if (R > 0 && (!y || !Lt || !q)) return SPEC_EINVAL;
+    if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
+    const size_t need = spec_workspace_bytes(SPEC_OP_LOSS, R, gamma, r, V, 0);
+    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_EINVAL;  // the mean over no positions is undefined
+    const spec::VerifyWs w = spec::carve_verify(ws, R, gamma, V, true, nullptr, true);
+    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, y, R, gamma, r, V, T, 0, 0, 0, ws);
+    spec::LossArgs l{};
+    l.q = q;
+    l.invT = (float)(1.0 / (double)T);
+    l.a_ce = a_ce; l.a_tv = a_tv; l.a_conf = a_conf;
+    l.loss = loss; l.terms = terms; l.dq = dq;
+    return launch_status(spec::launch_draft_loss(a, Lt, l, w, (hipStream_t)stream));
 }
 
 int spec_decode_rounds(const float* U, const void* W1, const void* W2p, int w_dtype, const int32_t* x0,

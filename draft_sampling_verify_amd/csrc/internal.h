@@ -53,9 +53,11 @@ struct VerifyWs {
     float2* dgran;   // confidence only: [VR, n_gran] draft per-granule stats
     int32_t* dgidx;  // confidence only
     float2* drow;    // confidence only: [VR] draft (M, S)
+    double* contrib; // loss only: [VR] weighted loss of each position
 };
 
-inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence, size_t* bytes)
+inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence, size_t* bytes,
+                             bool loss = false)
 {
     const size_t ng = (size_t)n_granules(V);
     const size_t VR = (size_t)R * gamma;
@@ -77,6 +79,7 @@ inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence,
         w.dgidx = c.take<int32_t>(VR * ng);
         w.drow = c.take<float2>(VR);
     }
+    if (loss) w.contrib = c.take<double>(VR);
     if (bytes) *bytes = c.off;
     return w;
 }
@@ -152,6 +155,16 @@ hipError_t launch_verify(const DraftArgs& a, const float* pd_stats, const float*
                          float* c_star, const VerifyWs& w, int32_t* counts, hipStream_t s);
 hipError_t launch_confidence(const DraftArgs& a, const float* pd_stats, const float* Lt,
                              float* c_star, double* a_star, const VerifyWs& w, hipStream_t s);
+struct LossArgs {
+    const float* q;          // [R,gamma] confidence logits
+    float invT;              // 1 / T
+    float a_ce, a_tv, a_conf;
+    double* loss;            // [1]
+    float* terms;            // [R,gamma,3] or NULL
+    float* dq;               // [R,gamma] or NULL
+};
+hipError_t launch_draft_loss(const DraftArgs& a, const float* Lt, const LossArgs& l, const VerifyWs& w,
+                             hipStream_t s);
 
 // schedule.hip
 hipError_t launch_schedule(const float* c, int R, int gamma, const float* sps, int B_max,

@@ -986,6 +986,78 @@ __global__ __launch_bounds__(TILE_THREADS) void k_conf_finalize(const float2* vp
     }
 }
 
+// ------------------------------------------------------- training loss
+
+// One wave per drafted position f = (r, k): the TV mass over the granule
+// records (same order as k_conf_finalize, so c* is the same), the draft
+// log-probability of the label from the draft row's (M, S) and the bias the
+// sweep recorded at it, the confidence BCE, the position weight
+// w_k = exp(-(k-1)/gamma) and d loss / dq.  A position whose label chain
+// holds an id outside [0, V) gets NaN terms, no contribution, and the flag.
+__global__ __launch_bounds__(TILE_THREADS) void k_loss_terms(const float2* vpart, const float* vbias, const float* U,
+                                                             const float* dstats, const float* q, const int32_t* x0,
+                                                             const int32_t* y, int R, int gamma, int V, int n_gran,
+                                                             float invT, float a_ce, float a_tv, float a_conf,
+                                                             double inv_wsum, float* terms, float* dq,
+                                                             double* contrib, uint32_t* status)
+{
+    const int f = blockIdx.x * (TILE_THREADS / WAVE) + threadIdx.x / WAVE;
+    const int lane = threadIdx.x & (WAVE - 1);
+    if (f >= R * gamma) return;
+    const int r = f / gamma, k = f - r * gamma + 1;
+    // the chain of labels up to this position: the anchor and y_1 .. y_k
+    bool bad = lane == 0 && (x0[r] < 0 || x0[r] >= V);
+    for (int j = lane; j < k; j += WAVE) bad = bad || y[(size_t)r * gamma + j] < 0 || y[(size_t)r * gamma + j] >= V;
+    if (__any(bad)) {
+        if (lane == 0) {
+            raise_flag(status, 1u);
+            contrib[f] = 0.0;
+            if (terms) terms[3 * (size_t)f] = terms[3 * (size_t)f + 1] = terms[3 * (size_t)f + 2] = NAN;
+            if (dq) dq[f] = NAN;
+        }
+        return;
+    }
+    const float2* vp = vpart + (size_t)f * n_gran;
+    float s = 0.0f;
+    for (int g = lane; g < n_gran; g += WAVE) s += vp[g].x;
+    const float l1 = wave_sum(s);
+    if (lane == 0) {
+        const float cs = fminf(fmaxf(1.0f - 0.5f * l1, 0.0f), 1.0f);
+        const int yk = y[f];
+        const float zy = U[(size_t)f * V + yk] + vbias[f];
+        const float ce = logf(dstats[2 * (size_t)f + 1]) - (zy - dstats[2 * (size_t)f]) * invT;
+        const float qv = q[f];
+        const float bce = fmaxf(qv, 0.0f) - qv * cs + log1pf(expf(-fabsf(qv)));
+        const double wk = exp(-(double)(k - 1) / (double)gamma);
+        contrib[f] = wk * ((double)a_ce * ce + (double)a_tv * l1 + (double)a_conf * bce);
+        if (terms) {
+            terms[3 * (size_t)f] = ce;
+            terms[3 * (size_t)f + 1] = l1;
+            terms[3 * (size_t)f + 2] = bce;
+        }
+        if (dq) dq[f] = (float)(wk * (double)a_conf * (double)(1.0f / (1.0f + expf(-qv)) - cs) * inv_wsum);
+    }
+}
+
+// The weighted mean: one workgroup, contributions summed in a fixed order
+// (lane-strided, then waves), so the loss is deterministic.
+__global__ __launch_bounds__(TILE_THREADS) void k_loss_reduce(const double* contrib, int n, double inv_wsum,
+                                                              double* loss)
+{
+    __shared__ double sw[TILE_THREADS / WAVE];
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    double s = 0.0;
+    for (int i = t; i < n; i += TILE_THREADS) s += contrib[i];
+    s = wave_sum(s);
+    if (lane == 0) sw[w] = s;
+    __syncthreads();
+    if (t == 0) {
+        double tot = 0.0;
+        for (int i = 0; i < TILE_THREADS / WAVE; ++i) tot += sw[i];
+        *loss = tot * inv_wsum;
+    }
+}
+
 // ------------------------------------------------------------ launchers
 
 // Workgroups cover one granule and `bpc` consecutive 32-row blocks; the row
@@ -1160,6 +1232,42 @@ static hipError_t confidence_impl(const DraftArgs& a, const float* pd_stats, con
     return hipGetLastError();
 }
 
+// Training loss over the drafted positions, teacher-forced on the labels
+// a.x: the draft rows' (M, S) with the labels' biases, the target rows'
+// (M, S), the sweep (TV mass and the bias at each label), then the terms
+// and their weighted mean.
+template <typename WT, int KS>
+static hipError_t loss_impl(const DraftArgs& a, const float* Lt, const LossArgs& l, const VerifyWs& w,
+                            hipStream_t s)
+{
+    hipError_t e = launch_draft_row_stats(a, w, s);
+    if (e != hipSuccess) return e;
+    const float* dstats = reinterpret_cast<const float*>(w.drow);
+    const int P = a.gamma;  // no bonus row
+    e = target_pass(a, Lt, P, a.R * P, w, nullptr, false, s);
+    if (e != hipSuccess) return e;
+    SweepArgs sw = make_sweep(a, dstats, Lt, P, w, nullptr, false);
+    {
+        ProfScope ps("verify_sweep", s);
+        launch_sweep<WT, KS>(sw, s);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    double wsum = 0.0;
+    for (int k = 1; k <= a.gamma; ++k) wsum += (double)a.R * exp(-(double)(k - 1) / (double)a.gamma);
+    const int n = a.R * a.gamma;
+    {
+        ProfScope ps("loss_terms", s);
+        hipLaunchKernelGGL(k_loss_terms, dim3((n + 3) / 4), dim3(TILE_THREADS), 0, s, (const float2*)w.vpart,
+                           (const float*)w.vbias, a.U, dstats, l.q, a.x0, a.x, a.R, a.gamma, a.V, sw.n_gran,
+                           l.invT, l.a_ce, l.a_tv, l.a_conf, 1.0 / wsum, l.terms, l.dq,
+                           w.contrib, a.status);
+        hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(TILE_THREADS), 0, s, (const double*)w.contrib, n,
+                           1.0 / wsum, l.loss);
+    }
+    return hipGetLastError();
+}
+
 template <typename WT, int KS>
 struct VerifyF {
     static hipError_t run(const DraftArgs& a, const float* pd_stats, const float* Lt, const int32_t* ell,
@@ -1189,6 +1297,20 @@ hipError_t launch_confidence(const DraftArgs& a, const float* pd_stats, const fl
                              double* a_star, const VerifyWs& w, hipStream_t s)
 {
     return dispatch_ks<ConfF>(a.w_dtype, a.r, a, pd_stats, Lt, c_star, a_star, w, s);
+}
+
+template <typename WT, int KS>
+struct LossF {
+    static hipError_t run(const DraftArgs& a, const float* Lt, const LossArgs& l, const VerifyWs& w, hipStream_t s)
+    {
+        return loss_impl<WT, KS>(a, Lt, l, w, s);
+    }
+};
+
+hipError_t launch_draft_loss(const DraftArgs& a, const float* Lt, const LossArgs& l, const VerifyWs& w,
+                             hipStream_t s)
+{
+    return dispatch_ks<LossF>(a.w_dtype, a.r, a, Lt, l, w, s);
 }
 
 }  // namespace spec

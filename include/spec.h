@@ -17,6 +17,8 @@
  *   spec_schedule        per-request verify lengths l_r maximising
  *                        Theta = tau * SPS(B), B = sum_r (1 + l_r),
  *                        tau = sum_r (1 + sum_{j<=l_r} a_{r,j}) (DSpark section 6)
+ *   spec_draft_loss      training-side loss over the same rows: CE, L1/TV
+ *                        and confidence BCE, position-weighted (section 9)
  *   spec_schedule_async  the production step: the same ranking, with the
  *                        verified count taken from the optimum two calls
  *                        earlier (a dynamic top-K)          (DSpark section 7)
@@ -87,7 +89,8 @@ enum spec_op {
     SPEC_OP_VERIFY = 1,
     SPEC_OP_CONFIDENCE = 2,
     SPEC_OP_SCHEDULE = 3,
-    SPEC_OP_ROUNDS = 4  /* spec_decode_rounds */
+    SPEC_OP_ROUNDS = 4, /* spec_decode_rounds */
+    SPEC_OP_LOSS = 5    /* spec_draft_loss */
 };
 
 /* Bits of the device status word. */
@@ -253,6 +256,31 @@ int spec_confidence(const float* U, const void* W1, const void* W2p, int w_dtype
 int spec_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
                   int32_t* ell, double* a, int32_t* K_star, double* theta_star,
                   void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Training-side loss of the draft over the same rows (DSpark section 9: a
+ * cross-entropy, an L1/TV distribution-matching term and the confidence BCE
+ * against the soft label c*, with position weights; DeepSpec's configuration
+ * in section 8 uses a_ce = 0.1, a_tv = 0.9, a_conf = 1.0).  Teacher-forced:
+ * position k's bias uses the label y_{k-1} (y_0 = x0), p_d = softmax((U_k +
+ * B_k)/T), p_t = softmax(Lt[r,k-1,:]/T).  Per position
+ *   ce = -log p_d(y_k),  l1 = ||p_d - p_t||_1 (= 2 TV),
+ *   c* = clamp(1 - l1/2, 0, 1),  bce = BCE-with-logits(q_k, c*),
+ *   w_k = exp(-(k-1)/gamma),
+ *   *loss (fp64) = sum w_k (a_ce ce + a_tv l1 + a_conf bce) / sum w_k over
+ *   all R*gamma positions;
+ * terms [R,gamma,3] fp32 (optional) = (ce, l1, bce); dq [R,gamma] fp32
+ * (optional) = d loss / d q (c* is a label: no gradient flows into it).
+ * In: U, W1, W2 (packed), x0 as spec_markov_propose; y [R,gamma] int32 labels;
+ * Lt [R,gamma+1,V] (rows 0..gamma-1 used); q [R,gamma] fp32.  R >= 1.
+ * A label chain with an id outside [0, V) raises SPEC_DEV_BAD_TOKEN; those
+ * positions get NaN terms and add nothing to the sum (the denominator is
+ * unchanged). */
+int spec_draft_loss(const float* U, const void* W1, const void* W2, int w_dtype,
+                    const int32_t* x0, const int32_t* y, const float* Lt, const float* q,
+                    int R, int gamma, int r, int V, float T,
+                    float a_ce, float a_tv, float a_conf,
+                    double* loss, float* terms, float* dq,
+                    void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Production step of the scheduler (DSpark section 7): the candidates are
  * ranked by the current confidences exactly as in spec_schedule, but the

@@ -37,7 +37,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # tensor tags of the seed sequences
-_TAG_U, _TAG_NOISE, _TAG_W1, _TAG_W2, _TAG_X0, _TAG_SIGMA, _TAG_C, _TAG_SPS, _TAG_PEAK = range(9)
+_TAG_U, _TAG_NOISE, _TAG_W1, _TAG_W2, _TAG_X0, _TAG_SIGMA, _TAG_C, _TAG_SPS, _TAG_PEAK, _TAG_Y, _TAG_Q = range(11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -134,6 +134,16 @@ def confidences(cfg: Config) -> np.ndarray:
     """c_{r,k} = sigmoid(N(1.5, 1)) as float32 [R, gamma]."""
     n = _rng(cfg, _TAG_C).normal(1.5, 1.0, size=(cfg.R, cfg.gamma))
     return (1.0 / (1.0 + np.exp(-n))).astype(np.float32)
+
+
+def loss_labels(cfg: Config) -> np.ndarray:
+    """Training labels y [R, gamma] int32, uniform over the vocabulary."""
+    return _rng(cfg, _TAG_Y).integers(0, cfg.V, size=(cfg.R, cfg.gamma), dtype=np.int64).astype(np.int32)
+
+
+def confidence_logits(cfg: Config) -> np.ndarray:
+    """Confidence-head logits q [R, gamma] = N(0, 1.5^2) as float32."""
+    return _rng(cfg, _TAG_Q).normal(0.0, 1.5, size=(cfg.R, cfg.gamma)).astype(np.float32)
 
 
 def sawtooth_sps(cfg: Config, length: int | None = None) -> np.ndarray:
