@@ -689,6 +689,30 @@ struct ResolveArgs {
     uint32_t* status;
 };
 
+// Lane-strided TV mass of one row's granule records: lane l adds granules
+// l, l + 64, l + 128, ... in that order, with the loads of a batch of 16
+// issued before any of them is added, so a row costs about one memory
+// latency rather than one per granule.  Every kernel that reports c* sums in
+// this order, so verify, confidence and the loss give the same bits.
+__device__ inline float lane_tv_mass(const float2* vp, int n)
+{
+    constexpr int NB = 16;
+    const int lane = threadIdx.x & (WAVE - 1);
+    float s = 0.0f;
+    for (int g0 = 0; g0 < n; g0 += NB * WAVE) {
+        float v[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int g = g0 + lane + WAVE * i;
+            v[i] = vp[min(g, n - 1)].x;
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (g0 + lane + WAVE * i < n) s += v[i];
+    }
+    return s;
+}
+
 // One wave, over the granule records of one verified row: the total TV mass
 // (for c*) and the residual draw with uniform u.  Lane l reads granules
 // l + 64 i, all at once; rows of more than 64 NR granules take the looped
@@ -719,9 +743,7 @@ __device__ inline int resid_pick(const float2* vp, int n, float u, float& Z, flo
     const int lane = threadIdx.x & (WAVE - 1);
     const int per = (n + WAVE - 1) / WAVE;
     const int g0 = min(lane * per, n), g1 = min(g0 + per, n);
-    float sm = 0.0f;
-    for (int g = g0; g < g1; ++g) sm += vp[g].x;
-    tv = wave_sum(sm);
+    tv = wave_sum(lane_tv_mass(vp, n));
     auto wf = [&](int g) { return vp[g].y; };
     float excl;
     wave_granule_scan(wf, g0, g1, excl, Z);
@@ -951,37 +973,39 @@ __global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
 
 // --------------------------------------------------------- confidence
 
-// One wave per request: c*_k for every drafted position and the running
-// products a*_k (fp64, left to right).
+// One workgroup per request, one wave per drafted position (positions
+// k, k + 4, ... for wave k): c*_k, then the running products a*_k (fp64,
+// left to right) by one thread.
 __global__ __launch_bounds__(TILE_THREADS) void k_conf_finalize(const float2* vpart, const int32_t* x0,
                                                                 const int32_t* x, int R, int gamma, int V,
                                                                 int n_gran, float* c_star, double* a_star,
                                                                 uint32_t* status)
 {
-    const int r = blockIdx.x * (TILE_THREADS / WAVE) + threadIdx.x / WAVE;
-    const int lane = threadIdx.x & (WAVE - 1);
-    if (r >= R) return;
+    __shared__ float s_cs[64];
+    const int r = blockIdx.x;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    // every wave checks the request's ids, so each takes the same branch
     bool bad = lane == 0 && (x0[r] < 0 || x0[r] >= V);
     for (int k = lane; k < gamma; k += WAVE) bad = bad || x[(size_t)r * gamma + k] < 0 || x[(size_t)r * gamma + k] >= V;
     if (__any(bad)) {
-        if (lane == 0) raise_flag(status, 1u);
-        for (int k = lane; k < gamma; k += WAVE) {
+        if (t == 0) raise_flag(status, 1u);
+        for (int k = t; k < gamma; k += TILE_THREADS) {
             c_star[(size_t)r * gamma + k] = NAN;
             if (a_star) a_star[(size_t)r * gamma + k] = NAN;
         }
         return;
     }
-    double run = 1.0;
-    for (int k = 0; k < gamma; ++k) {
-        const float2* vp = vpart + ((size_t)r * gamma + k) * n_gran;
-        float s = 0.0f;
-        for (int g = lane; g < n_gran; g += WAVE) s += vp[g].x;
-        s = wave_sum(s);
-        float cs = fminf(fmaxf(1.0f - 0.5f * s, 0.0f), 1.0f);
-        run *= (double)cs;
-        if (lane == 0) {
-            c_star[(size_t)r * gamma + k] = cs;
-            if (a_star) a_star[(size_t)r * gamma + k] = run;
+    for (int k = w; k < gamma; k += TILE_THREADS / WAVE) {
+        const float tv = wave_sum(lane_tv_mass(vpart + ((size_t)r * gamma + k) * n_gran, n_gran));
+        if (lane == 0) s_cs[k] = fminf(fmaxf(1.0f - 0.5f * tv, 0.0f), 1.0f);
+    }
+    __syncthreads();
+    if (t < gamma) c_star[(size_t)r * gamma + t] = s_cs[t];
+    if (a_star && t == 0) {
+        double run = 1.0;
+        for (int k = 0; k < gamma; ++k) {
+            run *= (double)s_cs[k];
+            a_star[(size_t)r * gamma + k] = run;
         }
     }
 }
@@ -989,7 +1013,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_conf_finalize(const float2* vp
 // ------------------------------------------------------- training loss
 
 // One wave per drafted position f = (r, k): the TV mass over the granule
-// records (same order as k_conf_finalize, so c* is the same), the draft
+// records (in the order every c* is summed), the draft
 // log-probability of the label from the draft row's (M, S) and the bias the
 // sweep recorded at it, the confidence BCE, the position weight
 // w_k = exp(-(k-1)/gamma) and d loss / dq.  A position whose label chain
@@ -1017,10 +1041,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_loss_terms(const float2* vpart
         }
         return;
     }
-    const float2* vp = vpart + (size_t)f * n_gran;
-    float s = 0.0f;
-    for (int g = lane; g < n_gran; g += WAVE) s += vp[g].x;
-    const float l1 = wave_sum(s);
+    const float l1 = wave_sum(lane_tv_mass(vpart + (size_t)f * n_gran, n_gran));
     if (lane == 0) {
         const float cs = fminf(fmaxf(1.0f - 0.5f * l1, 0.0f), 1.0f);
         const int yk = y[f];
@@ -1225,7 +1246,7 @@ static hipError_t confidence_impl(const DraftArgs& a, const float* pd_stats, con
     if (e != hipSuccess) return e;
     {
         ProfScope ps("conf_finalize", s);
-        hipLaunchKernelGGL(k_conf_finalize, dim3((a.R + 3) / 4), dim3(TILE_THREADS), 0, s,
+        hipLaunchKernelGGL(k_conf_finalize, dim3(a.R), dim3(TILE_THREADS), 0, s,
                            (const float2*)w.vpart, a.x0, a.x, a.R, a.gamma, a.V, sw.n_gran, c_star, a_star,
                            a.status);
     }
