@@ -473,6 +473,32 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
         load_u(1, ua);
         park_u(ua);
     }
+    // U of position kn + 1 (0-based row kn), parked in the result tile while
+    // the other workgroups finish, in four waited chunks: spread out, the
+    // 16 MB of all workgroups do not queue ahead of the small hand-over loads
+    auto park_next = [&](int kn) {
+        const int tt = opaque_v(threadIdx.x);
+        const int row = tt & 31, ww = tt / WAVE, hh = (tt >> 5) & 1;
+        const float* urow = p.U + ((size_t)(row < R ? row : 0) * p.gamma + kn) * p.V;
+        float* dst = sZ + row * ZS + 32 * ww + 4 * hh;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = g * GRAN + 32 * ww + 8 * q + 4 * hh;
+            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (row < R) {
+                if (p.vec4 && c + 3 < p.V) {
+                    v = *reinterpret_cast<const float4*>(urow + c);
+                } else {
+                    v.x = c < p.V ? urow[c] : -INFINITY;
+                    v.y = c + 1 < p.V ? urow[c + 1] : -INFINITY;
+                    v.z = c + 2 < p.V ? urow[c + 2] : -INFINITY;
+                    v.w = c + 3 < p.V ? urow[c + 3] : -INFINITY;
+                }
+            }
+            *reinterpret_cast<float4*>(dst + 8 * q) = v;
+            stores_done();
+        }
+    };
 
     bool failed = false;
     for (int k = 1; k <= p.gamma && !failed; ++k) {
@@ -559,32 +585,7 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
             }
         }
         __syncthreads();          // the tile's reads are complete
-        if (k < p.gamma) {
-            // the next position's U, parked while the other workgroups finish,
-            // in four waited chunks: spread out, the 16 MB of all workgroups
-            // do not queue ahead of the small hand-over loads
-            const int tt = opaque_v(threadIdx.x);
-            const int row = tt & 31, ww = tt / WAVE, hh = (tt >> 5) & 1;
-            const float* urow = p.U + ((size_t)(row < R ? row : 0) * p.gamma + k) * p.V;
-            float* dst = sZ + row * ZS + 32 * ww + 4 * hh;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = g * GRAN + 32 * ww + 8 * q + 4 * hh;
-                float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                if (row < R) {
-                    if (p.vec4 && c + 3 < p.V) {
-                        v = *reinterpret_cast<const float4*>(urow + c);
-                    } else {
-                        v.x = c < p.V ? urow[c] : -INFINITY;
-                        v.y = c + 1 < p.V ? urow[c + 1] : -INFINITY;
-                        v.z = c + 2 < p.V ? urow[c + 2] : -INFINITY;
-                        v.w = c + 3 < p.V ? urow[c + 3] : -INFINITY;
-                    }
-                }
-                *reinterpret_cast<float4*>(dst + 8 * q) = v;
-                stores_done();
-            }
-        }
+        if (k < p.gamma) park_next(k);
 
         // ---------------- pick phase (W2 registers are free here: reloaded below)
         if (g < R) {

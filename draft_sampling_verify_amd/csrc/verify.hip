@@ -498,15 +498,27 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
     const int nrows = p.max_rows;
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
     const long NU = (long)p.n_gran * n_rb;
-    const int u0 = (int)((long)blockIdx.x * NU / gridDim.x);
-    const int nu = (int)((long)(blockIdx.x + 1) * NU / gridDim.x) - u0;
+    // Run rho of the logical order: consecutive runs sit on one XCD.  Even
+    // runs go forward and odd runs backward, so the two runs that share a
+    // boundary granule both take it at their start or both at their end,
+    // and its W2 slice comes from HBM once for the two (the other load hits
+    // the XCD's L2).
+    const int rho = xcd_logical(blockIdx.x, gridDim.x);
+    const int u0 = (int)((long)rho * NU / gridDim.x);
+    const int nu = (int)((long)(rho + 1) * NU / gridDim.x) - u0;
     if (nu <= 0) return;
+    const bool fwd = (rho & 1) == 0;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
-    // unit j of this run (j may pass the run's end: only tokens and row
-    // context are loaded for such units, and they are never used)
-    auto ugran = [&](int j) { return (u0 + j) / n_rb; };
-    auto urow = [&](int j, int i) { return ((u0 + j) % n_rb) * BLOCK_ROWS + i; };
+    // unit j of this run (j may pass the run's end: such units repeat the
+    // last one, only their tokens and row context are loaded, and they are
+    // never used)
+    auto unit = [&](int j) {
+        const int jj = min(j, nu - 1);
+        return fwd ? u0 + jj : u0 + nu - 1 - jj;
+    };
+    auto ugran = [&](int j) { return unit(j) / n_rb; };
+    auto urow = [&](int j, int i) { return (unit(j) % n_rb) * BLOCK_ROWS + i; };
 
     // buffers of even and odd units
     __shared__ __align__(16) char sB0[SW::BYTES], sB1[SW::BYTES];  // W1 tiles
@@ -1161,12 +1173,17 @@ static void launch_sweep(const SweepArgs& sw, hipStream_t s)
             // as many workgroups as fit at once, each with one run of units
             const long units = (long)sw.n_gran * ((sw.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
             const dim3 blk2(2 * TILE_THREADS);
+            // (a multiple of the XCD count, rounded down unless that is zero)
+            auto grid_of = [&](int slots) {
+                const long n = std::min<long>(slots, units);
+                return (unsigned)(n >= NUM_XCD ? n / NUM_XCD * NUM_XCD : xcd_grid((int)n));
+            };
             if (sw.vec4) {
-                const dim3 grid2((unsigned)std::min<long>(sweep_ws_slots<KS, true>(), units));
-                hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), grid2, blk2, 0, s, sw);
+                hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), dim3(grid_of(sweep_ws_slots<KS, true>())), blk2, 0,
+                                   s, sw);
             } else {
-                const dim3 grid2((unsigned)std::min<long>(sweep_ws_slots<KS, false>(), units));
-                hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), grid2, blk2, 0, s, sw);
+                hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), dim3(grid_of(sweep_ws_slots<KS, false>())), blk2,
+                                   0, s, sw);
             }
             return;
         }
