@@ -18,6 +18,12 @@ Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
   draft_loss        pinned: scipy log-softmax cross-entropy, identical rows
                     (l1 = 0, c* = 1), l1 = 2(1 - c*) against confidence,
                     finite differences of dq, closed form at V = 2
+  cluster_propose   pinned: numpy top-K and softmax over the expanded set,
+                    full expansion with contiguous clusters = the plain
+                    inverse CDF over the whole softmax, chi-square of draws
+  cluster_verify    pinned: chi-square of emitted tokens vs p_t (lossless
+                    with a sparse draft), P(accept) = c*, full expansion =
+                    the Markov verify with U = H E^T and W2 = 0
 """
 from __future__ import annotations
 
@@ -80,6 +86,12 @@ def lib():
                                          P, P]
         L.ref_draft_loss.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, f32, f32, f32, f32, P, P, P]
+        L.ref_cluster_propose.argtypes = [P, P, P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, f32, ctypes.c_int, u64, u64,
+                                          P, P, P, P, P, P]
+        L.ref_cluster_verify.argtypes = [P, P, ctypes.c_int, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, f32, ctypes.c_int,
+                                         u64, u64, P, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -199,6 +211,57 @@ def confidence(U, W1, W2, x0, x, Lt, T):
     if st != 0:
         raise OracleError("ref_confidence rejected its arguments")
     return c, a
+
+
+def _mats(*arrays):
+    """float32 arrays, or bf16 given as uint16 bits (one dtype for all)."""
+    if arrays[0].dtype == np.uint16:
+        return [_c(a, np.uint16) for a in arrays] + [BF16]
+    return [_c(a, np.float32) for a in arrays] + [F32]
+
+
+def cluster_propose(H, C, E, cl_off, cl_tok, K_c, T, greedy=False, seed=1, rnd=0):
+    """Clustered draft head (ref_cluster_propose).  H [R,g,d], C [N_c,d],
+    E [V,d]; returns dict(x, pd_x, sel [R,g,K_c], pd_stats, cut, margin)."""
+    H, C, E, dt = _mats(H, C, E)
+    R, g, d = H.shape
+    N_c, V = C.shape[0], E.shape[0]
+    cl_off, cl_tok = _c(cl_off, np.int32), _c(cl_tok, np.int32)
+    o = dict(x=np.zeros((R, g), np.int32), pd_x=np.zeros((R, g)), sel=np.zeros((R, g, K_c), np.int32),
+             pd_stats=np.zeros((R, g, 2)), cut=np.zeros((R, g)), margin=np.zeros((R, g)))
+    st = lib().ref_cluster_propose(_p(H), _p(C), _p(E), dt, _p(cl_off), _p(cl_tok), R, g, d, N_c, int(K_c), V,
+                                   float(T), int(bool(greedy)), seed, rnd, _p(o["x"]), _p(o["pd_x"]),
+                                   _p(o["sel"]), _p(o["pd_stats"]), _p(o["cut"]), _p(o["margin"]))
+    if st != 0:
+        raise OracleError("ref_cluster_propose rejected its arguments")
+    return o
+
+
+def cluster_verify(H, E, cl_off, cl_tok, sel, x, Lt, T, greedy=False, seed=1, rnd=0, ell=None, N_c=None):
+    """Verification of clustered-head drafts (ref_cluster_verify), given the
+    selection sel; returns the same dict as verify()."""
+    H, E, dt = _mats(H, E)
+    R, g, d = H.shape
+    V = E.shape[0]
+    cl_off, cl_tok = _c(cl_off, np.int32), _c(cl_tok, np.int32)
+    N_c = cl_off.size - 1 if N_c is None else N_c
+    sel, x = _c(sel, np.int32), _c(x, np.int32)
+    K_c = sel.shape[-1]
+    Lt = _c(Lt, np.float32)
+    assert Lt.shape == (R, g + 1, V)
+    ell = _c(ell, np.int32)
+    o = dict(n_acc=np.zeros(R, np.int32), y=np.zeros((R, g + 1), np.int32),
+             pt_x=np.zeros((R, g)), pd_x=np.zeros((R, g)), c_star=np.zeros((R, g)),
+             acc=np.zeros((R, g), np.int32), acc_margin=np.zeros((R, g)),
+             y_alt=np.zeros((R, g + 1), np.int32), y_margin=np.zeros((R, g + 1)))
+    st = lib().ref_cluster_verify(_p(H), _p(E), dt, _p(cl_off), _p(cl_tok), _p(sel), _p(x), _p(Lt), _p(ell),
+                                  R, g, d, N_c, K_c, V, float(T), int(bool(greedy)), seed, rnd,
+                                  _p(o["n_acc"]), _p(o["y"]), _p(o["pt_x"]), _p(o["pd_x"]),
+                                  _p(o["c_star"]), _p(o["acc"]), _p(o["acc_margin"]), _p(o["y_alt"]),
+                                  _p(o["y_margin"]))
+    if st != 0:
+        raise OracleError("ref_cluster_verify rejected its arguments")
+    return o
 
 
 def draft_loss(U, W1, W2, x0, y, Lt, q, T, alphas=(0.1, 0.9, 1.0)):

@@ -204,28 +204,46 @@ int ref_markov_propose(const float* U, const void* W1, const void* W2, int w_dty
 
 /* ------------------------------------------------------------------ verify */
 
+/* The draft distribution of one drafted position: fills pd[0..V) for row
+ * `row`, position k (1-based), previous token xprev; returns 0, or -1 when
+ * the inputs name a token outside [0, V). */
+typedef int (*draft_pd_fn)(const void* ctx, int row, int k, int32_t xprev, double* pd);
+
+struct markov_ctx {
+    const float* U; const void* W1; const void* W2; int w_dtype;
+    int gamma, r, V; double T; double* z;
+};
+
+static int markov_pd(const void* vctx, int row, int k, int32_t xprev, double* pd)
+{
+    const struct markov_ctx* c = (const struct markov_ctx*)vctx;
+    if (xprev < 0 || xprev >= c->V) return -1;
+    draft_logits(c->U, c->W1, c->W2, c->w_dtype, row, k, c->gamma, c->r, c->V, xprev, c->z);
+    softmax_T(c->z, c->V, c->T, pd, NULL, NULL);
+    return 0;
+}
+
 /* Lossless verification (standard rejection rule; see ref.h): accept x_k with
  * probability min(1, p_t(x_k)/p_d(x_k)); at the first rejection draw from
  * normalize(max(0, p_t - p_d)) (p_t itself if that mass is zero); after a
  * full accept draw the bonus token from the next target row.  c*_k follows
- * the DSpark page, section 5, for every verified position. */
-int ref_verify(const float* U, const void* W1, const void* W2, int w_dtype,
-               const int32_t* x0, const int32_t* x, const float* Lt, const int32_t* ell,
-               int R, int gamma, int r, int V, float T, int greedy,
-               uint64_t seed, uint64_t round, const int32_t* req_ids,
-               int32_t* n_acc, int32_t* y, double* pt_x, double* pd_x, double* c_star,
-               int32_t* acc, double* acc_margin, int32_t* y_alt, double* y_margin)
+ * the DSpark page, section 5, for every verified position.  The draft
+ * distribution comes from draft_pd; x0 (may be NULL) starts the chain of
+ * previous tokens it receives. */
+static int verify_core(draft_pd_fn draft_pd, const void* ctx,
+                       const int32_t* x0, const int32_t* x, const float* Lt, const int32_t* ell,
+                       int R, int gamma, int V, float T, int greedy,
+                       uint64_t seed, uint64_t round, const int32_t* req_ids,
+                       int32_t* n_acc, int32_t* y, double* pt_x, double* pd_x, double* c_star,
+                       int32_t* acc, double* acc_margin, int32_t* y_alt, double* y_margin)
 {
-    if (bad_common(U, W1, W2, w_dtype, x0, R, gamma, r, V, T) || !x || !Lt || !n_acc || !y)
-        return -1;
     const double Td = (double)T;
-    double* z = (double*)malloc(sizeof(double) * (size_t)V);
     double* pd = (double*)malloc(sizeof(double) * (size_t)V);
     double* lt = (double*)malloc(sizeof(double) * (size_t)V);
     double* pt = (double*)malloc(sizeof(double) * (size_t)V);
     double* res = (double*)malloc(sizeof(double) * (size_t)V);
-    if (!z || !pd || !lt || !pt || !res) {
-        free(z); free(pd); free(lt); free(pt); free(res);
+    if (!pd || !lt || !pt || !res) {
+        free(pd); free(lt); free(pt); free(res);
         return -1;
     }
     int status = 0;
@@ -249,13 +267,11 @@ int ref_verify(const float* U, const void* W1, const void* W2, int w_dtype,
         }
         int first_reject = 0; /* 1-based; 0 = none */
         int32_t residual_tok = -1;
-        int32_t xprev = x0[row];
+        int32_t xprev = x0 ? x0[row] : -1;
         for (int k = 1; k <= L; ++k) {
             size_t o = (size_t)row * gamma + (size_t)(k - 1);
             int32_t xk = x[o];
-            if (xprev < 0 || xprev >= V || xk < 0 || xk >= V) { status = -1; break; }
-            draft_logits(U, W1, W2, w_dtype, row, k, gamma, r, V, xprev, z);
-            softmax_T(z, V, Td, pd, NULL, NULL);
+            if (xk < 0 || xk >= V || draft_pd(ctx, row, k, xprev, pd) != 0) { status = -1; break; }
             const float* lrow = Lt + ((size_t)row * (gamma + 1) + (size_t)(k - 1)) * (size_t)V;
             for (int v = 0; v < V; ++v)
                 lt[v] = (double)lrow[v];
@@ -334,8 +350,26 @@ int ref_verify(const float* U, const void* W1, const void* W2, int w_dtype,
             y[(size_t)row * (gamma + 1) + (size_t)k] = x[(size_t)row * gamma + (size_t)k];
         y[(size_t)row * (gamma + 1) + (size_t)na] = first_reject ? residual_tok : bonus;
     }
-    free(z); free(pd); free(lt); free(pt); free(res);
+    free(pd); free(lt); free(pt); free(res);
     return status;
+}
+
+int ref_verify(const float* U, const void* W1, const void* W2, int w_dtype,
+               const int32_t* x0, const int32_t* x, const float* Lt, const int32_t* ell,
+               int R, int gamma, int r, int V, float T, int greedy,
+               uint64_t seed, uint64_t round, const int32_t* req_ids,
+               int32_t* n_acc, int32_t* y, double* pt_x, double* pd_x, double* c_star,
+               int32_t* acc, double* acc_margin, int32_t* y_alt, double* y_margin)
+{
+    if (bad_common(U, W1, W2, w_dtype, x0, R, gamma, r, V, T) || !x || !Lt || !n_acc || !y)
+        return -1;
+    struct markov_ctx c = {U, W1, W2, w_dtype, gamma, r, V, (double)T, NULL};
+    c.z = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!c.z) return -1;
+    int st = verify_core(markov_pd, &c, x0, x, Lt, ell, R, gamma, V, T, greedy, seed, round, req_ids,
+                         n_acc, y, pt_x, pd_x, c_star, acc, acc_margin, y_alt, y_margin);
+    free(c.z);
+    return st;
 }
 
 /* -------------------------------------------------------------- confidence */
@@ -579,4 +613,187 @@ int ref_schedule_async(const float* c, int R, int gamma, const float* sps, int B
     K_hist[1] = *K_star;
     free(e);
     return 0;
+}
+
+/* ---------------------------------------------------- clustered draft head */
+
+/* cl_off/cl_tok partition [0, V): offsets nondecreasing from 0 to V, and
+ * every token listed exactly once. */
+static int cluster_partition_ok(const int32_t* cl_off, const int32_t* cl_tok, int N_c, int V)
+{
+    if (cl_off[0] != 0 || cl_off[N_c] != V) return 0;
+    for (int c = 0; c < N_c; ++c)
+        if (cl_off[c + 1] < cl_off[c]) return 0;
+    unsigned char* seen = (unsigned char*)calloc((size_t)V, 1);
+    if (!seen) return 0;
+    int ok = 1;
+    for (int i = 0; i < V && ok; ++i) {
+        int32_t v = cl_tok[i];
+        if (v < 0 || v >= V || seen[v]) ok = 0;
+        else seen[v] = 1;
+    }
+    free(seen);
+    return ok;
+}
+
+/* h . M[row] over d entries, in fp64. */
+static double dot_row(const void* Hm, size_t hoff, const void* M, size_t row, int w_dtype, int d)
+{
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i)
+        acc += weight_at(Hm, w_dtype, hoff + (size_t)i) * weight_at(M, w_dtype, row * (size_t)d + (size_t)i);
+    return acc;
+}
+
+/* The K_c clusters of largest coarse logit (ties: smaller index), returned in
+ * ascending cluster order; *cut = s of the last one taken minus the largest
+ * s left out (infinite when nothing is left out). */
+static void cluster_select(const void* H, size_t hoff, const void* C, int w_dtype, int d, int N_c, int K_c,
+                           double* s, unsigned char* taken, int32_t* sel, double* cut)
+{
+    for (int c = 0; c < N_c; ++c) {
+        s[c] = dot_row(H, hoff, C, (size_t)c, w_dtype, d);
+        taken[c] = 0;
+    }
+    double last = INFINITY;
+    for (int j = 0; j < K_c; ++j) {
+        int best = -1;
+        for (int c = 0; c < N_c; ++c)
+            if (!taken[c] && (best < 0 || s[c] > s[best])) best = c;
+        taken[best] = 1;
+        last = s[best];
+    }
+    double out_best = -INFINITY;
+    int n = 0;
+    for (int c = 0; c < N_c; ++c) {
+        if (taken[c]) sel[n++] = c;
+        else if (s[c] > out_best) out_best = s[c];
+    }
+    if (cut) *cut = K_c < N_c ? last - out_best : INFINITY;
+}
+
+/* Expansion of the selected clusters: ids and fine logits z = h . E[id] in
+ * expansion order; returns the count. */
+static int cluster_expand(const void* H, size_t hoff, const void* E, int w_dtype, int d,
+                          const int32_t* cl_off, const int32_t* cl_tok, const int32_t* sel, int K_c,
+                          int32_t* ids, double* z)
+{
+    int n = 0;
+    for (int j = 0; j < K_c; ++j)
+        for (int i = cl_off[sel[j]]; i < cl_off[sel[j] + 1]; ++i) {
+            ids[n] = cl_tok[i];
+            z[n] = dot_row(H, hoff, E, (size_t)cl_tok[i], w_dtype, d);
+            ++n;
+        }
+    return n;
+}
+
+static int bad_cluster(const void* H, const void* E, int w_dtype, const int32_t* cl_off, const int32_t* cl_tok,
+                       int R, int gamma, int d, int N_c, int K_c, int V, float T)
+{
+    if (!H || !E || !cl_off || !cl_tok) return 1;
+    if (w_dtype != REF_F32 && w_dtype != REF_BF16) return 1;
+    if (R < 0 || gamma < 1 || d < 1 || N_c < 1 || K_c < 1 || K_c > N_c || V < 1) return 1;
+    if (!(T > 0.0f) || isinf(T)) return 1;
+    return !cluster_partition_ok(cl_off, cl_tok, N_c, V);
+}
+
+int ref_cluster_propose(const void* H, const void* C, const void* E, int w_dtype,
+                        const int32_t* cl_off, const int32_t* cl_tok,
+                        int R, int gamma, int d, int N_c, int K_c, int V, float T,
+                        int greedy, uint64_t seed, uint64_t round,
+                        int32_t* x, double* pd_x, int32_t* sel, double* pd_stats,
+                        double* cut, double* margin)
+{
+    if (bad_cluster(H, E, w_dtype, cl_off, cl_tok, R, gamma, d, N_c, K_c, V, T) || !C || !x || !sel)
+        return -1;
+    const double Td = (double)T;
+    double* s = (double*)malloc(sizeof(double) * (size_t)N_c);
+    unsigned char* taken = (unsigned char*)malloc((size_t)N_c);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)V);
+    double* z = (double*)malloc(sizeof(double) * (size_t)V);
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!s || !taken || !ids || !z || !p) {
+        free(s); free(taken); free(ids); free(z); free(p);
+        return -1;
+    }
+    for (int row = 0; row < R; ++row)
+        for (int k = 1; k <= gamma; ++k) {
+            const size_t o = (size_t)row * gamma + (size_t)(k - 1);
+            const size_t hoff = o * (size_t)d;
+            int32_t* so = sel + o * (size_t)K_c;
+            cluster_select(H, hoff, C, w_dtype, d, N_c, K_c, s, taken, so, cut ? cut + o : NULL);
+            const int n = cluster_expand(H, hoff, E, w_dtype, d, cl_off, cl_tok, so, K_c, ids, z);
+            double M, Z, mg;
+            softmax_T(z, n, Td, p, &M, &Z);
+            int pick;
+            if (greedy) {
+                /* the largest z; ties to the smaller token id */
+                pick = 0;
+                for (int i = 1; i < n; ++i)
+                    if (z[i] > z[pick] || (z[i] == z[pick] && ids[i] < ids[pick])) pick = i;
+                double second = -INFINITY;
+                for (int i = 0; i < n; ++i)
+                    if (i != pick && z[i] > second) second = z[i];
+                mg = n > 1 ? z[pick] - second : INFINITY;
+            } else {
+                uint32_t w[4];
+                ref_draw(seed, round, row, k, w);
+                pick = ref_inverse_cdf(p, n, ref_u24(w[0]), &mg);
+            }
+            x[o] = ids[pick];
+            if (pd_x) pd_x[o] = p[pick];
+            if (pd_stats) { pd_stats[2 * o] = M; pd_stats[2 * o + 1] = Z; }
+            if (margin) margin[o] = mg;
+        }
+    free(s); free(taken); free(ids); free(z); free(p);
+    return 0;
+}
+
+struct cluster_ctx {
+    const void* H; const void* E; int w_dtype;
+    const int32_t* cl_off; const int32_t* cl_tok; const int32_t* sel;
+    int gamma, d, N_c, K_c, V; double T;
+    int32_t* ids; double* z; double* p;
+};
+
+static int cluster_pd(const void* vctx, int row, int k, int32_t xprev, double* pd)
+{
+    const struct cluster_ctx* c = (const struct cluster_ctx*)vctx;
+    (void)xprev;
+    const size_t o = (size_t)row * c->gamma + (size_t)(k - 1);
+    const int32_t* so = c->sel + o * (size_t)c->K_c;
+    for (int j = 0; j < c->K_c; ++j)
+        if (so[j] < 0 || so[j] >= c->N_c || (j > 0 && so[j] <= so[j - 1])) return -1;
+    const int n = cluster_expand(c->H, o * (size_t)c->d, c->E, c->w_dtype, c->d, c->cl_off, c->cl_tok, so,
+                                 c->K_c, c->ids, c->z);
+    softmax_T(c->z, n, c->T, c->p, NULL, NULL);
+    for (int v = 0; v < c->V; ++v)
+        pd[v] = 0.0;
+    for (int i = 0; i < n; ++i)
+        pd[c->ids[i]] = c->p[i];
+    return 0;
+}
+
+int ref_cluster_verify(const void* H, const void* E, int w_dtype,
+                       const int32_t* cl_off, const int32_t* cl_tok, const int32_t* sel,
+                       const int32_t* x, const float* Lt, const int32_t* ell,
+                       int R, int gamma, int d, int N_c, int K_c, int V, float T, int greedy,
+                       uint64_t seed, uint64_t round,
+                       int32_t* n_acc, int32_t* y, double* pt_x, double* pd_x, double* c_star,
+                       int32_t* acc, double* acc_margin, int32_t* y_alt, double* y_margin)
+{
+    if (bad_cluster(H, E, w_dtype, cl_off, cl_tok, R, gamma, d, N_c, K_c, V, T) || !sel || !x || !Lt ||
+        !n_acc || !y)
+        return -1;
+    struct cluster_ctx c = {H, E, w_dtype, cl_off, cl_tok, sel, gamma, d, N_c, K_c, V, (double)T, NULL, NULL, NULL};
+    c.ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)V);
+    c.z = (double*)malloc(sizeof(double) * (size_t)V);
+    c.p = (double*)malloc(sizeof(double) * (size_t)V);
+    int st = -1;
+    if (c.ids && c.z && c.p)
+        st = verify_core(cluster_pd, &c, NULL, x, Lt, ell, R, gamma, V, T, greedy, seed, round, NULL,
+                         n_acc, y, pt_x, pd_x, c_star, acc, acc_margin, y_alt, y_margin);
+    free(c.ids); free(c.z); free(c.p);
+    return st;
 }

@@ -147,6 +147,50 @@ int ref_schedule_async(const float* c, int R, int gamma, const float* sps, int B
                        int32_t* ell, double* a, int32_t* K_used, int32_t* K_star, double* theta_star,
                        double* theta_margin);
 
+/* Clustered draft head (the MTP survey page, zdszero.github.io "spec_mtp":
+ * its Gemma 4 assistant section -- 2048 cluster centres give coarse logits,
+ * the top clusters are expanded to cut the LM-head cost -- and the
+ * FROZEN_KV_MTP path of its SGLang section, which expands the top 32 by
+ * default).  Per drafted row (r, k) with hidden h = H[r,k,:]:
+ *   s_c = h . C[c]            coarse logit of cluster c (c = 0..N_c-1)
+ *   A   = the K_c clusters with the largest s_c (ties: smaller index),
+ *         listed in ascending cluster index                     -> sel
+ *   S   = the tokens of the clusters in A, in that order, each cluster's
+ *         tokens in its listed (CSR) order: the expansion order
+ *   z_v = h . E[v] for v in S;  p_d(v) = exp((z_v - M)/T) / Z on S, 0 elsewhere
+ *   x   = inverse CDF over S in expansion order with u from Philox word 0
+ *         (counter (k, request, round)); greedy: the largest z_v, ties to
+ *         the smaller token id.
+ * Positions are independent (no Markov bias: the clustered head replaces
+ * the LM head that produces the base logits).
+ * Layouts: H [R,gamma,d], C [N_c,d], E [V,d] (fp32 or bf16 bits, one dtype);
+ * cl_off [N_c+1], cl_tok [V]: a partition of the vocabulary (CSR).
+ * Outputs: x, pd_x, sel [R,gamma,K_c], pd_stats [R,gamma,2] = (M, Z);
+ * optional cut [R,gamma] = s_(K_c) - s_(K_c+1) (infinite when K_c = N_c) and
+ * margin [R,gamma] (the sampling decision's, as ref_markov_propose).
+ * Returns 0, or -1 on a bad argument or a cl_off/cl_tok that is not a
+ * partition. */
+int ref_cluster_propose(const void* H, const void* C, const void* E, int w_dtype,
+                        const int32_t* cl_off, const int32_t* cl_tok,
+                        int R, int gamma, int d, int N_c, int K_c, int V, float T,
+                        int greedy, uint64_t seed, uint64_t round,
+                        int32_t* x, double* pd_x, int32_t* sel, double* pd_stats,
+                        double* cut, double* margin);
+
+/* Verification of drafts from the clustered head: the same rule as
+ * ref_verify with p_d the sparse distribution above, built from the given
+ * selection sel (conditioned on the GPU's clusters as on its tokens).
+ * The residual max(0, p_t - p_d) and the bonus are drawn over the whole
+ * vocabulary in ascending id order; c* = clamp(1 - 1/2 ||p_d - p_t||_1).
+ * Outputs and margins as ref_verify (pd_x may be NULL). */
+int ref_cluster_verify(const void* H, const void* E, int w_dtype,
+                       const int32_t* cl_off, const int32_t* cl_tok, const int32_t* sel,
+                       const int32_t* x, const float* Lt, const int32_t* ell,
+                       int R, int gamma, int d, int N_c, int K_c, int V, float T, int greedy,
+                       uint64_t seed, uint64_t round,
+                       int32_t* n_acc, int32_t* y, double* pt_x, double* pd_x, double* c_star,
+                       int32_t* acc, double* acc_margin, int32_t* y_alt, double* y_margin);
+
 #ifdef __cplusplus
 }
 #endif
