@@ -20,6 +20,7 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH, SPEC_EDEVICE, 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE, SPEC_OP_ROUNDS, SPEC_OP_LOSS = range(6)
 SPEC_DEV_BAD_TOKEN, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_CONFIDENCE, SPEC_DEV_WAIT_FAILED = 1, 2, 4, 8
+SPEC_DEV_BAD_CLUSTER = 16
 
 
 class SpecError(RuntimeError):
@@ -45,6 +46,10 @@ _SIGS = {
     "spec_schedule": ([P, I, I, P, I, P, P, P, P, P, SZ, P], I),
     "spec_schedule_async": ([P, I, I, P, I, P, P, P, P, P, P, P, SZ, P], I),
     "spec_draft_loss": ([P, P, P, I, P, P, P, P, I, I, I, I, F, F, F, F, P, P, P, P, SZ, P], I),
+    "spec_cluster_workspace_bytes": ([I, I, I, I, I, I, I], SZ),
+    "spec_cluster_index": ([P, P, I, I, P, P, SZ, P], I),
+    "spec_cluster_propose": ([P, P, P, I, P, P, I, I, I, I, I, I, I, F, I, U64, U64, P, P, P, P, P, P, SZ, P], I),
+    "spec_cluster_verify": ([P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
     "spec_decode_rounds": ([P, P, P, I, P, P, I, I, I, I, F, I, U64, U64, I, P, P, P, P, P, P, SZ, P], I),
     "spec_status_str": ([I], ctypes.c_char_p),
     "spec_set_propose_fused": ([I], I),
@@ -307,6 +312,95 @@ def spec_draft_loss(U, W1, W2p, x0, y, Lt, q, T, alphas=(0.1, 0.9, 1.0), loss=No
                                _ptr(loss), _ptr(terms), _ptr(dq), ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_draft_loss")
     return loss, terms, dq
+
+
+# ------------------------------------------------------- clustered draft head
+
+def spec_cluster_workspace_bytes(R, gamma, d, N_c, K_c, max_cl, V) -> int:
+    return int(lib().spec_cluster_workspace_bytes(R, gamma, d, N_c, K_c, max_cl, V))
+
+
+class ClusterWorkspace(Workspace):
+    """A device workspace for spec_cluster_propose / spec_cluster_verify at
+    these sizes, with its status word zeroed."""
+
+    def __init__(self, R, gamma, d, N_c, K_c, max_cl, V, device=None):
+        need = spec_cluster_workspace_bytes(R, gamma, d, N_c, K_c, max_cl, V)
+        if need == 0:
+            raise SpecError(SPEC_EINVAL, "ClusterWorkspace")
+        self.tensor = torch.empty(need, dtype=torch.uint8, device=device or "cuda")
+        spec_workspace_init(self)
+
+
+def spec_cluster_index(cl_off, cl_tok, tok_slot=None, ws=None, stream=None):
+    """tok_slot [V] int32 = (cluster << 16) | place of every token."""
+    N_c, V = cl_off.numel() - 1, cl_tok.numel()
+    _need(cl_off, (N_c + 1,), torch.int32, "cl_off")
+    _need(cl_tok, (V,), torch.int32, "cl_tok")
+    _need(tok_slot, (V,), torch.int32, "tok_slot")
+    tok_slot = torch.empty(V, dtype=torch.int32, device=cl_tok.device) if tok_slot is None else tok_slot
+    if ws is None:
+        ws = ClusterWorkspace(1, 1, 16, 1, 1, 1, 1, device=cl_tok.device)
+    st = lib().spec_cluster_index(_ptr(cl_off), _ptr(cl_tok), N_c, V, _ptr(tok_slot), ws.ptr(), ws.nbytes,
+                                  _stream(stream))
+    _check(st, "spec_cluster_index")
+    return tok_slot
+
+
+def spec_cluster_propose(H, C, E, cl_off, cl_tok, K_c, max_cl, T, greedy=False, seed=1, round=0, x=None,
+                         pd_x=None, sel=None, zf=None, pd_stats=None, ws=None, stream=None):
+    """Clustered draft head.  H [R,gamma,d], C [N_c,d], E [V,d] bf16.
+    Returns (x, pd_x, sel, zf, pd_stats)."""
+    if H.dim() != 3:
+        raise ValueError("H must be [R, gamma, d]")
+    R, gamma, d = H.shape
+    N_c, V = C.shape[0], E.shape[0]
+    for name, t, shape in (("C", C, (N_c, d)), ("E", E, (V, d))):
+        _need(t, shape, H.dtype, name)
+    _need(cl_off, (N_c + 1,), torch.int32, "cl_off")
+    _need(cl_tok, (V,), torch.int32, "cl_tok")
+    dev = H.device
+    out = dict(x=(x, (R, gamma), torch.int32), pd_x=(pd_x, (R, gamma), torch.float32),
+               sel=(sel, (R, gamma, K_c), torch.int32), zf=(zf, (R, gamma, K_c, max_cl), torch.float32),
+               pd_stats=(pd_stats, (R, gamma, 2), torch.float32))
+    res = {}
+    for name, (t, shape, dt) in out.items():
+        _need(t, shape, dt, name)
+        res[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else t
+    if ws is None:
+        ws = ClusterWorkspace(R, gamma, d, N_c, K_c, max_cl, V, device=dev)
+    st = lib().spec_cluster_propose(_ptr(H), _ptr(C), _ptr(E), _wdtype(H), _ptr(cl_off), _ptr(cl_tok), R, gamma, d,
+                                    N_c, int(K_c), int(max_cl), V, float(T), int(bool(greedy)), seed, round,
+                                    _ptr(res["x"]), _ptr(res["pd_x"]), _ptr(res["sel"]), _ptr(res["zf"]),
+                                    _ptr(res["pd_stats"]), ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "spec_cluster_propose")
+    return res["x"], res["pd_x"], res["sel"], res["zf"], res["pd_stats"]
+
+
+def spec_cluster_verify(tok_slot, sel, zf, pd_stats, x, Lt, T, N_c, greedy=False, seed=1, round=0, ell=None,
+                        n_acc=None, y=None, pt_x=None, c_star=None, ws=None, stream=None, d=16):
+    """Verify clustered-head drafts.  Returns (n_acc, y, pt_x, c_star)."""
+    R, gamma, K_c, max_cl = zf.shape
+    V = tok_slot.numel()
+    dev = zf.device
+    _need(tok_slot, (V,), torch.int32, "tok_slot")
+    _need(sel, (R, gamma, K_c), torch.int32, "sel")
+    _need(pd_stats, (R, gamma, 2), torch.float32, "pd_stats")
+    _need(x, (R, gamma), torch.int32, "x")
+    _need(Lt, (R, gamma + 1, V), torch.float32, "Lt")
+    _need(ell, (R,), torch.int32, "ell")
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    y = torch.empty((R, gamma + 1), dtype=torch.int32, device=dev) if y is None else y
+    pt_x = torch.empty((R, gamma), dtype=torch.float32, device=dev) if pt_x is None else pt_x
+    c_star = torch.empty((R, gamma), dtype=torch.float32, device=dev) if c_star is None else c_star
+    if ws is None:
+        ws = ClusterWorkspace(R, gamma, d, N_c, K_c, max_cl, V, device=dev)
+    st = lib().spec_cluster_verify(_ptr(tok_slot), _ptr(sel), _ptr(zf), _ptr(pd_stats), _ptr(x), _ptr(Lt),
+                                   _ptr(ell), R, gamma, int(N_c), K_c, max_cl, V, float(T), int(bool(greedy)), seed,
+                                   round, _ptr(n_acc), _ptr(y), _ptr(pt_x), _ptr(c_star), ws.ptr(), ws.nbytes,
+                                   _stream(stream))
+    _check(st, "spec_cluster_verify")
+    return n_acc, y, pt_x, c_star
 
 
 def spec_schedule(c, sps, ell=None, a=None, K_star=None, theta_star=None, want_a=True, ws=None,

@@ -20,7 +20,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspec.so")
-SOURCES = ["api.hip", "propose.hip", "verify.hip", "schedule.hip"]
+SOURCES = ["api.hip", "propose.hip", "verify.hip", "schedule.hip", "cluster.hip"]
 ARCH = "gfx950"
 
 

@@ -55,6 +55,19 @@ DraftArgs make_args(const float* U, const void* W1, const void* W2, int w_dtype,
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH; }
 
+// Sizes of the clustered head the GPU path takes (everything but pointers).
+int check_cluster(int R, int gamma, int d, int N_c, int K_c, int max_cl, int V, float T)
+{
+    if (R < 0 || gamma < 1 || V < 1 || d < 16 || (d % 16) != 0 || N_c < 1 || K_c < 1 || K_c > N_c || max_cl < 1)
+        return SPEC_EINVAL;
+    if (!(T > 0.0f) || isinf(T)) return SPEC_EINVAL;
+    if (R > MAX_R || gamma > MAX_GAMMA || V > MAX_V || d > 16384 || N_c > spec::CL_MAX_NC || K_c > spec::CL_MAX_K ||
+        max_cl > spec::CL_MAX_SIZE || (long)K_c * max_cl > 65536 || (long)R * gamma > (1L << 20))
+        return SPEC_EUNSUPPORTED;
+    if ((double)R * (gamma + 1) * (double)V >= 1099511627776.0) return SPEC_EUNSUPPORTED;
+    return SPEC_OK;
+}
+
 // spec_decode_rounds keeps each round's p_d(x) and (M, S) after the larger of
 // the propose and verify regions (verify reads what propose wrote).
 size_t rounds_scratch_offset(size_t propose_bytes, size_t verify_bytes)
@@ -173,6 +186,73 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
     default:
         return 0;
     }
+}
+
+size_t spec_cluster_workspace_bytes(int R, int gamma, int d, int N_c, int K_c, int max_cl, int V)
+{
+    if (check_cluster(R, gamma, d, N_c, K_c, max_cl, V, 1.0f) != SPEC_OK) return 0;
+    size_t vb = 0;
+    spec::carve_verify(nullptr, R, gamma, V, false, &vb);
+    const size_t pb = spec::cluster_propose_ws_bytes(R * gamma, N_c, d);
+    return pb > vb ? pb : vb;
+}
+
+int spec_cluster_index(const int32_t* cl_off, const int32_t* cl_tok, int N_c, int V, int32_t* tok_slot, void* ws,
+                       size_t ws_bytes, spec_stream_t stream)
+{
+    if (N_c < 1 || V < 1 || !cl_off || !cl_tok || !tok_slot) return SPEC_EINVAL;
+    if (N_c > spec::CL_MAX_NC || V > MAX_V) return SPEC_EUNSUPPORTED;
+    if (!ws || ws_bytes < spec::WS_HEADER) return SPEC_EWORKSPACE;
+    return launch_status(spec::launch_cluster_index(cl_off, cl_tok, N_c, V, tok_slot, reinterpret_cast<uint32_t*>(ws),
+                                                    (hipStream_t)stream));
+}
+
+int spec_cluster_propose(const void* H, const void* C, const void* E, int w_dtype, const int32_t* cl_off,
+                         const int32_t* cl_tok, int R, int gamma, int d, int N_c, int K_c, int max_cl, int V, float T,
+                         int greedy, uint64_t seed, uint64_t round, int32_t* x, float* pd_x, int32_t* sel, float* zf,
+                         float* pd_stats, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    if (w_dtype != SPEC_F32 && w_dtype != SPEC_BF16) return SPEC_EDTYPE;
+    int st = check_cluster(R, gamma, d, N_c, K_c, max_cl, V, T);
+    if (st != SPEC_OK) return st;
+    if (w_dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+    if (R > 0 && (!H || !C || !E || !cl_off || !cl_tok || !x || !pd_x || !sel || !zf || !pd_stats))
+        return SPEC_EINVAL;
+    if (R > 0 && (!aligned16(H) || !aligned16(C) || !aligned16(E))) return SPEC_EINVAL;
+    if (!ws || ws_bytes < spec_cluster_workspace_bytes(R, gamma, d, N_c, K_c, max_cl, V)) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_OK;
+    spec::ClusterArgs a{};
+    a.H = H; a.C = C; a.E = E; a.cl_off = cl_off; a.cl_tok = cl_tok;
+    a.R = R; a.gamma = gamma; a.d = d; a.N_c = N_c; a.K_c = K_c; a.max_cl = max_cl; a.V = V;
+    a.c = (float)(1.4426950408889634 / (double)T);
+    a.greedy = greedy != 0; a.seed = seed; a.round = round;
+    a.x = x; a.pd_x = pd_x; a.sel = sel; a.zf = zf; a.pd_stats = pd_stats;
+    a.ws = ws; a.status = reinterpret_cast<uint32_t*>(ws);
+    return launch_status(spec::launch_cluster_propose(a, (hipStream_t)stream));
+}
+
+int spec_cluster_verify(const int32_t* tok_slot, const int32_t* sel, const float* zf, const float* pd_stats,
+                        const int32_t* x, const float* Lt, const int32_t* ell, int R, int gamma, int N_c, int K_c,
+                        int max_cl, int V, float T, int greedy, uint64_t seed, uint64_t round, int32_t* n_acc,
+                        int32_t* y, float* pt_x, float* c_star, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    int st = check_cluster(R, gamma, 16, N_c, K_c, max_cl, V, T);
+    if (st != SPEC_OK) return st;
+    if (R > 0 && (!tok_slot || !sel || !zf || !pd_stats || !x || !Lt || !n_acc || !y)) return SPEC_EINVAL;
+    if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
+    size_t need = 0;
+    spec::carve_verify(nullptr, R, gamma, V, false, &need);
+    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_OK;
+    const spec::VerifyWs w = spec::carve_verify(ws, R, gamma, V, false, nullptr);
+    spec::ClusterVerifyArgs cv{};
+    cv.tok_slot = tok_slot; cv.sel = sel; cv.zf = zf; cv.pd_stats = pd_stats; cv.x = x; cv.Lt = Lt; cv.ell = ell;
+    cv.R = R; cv.gamma = gamma; cv.N_c = N_c; cv.K_c = K_c; cv.max_cl = max_cl; cv.V = V;
+    cv.c = (float)(1.4426950408889634 / (double)T);
+    cv.greedy = greedy != 0; cv.seed = seed; cv.round = round;
+    cv.n_acc = n_acc; cv.y = y; cv.pt_x = pt_x; cv.c_star = c_star;
+    cv.status = reinterpret_cast<uint32_t*>(ws);
+    return launch_status(spec::launch_cluster_verify(cv, w, (hipStream_t)stream));
 }
 
 int spec_set_propose_fused(int enable) { return spec::set_propose_fused(enable); }

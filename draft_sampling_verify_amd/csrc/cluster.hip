@@ -1,0 +1,534 @@
+// cluster.hip -- the clustered draft head (the MTP survey page,
+// zdszero.github.io "spec_mtp": its Gemma 4 assistant section, where cluster
+// centres give coarse logits and only the top clusters are expanded through
+// the LM head, and the FROZEN_KV_MTP path of its SGLang section, which
+// expands the top 32 by default).
+//
+// Per drafted row with hidden h (bf16, d wide):
+//   coarse   s_c = h . C[c] for every cluster: one [rows, d] x [d, N_c]
+//            contraction on MFMA, split over d so that the launch fills the
+//            chip; the partial products are summed in a fixed order;
+//   select   the K_c clusters of largest s (ties to the smaller index) by a
+//            four-pass radix select on the order-preserving key of s, then
+//            listed in ascending cluster index;
+//   fine     z_v = h . E[v] for the tokens of the selected clusters: one
+//            workgroup per (cluster, 32-row block) multiplies the cluster's
+//            E rows by the block's hidden rows on MFMA, so a cluster's rows
+//            of E are read once for all rows of the block that chose it,
+//            and unselected clusters cost nothing;
+//   sample   per row, softmax over the expanded tokens in expansion order
+//            (cluster, then the cluster's listed order) and the inverse CDF
+//            with the row's Philox word 0, or the largest logit (ties to the
+//            smaller token id).
+// Positions are independent: there is no serial chain.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace spec {
+
+constexpr int CL_THREADS = 256;
+constexpr uint32_t DEV_BAD_CLUSTER = 16u;
+
+// ---------------------------------------------------------------- index
+
+__global__ void k_fill_i32(int32_t* p, int n, int32_t v)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// One workgroup per cluster: tok_slot[cl_tok[cl_off[c] + i]] = (c << 16) | i.
+__global__ __launch_bounds__(CL_THREADS) void k_cluster_scatter(const int32_t* cl_off, const int32_t* cl_tok,
+                                                                int N_c, int V, int32_t* tok_slot, uint32_t* status)
+{
+    const int c = blockIdx.x;
+    const int c0 = cl_off[c], c1 = cl_off[c + 1];
+    const bool ok = c0 >= 0 && c1 > c0 && c1 <= V && c1 - c0 <= CL_MAX_SIZE && (c > 0 || c0 == 0) &&
+                    (c < N_c - 1 || c1 == V);
+    if (!ok) {
+        if (threadIdx.x == 0) raise_flag(status, DEV_BAD_CLUSTER);
+        return;
+    }
+    for (int i = threadIdx.x; i < c1 - c0; i += CL_THREADS) {
+        const int v = cl_tok[c0 + i];
+        if (v < 0 || v >= V) raise_flag(status, DEV_BAD_CLUSTER);
+        else tok_slot[v] = (int32_t)(((uint32_t)c << 16) | (uint32_t)i);
+    }
+}
+
+// Every token must have been written exactly once: V slots and no -1 left
+// means no token was listed twice.
+__global__ void k_cluster_check(const int32_t* tok_slot, int V, uint32_t* status)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < V && tok_slot[i] < 0) raise_flag(status, DEV_BAD_CLUSTER);
+}
+
+hipError_t launch_cluster_index(const int32_t* cl_off, const int32_t* cl_tok, int N_c, int V, int32_t* tok_slot,
+                                uint32_t* status, hipStream_t s)
+{
+    const int nb = (V + CL_THREADS - 1) / CL_THREADS;
+    hipLaunchKernelGGL(k_fill_i32, dim3(nb), dim3(CL_THREADS), 0, s, tok_slot, V, -1);
+    hipLaunchKernelGGL(k_cluster_scatter, dim3(N_c), dim3(CL_THREADS), 0, s, cl_off, cl_tok, N_c, V, tok_slot,
+                       status);
+    hipLaunchKernelGGL(k_cluster_check, dim3(nb), dim3(CL_THREADS), 0, s, tok_slot, V, status);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ MFMA row products
+//
+// D[m][n] = sum_i A[m][i] * B[n][i] for a 32 x 32 tile on
+// v_mfma_f32_32x32x16_bf16: lane l = n + 32h supplies A row (l & 31) and B
+// row (l & 31), k-slice 8h .. 8h+7 of each 16-wide step, straight from
+// global memory (each row is contiguous along the reduction).  Result lane
+// l = n + 32h holds column n and rows m = 8 (j >> 2) + 4h + (j & 3).
+// Loads of four steps are issued before their products.
+__device__ inline f32x16 rows_dot(const uint4* pa, const uint4* pb, int s0, int s1, f32x16 acc)
+{
+    int s = s0;
+    for (; s + 4 <= s1; s += 4) {
+        uint4 a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a[u] = pa[2 * (s + u)];
+            b[u] = pb[2 * (s + u)];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                          __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+    }
+    for (; s < s1; ++s) {
+        const uint4 a = pa[2 * s], b = pb[2 * s];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// ---------------------------------------------------------------- coarse
+
+// Workgroup (column block cb of 128 clusters, row block rb of 32 rows,
+// reduction split q): wave w covers clusters 128 cb + 32 w .. +31 over the
+// k-steps of split q and stores its partial products part[q][row][cluster].
+// Rows and clusters past the end read row 0 and are not stored.
+__global__ __launch_bounds__(CL_THREADS) void k_cluster_coarse(const bf16w* H, const bf16w* C, int N, int N_c, int d,
+                                                               int nsplit, float* part)
+{
+    const int cb = blockIdx.x, rb = blockIdx.y, q = blockIdx.z;
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE, h = lane >> 5;
+    const int ks = d / 16;
+    const int s0 = (int)((long)q * ks / nsplit), s1 = (int)((long)(q + 1) * ks / nsplit);
+    const int cl = cb * 128 + 32 * w + (lane & 31);
+    const int row = rb * 32 + (lane & 31);
+    const uint4* pa = reinterpret_cast<const uint4*>(C + (size_t)(cl < N_c ? cl : 0) * d) + h;
+    const uint4* pb = reinterpret_cast<const uint4*>(H + (size_t)(row < N ? row : 0) * d) + h;
+    const f32x16 acc = rows_dot(pa, pb, s0, s1, f32x16{});
+    if (row >= N) return;
+    float* out = part + ((size_t)q * N + row) * N_c;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int m = cb * 128 + 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
+        if (m < N_c) out[m] = acc[j];
+    }
+}
+
+// ---------------------------------------------------------------- select
+
+__device__ inline uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive scan of one int per thread over the workgroup (CL_THREADS).
+__device__ inline int block_incl_scan(int v, int* s_tmp)
+{
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == WAVE - 1) s_tmp[w] = x;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += s_tmp[i];
+    __syncthreads();
+    return base + x;
+}
+
+// One workgroup per row: s_c summed over the splits in order, then the
+// K_c largest by radix select (8 bits a pass, most significant first) on
+// the order-preserving key; keys equal to the K_c-th are taken in
+// ascending cluster order.  Thread t owns clusters [t per, (t+1) per), so
+// "ascending" is thread order, then position.
+__global__ __launch_bounds__(CL_THREADS) void k_cluster_select(const float* part, int nsplit, int N, int N_c, int K_c,
+                                                               int32_t* sel)
+{
+    __shared__ uint32_t s_key[CL_MAX_NC];
+    __shared__ int s_hist[256];
+    __shared__ int s_tmp[CL_THREADS / WAVE];
+    __shared__ uint32_t s_digit;
+    __shared__ int s_krem;
+    const int n = blockIdx.x, t = threadIdx.x;
+    if (t == 0) {
+        s_digit = 0;
+        s_krem = K_c;
+    }
+    for (int c = t; c < N_c; c += CL_THREADS) {
+        float s = 0.0f;
+        for (int q = 0; q < nsplit; ++q) s += part[((size_t)q * N + n) * N_c + c];
+        s_key[c] = order_key(s);
+    }
+    uint32_t prefix = 0, pmask = 0;
+    int krem = K_c;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        s_hist[t] = 0;
+        __syncthreads();
+        for (int c = t; c < N_c; c += CL_THREADS) {
+            const uint32_t key = s_key[c];
+            if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        // thread t holds digit 255 - t: the scan counts keys with a digit >= it
+        const int hv = s_hist[255 - t];
+        const int ge = block_incl_scan(hv, s_tmp);
+        if (hv > 0 && ge >= krem && ge - hv < krem) {
+            s_digit = 255u - (uint32_t)t;
+            s_krem = krem - (ge - hv);
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        pmask |= 255u << shift;
+        krem = s_krem;
+        __syncthreads();
+    }
+    // prefix = the K_c-th largest key; krem keys equal to it are taken
+    const int per = (N_c + CL_THREADS - 1) / CL_THREADS;
+    const int c0 = min(t * per, N_c), c1 = min(c0 + per, N_c);
+    int ties = 0;
+    for (int c = c0; c < c1; ++c) ties += s_key[c] == prefix;
+    int tie_rank = block_incl_scan(ties, s_tmp) - ties;
+    int nsel = 0;
+    for (int c = c0; c < c1; ++c) {
+        const uint32_t key = s_key[c];
+        nsel += key > prefix || (key == prefix && tie_rank++ < krem);
+    }
+    int pos = block_incl_scan(nsel, s_tmp) - nsel;
+    tie_rank = block_incl_scan(ties, s_tmp) - ties;
+    int32_t* out = sel + (size_t)n * K_c;
+    for (int c = c0; c < c1; ++c) {
+        const uint32_t key = s_key[c];
+        if (key > prefix || (key == prefix && tie_rank++ < krem)) {
+            if (pos < K_c) out[pos] = c;  // exactly K_c are taken; the guard keeps writes in the row
+            ++pos;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fine
+
+// Workgroup (cluster c, row block rb): the rows of the block that selected
+// c (binary search in each row's ascending list) get z = h . E[v] for the
+// cluster's tokens, 128 per pass (32 per wave), written to
+// zf[row][j][i] (j = c's place in the row's list, i = place in the
+// cluster); slots from the cluster's size to max_cl get -inf.  Tokens
+// outside [0, V) read row 0 and raise the flag (the sampler rejects the
+// row).
+__global__ __launch_bounds__(CL_THREADS) void k_cluster_fine(const bf16w* H, const bf16w* E, const int32_t* cl_off,
+                                                             const int32_t* cl_tok, const int32_t* sel, int N, int K_c,
+                                                             int max_cl, int d, int V, float* zf, uint32_t* status)
+{
+    __shared__ int s_j[32];
+    __shared__ int s_any;
+    const int c = blockIdx.x, rb = blockIdx.y;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE, h = lane >> 5;
+    if (t < WAVE) {
+        const int n = rb * 32 + (lane & 31);
+        int j = -1;
+        if (lane < 32 && n < N) {
+            const int32_t* sr = sel + (size_t)n * K_c;
+            int lo = 0, hi = K_c;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (sr[mid] < c) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < K_c && sr[lo] == c) j = lo;
+        }
+        if (lane < 32) s_j[lane] = j;
+        const bool any = __ballot(j >= 0) != 0;
+        if (lane == 0) s_any = any;
+    }
+    __syncthreads();
+    if (!s_any) return;
+    const int c0 = cl_off[c];
+    int m = cl_off[c + 1] - c0;
+    if (c0 < 0 || m < 0 || c0 + m > V) m = 0;  // the sampler flags the row
+    if (m > max_cl) m = max_cl;
+    const int ks = d / 16;
+    const int nl = lane & 31;
+    const int row = rb * 32 + nl;
+    const uint4* pb = reinterpret_cast<const uint4*>(H + (size_t)(row < N ? row : 0) * d) + h;
+    const int jr = s_j[nl];
+    for (int i0 = 0; i0 < m; i0 += 128) {
+        const int i = i0 + 32 * w + nl;
+        int tok = i < m ? cl_tok[c0 + i] : 0;
+        if (tok < 0 || tok >= V) {
+            raise_flag(status, DEV_BAD_CLUSTER);
+            tok = 0;
+        }
+        const uint4* pa = reinterpret_cast<const uint4*>(E + (size_t)tok * d) + h;
+        const f32x16 acc = rows_dot(pa, pb, 0, ks, f32x16{});
+        if (jr >= 0) {
+            float* out = zf + ((size_t)row * K_c + jr) * max_cl;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int im = i0 + 32 * w + 8 * (jj >> 2) + 4 * h + (jj & 3);
+                if (im < m) out[im] = acc[jj];
+            }
+        }
+    }
+    // padding of the selecting rows
+    const int pad = max_cl - m;
+    for (int e = t; e < 32 * pad; e += CL_THREADS) {
+        const int rr = e / pad, ii = m + e % pad;
+        const int jj = s_j[rr];
+        if (jj >= 0) zf[((size_t)(rb * 32 + rr) * K_c + jj) * max_cl + ii] = -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------- sample
+
+template <typename T>
+__device__ inline T block_reduce(T v, T* s_tmp, T (*op)(T, T), T (*wop)(T))
+{
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+    v = wop(v);
+    if (lane == 0) s_tmp[w] = v;
+    __syncthreads();
+    T r = s_tmp[0];
+    for (int i = 1; i < CL_THREADS / WAVE; ++i) r = op(r, s_tmp[i]);
+    __syncthreads();
+    return r;
+}
+__device__ inline float fmax_op(float a, float b) { return fmaxf(a, b); }
+__device__ inline int imin_op(int a, int b) { return min(a, b); }
+__device__ inline int imax_op(int a, int b) { return max(a, b); }
+__device__ inline float wmax_f(float v) { return wave_max(v); }
+__device__ inline int wmin_i(int v) { return wave_min(v); }
+__device__ inline int wmax_i(int v) { return wave_max_int(v); }
+
+// Running sum of one float per thread over the workgroup, waves in order:
+// [lo, hi) is this thread's share.  Consecutive shares meet exactly (the next
+// share's lo is computed by the same additions as this one's hi).
+__device__ inline void block_share_f(float v, float* s_tmp, float& lo, float& hi, float& total)
+{
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+    const float x = wave_incl_scan(v);
+    float xe = __shfl_up(x, 1, WAVE);
+    if (lane == 0) xe = 0.0f;
+    if (lane == WAVE - 1) s_tmp[w] = x;
+    __syncthreads();
+    float base = 0.0f, tot = 0.0f;
+    for (int i = 0; i < CL_THREADS / WAVE; ++i) {
+        if (i == w) base = tot;
+        tot += s_tmp[i];
+    }
+    __syncthreads();
+    total = tot;
+    lo = lane == 0 ? base : base + xe;
+    hi = base + x;
+}
+
+struct ClusterSampleArgs {
+    const float* zf;
+    const int32_t* sel;
+    const int32_t* cl_off;
+    const int32_t* cl_tok;
+    int N, gamma, N_c, K_c, max_cl, V;
+    float c;
+    uint64_t seed, round;
+    int32_t* x;
+    float* pd_x;
+    float* pd_stats;
+    uint32_t* status;
+};
+
+// One workgroup per row f = (request, position).  Element e = j max_cl + i
+// (cluster j of the row's list, place i in it); thread t owns the
+// contiguous elements [t per, (t+1) per), so running sums follow the
+// expansion order: within a thread in sequence, then threads in order.
+template <bool GREEDY>
+__global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs a)
+{
+    __shared__ int s_c0[CL_MAX_K], s_m[CL_MAX_K];
+    __shared__ float s_ftmp[CL_THREADS / WAVE];
+    __shared__ int s_itmp[CL_THREADS / WAVE];
+    __shared__ int s_pick;
+    const int f = blockIdx.x, t = threadIdx.x;
+    const int r = f / a.gamma, k = f - r * a.gamma + 1;
+    bool bad = false;
+    if (t < a.K_c) {
+        const int cj = a.sel[(size_t)f * a.K_c + t];
+        int c0 = 0, m = 0;
+        if (cj < 0 || cj >= a.N_c) {
+            bad = true;
+        } else {
+            c0 = a.cl_off[cj];
+            m = a.cl_off[cj + 1] - c0;
+            bad = c0 < 0 || m < 0 || c0 + m > a.V || m > a.max_cl;
+        }
+        s_c0[t] = bad ? 0 : c0;
+        s_m[t] = bad ? 0 : m;
+    }
+    const int n_el = a.K_c * a.max_cl;
+    const int per = (n_el + CL_THREADS - 1) / CL_THREADS;
+    const int e0 = min(t * per, n_el), e1 = min(e0 + per, n_el);
+    __syncthreads();
+    const float* z = a.zf + (size_t)f * n_el;
+    auto valid = [&](int e) { return e % a.max_cl < s_m[e / a.max_cl]; };
+    auto token = [&](int e) { return a.cl_tok[s_c0[e / a.max_cl] + e % a.max_cl]; };
+    float mloc = -INFINITY;
+    for (int e = e0; e < e1; ++e) {
+        if (!valid(e)) continue;
+        const int v = token(e);
+        bad = bad || v < 0 || v >= a.V;
+        mloc = fmaxf(mloc, z[e]);
+    }
+    bad = __syncthreads_or(bad);
+    if (bad) {
+        if (t == 0) {
+            raise_flag(a.status, DEV_BAD_CLUSTER);
+            a.x[f] = -1;
+            a.pd_x[f] = NAN;
+            a.pd_stats[2 * (size_t)f] = NAN;
+            a.pd_stats[2 * (size_t)f + 1] = NAN;
+        }
+        return;
+    }
+    const float M = block_reduce<float>(mloc, s_ftmp, fmax_op, wmax_f);
+    if (M == -INFINITY) {  // the selected clusters hold no token
+        if (t == 0) {
+            raise_flag(a.status, DEV_BAD_CLUSTER);
+            a.x[f] = -1;
+            a.pd_x[f] = NAN;
+            a.pd_stats[2 * (size_t)f] = NAN;
+            a.pd_stats[2 * (size_t)f + 1] = NAN;
+        }
+        return;
+    }
+    float tsum = 0.0f;
+    for (int e = e0; e < e1; ++e)
+        if (valid(e)) tsum += softw(z[e], M, a.c);
+    float Z, lo, incl;
+    block_share_f(tsum, s_ftmp, lo, incl, Z);
+    int pick = -1;
+    if (GREEDY) {
+        int best = 0x7fffffff;
+        for (int e = e0; e < e1; ++e)
+            if (valid(e) && z[e] == M) best = min(best, token(e));
+        const int tok = block_reduce<int>(best, s_itmp, imin_op, wmin_i);
+        if (t == 0) {
+            const bool ok = tok != 0x7fffffff;  // no logit equals the maximum: NaN logits
+            if (!ok) raise_flag(a.status, DEV_BAD_CLUSTER);
+            a.x[f] = ok ? tok : -1;
+            a.pd_x[f] = ok ? 1.0f / Z : NAN;
+        }
+    } else {
+        const float target = u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[0]) * Z;
+        int last = -1;
+        if (tsum > 0.0f && lo <= target && target < incl) {
+            float run = lo;
+            for (int e = e0; e < e1; ++e) {
+                if (!valid(e)) continue;
+                const float wv = softw(z[e], M, a.c);
+                if (wv > 0.0f) {
+                    if (run + wv > target) { pick = e; break; }
+                    last = e;
+                }
+                run += wv;
+            }
+            if (pick < 0) pick = last;  // this share's own sum rounded below the target
+        }
+        if (pick >= 0) s_pick = pick;
+        // no share holds the target (the total rounded below it): the last
+        // element with weight
+        int lpos = -1;
+        for (int e = e0; e < e1; ++e)
+            if (valid(e) && softw(z[e], M, a.c) > 0.0f) lpos = e;
+        const int found = block_reduce<int>(pick, s_itmp, imax_op, wmax_i);
+        const int lastpos = block_reduce<int>(lpos, s_itmp, imax_op, wmax_i);
+        if (t == 0) {
+            const int e = found >= 0 ? s_pick : lastpos;
+            if (e < 0) {  // no element with weight: NaN logits
+                raise_flag(a.status, DEV_BAD_CLUSTER);
+                a.x[f] = -1;
+                a.pd_x[f] = NAN;
+            } else {
+                a.x[f] = token(e);
+                a.pd_x[f] = softw(z[e], M, a.c) / Z;
+            }
+        }
+    }
+    if (t == 0) {
+        a.pd_stats[2 * (size_t)f] = M;
+        a.pd_stats[2 * (size_t)f + 1] = Z;
+    }
+}
+
+// ------------------------------------------------------------- launcher
+
+static int coarse_splits(int N, int N_c, int d)
+{
+    const int nb = ((N + 31) / 32) * ((N_c + 127) / 128);
+    int q = (512 + nb - 1) / nb;
+    return std::max(1, std::min(q, d / 16));
+}
+
+size_t cluster_propose_ws_bytes(int N, int N_c, int d)
+{
+    return WS_HEADER + align256((size_t)coarse_splits(N, N_c, d) * N * N_c * sizeof(float));
+}
+
+hipError_t launch_cluster_propose(const ClusterArgs& a, hipStream_t s)
+{
+    const int N = a.R * a.gamma;
+    const int nsplit = coarse_splits(N, a.N_c, a.d);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(a.ws) + WS_HEADER);
+    const bf16w* H = static_cast<const bf16w*>(a.H);
+    {
+        ProfScope ps("cluster_coarse", s);
+        hipLaunchKernelGGL(k_cluster_coarse, dim3((a.N_c + 127) / 128, (N + 31) / 32, nsplit), dim3(CL_THREADS), 0,
+                           s, H, static_cast<const bf16w*>(a.C), N, a.N_c, a.d, nsplit, part);
+    }
+    {
+        ProfScope ps("cluster_select", s);
+        hipLaunchKernelGGL(k_cluster_select, dim3(N), dim3(CL_THREADS), 0, s, (const float*)part, nsplit, N, a.N_c,
+                           a.K_c, a.sel);
+    }
+    {
+        ProfScope ps("cluster_fine", s);
+        hipLaunchKernelGGL(k_cluster_fine, dim3(a.N_c, (N + 31) / 32), dim3(CL_THREADS), 0, s, H,
+                           static_cast<const bf16w*>(a.E), a.cl_off, a.cl_tok, (const int32_t*)a.sel, N, a.K_c,
+                           a.max_cl, a.d, a.V, a.zf, a.status);
+    }
+    ClusterSampleArgs sa{};
+    sa.zf = a.zf; sa.sel = a.sel; sa.cl_off = a.cl_off; sa.cl_tok = a.cl_tok;
+    sa.N = N; sa.gamma = a.gamma; sa.N_c = a.N_c; sa.K_c = a.K_c; sa.max_cl = a.max_cl; sa.V = a.V;
+    sa.c = a.c; sa.seed = a.seed; sa.round = a.round;
+    sa.x = a.x; sa.pd_x = a.pd_x; sa.pd_stats = a.pd_stats; sa.status = a.status;
+    {
+        ProfScope ps("cluster_sample", s);
+        if (a.greedy) hipLaunchKernelGGL(k_cluster_sample<true>, dim3(N), dim3(CL_THREADS), 0, s, sa);
+        else hipLaunchKernelGGL(k_cluster_sample<false>, dim3(N), dim3(CL_THREADS), 0, s, sa);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace spec

@@ -166,6 +166,52 @@ struct LossArgs {
 hipError_t launch_draft_loss(const DraftArgs& a, const float* Lt, const LossArgs& l, const VerifyWs& w,
                              hipStream_t s);
 
+// cluster.hip: the clustered draft head.  Limits of the GPU path.
+constexpr int CL_MAX_NC = 8192;     // clusters
+constexpr int CL_MAX_K = 256;       // clusters expanded per row
+constexpr int CL_MAX_SIZE = 65536;  // tokens per cluster (16-bit place in tok_slot)
+struct ClusterArgs {
+    const void* H;          // [R*gamma, d] bf16
+    const void* C;          // [N_c, d] bf16
+    const void* E;          // [V, d] bf16
+    const int32_t* cl_off;  // [N_c + 1]
+    const int32_t* cl_tok;  // [V]
+    int R, gamma, d, N_c, K_c, max_cl, V;
+    float c;                // log2(e) / T
+    int greedy;
+    uint64_t seed, round;
+    int32_t* x;             // [R, gamma]
+    float* pd_x;            // [R, gamma]
+    int32_t* sel;           // [R, gamma, K_c]
+    float* zf;              // [R, gamma, K_c, max_cl]
+    float* pd_stats;        // [R, gamma, 2]
+    void* ws;               // header + coarse partial products
+    uint32_t* status;
+};
+struct ClusterVerifyArgs {
+    const int32_t* tok_slot;  // [V] (cluster << 16) | place
+    const int32_t* sel;       // [R, gamma, K_c]
+    const float* zf;          // [R, gamma, K_c, max_cl]
+    const float* pd_stats;    // [R, gamma, 2]
+    const int32_t* x;         // [R, gamma]
+    const float* Lt;          // [R, gamma + 1, V]
+    const int32_t* ell;       // [R] or NULL
+    int R, gamma, N_c, K_c, max_cl, V;
+    float c;
+    int greedy;
+    uint64_t seed, round;
+    int32_t* n_acc;
+    int32_t* y;
+    float* pt_x;
+    float* c_star;
+    uint32_t* status;
+};
+hipError_t launch_cluster_verify(const ClusterVerifyArgs& cv, const VerifyWs& w, hipStream_t s);
+size_t cluster_propose_ws_bytes(int N, int N_c, int d);
+hipError_t launch_cluster_index(const int32_t* cl_off, const int32_t* cl_tok, int N_c, int V, int32_t* tok_slot,
+                                uint32_t* status, hipStream_t s);
+hipError_t launch_cluster_propose(const ClusterArgs& a, hipStream_t s);
+
 // schedule.hip
 hipError_t launch_schedule(const float* c, int R, int gamma, const float* sps, int B_max,
                            int32_t* ell, double* a, int32_t* K_star, double* theta_star,

@@ -813,18 +813,143 @@ __device__ inline int draw_target_row(const ResolveArgs& a, int trow, int req, i
     return gstar * GRAN + granule_pick(softw(za, M, c), softw(zb, M, c), before, target, fallback, e);
 }
 
+constexpr int RES_THREADS = 512;
+constexpr int RES_WAVES = RES_THREADS / WAVE;
+
+// The draft side of the resolve, for drafts of the Markov head: p_d(x) from
+// U, the bias the sweep recorded at x and propose's (M, S); the residual
+// rescan of one granule recomputes its bias on MFMA (waves 0-3) with the
+// sweep's own expression.
+template <typename WT, int KS>
+struct MarkovDraft {
+    __device__ inline bool bad_anchor(const ResolveArgs& a, int r) const
+    {
+        const int x0r = a.s.x0[r];
+        return x0r < 0 || x0r >= a.s.V;
+    }
+    __device__ inline double pd_at(const ResolveArgs& a, int r, int t, int xk, int voff) const
+    {
+        const SweepArgs& p = a.s;
+        const size_t so = (size_t)r * p.gamma + t;
+        const double zd = (double)p.U[so * p.V + xk] + (double)p.vbias[voff + t];
+        return exp2((zd - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
+    }
+    // zrow[i] = residual weight of id 128 gstar + i at position kstar.
+    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, float* zrow,
+                                            int w, int lane) const
+    {
+        const SweepArgs& p = a.s;
+        if (w >= 4) return;
+        const int G = p.gamma;
+        const int f = voff + kstar - 1;
+        const int nrows = p.vmap ? p.counts[0] : p.max_rows;
+        const int n = lane & 31, h = lane >> 5;
+        const int nf = f & (BLOCK_ROWS - 1);
+        const int ks = k_steps<WT>(p.r);
+        const int b = 4 * gstar + w;
+        const int c0 = gstar * GRAN + 32 * w;
+        const bool v4 = (p.V % 4) == 0;
+        const int xp = kstar == 1 ? p.x0[r] : p.x[(size_t)r * G + kstar - 2];
+        typename TileOps<WT, KS>::BRow brow;
+        brow.load(reinterpret_cast<const WT*>(p.W1), p.r, n == nf ? xp : -1, ks, lane);
+        float uu[16], ll[16];
+        load_acc16(p.U + ((size_t)r * G + kstar - 1) * p.V, c0, h, p.V, v4, uu);
+        load_acc16(p.Lt + ((size_t)r * (G + 1) + kstar - 1) * p.V, c0, h, p.V, v4, ll);
+        const RowCtx rc = row_ctx(p, f, nrows);
+        TileOps<WT, KS> A;
+        A.load_a(p.W2p, ks, b, b < (p.V + 31) / 32, lane);
+        const f32x16 acc = A.mfma_row(brow, ks);
+        if (n == nf) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int col = c0 + 8 * (j >> 2) + 4 * h + (j & 3);
+                float d;
+                zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] = col < p.V ? resid(uu[j], acc[j], ll[j], rc, p.c, d) : 0.0f;
+            }
+        }
+    }
+};
+
+// Residual weight max(0, p_t - p_d) of one id for a clustered draft (p_d = 0
+// outside the row's clusters); the sparse sweep and the resolve's rescan both
+// use this expression.
+__device__ inline float cl_resid(float lt, float zd, bool in, float Mt, float iSt, float Md, float iSd, float c, float& d)
+{
+    const float pd = in ? softw(zd, Md, c) * iSd : 0.0f;
+    const float pt = softw(lt, Mt, c) * iSt;
+    d = pt - pd;
+    return fmaxf(d, 0.0f);
+}
+
+// The draft side of the resolve for drafts of the clustered head: the fine
+// logit of id v is found through its cluster and place (tok_slot) and the
+// cluster's place in the row's ascending list (binary search).
+struct ClusterDraft {
+    const int32_t* tok_slot;
+    const int32_t* sel;
+    const float* zf;
+    int N_c, K_c, max_cl;
+    __device__ inline bool bad_anchor(const ResolveArgs&, int) const { return false; }
+    __device__ inline float logit(int f, int v, bool& in) const
+    {
+        in = false;
+        const int32_t slot = tok_slot[v];
+        if (slot < 0) return 0.0f;
+        const int c = (int)((uint32_t)slot >> 16), i = slot & 0xFFFF;
+        const int32_t* sr = sel + (size_t)f * K_c;
+        int lo = 0, hi = K_c;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sr[mid] < c) lo = mid + 1;
+            else hi = mid;
+        }
+        if (lo >= K_c || sr[lo] != c || i >= max_cl) return 0.0f;
+        in = true;
+        return zf[((size_t)f * K_c + lo) * max_cl + i];
+    }
+    __device__ inline double pd_at(const ResolveArgs& a, int r, int t, int xk, int voff) const
+    {
+        const SweepArgs& p = a.s;
+        const int f = voff + t;
+        bool in;
+        const float z = logit(f, xk, in);
+        if (!in) return 0.0;
+        const size_t so = (size_t)r * p.gamma + t;
+        return exp2(((double)z - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
+    }
+    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, float* zrow,
+                                            int w, int lane) const
+    {
+        const SweepArgs& p = a.s;
+        if (w >= 2) return;
+        const int f = voff + kstar - 1;
+        const int toff = a.toff ? a.toff[r] : r * p.P;
+        const float2 ts = p.trow[toff + kstar - 1];
+        const size_t so = (size_t)r * p.gamma + kstar - 1;
+        const float Md = p.dstats[2 * so], iSd = 1.0f / p.dstats[2 * so + 1];
+        const float iSt = 1.0f / ts.y;
+        const int i = 64 * w + lane, v = gstar * GRAN + i;
+        float res = 0.0f;
+        if (v < p.V) {
+            bool in;
+            const float z = logit(f, v, in);
+            const float lt = p.Lt[((size_t)r * (p.gamma + 1) + kstar - 1) * p.V + v];
+            float d;
+            res = cl_resid(lt, z, in, ts.x, iSt, Md, iSd, p.c, d);
+        }
+        zrow[i] = res;
+    }
+};
+
 // One workgroup of eight waves per request.
 // Phase 1 does everything that does not depend on which position is rejected
 // first, in parallel: the accept test of every verified position (one thread
 // each, fp64 on the drafted id), c* of every position and the residual
 // granule search of every position (one wave each), and the bonus draw.
 // Phase 2 rescans one granule of the first rejected position's residual
-// (waves 0-3, one 32-id column block each).
-constexpr int RES_THREADS = 512;
-constexpr int RES_WAVES = RES_THREADS / WAVE;
-
-template <typename WT, int KS, bool GREEDY>
-__global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
+// (the draft side's waves).
+template <class D, bool GREEDY>
+__device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
 {
     const SweepArgs& p = a.s;
     const int r = blockIdx.x, t = threadIdx.x;
@@ -844,8 +969,7 @@ __global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
     const int L = bad_len ? 0 : Lr;
     const int voff = a.voff ? a.voff[r] : r * G;
     const int toff = a.toff ? a.toff[r] : r * p.P;
-    const int x0r = p.x0[r];
-    bool bad = bad_len || x0r < 0 || x0r >= p.V;
+    bool bad = bad_len || dr.bad_anchor(a, r);
 
     // ---- phase 1a: accept tests, one thread per verified position
     if (t < L) {
@@ -861,10 +985,7 @@ __global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
             if (GREEDY) {
                 acc = xk == a.targ[tr];
             } else {
-                // p_d(x) from U, the bias the sweep recorded at x and propose's (M, S)
-                const size_t so = (size_t)r * G + t;
-                const double zd = (double)p.U[so * p.V + xk] + (double)p.vbias[voff + t];
-                const double pd = exp2((zd - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
+                const double pd = dr.pd_at(a, r, t, xk, voff);
                 double ratio;
                 if (pd > 0.0) ratio = pt / pd;
                 else ratio = pt > 0.0 ? INFINITY : 0.0;
@@ -926,38 +1047,8 @@ __global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
     } else if (GREEDY) {
         if (t == 0) s_y = a.targ[toff + kstar - 1];
     } else if (s_Z[kstar - 1] > 0.0f) {
-        // waves 0-3 recompute column block w of granule gstar for row f: the
-        // W2 block, the W1 row of x_{k*-1}, U and the target row
         const int gstar = s_g[kstar - 1];
-        if (w < 4) {
-            const int f = voff + kstar - 1;
-            const int nrows = p.vmap ? p.counts[0] : p.max_rows;
-            const int n = lane & 31, h = lane >> 5;
-            const int nf = f & (BLOCK_ROWS - 1);
-            const int ks = k_steps<WT>(p.r);
-            const int b = 4 * gstar + w;
-            const int c0 = gstar * GRAN + 32 * w;
-            const bool v4 = (p.V % 4) == 0;
-            const int xp = kstar == 1 ? x0r : p.x[(size_t)r * G + kstar - 2];
-            typename TileOps<WT, KS>::BRow brow;
-            brow.load(reinterpret_cast<const WT*>(p.W1), p.r, n == nf ? xp : -1, ks, lane);
-            float uu[16], ll[16];
-            load_acc16(p.U + ((size_t)r * G + kstar - 1) * p.V, c0, h, p.V, v4, uu);
-            load_acc16(p.Lt + ((size_t)r * (G + 1) + kstar - 1) * p.V, c0, h, p.V, v4, ll);
-            const RowCtx rc = row_ctx(p, f, nrows);
-            TileOps<WT, KS> A;
-            A.load_a(p.W2p, ks, b, b < (p.V + 31) / 32, lane);
-            const f32x16 acc = A.mfma_row(brow, ks);
-            if (n == nf) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int col = c0 + 8 * (j >> 2) + 4 * h + (j & 3);
-                    float d;
-                    zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] =
-                        col < p.V ? resid(uu[j], acc[j], ll[j], rc, p.c, d) : 0.0f;
-                }
-            }
-        }
+        dr.residual_granule(a, r, kstar, gstar, voff, zrow, w, lane);
         __syncthreads();
         if (w == 0) {
             float e;
@@ -980,6 +1071,82 @@ __global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
         if (t < nacc) v = p.x[(size_t)r * G + t];
         else if (t == nacc) v = s_y;
         a.y[(size_t)r * (G + 1) + t] = v;
+    }
+}
+
+template <typename WT, int KS, bool GREEDY>
+__global__ __launch_bounds__(RES_THREADS) void k_verify_resolve(ResolveArgs a)
+{
+    resolve_body<MarkovDraft<WT, KS>, GREEDY>(a, MarkovDraft<WT, KS>{});
+}
+
+template <bool GREEDY>
+__global__ __launch_bounds__(RES_THREADS) void k_cluster_resolve(ResolveArgs a, ClusterDraft cd)
+{
+    resolve_body<ClusterDraft, GREEDY>(a, cd);
+}
+
+// ------------------------------------------------------ clustered drafts
+
+// The sweep for drafts of the clustered head: one workgroup per (verified
+// row f = blockIdx.x, run of gpc granules = blockIdx.y).  An LDS table maps every cluster to its place
+// in the row's list (-1: not selected); each wave takes one granule at a
+// time (two ids per lane): p_t from the target row, p_d from the fine
+// logit of the id's cluster and place (0 outside the row's clusters), and
+// the granule's (TV mass, residual mass).  There is no contraction here:
+// the kernel streams the target rows and looks up the fine logits.
+struct ClusterSweepArgs {
+    const float* Lt;
+    const int32_t* tok_slot;
+    const int32_t* sel;
+    const float* zf;
+    const float* dstats;
+    const float2* trow;
+    int gamma, P, N_c, K_c, max_cl, V, n_gran, gpc;
+    float c;
+    float2* vpart;
+};
+
+__global__ __launch_bounds__(TILE_THREADS) void k_cluster_sweep(ClusterSweepArgs a)
+{
+    __shared__ short s_j[CL_MAX_NC];
+    const int f = blockIdx.x, t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const int r = f / a.gamma, kk = f - r * a.gamma;
+    for (int c = t; c < a.N_c; c += TILE_THREADS) s_j[c] = -1;
+    __syncthreads();
+    if (t < a.K_c) {
+        const int cj = a.sel[(size_t)f * a.K_c + t];
+        if (cj >= 0 && cj < a.N_c) s_j[cj] = (short)t;
+    }
+    __syncthreads();
+    const float Md = a.dstats[2 * (size_t)f], iSd = 1.0f / a.dstats[2 * (size_t)f + 1];
+    const float2 ts = a.trow[r * a.P + kk];
+    const float iSt = 1.0f / ts.y;
+    const float* lrow = a.Lt + ((size_t)r * (a.gamma + 1) + kk) * a.V;
+    const float* zr = a.zf + (size_t)f * a.K_c * a.max_cl;
+    const int g0 = blockIdx.y * a.gpc, g1 = min(g0 + a.gpc, a.n_gran);
+    for (int g = g0 + w; g < g1; g += TILE_THREADS / WAVE) {
+        float tv = 0.0f, res = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int v = g * GRAN + 2 * lane + e;
+            if (v < a.V) {
+                const int32_t slot = a.tok_slot[v];
+                int j = -1, i = 0;
+                if (slot >= 0) {
+                    const int c = (int)((uint32_t)slot >> 16);
+                    i = slot & 0xFFFF;
+                    j = c < a.N_c && i < a.max_cl ? s_j[c] : -1;
+                }
+                const float z = j >= 0 ? zr[(size_t)j * a.max_cl + i] : 0.0f;
+                float d;
+                res += cl_resid(lrow[v], z, j >= 0, ts.x, iSt, Md, iSd, a.c, d);
+                tv += fabsf(d);
+            }
+        }
+        tv = wave_sum(tv);
+        res = wave_sum(res);
+        if (lane == 0) a.vpart[(size_t)f * a.n_gran + g] = make_float2(tv, res);
     }
 }
 
@@ -1349,6 +1516,48 @@ hipError_t launch_draft_loss(const DraftArgs& a, const float* Lt, const LossArgs
                              hipStream_t s)
 {
     return dispatch_ks<LossF>(a.w_dtype, a.r, a, Lt, l, w, s);
+}
+
+hipError_t launch_cluster_verify(const ClusterVerifyArgs& cv, const VerifyWs& w, hipStream_t s)
+{
+    DraftArgs a{};
+    a.R = cv.R; a.gamma = cv.gamma; a.V = cv.V; a.c = cv.c; a.x = cv.x; a.status = cv.status;
+    const int P = cv.gamma + 1;
+    hipError_t e = target_pass(a, cv.Lt, P, cv.R * P, w, nullptr, false, s);
+    if (e != hipSuccess) return e;
+    const int n_gran = n_granules(cv.V);
+    const int N = cv.R * cv.gamma;
+    ClusterSweepArgs ca{};
+    ca.Lt = cv.Lt; ca.tok_slot = cv.tok_slot; ca.sel = cv.sel; ca.zf = cv.zf; ca.dstats = cv.pd_stats;
+    ca.trow = w.trow; ca.gamma = cv.gamma; ca.P = P; ca.N_c = cv.N_c; ca.K_c = cv.K_c; ca.max_cl = cv.max_cl;
+    ca.V = cv.V; ca.n_gran = n_gran; ca.c = cv.c; ca.vpart = w.vpart;
+    // runs of 32 granules (eight per wave), more rows -> longer runs
+    ca.gpc = 32 * std::max(1, N / 256);
+    {
+        ProfScope ps("cluster_sweep", s);
+        hipLaunchKernelGGL(k_cluster_sweep, dim3(N, (n_gran + ca.gpc - 1) / ca.gpc), dim3(TILE_THREADS), 0, s, ca);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ResolveArgs ra{};
+    SweepArgs& sw = ra.s;
+    sw.x = cv.x; sw.dstats = cv.pd_stats; sw.Lt = cv.Lt; sw.R = cv.R; sw.gamma = cv.gamma; sw.V = cv.V; sw.P = P;
+    sw.c = cv.c; sw.vec4 = (cv.V % 4) == 0; sw.n_gran = n_gran; sw.max_rows = N; sw.trow = w.trow;
+    sw.vpart = w.vpart;
+    ra.ell = cv.ell;
+    ra.tgran = w.tgran;
+    ra.targ = w.targ;
+    ra.seed = cv.seed; ra.round = cv.round;
+    ra.n_acc = cv.n_acc; ra.y = cv.y; ra.pt_x = cv.pt_x; ra.c_star = cv.c_star; ra.status = cv.status;
+    ClusterDraft cd{cv.tok_slot, cv.sel, cv.zf, cv.N_c, cv.K_c, cv.max_cl};
+    {
+        ProfScope ps("cluster_resolve", s);
+        if (cv.greedy)
+            hipLaunchKernelGGL(k_cluster_resolve<true>, dim3(cv.R), dim3(RES_THREADS), 0, s, ra, cd);
+        else
+            hipLaunchKernelGGL(k_cluster_resolve<false>, dim3(cv.R), dim3(RES_THREADS), 0, s, ra, cd);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace spec

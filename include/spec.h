@@ -22,6 +22,13 @@
  *   spec_schedule_async  the production step: the same ranking, with the
  *                        verified count taken from the optimum two calls
  *                        earlier (a dynamic top-K)          (DSpark section 7)
+ *   spec_cluster_propose a clustered draft head: coarse logits over cluster
+ *                        centres, the top K_c clusters expanded through the
+ *                        LM head, drafts from the softmax over their tokens
+ *   spec_cluster_verify  lossless verification of those sparse drafts
+ *                        (the MTP survey page, zdszero.github.io "spec_mtp":
+ *                        Gemma 4 assistant section; FROZEN_KV_MTP in its
+ *                        SGLang section expands the top 32 by default)
  *
  * Conventions shared by every entry point
  *   Memory      Every pointer argument is DEVICE memory unless its comment says
@@ -98,6 +105,9 @@ enum spec_device_flag {
     SPEC_DEV_BAD_TOKEN = 1,       /* an anchor or draft id outside [0, V)          */
     SPEC_DEV_BAD_LENGTH = 2,      /* an l_r outside [0, gamma]                     */
     SPEC_DEV_BAD_CONFIDENCE = 4,  /* a confidence outside [0, 1] (or NaN)          */
+    SPEC_DEV_BAD_CLUSTER = 16,    /* a clustering that is not a partition into
+                                     non-empty clusters of at most max_cl tokens,
+                                     or a selection naming a cluster outside it */
     SPEC_DEV_WAIT_FAILED = 8      /* the fused propose gave up waiting for another
                                      of its workgroups (not all of them could run
                                      at once: e.g. two fused calls on different
@@ -281,6 +291,74 @@ int spec_draft_loss(const float* U, const void* W1, const void* W2, int w_dtype,
                     float a_ce, float a_tv, float a_conf,
                     double* loss, float* terms, float* dq,
                     void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* ---- Clustered draft head (the MTP survey page, zdszero.github.io
+ * "spec_mtp": its Gemma 4 assistant section -- coarse logits from 2048
+ * cluster centres, then only the top clusters go through the LM head -- and
+ * the FROZEN_KV_MTP path of its SGLang section, top 32 by default).
+ *
+ * The vocabulary is partitioned into N_c non-empty clusters, given in CSR
+ * form: cluster c holds tokens cl_tok[cl_off[c] .. cl_off[c+1]) in that
+ * listed order (cl_off [N_c+1], cl_tok [V], int32).  Per drafted row (r, k)
+ * with hidden h = H[r,k,:]:
+ *   s_c = h . C[c]                 coarse logit of every cluster
+ *   sel = the K_c clusters of largest s_c (ties: smaller index), ascending
+ *   z_v = h . E[v]                 for the tokens v of the selected clusters
+ *   p_d = softmax(z / T) over those tokens, 0 on every other token
+ *   x_k = inverse CDF over them in expansion order (clusters ascending, each
+ *         in its listed order) with Philox word 0 of counter (k, r, round);
+ *         greedy: the largest z_v, ties to the smaller token id.
+ * Positions are independent (no Markov bias; the clustered head replaces
+ * the LM head that would produce the base logits).
+ * Limits: bf16 H, C, E only; d % 16 == 0, 16 <= d <= 16384; N_c <= 8192;
+ * K_c <= 256; max_cl <= 65536; K_c * max_cl <= 65536; R * gamma <= 2^20. */
+
+/* Workspace bytes for spec_cluster_propose and spec_cluster_verify at these
+ * sizes (0 if rejected).  The status word is the workspace's. */
+size_t spec_cluster_workspace_bytes(int R, int gamma, int d, int N_c, int K_c, int max_cl, int V);
+
+/* tok_slot [V] int32 = (c << 16) | i for cl_tok[cl_off[c] + i] = v: where
+ * each token sits in the clustering (once per clustering, for
+ * spec_cluster_verify).  Checks on the device that cl_off/cl_tok partition
+ * [0, V) into non-empty clusters of at most 65536 tokens; otherwise raises
+ * SPEC_DEV_BAD_CLUSTER (tok_slot is then unusable).  ws: any workspace of at
+ * least 256 bytes (its status word). */
+int spec_cluster_index(const int32_t* cl_off, const int32_t* cl_tok, int N_c, int V, int32_t* tok_slot,
+                       void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Draft with the clustered head.
+ * In:  H [R,gamma,d], C [N_c,d], E [V,d] (bf16, w_dtype = SPEC_BF16, 16-byte
+ *      aligned); cl_off, cl_tok as above; max_cl >= the largest selected
+ *      cluster (a larger one raises SPEC_DEV_BAD_CLUSTER and blanks the row).
+ * Out: x [R,gamma] int32; pd_x [R,gamma] = p_d(x); sel [R,gamma,K_c]
+ *      ascending cluster ids; zf [R,gamma,K_c,max_cl] fp32 fine logits of the
+ *      expanded tokens (slot i of the j-th selected cluster; -inf past its
+ *      size); pd_stats [R,gamma,2] = (M, Z) with M the largest z and
+ *      Z = sum exp((z - M)/T) over the expanded tokens.
+ * A row whose clusters break the limits or the partition gets x = -1, NaN
+ * statistics and SPEC_DEV_BAD_CLUSTER. */
+int spec_cluster_propose(const void* H, const void* C, const void* E, int w_dtype,
+                         const int32_t* cl_off, const int32_t* cl_tok,
+                         int R, int gamma, int d, int N_c, int K_c, int max_cl, int V, float T,
+                         int greedy, uint64_t seed, uint64_t round,
+                         int32_t* x, float* pd_x, int32_t* sel, float* zf, float* pd_stats,
+                         void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* Verify drafts of the clustered head: the rule of spec_verify (accept with
+ * min(1, p_t/p_d), residual max(0, p_t - p_d) drawn over the whole
+ * vocabulary in ascending id order, bonus from target row l_r) with p_d the
+ * sparse distribution given by sel, zf and pd_stats from
+ * spec_cluster_propose, found per token through tok_slot
+ * (spec_cluster_index).  Outputs as spec_verify: n_acc [R], y [R,gamma+1],
+ * pt_x [R,gamma] (optional), c_star [R,gamma] (optional; c* = clamp(1 -
+ * 1/2 ||p_d - p_t||_1, 0, 1)).  ell [R] (optional) limits the verified
+ * positions.  Lt [R,gamma+1,V] fp32, 16-byte aligned. */
+int spec_cluster_verify(const int32_t* tok_slot, const int32_t* sel, const float* zf, const float* pd_stats,
+                        const int32_t* x, const float* Lt, const int32_t* ell,
+                        int R, int gamma, int N_c, int K_c, int max_cl, int V, float T,
+                        int greedy, uint64_t seed, uint64_t round,
+                        int32_t* n_acc, int32_t* y, float* pt_x, float* c_star,
+                        void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Production step of the scheduler (DSpark section 7): the candidates are
  * ranked by the current confidences exactly as in spec_schedule, but the

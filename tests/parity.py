@@ -98,6 +98,12 @@ def check_verify(d, x, ell, n_acc, y, pt_x, c_star, greedy, seed=1, rnd=0):
     T = np.float32(d["cfg"].T)
     o = oracle.verify(d["U"], d["W1"], d["W2"], d["x0"], x, d["Lt"], T, greedy, seed, rnd,
                       ell=ell, req_ids=d["req_ids"])
+    return check_verify_against(o, x, ell, n_acc, y, pt_x, c_star)
+
+
+def check_verify_against(o, x, ell, n_acc, y, pt_x, c_star):
+    """GPU verify outputs against an oracle verify dict conditioned on the
+    same drafts x."""
     R, g = x.shape
     excluded = 0
     for i in range(R):

@@ -37,7 +37,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # tensor tags of the seed sequences
-_TAG_U, _TAG_NOISE, _TAG_W1, _TAG_W2, _TAG_X0, _TAG_SIGMA, _TAG_C, _TAG_SPS, _TAG_PEAK, _TAG_Y, _TAG_Q = range(11)
+(_TAG_U, _TAG_NOISE, _TAG_W1, _TAG_W2, _TAG_X0, _TAG_SIGMA, _TAG_C, _TAG_SPS, _TAG_PEAK, _TAG_Y, _TAG_Q,
+ _TAG_CL_PERM, _TAG_CL_SIZE, _TAG_CL_MU, _TAG_CL_EPS, _TAG_CL_H, _TAG_CL_HT) = range(17)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -204,3 +205,94 @@ def make(cfg: Config | str, requests=None, threads: int | None = None) -> dict:
     if cfg.sps_len:
         out["sps"] = sawtooth_sps(cfg)
     return out
+
+
+# ------------------------------------------------------ clustered draft head
+#
+# Inputs of the clustered head: the vocabulary is split into N_c clusters by
+# a seeded permutation (equal sizes, or sizes 1 + multinomial); each token's
+# LM-head row is its cluster's mean plus noise, E_v = mu_c + eps_v (coherent
+# clusters, as an embedding clustered by k-means would give), rounded to
+# bf16; the centres C_c are the means of their clusters' bf16 rows, rounded
+# to bf16; hidden rows H ~ N(0, h_std); the target's logits are those of a
+# perturbed hidden state through the same rows, Lt = (H + N(0, t_std)) E^T
+# (the bonus row from its own draw), fp32.
+
+
+@dataclasses.dataclass(frozen=True)
+class ClusterConfig:
+    name: str
+    index: int
+    R: int
+    gamma: int
+    d: int
+    V: int
+    N_c: int
+    K_c: int
+    T: float
+    equal: bool = True     # equal cluster sizes (V % N_c == 0), else 1 + multinomial
+    mu_std: float = 0.07
+    eps_std: float = 0.03
+    h_std: float = 1.0
+    t_std: float = 0.5
+
+    def replace(self, **kw) -> "ClusterConfig":
+        return dataclasses.replace(self, **kw)
+
+
+CLUSTER_CONFIGS = {
+    # Gemma 4 E2B-like drafter head: 262144-token vocabulary, hidden 1536,
+    # 2048 centres, the top 32 expanded; 4 requests of 8 drafted tokens
+    "gemma_e2b": ClusterConfig("gemma_e2b", 60, 4, 8, 1536, 262144, 2048, 32, 1.0),
+    "cl_tiny": ClusterConfig("cl_tiny", 61, 3, 2, 16, 60, 6, 2, 1.0, equal=False, mu_std=0.5, eps_std=0.3),
+    "cl_ragged": ClusterConfig("cl_ragged", 62, 5, 3, 48, 1001, 40, 5, 0.8, equal=False, mu_std=0.4,
+                               eps_std=0.2),
+    "cl_mid": ClusterConfig("cl_mid", 63, 4, 4, 256, 20000, 160, 8, 1.0, equal=False, mu_std=0.15,
+                            eps_std=0.08),
+    "cl_rows": ClusterConfig("cl_rows", 64, 40, 2, 64, 4096, 64, 8, 1.0, mu_std=0.3, eps_std=0.15),
+}
+
+
+def _crng(cfg: ClusterConfig, tag: int, idx: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.index, tag, idx])))
+
+
+def make_cluster(cfg: ClusterConfig | str) -> dict:
+    """H [R,gamma,d], C [N_c,d], E [V,d] (bf16 bits, uint16), cl_off [N_c+1],
+    cl_tok [V] (int32), Lt [R,gamma+1,V] fp32, and max_cl."""
+    if isinstance(cfg, str):
+        cfg = CLUSTER_CONFIGS[cfg]
+    V, N_c, d = cfg.V, cfg.N_c, cfg.d
+    perm = _crng(cfg, _TAG_CL_PERM).permutation(V).astype(np.int32)
+    if cfg.equal:
+        sizes = np.full(N_c, V // N_c, np.int64)
+    else:
+        sizes = 1 + _crng(cfg, _TAG_CL_SIZE).multinomial(V - N_c, np.full(N_c, 1.0 / N_c))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    clus = np.empty(V, np.int64)
+    clus[perm] = np.repeat(np.arange(N_c), sizes)           # cluster of each token
+    mu = _crng(cfg, _TAG_CL_MU).standard_normal((N_c, d), dtype=np.float32) * np.float32(cfg.mu_std)
+    E = np.empty((V, d), np.uint16)
+
+    def fill(c):
+        lo, hi = c * _WCHUNK, min(V, (c + 1) * _WCHUNK)
+        e = _crng(cfg, _TAG_CL_EPS, c).standard_normal((hi - lo, d), dtype=np.float32)
+        e *= np.float32(cfg.eps_std)
+        e += mu[clus[lo:hi]]
+        E[lo:hi] = to_bf16_bits(e)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range((V + _WCHUNK - 1) // _WCHUNK)))
+    Ef = bf16_bits_to_f32(E)
+    # cluster c's rows are Ef[perm[off[c]:off[c+1]]]
+    sums = np.add.reduceat(Ef[perm], off[:-1], axis=0)
+    C = to_bf16_bits((sums / sizes[:, None].astype(np.float32)).astype(np.float32))
+    H = to_bf16_bits(_crng(cfg, _TAG_CL_H).standard_normal((cfg.R, cfg.gamma, d), dtype=np.float32)
+                     * np.float32(cfg.h_std))
+    Hf = bf16_bits_to_f32(H)
+    ht = _crng(cfg, _TAG_CL_HT).standard_normal((cfg.R, cfg.gamma + 1, d), dtype=np.float32)
+    ht[:, : cfg.gamma] = Hf + np.float32(cfg.t_std) * ht[:, : cfg.gamma]
+    ht[:, cfg.gamma] *= np.float32(cfg.h_std)
+    Lt = (ht.reshape(-1, d) @ Ef.T).reshape(cfg.R, cfg.gamma + 1, V).astype(np.float32)
+    return dict(cfg=cfg, H=H, C=C, E=E, cl_off=off, cl_tok=perm, Lt=Lt, max_cl=int(sizes.max()))
+
