@@ -126,6 +126,73 @@ def cpu_baseline(cfg, seconds_target=12.0):
                       % (len(reqs), cfg.R, cfg.name, t_total)}
 
 
+def cluster_bench(spec, workloads, dev, stream, n):
+    """Time spec_cluster_propose and spec_cluster_verify on the gemma_e2b
+    workload (inputs resident); per-kernel times from the library's events."""
+    import torch
+    d = workloads.make_cluster("gemma_e2b")
+    cfg = d["cfg"]
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    H, C, E = bf(d["H"]), bf(d["C"]), bf(d["E"])
+    off = torch.from_numpy(d["cl_off"]).to(dev)
+    tok = torch.from_numpy(d["cl_tok"]).to(dev)
+    Lt = torch.from_numpy(d["Lt"]).to(dev)
+    mc = d["max_cl"]
+    ws = spec.ClusterWorkspace(cfg.R, cfg.gamma, cfg.d, cfg.N_c, cfg.K_c, mc, cfg.V, device=dev)
+    slot = spec.spec_cluster_index(off, tok, ws=ws, stream=stream)
+    po = spec.spec_cluster_propose(H, C, E, off, tok, cfg.K_c, mc, cfg.T, ws=ws, stream=stream)
+    vo = spec.spec_cluster_verify(slot, po[2], po[3], po[4], po[0], Lt, cfg.T, cfg.N_c, ws=ws, stream=stream)
+
+    def step(i):
+        spec.spec_cluster_propose(H, C, E, off, tok, cfg.K_c, mc, cfg.T, False, 1, i, *po, ws=ws, stream=stream)
+        spec.spec_cluster_verify(slot, po[2], po[3], po[4], po[0], Lt, cfg.T, cfg.N_c, False, 1, i, None, *vo,
+                                 ws=ws, stream=stream)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / n
+    spec.spec_profile_reset()
+    spec.spec_profile_enable(True)
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    spec.spec_profile_enable(False)
+    kern = {}
+    for name in spec.spec_profile_names():
+        c, ms = spec.spec_profile_read(name)
+        kern[name] = round(1000.0 * ms / c, 2)
+    spec.spec_profile_reset()
+    # algorithmic bytes: the LM-head rows of the clusters some row selected,
+    # the centres and hidden rows once; verify streams the gamma + 1 target
+    # rows twice (statistics, sweep)
+    sel = po[2].cpu().numpy()
+    used = np.unique(sel)
+    sizes = np.diff(d["cl_off"])
+    pb = float(sizes[used].sum()) * cfg.d * 2 + cfg.N_c * cfg.d * 2 + cfg.R * cfg.gamma * cfg.d * 2
+    vb = 2.0 * cfg.R * (cfg.gamma + 1) * cfg.V * 4
+    full_head = float(cfg.V) * cfg.d * 2
+    ok = spec.spec_device_status(ws) == 0
+    del H, C, E, Lt
+    return {"workload": "gemma_e2b: R=%d, gamma=%d, d=%d, V=%d, N_c=%d, K_c=%d, bf16 H/C/E, equal clusters of %d, "
+                        "sampled, T=%g" % (cfg.R, cfg.gamma, cfg.d, cfg.V, cfg.N_c, cfg.K_c, mc, cfg.T),
+            "ms_per_step": round(1000.0 * el, 4), "kernels_us": kern,
+            "clusters_expanded_distinct": int(used.size),
+            "propose_algorithmic_bytes": pb, "full_lm_head_bytes": full_head,
+            "propose_algorithmic_GBs": round(pb / (sum(v for k, v in kern.items() if k.startswith("cluster_")
+                                                       and k not in ("cluster_sweep", "cluster_resolve")) * 1e-6)
+                                             / 1e9, 1),
+            "verify_algorithmic_bytes": vb,
+            "mean_n_acc": round(float(vo[0].float().mean()), 3), "device_status_ok": ok}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +207,8 @@ def main():
                          "per draft position")
     ap.add_argument("--rounds", type=int, default=8,
                     help="rounds of the multi-round loop measured after the main steps (0 = skip)")
+    ap.add_argument("--no-cluster", dest="cluster", action="store_false",
+                    help="skip the clustered draft head measurement")
     ap.add_argument("--calib-copy-mb", type=int, default=512,
                     help="size of the device-to-device copy timed as the achievable-bandwidth reference")
     args = ap.parse_args()
@@ -333,6 +402,12 @@ def main():
                      "loss": round(float(lo[0].item()), 6)}
         del yl, ql, lo
 
+    # the clustered draft head (Gemma 4 E2B-like: V = 262144, d = 1536, 2048
+    # centres, top 32 expanded) on its own workload: propose and verify
+    cluster = None
+    if not args.profile_only and args.cluster:
+        cluster = cluster_bench(spec, workloads, dev, stream, max(10, args.steps // 4))
+
     acc = float(n_acc.float().mean())
     cmean = float(c_star.float().mean())
     flags = spec.spec_device_status(ws)
@@ -379,6 +454,7 @@ def main():
         "multi_round": multi,
         "scheduler": sched,
         "training_loss": loss_info,
+        "cluster_head": cluster,
         "mean_n_acc": round(acc, 4),
         "mean_c_star": round(cmean, 4),
         "device_status": flags,

@@ -243,7 +243,7 @@ class ClusterConfig:
 CLUSTER_CONFIGS = {
     # Gemma 4 E2B-like drafter head: 262144-token vocabulary, hidden 1536,
     # 2048 centres, the top 32 expanded; 4 requests of 8 drafted tokens
-    "gemma_e2b": ClusterConfig("gemma_e2b", 60, 4, 8, 1536, 262144, 2048, 32, 1.0),
+    "gemma_e2b": ClusterConfig("gemma_e2b", 60, 4, 8, 1536, 262144, 2048, 32, 1.0, t_std=0.1),
     "cl_tiny": ClusterConfig("cl_tiny", 61, 3, 2, 16, 60, 6, 2, 1.0, equal=False, mu_std=0.5, eps_std=0.3),
     "cl_ragged": ClusterConfig("cl_ragged", 62, 5, 3, 48, 1001, 40, 5, 0.8, equal=False, mu_std=0.4,
                                eps_std=0.2),
