@@ -79,31 +79,79 @@ hipError_t launch_cluster_index(const int32_t* cl_off, const int32_t* cl_tok, in
 
 // ------------------------------------------------------ MFMA row products
 //
-// D[m][n] = sum_i A[m][i] * B[n][i] for a 32 x 32 tile on
-// v_mfma_f32_32x32x16_bf16: lane l = n + 32h supplies A row (l & 31) and B
-// row (l & 31), k-slice 8h .. 8h+7 of each 16-wide step, straight from
-// global memory (each row is contiguous along the reduction).  Result lane
-// l = n + 32h holds column n and rows m = 8 (j >> 2) + 4h + (j & 3).
-// Loads of four steps are issued before their products.
-__device__ inline f32x16 rows_dot(const uint4* pa, const uint4* pb, int s0, int s1, f32x16 acc)
+// acc_w[m][n] = sum_k A[arow[32 w + m]][k] * B[brow[n]][k] for the 128 A rows
+// and 32 B rows of a workgroup (wave w takes A rows 32 w .. 32 w + 31) on
+// v_mfma_f32_32x32x16_bf16.  The rows are gathered (token or cluster ids),
+// so the operands are staged through LDS: per batch of 64 reduction
+// elements every thread loads 16-byte pieces such that eight consecutive
+// threads read one row's 128 contiguous bytes (whole cache lines), and the
+// tiles are stored with a padded row stride (72 elements: the 32 rows of an
+// MFMA operand read fall on distinct bank groups).  The next batch's loads
+// are in flight during the current batch's products.  MFMA operand lane
+// l = n + 32h reads row (l & 31), elements 16 s + 8h .. +7 of step s; the
+// result lane l = n + 32h holds B row n and A rows m = 8 (j >> 2) + 4h +
+// (j & 3).  Rows whose id is negative read row 0; their results are never
+// stored.  All threads of the workgroup call this (it holds barriers).
+constexpr int TS = 72;  // LDS row stride (elements) of a staged tile
+
+struct TileStage {
+    uint4 a[4];
+    uint4 b;
+};
+
+__device__ inline void tile_load(TileStage& st, const bf16w* A, const int* s_arow, const bf16w* B, const int* s_brow,
+                                 int d, int kb, int k1)
 {
-    int s = s0;
-    for (; s + 4 <= s1; s += 4) {
-        uint4 a[4], b[4];
+    const int t = threadIdx.x;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = pa[2 * (s + u)];
-            b[u] = pb[2 * (s + u)];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                          __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+    for (int u = 0; u < 4; ++u) {
+        const int q = t + CL_THREADS * u, row = q >> 3, part = q & 7;
+        const int ar = s_arow[row];
+        const int k = kb + 8 * part;
+        st.a[u] = k < k1 ? *reinterpret_cast<const uint4*>(A + (size_t)(ar >= 0 ? ar : 0) * d + k)
+                         : make_uint4(0, 0, 0, 0);
     }
-    for (; s < s1; ++s) {
-        const uint4 a = pa[2 * s], b = pb[2 * s];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                      acc, 0, 0, 0);
+    const int row = t >> 3, part = t & 7;
+    const int br = s_brow[row];
+    const int k = kb + 8 * part;
+    st.b = k < k1 ? *reinterpret_cast<const uint4*>(B + (size_t)(br >= 0 ? br : 0) * d + k) : make_uint4(0, 0, 0, 0);
+}
+
+__device__ inline void tile_store(const TileStage& st, uint16_t* sA, uint16_t* sB)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int q = t + CL_THREADS * u;
+        *reinterpret_cast<uint4*>(sA + (q >> 3) * TS + 8 * (q & 7)) = st.a[u];
+    }
+    *reinterpret_cast<uint4*>(sB + (t >> 3) * TS + 8 * (t & 7)) = st.b;
+}
+
+__device__ inline f32x16 tile_dot(const bf16w* A, const int* s_arow, const bf16w* B, const int* s_brow, int d, int k0,
+                                  int k1, uint16_t* sA, uint16_t* sB)
+{
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE, h = lane >> 5;
+    f32x16 acc = {};
+    TileStage st;
+    if (k0 < k1) tile_load(st, A, s_arow, B, s_brow, d, k0, k1);
+    for (int kb = k0; kb < k1; kb += 64) {
+        tile_store(st, sA, sB);
+        __syncthreads();
+        if (kb + 64 < k1) tile_load(st, A, s_arow, B, s_brow, d, kb + 64, k1);
+        const uint16_t* pa = sA + (32 * w + (lane & 31)) * TS + 8 * h;
+        const uint16_t* pb = sB + (lane & 31) * TS + 8 * h;
+        const int steps = min(4, (k1 - kb) / 16);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            if (s2 < steps) {
+                const uint4 av = *reinterpret_cast<const uint4*>(pa + 16 * s2);
+                const uint4 bv = *reinterpret_cast<const uint4*>(pb + 16 * s2);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                              __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            }
+        }
+        __syncthreads();
     }
     return acc;
 }
@@ -111,21 +159,23 @@ __device__ inline f32x16 rows_dot(const uint4* pa, const uint4* pb, int s0, int 
 // ---------------------------------------------------------------- coarse
 
 // Workgroup (column block cb of 128 clusters, row block rb of 32 rows,
-// reduction split q): wave w covers clusters 128 cb + 32 w .. +31 over the
-// k-steps of split q and stores its partial products part[q][row][cluster].
-// Rows and clusters past the end read row 0 and are not stored.
+// reduction split q): the 128 x 32 tile of coarse logits over the split's
+// part of d, stored as part[q][row][cluster].
 __global__ __launch_bounds__(CL_THREADS) void k_cluster_coarse(const bf16w* H, const bf16w* C, int N, int N_c, int d,
                                                                int nsplit, float* part)
 {
+    __shared__ __align__(16) uint16_t sA[128 * TS];
+    __shared__ __align__(16) uint16_t sB[32 * TS];
+    __shared__ int s_arow[128], s_brow[32];
     const int cb = blockIdx.x, rb = blockIdx.y, q = blockIdx.z;
-    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE, h = lane >> 5;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE, h = lane >> 5;
+    if (t < 128) s_arow[t] = cb * 128 + t < N_c ? cb * 128 + t : -1;
+    if (t < 32) s_brow[t] = rb * 32 + t < N ? rb * 32 + t : -1;
+    __syncthreads();
     const int ks = d / 16;
-    const int s0 = (int)((long)q * ks / nsplit), s1 = (int)((long)(q + 1) * ks / nsplit);
-    const int cl = cb * 128 + 32 * w + (lane & 31);
+    const int k0 = 16 * (int)((long)q * ks / nsplit), k1 = 16 * (int)((long)(q + 1) * ks / nsplit);
+    const f32x16 acc = tile_dot(C, s_arow, H, s_brow, d, k0, k1, sA, sB);
     const int row = rb * 32 + (lane & 31);
-    const uint4* pa = reinterpret_cast<const uint4*>(C + (size_t)(cl < N_c ? cl : 0) * d) + h;
-    const uint4* pb = reinterpret_cast<const uint4*>(H + (size_t)(row < N ? row : 0) * d) + h;
-    const f32x16 acc = rows_dot(pa, pb, s0, s1, f32x16{});
     if (row >= N) return;
     float* out = part + ((size_t)q * N + row) * N_c;
 #pragma unroll
@@ -179,10 +229,23 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_select(const float* part
         s_digit = 0;
         s_krem = K_c;
     }
-    for (int c = t; c < N_c; c += CL_THREADS) {
-        float s = 0.0f;
-        for (int q = 0; q < nsplit; ++q) s += part[((size_t)q * N + n) * N_c + c];
-        s_key[c] = order_key(s);
+    // the splits' partial products, summed in split order, eight clusters
+    // per thread in flight
+    for (int cb = t; cb < N_c; cb += 8 * CL_THREADS) {
+        float v[8] = {};
+        for (int q = 0; q < nsplit; ++q) {
+            const float* pq = part + ((size_t)q * N + n) * N_c;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = cb + u * CL_THREADS;
+                v[u] += c < N_c ? pq[c] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = cb + u * CL_THREADS;
+            if (c < N_c) s_key[c] = order_key(v[u]);
+        }
     }
     uint32_t prefix = 0, pmask = 0;
     int krem = K_c;
@@ -239,11 +302,14 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_select(const float* part
 // zf[row][j][i] (j = c's place in the row's list, i = place in the
 // cluster); slots from the cluster's size to max_cl get -inf.  Tokens
 // outside [0, V) read row 0 and raise the flag (the sampler rejects the
-// row).
+// row).  Workgroups of clusters no row of the block selected exit at once.
 __global__ __launch_bounds__(CL_THREADS) void k_cluster_fine(const bf16w* H, const bf16w* E, const int32_t* cl_off,
                                                              const int32_t* cl_tok, const int32_t* sel, int N, int K_c,
                                                              int max_cl, int d, int V, float* zf, uint32_t* status)
 {
+    __shared__ __align__(16) uint16_t sA[128 * TS];
+    __shared__ __align__(16) uint16_t sB[32 * TS];
+    __shared__ int s_arow[128], s_brow[32];
     __shared__ int s_j[32];
     __shared__ int s_any;
     const int c = blockIdx.x, rb = blockIdx.y;
@@ -261,7 +327,10 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_fine(const bf16w* H, con
             }
             if (lo < K_c && sr[lo] == c) j = lo;
         }
-        if (lane < 32) s_j[lane] = j;
+        if (lane < 32) {
+            s_j[lane] = j;
+            s_brow[lane] = n < N ? n : -1;
+        }
         const bool any = __ballot(j >= 0) != 0;
         if (lane == 0) s_any = any;
     }
@@ -271,20 +340,20 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_fine(const bf16w* H, con
     int m = cl_off[c + 1] - c0;
     if (c0 < 0 || m < 0 || c0 + m > V) m = 0;  // the sampler flags the row
     if (m > max_cl) m = max_cl;
-    const int ks = d / 16;
     const int nl = lane & 31;
     const int row = rb * 32 + nl;
-    const uint4* pb = reinterpret_cast<const uint4*>(H + (size_t)(row < N ? row : 0) * d) + h;
     const int jr = s_j[nl];
     for (int i0 = 0; i0 < m; i0 += 128) {
-        const int i = i0 + 32 * w + nl;
-        int tok = i < m ? cl_tok[c0 + i] : 0;
-        if (tok < 0 || tok >= V) {
-            raise_flag(status, DEV_BAD_CLUSTER);
-            tok = 0;
+        if (t < 128) {
+            int tok = i0 + t < m ? cl_tok[c0 + i0 + t] : -1;
+            if (tok >= V || (tok < 0 && i0 + t < m)) {
+                raise_flag(status, DEV_BAD_CLUSTER);
+                tok = -1;
+            }
+            s_arow[t] = tok;
         }
-        const uint4* pa = reinterpret_cast<const uint4*>(E + (size_t)tok * d) + h;
-        const f32x16 acc = rows_dot(pa, pb, 0, ks, f32x16{});
+        __syncthreads();
+        const f32x16 acc = tile_dot(E, s_arow, H, s_brow, d, 0, d, sA, sB);
         if (jr >= 0) {
             float* out = zf + ((size_t)row * K_c + jr) * max_cl;
 #pragma unroll
@@ -361,9 +430,13 @@ struct ClusterSampleArgs {
 };
 
 // One workgroup per row f = (request, position).  Element e = j max_cl + i
-// (cluster j of the row's list, place i in it); thread t owns the
+// (cluster j of the row's list, place i in it); slots past a cluster's size
+// hold -inf, so they weigh nothing and need no test.  Thread t owns the
 // contiguous elements [t per, (t+1) per), so running sums follow the
 // expansion order: within a thread in sequence, then threads in order.
+// Loads go in batches of SB (one memory latency per batch).
+constexpr int SB = 16;
+
 template <bool GREEDY>
 __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs a)
 {
@@ -390,93 +463,93 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
     const int n_el = a.K_c * a.max_cl;
     const int per = (n_el + CL_THREADS - 1) / CL_THREADS;
     const int e0 = min(t * per, n_el), e1 = min(e0 + per, n_el);
-    __syncthreads();
     const float* z = a.zf + (size_t)f * n_el;
-    auto valid = [&](int e) { return e % a.max_cl < s_m[e / a.max_cl]; };
+    auto blank = [&]() {
+        raise_flag(a.status, DEV_BAD_CLUSTER);
+        a.x[f] = -1;
+        a.pd_x[f] = NAN;
+        a.pd_stats[2 * (size_t)f] = NAN;
+        a.pd_stats[2 * (size_t)f + 1] = NAN;
+    };
+    // token of element e (e must hold a token of the row's clusters)
     auto token = [&](int e) { return a.cl_tok[s_c0[e / a.max_cl] + e % a.max_cl]; };
     float mloc = -INFINITY;
-    for (int e = e0; e < e1; ++e) {
-        if (!valid(e)) continue;
-        const int v = token(e);
-        bad = bad || v < 0 || v >= a.V;
-        mloc = fmaxf(mloc, z[e]);
+    for (int e = e0; e < e1; e += SB) {
+        float zz[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) zz[u] = z[min(e + u, e1 - 1)];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) mloc = fmaxf(mloc, zz[u]);
     }
     bad = __syncthreads_or(bad);
     if (bad) {
-        if (t == 0) {
-            raise_flag(a.status, DEV_BAD_CLUSTER);
-            a.x[f] = -1;
-            a.pd_x[f] = NAN;
-            a.pd_stats[2 * (size_t)f] = NAN;
-            a.pd_stats[2 * (size_t)f + 1] = NAN;
-        }
+        if (t == 0) blank();
         return;
     }
     const float M = block_reduce<float>(mloc, s_ftmp, fmax_op, wmax_f);
-    if (M == -INFINITY) {  // the selected clusters hold no token
-        if (t == 0) {
-            raise_flag(a.status, DEV_BAD_CLUSTER);
-            a.x[f] = -1;
-            a.pd_x[f] = NAN;
-            a.pd_stats[2 * (size_t)f] = NAN;
-            a.pd_stats[2 * (size_t)f + 1] = NAN;
-        }
+    if (!(M > -INFINITY)) {  // no token (or NaN logits)
+        if (t == 0) blank();
         return;
     }
     float tsum = 0.0f;
-    for (int e = e0; e < e1; ++e)
-        if (valid(e)) tsum += softw(z[e], M, a.c);
+    for (int e = e0; e < e1; e += SB) {
+        float zz[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) zz[u] = z[min(e + u, e1 - 1)];
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            if (e + u < e1) tsum += softw(zz[u], M, a.c);
+    }
     float Z, lo, incl;
     block_share_f(tsum, s_ftmp, lo, incl, Z);
     int pick = -1;
     if (GREEDY) {
+        // the largest logit; ties to the smaller token id
         int best = 0x7fffffff;
         for (int e = e0; e < e1; ++e)
-            if (valid(e) && z[e] == M) best = min(best, token(e));
-        const int tok = block_reduce<int>(best, s_itmp, imin_op, wmin_i);
+            if (z[e] == M) best = min(best, token(e));
+        pick = block_reduce<int>(best, s_itmp, imin_op, wmin_i);
         if (t == 0) {
-            const bool ok = tok != 0x7fffffff;  // no logit equals the maximum: NaN logits
-            if (!ok) raise_flag(a.status, DEV_BAD_CLUSTER);
-            a.x[f] = ok ? tok : -1;
-            a.pd_x[f] = ok ? 1.0f / Z : NAN;
+            if (pick < 0 || pick >= a.V) {
+                blank();
+            } else {
+                a.x[f] = pick;
+                a.pd_x[f] = 1.0f / Z;
+            }
         }
     } else {
         const float target = u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[0]) * Z;
-        int last = -1;
-        if (tsum > 0.0f && lo <= target && target < incl) {
-            float run = lo;
-            for (int e = e0; e < e1; ++e) {
-                if (!valid(e)) continue;
-                const float wv = softw(z[e], M, a.c);
-                if (wv > 0.0f) {
-                    if (run + wv > target) { pick = e; break; }
-                    last = e;
-                }
-                run += wv;
+        int last = -1, lpos = -1;
+        float run = lo;
+        // this thread's share [lo, incl) holds the target: walk it
+        const bool mine = tsum > 0.0f && lo <= target && target < incl;
+        for (int e = e0; e < e1; ++e) {
+            const float wv = softw(z[e], M, a.c);
+            if (wv > 0.0f) {
+                if (mine && pick < 0 && run + wv > target) pick = e;
+                lpos = e;
             }
-            if (pick < 0) pick = last;  // this share's own sum rounded below the target
+            run += wv;
         }
+        last = lpos;
+        if (mine && pick < 0) pick = last;  // the share's own sum rounded below the target
         if (pick >= 0) s_pick = pick;
+        const int found = block_reduce<int>(pick, s_itmp, imax_op, wmax_i);
         // no share holds the target (the total rounded below it): the last
         // element with weight
-        int lpos = -1;
-        for (int e = e0; e < e1; ++e)
-            if (valid(e) && softw(z[e], M, a.c) > 0.0f) lpos = e;
-        const int found = block_reduce<int>(pick, s_itmp, imax_op, wmax_i);
         const int lastpos = block_reduce<int>(lpos, s_itmp, imax_op, wmax_i);
         if (t == 0) {
             const int e = found >= 0 ? s_pick : lastpos;
-            if (e < 0) {  // no element with weight: NaN logits
-                raise_flag(a.status, DEV_BAD_CLUSTER);
-                a.x[f] = -1;
-                a.pd_x[f] = NAN;
+            const int v = e >= 0 ? token(e) : -1;
+            if (v < 0 || v >= a.V) {
+                blank();
             } else {
-                a.x[f] = token(e);
+                a.x[f] = v;
                 a.pd_x[f] = softw(z[e], M, a.c) / Z;
             }
         }
     }
-    if (t == 0) {
+    if (t == 0 && a.x[f] >= 0) {
         a.pd_stats[2 * (size_t)f] = M;
         a.pd_stats[2 * (size_t)f + 1] = Z;
     }
@@ -484,11 +557,13 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
 
 // ------------------------------------------------------------- launcher
 
+// Splits of d for the coarse product: enough workgroups to spread the
+// centres over the chip, at most 4 partial products to sum per logit.
 static int coarse_splits(int N, int N_c, int d)
 {
     const int nb = ((N + 31) / 32) * ((N_c + 127) / 128);
-    int q = (512 + nb - 1) / nb;
-    return std::max(1, std::min(q, d / 16));
+    int q = (256 + nb - 1) / nb;
+    return std::max(1, std::min(std::min(q, 4), d / 64));
 }
 
 size_t cluster_propose_ws_bytes(int N, int N_c, int d)

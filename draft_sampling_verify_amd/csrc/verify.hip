@@ -1125,28 +1125,52 @@ __global__ __launch_bounds__(TILE_THREADS) void k_cluster_sweep(ClusterSweepArgs
     const float* lrow = a.Lt + ((size_t)r * (a.gamma + 1) + kk) * a.V;
     const float* zr = a.zf + (size_t)f * a.K_c * a.max_cl;
     const int g0 = blockIdx.y * a.gpc, g1 = min(g0 + a.gpc, a.n_gran);
-    for (int g = g0 + w; g < g1; g += TILE_THREADS / WAVE) {
-        float tv = 0.0f, res = 0.0f;
+    // batches of CSB granules per wave: the target values and slots of the
+    // whole batch are loaded first, then the fine logits they name
+    constexpr int CSB = 8;
+    for (int gb = g0 + w; gb < g1; gb += CSB * (TILE_THREADS / WAVE)) {
+        float lt[CSB][2];
+        int32_t sl[CSB][2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int v = g * GRAN + 2 * lane + e;
-            if (v < a.V) {
-                const int32_t slot = a.tok_slot[v];
+        for (int u = 0; u < CSB; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int v = min((gb + u * (TILE_THREADS / WAVE)) * GRAN + 2 * lane + e, a.V - 1);
+                lt[u][e] = lrow[v];
+                sl[u][e] = a.tok_slot[v];
+            }
+        float zz[CSB][2];
+        int jj[CSB][2];
+#pragma unroll
+        for (int u = 0; u < CSB; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int32_t slot = sl[u][e];
                 int j = -1, i = 0;
                 if (slot >= 0) {
                     const int c = (int)((uint32_t)slot >> 16);
                     i = slot & 0xFFFF;
                     j = c < a.N_c && i < a.max_cl ? s_j[c] : -1;
                 }
-                const float z = j >= 0 ? zr[(size_t)j * a.max_cl + i] : 0.0f;
-                float d;
-                res += cl_resid(lrow[v], z, j >= 0, ts.x, iSt, Md, iSd, a.c, d);
-                tv += fabsf(d);
+                jj[u][e] = j;
+                zz[u][e] = j >= 0 ? zr[(size_t)j * a.max_cl + i] : 0.0f;
             }
+#pragma unroll
+        for (int u = 0; u < CSB; ++u) {
+            const int g = gb + u * (TILE_THREADS / WAVE);
+            float tv = 0.0f, res = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if (g * GRAN + 2 * lane + e < a.V) {
+                    float d;
+                    res += cl_resid(lt[u][e], zz[u][e], jj[u][e] >= 0, ts.x, iSt, Md, iSd, a.c, d);
+                    tv += fabsf(d);
+                }
+            }
+            tv = wave_sum(tv);
+            res = wave_sum(res);
+            if (lane == 0 && g < g1) a.vpart[(size_t)f * a.n_gran + g] = make_float2(tv, res);
         }
-        tv = wave_sum(tv);
-        res = wave_sum(res);
-        if (lane == 0) a.vpart[(size_t)f * a.n_gran + g] = make_float2(tv, res);
     }
 }
 
