@@ -54,6 +54,7 @@ struct VerifyWs {
     int32_t* dgidx;  // confidence only
     float2* drow;    // confidence only: [VR] draft (M, S)
     double* contrib; // loss only: [VR] weighted loss of each position
+    float4* tpart;   // [TR, 16] per-part target row statistics (rows split over workgroups)
 };
 
 inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence, size_t* bytes,
@@ -80,6 +81,7 @@ inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence,
         w.drow = c.take<float2>(VR);
     }
     if (loss) w.contrib = c.take<double>(VR);
+    w.tpart = c.take<float4>(TR * 16);
     if (bytes) *bytes = c.off;
     return w;
 }

@@ -91,6 +91,8 @@ struct TargetArgs {
     float c;
     int vec4;
     int n_gran, max_rows;
+    int nsplit;              // workgroups per row (1: the row's statistics are final)
+    float4* tpart;           // nsplit > 1: [rows, nsplit] (max, sum, argmax bits, -) per part
     const int2* tmap;        // NULL = implicit
     const int32_t* counts;   // counts[1] = rows when tmap != NULL
     float2* tgran;
@@ -107,21 +109,26 @@ struct TargetArgs {
 // (M_t, S_t, argmax) at the end, so no separate merge pass is needed.
 constexpr int TROW_THREADS = 1024;
 constexpr int TROW_GRANS = TROW_THREADS / 8;  // granules per step
+constexpr int TROW_MAX_SPLIT = 16;            // workgroups per row at most
 
+// With few rows a row is split over nsplit workgroups (consecutive runs of
+// steps); each writes its part's (max, sum, argmax) and k_target_merge folds
+// the parts in order.
 __global__ __launch_bounds__(TROW_THREADS) void k_target_rows(TargetArgs p)
 {
-    const int row = blockIdx.x;
+    const int row = blockIdx.x / p.nsplit, part = blockIdx.x - row * p.nsplit;
     const int nrows = p.tmap ? p.counts[1] : p.max_rows;
     if (row >= nrows) return;
     const int2 ti = trow_info(p.tmap, row, p.P);
     const float* L = p.Lt + ((size_t)ti.x * (p.gamma + 1) + ti.y) * p.V;
     const int t = threadIdx.x, gi = t >> 3, l8 = t & 7;
-    const int steps = (p.n_gran + TROW_GRANS - 1) / TROW_GRANS;
+    const int steps_all = (p.n_gran + TROW_GRANS - 1) / TROW_GRANS;
+    const int st0 = part * steps_all / p.nsplit, steps = (part + 1) * steps_all / p.nsplit;
     float rm = -INFINITY, rs = 0.0f;
     int rbi = 0x7fffffff;
     float cur[16], nxt[16];
-    load16(L, gi * GRAN + 16 * l8, p.V, p.vec4, cur);
-    for (int st = 0; st < steps; ++st) {
+    load16(L, (st0 * TROW_GRANS + gi) * GRAN + 16 * l8, p.V, p.vec4, cur);
+    for (int st = st0; st < steps; ++st) {
         if (st + 1 < steps) load16(L, ((st + 1) * TROW_GRANS + gi) * GRAN + 16 * l8, p.V, p.vec4, nxt);
         const int g = st * TROW_GRANS + gi;
         const int c0 = g * GRAN + 16 * l8;
@@ -188,9 +195,34 @@ __global__ __launch_bounds__(TROW_THREADS) void k_target_rows(TargetArgs p)
             S += s_s[i] * softw(s_m[i], Ms, p.c);
             if (s_m[i] == M && s_i[i] < best) best = s_i[i];
         }
-        p.trow[row] = make_float2(M, S);
-        p.targ[row] = best;
+        if (p.nsplit == 1) {
+            p.trow[row] = make_float2(M, S);
+            p.targ[row] = best;
+        } else {
+            p.tpart[(size_t)row * p.nsplit + part] = make_float4(M, S, __int_as_float(best), 0.0f);
+        }
     }
+}
+
+// One thread per row: the parts' (max, sum, argmax) folded in part order.
+__global__ void k_target_merge(TargetArgs p)
+{
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    const int nrows = p.tmap ? p.counts[1] : p.max_rows;
+    if (row >= nrows) return;
+    const float4* tp = p.tpart + (size_t)row * p.nsplit;
+    float M = -INFINITY;
+    for (int i = 0; i < p.nsplit; ++i) M = fmaxf(M, tp[i].x);
+    const float Ms = safe_ref(M);
+    float S = 0.0f;
+    int best = 0x7fffffff;
+    for (int i = 0; i < p.nsplit; ++i) {
+        const float4 v = tp[i];
+        S += v.y * softw(v.x, Ms, p.c);
+        if (v.x == M && __float_as_int(v.z) < best) best = __float_as_int(v.z);
+    }
+    p.trow[row] = make_float2(M, S);
+    p.targ[row] = best;
 }
 
 // ------------------------------------------------------------ TV sweep
@@ -1324,9 +1356,15 @@ static hipError_t target_pass(const DraftArgs& a, const float* Lt, int P, int ma
     t.tmap = maps ? w.tmap : nullptr;
     t.counts = counts;
     t.tgran = w.tgran; t.tgidx = w.tgidx; t.trow = w.trow; t.targ = w.targ;
+    // split rows over several workgroups while there are fewer than about
+    // 256 of them
+    const int steps = (t.n_gran + TROW_GRANS - 1) / TROW_GRANS;
+    t.nsplit = std::max(1, std::min(std::min(256 / std::max(max_rows, 1), steps), TROW_MAX_SPLIT));
+    t.tpart = w.tpart;
     {
         ProfScope ps("target_rows", s);
-        hipLaunchKernelGGL(k_target_rows, dim3(max_rows), dim3(TROW_THREADS), 0, s, t);
+        hipLaunchKernelGGL(k_target_rows, dim3(max_rows * t.nsplit), dim3(TROW_THREADS), 0, s, t);
+        if (t.nsplit > 1) hipLaunchKernelGGL(k_target_merge, dim3((max_rows + 255) / 256), dim3(256), 0, s, t);
     }
     return hipGetLastError();
 }
