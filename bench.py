@@ -209,6 +209,8 @@ def main():
                     help="rounds of the multi-round loop measured after the main steps (0 = skip)")
     ap.add_argument("--no-cluster", dest="cluster", action="store_false",
                     help="skip the clustered draft head measurement")
+    ap.add_argument("--profile-cluster", action="store_true",
+                    help="run only the clustered draft head's steps (for rocprofv3), print its JSON object")
     ap.add_argument("--calib-copy-mb", type=int, default=512,
                     help="size of the device-to-device copy timed as the achievable-bandwidth reference")
     args = ap.parse_args()
@@ -225,6 +227,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     spec.lib()
+    if args.profile_cluster:
+        print(json.dumps(cluster_bench(spec, workloads, torch.device("cuda:0"), torch.cuda.current_stream(),
+                                       args.steps)), flush=True)
+        return
     spec.spec_set_propose_fused(args.propose_path == "auto")
     cfg = workloads.CONFIGS[args.workload]
     d = workloads.make(cfg)

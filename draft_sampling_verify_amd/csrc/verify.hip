@@ -110,6 +110,7 @@ struct TargetArgs {
 constexpr int TROW_THREADS = 1024;
 constexpr int TROW_GRANS = TROW_THREADS / 8;  // granules per step
 constexpr int TROW_MAX_SPLIT = 16;            // workgroups per row at most
+constexpr int TROW_TARGET_WGS = 256;          // rows are split while fewer than this (more is slower)
 
 // With few rows a row is split over nsplit workgroups (consecutive runs of
 // steps); each writes its part's (max, sum, argmax) and k_target_merge folds
@@ -1359,7 +1360,7 @@ static hipError_t target_pass(const DraftArgs& a, const float* Lt, int P, int ma
     // split rows over several workgroups while there are fewer than about
     // 256 of them
     const int steps = (t.n_gran + TROW_GRANS - 1) / TROW_GRANS;
-    t.nsplit = std::max(1, std::min(std::min(256 / std::max(max_rows, 1), steps), TROW_MAX_SPLIT));
+    t.nsplit = std::max(1, std::min(std::min(TROW_TARGET_WGS / std::max(max_rows, 1), steps), TROW_MAX_SPLIT));
     t.tpart = w.tpart;
     {
         ProfScope ps("target_rows", s);
