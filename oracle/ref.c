@@ -617,13 +617,13 @@ int ref_schedule_async(const float* c, int R, int gamma, const float* sps, int B
 
 /* ---------------------------------------------------- clustered draft head */
 
-/* cl_off/cl_tok partition [0, V): offsets nondecreasing from 0 to V, and
- * every token listed exactly once. */
+/* cl_off/cl_tok partition [0, V) into non-empty clusters: offsets strictly
+ * increasing from 0 to V, and every token listed exactly once. */
 static int cluster_partition_ok(const int32_t* cl_off, const int32_t* cl_tok, int N_c, int V)
 {
     if (cl_off[0] != 0 || cl_off[N_c] != V) return 0;
     for (int c = 0; c < N_c; ++c)
-        if (cl_off[c + 1] < cl_off[c]) return 0;
+        if (cl_off[c + 1] <= cl_off[c]) return 0;  /* every cluster holds a token */
     unsigned char* seen = (unsigned char*)calloc((size_t)V, 1);
     if (!seen) return 0;
     int ok = 1;

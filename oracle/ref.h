@@ -164,7 +164,8 @@ int ref_schedule_async(const float* c, int R, int gamma, const float* sps, int B
  * Positions are independent (no Markov bias: the clustered head replaces
  * the LM head that produces the base logits).
  * Layouts: H [R,gamma,d], C [N_c,d], E [V,d] (fp32 or bf16 bits, one dtype);
- * cl_off [N_c+1], cl_tok [V]: a partition of the vocabulary (CSR).
+ * cl_off [N_c+1], cl_tok [V]: a partition of the vocabulary into non-empty
+ * clusters (CSR).
  * Outputs: x, pd_x, sel [R,gamma,K_c], pd_stats [R,gamma,2] = (M, Z);
  * optional cut [R,gamma] = s_(K_c) - s_(K_c+1) (infinite when K_c = N_c) and
  * margin [R,gamma] (the sampling decision's, as ref_markov_propose).
