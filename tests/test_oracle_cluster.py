@@ -179,6 +179,10 @@ def test_bad_arguments_are_rejected():
         oracle.cluster_propose(H, C, E, off, bad, 2, 1.0)
     with pytest.raises(oracle.OracleError):
         oracle.cluster_propose(H, C, E, off, tok, off.size, 1.0)   # K_c > N_c
+    empty = off.copy()
+    empty[1] = empty[0]                                # cluster 0 holds no token
+    with pytest.raises(oracle.OracleError):
+        oracle.cluster_propose(H, C, E, empty, tok, 2, 1.0)
     o = oracle.cluster_propose(H, C, E, off, tok, 3, 1.0)
     sel = o["sel"].copy()
     sel[0, 0] = sel[0, 0][::-1]                        # not ascending
