@@ -215,3 +215,45 @@ def test_gemma_e2b_shape_sampled_rows(greedy):
     log("  gemma_e2b verify", check_verify_against(ov, g["x"][:1], None, g["n_acc"][:1], g["y"][:1], g["pt_x"][:1],
                                                   g["c_star"][:1]))
     assert (g["n_acc"] >= 0).all()
+
+
+def test_cluster_graph_replays_match_eager():
+    """propose + verify of the clustered head captured in one HIP graph:
+    every replay (with eager work in between) equals the eager call."""
+    d = _inputs("cl_mid")
+    cfg = d["cfg"]
+    t = _dev(d)
+    mc = d["max_cl"]
+    ws = spec.ClusterWorkspace(cfg.R, cfg.gamma, cfg.d, cfg.N_c, cfg.K_c, mc, cfg.V)
+    slot = spec.spec_cluster_index(t["cl_off"], t["cl_tok"], ws=ws)
+    po = spec.spec_cluster_propose(t["H"], t["C"], t["E"], t["cl_off"], t["cl_tok"], cfg.K_c, mc, cfg.T, ws=ws)
+    vo = spec.spec_cluster_verify(slot, po[2], po[3], po[4], po[0], t["Lt"], cfg.T, cfg.N_c, ws=ws)
+    outs = list(po) + list(vo)
+
+    def run(stream):
+        spec.spec_cluster_propose(t["H"], t["C"], t["E"], t["cl_off"], t["cl_tok"], cfg.K_c, mc, cfg.T, False, 5, 9,
+                                  *po, ws=ws, stream=stream)
+        spec.spec_cluster_verify(slot, po[2], po[3], po[4], po[0], t["Lt"], cfg.T, cfg.N_c, False, 5, 9, None, *vo,
+                                 ws=ws, stream=stream)
+
+    run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run(torch.cuda.current_stream())
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), (rep, i)
+    assert spec.spec_device_status(ws) == 0

@@ -170,3 +170,36 @@ def test_loss_rejects_empty_batch():
         spec.spec_draft_loss(t["U"][:0], t["W1"], t["W2p"], t["x0"][:0], t["y"][:0], t["Lt"][:0], t["q"][:0],
                              cfg.T, ALPHAS, ws=ws)
     assert e.value.status == spec.SPEC_EINVAL
+
+
+def test_loss_graph_replays_match_eager():
+    cfg = SMALL["lds_multi"]
+    d, t = _inputs(cfg)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    outs = spec.spec_draft_loss(t["U"], t["W1"], t["W2p"], t["x0"], t["y"], t["Lt"], t["q"], cfg.T, ALPHAS, ws=ws)
+
+    def run(stream):
+        spec.spec_draft_loss(t["U"], t["W1"], t["W2p"], t["x0"], t["y"], t["Lt"], t["q"], cfg.T, ALPHAS,
+                             loss=outs[0], terms=outs[1], dq=outs[2], ws=ws, stream=stream)
+
+    run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run(torch.cuda.current_stream())
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), (rep, i)
+    assert spec.spec_device_status(ws) == 0
