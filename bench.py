@@ -87,6 +87,23 @@ def step_algorithmic_bytes(cfg, K: int) -> float:
     return propose + verify
 
 
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def mfma_report(cfg, K: int, kernels: dict) -> dict:
+    """The Markov-bias contraction's rate on the matrix cores: 2 r V flops
+    per biased row (propose: R gamma rows, verify sweep: K rows), over each
+    kernel's time.  Not the bound (about 128 flop per HBM byte against a
+    ridge near 312), reported for completeness."""
+    out = {"peak_TFLOPs": PEAK_BF16_TFLOPS, "dtype": "bf16" if cfg.bf16 else "fp32"}
+    for name, rows in (("propose_fused", cfg.R * cfg.gamma), ("draft_tile", cfg.R), ("verify_sweep", K)):
+        if name in kernels:
+            fl = 2.0 * cfg.r * cfg.V * rows
+            tf = fl / (kernels[name]["avg_us"] * 1e-6) / 1e12
+            out[name] = {"flop_per_launch": fl, "TFLOPs": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel's sources changed since."""
@@ -453,6 +470,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": per_launch},
         "hbm_roofline_frac_step": round(step_bytes / (PEAK_HBM_GBS * 1e9) / (elapsed / args.steps), 4),
+        "mfma": mfma_report(cfg, K, kernels),
         "device_copy_GBs": None if copy_gbs is None else round(copy_gbs, 1),
         "step_algorithmic_bytes": step_bytes,
         "ms_per_step_with_kernel_events": round(1000.0 * elapsed_prof / args.steps, 4),
