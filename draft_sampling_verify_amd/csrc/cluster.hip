@@ -393,18 +393,19 @@ __device__ inline float wmax_f(float v) { return wave_max(v); }
 __device__ inline int wmin_i(int v) { return wave_min(v); }
 __device__ inline int wmax_i(int v) { return wave_max_int(v); }
 
-// Running sum of one float per thread over the workgroup, waves in order:
+// Running sum of one value per thread over the workgroup, waves in order:
 // [lo, hi) is this thread's share.  Consecutive shares meet exactly (the next
-// share's lo is computed by the same additions as this one's hi).
-__device__ inline void block_share_f(float v, float* s_tmp, float& lo, float& hi, float& total)
+// share's lo is computed by the same additions as this one's hi).  fp64: a
+// row expands up to 65536 tokens, 256 per thread.
+__device__ inline void block_share_d(double v, double* s_tmp, double& lo, double& hi, double& total)
 {
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-    const float x = wave_incl_scan(v);
-    float xe = __shfl_up(x, 1, WAVE);
-    if (lane == 0) xe = 0.0f;
+    const double x = wave_incl_scan(v);
+    double xe = __shfl_up(x, 1, WAVE);
+    if (lane == 0) xe = 0.0;
     if (lane == WAVE - 1) s_tmp[w] = x;
     __syncthreads();
-    float base = 0.0f, tot = 0.0f;
+    double base = 0.0, tot = 0.0;
     for (int i = 0; i < CL_THREADS / WAVE; ++i) {
         if (i == w) base = tot;
         tot += s_tmp[i];
@@ -442,6 +443,7 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
 {
     __shared__ int s_c0[CL_MAX_K], s_m[CL_MAX_K];
     __shared__ float s_ftmp[CL_THREADS / WAVE];
+    __shared__ double s_dtmp[CL_THREADS / WAVE];
     __shared__ int s_itmp[CL_THREADS / WAVE];
     __shared__ int s_pick;
     const int f = blockIdx.x, t = threadIdx.x;
@@ -491,17 +493,18 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
         if (t == 0) blank();
         return;
     }
-    float tsum = 0.0f;
+    double tsum = 0.0;
     for (int e = e0; e < e1; e += SB) {
         float zz[SB];
 #pragma unroll
         for (int u = 0; u < SB; ++u) zz[u] = z[min(e + u, e1 - 1)];
 #pragma unroll
         for (int u = 0; u < SB; ++u)
-            if (e + u < e1) tsum += softw(zz[u], M, a.c);
+            if (e + u < e1) tsum += (double)softw(zz[u], M, a.c);
     }
-    float Z, lo, incl;
-    block_share_f(tsum, s_ftmp, lo, incl, Z);
+    double Zd, lo, incl;
+    block_share_d(tsum, s_dtmp, lo, incl, Zd);
+    const float Z = (float)Zd;
     int pick = -1;
     if (GREEDY) {
         // the largest logit; ties to the smaller token id
@@ -518,18 +521,18 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
             }
         }
     } else {
-        const float target = u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[0]) * Z;
+        const double target = (double)u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[0]) * Zd;
         int last = -1, lpos = -1;
-        float run = lo;
+        double run = lo;
         // this thread's share [lo, incl) holds the target: walk it
-        const bool mine = tsum > 0.0f && lo <= target && target < incl;
+        const bool mine = tsum > 0.0 && lo <= target && target < incl;
         for (int e = e0; e < e1; ++e) {
             const float wv = softw(z[e], M, a.c);
             if (wv > 0.0f) {
-                if (mine && pick < 0 && run + wv > target) pick = e;
+                if (mine && pick < 0 && run + (double)wv > target) pick = e;
                 lpos = e;
             }
-            run += wv;
+            run += (double)wv;
         }
         last = lpos;
         if (mine && pick < 0) pick = last;  // the share's own sum rounded below the target

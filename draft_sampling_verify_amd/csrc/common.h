@@ -211,6 +211,16 @@ __device__ inline float wave_incl_scan(float v)
     }
     return v;
 }
+__device__ inline double wave_incl_scan(double v)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        double t = __shfl_up(v, o, WAVE);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
 
 // ---------------------------------------------------- block-wide scans (256)
 
@@ -269,18 +279,24 @@ __device__ inline int block_min(int v, int* sm)
 // sum first exceeds target = u * total; one wave then rescans that
 // granule's 128 weights.  Threads of a 256-wide block own contiguous
 // granule ranges [g0, g1).
+//
+// Sums across granules run in fp64: a lane may own thousands of granules
+// (131072 of them at V = 2^24), and an fp32 running sum of that length
+// drifts by up to its length in units of the last place, enough to move a
+// draw whose u lies within 1e-5 of a token boundary.  In fp64 the error
+// left is that of the fp32 granule masses themselves (about 1e-7 relative).
 
 // One wave; lane l owns the contiguous granule range [g0, g1).  Returns the
 // lane's exclusive prefix of the granule masses and the wave total.
 template <typename WF>
-__device__ inline void wave_granule_scan(WF wf, int g0, int g1, float& excl, float& total)
+__device__ inline void wave_granule_scan(WF wf, int g0, int g1, double& excl, double& total)
 {
     const int lane = threadIdx.x & (WAVE - 1);
-    float tsum = 0.0f;
-    for (int g = g0; g < g1; ++g) tsum += wf(g);
-    const float incl = wave_incl_scan(tsum);
+    double tsum = 0.0;
+    for (int g = g0; g < g1; ++g) tsum += (double)wf(g);
+    const double incl = wave_incl_scan(tsum);
     excl = __shfl_up(incl, 1, WAVE);
-    if (lane == 0) excl = 0.0f;
+    if (lane == 0) excl = 0.0;
     total = __shfl(incl, WAVE - 1, WAVE);
 }
 
@@ -291,17 +307,17 @@ __device__ inline void wave_granule_scan(WF wf, int g0, int g1, float& excl, flo
 // identical in every lane; if no partial sum exceeds target (rounding),
 // returns the last granule with positive mass and sets fallback.
 template <typename WF>
-__device__ inline int wave_granule_find(WF wf, int g0, int g1, float excl, float target, float& before,
+__device__ inline int wave_granule_find(WF wf, int g0, int g1, double excl, double target, double& before,
                                         bool& fallback)
 {
-    float run = excl, prev = excl;
+    double run = excl, prev = excl;
     int pick = -1, lastpos = -1;
     for (int g = g0; g < g1; ++g) {
         const float wg = wf(g);
         if (wg > 0.0f) lastpos = g;
         if (pick < 0) {
             prev = run;
-            run += wg;
+            run += (double)wg;
             if (run > target && wg > 0.0f) pick = g;
         }
     }
@@ -313,7 +329,7 @@ __device__ inline int wave_granule_find(WF wf, int g0, int g1, float excl, float
         return __shfl(pick, L, WAVE);
     }
     fallback = true;
-    before = 0.0f;
+    before = 0.0;
     const int lp = -wave_min(-lastpos);
     return lp < 0 ? 0 : lp;
 }
@@ -331,15 +347,15 @@ __device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& tot
 {
     const int lane = threadIdx.x & (WAVE - 1);
     float T[NR];
-    float Z = 0.0f;
+    double Z = 0.0;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         T[i] = wave_sum(w[i]);
-        Z += T[i];
+        Z += (double)T[i];
     }
-    total = Z;
-    const float target = u * Z;
-    float pre = 0.0f, rbase = 0.0f;
+    total = (float)Z;
+    const double target = (double)u * Z;
+    double pre = 0.0, rbase = 0.0;
     int rstar = -1;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -359,12 +375,12 @@ __device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& tot
     const float incl = wave_incl_scan(wr);
     float ex = __shfl_up(incl, 1, WAVE);
     if (lane == 0) ex = 0.0f;
-    const float run0 = rbase + ex;
-    const unsigned long long hit = __ballot(rstar >= 0 && wr > 0.0f && run0 + wr > target);
+    const double run0 = rbase + (double)ex;
+    const unsigned long long hit = __ballot(rstar >= 0 && wr > 0.0f && run0 + (double)wr > target);
     if (hit) {
         const int L = __ffsll((long long)hit) - 1;
         fallback = false;
-        before = __shfl(run0, L, WAVE);
+        before = (float)__shfl(run0, L, WAVE);
         return L + WAVE * rstar;
     }
     fallback = true;

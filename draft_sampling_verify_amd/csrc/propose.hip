@@ -261,18 +261,20 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
     for (int g = g0 + PICK_CACHE; g < g1; ++g) m = fmaxf(m, gs[g].x);
     const float M = wave_max(m);
     const float c = p.c;
+    // sums across granules in fp64 (a lane owns up to 2048 granules)
     float wv[PICK_CACHE];
-    float tsum = 0.0f;
+    double tsum = 0.0;
 #pragma unroll
     for (int i = 0; i < PICK_CACHE; ++i) {
         wv[i] = gc[i].y * softw(gc[i].x, M, c);  // padding: 0 * 0
-        tsum += wv[i];
+        tsum += (double)wv[i];
     }
-    for (int g = g0 + PICK_CACHE; g < g1; ++g) tsum += gs[g].y * softw(gs[g].x, M, c);
-    const float incl = wave_incl_scan(tsum);
-    float excl = __shfl_up(incl, 1, WAVE);
-    if (lane == 0) excl = 0.0f;
-    const float S = __shfl(incl, WAVE - 1, WAVE);
+    for (int g = g0 + PICK_CACHE; g < g1; ++g) tsum += (double)(gs[g].y * softw(gs[g].x, M, c));
+    const double incl = wave_incl_scan(tsum);
+    double excl = __shfl_up(incl, 1, WAVE);
+    if (lane == 0) excl = 0.0;
+    const double Sd = __shfl(incl, WAVE - 1, WAVE);
+    const float S = (float)Sd;
 
     if (GREEDY) {
         if (w != 0) return;
@@ -290,17 +292,18 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
     }
 
     const float u = u24f(philox((uint32_t)p.k, (uint32_t)q, p.round, p.seed).w[0]);
-    const float target = u * S;
+    const double target_d = (double)u * Sd;
+    const float target = (float)target_d;
     // first granule of positive mass whose running sum exceeds target
-    float run = excl, prev = excl;
+    double run = excl, prev = excl;
     int pick = -1, lastpos = -1;
 #pragma unroll
     for (int i = 0; i < PICK_CACHE; ++i) {
         if (wv[i] > 0.0f) lastpos = g0 + i;
         if (pick < 0) {
             prev = run;
-            run += wv[i];
-            if (run > target && wv[i] > 0.0f) pick = g0 + i;
+            run += (double)wv[i];
+            if (run > target_d && wv[i] > 0.0f) pick = g0 + i;
         }
     }
     for (int g = g0 + PICK_CACHE; g < g1; ++g) {
@@ -308,8 +311,8 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         if (wg > 0.0f) lastpos = g;
         if (pick < 0) {
             prev = run;
-            run += wg;
-            if (run > target && wg > 0.0f) pick = g;
+            run += (double)wg;
+            if (run > target_d && wg > 0.0f) pick = g;
         }
     }
     const unsigned long long hit = __ballot(pick >= 0);
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
     if (hit) {
         const int L = __ffsll((long long)hit) - 1;
         fallback = false;
-        before = __shfl(prev, L, WAVE);
+        before = (float)__shfl(prev, L, WAVE);
         gstar = __shfl(pick, L, WAVE);
     } else {
         fallback = true;

@@ -735,15 +735,16 @@ struct ResolveArgs {
 };
 
 // Lane-strided TV mass of one row's granule records: lane l adds granules
-// l, l + 64, l + 128, ... in that order, with the loads of a batch of 16
+// l, l + 64, l + 128, ... in that order, in fp64 (thousands of terms per
+// lane at the largest vocabularies), with the loads of a batch of 16
 // issued before any of them is added, so a row costs about one memory
 // latency rather than one per granule.  Every kernel that reports c* sums in
 // this order, so verify, confidence and the loss give the same bits.
-__device__ inline float lane_tv_mass(const float2* vp, int n)
+__device__ inline double lane_tv_mass(const float2* vp, int n)
 {
     constexpr int NB = 16;
     const int lane = threadIdx.x & (WAVE - 1);
-    float s = 0.0f;
+    double s = 0.0;
     for (int g0 = 0; g0 < n; g0 += NB * WAVE) {
         float v[NB];
 #pragma unroll
@@ -753,7 +754,7 @@ __device__ inline float lane_tv_mass(const float2* vp, int n)
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            if (g0 + lane + WAVE * i < n) s += v[i];
+            if (g0 + lane + WAVE * i < n) s += (double)v[i];
     }
     return s;
 }
@@ -768,15 +769,15 @@ __device__ inline int resid_pick_cached(const float2* vp, int n, float u, float&
 {
     const int lane = threadIdx.x & (WAVE - 1);
     float w[NR];
-    float tl = 0.0f;
+    double tl = 0.0;  // the order and precision of lane_tv_mass
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int g = lane + WAVE * i;
         const float2 v = g < n ? vp[g] : make_float2(0.0f, 0.0f);
         w[i] = v.y;
-        tl += v.x;
+        if (g < n) tl += (double)v.x;
     }
-    tv = wave_sum(tl);
+    tv = (float)wave_sum(tl);
     return wave_rounds_pick(w, u, Z, before, fallback);
 }
 
@@ -788,13 +789,17 @@ __device__ inline int resid_pick(const float2* vp, int n, float u, float& Z, flo
     const int lane = threadIdx.x & (WAVE - 1);
     const int per = (n + WAVE - 1) / WAVE;
     const int g0 = min(lane * per, n), g1 = min(g0 + per, n);
-    tv = wave_sum(lane_tv_mass(vp, n));
+    tv = (float)wave_sum(lane_tv_mass(vp, n));
     auto wf = [&](int g) { return vp[g].y; };
-    float excl;
-    wave_granule_scan(wf, g0, g1, excl, Z);
+    double excl, Zd, bd = 0.0;
+    wave_granule_scan(wf, g0, g1, excl, Zd);
+    Z = (float)Zd;
     before = 0.0f;
     fallback = true;
-    return Z > 0.0f ? wave_granule_find(wf, g0, g1, excl, u * Z, before, fallback) : 0;
+    if (!(Zd > 0.0)) return 0;
+    const int gs = wave_granule_find(wf, g0, g1, excl, (double)u * Zd, bd, fallback);
+    before = (float)bd;
+    return gs;
 }
 
 template <int NR>
@@ -834,9 +839,11 @@ __device__ inline int draw_target_row(const ResolveArgs& a, int trow, int req, i
         const int per = (n + WAVE - 1) / WAVE;
         const int g0 = min(lane * per, n), g1 = min(g0 + per, n);
         auto wf = [&](int g) { const float2 v = gs[g]; return v.y * softw(v.x, M, c); };
-        float excl;
-        wave_granule_scan(wf, g0, g1, excl, S);
-        gstar = wave_granule_find(wf, g0, g1, excl, u * S, before, fallback);
+        double excl, Sd, bd;
+        wave_granule_scan(wf, g0, g1, excl, Sd);
+        gstar = wave_granule_find(wf, g0, g1, excl, (double)u * Sd, bd, fallback);
+        S = (float)Sd;
+        before = (float)bd;
     }
     const float target = u * S;
     const float* L = p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V;
@@ -1232,7 +1239,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_conf_finalize(const float2* vp
         return;
     }
     for (int k = w; k < gamma; k += TILE_THREADS / WAVE) {
-        const float tv = wave_sum(lane_tv_mass(vpart + ((size_t)r * gamma + k) * n_gran, n_gran));
+        const float tv = (float)wave_sum(lane_tv_mass(vpart + ((size_t)r * gamma + k) * n_gran, n_gran));
         if (lane == 0) s_cs[k] = fminf(fmaxf(1.0f - 0.5f * tv, 0.0f), 1.0f);
     }
     __syncthreads();
@@ -1277,7 +1284,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_loss_terms(const float2* vpart
         }
         return;
     }
-    const float l1 = wave_sum(lane_tv_mass(vpart + (size_t)f * n_gran, n_gran));
+    const float l1 = (float)wave_sum(lane_tv_mass(vpart + (size_t)f * n_gran, n_gran));
     if (lane == 0) {
         const float cs = fminf(fmaxf(1.0f - 0.5f * l1, 0.0f), 1.0f);
         const int yk = y[f];

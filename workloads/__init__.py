@@ -174,17 +174,11 @@ def _request_rows(cfg: Config, req: int, sigma: float):
     return u, u + noise
 
 
-def make(cfg: Config | str, requests=None, threads: int | None = None) -> dict:
-    """Build the inputs of a workload.
-
-    requests: None for all R requests, else an iterable of request indices;
-    the returned per-request arrays then hold only those rows, in that order,
-    and 'req_ids' names them (the Philox request index of each row).
-    """
-    if isinstance(cfg, str):
-        cfg = CONFIGS[cfg]
-    req = np.arange(cfg.R, dtype=np.int32) if requests is None else \
-        np.asarray(list(requests), dtype=np.int32)
+def request_rows(cfg: Config, requests, threads: int | None = None):
+    """(U [n, gamma, V], Lt [n, gamma+1, V]) float32 of the listed requests,
+    in that order: the per-request part of make(), so that large inputs can
+    be built a slice of requests at a time."""
+    req = np.asarray(list(requests), dtype=np.int32)
     n = req.size
     U = np.empty((n, cfg.gamma, cfg.V), np.float32)
     Lt = np.empty((n, cfg.gamma + 1, cfg.V), np.float32)
@@ -197,6 +191,21 @@ def make(cfg: Config | str, requests=None, threads: int | None = None) -> dict:
 
     with ThreadPoolExecutor(threads or _threads()) as ex:
         list(ex.map(fill, range(n)))
+    return U, Lt
+
+
+def make(cfg: Config | str, requests=None, threads: int | None = None) -> dict:
+    """Build the inputs of a workload.
+
+    requests: None for all R requests, else an iterable of request indices;
+    the returned per-request arrays then hold only those rows, in that order,
+    and 'req_ids' names them (the Philox request index of each row).
+    """
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    req = np.arange(cfg.R, dtype=np.int32) if requests is None else \
+        np.asarray(list(requests), dtype=np.int32)
+    U, Lt = request_rows(cfg, req, threads)
     W1, W2 = weights(cfg)
     out = dict(cfg=cfg, req_ids=req, U=U, Lt=Lt, W1=W1, W2=W2,
                x0=anchors(cfg)[req], T=np.float32(cfg.T))
