@@ -395,17 +395,17 @@ __device__ inline int wmax_i(int v) { return wave_max_int(v); }
 
 // Running sum of one value per thread over the workgroup, waves in order:
 // [lo, hi) is this thread's share.  Consecutive shares meet exactly (the next
-// share's lo is computed by the same additions as this one's hi).  fp64: a
-// row expands up to 65536 tokens, 256 per thread.
-__device__ inline void block_share_d(double v, double* s_tmp, double& lo, double& hi, double& total)
+// share's lo is computed by the same additions as this one's hi).
+template <typename ACC>
+__device__ inline void block_share(ACC v, ACC* s_tmp, ACC& lo, ACC& hi, ACC& total)
 {
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-    const double x = wave_incl_scan(v);
-    double xe = __shfl_up(x, 1, WAVE);
-    if (lane == 0) xe = 0.0;
+    const ACC x = wave_incl_scan(v);
+    ACC xe = __shfl_up(x, 1, WAVE);
+    if (lane == 0) xe = 0;
     if (lane == WAVE - 1) s_tmp[w] = x;
     __syncthreads();
-    double base = 0.0, tot = 0.0;
+    ACC base = 0, tot = 0;
     for (int i = 0; i < CL_THREADS / WAVE; ++i) {
         if (i == w) base = tot;
         tot += s_tmp[i];
@@ -438,12 +438,15 @@ struct ClusterSampleArgs {
 // Loads go in batches of SB (one memory latency per batch).
 constexpr int SB = 16;
 
-template <bool GREEDY>
+// ACC: the precision of the running sums, float when a thread's share is at
+// most 32 elements, double for longer shares (up to 256 of them), whose
+// fp32 running sums would drift by more than 1e-6 of the row's mass.
+template <bool GREEDY, typename ACC>
 __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs a)
 {
     __shared__ int s_c0[CL_MAX_K], s_m[CL_MAX_K];
     __shared__ float s_ftmp[CL_THREADS / WAVE];
-    __shared__ double s_dtmp[CL_THREADS / WAVE];
+    __shared__ ACC s_atmp[CL_THREADS / WAVE];
     __shared__ int s_itmp[CL_THREADS / WAVE];
     __shared__ int s_pick;
     const int f = blockIdx.x, t = threadIdx.x;
@@ -493,17 +496,17 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
         if (t == 0) blank();
         return;
     }
-    double tsum = 0.0;
+    ACC tsum = 0;
     for (int e = e0; e < e1; e += SB) {
         float zz[SB];
 #pragma unroll
         for (int u = 0; u < SB; ++u) zz[u] = z[min(e + u, e1 - 1)];
 #pragma unroll
         for (int u = 0; u < SB; ++u)
-            if (e + u < e1) tsum += (double)softw(zz[u], M, a.c);
+            if (e + u < e1) tsum += (ACC)softw(zz[u], M, a.c);
     }
-    double Zd, lo, incl;
-    block_share_d(tsum, s_dtmp, lo, incl, Zd);
+    ACC Zd, lo, incl;
+    block_share(tsum, s_atmp, lo, incl, Zd);
     const float Z = (float)Zd;
     int pick = -1;
     if (GREEDY) {
@@ -521,18 +524,18 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
             }
         }
     } else {
-        const double target = (double)u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[0]) * Zd;
+        const ACC target = (ACC)u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[0]) * Zd;
         int last = -1, lpos = -1;
-        double run = lo;
+        ACC run = lo;
         // this thread's share [lo, incl) holds the target: walk it
-        const bool mine = tsum > 0.0 && lo <= target && target < incl;
+        const bool mine = tsum > 0 && lo <= target && target < incl;
         for (int e = e0; e < e1; ++e) {
             const float wv = softw(z[e], M, a.c);
             if (wv > 0.0f) {
-                if (mine && pick < 0 && run + (double)wv > target) pick = e;
+                if (mine && pick < 0 && run + (ACC)wv > target) pick = e;
                 lpos = e;
             }
-            run += (double)wv;
+            run += (ACC)wv;
         }
         last = lpos;
         if (mine && pick < 0) pick = last;  // the share's own sum rounded below the target
@@ -603,8 +606,14 @@ hipError_t launch_cluster_propose(const ClusterArgs& a, hipStream_t s)
     sa.x = a.x; sa.pd_x = a.pd_x; sa.pd_stats = a.pd_stats; sa.status = a.status;
     {
         ProfScope ps("cluster_sample", s);
-        if (a.greedy) hipLaunchKernelGGL(k_cluster_sample<true>, dim3(N), dim3(CL_THREADS), 0, s, sa);
-        else hipLaunchKernelGGL(k_cluster_sample<false>, dim3(N), dim3(CL_THREADS), 0, s, sa);
+        const bool wide = (long)a.K_c * a.max_cl > 32L * CL_THREADS;  // more than 32 elements per thread
+        if (a.greedy) {
+            if (wide) hipLaunchKernelGGL((k_cluster_sample<true, double>), dim3(N), dim3(CL_THREADS), 0, s, sa);
+            else hipLaunchKernelGGL((k_cluster_sample<true, float>), dim3(N), dim3(CL_THREADS), 0, s, sa);
+        } else {
+            if (wide) hipLaunchKernelGGL((k_cluster_sample<false, double>), dim3(N), dim3(CL_THREADS), 0, s, sa);
+            else hipLaunchKernelGGL((k_cluster_sample<false, float>), dim3(N), dim3(CL_THREADS), 0, s, sa);
+        }
     }
     return hipGetLastError();
 }

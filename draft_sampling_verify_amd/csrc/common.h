@@ -280,11 +280,14 @@ __device__ inline int block_min(int v, int* sm)
 // granule's 128 weights.  Threads of a 256-wide block own contiguous
 // granule ranges [g0, g1).
 //
-// Sums across granules run in fp64: a lane may own thousands of granules
-// (131072 of them at V = 2^24), and an fp32 running sum of that length
-// drifts by up to its length in units of the last place, enough to move a
-// draw whose u lies within 1e-5 of a token boundary.  In fp64 the error
-// left is that of the fp32 granule masses themselves (about 1e-7 relative).
+// Where a lane owns a contiguous run of granules (rows of more than 2048
+// granules: up to 131072 at V = 2^24) the sums across granules run in fp64:
+// an fp32 running sum of that length drifts by up to its length in units of
+// the last place, enough to move a draw whose u lies within 1e-6 of a
+// token boundary.  In fp64 the error left is that of the fp32 granule
+// masses themselves (about 1e-7 relative).  The register-cached pick below
+// (at most 2048 granules: a 64-lane tree, then at most 32 rounds in
+// sequence) stays in fp32.
 
 // One wave; lane l owns the contiguous granule range [g0, g1).  Returns the
 // lane's exclusive prefix of the granule masses and the wave total.
@@ -347,15 +350,15 @@ __device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& tot
 {
     const int lane = threadIdx.x & (WAVE - 1);
     float T[NR];
-    double Z = 0.0;
+    float Z = 0.0f;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         T[i] = wave_sum(w[i]);
-        Z += (double)T[i];
+        Z += T[i];
     }
-    total = (float)Z;
-    const double target = (double)u * Z;
-    double pre = 0.0, rbase = 0.0;
+    total = Z;
+    const float target = u * Z;
+    float pre = 0.0f, rbase = 0.0f;
     int rstar = -1;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -375,12 +378,12 @@ __device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& tot
     const float incl = wave_incl_scan(wr);
     float ex = __shfl_up(incl, 1, WAVE);
     if (lane == 0) ex = 0.0f;
-    const double run0 = rbase + (double)ex;
-    const unsigned long long hit = __ballot(rstar >= 0 && wr > 0.0f && run0 + (double)wr > target);
+    const float run0 = rbase + ex;
+    const unsigned long long hit = __ballot(rstar >= 0 && wr > 0.0f && run0 + wr > target);
     if (hit) {
         const int L = __ffsll((long long)hit) - 1;
         fallback = false;
-        before = (float)__shfl(run0, L, WAVE);
+        before = __shfl(run0, L, WAVE);
         return L + WAVE * rstar;
     }
     fallback = true;

@@ -735,16 +735,19 @@ struct ResolveArgs {
 };
 
 // Lane-strided TV mass of one row's granule records: lane l adds granules
-// l, l + 64, l + 128, ... in that order, in fp64 (thousands of terms per
-// lane at the largest vocabularies), with the loads of a batch of 16
+// l, l + 64, l + 128, ... in that order, with the loads of a batch of 16
 // issued before any of them is added, so a row costs about one memory
-// latency rather than one per granule.  Every kernel that reports c* sums in
-// this order, so verify, confidence and the loss give the same bits.
-__device__ inline double lane_tv_mass(const float2* vp, int n)
+// latency rather than one per granule; then the 64-lane tree.  Rows of at
+// most 2048 granules sum in fp32 (at most 32 terms per lane), longer rows
+// in fp64 (up to 2048 terms per lane at V = 2^24).  Every kernel that
+// reports c* sums in this order and precision, so verify, confidence and
+// the loss give the same bits.
+template <typename ACC>
+__device__ inline ACC lane_tv_mass_t(const float2* vp, int n)
 {
     constexpr int NB = 16;
     const int lane = threadIdx.x & (WAVE - 1);
-    double s = 0.0;
+    ACC s = 0;
     for (int g0 = 0; g0 < n; g0 += NB * WAVE) {
         float v[NB];
 #pragma unroll
@@ -754,9 +757,14 @@ __device__ inline double lane_tv_mass(const float2* vp, int n)
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            if (g0 + lane + WAVE * i < n) s += (double)v[i];
+            if (g0 + lane + WAVE * i < n) s += (ACC)v[i];
     }
     return s;
+}
+__device__ inline float row_tv_mass(const float2* vp, int n)
+{
+    if (n <= 32 * WAVE) return wave_sum(lane_tv_mass_t<float>(vp, n));
+    return (float)wave_sum(lane_tv_mass_t<double>(vp, n));
 }
 
 // One wave, over the granule records of one verified row: the total TV mass
@@ -769,15 +777,15 @@ __device__ inline int resid_pick_cached(const float2* vp, int n, float u, float&
 {
     const int lane = threadIdx.x & (WAVE - 1);
     float w[NR];
-    double tl = 0.0;  // the order and precision of lane_tv_mass
+    float tl = 0.0f;  // the order and precision of row_tv_mass for n <= 2048
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int g = lane + WAVE * i;
         const float2 v = g < n ? vp[g] : make_float2(0.0f, 0.0f);
         w[i] = v.y;
-        if (g < n) tl += (double)v.x;
+        tl += v.x;
     }
-    tv = (float)wave_sum(tl);
+    tv = wave_sum(tl);
     return wave_rounds_pick(w, u, Z, before, fallback);
 }
 
@@ -789,7 +797,7 @@ __device__ inline int resid_pick(const float2* vp, int n, float u, float& Z, flo
     const int lane = threadIdx.x & (WAVE - 1);
     const int per = (n + WAVE - 1) / WAVE;
     const int g0 = min(lane * per, n), g1 = min(g0 + per, n);
-    tv = (float)wave_sum(lane_tv_mass(vp, n));
+    tv = row_tv_mass(vp, n);
     auto wf = [&](int g) { return vp[g].y; };
     double excl, Zd, bd = 0.0;
     wave_granule_scan(wf, g0, g1, excl, Zd);
@@ -1239,7 +1247,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_conf_finalize(const float2* vp
         return;
     }
     for (int k = w; k < gamma; k += TILE_THREADS / WAVE) {
-        const float tv = (float)wave_sum(lane_tv_mass(vpart + ((size_t)r * gamma + k) * n_gran, n_gran));
+        const float tv = row_tv_mass(vpart + ((size_t)r * gamma + k) * n_gran, n_gran);
         if (lane == 0) s_cs[k] = fminf(fmaxf(1.0f - 0.5f * tv, 0.0f), 1.0f);
     }
     __syncthreads();
@@ -1284,7 +1292,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_loss_terms(const float2* vpart
         }
         return;
     }
-    const float l1 = (float)wave_sum(lane_tv_mass(vpart + (size_t)f * n_gran, n_gran));
+    const float l1 = row_tv_mass(vpart + (size_t)f * n_gran, n_gran);
     if (lane == 0) {
         const float cs = fminf(fmaxf(1.0f - 0.5f * l1, 0.0f), 1.0f);
         const int yk = y[f];

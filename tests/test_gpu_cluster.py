@@ -28,7 +28,7 @@ import draft_sampling_verify_amd as spec
 pytestmark = pytest.mark.gpu
 
 CUT_TOL = 1e-4
-SMALL = ["cl_tiny", "cl_ragged", "cl_mid", "cl_rows"]
+SMALL = ["cl_tiny", "cl_ragged", "cl_mid", "cl_rows", "cl_wide", "cl_max"]
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -259,6 +259,10 @@ CLUSTER_CONFIGS = {
     "cl_mid": ClusterConfig("cl_mid", 63, 4, 4, 256, 20000, 160, 8, 1.0, equal=False, mu_std=0.15,
                             eps_std=0.08),
     "cl_rows": ClusterConfig("cl_rows", 64, 40, 2, 64, 4096, 64, 8, 1.0, mu_std=0.3, eps_std=0.15),
+    # long expansions: 16 clusters of 1000 tokens (16000 per row), and the
+    # largest the interface takes, 16 x 4096 = 65536 tokens per row
+    "cl_wide": ClusterConfig("cl_wide", 65, 3, 2, 32, 40000, 40, 16, 1.0, mu_std=0.3, eps_std=0.15),
+    "cl_max": ClusterConfig("cl_max", 66, 3, 2, 32, 262144, 64, 16, 1.0, mu_std=0.3, eps_std=0.15),
 }
 
 
