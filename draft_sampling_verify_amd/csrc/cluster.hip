@@ -568,6 +568,7 @@ __global__ __launch_bounds__(CL_THREADS) void k_cluster_sample(ClusterSampleArgs
 static int coarse_splits(int N, int N_c, int d)
 {
     const int nb = ((N + 31) / 32) * ((N_c + 127) / 128);
+    if (nb < 1) return 1;  // no rows
     int q = (256 + nb - 1) / nb;
     return std::max(1, std::min(std::min(q, 4), d / 64));
 }

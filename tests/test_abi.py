@@ -72,6 +72,26 @@ def test_workspace_bytes(L):
 FAKE = ctypes.c_void_p(4096)  # aligned, never dereferenced: validation fails first
 
 
+def test_empty_batch_returns_before_any_device_call(L):
+    """R = 0 is valid for every entry point but the scheduler: the size
+    queries stay finite and the calls return SPEC_OK from host code alone
+    (null data pointers; nothing is enqueued)."""
+    import draft_sampling_verify_amd as d
+    for op in (d.SPEC_OP_PROPOSE, d.SPEC_OP_VERIFY, d.SPEC_OP_CONFIDENCE, d.SPEC_OP_ROUNDS):
+        assert d.spec_workspace_bytes(op, 0, 4, 16, 1024) > 0
+    assert d.spec_workspace_bytes(d.SPEC_OP_SCHEDULE, 0, 4, 0, 0, 8) == 0
+    assert d.spec_cluster_workspace_bytes(0, 2, 16, 6, 2, 20, 60) > 0
+    big = 1 << 30
+    assert L.spec_markov_propose(None, FAKE, FAKE, 1, None, 0, 4, 16, 1024, 1.0, 0, 1, 0, None, None, None,
+                                 FAKE, big, None) == d.SPEC_OK
+    assert L.spec_verify(None, FAKE, FAKE, 1, None, None, None, None, None, 0, 4, 16, 1024, 1.0, 0, 1, 0,
+                         None, None, None, None, FAKE, big, None) == d.SPEC_OK
+    assert L.spec_cluster_propose(None, None, None, 1, None, None, 0, 2, 16, 6, 2, 20, 60, 1.0, 0, 1, 0,
+                                  None, None, None, None, None, FAKE, big, None) == d.SPEC_OK
+    assert L.spec_cluster_verify(None, None, None, None, None, None, None, 0, 2, 6, 2, 20, 60, 1.0, 0, 1, 0,
+                                 None, None, None, None, FAKE, big, None) == d.SPEC_OK
+
+
 def _propose(L, **kw):
     a = dict(U=FAKE, W1=FAKE, W2=FAKE, dt=1, x0=FAKE, R=4, g=4, r=16, V=1024, T=1.0, greedy=0,
              seed=1, rnd=0, x=FAKE, pdx=FAKE, pds=FAKE, ws=FAKE, wsb=1 << 30, s=None)

@@ -142,6 +142,23 @@ def test_cluster_propose_and_verify_match_oracle(name, greedy):
     log("  verify", sv)
 
 
+def test_cluster_empty_batch_is_a_no_op():
+    d = _inputs("cl_tiny")
+    cfg = d["cfg"]
+    t = _dev(d)
+    ws = spec.ClusterWorkspace(1, cfg.gamma, cfg.d, cfg.N_c, cfg.K_c, d["max_cl"], cfg.V)
+    tok_slot = spec.spec_cluster_index(t["cl_off"], t["cl_tok"], ws=ws)
+    H = t["H"][:0]
+    x, pd_x, sel, zf, pds = spec.spec_cluster_propose(H, t["C"], t["E"], t["cl_off"], t["cl_tok"], cfg.K_c,
+                                                      d["max_cl"], cfg.T, ws=ws)
+    assert x.shape == (0, cfg.gamma) and sel.shape == (0, cfg.gamma, cfg.K_c)
+    n_acc, y, pt_x, c_star = spec.spec_cluster_verify(tok_slot, sel, zf, pds, x, t["Lt"][:0], cfg.T, cfg.N_c,
+                                                      ws=ws)
+    assert n_acc.shape == (0,) and y.shape == (0, cfg.gamma + 1) and c_star.shape == (0, cfg.gamma)
+    torch.cuda.synchronize()
+    assert spec.spec_device_status(ws) == 0
+
+
 def test_cluster_index_is_the_inverse_of_the_clustering():
     d = workloads.make_cluster("cl_ragged")
     t = _dev(d)

@@ -202,12 +202,27 @@ def test_verify_sweep_paths_identical(name):
 
 
 def test_empty_batch_is_a_no_op():
-    e = torch.empty((0, 4, 1024), device="cuda")
-    W = torch.zeros((1024, 16), device="cuda")
+    """R = 0: every entry point returns success at once with empty outputs;
+    the scheduler, whose batch must hold at least one request, rejects it."""
+    g, V, r = 4, 1024, 16
+    e = torch.empty((0, g, V), device="cuda")
+    lt = torch.empty((0, g + 1, V), device="cuda")
+    W = torch.zeros((V, r), device="cuda")
     x0 = torch.empty(0, dtype=torch.int32, device="cuda")
     Wp = spec.spec_pack_w2(W)
-    x, pdx, pds = spec.spec_markov_propose(e, W, Wp, x0, 1.0, ws=spec.Workspace(1, 4, 16, 1024))
-    assert x.shape == (0, 4)
+    ws = spec.Workspace(1, g, r, V, B_max=8)
+    x, pdx, pds = spec.spec_markov_propose(e, W, Wp, x0, 1.0, ws=ws)
+    assert x.shape == (0, g) and pdx.shape == (0, g) and pds.shape == (0, g, 2)
+    n_acc, y, pt_x, c_star = spec.spec_verify(e, W, Wp, x0, x, pds, lt, 1.0, ws=ws)
+    assert n_acc.shape == (0,) and y.shape == (0, g + 1) and pt_x.shape == (0, g) and c_star.shape == (0, g)
+    cs, a_star = spec.spec_confidence(e, W, Wp, x0, x, lt, 1.0, pd_stats=pds, ws=ws)
+    assert cs.shape == (0, g) and a_star.shape == (0, g)
+    anchors, xr, nr, yr, cr = spec.spec_decode_rounds(e, W, Wp, x0, lt, 1.0, 3, want_c_star=True, ws=ws)
+    assert anchors.shape == (4, 0) and xr.shape == (3, 0, g) and yr.shape == (3, 0, g + 1) and cr.shape == (3, 0, g)
+    torch.cuda.synchronize()
+    assert spec.spec_device_status(ws) == 0
+    with pytest.raises(spec.SpecError):
+        spec.spec_schedule(torch.empty((0, g), device="cuda"), torch.ones(8, device="cuda"), ws=ws)
 
 
 def _chi2_case(V=16, r=16, rounds=16, R=65536, seed=21):
