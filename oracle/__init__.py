@@ -74,7 +74,8 @@ def lib():
         L.ref_argmax.restype = i32
         L.ref_markov_propose.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, f32, ctypes.c_int, u64, u64,
-                                         P, P, P, P, P, P]
+                                         P, P, P, P, P, P, P]
+        L.ref_block_uniforms.argtypes = [u64, u64, i32, i32, i32, P, P]
         L.ref_verify.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, f32, ctypes.c_int, u64, u64, P,
                                  P, P, P, P, P, P, P, P, P]
@@ -127,6 +128,17 @@ def u24(w):
     return lib().ref_u24(int(w))
 
 
+def block_uniforms(seed, rnd, req, k, n_blocks):
+    """(e [n_blocks], u [n_blocks]): the race and in-block uniforms of the
+    draft draw's blocks at (seed, round, request, position k)."""
+    e, u = np.zeros(n_blocks), np.zeros(n_blocks)
+    a, b = ctypes.c_double(), ctypes.c_double()
+    for i in range(n_blocks):
+        lib().ref_block_uniforms(seed, rnd, req, k, i, ctypes.byref(a), ctypes.byref(b))
+        e[i], u[i] = a.value, b.value
+    return e, u
+
+
 def bias(W1, W2, xprev):
     W1, W2, dt = _weights(W1, W2)
     V, r = W2.shape
@@ -154,7 +166,10 @@ class OracleError(RuntimeError):
 
 
 def markov_propose(U, W1, W2, x0, T, greedy, seed, rnd, req_ids=None, x_cond=None):
-    """Returns dict with x [R,g], pd_x [R,g], pd_stats [R,g,2], margin [R,g]."""
+    """Returns dict with x [R,g], pd_x [R,g], pd_stats [R,g,2], margin [R,g]
+    (sampled: the block race's key gap, natural log units; greedy: the
+    top-2 logit gap) and margin_within [R,g] (sampled: the inverse-CDF
+    margin inside the winning block)."""
     U = _c(U, np.float32)
     R, g, V = U.shape
     W1, W2, dt = _weights(W1, W2)
@@ -163,11 +178,11 @@ def markov_propose(U, W1, W2, x0, T, greedy, seed, rnd, req_ids=None, x_cond=Non
     req_ids = _c(req_ids, np.int32)
     x_cond = _c(x_cond, np.int32)
     out = dict(x=np.zeros((R, g), np.int32), pd_x=np.zeros((R, g)),
-               pd_stats=np.zeros((R, g, 2)), margin=np.zeros((R, g)))
+               pd_stats=np.zeros((R, g, 2)), margin=np.zeros((R, g)), margin_within=np.zeros((R, g)))
     st = lib().ref_markov_propose(_p(U), _p(W1), _p(W2), dt, _p(x0), R, g, r, V, float(T),
                                   int(bool(greedy)), seed, rnd, _p(req_ids), _p(x_cond),
                                   _p(out["x"]), _p(out["pd_x"]), _p(out["pd_stats"]),
-                                  _p(out["margin"]))
+                                  _p(out["margin"]), _p(out["margin_within"]))
     if st != 0:
         raise OracleError("ref_markov_propose rejected its arguments")
     return out
