@@ -158,7 +158,7 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
         if (check_draft(nullptr, nullptr, nullptr, SPEC_BF16, nullptr, 0, gamma, r, V, 1.0f) != SPEC_OK || R < 0 ||
             R > MAX_R)
             return 0;
-        spec::carve_propose(nullptr, R, V, &bytes);
+        spec::carve_propose(nullptr, R, gamma, V, &bytes);
         return bytes;
     case SPEC_OP_VERIFY:
     case SPEC_OP_CONFIDENCE:
@@ -303,10 +303,10 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dt
     if (st != SPEC_OK) return st;
     if (R > 0 && (!x || !pd_x || !pd_stats)) return SPEC_EINVAL;
     size_t need = 0;
-    spec::carve_propose(nullptr, R, V, &need);
+    spec::carve_propose(nullptr, R, gamma, V, &need);
     if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
     if (R == 0) return SPEC_OK;
-    const spec::ProposeWs w = spec::carve_propose(ws, R, V, nullptr);
+    const spec::ProposeWs w = spec::carve_propose(ws, R, gamma, V, nullptr);
     DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, greedy, seed, round, ws);
     return launch_status(spec::launch_propose(a, x, pd_x, pd_stats, w, (hipStream_t)stream));
 }

@@ -49,13 +49,16 @@
  *   Asynchrony  Calls only validate on the host and enqueue kernels on
  *               `stream` (a hipStream_t; NULL = the null stream).  Outputs are
  *               valid once the caller synchronises that stream.
- *   Randomness  Every uniform is Philox4x32-10 with key = seed and counter =
- *               (k, request, round_lo, round_hi); word 0 draws x_k, word 1 is
- *               the accept test at k, word 2 the residual draw at k or the
- *               bonus draw at k = l_r + 1; u = (w >> 8) * 2^-24.  Sampling is
- *               by inverse CDF in vocabulary order (smallest v whose running
- *               sum exceeds u * total), so results are a pure function of
- *               (inputs, seed, round).
+ *   Randomness  Every uniform is Philox4x32-10 with key = seed.  Counter
+ *               (k, request, round_lo, round_hi): word 1 is the accept test at
+ *               k, word 2 the residual draw at k or the bonus draw at
+ *               k = l_r + 1, word 0 the clustered head's draw;
+ *               u = (w >> 8) * 2^-24.  The Markov head's draft draw takes its
+ *               uniforms per 128-id block from the counters described at
+ *               spec_markov_propose.  Residual and bonus draws are by inverse
+ *               CDF in vocabulary order (smallest v whose running sum exceeds
+ *               u * total), so results are a pure function of (inputs, seed,
+ *               round).
  *   Greedy      greedy != 0 replaces every draw by the lowest-index argmax of
  *               the same logits (draft: U+B; accept iff x_k equals the target
  *               argmax).  Probabilities and c* are still reported at T.
@@ -147,7 +150,15 @@ int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags);
 /* Draft gamma tokens per request with the Markov head (DSpark sections 3-4):
  *   x_0 = x0[r];  for k = 1..gamma:
  *     z_k = U[r,k-1,:] + W1[x_{k-1}] W2^T        (raw draft logits)
- *     p_k = softmax(z_k / T);  x_k ~ p_k (word 0), or argmax z_k if greedy
+ *     p_k = softmax(z_k / T);  x_k ~ p_k, or argmax z_k if greedy
+ * The sample is drawn exactly in two levels over blocks of 128 ids
+ * (128 b .. 128 b + 127): inside every block a candidate by inverse CDF over
+ * the block's own probabilities with uniform u_b, then the block that wins
+ * the Gumbel-max race on the block masses P_b, argmax_b ln P_b - ln(-ln e_b)
+ * (ties: smaller b), gives x_k.  u_b and e_b are word b & 3 of Philox4x32-10
+ * (key = seed) at counter (0xC0000000 | k << 20 | b >> 2, r, round) and
+ * (0x80000000 | k << 20 | b >> 2, r, round): u_b = (w >> 8) 2^-24,
+ * e_b = ((w >> 9) + 1/2) 2^-23.
  * In:  U [R,gamma,V] fp32; W1 [V,r] (w_dtype); W2p = spec_pack_w2(W2);
  *      x0 [R] int32.
  * Out: x [R,gamma] int32; pd_x [R,gamma] fp32 = p_k(x_k);
