@@ -68,14 +68,14 @@ def algorithmic_bytes(kernel: str, cfg, K: int) -> float:
         return R * g * (8.0 * ng + 20.0)
     if kernel == "clear_flags":
         return 4.0 * (ng + R + 1)
-    if kernel == "draft_tile":      # one position: U_k rows, W2, W1 rows; (max, sum, candidate, key, weight) out
-        return 4.0 * R * V + wb * r * V + wb * R * r + 20.0 * R * ng
+    if kernel == "draft_tile":      # one position: U_k rows, W2, W1 rows; (max, sum) partials out
+        return 4.0 * R * V + wb * r * V + wb * R * r + 8.0 * R * ng
     if kernel == "target_rows":     # every target row once; (max, sum, argmax) partials out
         return (R + K) * (4.0 * V + 12.0 * ng)
     if kernel == "verify_sweep":    # U and target rows of every verified row, W2, W1 rows; partials out
         return K * (8.0 * V + wb * r + 8.0 * ng) + wb * r * V
-    if kernel == "propose_pick":    # partials of every request (max, sum, key; the winner's candidate and weight)
-        return R * (12.0 * ng + 24.0)
+    if kernel == "propose_pick":    # partials of every request + one granule rescan
+        return R * (8.0 * ng + 128 * (4.0 + wb * r) + 16.0)
     if kernel == "verify_resolve":
         return R * (8.0 * ng * (g + 2) + 128 * (8.0 + wb * r))
     return float("nan")

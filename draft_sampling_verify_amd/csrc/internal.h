@@ -97,8 +97,6 @@ constexpr int FUSED_PART_WORDS = 10;  // per (request, granule), for odd and eve
 struct ProposeWs {
     float2* gstat;    // [R, n_gran] per-position kernels
     int32_t* gidx;    // [R, n_gran]
-    float* gkey;      // [R, n_gran] race keys of the sampled draw
-    float* gw;        // [R, n_gran] candidate weights of the sampled draw
     uint64_t* part;   // [FUSED_PART_WORDS][R][n_gran] fused: tagged partials (R <= FUSED_MAX_R), else null
     uint64_t* words;  // [FUSED_TOKEN_COPIES, 32] fused: tagged token words
     float2* gstat_all;  // [R, gamma, n_gran] fused, sampled: (max, sum) of every position
@@ -112,8 +110,6 @@ inline ProposeWs carve_propose(void* ws, int R, int gamma, int V, size_t* bytes)
     ProposeWs w{};
     w.gstat = c.take<float2>((size_t)R * ng);
     w.gidx = c.take<int32_t>((size_t)R * ng);
-    w.gkey = c.take<float>((size_t)R * ng);
-    w.gw = c.take<float>((size_t)R * ng);
     if (R <= FUSED_MAX_R) {
         w.part = c.take<uint64_t>((size_t)R * ng * FUSED_PART_WORDS);
         w.words = c.take<uint64_t>((size_t)FUSED_TOKEN_COPIES * 32);

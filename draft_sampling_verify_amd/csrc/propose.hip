@@ -89,10 +89,7 @@ struct TileArgs {
     int n_chunks;  // chunks of row blocks
     int bpc;       // row blocks per chunk
     float2* gstat; // [nrows, n_gran]
-    int32_t* gidx; // [nrows, n_gran] argmax (greedy) or candidate of the inside draw (sampled)
-    float* gkey;   // [nrows, n_gran] race keys (sampled)
-    float* gw;     // [nrows, n_gran] candidate weights (sampled)
-    uint64_t seed, round;
+    int32_t* gidx; // [nrows, n_gran] argmax (greedy)
     uint32_t* status;
 };
 
@@ -109,10 +106,8 @@ __device__ inline void draft_row(const TileArgs& p, int row, int& req, int& kk, 
     tok = kk == 0 ? p.x0[req] : p.x[(size_t)req * p.gamma + kk - 1];
 }
 
-// Per (row, granule): max and sum of weights; greedy adds the argmax;
-// DRAW (the sampled propose, rows = requests at position kfix + 1) adds the
-// inside draw's candidate, its weight and the granule's race key.
-template <typename WT, int KS, bool GREEDY, bool DRAW = false>
+// Per (row, granule): max and sum of weights; greedy adds the argmax.
+template <typename WT, int KS, bool GREEDY>
 __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 {
     using Ops = TileOps<WT, KS>;
@@ -146,13 +141,6 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) z[j] = -INFINITY;
-        }
-        float u_in = 0.0f, rterm = 0.0f;
-        if (DRAW) {  // this row's uniforms for granule g (rows are requests)
-            uint32_t wd = 0u;
-            if ((t & 7) < 2 && erow < p.nrows) wd = block_word((t & 7) == 0, p.kfix + 1, erow, g, p.round, p.seed);
-            rterm = race_term(__shfl(wd, lane & ~7, WAVE));
-            u_in = u24f(__shfl(wd, (lane & ~7) + 1, WAVE));
         }
         if (t < 32) {
             const int row = rb * BLOCK_ROWS + t;
@@ -192,29 +180,15 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
         }
         m = oct_max(m);
         const float ms = safe_ref(m);
-        float s = 0.0f, wx = 0.0f, key = -INFINITY;
-        int cand = -1;
-        if (DRAW) {
+        float s = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) z[j] = softw(z[j], ms, p.c);  // weights, in place
-            const int id = granule_inside_draw(z, u_in, wx, s);
-            cand = id >= 0 ? g * GRAN + id : -1;
-            key = race_key(m, s, p.c, rterm);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) s += softw(z[j], ms, p.c);
-            s = oct_sum(s);
-        }
+        for (int j = 0; j < 16; ++j) s += softw(z[j], ms, p.c);
+        s = oct_sum(s);
         if (GREEDY) oct_argmax(bv, bi);
         if ((t & 7) == 0 && valid) {
             const size_t o = (size_t)erow * p.n_gran + g;
             p.gstat[o] = make_float2(m, s);
             if (GREEDY) p.gidx[o] = bi;
-            if (DRAW) {
-                p.gidx[o] = cand;
-                p.gkey[o] = key;
-                p.gw[o] = wx;
-            }
         }
     }
 }
@@ -222,25 +196,29 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 // ------------------------------------------------------------ pick
 
 struct PickArgs {
+    const float* U;
+    const void* W1;
+    const void* W2p;
     const int32_t* x0;
     int32_t* x;  // [R, gamma]; position k is written, k-1 is read
-    int V, gamma;
+    int gamma, r, V;
     float c;
     int k;       // 1-based position
     int n_gran;
+    uint64_t seed, round;
     const float2* gstat;  // [R, n_gran] (max, sum)
-    const int32_t* gidx;  // [R, n_gran] argmax (greedy) or candidate (sampled)
-    const float* gkey;    // [R, n_gran] race keys (sampled)
-    const float* gw;      // [R, n_gran] candidate weights (sampled)
+    const int32_t* gidx;  // [R, n_gran] argmax (greedy)
     float* pd_x;
     float* pd_stats;
 };
 
-// One workgroup per request merges the granule partials of its row: M, S
-// (fp64 across granules), and the token, either the smallest argmax id at M
-// (greedy) or the race winner's candidate (sampled; ties: smaller granule).
-// Thread t owns the contiguous granules [g0, g1).
-template <bool GREEDY>
+// One workgroup per request merges the granule partials of its row: M and
+// S (fp64 across granules; thread t owns the contiguous granules [g0, g1)),
+// then the token: greedy, the smallest argmax id at M; sampled, the
+// two-level draw, with the race keys computed here (one Philox block per
+// four granules) and the inside draw over the winning granule only, whose
+// 128 logits wave w recomputes (column block w) on MFMA with U added.
+template <typename WT, int KS, bool GREEDY>
 __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
 {
     const int q = blockIdx.x;
@@ -249,13 +227,23 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
     __shared__ float s_f[NW], s_k[NW];
     __shared__ double s_d[NW];
     __shared__ int s_i[NW];
+    __shared__ float zrow[GRAN];
     const size_t o = (size_t)q * p.gamma + (p.k - 1);
     const size_t ro = (size_t)q * p.n_gran;
     const float2* gs = p.gstat + ro;
     const int per = (p.n_gran + TILE_THREADS - 1) / TILE_THREADS;
     const int g0 = min(t * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
     const int tok = p.k == 1 ? p.x0[q] : p.x[(size_t)q * p.gamma + p.k - 2];
-    if (!(tok >= 0 && tok < p.V)) {
+    const bool ok = tok >= 0 && tok < p.V;
+    // B operand of the rescan: only this request's W1 row (column n == q's
+    // slot); a matrix-core output element depends only on its own row and
+    // column operands
+    const int n = lane & 31, h = lane >> 5, nq = q & (BLOCK_ROWS - 1);
+    const int ks = k_steps<WT>(p.r);
+    TileOps<WT, KS> A;
+    typename TileOps<WT, KS>::BRow brow;
+    if (!GREEDY) brow.load(reinterpret_cast<const WT*>(p.W1), p.r, (ok && n == nq) ? tok : -1, ks, lane);
+    if (!ok) {
         if (t == 0) {
             p.x[o] = -1;
             p.pd_x[o] = NAN;
@@ -275,8 +263,6 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
     double ts = 0.0;
     for (int g = g0; g < g1; ++g) ts += (double)(gs[g].y * softw(gs[g].x, M, p.c));
     ts = wave_sum(ts);
-    // the token: greedy, the smallest argmax id at M; sampled, the best race
-    // key (value, granule), ties to the smaller granule
     float bk = -INFINITY;
     int bg = 0x7fffffff;
     if (GREEDY) {
@@ -284,11 +270,20 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
             if (gs[g].x == M) bg = min(bg, p.gidx[ro + g]);
         bg = wave_min(bg);
     } else {
-        for (int g = g0; g < g1; ++g) {
-            const float kv = p.gkey[ro + g];
-            if (kv > bk) {
-                bk = kv;
-                bg = g;
+        // race keys, ties to the smaller granule
+        for (int g = g0; g < g1;) {
+            const int quad = g >> 2;
+            const u32x4 P = philox(0x80000000u | ((uint32_t)p.k << 20) | (uint32_t)quad, (uint32_t)q, p.round,
+                                   p.seed);
+            for (; g < g1 && (g >> 2) == quad; ++g) {
+                const float2 v = gs[g];
+                const int i = g & 3;
+                const uint32_t wd = i == 0 ? P.w[0] : i == 1 ? P.w[1] : i == 2 ? P.w[2] : P.w[3];
+                const float kv = race_key(v.x, v.y, p.c, race_term(wd));
+                if (kv > bk) {
+                    bk = kv;
+                    bg = g;
+                }
             }
         }
 #pragma unroll
@@ -307,7 +302,6 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         s_k[w] = bk;
     }
     __syncthreads();
-    if (t != 0) return;
     double Sd = 0.0;
     float kb = s_k[0];
     int gb = s_i[0];
@@ -322,22 +316,52 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         }
     }
     const float S = (float)Sd;
-    int xk;
-    float pdx;
     if (GREEDY) {
-        xk = gb == 0x7fffffff ? -1 : gb;
-        pdx = 1.0f / S;
-    } else if (kb > -INFINITY) {
-        xk = p.gidx[ro + gb];
-        pdx = p.gw[ro + gb] * softw(gs[gb].x, M, p.c) / S;
-    } else {  // no granule holds weight
-        xk = -1;
-        pdx = NAN;
+        if (t == 0) {
+            p.x[o] = gb == 0x7fffffff ? -1 : gb;
+            p.pd_x[o] = 1.0f / S;
+            p.pd_stats[2 * o] = M;
+            p.pd_stats[2 * o + 1] = S;
+        }
+        return;
     }
-    p.x[o] = xk;
-    p.pd_x[o] = pdx;
-    p.pd_stats[2 * o] = M;
-    p.pd_stats[2 * o + 1] = S;
+    if (!(kb > -INFINITY)) {  // no granule holds weight
+        if (t == 0) {
+            p.x[o] = -1;
+            p.pd_x[o] = NAN;
+            p.pd_stats[2 * o] = M;
+            p.pd_stats[2 * o + 1] = S;
+        }
+        return;
+    }
+    // the winning granule's weights (relative to M), then the inside draw
+    const int gstar = gb;
+    {
+        const int nblk = (p.V + 31) / 32;
+        const int b = 4 * gstar + w;
+        float uv[16];
+        load_acc16(p.U + ((size_t)q * p.gamma + (p.k - 1)) * p.V, gstar * GRAN + 32 * w, h, p.V, (p.V % 4) == 0,
+                   uv);
+        A.load_a(p.W2p, ks, b, b < nblk, lane);
+        const f32x16 acc = A.mfma_row(brow, ks);
+        if (n == nq) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] = softw(uv[j] + acc[j], M, p.c);
+        }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const float ea = zrow[2 * lane], eb = zrow[2 * lane + 1];
+    const float tot = wave_sum(ea + eb);
+    const float u = u24f(block_word(false, p.k, q, gstar, p.round, p.seed));
+    float e;
+    const int col = granule_pick(ea, eb, 0.0f, u * tot, false, e);
+    if (lane == 0) {
+        p.x[o] = gstar * GRAN + col;
+        p.pd_x[o] = e / S;
+        p.pd_stats[2 * o] = M;
+        p.pd_stats[2 * o + 1] = S;
+    }
 }
 
 // ------------------------------------------------------------ fused propose
@@ -903,13 +927,12 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
     t.R = a.R; t.gamma = a.gamma; t.r = a.r; t.V = a.V; t.c = a.c; t.vec4 = (a.V % 4) == 0;
     t.nrows = a.R; t.n_gran = n_gran;
     tile_grid(a.R, n_gran, t.bpc, t.n_chunks);
-    t.gstat = ws.gstat; t.gidx = ws.gidx; t.gkey = ws.gkey; t.gw = ws.gw; t.status = a.status;
-    t.seed = a.seed; t.round = a.round;
+    t.gstat = ws.gstat; t.gidx = ws.gidx; t.status = a.status;
     PickArgs pk{};
-    pk.x0 = a.x0; pk.x = x_out;
-    pk.V = a.V; pk.gamma = a.gamma; pk.c = a.c;
-    pk.n_gran = n_gran;
-    pk.gstat = ws.gstat; pk.gidx = ws.gidx; pk.gkey = ws.gkey; pk.gw = ws.gw;
+    pk.U = a.U; pk.W1 = a.W1; pk.W2p = a.W2; pk.x0 = a.x0; pk.x = x_out;
+    pk.V = a.V; pk.gamma = a.gamma; pk.r = a.r; pk.c = a.c;
+    pk.n_gran = n_gran; pk.seed = a.seed; pk.round = a.round;
+    pk.gstat = ws.gstat; pk.gidx = ws.gidx;
     pk.pd_x = pd_x; pk.pd_stats = pd_stats;
     if (ws.part && propose_fused_enabled() && n_gran <= FUSED_PER * TILE_THREADS && k_steps<WT>(a.r) == KS) {
         const bool fits = a.greedy ? n_gran <= fused_capacity<WT, KS, true>()
@@ -930,16 +953,16 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
             if (a.greedy)
                 hipLaunchKernelGGL((k_draft_tile<WT, KS, true>), dim3(grid), dim3(TILE_THREADS), 0, s, t);
             else
-                hipLaunchKernelGGL((k_draft_tile<WT, KS, false, true>), dim3(grid), dim3(TILE_THREADS), 0, s, t);
+                hipLaunchKernelGGL((k_draft_tile<WT, KS, false>), dim3(grid), dim3(TILE_THREADS), 0, s, t);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         {
             ProfScope ps("propose_pick", s);
             if (a.greedy)
-                hipLaunchKernelGGL(k_propose_pick<true>, dim3(a.R), dim3(TILE_THREADS), 0, s, pk);
+                hipLaunchKernelGGL((k_propose_pick<WT, KS, true>), dim3(a.R), dim3(TILE_THREADS), 0, s, pk);
             else
-                hipLaunchKernelGGL(k_propose_pick<false>, dim3(a.R), dim3(TILE_THREADS), 0, s, pk);
+                hipLaunchKernelGGL((k_propose_pick<WT, KS, false>), dim3(a.R), dim3(TILE_THREADS), 0, s, pk);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
