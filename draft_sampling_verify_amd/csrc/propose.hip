@@ -334,8 +334,10 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         }
         return;
     }
-    // the winning granule's weights (relative to M), then the inside draw
+    // the winning granule's weights, relative to its own maximum (no
+    // underflow however far below M it lies), then the inside draw
     const int gstar = gb;
+    const float mg = gs[gstar].x;
     {
         const int nblk = (p.V + 31) / 32;
         const int b = 4 * gstar + w;
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         const f32x16 acc = A.mfma_row(brow, ks);
         if (n == nq) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] = softw(uv[j] + acc[j], M, p.c);
+            for (int j = 0; j < 16; ++j) zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] = softw(uv[j] + acc[j], mg, p.c);
         }
     }
     __syncthreads();
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
     const int col = granule_pick(ea, eb, 0.0f, u * tot, false, e);
     if (lane == 0) {
         p.x[o] = gstar * GRAN + col;
-        p.pd_x[o] = e / S;
+        p.pd_x[o] = e * softw(mg, M, p.c) / S;
         p.pd_stats[2 * o] = M;
         p.pd_stats[2 * o + 1] = S;
     }
