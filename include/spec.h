@@ -158,7 +158,9 @@ int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags);
  * (ties: smaller b), gives x_k.  u_b and e_b are word b & 3 of Philox4x32-10
  * (key = seed) at counter (0xC0000000 | k << 20 | b >> 2, r, round) and
  * (0x80000000 | k << 20 | b >> 2, r, round): u_b = (w >> 8) 2^-24,
- * e_b = ((w >> 9) + 1/2) 2^-23.
+ * e_b = ((w >> 9) + 1/2) 2^-23.  A row whose logits are all -inf (or NaN)
+ * has no sample: its x_k is -1 (p_d(x) and (M, S) NaN), and the next
+ * position of that request raises SPEC_DEV_BAD_TOKEN.
  * In:  U [R,gamma,V] fp32; W1 [V,r] (w_dtype); W2p = spec_pack_w2(W2);
  *      x0 [R] int32.
  * Out: x [R,gamma] int32; pd_x [R,gamma] fp32 = p_k(x_k);
