@@ -159,7 +159,7 @@ int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags);
  * (key = seed) at counter (0xC0000000 | k << 20 | b >> 2, r, round) and
  * (0x80000000 | k << 20 | b >> 2, r, round): u_b = (w >> 8) 2^-24,
  * e_b = ((w >> 9) + 1/2) 2^-23.  A row whose logits are all -inf (or NaN)
- * has no sample: its x_k is -1 (p_d(x) and (M, S) NaN), and the next
+ * has no sample: its x_k is -1 and p_d(x) is NaN, and the next
  * position of that request raises SPEC_DEV_BAD_TOKEN.
  * In:  U [R,gamma,V] fp32; W1 [V,r] (w_dtype); W2p = spec_pack_w2(W2);
  *      x0 [R] int32.
