@@ -263,6 +263,43 @@ def test_emitted_tokens_follow_target_chi_square():
     assert abs(acc.mean() - c_exact) < 5 * se
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "per_position"])
+def test_drafts_follow_pd_across_blocks_chi_square(fused):
+    """The GPU's two-level draw has the law p_d: nine tokens of mass spread
+    over three 128-id blocks (all other logits -inf), W2 = 0 so that every
+    position draws from the same p_d; 2^18 draws per path (R = 32 takes the
+    fused kernel, R = 64 the per-position kernels), chi-square against the
+    exact softmax."""
+    from scipy import special, stats
+    V, r, g = 3 * 128, 64, 8
+    R = 32 if fused else 64
+    ids = np.array([3, 60, 127, 128, 200, 255, 256, 300, 383])
+    rng = np.random.default_rng(31)
+    z = (rng.standard_normal(ids.size) * 1.2).astype(np.float32)
+    u_row = np.full(V, -np.inf, np.float32)
+    u_row[ids] = z
+    U = torch.from_numpy(u_row).cuda().expand(R, g, V).contiguous()
+    W1 = torch.from_numpy((rng.standard_normal((V, r)) * 0.5).astype(np.float32)).cuda().to(torch.bfloat16)
+    W2p = spec.spec_pack_w2(torch.zeros((V, r), dtype=torch.bfloat16, device="cuda"))
+    x0 = torch.from_numpy(rng.integers(0, V, R).astype(np.int32)).cuda()
+    ws = spec.Workspace(R, g, r, V)
+    prev = spec.spec_set_propose_fused(fused)
+    try:
+        counts = np.zeros(V, np.int64)
+        for rnd in range((1 << 18) // (R * g)):
+            x, pdx, pds = spec.spec_markov_propose(U, W1, W2p, x0, 1.0, False, 7, rnd, ws=ws)
+            counts += np.bincount(np_(x).ravel(), minlength=V)
+    finally:
+        spec.spec_set_propose_fused(prev)
+    assert spec.spec_device_status(ws) == 0
+    assert counts[np.setdiff1d(np.arange(V), ids)].sum() == 0
+    p = special.softmax(z.astype(np.float64))
+    pv = stats.chisquare(counts[ids], p * counts.sum()).pvalue
+    log("  chi-square p-value", pv, "draws", int(counts.sum()))
+    assert pv > 1e-4
+    np.testing.assert_allclose(np_(pdx), p[np.searchsorted(ids, np_(x))], rtol=0, atol=1e-6)
+
+
 # ------------------------------------------------------- measured workloads
 
 def _sample(R):
