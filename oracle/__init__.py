@@ -8,7 +8,10 @@ no code with the HIP library and never imports it.
 Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
   philox / u24      pinned: published known-answer blocks + ATen's Philox engine
   bias / softmax    pinned: numpy matmul, scipy softmax, W2 = 0 reduction
-  propose           pinned: brute-force inverse CDF, chi-square at V = 16
+  propose           pinned: numpy searchsorted on the whole softmax (one
+                    inverse CDF over the row), chi-square at V = 16 and over
+                    tokens spread across several 128-id granules, rows
+                    without probability mass
   verify            pinned: chi-square of emitted tokens vs p_t, closed forms
                     for P(accept), E[n_acc], special cases
   confidence        pinned: V = 2 closed form, identical rows, TV identity
@@ -65,6 +68,7 @@ def lib():
         i32, u64, f32 = ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
         L.ref_philox4x32_10.argtypes = [P, P, P]
         L.ref_draw.argtypes = [u64, u64, i32, i32, P]
+        L.ref_philox_words.argtypes = [u64, u64, u64, P]
         L.ref_u24.argtypes = [ctypes.c_uint32]
         L.ref_u24.restype = ctypes.c_double
         L.ref_bias.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32, P]
@@ -74,8 +78,7 @@ def lib():
         L.ref_argmax.restype = i32
         L.ref_markov_propose.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, f32, ctypes.c_int, u64, u64,
-                                         P, P, P, P, P, P, P]
-        L.ref_block_uniforms.argtypes = [u64, u64, i32, i32, i32, P, P]
+                                         P, P, P, P, P, P]
         L.ref_verify.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, f32, ctypes.c_int, u64, u64, P,
                                  P, P, P, P, P, P, P, P, P]
@@ -128,15 +131,11 @@ def u24(w):
     return lib().ref_u24(int(w))
 
 
-def block_uniforms(seed, rnd, req, k, n_blocks):
-    """(e [n_blocks], u [n_blocks]): the race and in-block uniforms of the
-    draft draw's blocks at (seed, round, request, position k)."""
-    e, u = np.zeros(n_blocks), np.zeros(n_blocks)
-    a, b = ctypes.c_double(), ctypes.c_double()
-    for i in range(n_blocks):
-        lib().ref_block_uniforms(seed, rnd, req, k, i, ctypes.byref(a), ctypes.byref(b))
-        e[i], u[i] = a.value, b.value
-    return e, u
+def philox_words(seed, rnd, n):
+    """[n, 4] uint32: the blocks at counters (i mod 2^16, i / 2^16, round)."""
+    out = np.zeros((n, 4), np.uint32)
+    lib().ref_philox_words(seed, rnd, n, _p(out))
+    return out
 
 
 def bias(W1, W2, xprev):
@@ -165,11 +164,11 @@ class OracleError(RuntimeError):
     pass
 
 
-def markov_propose(U, W1, W2, x0, T, greedy, seed, rnd, req_ids=None, x_cond=None):
+def markov_propose(U, W1, W2, x0, T, greedy, seed, rnd, req_ids=None, x_cond=None, allow_blank=False):
     """Returns dict with x [R,g], pd_x [R,g], pd_stats [R,g,2], margin [R,g]
-    (sampled: the block race's key gap, natural log units; greedy: the
-    top-2 logit gap) and margin_within [R,g] (sampled: the inverse-CDF
-    margin inside the winning block)."""
+    and blanked (True if a request had no valid chain: an anchor outside
+    [0, V) or a row without probability mass; its entries are -1 / NaN).
+    A blanked request raises OracleError unless allow_blank."""
     U = _c(U, np.float32)
     R, g, V = U.shape
     W1, W2, dt = _weights(W1, W2)
@@ -178,13 +177,18 @@ def markov_propose(U, W1, W2, x0, T, greedy, seed, rnd, req_ids=None, x_cond=Non
     req_ids = _c(req_ids, np.int32)
     x_cond = _c(x_cond, np.int32)
     out = dict(x=np.zeros((R, g), np.int32), pd_x=np.zeros((R, g)),
-               pd_stats=np.zeros((R, g, 2)), margin=np.zeros((R, g)), margin_within=np.zeros((R, g)))
+               pd_stats=np.zeros((R, g, 2)), margin=np.zeros((R, g)))
     st = lib().ref_markov_propose(_p(U), _p(W1), _p(W2), dt, _p(x0), R, g, r, V, float(T),
                                   int(bool(greedy)), seed, rnd, _p(req_ids), _p(x_cond),
                                   _p(out["x"]), _p(out["pd_x"]), _p(out["pd_stats"]),
-                                  _p(out["margin"]), _p(out["margin_within"]))
+                                  _p(out["margin"]))
+    if st == 1 and allow_blank:
+        out["blanked"] = True
+        return out
     if st != 0:
-        raise OracleError("ref_markov_propose rejected its arguments")
+        raise OracleError("ref_markov_propose rejected its arguments" if st < 0 else
+                          "ref_markov_propose: a request has no valid chain")
+    out["blanked"] = False
     return out
 
 

@@ -44,31 +44,19 @@ void ref_draw(uint64_t seed, uint64_t round, int32_t req, int32_t k, uint32_t ou
     ref_philox4x32_10(ctr, key, out);
 }
 
+void ref_philox_words(uint64_t seed, uint64_t round, uint64_t n, uint32_t* out)
+{
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    for (uint64_t i = 0; i < n; ++i) {
+        const uint32_t ctr[4] = {(uint32_t)(i % 65536u), (uint32_t)(i / 65536u), (uint32_t)round,
+                                 (uint32_t)(round >> 32)};
+        ref_philox4x32_10(ctr, key, out + 4 * i);
+    }
+}
+
 double ref_u24(uint32_t w)
 {
     return (double)(w >> 8) * (1.0 / 16777216.0);
-}
-
-/* The two uniforms of block b at (seed, round, request, position k), from two
- * counter ranges that the four-word draws above never use (their first
- * counter word is k <= 65): first word 0x80000000 | k << 20 | b >> 2 for the
- * race, 0xC0000000 | k << 20 | b >> 2 for the draw inside the block; word
- * b & 3 of each.  The race uniform is the cell centre ((w >> 9) + 1/2) 2^-23
- * of 23 bits, inside (0, 1) so that -ln(-ln e) is finite, and exactly
- * representable in single precision; the in-block uniform is the 24-bit
- * ref_u24. */
-void ref_block_uniforms(uint64_t seed, uint64_t round, int32_t req, int32_t k, int32_t b, double* e_race,
-                        double* u_within)
-{
-    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
-    const uint32_t c0 = ((uint32_t)k << 20) | ((uint32_t)b >> 2);
-    uint32_t ctr[4] = {0x80000000u | c0, (uint32_t)req, (uint32_t)round, (uint32_t)(round >> 32)};
-    uint32_t w[4];
-    ref_philox4x32_10(ctr, key, w);
-    *e_race = ((double)(w[b & 3] >> 9) + 0.5) * (1.0 / 8388608.0);
-    ctr[0] = 0xC0000000u | c0;
-    ref_philox4x32_10(ctr, key, w);
-    *u_within = ref_u24(w[b & 3]);
 }
 
 /* ----------------------------------------------------------------- helpers */
@@ -180,49 +168,6 @@ static int bad_common(const float* U, const void* W1, const void* W2, int w_dtyp
 
 /* ----------------------------------------------------------------- propose */
 
-/* The draft draw x ~ p (DSpark page, section 3 asks for a sample of p_k; how
- * the sample is drawn is this library's reading).  Two levels over blocks of
- * REF_BLOCK consecutive ids: each block b holds a candidate c_b, drawn by
- * inverse CDF over the block's own probabilities with uniform u_b; the blocks
- * race by the Gumbel-max rule on their masses P_b = sum_{v in b} p_v, the
- * winner b* = argmax_b ln P_b - ln(-ln e_b) (ties: smaller b); x = c_{b*}.
- * Exact: P(x = v) = P(b* = b(v)) P(c_b = v) = P_b (p_v / P_b) = p_v.
- * *race_margin = key(b*) - (second key), infinite with one block of mass;
- * *within_margin = the inverse-CDF margin inside b*. */
-static int32_t block_race_draw(const double* p, int V, uint64_t seed, uint64_t round, int32_t req, int32_t k,
-                               double* race_margin, double* within_margin)
-{
-    const int nb = (V + REF_BLOCK - 1) / REF_BLOCK;
-    double best = -INFINITY, second = -INFINITY;
-    int bstar = -1;
-    double ustar = 0.0;
-    for (int b = 0; b < nb; ++b) {
-        const int lo = b * REF_BLOCK, hi = lo + REF_BLOCK < V ? lo + REF_BLOCK : V;
-        double P = 0.0;
-        for (int v = lo; v < hi; ++v)
-            P += p[v];
-        if (!(P > 0.0)) continue;
-        double e, u;
-        ref_block_uniforms(seed, round, req, k, b, &e, &u);
-        const double key = log(P) - log(-log(e));
-        if (key > best) {
-            second = best;
-            best = key;
-            bstar = b;
-            ustar = u;
-        } else if (key > second) {
-            second = key;
-        }
-    }
-    *race_margin = bstar >= 0 ? best - second : 0.0;
-    if (bstar < 0) {
-        *within_margin = 0.0;
-        return -1;
-    }
-    const int lo = bstar * REF_BLOCK, n = (lo + REF_BLOCK < V ? lo + REF_BLOCK : V) - lo;
-    return lo + ref_inverse_cdf(p + lo, n, ustar, within_margin);
-}
-
 /* DSpark page, section 3: x_k ~ p_k = softmax(U_k + B_k) with B_k from
  * x_{k-1} (section 4); the anchor x_0 conditions position 1.  Temperature T
  * divides the logits. */
@@ -230,7 +175,7 @@ int ref_markov_propose(const float* U, const void* W1, const void* W2, int w_dty
                        const int32_t* x0, int R, int gamma, int r, int V, float T,
                        int greedy, uint64_t seed, uint64_t round,
                        const int32_t* req_ids, const int32_t* x_cond,
-                       int32_t* x, double* pd_x, double* pd_stats, double* margin, double* margin_within)
+                       int32_t* x, double* pd_x, double* pd_stats, double* margin)
 {
     if (bad_common(U, W1, W2, w_dtype, x0, R, gamma, r, V, T) || !x) return -1;
     const double Td = (double)T;
@@ -238,27 +183,48 @@ int ref_markov_propose(const float* U, const void* W1, const void* W2, int w_dty
     double* p = (double*)malloc(sizeof(double) * (size_t)V);
     if (!z || !p) { free(z); free(p); return -1; }
     int status = 0;
-    for (int row = 0; row < R && status == 0; ++row) {
+    for (int row = 0; row < R; ++row) {
         int32_t rid = req_ids ? req_ids[row] : row;
         int32_t xprev = x0[row];
         for (int k = 1; k <= gamma; ++k) {
             size_t o = (size_t)row * gamma + (size_t)(k - 1);
-            if (xprev < 0 || xprev >= V) { status = -1; break; }
+            if (xprev < 0 || xprev >= V) {
+                /* no previous token (an anchor outside [0, V), or a row
+                 * without a sample): the rest of the chain is undefined */
+                x[o] = -1;
+                if (pd_x) pd_x[o] = NAN;
+                if (pd_stats) { pd_stats[2 * o] = NAN; pd_stats[2 * o + 1] = NAN; }
+                if (margin) margin[o] = INFINITY;
+                status = 1;
+                xprev = -1;
+                continue;
+            }
             draft_logits(U, W1, W2, w_dtype, row, k, gamma, r, V, xprev, z);
-            double M, S, mg, mw = INFINITY;
+            double M, S, mg;
             softmax_T(z, V, Td, p, &M, &S);
+            if (!(S > 0.0) || isnan(S) || isinf(M)) {
+                /* every logit -inf (or NaN): softmax is 0/0, there is no
+                 * distribution to draw from */
+                x[o] = -1;
+                if (pd_x) pd_x[o] = NAN;
+                if (pd_stats) { pd_stats[2 * o] = NAN; pd_stats[2 * o + 1] = NAN; }
+                if (margin) margin[o] = INFINITY;
+                status = 1;
+                xprev = x_cond ? x_cond[o] : -1;
+                continue;
+            }
             int32_t tok;
             if (greedy) {
                 tok = ref_argmax(z, V, &mg);
             } else {
-                tok = block_race_draw(p, V, seed, round, rid, k, &mg, &mw);
-                if (tok < 0) { status = -1; break; }
+                uint32_t w[4];
+                ref_draw(seed, round, rid, k, w);
+                tok = ref_inverse_cdf(p, V, ref_u24(w[0]), &mg);
             }
             x[o] = tok;
             if (pd_x) pd_x[o] = p[tok];
             if (pd_stats) { pd_stats[2 * o] = M; pd_stats[2 * o + 1] = S; }
             if (margin) margin[o] = mg;
-            if (margin_within) margin_within[o] = mw;
             xprev = x_cond ? x_cond[o] : tok;
         }
     }

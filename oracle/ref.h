@@ -51,15 +51,11 @@ enum { REF_F32 = 0, REF_BF16 = 1 };
 void ref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 /* The four words for (seed, round, request id, position k). */
 void ref_draw(uint64_t seed, uint64_t round, int32_t req, int32_t k, uint32_t out[4]);
+/* out[4i .. 4i+3] = the block at counter (i mod 2^16, i / 2^16, round_lo,
+ * round_hi), key = seed, for i < n (a bulk form for comparisons). */
+void ref_philox_words(uint64_t seed, uint64_t round, uint64_t n, uint32_t* out);
 /* 24-bit uniform in [0, 1 - 2^-24]. */
 double ref_u24(uint32_t w);
-
-/* Blocks of the draft draw: REF_BLOCK consecutive vocabulary ids. */
-enum { REF_BLOCK = 128 };
-/* Race uniform e in (0, 1) and in-block uniform u in [0, 1) of block b at
- * (seed, round, request id, position k); see ref.c for the counters. */
-void ref_block_uniforms(uint64_t seed, uint64_t round, int32_t req, int32_t k, int32_t b, double* e_race,
-                        double* u_within);
 
 /* B[v] = sum_i W1[xprev, i] * W2[v, i], accumulated in double, i ascending. */
 void ref_bias(const void* W1, const void* W2, int w_dtype, int r, int V,
@@ -75,22 +71,20 @@ int32_t ref_argmax(const double* z, int V, double* margin);
  *   req_ids  : Philox request index of each row (NULL -> 0..R-1)
  *   x_cond   : NULL for free running; else [R,gamma] tokens whose prefix
  *              conditions each position (conditioned mode)
- * Sampled draws take the two-level block race of ref.c (a Gumbel-max race
- * of REF_BLOCK-id blocks on their masses, inverse CDF inside the winner).
  * Outputs (all [R,gamma], stats [R,gamma,2]):
  *   x       : drafted tokens
  *   pd_x    : p_d(x_k)
  *   pd_stats: (M, S) with M = max_v (U+B)(v), S = sum_v exp(((U+B)(v) - M)/T)
- *   margin  : decision margin (sampled: the race's top1 - top2 key, natural
- *             log units; greedy: top1 - top2 logit)
- *   margin_within: sampled: the inverse-CDF margin inside the winning block
- *             (infinite when greedy); may be NULL
- * Returns 0, or -1 on a bad argument or an out-of-range token id. */
+ *   margin  : decision margin (CDF margin when sampled, top1-top2 logit when greedy)
+ * A row whose logits are all -inf (or NaN) has no distribution: its x is -1,
+ * pd_x and pd_stats NaN, and so are the later positions of that request
+ * (free running); an anchor outside [0, V) blanks the whole request.
+ * Returns 0; 1 if some request was blanked that way; -1 on a bad argument. */
 int ref_markov_propose(const float* U, const void* W1, const void* W2, int w_dtype,
                        const int32_t* x0, int R, int gamma, int r, int V, float T,
                        int greedy, uint64_t seed, uint64_t round,
                        const int32_t* req_ids, const int32_t* x_cond,
-                       int32_t* x, double* pd_x, double* pd_stats, double* margin, double* margin_within);
+                       int32_t* x, double* pd_x, double* pd_stats, double* margin);
 
 /* Lossless verification of the drafts x against the target rows Lt.
  *   ell      : verified length per request (NULL -> gamma for every request)
