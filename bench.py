@@ -32,7 +32,6 @@ _PROPOSE = ["draft_sampling_verify_amd/csrc/propose.hip", "draft_sampling_verify
 _VERIFY = ["draft_sampling_verify_amd/csrc/verify.hip", "draft_sampling_verify_amd/csrc/common.h"]
 KERNEL_SOURCES = {
     "propose_fused": _PROPOSE,
-    "propose_stats": _PROPOSE,
     "clear_flags": _PROPOSE,
     "draft_tile": _PROPOSE,
     "propose_pick": _PROPOSE,
@@ -62,10 +61,8 @@ def algorithmic_bytes(kernel: str, cfg, K: int) -> float:
     R, g, V, r = cfg.R, cfg.gamma, cfg.V, cfg.r
     wb = 2 if cfg.bf16 else 4
     ng = (V + 127) // 128
-    if kernel == "propose_fused":   # all positions: U rows, W2 once, W1 rows; x out
-        return 4.0 * R * g * V + wb * r * V + wb * R * g * r + 4.0 * R * g
-    if kernel == "propose_stats":   # every row's granule (max, sum), the token and its weight; p_d(x), (M, S) out
-        return R * g * (8.0 * ng + 20.0)
+    if kernel == "propose_fused":   # all positions: U rows, W2 once, W1 rows; x, p_d(x), (M, S) out
+        return 4.0 * R * g * V + wb * r * V + wb * R * g * r + 16.0 * R * g
     if kernel == "clear_flags":
         return 4.0 * (ng + R + 1)
     if kernel == "draft_tile":      # one position: U_k rows, W2, W1 rows; (max, sum) partials out
@@ -78,6 +75,10 @@ def algorithmic_bytes(kernel: str, cfg, K: int) -> float:
         return R * (8.0 * ng + 128 * (4.0 + wb * r) + 16.0)
     if kernel == "verify_resolve":
         return R * (8.0 * ng * (g + 2) + 128 * (8.0 + wb * r))
+    if kernel == "plan":            # verified lengths in, row maps out
+        return R * 4.0 + K * 16.0 + (R + K) * 8.0
+    if kernel == "schedule":        # confidences and the SPS table in, lengths out
+        return 4.0 * R * g + 4.0 * cfg.sps_len + 4.0 * R
     return float("nan")
 
 
@@ -121,29 +122,106 @@ def read_traffic(kernel: str, workload: str):
     return float(m_t.group(1))
 
 
-def cpu_baseline(cfg, seconds_target=12.0):
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_requests(args):
+    """Worker of the all-cores leg: the oracle on its share of requests,
+    rounds 0, 1, ... until `seconds` have passed; returns (tokens, t0, t1)."""
+    cfg, reqs, seconds = args
+    import oracle
+    import workloads
+    d = workloads.make(cfg, requests=reqs, threads=1)
+    T = np.float32(cfg.T)
+    t0 = time.perf_counter()
+    done, rnd = 0, 0
+    while True:
+        for i in range(len(reqs)):
+            sub = {k: d[k][i:i + 1] for k in ("U", "Lt", "x0", "req_ids")}
+            p = oracle.markov_propose(sub["U"], d["W1"], d["W2"], sub["x0"], T, False, 1, rnd,
+                                      req_ids=sub["req_ids"])
+            oracle.verify(sub["U"], d["W1"], d["W2"], sub["x0"], p["x"], sub["Lt"], T, False, 1, rnd,
+                          req_ids=sub["req_ids"])
+            done += cfg.gamma
+        rnd += 1
+        if time.perf_counter() - t0 >= seconds:
+            return done, t0, time.perf_counter()
+
+
+def cpu_baseline(cfg, gpu_x=None, gpu_n_acc=None, gpu_y=None, seconds_target=12.0, all_cores_seconds=8.0):
     """The oracle (single-threaded C, fp64) on a bounded sample of requests
-    of the same workload: propose + verify with c*, timed on the host."""
+    of the same workload: propose + verify with c*, timed on the host.  The
+    single-core leg runs in conditioned mode on the GPU's own round-0 tokens
+    (same arithmetic as a free run), so it also counts the GPU's decisions
+    that differ from the oracle's and how many lie within 1e-6 of a boundary.
+    A second leg runs the same oracle in one process per host core (at most
+    16) over request shards and reports the aggregate rate."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
     import oracle
     import workloads
     oracle.build()
-    per_req = None
+    T = np.float32(cfg.T)
     done, t_total, reqs = 0, 0.0, []
+    par = {"decisions": 0, "low_margin": 0, "token_mismatches": 0, "hard_mismatches": 0,
+           "verify_requests": 0, "verify_differ": 0, "verify_differ_outside_margin": 0}
     rid = 0
     while t_total < seconds_target and rid < cfg.R:
         d = workloads.make(cfg, requests=[rid])
+        xc = None if gpu_x is None else gpu_x[rid:rid + 1]
         t0 = time.perf_counter()
-        p = oracle.markov_propose(d["U"], d["W1"], d["W2"], d["x0"], np.float32(cfg.T), False, 1, 0,
-                                  req_ids=d["req_ids"])
-        oracle.verify(d["U"], d["W1"], d["W2"], d["x0"], p["x"], d["Lt"], np.float32(cfg.T), False, 1, 0,
-                      req_ids=d["req_ids"])
+        p = oracle.markov_propose(d["U"], d["W1"], d["W2"], d["x0"], T, False, 1, 0, req_ids=d["req_ids"],
+                                  x_cond=xc, allow_blank=True)
+        xs = p["x"] if xc is None else xc
+        v = oracle.verify(d["U"], d["W1"], d["W2"], d["x0"], xs, d["Lt"], T, False, 1, 0, req_ids=d["req_ids"])
         t_total += time.perf_counter() - t0
+        if xc is not None:
+            mism = p["x"] != xc
+            low = p["margin"] < 1e-6
+            par["decisions"] += int(xc.size)
+            par["low_margin"] += int(low.sum())
+            par["token_mismatches"] += int(mism.sum())
+            par["hard_mismatches"] += int((mism & ~low).sum())
+            par["verify_requests"] += 1
+            na = int(gpu_n_acc[rid])
+            if na != int(v["n_acc"][0]) or int(gpu_y[rid, na]) != int(v["y"][0, na]):
+                par["verify_differ"] += 1
+                k = min(na, int(v["n_acc"][0]))
+                near = (v["acc_margin"][0, :k + 1] < 1e-6).any() or v["y_margin"][0, na] < 1e-6
+                par["verify_differ_outside_margin"] += int(not near)
         reqs.append(rid)
         done += cfg.gamma
         rid += 1
-    return {"value": done / t_total, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of %d requests of workload %s (propose + verify with c*), %.1f s single-threaded"
-                      % (len(reqs), cfg.R, cfg.name, t_total)}
+    nproc = os.cpu_count() or 1
+    out = {"value": round(done / t_total, 2), "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
+           "sample": "%d of %d requests of workload %s (propose + verify with c*, round 0), %.1f s "
+                     "single-threaded" % (len(reqs), cfg.R, cfg.name, t_total),
+           "host_nproc": nproc, "host_cpu": _cpu_model()}
+    if gpu_x is not None:
+        out["parity_on_sample"] = par
+    # all host cores: one process per core (at most 16), request shards
+    n = max(1, min(16, nproc))
+    shards = [list(range(i, cfg.R, n)) for i in range(n) if i < cfg.R]
+    try:
+        ctx = multiprocessing.get_context("spawn")
+        with ProcessPoolExecutor(len(shards), mp_context=ctx) as ex:
+            res = list(ex.map(_oracle_requests, [(cfg, sh, all_cores_seconds) for sh in shards]))
+        tok = sum(r[0] for r in res)
+        wall = max(r[2] for r in res) - min(r[1] for r in res)
+        out["all_cores"] = {"value": round(tok / wall, 2), "cores": len(shards),
+                            "sample": "the %d requests of %s in %d processes (one per core, rounds 0, 1, ... for "
+                                      "about %.0f s each), %d draft tokens in %.1f s wall" %
+                                      (cfg.R, cfg.name, len(shards), all_cores_seconds, tok, wall)}
+    except Exception as e:   # the single-core figure stands on its own
+        out["all_cores"] = {"error": repr(e)}
+    return out
 
 
 def cluster_bench(spec, workloads, dev, stream, n):
@@ -213,6 +291,115 @@ def cluster_bench(spec, workloads, dev, stream, n):
             "mean_n_acc": round(float(vo[0].float().mean()), 3), "device_status_ok": ok}
 
 
+def _load(spec, workloads, cfg, dev):
+    """Device copies of a workload's inputs (W2 packed once, outside any
+    timed region)."""
+    import torch
+    d = workloads.make(cfg)
+    t = {"U": torch.from_numpy(d["U"]).to(dev), "Lt": torch.from_numpy(d["Lt"]).to(dev),
+         "x0": torch.from_numpy(d["x0"]).to(dev)}
+    if cfg.bf16:
+        t["W1"] = torch.from_numpy(d["W1"].view(np.int16)).to(dev).view(torch.bfloat16)
+        W2 = torch.from_numpy(d["W2"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        t["W1"], W2 = torch.from_numpy(d["W1"]).to(dev), torch.from_numpy(d["W2"]).to(dev)
+    t["W2p"] = spec.spec_pack_w2(W2)
+    if "c" in d:
+        t["c"] = torch.from_numpy(d["c"]).to(dev)
+    if "sps" in d:
+        t["sps"] = torch.from_numpy(d["sps"]).to(dev)
+    del d, W2
+    return t
+
+
+def _kernel_table(spec, run, n, cfg, K):
+    """run(i) for i < n with the library's HIP events on: per-kernel average
+    launch time, launches per step and algorithmic GB/s."""
+    import torch
+    spec.spec_profile_reset()
+    spec.spec_profile_enable(True)
+    for i in range(n):
+        run(i)
+    torch.cuda.synchronize()
+    spec.spec_profile_enable(False)
+    kernels = {}
+    for name in spec.spec_profile_names():
+        c, ms = spec.spec_profile_read(name)
+        avg = 1000.0 * ms / c
+        b = algorithmic_bytes(name, cfg, K)
+        kernels[name] = {"launches_per_step": c / n, "avg_us": round(avg, 2),
+                         "us_per_step": round(1000.0 * ms / n, 2),
+                         "algorithmic_GBs": None if b != b else round(b / (avg * 1e-6) / 1e9, 1)}
+    spec.spec_profile_reset()
+    return kernels
+
+
+def measure_config(spec, workloads, name, dev, stream, steps, warmup=3):
+    """One more workload, timed with the headline's protocol (warm-up, then
+    `steps` steps bracketed by device synchronisation; round = step index).
+    c1: latency of one propose + verify step.  c3, c5: propose + verify of
+    every position.  c4: the serving pipeline propose -> schedule(c) ->
+    verify(l) with c* fused; verified draft tokens = K* of the schedule."""
+    import torch
+    cfg = workloads.CONFIGS["tiny" if name == "c1" else name]
+    t = _load(spec, workloads, cfg, dev)
+    R, g, V = cfg.R, cfg.gamma, cfg.V
+    x = torch.empty((R, g), dtype=torch.int32, device=dev)
+    pd_x = torch.empty((R, g), dtype=torch.float32, device=dev)
+    pd_stats = torch.empty((R, g, 2), dtype=torch.float32, device=dev)
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev)
+    y = torch.empty((R, g + 1), dtype=torch.int32, device=dev)
+    pt_x = torch.empty((R, g), dtype=torch.float32, device=dev)
+    c_star = torch.empty((R, g), dtype=torch.float32, device=dev)
+    ws = spec.Workspace(R, g, cfg.r, V, B_max=max(cfg.sps_len, R), device=dev)
+    sched = name == "c4"
+    if sched:
+        ell = torch.empty(R, dtype=torch.int32, device=dev)
+        K_star = torch.empty(1, dtype=torch.int32, device=dev)
+        theta = torch.empty(1, dtype=torch.float64, device=dev)
+
+    def step(i):
+        spec.spec_markov_propose(t["U"], t["W1"], t["W2p"], t["x0"], cfg.T, False, 1, i, x=x, pd_x=pd_x,
+                                 pd_stats=pd_stats, ws=ws, stream=stream)
+        if sched:
+            spec.spec_schedule(t["c"], t["sps"], ell=ell, K_star=K_star, theta_star=theta, want_a=False, ws=ws,
+                               stream=stream)
+        spec.spec_verify(t["U"], t["W1"], t["W2p"], t["x0"], x, pd_stats, t["Lt"], cfg.T, False, 1, i,
+                         ell=ell if sched else None, n_acc=n_acc, y=y, pt_x=pt_x, c_star=c_star, ws=ws,
+                         stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    K = int(K_star.item()) if sched else R * g
+    kernels = _kernel_table(spec, lambda i: step(warmup + i), steps, cfg, K)
+    sb = step_algorithmic_bytes(cfg, K) + (4.0 * R * g + 4.0 * cfg.sps_len if sched else 0.0)
+    out = {"workload": "%s: R=%d, gamma=%d, V=%d, r=%d, %s weights, sampled, T=%g%s" % (
+               cfg.name if name != "c1" else "c1 (tiny)", R, g, V, cfg.r, "bf16" if cfg.bf16 else "fp32", cfg.T,
+               ", propose -> schedule(c) -> verify(l), c* fused" if sched else ", every position verified"),
+           "steps": steps, "ms_per_step": round(1000.0 * el, 4),
+           "verified_draft_tokens_per_step": K,
+           "value": round(K / el, 1), "unit": "verified draft tokens/s",
+           "step_algorithmic_bytes": sb,
+           "hbm_roofline_frac_step": round(sb / (PEAK_HBM_GBS * 1e9) / el, 4),
+           "kernels": kernels,
+           "mean_n_acc": round(float(n_acc.float().mean()), 4),
+           "device_status": spec.spec_device_status(ws)}
+    if name == "c1":
+        out["us_per_step"] = round(1e6 * el, 2)
+    if sched:
+        out["K_star"] = K
+        out["candidates"] = R * g
+    del t, ws
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +418,8 @@ def main():
                     help="skip the clustered draft head measurement")
     ap.add_argument("--profile-cluster", action="store_true",
                     help="run only the clustered draft head's steps (for rocprofv3), print its JSON object")
+    ap.add_argument("--configs", default="c1,c3,c4,c5",
+                    help="other workloads timed after the headline (comma list; empty = none)")
     ap.add_argument("--calib-copy-mb", type=int, default=512,
                     help="size of the device-to-device copy timed as the achievable-bandwidth reference")
     args = ap.parse_args()
@@ -251,7 +440,7 @@ def main():
         print(json.dumps(cluster_bench(spec, workloads, torch.device("cuda:0"), torch.cuda.current_stream(),
                                        args.steps)), flush=True)
         return
-    spec.spec_set_propose_fused(args.propose_path == "auto")
+    ppath = spec.SPEC_PATH_AUTO if args.propose_path == "auto" else spec.SPEC_PATH_NO_FUSED_PROPOSE
     cfg = workloads.CONFIGS[args.workload]
     d = workloads.make(cfg)
     dev = torch.device("cuda:0")
@@ -279,10 +468,14 @@ def main():
 
     def step(i):
         spec.spec_markov_propose(U, W1, W2p, x0, cfg.T, False, 1, i, x=x, pd_x=pd_x, pd_stats=pd_stats,
-                                 ws=ws, stream=stream)
+                                 ws=ws, stream=stream, path=ppath)
         spec.spec_verify(U, W1, W2p, x0, x, pd_stats, Lt, cfg.T, False, 1, i, n_acc=n_acc, y=y, pt_x=pt_x,
                          c_star=c_star, ws=ws, stream=stream)
 
+    # the GPU's round-0 outputs, for the oracle sample of the CPU baseline
+    step(0)
+    torch.cuda.synchronize()
+    gx0, gn0, gy0 = x.cpu().numpy(), n_acc.cpu().numpy(), y.cpu().numpy()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -448,7 +641,7 @@ def main():
     step_bytes = step_algorithmic_bytes(cfg, K)
     for k, v in kernels.items():
         b = algorithmic_bytes(k, cfg, K)
-        v["algorithmic_GBs"] = round(b / (v["avg_us"] * 1e-6) / 1e9, 1)
+        v["algorithmic_GBs"] = None if b != b else round(b / (v["avg_us"] * 1e-6) / 1e9, 1)
         v["avg_us"] = round(v["avg_us"], 2)
         v["us_per_step"] = round(v["us_per_step"], 2)
     out = {
@@ -486,8 +679,18 @@ def main():
         "mean_c_star": round(cmean, 4),
         "device_status": flags,
     }
+    configs = {}
+    if not args.profile_only and args.configs:
+        del U, Lt, W1, W2p
+        torch.cuda.empty_cache()
+        for name in [c for c in args.configs.split(",") if c]:
+            n = {"c1": 200, "c3": 20, "c4": 10, "c5": 20}.get(name, 20)
+            print("bench: %s" % name, file=sys.stderr, flush=True)
+            configs[name] = measure_config(spec, workloads, name, dev, stream, n)
+    out["configs"] = configs
     if not args.no_cpu_baseline and not args.profile_only:
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, gx0, gn0, gy0)
     print(json.dumps(out), flush=True)
 
 

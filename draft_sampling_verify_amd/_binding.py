@@ -21,6 +21,7 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OP_PROPOSE, SPEC_OP_VERIFY, SPEC_OP_CONFIDENCE, SPEC_OP_SCHEDULE, SPEC_OP_ROUNDS, SPEC_OP_LOSS = range(6)
 SPEC_DEV_BAD_TOKEN, SPEC_DEV_BAD_LENGTH, SPEC_DEV_BAD_CONFIDENCE, SPEC_DEV_WAIT_FAILED = 1, 2, 4, 8
 SPEC_DEV_BAD_CLUSTER = 16
+SPEC_PATH_AUTO, SPEC_PATH_NO_FUSED_PROPOSE, SPEC_PATH_NO_PIPELINED_SWEEP = 0, 1, 2
 
 
 class SpecError(RuntimeError):
@@ -39,10 +40,14 @@ _SIGS = {
     "spec_workspace_init": ([P, SZ, P], I),
     "spec_packed_w2_bytes": ([I, I, I], SZ),
     "spec_pack_w2": ([P, I, I, I, P, P], I),
+    "spec_pack_w2_rv": ([P, I, I, I, P, P], I),
     "spec_device_status": ([P, P, I, P], I),
     "spec_markov_propose": ([P, P, P, I, P, I, I, I, I, F, I, U64, U64, P, P, P, P, SZ, P], I),
+    "spec_markov_propose_ex": ([P, P, P, I, P, I, I, I, I, F, I, U64, U64, P, P, P, I, P, SZ, P], I),
     "spec_verify": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
+    "spec_verify_ex": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, I, P, SZ, P], I),
     "spec_confidence": ([P, P, P, I, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P], I),
+    "spec_confidence_ex": ([P, P, P, I, P, P, P, P, I, I, I, I, F, P, P, I, P, SZ, P], I),
     "spec_schedule": ([P, I, I, P, I, P, P, P, P, P, SZ, P], I),
     "spec_schedule_async": ([P, I, I, P, I, P, P, P, P, P, P, P, SZ, P], I),
     "spec_draft_loss": ([P, P, P, I, P, P, P, P, I, I, I, I, F, F, F, F, P, P, P, P, SZ, P], I),
@@ -51,13 +56,13 @@ _SIGS = {
     "spec_cluster_propose": ([P, P, P, I, P, P, I, I, I, I, I, I, I, F, I, U64, U64, P, P, P, P, P, P, SZ, P], I),
     "spec_cluster_verify": ([P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
     "spec_decode_rounds": ([P, P, P, I, P, P, I, I, I, I, F, I, U64, U64, I, P, P, P, P, P, P, SZ, P], I),
+    "spec_decode_rounds_ex": ([P, P, P, I, P, P, I, I, I, I, F, I, U64, U64, I, P, P, P, P, P, I, P, SZ, P], I),
     "spec_status_str": ([I], ctypes.c_char_p),
-    "spec_set_propose_fused": ([I], I),
-    "spec_set_verify_lds": ([I], I),
     "spec_profile_enable": ([I], I),
     "spec_profile_reset": ([], I),
     "spec_profile_read": ([ctypes.c_char_p, P, P], I),
     "spec_profile_names": ([ctypes.c_char_p, I], I),
+    "spec_philox_words": ([U64, U64, SZ, P, P], I),
 }
 
 
@@ -151,6 +156,22 @@ def spec_pack_w2(W2, out=None, stream=None):
     return out
 
 
+def spec_pack_w2_rv(W2_rv, out=None, stream=None):
+    """spec_pack_w2 for W2 held as the r x V matrix of B = W1[x] W2 (W2_rv
+    [r, V]); returns the same packed tensor."""
+    if W2_rv.dim() != 2:
+        raise ValueError("W2_rv must be [r, V]")
+    r, V = W2_rv.shape
+    dt = _wdtype(W2_rv)
+    nbytes = spec_packed_w2_bytes(dt, r, V)
+    if nbytes == 0:
+        raise SpecError(SPEC_EINVAL, "spec_pack_w2_rv")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=W2_rv.device) if out is None else out
+    _need(out, (nbytes,), torch.uint8, "out")
+    _check(lib().spec_pack_w2_rv(_ptr(W2_rv), dt, r, V, _ptr(out), _stream(stream)), "spec_pack_w2_rv")
+    return out
+
+
 def spec_workspace_bytes(op, R, gamma, r, V, B_max=0) -> int:
     return int(lib().spec_workspace_bytes(op, R, gamma, r, V, B_max))
 
@@ -194,7 +215,8 @@ def spec_device_status(ws: Workspace, stream=None, clear=False) -> int:
 
 
 def spec_markov_propose(U, W1, W2p, x0, T, greedy=False, seed=1, round=0, x=None, pd_x=None,
-                        pd_stats=None, ws=None, stream=None):
+                        pd_stats=None, ws=None, stream=None, path=SPEC_PATH_AUTO):
+    """path != 0 calls spec_markov_propose_ex with those SPEC_PATH_* bits."""
     R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
     dev = U.device
     _need(x, (R, gamma), torch.int32, "x")
@@ -204,16 +226,20 @@ def spec_markov_propose(U, W1, W2p, x0, T, greedy=False, seed=1, round=0, x=None
     pd_x = torch.empty((R, gamma), dtype=torch.float32, device=dev) if pd_x is None else pd_x
     pd_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev) if pd_stats is None else pd_stats
     ws = _ws(ws, R, gamma, r, V, dev)
-    st = lib().spec_markov_propose(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), R, gamma, r, V,
-                                   float(T), int(bool(greedy)), int(seed), int(round), _ptr(x), _ptr(pd_x),
-                                   _ptr(pd_stats), ws.ptr(), ws.nbytes, _stream(stream))
+    args = (_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), R, gamma, r, V, float(T), int(bool(greedy)),
+            int(seed), int(round), _ptr(x), _ptr(pd_x), _ptr(pd_stats))
+    if path:
+        st = lib().spec_markov_propose_ex(*args, int(path), ws.ptr(), ws.nbytes, _stream(stream))
+    else:
+        st = lib().spec_markov_propose(*args, ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_markov_propose")
     return x, pd_x, pd_stats
 
 
 def spec_verify(U, W1, W2p, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=0, ell=None,
                 n_acc=None, y=None, pt_x=None, c_star=None, want_pt_x=True, want_c_star=True,
-                ws=None, stream=None):
+                ws=None, stream=None, path=SPEC_PATH_AUTO):
+    """path != 0 calls spec_verify_ex with those SPEC_PATH_* bits."""
     R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
     dev = U.device
     _need(x, (R, gamma), torch.int32, "x")
@@ -231,16 +257,20 @@ def spec_verify(U, W1, W2p, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=
     if c_star is None and want_c_star:
         c_star = torch.empty((R, gamma), dtype=torch.float32, device=dev)
     ws = _ws(ws, R, gamma, r, V, dev)
-    st = lib().spec_verify(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(x), _ptr(pd_stats),
-                           _ptr(Lt), _ptr(ell), R, gamma, r, V, float(T), int(bool(greedy)), int(seed),
-                           int(round), _ptr(n_acc), _ptr(y), _ptr(pt_x), _ptr(c_star), ws.ptr(), ws.nbytes,
-                           _stream(stream))
+    args = (_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(x), _ptr(pd_stats), _ptr(Lt), _ptr(ell), R,
+            gamma, r, V, float(T), int(bool(greedy)), int(seed), int(round), _ptr(n_acc), _ptr(y), _ptr(pt_x),
+            _ptr(c_star))
+    if path:
+        st = lib().spec_verify_ex(*args, int(path), ws.ptr(), ws.nbytes, _stream(stream))
+    else:
+        st = lib().spec_verify(*args, ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_verify")
     return n_acc, y, pt_x, c_star
 
 
 def spec_decode_rounds(U, W1, W2p, x0, Lt, T, n_rounds, greedy=False, seed=1, round0=0, want_c_star=False,
-                       anchors=None, x=None, n_acc=None, y=None, c_star=None, ws=None, stream=None):
+                       anchors=None, x=None, n_acc=None, y=None, c_star=None, ws=None, stream=None,
+                       path=SPEC_PATH_AUTO):
     """n_rounds propose + verify rounds on the device, each round's anchors
     being the previous round's last emitted tokens.  Returns (anchors
     [n+1, R], x [n, R, gamma], n_acc [n, R], y [n, R, gamma+1], c_star or
@@ -261,15 +291,18 @@ def spec_decode_rounds(U, W1, W2p, x0, Lt, T, n_rounds, greedy=False, seed=1, ro
     if c_star is None and want_c_star:
         c_star = torch.empty((n, R, gamma), dtype=torch.float32, device=dev)
     ws = _ws(ws, R, gamma, r, V, dev)
-    st = lib().spec_decode_rounds(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(Lt), R, gamma, r, V,
-                                  float(T), int(bool(greedy)), int(seed), int(round0), n, _ptr(anchors), _ptr(x),
-                                  _ptr(n_acc), _ptr(y), _ptr(c_star), ws.ptr(), ws.nbytes, _stream(stream))
+    args = (_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(Lt), R, gamma, r, V, float(T),
+            int(bool(greedy)), int(seed), int(round0), n, _ptr(anchors), _ptr(x), _ptr(n_acc), _ptr(y), _ptr(c_star))
+    if path:
+        st = lib().spec_decode_rounds_ex(*args, int(path), ws.ptr(), ws.nbytes, _stream(stream))
+    else:
+        st = lib().spec_decode_rounds(*args, ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_decode_rounds")
     return anchors, x, n_acc, y, c_star
 
 
 def spec_confidence(U, W1, W2p, x0, x, Lt, T, pd_stats=None, c_star=None, a_star=None, want_a_star=True,
-                    ws=None, stream=None):
+                    ws=None, stream=None, path=SPEC_PATH_AUTO):
     R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
     dev = U.device
     _need(x, (R, gamma), torch.int32, "x")
@@ -281,9 +314,12 @@ def spec_confidence(U, W1, W2p, x0, x, Lt, T, pd_stats=None, c_star=None, a_star
     if a_star is None and want_a_star:
         a_star = torch.empty((R, gamma), dtype=torch.float64, device=dev)
     ws = _ws(ws, R, gamma, r, V, dev)
-    st = lib().spec_confidence(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(x), _ptr(pd_stats),
-                               _ptr(Lt), R, gamma, r, V, float(T), _ptr(c_star), _ptr(a_star), ws.ptr(),
-                               ws.nbytes, _stream(stream))
+    args = (_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), _ptr(x), _ptr(pd_stats), _ptr(Lt), R, gamma, r, V,
+            float(T), _ptr(c_star), _ptr(a_star))
+    if path:
+        st = lib().spec_confidence_ex(*args, int(path), ws.ptr(), ws.nbytes, _stream(stream))
+    else:
+        st = lib().spec_confidence(*args, ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_confidence")
     return c_star, a_star
 
@@ -455,19 +491,7 @@ def spec_schedule_async(c, sps, K_hist, ell=None, a=None, K_used=None, K_star=No
     return ell, a, K_used, K_star, theta_star
 
 
-def spec_set_propose_fused(enable: bool) -> bool:
-    """Process-wide: allow (True, the default) or forbid the fused propose
-    launch; returns the previous setting."""
-    return bool(lib().spec_set_propose_fused(int(bool(enable))))
-
-
-def spec_set_verify_lds(enable: bool) -> bool:
-    """Process-wide: allow (True, the default) or forbid the pipelined
-    verify sweep (W1 rows gathered straight into LDS by half of each
-    workgroup, U and target rows streamed by the other half); returns the
-    previous setting."""
-    return bool(lib().spec_set_verify_lds(int(bool(enable))))
-
+# ---- kernel timing (include/spec_debug.h)
 
 def spec_profile_enable(on=True):
     _check(lib().spec_profile_enable(int(bool(on))), "spec_profile_enable")
@@ -489,3 +513,13 @@ def spec_profile_names():
     buf = ctypes.create_string_buffer(need + 1)
     lib().spec_profile_names(buf, need + 1)
     return [s for s in buf.value.decode().split(",") if s]
+
+
+def spec_philox_words(seed, rnd, n, out=None, stream=None):
+    """[n, 4] int32 tensor (uint32 bits): the kernels' Philox4x32-10 blocks
+    at counters (i mod 2^16, i / 2^16, round) with key = seed."""
+    out = torch.empty((n, 4), dtype=torch.int32, device="cuda") if out is None else out
+    _need(out, (n, 4), torch.int32, "out")
+    _check(lib().spec_philox_words(int(seed), int(rnd), int(n), _ptr(out), _stream(stream)), "spec_philox_words")
+    return out
+

@@ -5,12 +5,13 @@
 #include <math.h>
 #include <string.h>
 
-#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/spec.h"
+#include "../../include/spec_debug.h"
 #include "common.h"
 #include "internal.h"
 
@@ -40,7 +41,7 @@ int check_draft(const float* U, const void* W1, const void* W2, int w_dtype, con
 
 DraftArgs make_args(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0,
                     const int32_t* x, int R, int gamma, int r, int V, float T, int greedy, uint64_t seed,
-                    uint64_t round, void* ws)
+                    uint64_t round, void* ws, int path = 0)
 {
     DraftArgs a{};
     a.U = U; a.W1 = W1; a.W2 = W2; a.w_dtype = w_dtype; a.x0 = x0; a.x = x;
@@ -50,8 +51,11 @@ DraftArgs make_args(const float* U, const void* W1, const void* W2, int w_dtype,
     a.greedy = greedy != 0;
     a.seed = seed; a.round = round;
     a.status = reinterpret_cast<uint32_t*>(ws);
+    a.path = path;
     return a;
 }
+
+bool path_ok(int path) { return (path & ~(SPEC_PATH_NO_FUSED_PROPOSE | SPEC_PATH_NO_PIPELINED_SWEEP)) == 0; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH; }
 
@@ -68,11 +72,22 @@ int check_cluster(int R, int gamma, int d, int N_c, int K_c, int max_cl, int V, 
     return SPEC_OK;
 }
 
-// spec_decode_rounds keeps each round's p_d(x) and (M, S) after the larger of
-// the propose and verify regions (verify reads what propose wrote).
-size_t rounds_scratch_offset(size_t propose_bytes, size_t verify_bytes)
+// spec_decode_rounds lays its workspace out as [header | verify regions |
+// propose regions | p_d(x) | (M, S)]: the propose's tagged hand-over words
+// never share memory with the verify's data.
+struct RoundsLayout {
+    size_t propose_start, pd_x, pd_stats, end;
+};
+RoundsLayout rounds_layout(int R, int gamma, int V)
 {
-    return spec::align256(propose_bytes > verify_bytes ? propose_bytes : verify_bytes);
+    RoundsLayout l{};
+    spec::carve_verify(nullptr, R, gamma, V, false, &l.propose_start);
+    size_t pe = 0;
+    spec::carve_propose(nullptr, R, V, &pe, l.propose_start);
+    l.pd_x = spec::align256(pe);
+    l.pd_stats = l.pd_x + spec::align256((size_t)R * gamma * 4);
+    l.end = l.pd_stats + spec::align256((size_t)R * gamma * 8);
+    return l;
 }
 
 __global__ void k_copy_words(const int32_t* src, int32_t* dst, int n)
@@ -90,6 +105,14 @@ __global__ void k_next_anchor(const int32_t* n_acc, const int32_t* y, int R, int
     next[i] = (n >= 0 && n <= gamma) ? y[(size_t)i * (gamma + 1) + n] : -1;
 }
 
+__global__ void k_philox_words(uint64_t seed, uint64_t round, size_t n, uint32_t* out)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const spec::u32x4 w = spec::philox((uint32_t)(i & 0xFFFFu), (uint32_t)(i >> 16), round, seed);
+        reinterpret_cast<uint4*>(out)[i] = make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]);
+    }
+}
+
 __global__ void k_zero_words(uint32_t* p, size_t n)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -97,11 +120,13 @@ __global__ void k_zero_words(uint32_t* p, size_t n)
 }
 
 
-// ---- profiling records
+// ---- kernel timing records (spec_debug.h): off unless a benchmark turns
+// them on; guarded by one mutex
 struct ProfRecord {
     std::string name;
     hipEvent_t start, stop;
 };
+std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRecord> g_records;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_event_pool;
@@ -111,19 +136,9 @@ size_t g_pool_used = 0;
 
 namespace spec {
 
-namespace {
-std::atomic<int> g_fused{1};
-}
-int set_propose_fused(int enable) { return g_fused.exchange(enable ? 1 : 0); }
-int propose_fused_enabled() { return g_fused.load(); }
-namespace {
-std::atomic<int> g_sweep_lds{1};
-}
-int set_sweep_lds(int enable) { return g_sweep_lds.exchange(enable ? 1 : 0); }
-int sweep_lds_enabled() { return g_sweep_lds.load(); }
-
 ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s)
 {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
     if (g_pool_used == g_event_pool.size()) {
         hipEvent_t a, b;
@@ -143,7 +158,9 @@ ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s)
 
 ProfScope::~ProfScope()
 {
-    if (slot >= 0) hipEventRecord(g_records[slot].stop, stream);
+    if (slot < 0) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (slot < (int)g_records.size()) hipEventRecord(g_records[slot].stop, stream);
 }
 
 }  // namespace spec
@@ -158,7 +175,7 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
         if (check_draft(nullptr, nullptr, nullptr, SPEC_BF16, nullptr, 0, gamma, r, V, 1.0f) != SPEC_OK || R < 0 ||
             R > MAX_R)
             return 0;
-        spec::carve_propose(nullptr, R, gamma, V, &bytes);
+        spec::carve_propose(nullptr, R, V, &bytes);
         return bytes;
     case SPEC_OP_VERIFY:
     case SPEC_OP_CONFIDENCE:
@@ -167,13 +184,11 @@ size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max)
             return 0;
         spec::carve_verify(nullptr, R, gamma, V, op == SPEC_OP_CONFIDENCE, &bytes);
         return bytes;
-    case SPEC_OP_ROUNDS: {
-        const size_t pb = spec_workspace_bytes(SPEC_OP_PROPOSE, R, gamma, r, V, B_max);
-        const size_t vb = spec_workspace_bytes(SPEC_OP_VERIFY, R, gamma, r, V, B_max);
-        if (!pb || !vb) return 0;
-        return rounds_scratch_offset(pb, vb) + spec::align256((size_t)R * gamma * 4) +
-               spec::align256((size_t)R * gamma * 8);
-    }
+    case SPEC_OP_ROUNDS:
+        if (check_draft(nullptr, nullptr, nullptr, SPEC_BF16, nullptr, 0, gamma, r, V, 1.0f) != SPEC_OK || R < 0 ||
+            R > MAX_R)
+            return 0;
+        return rounds_layout(R, gamma, V).end;
     case SPEC_OP_LOSS:
         if (check_draft(nullptr, nullptr, nullptr, SPEC_BF16, nullptr, 0, gamma, r, V, 1.0f) != SPEC_OK || R < 0 ||
             R > MAX_R)
@@ -255,14 +270,14 @@ int spec_cluster_verify(const int32_t* tok_slot, const int32_t* sel, const float
     return launch_status(spec::launch_cluster_verify(cv, w, (hipStream_t)stream));
 }
 
-int spec_set_propose_fused(int enable) { return spec::set_propose_fused(enable); }
-int spec_set_verify_lds(int enable) { return spec::set_sweep_lds(enable); }
-
 int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream)
 {
     if (!ws || ws_bytes < spec::WS_HEADER) return SPEC_EWORKSPACE;
-    hipLaunchKernelGGL(k_zero_words, dim3(256), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ws,
-                       spec::WS_HEADER / 4);
+    // the whole workspace: the status word, the call counter of the fused
+    // propose and its hand-over words (0 is never a valid tag)
+    const size_t words = ws_bytes / 4;
+    const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_zero_words, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ws, words);
     return launch_status(hipGetLastError());
 }
 
@@ -277,7 +292,15 @@ int spec_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, spec_stre
     int st = check_draft(nullptr, nullptr, nullptr, w_dtype, nullptr, 0, 1, r, V, 1.0f);
     if (st != SPEC_OK) return st;
     if (!W2 || !W2p || !aligned16(W2) || !aligned16(W2p)) return SPEC_EINVAL;
-    return launch_status(spec::launch_pack_w2(W2, w_dtype, r, V, W2p, (hipStream_t)stream));
+    return launch_status(spec::launch_pack_w2(W2, w_dtype, r, V, W2p, false, (hipStream_t)stream));
+}
+
+int spec_pack_w2_rv(const void* W2_rv, int w_dtype, int r, int V, void* W2p, spec_stream_t stream)
+{
+    int st = check_draft(nullptr, nullptr, nullptr, w_dtype, nullptr, 0, 1, r, V, 1.0f);
+    if (st != SPEC_OK) return st;
+    if (!W2_rv || !W2p || !aligned16(W2p)) return SPEC_EINVAL;
+    return launch_status(spec::launch_pack_w2(W2_rv, w_dtype, r, V, W2p, true, (hipStream_t)stream));
 }
 
 int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags)
@@ -295,20 +318,43 @@ int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags)
     return word ? SPEC_EDEVICE : SPEC_OK;
 }
 
+namespace {
+
+// propose with its regions starting at `start` (after the header, or after
+// the verify regions in spec_decode_rounds)
+int propose_at(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, int R, int gamma,
+               int r, int V, float T, int greedy, uint64_t seed, uint64_t round, int32_t* x, float* pd_x,
+               float* pd_stats, int path, void* ws, size_t ws_bytes, size_t start, spec_stream_t stream)
+{
+    int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
+    if (st != SPEC_OK) return st;
+    if (!path_ok(path)) return SPEC_EINVAL;
+    if (R > 0 && (!x || !pd_x || !pd_stats)) return SPEC_EINVAL;
+    size_t need = 0;
+    spec::carve_propose(nullptr, R, V, &need, start);
+    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
+    if (R == 0) return SPEC_OK;
+    const spec::ProposeWs w = spec::carve_propose(ws, R, V, nullptr, start);
+    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, greedy, seed, round, ws, path);
+    return launch_status(spec::launch_propose(a, x, pd_x, pd_stats, w, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int spec_markov_propose_ex(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, int R,
+                           int gamma, int r, int V, float T, int greedy, uint64_t seed, uint64_t round, int32_t* x,
+                           float* pd_x, float* pd_stats, int path, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
+    return propose_at(U, W1, W2, w_dtype, x0, R, gamma, r, V, T, greedy, seed, round, x, pd_x, pd_stats, path, ws,
+                      ws_bytes, spec::WS_HEADER, stream);
+}
+
 int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, int R,
                         int gamma, int r, int V, float T, int greedy, uint64_t seed, uint64_t round, int32_t* x,
                         float* pd_x, float* pd_stats, void* ws, size_t ws_bytes, spec_stream_t stream)
 {
-    int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
-    if (st != SPEC_OK) return st;
-    if (R > 0 && (!x || !pd_x || !pd_stats)) return SPEC_EINVAL;
-    size_t need = 0;
-    spec::carve_propose(nullptr, R, gamma, V, &need);
-    if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
-    if (R == 0) return SPEC_OK;
-    const spec::ProposeWs w = spec::carve_propose(ws, R, gamma, V, nullptr);
-    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, greedy, seed, round, ws);
-    return launch_status(spec::launch_propose(a, x, pd_x, pd_stats, w, (hipStream_t)stream));
+    return spec_markov_propose_ex(U, W1, W2, w_dtype, x0, R, gamma, r, V, T, greedy, seed, round, x, pd_x, pd_stats,
+                                  SPEC_PATH_AUTO, ws, ws_bytes, stream);
 }
 
 int spec_verify(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, const int32_t* x,
@@ -316,8 +362,18 @@ int spec_verify(const float* U, const void* W1, const void* W2, int w_dtype, con
                 int greedy, uint64_t seed, uint64_t round, int32_t* n_acc, int32_t* y, float* pt_x, float* c_star,
                 void* ws, size_t ws_bytes, spec_stream_t stream)
 {
+    return spec_verify_ex(U, W1, W2, w_dtype, x0, x, pd_stats, Lt, ell, R, gamma, r, V, T, greedy, seed, round,
+                          n_acc, y, pt_x, c_star, SPEC_PATH_AUTO, ws, ws_bytes, stream);
+}
+
+int spec_verify_ex(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0,
+                   const int32_t* x, const float* pd_stats, const float* Lt, const int32_t* ell, int R, int gamma,
+                   int r, int V, float T, int greedy, uint64_t seed, uint64_t round, int32_t* n_acc, int32_t* y,
+                   float* pt_x, float* c_star, int path, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
     int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
     if (st != SPEC_OK) return st;
+    if (!path_ok(path)) return SPEC_EINVAL;
     if (R > 0 && (!x || !pd_stats || !Lt || !n_acc || !y)) return SPEC_EINVAL;
     if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
     size_t need = 0;
@@ -325,7 +381,7 @@ int spec_verify(const float* U, const void* W1, const void* W2, int w_dtype, con
     if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
     if (R == 0) return SPEC_OK;
     const spec::VerifyWs w = spec::carve_verify(ws, R, gamma, V, false, nullptr);
-    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, greedy, seed, round, ws);
+    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, greedy, seed, round, ws, path);
     int32_t* counts = reinterpret_cast<spec::WsHeader*>(ws)->counts;
     return launch_status(
         spec::launch_verify(a, pd_stats, Lt, ell, n_acc, y, pt_x, c_star, w, counts, (hipStream_t)stream));
@@ -335,8 +391,18 @@ int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
                     const int32_t* x, const float* pd_stats, const float* Lt, int R, int gamma, int r, int V,
                     float T, float* c_star, double* a_star, void* ws, size_t ws_bytes, spec_stream_t stream)
 {
+    return spec_confidence_ex(U, W1, W2, w_dtype, x0, x, pd_stats, Lt, R, gamma, r, V, T, c_star, a_star,
+                              SPEC_PATH_AUTO, ws, ws_bytes, stream);
+}
+
+int spec_confidence_ex(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0,
+                       const int32_t* x, const float* pd_stats, const float* Lt, int R, int gamma, int r, int V,
+                       float T, float* c_star, double* a_star, int path, void* ws, size_t ws_bytes,
+                       spec_stream_t stream)
+{
     int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
     if (st != SPEC_OK) return st;
+    if (!path_ok(path)) return SPEC_EINVAL;
     if (R > 0 && (!x || !Lt || !c_star)) return SPEC_EINVAL;
     if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
     size_t need = 0;
@@ -344,7 +410,7 @@ int spec_confidence(const float* U, const void* W1, const void* W2, int w_dtype,
     if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
     if (R == 0) return SPEC_OK;
     const spec::VerifyWs w = spec::carve_verify(ws, R, gamma, V, true, nullptr);
-    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, 0, 0, 0, ws);
+    DraftArgs a = make_args(U, W1, W2, w_dtype, x0, x, R, gamma, r, V, T, 0, 0, 0, ws, path);
     return launch_status(
         spec::launch_confidence(a, pd_stats, Lt, c_star, a_star, w, (hipStream_t)stream));
 }
@@ -377,18 +443,26 @@ int spec_decode_rounds(const float* U, const void* W1, const void* W2p, int w_dt
                        uint64_t round0, int n_rounds, int32_t* anchors, int32_t* x, int32_t* n_acc, int32_t* y,
                        float* c_star, void* ws, size_t ws_bytes, spec_stream_t stream)
 {
+    return spec_decode_rounds_ex(U, W1, W2p, w_dtype, x0, Lt, R, gamma, r, V, T, greedy, seed, round0, n_rounds,
+                                 anchors, x, n_acc, y, c_star, SPEC_PATH_AUTO, ws, ws_bytes, stream);
+}
+
+int spec_decode_rounds_ex(const float* U, const void* W1, const void* W2p, int w_dtype, const int32_t* x0,
+                          const float* Lt, int R, int gamma, int r, int V, float T, int greedy, uint64_t seed,
+                          uint64_t round0, int n_rounds, int32_t* anchors, int32_t* x, int32_t* n_acc, int32_t* y,
+                          float* c_star, int path, void* ws, size_t ws_bytes, spec_stream_t stream)
+{
     int st = check_draft(U, W1, W2p, w_dtype, x0, R, gamma, r, V, T);
     if (st != SPEC_OK) return st;
-    if (n_rounds < 1) return SPEC_EINVAL;
+    if (n_rounds < 1 || !path_ok(path)) return SPEC_EINVAL;
     if (R > 0 && (!Lt || !anchors || !x || !n_acc || !y)) return SPEC_EINVAL;
     if (R > 0 && !aligned16(Lt)) return SPEC_EINVAL;
     const size_t need = spec_workspace_bytes(SPEC_OP_ROUNDS, R, gamma, r, V, 0);
     if (!ws || ws_bytes < need) return SPEC_EWORKSPACE;
     if (R == 0) return SPEC_OK;
-    const size_t off = rounds_scratch_offset(spec_workspace_bytes(SPEC_OP_PROPOSE, R, gamma, r, V, 0),
-                                             spec_workspace_bytes(SPEC_OP_VERIFY, R, gamma, r, V, 0));
-    float* pd_x = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
-    float* pd_stats = reinterpret_cast<float*>(static_cast<char*>(ws) + off + spec::align256((size_t)R * gamma * 4));
+    const RoundsLayout lay = rounds_layout(R, gamma, V);
+    float* pd_x = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.pd_x);
+    float* pd_stats = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.pd_stats);
     hipStream_t s = (hipStream_t)stream;
     const int nb = (R + 255) / 256;
     hipLaunchKernelGGL(k_copy_words, dim3(nb), dim3(256), 0, s, x0, anchors, R);
@@ -399,11 +473,11 @@ int spec_decode_rounds(const float* U, const void* W1, const void* W2p, int w_dt
         int32_t* n_i = n_acc + (size_t)i * R;
         int32_t* y_i = y + (size_t)i * R * (gamma + 1);
         float* c_i = c_star ? c_star + (size_t)i * R * gamma : nullptr;
-        st = spec_markov_propose(U, W1, W2p, w_dtype, a_i, R, gamma, r, V, T, greedy, seed, round0 + i, x_i, pd_x,
-                                 pd_stats, ws, ws_bytes, stream);
+        st = propose_at(U, W1, W2p, w_dtype, a_i, R, gamma, r, V, T, greedy, seed, round0 + i, x_i, pd_x, pd_stats,
+                        path, ws, ws_bytes, lay.propose_start, stream);
         if (st != SPEC_OK) return st;
-        st = spec_verify(U, W1, W2p, w_dtype, a_i, x_i, pd_stats, Lt, nullptr, R, gamma, r, V, T, greedy, seed,
-                         round0 + i, n_i, y_i, nullptr, c_i, ws, ws_bytes, stream);
+        st = spec_verify_ex(U, W1, W2p, w_dtype, a_i, x_i, pd_stats, Lt, nullptr, R, gamma, r, V, T, greedy, seed,
+                            round0 + i, n_i, y_i, nullptr, c_i, path, ws, ws_bytes, stream);
         if (st != SPEC_OK) return st;
         hipLaunchKernelGGL(k_next_anchor, dim3(nb), dim3(256), 0, s, n_i, y_i, R, gamma,
                            anchors + (size_t)(i + 1) * R);
@@ -449,14 +523,25 @@ const char* spec_status_str(int status)
     }
 }
 
+int spec_philox_words(uint64_t seed, uint64_t round, size_t n, uint32_t* out, void* stream)
+{
+    if (!out || n > ((size_t)1 << 32)) return SPEC_EINVAL;
+    if (n == 0) return SPEC_OK;
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(k_philox_words, dim3(blocks), dim3(256), 0, (hipStream_t)stream, seed, round, n, out);
+    return launch_status(hipGetLastError());
+}
+
 int spec_profile_enable(int on)
 {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_on = on != 0;
     return SPEC_OK;
 }
 
 int spec_profile_reset(void)
 {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     g_records.clear();
     g_pool_used = 0;
     return SPEC_OK;
@@ -465,6 +550,7 @@ int spec_profile_reset(void)
 int spec_profile_read(const char* kernel, int* launches, double* total_ms)
 {
     if (!kernel || !launches || !total_ms) return SPEC_EINVAL;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     int n = 0;
     double tot = 0.0;
     for (const ProfRecord& rec : g_records) {
@@ -482,6 +568,7 @@ int spec_profile_read(const char* kernel, int* launches, double* total_ms)
 
 int spec_profile_names(char* buf, int buf_len)
 {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     std::string all;
     for (const ProfRecord& rec : g_records) {
         const std::string key = "," + rec.name + ",";

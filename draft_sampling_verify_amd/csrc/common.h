@@ -58,39 +58,6 @@ __device__ inline u32x4 philox(uint32_t k, uint32_t req, uint64_t round, uint64_
 __device__ inline float u24f(uint32_t w) { return (float)(w >> 8) * (1.0f / 16777216.0f); }
 __device__ inline double u24d(uint32_t w) { return (double)(w >> 8) * (1.0 / 16777216.0); }
 
-// ------------------------------------------------ the sampled draft draw
-//
-// A draft token is drawn in two levels over the 128-id granules (exact: the
-// granule wins with its probability mass, the id inside it with its
-// conditional probability):
-//   inside   each granule's candidate c_g is drawn by inverse CDF over the
-//            granule's own weights with uniform u_g (the workgroup holding
-//            the granule's logits does this before any other granule is known);
-//   race     the granules race by the Gumbel-max rule on their masses:
-//            g* = argmax_g log2(mass_g) - log2(-ln e_g) (ties: smaller g), and
-//            x = c_{g*}.
-// The uniforms of granule g at (request, position k) are word g & 3 of the
-// Philox block with counter (0x80000000 | k << 20 | g >> 2, request, round)
-// (race, e_g = ((w >> 9) + 1/2) 2^-23) and (0xC0000000 | ...) (inside,
-// u_g = u24f(w)); the accept / residual draws never use such counters (their
-// first word is k <= 65).
-__device__ inline uint32_t block_word(bool race, int k, int req, int g, uint64_t round, uint64_t seed)
-{
-    const u32x4 P = philox((race ? 0x80000000u : 0xC0000000u) | ((uint32_t)k << 20) | ((uint32_t)g >> 2),
-                           (uint32_t)req, round, seed);
-    const int i = g & 3;
-    return i == 0 ? P.w[0] : i == 1 ? P.w[1] : i == 2 ? P.w[2] : P.w[3];
-}
-// log2(-ln e) of a race word.  -ln e goes through log1p for e > 1/2, where
-// 1 - e is exact, so that it keeps its relative accuracy as e -> 1 (the
-// granules most likely to win).
-__device__ inline float race_term(uint32_t w)
-{
-    const float e = ((float)(w >> 9) + 0.5f) * (1.0f / 8388608.0f);
-    const float E = e < 0.5f ? -logf(e) : -log1pf(-(1.0f - e));
-    return log2f(E);
-}
-
 // ------------------------------------------- exchange between workgroups
 //
 // Values one workgroup of a running kernel hands to another go through
@@ -966,86 +933,6 @@ __device__ inline void oct_argmax(float& v, int& i)
     argmax_merge(v, i, dpp_f<DPP_XOR2>(v), dpp_i<DPP_XOR2>(i));
     argmax_merge(v, i, dpp_f<DPP_HALF_MIRROR>(v), dpp_i<DPP_HALF_MIRROR>(i));
 }
-__device__ inline int oct_max_i(int v)
-{
-    v = max(v, dpp_i<DPP_XOR1>(v));
-    v = max(v, dpp_i<DPP_XOR2>(v));
-    return max(v, dpp_i<DPP_HALF_MIRROR>(v));
-}
-// The inside draw of one granule for one row, run by the row's 8 lanes
-// (lane l of the group holds the weights w[0..16) of ids 16 l .. 16 l + 15):
-// the first id whose running sum (ids in order) exceeds u * total; if
-// rounding leaves none, the last id of positive weight.  Returns, identical
-// in the 8 lanes, the id within the granule (-1 if the granule has no
-// weight), its weight and the total.  Kept short (it runs on every
-// workgroup's path between the tokens and its partials): the lane's own
-// running sums are formed once, the target's place among them is a count,
-// and the cross-lane steps are DPP moves within the group (a Kogge-Stone
-// running sum over the lane totals, masked at the group's start; butterfly
-// sums for the total and for the chosen weight, which only one lane holds).
-constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114;
-__device__ inline int granule_inside_draw(const float (&w)[16], float u, float& w_out, float& total)
-{
-    const int l = threadIdx.x & 7;
-    float pre[16];  // the lane's running sums, ids in order
-    float ts = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        ts += w[j];
-        pre[j] = ts;
-    }
-    float incl = ts;
-    {
-        const float t1 = dpp_f<DPP_ROW_SHR1>(incl);
-        if (l >= 1) incl += t1;
-        const float t2 = dpp_f<DPP_ROW_SHR2>(incl);
-        if (l >= 2) incl += t2;
-        const float t4 = dpp_f<DPP_ROW_SHR4>(incl);
-        if (l >= 4) incl += t4;
-    }
-    float ex = dpp_f<DPP_ROW_SHR1>(incl);
-    if (l == 0) ex = 0.0f;
-    total = oct_sum(ts);
-    // within the lane's share [ex, incl) (consecutive shares meet exactly),
-    // the first id whose running sum passes the target: the number of ids
-    // whose running sum does not (those of zero weight never pass first)
-    const float target = u * total;
-    const bool mine = ts > 0.0f && ex <= target && target < incl;
-    const float r = target - ex;
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) cnt += pre[j] <= r ? 1 : 0;
-    const int cj = mine ? min(cnt, 15) : -1;
-    float wc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) wc = j == cj ? w[j] : wc;
-    const int cand = oct_max_i(cj >= 0 ? 16 * l + cj : -1);
-    // group-uniform (the fallback's DPP moves stay inside the group)
-    const bool redo = cand < 0 || oct_max_i(mine && wc <= 0.0f ? 1 : 0) > 0;
-    if (__builtin_expect(redo, 0)) {
-        // rounding: the target at or past the last share, or on a zero
-        // weight at the share's end; the last id with positive weight
-        int lj = -1;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) lj = w[j] > 0.0f ? j : lj;
-        float wl = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) wl = j == lj ? w[j] : wl;
-        const int last = oct_max_i(lj >= 0 ? 16 * l + lj : -1);
-        const bool hold = last >= 0 && (last >> 4) == l;
-        w_out = oct_sum(hold ? wl : 0.0f);
-        return last;
-    }
-    w_out = oct_sum((cand >> 4) == l ? wc : 0.0f);
-    return cand;
-}
-// Race key of a granule: log2 of its mass in 2^(c z) units minus the race
-// term; -inf for a granule without weight.
-__device__ inline float race_key(float m, float total, float c, float term)
-{
-    return (total > 0.0f && m > -INFINITY) ? __fsub_rn(__fadd_rn(__fmul_rn(c, m), log2f(total)), term) : -INFINITY;
-}
-
 // Instantiations of the rank-dependent kernels: bf16 weights use r/16 k-steps
 // (4, 8, 16 or 32 held; fewer real steps multiply zeros), fp32 weights r/8
 // groups of four k-steps (2, 8 or 32 held).

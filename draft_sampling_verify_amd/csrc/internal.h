@@ -91,43 +91,37 @@ inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence,
 // copies (every workgroup polls them).
 constexpr int FUSED_MAX_R = 32;
 constexpr int FUSED_TOKEN_COPIES = 64;
-constexpr int FUSED_PART_WORDS = 10;  // per (request, granule), for odd and even positions: max, sum,
-                                      // argmax or candidate, race key, candidate weight
+constexpr int FUSED_PART_WORDS = 3;  // per (request, granule): max, sum, argmax
 
 struct ProposeWs {
     float2* gstat;    // [R, n_gran] per-position kernels
     int32_t* gidx;    // [R, n_gran]
     uint64_t* part;   // [FUSED_PART_WORDS][R][n_gran] fused: tagged partials (R <= FUSED_MAX_R), else null
     uint64_t* words;  // [FUSED_TOKEN_COPIES, 32] fused: tagged token words
-    float2* gstat_all;  // [R, gamma, n_gran] fused, sampled: (max, sum) of every position
-    float* wx_all;      // [R, gamma, n_gran] fused, sampled: candidate weights of every position
 };
 
-inline ProposeWs carve_propose(void* ws, int R, int gamma, int V, size_t* bytes)
+// Propose regions start at `start` bytes (the header by default; after the
+// verify regions in spec_decode_rounds, so that the tagged hand-over words
+// never share memory with other data).  *bytes = the end offset.
+inline ProposeWs carve_propose(void* ws, int R, int V, size_t* bytes, size_t start = WS_HEADER)
 {
     const size_t ng = (size_t)n_granules(V);
     Carver c(ws);
+    c.off = start;
     ProposeWs w{};
     w.gstat = c.take<float2>((size_t)R * ng);
     w.gidx = c.take<int32_t>((size_t)R * ng);
     if (R <= FUSED_MAX_R) {
         w.part = c.take<uint64_t>((size_t)R * ng * FUSED_PART_WORDS);
         w.words = c.take<uint64_t>((size_t)FUSED_TOKEN_COPIES * 32);
-        w.gstat_all = c.take<float2>((size_t)R * gamma * ng);
-        w.wx_all = c.take<float>((size_t)R * gamma * ng);
     }
     if (bytes) *bytes = c.off;
     return w;
 }
 
-// Process-wide switch: 0 keeps the propose on the per-position kernels even
-// where the fused launch fits (returns the previous value).
-int set_propose_fused(int enable);
-int propose_fused_enabled();
-// Process-wide switch: 0 keeps the verify sweep on the register-staged
-// kernel even where the pipelined direct-to-LDS one applies.
-int set_sweep_lds(int enable);
-int sweep_lds_enabled();
+// Kernel-path choices of one call (the SPEC_PATH_* bits of spec.h).
+constexpr int PATH_NO_FUSED_PROPOSE = 1;    // per-position propose kernels even where the fused launch fits
+constexpr int PATH_NO_PIPELINED_SWEEP = 2;  // staged verify sweep even where the pipelined one applies
 
 // Arguments common to the draft-side kernels.
 struct DraftArgs {
@@ -142,10 +136,12 @@ struct DraftArgs {
     int greedy;
     uint64_t seed, round;
     uint32_t* status;
+    int path;          // PATH_* bits
 };
 
 // propose.hip
-hipError_t launch_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, hipStream_t s);
+// rv: W2 given as [r, V] instead of [V, r]
+hipError_t launch_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, bool rv, hipStream_t s);
 inline size_t packed_w2_bytes(int w_dtype, int r, int V)
 {
     return (size_t)((V + 31) / 32) * 32 * (size_t)r * (w_dtype == 1 ? 2 : 4);

@@ -26,7 +26,15 @@ namespace spec {
 
 // ------------------------------------------------------------ W2 packing
 
-__global__ void k_pack_w2_bf16(const uint16_t* W2, int r, int V, int ks, uint4* out, size_t total)
+// Element (v, i) of W2: stored [V, r] (a linear layer's weight, rv = false)
+// or [r, V] (the page's formula as written, rv = true).
+template <typename T>
+__device__ inline T w2_at(const T* W2, int r, int V, int v, int i, bool rv)
+{
+    return rv ? W2[(size_t)i * V + v] : W2[(size_t)v * r + i];
+}
+
+__global__ void k_pack_w2_bf16(const uint16_t* W2, int r, int V, int ks, bool rv, uint4* out, size_t total)
 {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total) return;
@@ -35,10 +43,21 @@ __global__ void k_pack_w2_bf16(const uint16_t* W2, int r, int V, int ks, uint4* 
     const int s = (int)(bs % ks);
     const int b = (int)(bs / ks);
     const int v = 32 * b + (l & 31), h = l >> 5;
-    out[idx] = v < V ? *reinterpret_cast<const uint4*>(W2 + (size_t)v * r + 16 * s + 8 * h) : make_uint4(0, 0, 0, 0);
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (v < V) {
+        if (!rv) {
+            o = *reinterpret_cast<const uint4*>(W2 + (size_t)v * r + 16 * s + 8 * h);
+        } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = w2_at(W2, r, V, v, 16 * s + 8 * h + j, true);
+            o = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+        }
+    }
+    out[idx] = o;
 }
 
-__global__ void k_pack_w2_f32(const float* W2, int r, int V, int ks, float4* out, size_t total)
+__global__ void k_pack_w2_f32(const float* W2, int r, int V, int ks, bool rv, float4* out, size_t total)
 {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total) return;
@@ -49,25 +68,26 @@ __global__ void k_pack_w2_f32(const float* W2, int r, int V, int ks, float4* out
     const int v = 32 * b + (l & 31), h = l >> 5;
     float4 o = make_float4(0, 0, 0, 0);
     if (v < V) {
-        const float* row = W2 + (size_t)v * r + 8 * tq + h;
-        o = make_float4(row[0], row[2], row[4], row[6]);
+        const int i0 = 8 * tq + h;
+        o = make_float4(w2_at(W2, r, V, v, i0, rv), w2_at(W2, r, V, v, i0 + 2, rv), w2_at(W2, r, V, v, i0 + 4, rv),
+                        w2_at(W2, r, V, v, i0 + 6, rv));
     }
     out[idx] = o;
 }
 
-hipError_t launch_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, hipStream_t s)
+hipError_t launch_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, bool rv, hipStream_t s)
 {
     const int nblk = (V + 31) / 32;
     if (w_dtype == 1) {
         const int ks = r / 16;
         const size_t total = (size_t)nblk * ks * WAVE;
         hipLaunchKernelGGL(k_pack_w2_bf16, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                           (const uint16_t*)W2, r, V, ks, (uint4*)W2p, total);
+                           (const uint16_t*)W2, r, V, ks, rv, (uint4*)W2p, total);
     } else {
         const int ks = r / 8;
         const size_t total = (size_t)nblk * ks * WAVE;
         hipLaunchKernelGGL(k_pack_w2_f32, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                           (const float*)W2, r, V, ks, (float4*)W2p, total);
+                           (const float*)W2, r, V, ks, rv, (float4*)W2p, total);
     }
     return hipGetLastError();
 }
@@ -89,7 +109,7 @@ struct TileArgs {
     int n_chunks;  // chunks of row blocks
     int bpc;       // row blocks per chunk
     float2* gstat; // [nrows, n_gran]
-    int32_t* gidx; // [nrows, n_gran] argmax (greedy)
+    int32_t* gidx; // [nrows, n_gran]
     uint32_t* status;
 };
 
@@ -106,7 +126,6 @@ __device__ inline void draft_row(const TileArgs& p, int row, int& req, int& kk, 
     tok = kk == 0 ? p.x0[req] : p.x[(size_t)req * p.gamma + kk - 1];
 }
 
-// Per (row, granule): max and sum of weights; greedy adds the argmax.
 template <typename WT, int KS, bool GREEDY>
 __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 {
@@ -201,48 +220,50 @@ struct PickArgs {
     const void* W2p;
     const int32_t* x0;
     int32_t* x;  // [R, gamma]; position k is written, k-1 is read
-    int gamma, r, V;
+    int R, gamma, r, V;
     float c;
     int k;       // 1-based position
     int n_gran;
     uint64_t seed, round;
-    const float2* gstat;  // [R, n_gran] (max, sum)
-    const int32_t* gidx;  // [R, n_gran] argmax (greedy)
+    const float2* gstat;
+    const int32_t* gidx;
     float* pd_x;
     float* pd_stats;
 };
 
-// One workgroup per request merges the granule partials of its row: M and
-// S (fp64 across granules; thread t owns the contiguous granules [g0, g1)),
-// then the token: greedy, the smallest argmax id at M; sampled, the
-// two-level draw, with the race keys computed here (one Philox block per
-// four granules) and the inside draw over the winning granule only, whose
-// 128 logits wave w recomputes (column block w) on MFMA with U added.
+// One workgroup of four waves per request.  Everything that does not depend
+// on the drawn granule is loaded first (the previous token, this request's
+// W1 row, its granule partials); every wave then merges the partials and
+// locates the granule (identical results), wave w recomputes column block w
+// of that granule on MFMA with U added, and wave 0 picks the id.
+constexpr int PICK_CACHE = 32;  // granule partials held in registers per lane
+
 template <typename WT, int KS, bool GREEDY>
 __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
 {
     const int q = blockIdx.x;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
-    constexpr int NW = TILE_THREADS / WAVE;
-    __shared__ float s_f[NW], s_k[NW];
-    __shared__ double s_d[NW];
-    __shared__ int s_i[NW];
-    __shared__ float zrow[GRAN];
+    const int n = lane & 31, h = lane >> 5;
     const size_t o = (size_t)q * p.gamma + (p.k - 1);
-    const size_t ro = (size_t)q * p.n_gran;
-    const float2* gs = p.gstat + ro;
-    const int per = (p.n_gran + TILE_THREADS - 1) / TILE_THREADS;
-    const int g0 = min(t * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
+    const int ks = k_steps<WT>(p.r);
+    const int nblk = (p.V + 31) / 32;
+    __shared__ float zrow[GRAN];
+
+    // independent loads first
+    const float2* gs = p.gstat + (size_t)q * p.n_gran;
+    const int per = (p.n_gran + WAVE - 1) / WAVE;
+    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
+    float2 gc[PICK_CACHE];
+#pragma unroll
+    for (int i = 0; i < PICK_CACHE; ++i) gc[i] = (g0 + i < g1) ? gs[g0 + i] : make_float2(-INFINITY, 0.0f);
     const int tok = p.k == 1 ? p.x0[q] : p.x[(size_t)q * p.gamma + p.k - 2];
     const bool ok = tok >= 0 && tok < p.V;
-    // B operand of the rescan: only this request's W1 row (column n == q's
-    // slot); a matrix-core output element depends only on its own row and
-    // column operands
-    const int n = lane & 31, h = lane >> 5, nq = q & (BLOCK_ROWS - 1);
-    const int ks = k_steps<WT>(p.r);
+    // B operand: only this request's W1 row (column n == q's slot); a matrix
+    // core output element depends only on its own row and column operands
+    const int nq = q & (BLOCK_ROWS - 1);
     TileOps<WT, KS> A;
     typename TileOps<WT, KS>::BRow brow;
-    if (!GREEDY) brow.load(reinterpret_cast<const WT*>(p.W1), p.r, (ok && n == nq) ? tok : -1, ks, lane);
+    brow.load(reinterpret_cast<const WT*>(p.W1), p.r, (ok && n == nq) ? tok : -1, ks, lane);
     if (!ok) {
         if (t == 0) {
             p.x[o] = -1;
@@ -252,115 +273,111 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         }
         return;
     }
+    // merge the granule partials: M = max, w_g = S_g 2^((M_g - M) c); the
+    // first PICK_CACHE granules of each lane come from registers
     float m = -INFINITY;
-    for (int g = g0; g < g1; ++g) m = fmaxf(m, gs[g].x);
-    m = wave_max(m);
-    if (lane == 0) s_f[w] = m;
-    __syncthreads();
-    float M = s_f[0];
 #pragma unroll
-    for (int v = 1; v < NW; ++v) M = fmaxf(M, s_f[v]);
-    double ts = 0.0;
-    for (int g = g0; g < g1; ++g) ts += (double)(gs[g].y * softw(gs[g].x, M, p.c));
-    ts = wave_sum(ts);
-    float bk = -INFINITY;
-    int bg = 0x7fffffff;
-    if (GREEDY) {
-        for (int g = g0; g < g1; ++g)
-            if (gs[g].x == M) bg = min(bg, p.gidx[ro + g]);
-        bg = wave_min(bg);
-    } else {
-        // race keys, ties to the smaller granule
-        for (int g = g0; g < g1;) {
-            const int quad = g >> 2;
-            const u32x4 P = philox(0x80000000u | ((uint32_t)p.k << 20) | (uint32_t)quad, (uint32_t)q, p.round,
-                                   p.seed);
-            for (; g < g1 && (g >> 2) == quad; ++g) {
-                const float2 v = gs[g];
-                const int i = g & 3;
-                const uint32_t wd = i == 0 ? P.w[0] : i == 1 ? P.w[1] : i == 2 ? P.w[2] : P.w[3];
-                const float kv = race_key(v.x, v.y, p.c, race_term(wd));
-                if (kv > bk) {
-                    bk = kv;
-                    bg = g;
-                }
-            }
-        }
+    for (int i = 0; i < PICK_CACHE; ++i) m = fmaxf(m, gc[i].x);
+    for (int g = g0 + PICK_CACHE; g < g1; ++g) m = fmaxf(m, gs[g].x);
+    const float M = wave_max(m);
+    const float c = p.c;
+    // sums across granules in fp64 (a lane owns up to 2048 granules)
+    float wv[PICK_CACHE];
+    double tsum = 0.0;
 #pragma unroll
-        for (int off = WAVE / 2; off > 0; off >>= 1) {
-            const float ov = shfl_xor(bk, off);
-            const int og = shfl_xor(bg, off);
-            if (ov > bk || (ov == bk && og < bg)) {
-                bk = ov;
-                bg = og;
-            }
-        }
+    for (int i = 0; i < PICK_CACHE; ++i) {
+        wv[i] = gc[i].y * softw(gc[i].x, M, c);  // padding: 0 * 0
+        tsum += (double)wv[i];
     }
-    if (lane == 0) {
-        s_d[w] = ts;
-        s_i[w] = bg;
-        s_k[w] = bk;
-    }
-    __syncthreads();
-    double Sd = 0.0;
-    float kb = s_k[0];
-    int gb = s_i[0];
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-        Sd += s_d[v];
-        if (GREEDY) {
-            gb = min(gb, s_i[v]);
-        } else if (v > 0 && (s_k[v] > kb || (s_k[v] == kb && s_i[v] < gb))) {
-            kb = s_k[v];
-            gb = s_i[v];
-        }
-    }
+    for (int g = g0 + PICK_CACHE; g < g1; ++g) tsum += (double)(gs[g].y * softw(gs[g].x, M, c));
+    const double incl = wave_incl_scan(tsum);
+    double excl = __shfl_up(incl, 1, WAVE);
+    if (lane == 0) excl = 0.0;
+    const double Sd = __shfl(incl, WAVE - 1, WAVE);
     const float S = (float)Sd;
+
     if (GREEDY) {
-        if (t == 0) {
-            p.x[o] = gb == 0x7fffffff ? -1 : gb;
-            p.pd_x[o] = 1.0f / S;
-            p.pd_stats[2 * o] = M;
-            p.pd_stats[2 * o + 1] = S;
+        if (w != 0) return;
+        int cand = 0x7fffffff;
+        for (int g = g0; g < g1; ++g)
+            if (gs[g].x == M) { cand = p.gidx[(size_t)q * p.n_gran + g]; break; }
+        const int best = wave_min(cand);
+        if (lane == 0) {
+            const bool mass = S > 0.0f && best != 0x7fffffff;  // a row of -inf logits has no argmax
+            p.x[o] = mass ? best : -1;
+            p.pd_x[o] = mass ? 1.0f / S : NAN;
+            p.pd_stats[2 * o] = mass ? M : NAN;
+            p.pd_stats[2 * o + 1] = mass ? S : NAN;
         }
         return;
     }
-    if (!(kb > -INFINITY)) {  // no granule holds weight
+    if (!(S > 0.0f)) {  // no probability mass (every logit -inf, or NaN): no sample
         if (t == 0) {
             p.x[o] = -1;
             p.pd_x[o] = NAN;
-            p.pd_stats[2 * o] = M;
-            p.pd_stats[2 * o + 1] = S;
+            p.pd_stats[2 * o] = NAN;
+            p.pd_stats[2 * o + 1] = NAN;
         }
         return;
     }
-    // the winning granule's weights, relative to its own maximum (no
-    // underflow however far below M it lies), then the inside draw
-    const int gstar = gb;
-    const float mg = gs[gstar].x;
-    {
-        const int nblk = (p.V + 31) / 32;
-        const int b = 4 * gstar + w;
-        float uv[16];
-        load_acc16(p.U + ((size_t)q * p.gamma + (p.k - 1)) * p.V, gstar * GRAN + 32 * w, h, p.V, (p.V % 4) == 0,
-                   uv);
-        A.load_a(p.W2p, ks, b, b < nblk, lane);
-        const f32x16 acc = A.mfma_row(brow, ks);
-        if (n == nq) {
+
+    const float u = u24f(philox((uint32_t)p.k, (uint32_t)q, p.round, p.seed).w[0]);
+    const double target_d = (double)u * Sd;
+    const float target = (float)target_d;
+    // first granule of positive mass whose running sum exceeds target
+    double run = excl, prev = excl;
+    int pick = -1, lastpos = -1;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] = softw(uv[j] + acc[j], mg, p.c);
+    for (int i = 0; i < PICK_CACHE; ++i) {
+        if (wv[i] > 0.0f) lastpos = g0 + i;
+        if (pick < 0) {
+            prev = run;
+            run += (double)wv[i];
+            if (run > target_d && wv[i] > 0.0f) pick = g0 + i;
         }
+    }
+    for (int g = g0 + PICK_CACHE; g < g1; ++g) {
+        const float wg = gs[g].y * softw(gs[g].x, M, c);
+        if (wg > 0.0f) lastpos = g;
+        if (pick < 0) {
+            prev = run;
+            run += (double)wg;
+            if (run > target_d && wg > 0.0f) pick = g;
+        }
+    }
+    const unsigned long long hit = __ballot(pick >= 0);
+    bool fallback;
+    float before;
+    int gstar;
+    if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        fallback = false;
+        before = (float)__shfl(prev, L, WAVE);
+        gstar = __shfl(pick, L, WAVE);
+    } else {
+        fallback = true;
+        before = 0.0f;
+        const int lp = -wave_min(-lastpos);
+        gstar = lp < 0 ? 0 : lp;
+    }
+
+    // column block w of granule gstar for q's row (same operands as the tile)
+    const int b = 4 * gstar + w;
+    float uv[16];
+    load_acc16(p.U + ((size_t)q * p.gamma + (p.k - 1)) * p.V, gstar * GRAN + 32 * w, h, p.V, (p.V % 4) == 0, uv);
+    A.load_a(p.W2p, ks, b, b < nblk, lane);
+    const f32x16 acc = A.mfma_row(brow, ks);
+    if (n == nq) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) zrow[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)] = softw(uv[j] + acc[j], M, c);
     }
     __syncthreads();
     if (w != 0) return;
-    const float ea = zrow[2 * lane], eb = zrow[2 * lane + 1];
-    const float tot = wave_sum(ea + eb);
-    const float u = u24f(block_word(false, p.k, q, gstar, p.round, p.seed));
     float e;
-    const int col = granule_pick(ea, eb, 0.0f, u * tot, false, e);
+    const int col = granule_pick(zrow[2 * lane], zrow[2 * lane + 1], before, target, fallback, e);
     if (lane == 0) {
         p.x[o] = gstar * GRAN + col;
-        p.pd_x[o] = e * softw(mg, M, p.c) / S;
+        p.pd_x[o] = e / S;
         p.pd_stats[2 * o] = M;
         p.pd_stats[2 * o + 1] = S;
     }
@@ -374,16 +391,13 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
 // call (W2 is read from HBM once instead of once per position) and, per
 // position k:
 //   tile  z = U_k + W1[x_{k-1}] W2^T for its 128 ids and every request on
-//         MFMA, then per request the granule's max and sum of weights, and
-//         either its argmax (greedy) or its candidate of the inside draw,
-//         race key and candidate weight (sampled), stored with a tag naming
-//         (call, k);
-//   pick  for request q = g (and g + n_gran, ...): poll q's race keys and
-//         candidates of all granules until every tag reads k (the values
-//         arrive with the poll), take the winner's candidate and send it
-//         out as a tagged word, which the next tile phase polls; then merge
-//         (M, S) and p_d(x) off the critical path (greedy: merge the maxima
-//         and take the smallest argmax id).
+//         MFMA, then per request the granule's (max, sum of weights) or
+//         (max, argmax), stored with a tag naming (call, k);
+//   pick  for request q = g (and g + n_gran, ...): poll q's partials of all
+//         granules until every tag reads k (the values arrive with the
+//         poll), merge, draw, recompute the chosen granule on MFMA with the
+//         tile's own operands (bit-identical logits) and pick the id; the
+//         token goes out as a tagged word, which the next tile phase polls.
 // Hand-over values use agent-scope atomic stores and loads (common.h).
 // Tags carry a per-workspace call counter, so nothing needs clearing
 // between calls; every wait is bounded.
@@ -394,11 +408,8 @@ struct FusedArgs {
     int32_t* x;            // [R, gamma]
     float* pd_x;           // [R, gamma]
     float* pd_stats;       // [R, gamma, 2]
-    uint64_t* part;        // [FUSED_PART_WORDS][R][n_gran] tagged partials: max, sum, argmax (greedy) or
-                           // candidate, race key, candidate weight (sampled)
+    uint64_t* part;        // [FUSED_PART_WORDS][R][n_gran] tagged partials: max, sum, argmax
     uint64_t* words;       // [FUSED_TOKEN_COPIES, 32] tagged token words
-    float2* gstat_all;     // (sampled) [R, gamma, n_gran] (max, sum) of every position
-    float* wx_all;         // (sampled) [R, gamma, n_gran] candidate weight of every position
     uint32_t* epoch;       // calls so far on this workspace
     uint32_t* abort_flag;  // abort_word(epoch) of a call that gave up waiting
 };
@@ -407,13 +418,15 @@ constexpr int SPIN_LIMIT = 1 << 20;     // polls before a wait is declared faile
 constexpr int ABORT_EVERY = 32;         // polls between looks at the (single, shared) abort word
 constexpr uint32_t DEV_WAIT_FAILED = 8u;
 constexpr int FUSED_PER = 4;            // granules per thread in the merge: n_gran <= 1024
-constexpr int PART_PLANES = 5;          // planes of partials per parity of k: max, sum, argmax/candidate, key, weight
 
-// Tag of (call, position): the fixed high byte keeps it apart from any float
-// or id that other calls leave in the workspace.
+// Tag of (call, position), k = 1..64: the low 25 bits of the call counter
+// and k.  The hand-over regions hold nothing but tagged words (the workspace
+// is zeroed at initialisation, and 0 is no tag), so a word can only match a
+// tag if this call wrote it, or if a call 2^25 calls earlier wrote the same
+// word and nothing has overwritten it since.
 __device__ inline uint32_t call_tag(uint32_t epoch, int k)
 {
-    return 0x5A000000u | ((epoch & 0xFFFFu) << 7) | (uint32_t)k;
+    return ((epoch & 0x1FFFFFFu) << 7) | (uint32_t)k;
 }
 // What a call that gives up leaves in the abort word: never 0 (the value of
 // a fresh workspace) and distinct for every epoch below 2^31.
@@ -462,7 +475,9 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
     __shared__ float s_red[TILE_THREADS / WAVE];
     __shared__ int s_ired[TILE_THREADS / WAVE];
     __shared__ float s_wtot[TILE_THREADS / WAVE];
-    __shared__ int s_cand[TILE_THREADS / WAVE];
+    __shared__ int s_cand[TILE_THREADS / WAVE], s_last[TILE_THREADS / WAVE];
+    __shared__ float s_cbefore[TILE_THREADS / WAVE];
+    __shared__ float zrow[GRAN];
     __shared__ int s_prev[FUSED_MAX_R];  // previous token of each request this workgroup picks
 
     for (int j = threadIdx.x; g + j * NG < R; j += TILE_THREADS) {
@@ -531,17 +546,6 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
         const int cbase = g * GRAN + ec;
         const uint32_t tag = call_tag(epoch, k);
 
-        // the uniforms of this granule's inside draw and race for row er
-        // (they do not depend on the tokens: computed before the wait)
-        float u_in = 0.0f, rterm = 0.0f;
-        if (!GREEDY) {
-            const int j8 = t & 7;
-            uint32_t wd = 0u;
-            if (j8 < 2 && er < R) wd = block_word(j8 == 0, k, er, g, f.round, f.seed);
-            rterm = race_term(__shfl(wd, lane & ~7, WAVE));
-            u_in = u24f(__shfl(wd, (lane & ~7) + 1, WAVE));
-        }
-
         // ---------------- tile phase
         int tok = -1;
         if (k == 1) {
@@ -602,135 +606,35 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
             }
             m = oct_max(m);
             const float ms = safe_ref(m);
-            float s = 0.0f, wx = 0.0f, key = -INFINITY;
-            int cand = -1;
-            if (GREEDY) {
+            float s = 0.0f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s += softw(z[j], ms, p.c);
-                s = oct_sum(s);
-                oct_argmax(bv, bi);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) z[j] = softw(z[j], ms, p.c);  // weights, in place
-                const int id = granule_inside_draw(z, u_in, wx, s);
-                cand = id >= 0 ? g * GRAN + id : -1;
-                key = race_key(m, s, p.c, rterm);
-            }
+            for (int j = 0; j < 16; ++j) s += softw(z[j], ms, p.c);
+            s = oct_sum(s);
+            if (GREEDY) oct_argmax(bv, bi);
             if ((t & 7) == 0 && valid) {
-                // partials as arrays [R][n_gran], so that a poll reads them
-                // granule-contiguous: greedy, max, sum and argmax; sampled,
-                // the race key and the candidate.  Positions of odd and even
-                // k use separate planes.
+                // partials as three arrays [R][n_gran] (max, sum, argmax), so
+                // that a poll reads them granule-contiguous
                 const size_t o = (size_t)er * NG + g, plane = (size_t)R * NG;
-                uint64_t* pk = f.part + (size_t)(k & 1) * PART_PLANES * plane;
-                if (GREEDY) {
-                    st_dev(pk + o, tagged(__float_as_uint(m), tag));
-                    st_dev(pk + plane + o, tagged(__float_as_uint(s), tag));
-                    st_dev(pk + 2 * plane + o, tagged((uint32_t)bi, tag));
-                } else {
-                    st_dev(pk + 3 * plane + o, tagged(__float_as_uint(key), tag));
-                    st_dev(pk + 2 * plane + o, tagged((uint32_t)cand, tag));
-                    // (max, sum) and the candidate's weight for the statistics
-                    // kernel that follows this launch: plain stores
-                    const size_t so = ((size_t)er * p.gamma + (k - 1)) * NG + g;
-                    f.gstat_all[so] = make_float2(m, s);
-                    f.wx_all[so] = wx;
-                }
+                st_dev(f.part + o, tagged(__float_as_uint(m), tag));
+                st_dev(f.part + plane + o, tagged(__float_as_uint(s), tag));
+                if (GREEDY) st_dev(f.part + 2 * plane + o, tagged((uint32_t)bi, tag));
             }
         }
         __syncthreads();          // the tile's reads are complete
         if (k < p.gamma) park_next(k);
 
-        // ---------------- pick phase
+        // ---------------- pick phase (W2 registers are free here: reloaded below)
         if (g < R) {
             int j = 0;
             for (int q = g; q < R; q += NG, ++j) {
                 const size_t o = (size_t)q * p.gamma + (k - 1);
-                const size_t plane = (size_t)R * NG;
-                const uint64_t* rm = opaque(f.part) + (size_t)(k & 1) * PART_PLANES * plane + (size_t)q * NG;
-                const bool live = s_prev[j] >= 0;
-                if (!GREEDY) {
-                    // the race: key and candidate of every granule, polled
-                    // until all carry this position; thread t reads granules
-                    // 4t .. 4t+3 and keeps the best (ties: smaller granule)
-                    int xk = -1;
-                    if (live) {
-                        float bk;
-                        int bg, bt;
-                        for (int spin = 0;; ++spin) {
-                            bool ok = true;
-                            bk = -INFINITY;
-                            bg = 0x7fffffff;
-                            bt = -1;
-#pragma unroll
-                            for (int i = 0; i < FUSED_PER; ++i) {
-                                const int gg = FUSED_PER * t + i;
-                                if (gg < NG) {
-                                    const uint64_t a3 = ld_dev(rm + 3 * plane + gg), a2 = ld_dev(rm + 2 * plane + gg);
-                                    ok &= tag_of(a3) == tag && tag_of(a2) == tag;
-                                    const float kv = __uint_as_float((uint32_t)a3);
-                                    if (kv > bk) {
-                                        bk = kv;
-                                        bg = gg;
-                                        bt = (int)(uint32_t)a2;
-                                    }
-                                }
-                            }
-                            const bool ab = look_abort(spin) && ld_dev(f.abort_flag) == abort_word(epoch);
-                            if (__syncthreads_and(ok)) break;
-                            if (poll_failed<1>(spin, ab, epoch, f.abort_flag, p.status)) {
-                                failed = true;
-                                break;
-                            }
-                        }
-                        if (failed) break;
-#pragma unroll
-                        for (int off = WAVE / 2; off > 0; off >>= 1) {
-                            const float ov = shfl_xor(bk, off);
-                            const int og = shfl_xor(bg, off), ot = shfl_xor(bt, off);
-                            if (ov > bk || (ov == bk && og < bg)) {
-                                bk = ov;
-                                bg = og;
-                                bt = ot;
-                            }
-                        }
-                        if (lane == 0) {
-                            s_red[w] = bk;
-                            s_ired[w] = bg;
-                            s_cand[w] = bt;
-                        }
-                        __syncthreads();
-                        float kb = s_red[0];
-                        int gstar = s_ired[0];
-                        xk = s_cand[0];
-#pragma unroll
-                        for (int v = 1; v < TILE_THREADS / WAVE; ++v)
-                            if (s_red[v] > kb || (s_red[v] == kb && s_ired[v] < gstar)) {
-                                kb = s_red[v];
-                                gstar = s_ired[v];
-                                xk = s_cand[v];
-                            }
-                        if (!(kb > -INFINITY)) xk = -1;  // no granule holds weight
-                    }
-                    // the token goes out (copies in lanes 0..7); p_d(x) and
-                    // (M, S) come from the statistics kernel after the launch
-                    if (w == 0) {
-                        if (lane < FUSED_TOKEN_COPIES)
-                            st_dev(f.words + (size_t)lane * 32 + q, tagged((uint32_t)xk, tag));
-                        if (lane == 0) {
-                            s_prev[j] = xk;
-                            f.x[o] = xk;
-                        }
-                    }
-                    __syncthreads();
-                    continue;
-                }
-                // greedy: q's (max, sum, argmax) of every granule, polled
-                // until all carry this position; thread t reads granules
-                // 4t .. 4t+3
                 int xk = -1;
                 float pdx = NAN, sM = NAN, sS = NAN;
-                if (live) {
+                if (s_prev[j] >= 0) {
+                    // q's partials of every granule, polled until all carry
+                    // this position; thread t reads granules 4t .. 4t+3
+                    const size_t plane = (size_t)R * NG;
+                    const uint64_t* rm = opaque(f.part) + (size_t)q * NG;
                     float gm[FUSED_PER], gs[FUSED_PER];
                     uint32_t gi[FUSED_PER];
                     for (int spin = 0;; ++spin) {
@@ -743,7 +647,7 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                             gi[i] = 0u;
                             if (gg < NG) {
                                 const uint64_t a0 = ld_dev(rm + gg), a1 = ld_dev(rm + plane + gg);
-                                const uint64_t a2 = ld_dev(rm + 2 * plane + gg);
+                                const uint64_t a2 = GREEDY ? ld_dev(rm + 2 * plane + gg) : tagged(0u, tag);
                                 ok &= tag_of(a0) == tag && tag_of(a1) == tag && tag_of(a2) == tag;
                                 gm[i] = __uint_as_float((uint32_t)a0);
                                 gs[i] = __uint_as_float((uint32_t)a1);
@@ -758,7 +662,10 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                         }
                     }
                     if (failed) break;
-                    // the maximum M, then S and the smallest id reaching M
+                    // three barriers: the maximum M; the wave totals of the
+                    // weights (a running sum in granule order: lanes, then
+                    // waves); the first granule whose running sum passes the
+                    // target
                     float mloc = -INFINITY;
 #pragma unroll
                     for (int i = 0; i < FUSED_PER; ++i) mloc = fmaxf(mloc, gm[i]);
@@ -766,27 +673,122 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                     if (lane == 0) s_red[w] = mloc;
                     __syncthreads();
                     const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-                    float tsum = 0.0f;
+                    float wv[FUSED_PER], tsum = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < FUSED_PER; ++i) tsum += gs[i] * softw(gm[i], M, p.c);  // padding: 0 * 0
+                    for (int i = 0; i < FUSED_PER; ++i) {
+                        wv[i] = gs[i] * softw(gm[i], M, p.c);  // padding: 0 * 0
+                        tsum += wv[i];
+                    }
                     const float incl = wave_incl_scan(tsum);
+                    float exl = __shfl_up(incl, 1, WAVE);
+                    if (lane == 0) exl = 0.0f;
                     if (lane == WAVE - 1) s_wtot[w] = incl;
-                    int cnd = 0x7fffffff;
+                    if (GREEDY) {
+                        int cand = 0x7fffffff;
 #pragma unroll
-                    for (int i = 0; i < FUSED_PER; ++i)
-                        if (FUSED_PER * t + i < NG && gm[i] == M) cnd = min(cnd, (int)gi[i]);
-                    cnd = wave_min(cnd);
-                    if (lane == 0) s_ired[w] = cnd;
+                        for (int i = 0; i < FUSED_PER; ++i)
+                            if (FUSED_PER * t + i < NG && gm[i] == M) cand = min(cand, (int)gi[i]);
+                        cand = wave_min(cand);
+                        if (lane == 0) s_ired[w] = cand;
+                    }
                     __syncthreads();
-                    float S = 0.0f;
+                    float S = 0.0f, woff = 0.0f;
 #pragma unroll
-                    for (int v = 0; v < TILE_THREADS / WAVE; ++v) S += s_wtot[v];
+                    for (int v = 0; v < TILE_THREADS / WAVE; ++v) {
+                        if (v == w) woff = S;
+                        S += s_wtot[v];
+                    }
                     sM = M;
                     sS = S;
-                    xk = min(min(s_ired[0], s_ired[1]), min(s_ired[2], s_ired[3]));
-                    pdx = 1.0f / S;
+                    if (!(S > 0.0f)) {
+                        // no probability mass (every logit -inf, or NaN): no token
+                        xk = -1;
+                        sM = NAN;
+                        sS = NAN;
+                    } else if (GREEDY) {
+                        xk = min(min(s_ired[0], s_ired[1]), min(s_ired[2], s_ired[3]));
+                        pdx = 1.0f / S;
+                    } else {
+                        const float target = u24f(philox((uint32_t)k, (uint32_t)q, f.round, f.seed).w[0]) * S;
+                        // this thread's share of the running sum is
+                        // [woff + exl, woff + incl): consecutive shares meet
+                        // exactly, so at most one thread holds the target
+                        const float lo = woff + exl, hi = woff + incl;
+                        const bool hit = tsum > 0.0f && lo <= target && target < hi;
+                        int ig = -1, ilast = -1;
+                        float c = lo, cbefore = lo;
+#pragma unroll
+                        for (int i = 0; i < FUSED_PER; ++i) {
+                            if (wv[i] > 0.0f) {
+                                if (ig < 0 && c + wv[i] > target) {
+                                    ig = i;
+                                    cbefore = c;
+                                }
+                                ilast = i;
+                            }
+                            c += wv[i];
+                        }
+                        if (hit && ig < 0) {  // the share's own sum rounded below the target
+                            ig = ilast;
+                            float c2 = lo;
+#pragma unroll
+                            for (int i = 0; i < FUSED_PER; ++i)
+                                if (i < ilast) c2 += wv[i];
+                            cbefore = c2;
+                        }
+                        const unsigned long long hits = __ballot(hit);
+                        const int lastpos = wave_max_int(ilast >= 0 ? FUSED_PER * t + ilast : -1);
+                        if (hits) {
+                            if (lane == __ffsll((long long)hits) - 1) {
+                                s_cand[w] = FUSED_PER * t + ig;
+                                s_cbefore[w] = cbefore;
+                            }
+                        } else if (lane == 0) {
+                            s_cand[w] = -1;
+                        }
+                        if (lane == 0) s_last[w] = lastpos;
+                        __syncthreads();
+                        int gstar = -1;
+                        float before = 0.0f;
+#pragma unroll
+                        for (int v = TILE_THREADS / WAVE - 1; v >= 0; --v)
+                            if (s_cand[v] >= 0) {
+                                gstar = s_cand[v];
+                                before = s_cbefore[v];
+                            }
+                        const bool fallback = gstar < 0;
+                        if (fallback) gstar = max(max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])), 0);
+                        // granule gstar for q with the tile's own operands: W2
+                        // block, U_k as the starting accumulator, and sB, which
+                        // still holds this position's W1 rows (column q)
+                        {
+                            Ops A2;
+                            A2.load_a(p.W2p, ks, 4 * gstar + w, 4 * gstar + w < nblk, lane);
+                            float uq[16];
+                            load_acc16(p.U + ((size_t)q * p.gamma + (k - 1)) * p.V, gstar * GRAN + 32 * w, h, p.V,
+                                       p.vec4 != 0, uq);
+                            f32x16 acc;
+#pragma unroll
+                            for (int jj = 0; jj < 16; ++jj) acc[jj] = uq[jj];
+                            acc = A2.mfma_acc(sB, lane, acc);
+                            if (n == (q & 31)) {
+#pragma unroll
+                                for (int jj = 0; jj < 16; ++jj)
+                                    zrow[32 * w + 8 * (jj >> 2) + 4 * h + (jj & 3)] = softw(acc[jj], M, p.c);
+                            }
+                        }
+                        __syncthreads();
+                        if (w == 0) {
+                            float e;
+                            const int col = granule_pick(zrow[2 * lane], zrow[2 * lane + 1], before, target,
+                                                         fallback, e);
+                            xk = gstar * GRAN + col;
+                            pdx = e / S;
+                        }
+                    }
                 }
-                // wave 0 publishes the token and records the outputs
+                // wave 0 publishes the token (copies in lanes 0..7) and
+                // records the outputs
                 if (w == 0) {
                     if (lane < FUSED_TOKEN_COPIES) st_dev(f.words + (size_t)lane * 32 + q, tagged((uint32_t)xk, tag));
                     if (lane == 0) {
@@ -799,6 +801,9 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                 }
                 __syncthreads();
             }
+            // unconditional, so that the W2 registers are provably free
+            // during the picks (32 workgroups re-read 64 KB each)
+            if (!GREEDY) A.load_a(p.W2p, ks, 4 * g + w, 4 * g + w < nblk, lane);
         }
     }
     // the call counter advances once every workgroup has read it: workgroup
@@ -842,52 +847,6 @@ static int fused_capacity()
     return v - 1;
 }
 
-// After a sampled fused propose: (M, S) and p_d(x) of every drafted row
-// from the (max, sum) of each granule and the candidate weight of the
-// winning granule, which is the token's own (ids 128 g .. 128 g + 127).  One
-// workgroup per row f = q * gamma + k - 1; S sums in fp64 across granules.
-__global__ __launch_bounds__(TILE_THREADS) void k_propose_stats(const float2* gstat_all, const float* wx_all,
-                                                                const int32_t* x, int n_gran, float c, float* pd_x,
-                                                                float* pd_stats)
-{
-    constexpr int NW = TILE_THREADS / WAVE;
-    __shared__ float s_m[NW];
-    __shared__ double s_s[NW];
-    const int f = blockIdx.x, t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
-    const int xk = x[f];
-    if (xk < 0 || (xk >> 7) >= n_gran) {  // no token (an invalid chain, or no weight)
-        if (t == 0) {
-            pd_x[f] = NAN;
-            pd_stats[2 * (size_t)f] = NAN;
-            pd_stats[2 * (size_t)f + 1] = NAN;
-        }
-        return;
-    }
-    const float2* gs = gstat_all + (size_t)f * n_gran;
-    float m = -INFINITY;
-    for (int g = t; g < n_gran; g += TILE_THREADS) m = fmaxf(m, gs[g].x);
-    m = wave_max(m);
-    if (lane == 0) s_m[w] = m;
-    __syncthreads();
-    float M = s_m[0];
-#pragma unroll
-    for (int v = 1; v < NW; ++v) M = fmaxf(M, s_m[v]);
-    double sum = 0.0;
-    for (int g = t; g < n_gran; g += TILE_THREADS) sum += (double)(gs[g].y * softw(gs[g].x, M, c));
-    sum = wave_sum(sum);
-    if (lane == 0) s_s[w] = sum;
-    __syncthreads();
-    if (t != 0) return;
-    double Sd = 0.0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) Sd += s_s[v];
-    const float S = (float)Sd;
-    const int gstar = xk >> 7;
-    pd_x[f] = wx_all[(size_t)f * n_gran + gstar] * softw(gs[gstar].x, M, c) / S;
-    pd_stats[2 * (size_t)f] = M;
-    pd_stats[2 * (size_t)f + 1] = S;
-}
-
 template <typename WT, int KS, bool GREEDY>
 static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* x_out, float* pd_x,
                                 float* pd_stats, const ProposeWs& ws, hipStream_t s)
@@ -898,8 +857,6 @@ static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* 
     f.x = x_out; f.pd_x = pd_x; f.pd_stats = pd_stats;
     f.part = ws.part;
     f.words = ws.words;
-    f.gstat_all = ws.gstat_all;
-    f.wx_all = ws.wx_all;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(a.status);
     f.epoch = &hdr->epoch;
     f.abort_flag = &hdr->abort;
@@ -907,15 +864,8 @@ static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* 
     // once (fused_capacity), so on an otherwise free device every workgroup
     // becomes resident; waits are bounded in any case.  (A cooperative launch
     // gives the same guarantee formally but costs ~17 us per call here.)
-    {
-        ProfScope ps("propose_fused", s);
-        hipLaunchKernelGGL((k_propose_fused<WT, KS, GREEDY>), dim3(t.n_gran), dim3(TILE_THREADS), 0, s, f);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || GREEDY) return e;
-    ProfScope ps("propose_stats", s);
-    hipLaunchKernelGGL(k_propose_stats, dim3(a.R * a.gamma), dim3(TILE_THREADS), 0, s, ws.gstat_all, ws.wx_all,
-                       x_out, t.n_gran, a.c, pd_x, pd_stats);
+    ProfScope ps("propose_fused", s);
+    hipLaunchKernelGGL((k_propose_fused<WT, KS, GREEDY>), dim3(t.n_gran), dim3(TILE_THREADS), 0, s, f);
     return hipGetLastError();
 }
 
@@ -932,11 +882,10 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
     t.gstat = ws.gstat; t.gidx = ws.gidx; t.status = a.status;
     PickArgs pk{};
     pk.U = a.U; pk.W1 = a.W1; pk.W2p = a.W2; pk.x0 = a.x0; pk.x = x_out;
-    pk.V = a.V; pk.gamma = a.gamma; pk.r = a.r; pk.c = a.c;
+    pk.R = a.R; pk.gamma = a.gamma; pk.r = a.r; pk.V = a.V; pk.c = a.c;
     pk.n_gran = n_gran; pk.seed = a.seed; pk.round = a.round;
-    pk.gstat = ws.gstat; pk.gidx = ws.gidx;
-    pk.pd_x = pd_x; pk.pd_stats = pd_stats;
-    if (ws.part && propose_fused_enabled() && n_gran <= FUSED_PER * TILE_THREADS && k_steps<WT>(a.r) == KS) {
+    pk.gstat = ws.gstat; pk.gidx = ws.gidx; pk.pd_x = pd_x; pk.pd_stats = pd_stats;
+    if (ws.part && !(a.path & PATH_NO_FUSED_PROPOSE) && n_gran <= FUSED_PER * TILE_THREADS && k_steps<WT>(a.r) == KS) {
         const bool fits = a.greedy ? n_gran <= fused_capacity<WT, KS, true>()
                                    : n_gran <= fused_capacity<WT, KS, false>();
         if (fits) {

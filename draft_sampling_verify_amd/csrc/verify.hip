@@ -245,6 +245,7 @@ struct SweepArgs {
     const float2* trow;
     float2* vpart;        // [rows, n_gran] (TV mass, residual mass)
     float* vbias;         // [rows] Markov bias at the drafted id x_k
+    int staged_only;      // the call asked for the staged sweep (PATH_NO_PIPELINED_SWEEP)
 };
 
 // Verified row f: where its data lives and the normalisers of p_d and p_t.
@@ -1359,6 +1360,7 @@ static SweepArgs make_sweep(const DraftArgs& a, const float* dstats, const float
     s.trow = w.trow;
     s.vpart = w.vpart;
     s.vbias = w.vbias;
+    s.staged_only = (a.path & PATH_NO_PIPELINED_SWEEP) != 0;
     return s;
 }
 
@@ -1414,7 +1416,7 @@ static void launch_sweep(const SweepArgs& sw, hipStream_t s)
     const dim3 grid(xcd_grid(sw.n_gran * sw.n_chunks));
     const dim3 blk(TILE_THREADS);
     if constexpr (std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16 || KS == 32)) {
-        if (sw.r == 16 * KS && !sw.vmap && sweep_lds_enabled()) {
+        if (sw.r == 16 * KS && !sw.vmap && !sw.staged_only) {
             // as many workgroups as fit at once, each with one run of units
             const long units = (long)sw.n_gran * ((sw.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
             const dim3 blk2(2 * TILE_THREADS);

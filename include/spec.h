@@ -49,13 +49,11 @@
  *   Asynchrony  Calls only validate on the host and enqueue kernels on
  *               `stream` (a hipStream_t; NULL = the null stream).  Outputs are
  *               valid once the caller synchronises that stream.
- *   Randomness  Every uniform is Philox4x32-10 with key = seed.  Counter
- *               (k, request, round_lo, round_hi): word 1 is the accept test at
- *               k, word 2 the residual draw at k or the bonus draw at
- *               k = l_r + 1, word 0 the clustered head's draw;
- *               u = (w >> 8) * 2^-24.  The Markov head's draft draw takes its
- *               uniforms per 128-id block from the counters described at
- *               spec_markov_propose.  Residual and bonus draws are by inverse
+ *   Randomness  Every uniform is Philox4x32-10 with key = seed and counter =
+ *               (k, request, round_lo, round_hi); word 0 draws x_k (the Markov
+ *               head's and the clustered head's draft), word 1 is the accept
+ *               test at k, word 2 the residual draw at k or the bonus draw at
+ *               k = l_r + 1; u = (w >> 8) * 2^-24.  Every draw is by inverse
  *               CDF in vocabulary order (smallest v whose running sum exceeds
  *               u * total), so results are a pure function of (inputs, seed,
  *               round).
@@ -126,8 +124,12 @@ enum spec_device_flag {
  * Returns 0 for sizes the entry point would reject. */
 size_t spec_workspace_bytes(int op, int R, int gamma, int r, int V, int B_max);
 
-/* Zero the status word of a freshly allocated workspace (enqueued on
- * stream).  Call once after allocating a workspace. */
+/* Zero all ws_bytes of a freshly allocated workspace (enqueued on stream):
+ * the status word, the fused propose's call counter and its hand-over words.
+ * Call once after allocating a workspace, and again if the memory was used
+ * for anything else in between (a workspace is only ever valid for the
+ * library after this call).  Returns SPEC_EWORKSPACE if ws is NULL or
+ * ws_bytes < 256. */
 int spec_workspace_init(void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Bytes of the packed W2 for these sizes (0 if rejected). */
@@ -142,6 +144,20 @@ size_t spec_packed_w2_bytes(int w_dtype, int r, int V);
  * spec_packed_w2_bytes() long.  Enqueued on stream. */
 int spec_pack_w2(const void* W2, int w_dtype, int r, int V, void* W2p, spec_stream_t stream);
 
+/* spec_pack_w2 for W2 held as the page's r x V matrix (DSpark section 4,
+ * B = W1[x] W2): W2_rv [r,V] row-major, W2_rv[i*V + v] = W2[v,i].  Same W2p.
+ * W2_rv needs only its element alignment. */
+int spec_pack_w2_rv(const void* W2_rv, int w_dtype, int r, int V, void* W2p, spec_stream_t stream);
+
+/* Kernel-path choices of one call (the `path` argument of the _ex entry
+ * points; 0 = the library picks).  Every path computes the same function;
+ * they exist so that tests can run each kernel on any shape. */
+enum spec_path {
+    SPEC_PATH_AUTO = 0,
+    SPEC_PATH_NO_FUSED_PROPOSE = 1,  /* per-position propose kernels even where the fused launch fits */
+    SPEC_PATH_NO_PIPELINED_SWEEP = 2 /* staged verify sweep even where the pipelined one applies      */
+};
+
 /* Synchronise `stream`, then return the status word of `ws` in *flags (host
  * pointer; SPEC_DEV_* bits, sticky across calls).  clear != 0 zeroes it.
  * Returns SPEC_OK, or SPEC_EDEVICE when a bit is set. */
@@ -150,17 +166,13 @@ int spec_device_status(void* ws, spec_stream_t stream, int clear, int* flags);
 /* Draft gamma tokens per request with the Markov head (DSpark sections 3-4):
  *   x_0 = x0[r];  for k = 1..gamma:
  *     z_k = U[r,k-1,:] + W1[x_{k-1}] W2^T        (raw draft logits)
- *     p_k = softmax(z_k / T);  x_k ~ p_k, or argmax z_k if greedy
- * The sample is drawn exactly in two levels over blocks of 128 ids
- * (128 b .. 128 b + 127): inside every block a candidate by inverse CDF over
- * the block's own probabilities with uniform u_b, then the block that wins
- * the Gumbel-max race on the block masses P_b, argmax_b ln P_b - ln(-ln e_b)
- * (ties: smaller b), gives x_k.  u_b and e_b are word b & 3 of Philox4x32-10
- * (key = seed) at counter (0xC0000000 | k << 20 | b >> 2, r, round) and
- * (0x80000000 | k << 20 | b >> 2, r, round): u_b = (w >> 8) 2^-24,
- * e_b = ((w >> 9) + 1/2) 2^-23.  A row whose logits are all -inf (or NaN)
- * has no sample: its x_k is -1 and p_d(x) is NaN, and the next
- * position of that request raises SPEC_DEV_BAD_TOKEN.
+ *     p_k = softmax(z_k / T);  x_k ~ p_k (word 0), or argmax z_k if greedy
+ * The sample is one inverse CDF over the whole row in vocabulary order: the
+ * smallest v whose running sum of p_k exceeds u = (w0 >> 8) 2^-24, w0 =
+ * word 0 of Philox4x32-10 (key = seed) at counter (k, r, round_lo,
+ * round_hi).  A row whose logits are all -inf (or NaN) has no sample: its
+ * x_k is -1, p_d(x) and (M, S) are NaN, and the next position of that
+ * request raises SPEC_DEV_BAD_TOKEN (its later outputs are -1 / NaN too).
  * In:  U [R,gamma,V] fp32; W1 [V,r] (w_dtype); W2p = spec_pack_w2(W2);
  *      x0 [R] int32.
  * Out: x [R,gamma] int32; pd_x [R,gamma] fp32 = p_k(x_k);
@@ -174,37 +186,30 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2p, int w_d
                         int32_t* x, float* pd_x, float* pd_stats,
                         void* ws, size_t ws_bytes, spec_stream_t stream);
 
-/* Propose runs in one of two ways; tokens agree except at decisions within
- * fp32 rounding of a boundary (the logits are computed with the same
- * operands, the sums in a different order).  Fused: one launch for all gamma
- * positions; each workgroup keeps the W2 columns of one 128-id granule in
- * registers for the whole call, so W2 is read from HBM once, and workgroups
- * hand partials and tokens to each other through device memory.  It is taken
- * when every granule's workgroup fits on the device at once, r fills the
- * matrix-core k-steps exactly (r = 64, 128, 256 or 512 for bf16; 16, 64 or
- * 256 for fp32), R <= 32 and the switch below is on.  Concurrent fused calls
- * on different streams of one GPU can starve each other of workgroup slots
- * and end with SPEC_DEV_WAIT_FAILED (after about a second); issue them on one
- * stream.  Otherwise: two kernels per position (partials, then the pick), W2
- * streamed once per position.
- * spec_set_propose_fused(0) forces the per-position kernels for every later
- * call in the process (1 restores the default); returns the previous value.
- * Not synchronised with calls running in other threads. */
-int spec_set_propose_fused(int enable);
-
-/* The verify sweep (and spec_confidence's) recomputes the Markov bias of
- * every verified row in 32-row blocks.  For bf16 weights with r = 128, 256
- * or 512 and every position verified (ell == NULL, and always in
- * spec_confidence) it runs as a software pipeline: half of each workgroup
- * gathers W1 rows straight into on-chip memory one block ahead and computes
- * the bias tiles on the matrix cores, the other half streams U and target
- * rows two blocks ahead and finishes each block.  Otherwise the W1 rows are
- * staged through registers and one workgroup does each block start to end.
- * Both compute the same products in the same order (identical results).
- * spec_set_verify_lds(0) forces the staged kernel for every later call in
- * the process (1 restores the default); returns the previous value.  Not
- * synchronised with calls running in other threads. */
-int spec_set_verify_lds(int enable);
+/* spec_markov_propose with an explicit kernel path (SPEC_PATH_* bits; other
+ * bits: SPEC_EINVAL).  Propose runs in one of two ways; tokens agree except
+ * at decisions within fp32 rounding of a boundary (the logits are computed
+ * with the same operands, the sums in a different order).
+ * Fused: one launch for all gamma positions; each workgroup keeps the W2
+ * columns of one 128-id granule in registers for the whole call, so W2 is
+ * read from HBM once, and workgroups hand partials and tokens to each other
+ * through the workspace.  It is taken when every granule's workgroup fits on
+ * the device at once, r fills the matrix-core k-steps exactly (r = 64, 128,
+ * 256 or 512 for bf16; 16, 64 or 256 for fp32), R <= 32 and path does not
+ * hold SPEC_PATH_NO_FUSED_PROPOSE.  Its workgroups wait for one another, so
+ * they must all run at once: a fused call shares the GPU safely with work
+ * queued before or after it on its stream, but kernels running at the same
+ * time on other streams or in other processes can take the slots some of
+ * its workgroups need.  Every wait is bounded: after about 2^20 polls (a
+ * second or more) the call gives up, its workgroups exit, its outputs are
+ * undefined and SPEC_DEV_WAIT_FAILED is raised; the next call on the same
+ * workspace is unaffected.  Otherwise: two kernels per position (partials,
+ * then the pick), W2 streamed once per position. */
+int spec_markov_propose_ex(const float* U, const void* W1, const void* W2p, int w_dtype,
+                           const int32_t* x0, int R, int gamma, int r, int V, float T,
+                           int greedy, uint64_t seed, uint64_t round,
+                           int32_t* x, float* pd_x, float* pd_stats, int path,
+                           void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Several speculative rounds back to back on the device: the loop around
  * one step.  Round i (Philox round round0 + i) drafts gamma tokens from the
@@ -229,6 +234,12 @@ int spec_decode_rounds(const float* U, const void* W1, const void* W2p, int w_dt
                        float T, int greedy, uint64_t seed, uint64_t round0, int n_rounds,
                        int32_t* anchors, int32_t* x, int32_t* n_acc, int32_t* y, float* c_star,
                        void* ws, size_t ws_bytes, spec_stream_t stream);
+/* spec_decode_rounds with an explicit kernel path (SPEC_PATH_* bits). */
+int spec_decode_rounds_ex(const float* U, const void* W1, const void* W2p, int w_dtype,
+                          const int32_t* x0, const float* Lt, int R, int gamma, int r, int V,
+                          float T, int greedy, uint64_t seed, uint64_t round0, int n_rounds,
+                          int32_t* anchors, int32_t* x, int32_t* n_acc, int32_t* y, float* c_star,
+                          int path, void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Verify drafts against target logits (standard lossless rule):
  *   for k = 1..l_r: accept x_k iff u1 < p_t,k(x_k) / p_k(x_k) (greedy: iff
@@ -243,7 +254,8 @@ int spec_decode_rounds(const float* U, const void* W1, const void* W2p, int w_dt
  *      y [R,gamma+1] int32 = x_1..x_{n_acc}, correction or bonus, then -1;
  *      pt_x [R,gamma] fp32 = p_t,k(x_k) (optional, NULL to skip);
  *      c_star [R,gamma] fp32 = 1 - 1/2 ||p_k - p_t,k||_1 clamped to [0,1]
- *      (optional; NULL skips the full-row sweep of accepted positions).
+ *      (optional; the sweep that forms the residual masses forms the TV
+ *      masses too, so NULL only skips writing them).
  * Entries past l_r are NaN (pt_x, c_star). */
 int spec_verify(const float* U, const void* W1, const void* W2p, int w_dtype,
                 const int32_t* x0, const int32_t* x, const float* pd_stats,
@@ -252,6 +264,24 @@ int spec_verify(const float* U, const void* W1, const void* W2p, int w_dtype,
                 uint64_t seed, uint64_t round,
                 int32_t* n_acc, int32_t* y, float* pt_x, float* c_star,
                 void* ws, size_t ws_bytes, spec_stream_t stream);
+
+/* spec_verify with an explicit kernel path (SPEC_PATH_* bits).  The sweep
+ * recomputes the Markov bias of every verified row in 32-row blocks.  For
+ * bf16 weights with r = 128, 256 or 512 and every position verified
+ * (ell == NULL) it runs as a software pipeline: half of each workgroup
+ * gathers W1 rows straight into on-chip memory one block ahead and computes
+ * the bias tiles on the matrix cores, the other half streams U and target
+ * rows two blocks ahead and finishes each block.  Otherwise (or with
+ * SPEC_PATH_NO_PIPELINED_SWEEP) the W1 rows are staged through registers and
+ * one workgroup does each block start to end.  Both compute the same
+ * products in the same order (identical results). */
+int spec_verify_ex(const float* U, const void* W1, const void* W2p, int w_dtype,
+                   const int32_t* x0, const int32_t* x, const float* pd_stats,
+                   const float* Lt, const int32_t* ell,
+                   int R, int gamma, int r, int V, float T, int greedy,
+                   uint64_t seed, uint64_t round,
+                   int32_t* n_acc, int32_t* y, float* pt_x, float* c_star, int path,
+                   void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Confidence labels of every drafted position (DSpark section 5) and their
  * running products (section 6):
@@ -263,6 +293,12 @@ int spec_confidence(const float* U, const void* W1, const void* W2p, int w_dtype
                     const float* Lt, int R, int gamma, int r, int V, float T,
                     float* c_star, double* a_star,
                     void* ws, size_t ws_bytes, spec_stream_t stream);
+/* spec_confidence with an explicit kernel path (SPEC_PATH_* bits). */
+int spec_confidence_ex(const float* U, const void* W1, const void* W2p, int w_dtype,
+                       const int32_t* x0, const int32_t* x, const float* pd_stats,
+                       const float* Lt, int R, int gamma, int r, int V, float T,
+                       float* c_star, double* a_star, int path,
+                       void* ws, size_t ws_bytes, spec_stream_t stream);
 
 /* Hardware-aware prefix scheduler (DSpark section 6):
  *   a_{r,j} = prod_{i<=j} c_{r,i} in fp64, left to right;
@@ -396,18 +432,6 @@ int spec_schedule_async(const float* c, int R, int gamma, const float* sps, int 
 
 /* Name of a status code (static string). */
 const char* spec_status_str(int status);
-
-/* Kernel timing.  spec_profile_enable(1) makes every later launch on every
- * stream record HIP events around itself (not thread-safe; for benchmarks).
- * spec_profile_read() synchronises the recorded events and returns, for the
- * kernel named `kernel`, the number of launches and their total duration in
- * milliseconds since the last reset.  spec_profile_reset() drops the records. */
-int spec_profile_enable(int on);
-int spec_profile_reset(void);
-int spec_profile_read(const char* kernel, int* launches, double* total_ms);
-/* Names of kernels with records, separated by ',' into buf (host); returns the
- * length needed. */
-int spec_profile_names(char* buf, int buf_len);
 
 #ifdef __cplusplus
 }

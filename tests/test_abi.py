@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spec.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "spec_debug.h")]
 
 
 @pytest.fixture(scope="module")
@@ -21,10 +22,13 @@ def L():
     return d.lib()
 
 
-def declared_symbols():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(spec_\w+)\s*\(", text, flags=re.M)))
+def declared_symbols(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(spec_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_four_operations():
@@ -123,6 +127,29 @@ def test_propose_validation(L):
     assert _propose(L, R=0, U=None, W1=None, W2=None, x0=None, x=None, pdx=None, pds=None) == d.SPEC_OK
 
 
+def test_path_flags(L):
+    """The _ex entry points take the kernel path per call: unknown bits are
+    rejected before anything is enqueued; known bits pass validation (an
+    empty batch then returns at once).  No process-wide switch exists."""
+    import draft_sampling_verify_amd as d
+    F = FAKE
+    for name in ("spec_set_propose_fused", "spec_set_verify_lds"):
+        assert not hasattr(L, name) or name not in declared_symbols()
+    base = [F, F, F, 1, F, 4, 4, 16, 1024, 1.0, 0, 1, 0, F, F, F]
+    assert L.spec_markov_propose_ex(*base, 4, F, 1 << 30, None) == d.SPEC_EINVAL
+    assert L.spec_markov_propose_ex(*base, -1, F, 1 << 30, None) == d.SPEC_EINVAL
+    empty = [None, F, F, 1, None, 0, 4, 16, 1024, 1.0, 0, 1, 0, None, None, None]
+    for path in (d.SPEC_PATH_AUTO, d.SPEC_PATH_NO_FUSED_PROPOSE, d.SPEC_PATH_NO_PIPELINED_SWEEP, 3):
+        assert L.spec_markov_propose_ex(*empty, path, F, 1 << 30, None) == d.SPEC_OK
+    vargs = [F, F, F, 1, F, F, F, F, None, 4, 4, 16, 1024, 1.0, 0, 1, 0, F, F, None, None]
+    assert L.spec_verify_ex(*vargs, 8, F, 1 << 30, None) == d.SPEC_EINVAL
+    cargs = [F, F, F, 1, F, F, None, F, 4, 4, 16, 1024, 1.0, F, None]
+    assert L.spec_confidence_ex(*cargs, 16, F, 1 << 30, None) == d.SPEC_EINVAL
+    need = d.spec_workspace_bytes(d.SPEC_OP_ROUNDS, 4, 4, 16, 1024)
+    rargs = [F, F, F, 1, F, F, 4, 4, 16, 1024, 1.0, 0, 1, 0, 3, F, F, F, F, None]
+    assert L.spec_decode_rounds_ex(*rargs, 32, F, need, None) == d.SPEC_EINVAL
+
+
 def test_pack_validation(L):
     import draft_sampling_verify_amd as d
     assert L.spec_packed_w2_bytes(1, 256, 129280) == 129280 * 256 * 2
@@ -134,6 +161,9 @@ def test_pack_validation(L):
     assert L.spec_pack_w2(FAKE, 1, 16, 100, ctypes.c_void_p(4100), None) == d.SPEC_EINVAL
     assert L.spec_pack_w2(FAKE, 4, 16, 100, FAKE, None) == d.SPEC_EDTYPE
     assert L.spec_pack_w2(FAKE, 1, 16, 0, FAKE, None) == d.SPEC_EINVAL
+    assert L.spec_pack_w2_rv(FAKE, 1, 16, 100, None, None) == d.SPEC_EINVAL
+    assert L.spec_pack_w2_rv(FAKE, 1, 24, 100, FAKE, None) == d.SPEC_EINVAL
+    assert L.spec_pack_w2_rv(FAKE, 4, 16, 100, FAKE, None) == d.SPEC_EDTYPE
 
 
 def test_verify_confidence_schedule_validation(L):

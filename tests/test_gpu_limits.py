@@ -28,10 +28,10 @@ def _gpu():
     spec.lib()
 
 
-def _check_all(cfg, d, greedy):
+def _check_all(cfg, d, greedy, path=0):
     t = to_dev(d)
     ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
-    x, pdx, pds = run_propose(t, cfg, greedy, ws=ws)
+    x, pdx, pds = run_propose(t, cfg, greedy, ws=ws, path=path)
     log("  propose", check_propose(d, np_(x), np_(pdx), np_(pds), greedy))
     n_acc, y, pt_x, c_star = run_verify(t, cfg, x, pds, greedy, ws=ws)
     log("  verify", check_verify(d, np_(x), None, np_(n_acc), np_(y), np_(pt_x), np_(c_star), greedy))
@@ -45,11 +45,8 @@ GAMMA64 = Config("gamma64", 30, 5, 64, 3000, 64, True, 1.0, 2.0, 0.05, 0.5)
 @pytest.mark.parametrize("greedy", [False, True], ids=["sampled", "greedy"])
 def test_longest_draft_chain(fused, greedy):
     log("case gamma=64", "fused" if fused else "per_position", "greedy" if greedy else "sampled")
-    prev = spec.spec_set_propose_fused(fused)
-    try:
-        _check_all(GAMMA64, workloads.make(GAMMA64), greedy)
-    finally:
-        spec.spec_set_propose_fused(prev)
+    _check_all(GAMMA64, workloads.make(GAMMA64), greedy,
+               path=spec.SPEC_PATH_AUTO if fused else spec.SPEC_PATH_NO_FUSED_PROPOSE)
 
 
 VMAX = Config("vmax", 31, 2, 2, 1 << 24, 16, True, 1.0, 2.0, 0.05, 0.5)
@@ -84,11 +81,7 @@ def test_more_than_2_31_elements():
     ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
     x, pdx, pds = run_propose(t, cfg, False, ws=ws)
     out = run_verify(t, cfg, x, pds, False, ws=ws)
-    prev = spec.spec_set_verify_lds(0)             # the register-staged sweep
-    try:
-        out2 = run_verify(t, cfg, x, pds, False, ws=ws)
-    finally:
-        spec.spec_set_verify_lds(prev)
+    out2 = run_verify(t, cfg, x, pds, False, ws=ws, path=spec.SPEC_PATH_NO_PIPELINED_SWEEP)  # the staged sweep
     assert spec.spec_device_status(ws) == 0
     n_acc, y, pt_x, c_star = (np_(a) for a in out)
     for a, b in zip(out, out2):
