@@ -10,7 +10,8 @@ from ._binding import (  # noqa: F401
     SPEC_EWORKSPACE, SPEC_F32, SPEC_OK, SPEC_OP_CONFIDENCE, SPEC_OP_LOSS, SPEC_OP_PROPOSE,
     SPEC_OP_ROUNDS, SPEC_OP_SCHEDULE, SPEC_OP_VERIFY, SpecError, Workspace, lib, spec_cluster_index, spec_cluster_propose,
     spec_cluster_verify, spec_cluster_workspace_bytes, spec_confidence, spec_decode_rounds, spec_draft_loss,
-    spec_device_status, spec_markov_propose, spec_pack_w2, spec_pack_w2_rv, spec_packed_w2_bytes, spec_philox_words,
+    spec_device_status, spec_markov_propose, spec_markov_propose_noalloc, SPEC_NOALLOC_BYTES,
+    spec_pack_w2, spec_pack_w2_rv, spec_packed_w2_bytes, spec_philox_words,
     spec_profile_enable, spec_profile_names, spec_profile_read, spec_profile_reset, spec_schedule,
     spec_schedule_async, spec_verify, spec_workspace_bytes, spec_workspace_init, status_str,
     SPEC_PATH_AUTO, SPEC_PATH_NO_FUSED_PROPOSE, SPEC_PATH_NO_PIPELINED_SWEEP)

@@ -43,6 +43,7 @@ _SIGS = {
     "spec_pack_w2_rv": ([P, I, I, I, P, P], I),
     "spec_device_status": ([P, P, I, P], I),
     "spec_markov_propose": ([P, P, P, I, P, I, I, I, I, F, I, U64, U64, P, P, P, P, SZ, P], I),
+    "spec_markov_propose_noalloc": ([P, P, P, I, P, I, I, I, I, F, I, U64, U64, P, P, P, P, P], I),
     "spec_markov_propose_ex": ([P, P, P, I, P, I, I, I, I, F, I, U64, U64, P, P, P, I, P, SZ, P], I),
     "spec_verify": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, P, SZ, P], I),
     "spec_verify_ex": ([P, P, P, I, P, P, P, P, P, I, I, I, I, F, I, U64, U64, P, P, P, P, I, P, SZ, P], I),
@@ -234,6 +235,31 @@ def spec_markov_propose(U, W1, W2p, x0, T, greedy=False, seed=1, round=0, x=None
         st = lib().spec_markov_propose(*args, ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "spec_markov_propose")
     return x, pd_x, pd_stats
+
+
+SPEC_NOALLOC_BYTES = 8 << 20
+
+
+def spec_markov_propose_noalloc(U, W1, W2p, x0, T, greedy=False, seed=1, round=0, x=None, pd_x=None,
+                                pd_stats=None, flags=None, stream=None):
+    """spec_markov_propose with the library's static workspace (no device
+    allocation inside the call; pass preallocated outputs to allocate
+    nothing at all).  Returns (x, pd_x, pd_stats, flags [1] int32 device)."""
+    R, gamma, V, r = _draft_shapes(U, W1, W2p, x0)
+    dev = U.device
+    _need(x, (R, gamma), torch.int32, "x")
+    _need(pd_x, (R, gamma), torch.float32, "pd_x")
+    _need(pd_stats, (R, gamma, 2), torch.float32, "pd_stats")
+    _need(flags, (1,), torch.int32, "flags")
+    x = torch.empty((R, gamma), dtype=torch.int32, device=dev) if x is None else x
+    pd_x = torch.empty((R, gamma), dtype=torch.float32, device=dev) if pd_x is None else pd_x
+    pd_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev) if pd_stats is None else pd_stats
+    flags = torch.empty(1, dtype=torch.int32, device=dev) if flags is None else flags
+    st = lib().spec_markov_propose_noalloc(_ptr(U), _ptr(W1), _ptr(W2p), _wdtype(W1), _ptr(x0), R, gamma, r, V,
+                                           float(T), int(bool(greedy)), int(seed), int(round), _ptr(x), _ptr(pd_x),
+                                           _ptr(pd_stats), _ptr(flags), _stream(stream))
+    _check(st, "spec_markov_propose_noalloc")
+    return x, pd_x, pd_stats, flags
 
 
 def spec_verify(U, W1, W2p, x0, x, pd_stats, Lt, T, greedy=False, seed=1, round=0, ell=None,

@@ -349,6 +349,68 @@ int spec_markov_propose_ex(const float* U, const void* W1, const void* W2, int w
                       ws_bytes, spec::WS_HEADER, stream);
 }
 
+// ---- spec_markov_propose_noalloc: the workspace in a static device array
+//
+// `scratch` is a host-side stand-in in host code: its device address on the
+// current GPU comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[SPEC_NOALLOC_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEV = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[NOALLOC_MAX_DEV];    // device address of `scratch` per device (null: not yet set up)
+bool g_noalloc_zeroed[NOALLOC_MAX_DEV];  // the zero fill has been enqueued on this device
+
+// The current device's scratch address; on the first call on a device, look
+// it up and enqueue the one zero fill of the whole array (the status word,
+// the fused propose's call counter and hand-over words start at zero).
+int noalloc_scratch(hipStream_t s, void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEV) return SPEC_ELAUNCH;
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SPEC_ELAUNCH;
+        g_noalloc_ptr[dev] = ptr;
+    }
+    if (!g_noalloc_zeroed[dev]) {
+        const size_t words = SPEC_NOALLOC_BYTES / 4;
+        hipLaunchKernelGGL(k_zero_words, dim3(1024), dim3(256), 0, s, (uint32_t*)g_noalloc_ptr[dev], words);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+        g_noalloc_zeroed[dev] = true;
+    }
+    *out = g_noalloc_ptr[dev];
+    return SPEC_OK;
+}
+}  // namespace
+
+int spec_markov_propose_noalloc(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0,
+                                int R, int gamma, int r, int V, float T, int greedy, uint64_t seed, uint64_t round,
+                                int32_t* x, float* pd_x, float* pd_stats, uint32_t* flags, spec_stream_t stream)
+{
+    int st = check_draft(U, W1, W2, w_dtype, x0, R, gamma, r, V, T);
+    if (st != SPEC_OK) return st;
+    if (R > 0 && (!x || !pd_x || !pd_stats || !flags)) return SPEC_EINVAL;
+    const size_t need = spec_workspace_bytes(SPEC_OP_PROPOSE, R, gamma, r, V, 0);
+    if (need == 0) return SPEC_EINVAL;
+    if (need > SPEC_NOALLOC_BYTES) return SPEC_EUNSUPPORTED;
+    if (R == 0) return SPEC_OK;
+    hipStream_t s = (hipStream_t)stream;
+    void* ptr = nullptr;
+    st = noalloc_scratch(s, &ptr);
+    if (st != SPEC_OK) return st;
+    // this call's status bits start clear (a fill kernel: graph-capturable)
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, (uint32_t*)ptr, (size_t)1);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    st = propose_at(U, W1, W2, w_dtype, x0, R, gamma, r, V, T, greedy, seed, round, x, pd_x, pd_stats,
+                    SPEC_PATH_AUTO, ptr, SPEC_NOALLOC_BYTES, spec::WS_HEADER, stream);
+    if (st != SPEC_OK) return st;
+    hipLaunchKernelGGL(k_copy_words, dim3(1), dim3(64), 0, s, (const int32_t*)ptr, (int32_t*)flags, 1);
+    return launch_status(hipGetLastError());
+}
+
 int spec_markov_propose(const float* U, const void* W1, const void* W2, int w_dtype, const int32_t* x0, int R,
                         int gamma, int r, int V, float T, int greedy, uint64_t seed, uint64_t round, int32_t* x,
                         float* pd_x, float* pd_stats, void* ws, size_t ws_bytes, spec_stream_t stream)

@@ -186,6 +186,28 @@ int spec_markov_propose(const float* U, const void* W1, const void* W2p, int w_d
                         int32_t* x, float* pd_x, float* pd_stats,
                         void* ws, size_t ws_bytes, spec_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * spec_markov_propose with its workspace in a static device array of
+ * SPEC_NOALLOC_BYTES (8 MiB) that the library holds on every GPU it runs on
+ * until the process ends, instead of a caller buffer.  Inputs, outputs and
+ * their layouts are those of spec_markov_propose; the kernel path is the
+ * default one.  flags (device, uint32 [1]) receives the SPEC_DEV_* bits this
+ * call raised (the call clears them first).  Sizes whose propose workspace
+ * (spec_workspace_bytes(SPEC_OP_PROPOSE, ...)) exceeds SPEC_NOALLOC_BYTES
+ * return SPEC_EUNSUPPORTED before anything is enqueued (R*ceil(V/128) up to
+ * about 230000 for R <= 32, about 690000 beyond).  The first call on a GPU
+ * also enqueues one zero fill of the array on `stream`.  Every call on one
+ * GPU shares that GPU's array and it keeps the last call's contents: calls
+ * that overlap in time on one GPU (other streams or threads) race and must
+ * not be issued.  Calls no hipMalloc, hipFree or allocating library routine. */
+#define SPEC_NOALLOC_BYTES ((size_t)8 << 20)
+int spec_markov_propose_noalloc(const float* U, const void* W1, const void* W2p, int w_dtype,
+                                const int32_t* x0, int R, int gamma, int r, int V, float T,
+                                int greedy, uint64_t seed, uint64_t round,
+                                int32_t* x, float* pd_x, float* pd_stats, uint32_t* flags,
+                                spec_stream_t stream);
+
 /* spec_markov_propose with an explicit kernel path (SPEC_PATH_* bits; other
  * bits: SPEC_EINVAL).  Propose runs in one of two ways; tokens agree except
  * at decisions within fp32 rounding of a boundary (the logits are computed
