@@ -933,6 +933,178 @@ __device__ inline void oct_argmax(float& v, int& i)
     argmax_merge(v, i, dpp_f<DPP_XOR2>(v), dpp_i<DPP_XOR2>(i));
     argmax_merge(v, i, dpp_f<DPP_HALF_MIRROR>(v), dpp_i<DPP_HALF_MIRROR>(i));
 }
+
+// Whole-wave scans on DPP moves (no LDS round trip): rows of 16 lanes by
+// row_shr 1, 2, 4, 8, then row_bcast15 (rows 1 and 3 add lane 15 of the row
+// before) and row_bcast31 (rows 2 and 3 add lane 31).  Disabled rows read 0.
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143, DPP_WAVE_SHR1 = 0x138;
+template <int CTRL, int ROWS>
+__device__ inline float dpp_z(float v)  // source lane's value, 0 where none
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ inline int dpp_zi(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+// Inclusive prefix sum over the wave's lanes in lane order (a fixed order:
+// the same inputs give the same bits in every wave).
+__device__ inline float wave_scan_dpp(float v)
+{
+    const int l = threadIdx.x & 15;
+    float t = dpp_z<DPP_ROW_SHR1, 0xF>(v);
+    if (l >= 1) v += t;
+    t = dpp_z<DPP_ROW_SHR2, 0xF>(v);
+    if (l >= 2) v += t;
+    t = dpp_z<DPP_ROW_SHR4, 0xF>(v);
+    if (l >= 4) v += t;
+    t = dpp_z<DPP_ROW_SHR8, 0xF>(v);
+    if (l >= 8) v += t;
+    v += dpp_z<DPP_ROW_BCAST15, 0xA>(v);
+    v += dpp_z<DPP_ROW_BCAST31, 0xC>(v);
+    return v;
+}
+// The previous lane's value (0 in lane 0).
+__device__ inline float lane_before(float v) { return dpp_z<DPP_WAVE_SHR1, 0xF>(v); }
+__device__ inline float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+// Maximum over the wave, in every lane.
+__device__ inline float wave_max_dpp(float v)
+{
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));                  // 8-lane groups
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x118, 0xF, 0xF,
+                                                            false)));  // row_shr:8: lanes 8-15 see 0-7
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), DPP_ROW_BCAST15,
+                                                            0xA, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), DPP_ROW_BCAST31,
+                                                            0xC, 0xF, false)));
+    return lane63(v);
+}
+__device__ inline int wave_max_int_dpp(int v)
+{
+    v = max(v, dpp_i<DPP_XOR1>(v));
+    v = max(v, dpp_i<DPP_XOR2>(v));
+    v = max(v, dpp_i<DPP_HALF_MIRROR>(v));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, DPP_ROW_BCAST15, 0xA, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, DPP_ROW_BCAST31, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ inline int wave_min_int_dpp(int v) { return -wave_max_int_dpp(-v); }
+
+// granule_pick with DPP scans: one full wave, lane l holds the weights of
+// ids 2l and 2l+1; the first id whose running sum (from `before`) exceeds
+// target, else (rounding, or `fallback`) the last id of positive weight.
+__device__ inline int granule_pick_dpp(float ea, float eb, float before, float target, bool fallback, float& e_out)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    const float incl = wave_scan_dpp(ea + eb);
+    const float ex = lane_before(incl);
+    const float ca = (before + ex) + ea;
+    const float cb = ca + eb;
+    const bool ha = ca > target && ea > 0.0f, hb = cb > target && eb > 0.0f;
+    const unsigned long long hit = __ballot(!fallback && (ha || hb));
+    if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        const bool la = __builtin_amdgcn_readlane((int)ha, L) != 0;
+        const float lea = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ea), L));
+        const float leb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eb), L));
+        e_out = la ? lea : leb;
+        return la ? 2 * L : 2 * L + 1;
+    }
+    const unsigned long long nz = __ballot(ea > 0.0f || eb > 0.0f);
+    const int L = nz ? 63 - __clzll((long long)nz) : 0;
+    const float lea = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ea), L));
+    const float leb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eb), L));
+    e_out = leb > 0.0f ? leb : lea;
+    return leb > 0.0f ? 2 * L + 1 : 2 * L;
+}
+
+// Direct-to-LDS gather of the W1 rows of a 32-row block, for bf16 weights
+// whose rows fill the k-steps exactly (r = 128, 256, 512).  The pipelined
+// kernels gather a block's W1 rows by direct global-to-LDS loads (no
+// registers involved) one block ahead, into the other half of a
+// double-buffered tile, so the gather of block b+1 is in flight during
+// block b's MFMA and epilogue.  A direct load writes 16 bytes
+// per lane at consecutive LDS addresses from a per-wave base, so each load
+// moves one W1 row with half a wave (32 lanes x 16 bytes = 512 bytes at
+// r = 256; longer rows take several loads) and the tile keeps the padded row
+// stride of TileOps (RS elements), which spreads the rows of an operand read
+// over the LDS banks.
+template <int KS>
+struct LdsW1 {
+    using Ops = TileOps<bf16w, KS>;
+    static constexpr int ROW = 32 * KS;                   // bytes per W1 row
+    static constexpr int STRIDE = Ops::RS * Ops::ELEM;    // bytes per LDS row
+    static constexpr int BYTES = 32 * STRIDE;             // one 32-row tile
+    static constexpr int PARTS = ROW / 512;               // 512-byte loads per row
+    static constexpr int PER_WAVE = 32 * PARTS / 4;       // loads per wave per tile
+    static_assert(ROW % 512 == 0 || ROW == 256, "W1 rows of 256, 512 or 1024 bytes");
+
+    // Gather W1[tok[n]] for the 32 rows into buf (tok < 0: row 0, whose
+    // values the caller ignores).  Load j of the workgroup moves part j %
+    // PARTS of row j / PARTS.  At r = 128 (256-byte rows) the half wave
+    // covers two rows: lanes 16-31 write the second row at the padded
+    // stride's offset, which a single contiguous load cannot do, so there
+    // each load takes one row with a quarter wave instead.
+    __device__ static inline void gather(__attribute__((address_space(3))) char* buf, const bf16w* W1,
+                                         const int* tok, int w, int lane)
+    {
+        if constexpr (ROW == 256) {
+            // 8 loads per wave, lanes 0-15 active: 16 x 16 bytes = one row
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 8 * w + i;
+                const int tk = tok[row];
+                if (lane < 16) {
+                    const uint4* src = reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * 16 + lane;
+                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE, 16, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const int j = w * PER_WAVE + i;
+                const int row = j / PARTS, part = j % PARTS;
+                const int tk = tok[row];
+                if (lane < 32) {
+                    const uint4* src =
+                        reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * (2 * KS) + 32 * part + lane;
+                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE + 512 * part, 16, 0, 0);
+                }
+            }
+        }
+    }
+};
+
+// The (granule, 32-row block) units a workgroup of a pipelined kernel takes,
+// unit u = granule u / n_rb, block u % n_rb: run rho of the unit order (runs
+// differ by at most one unit).  Consecutive runs sit on one XCD and
+// alternate runs go backward, so the two runs that share a boundary granule
+// both take it at their start or both at their end, and its W2 slice comes
+// from HBM once for the two (the other load hits the XCD's L2).
+struct UnitRun {
+    int rho, u0, nu;
+    bool fwd;
+    __device__ inline UnitRun(int n_gran, int n_rb)
+    {
+        const long NU = (long)n_gran * n_rb;
+        rho = xcd_logical(blockIdx.x, gridDim.x);
+        u0 = (int)((long)rho * NU / gridDim.x);
+        nu = (int)((long)(rho + 1) * NU / gridDim.x) - u0;
+        fwd = (rho & 1) == 0;
+    }
+    // unit j of this run (j past the end repeats the last unit)
+    __device__ inline int unit(int j) const
+    {
+        const int jj = min(j, nu - 1);
+        return fwd ? u0 + jj : u0 + nu - 1 - jj;
+    }
+};
+
 // Instantiations of the rank-dependent kernels: bf16 weights use r/16 k-steps
 // (4, 8, 16 or 32 held; fewer real steps multiply zeros), fp32 weights r/8
 // groups of four k-steps (2, 8 or 32 held).

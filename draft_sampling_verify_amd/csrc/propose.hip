@@ -17,7 +17,9 @@
 //                  sum crosses u * S, recompute that granule's 128 logits
 //                  with the same MFMA operands and pick the id.
 // x_k stays on the device and feeds the next position's W1 gather.
+#include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -210,6 +212,174 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
             if (GREEDY) p.gidx[o] = bi;
         }
     }
+}
+
+// ------------------------------------------------ pipelined draft tile
+//
+// The per-position tile for many requests (bf16 weights, r = 128, 256 or
+// 512), organised as the verify sweep's pipeline: the work is the sequence
+// of (granule, 32-row block) units, unit u = (granule u / n_rb, block u %
+// n_rb); each workgroup takes a contiguous run of units, so W2's granule
+// slice is loaded once per granule a run touches (W2 crosses HBM about
+// once per position instead of once per chunk of row blocks) and the
+// pipeline fills once per workgroup.  Two groups of four waves run one
+// stage apart:
+//   MFMA waves (0-3)      hold the granule's W2 slice (A operand); in stage
+//                         s they gather unit s+1's W1 rows into LDS by direct
+//                         loads, compute unit s's 32 x 128 bias tile into LDS
+//                         and store unit s-2's partials;
+//   epilogue waves (4-7)  hold the U rows of two units in registers; in
+//                         stage s they reduce unit s-1 (z = U + bias: the
+//                         granule's max, sum of weights and greedy argmax per
+//                         row) into LDS, then issue unit s+1's U loads.
+// One barrier per stage; the arithmetic per row is the staged tile's
+// (same products, same order), so both give identical partials.
+template <int KS, bool VEC4, bool GREEDY>
+__global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_draft_tile_ws(TileArgs p)
+{
+    using Ops = TileOps<bf16w, KS>;
+    using SW = LdsW1<KS>;
+    typedef __attribute__((address_space(3))) char lchar;
+    const int nrows = p.nrows;  // rows are the requests at position kfix + 1
+    const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
+    const UnitRun run(p.n_gran, n_rb);
+    const int nu = run.nu;
+    if (nu <= 0) return;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
+    const int kfix = p.kfix;
+    auto unit = [&](int j) { return run.unit(j); };
+    auto ugran = [&](int j) { return unit(j) / n_rb; };
+    auto urow = [&](int j, int i) { return (unit(j) % n_rb) * BLOCK_ROWS + i; };
+    // the token whose W1 row biases request q at this position
+    auto tok_src = [&](int q) { return kfix == 0 ? p.x0 + q : p.x + (size_t)q * p.gamma + kfix - 1; };
+
+    __shared__ __align__(16) char sB0[SW::BYTES], sB1[SW::BYTES];  // W1 tiles of even / odd units
+    __shared__ __align__(16) float sZ0[32 * ZS], sZ1[32 * ZS];     // bias tiles
+    __shared__ int s_tok[4][32];                                    // checked tokens, unit j in j & 3
+    __shared__ int s_tr[2][32];                                     // raw tokens (direct loads)
+    __shared__ float2 s_part[2][32];                                // results: (max, sum of weights)
+    __shared__ int s_arg[2][32];                                    // results: argmax (greedy)
+    __shared__ int s_ok[2][32];                                     // row exists, token valid
+    auto L = [](void* q) { return (lchar*)q; };
+
+    auto checked = [&](int tk, int q, int j) {
+        if (q >= nrows) return -1;
+        if (tk < 0 || tk >= p.V) {
+            if (ugran(j) == 0) raise_flag(p.status, 1u);  // once per row: its granule-0 unit
+            return -1;
+        }
+        return tk;
+    };
+    if (t < 64) {
+        const int j = t >> 5, q = urow(j, t & 31);
+        s_tok[j][t & 31] = checked(q < nrows ? *tok_src(q) : -1, q, j);
+    }
+    auto load_tokens = [&](int j, int* tr) __attribute__((always_inline)) {
+        const int q = urow(j, lane), qc = q < nrows ? q : 0;
+        dma32(tok_src(qc), L(tr));
+    };
+    if (t < 32) load_tokens(2, s_tr[0]);
+    const int n_stages = (nu + 3) & ~1;
+
+    if (w < 4) {
+        // ------------------------------------------------ MFMA waves
+        const int nblk = (p.V + 31) / 32;
+        int ga = ugran(0);
+        Ops A;
+        A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
+        stores_done();
+        __syncthreads();
+        SW::gather(L(sB0), W1, s_tok[0], w, lane);
+        stores_done();
+        __syncthreads();
+        auto stage = [&](char* bcur, char* bnxt, float* zcur, int s) __attribute__((always_inline)) {
+            if (t < 32) {
+                const int q = urow(s + 2, t);
+                s_tok[(s + 2) & 3][t] = checked(s_tr[s & 1][t], q, s + 2);
+            } else if (w == 2 && lane < 32 && s >= 2 && s - 2 < nu) {
+                // unit s-2's partials (reduced last stage)
+                const int e = s - 2, f = urow(e, lane);
+                if (s_ok[e & 1][lane]) {
+                    const size_t o = (size_t)f * p.n_gran + ugran(e);
+                    p.gstat[o] = s_part[e & 1][lane];
+                    if (GREEDY) p.gidx[o] = s_arg[e & 1][lane];
+                }
+            }
+            if (s + 1 < nu) SW::gather(L(bnxt), W1, s_tok[(s + 1) & 3], w, lane);
+            if (t < 32) load_tokens(s + 3, s_tr[(s + 1) & 1]);
+            if (s < nu) {
+                store_tile(zcur, A.mfma_acc(bcur, lane, f32x16{}), w, lane);
+                const int gn = ugran(s + 1);
+                if (s + 1 < nu && gn != ga) {
+                    ga = gn;
+                    A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
+                }
+            }
+            stores_done();
+            __syncthreads();
+        };
+        for (int s = 0; s < n_stages; s += 2) {
+            stage(sB0, sB1, sZ0, s);
+            stage(sB1, sB0, sZ1, s + 1);
+        }
+    } else {
+        // ---------------------------------------------- epilogue waves
+        const int te = t - TILE_THREADS;
+        const int er = te >> 3, ec = (te & 7) * 16;
+        auto issue = [&](int j, float (&zu)[16]) __attribute__((always_inline)) {
+            const int jj = min(j, nu - 1);
+            const int f = urow(jj, er), fc = f < nrows ? f : 0;
+            load16_raw<VEC4>(p.U + ((size_t)fc * p.gamma + kfix) * p.V, ugran(jj) * GRAN + ec, p.V, zu);
+        };
+        float zuA[16], zuB[16];
+        __syncthreads();
+        issue(0, zuA);
+        __syncthreads();
+        auto stage = [&](float (&zu)[16], const float* zprev, int s) __attribute__((always_inline)) {
+            const int e = s - 1;
+            const int cbase = ugran(e) * GRAN + ec;
+            const bool ok = urow(e, er) < nrows && s_tok[e & 3][er] >= 0;
+            if (s >= 1 && s <= nu && (te & 7) == 0) s_ok[e & 1][er] = ok;
+            if (s >= 1 && s <= nu && ok) {
+                const float* zr = zprev + er * ZS + ec;
+                float z[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
+                    const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        z[4 * q + k] = cbase + 4 * q + k < p.V ? zu[4 * q + k] + bb[k] : -INFINITY;
+                }
+                float m = -INFINITY, bv = -INFINITY;
+                int bi = 0x7fffffff;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    m = fmaxf(m, z[j]);
+                    if (GREEDY && z[j] > bv) { bv = z[j]; bi = cbase + j; }
+                }
+                m = oct_max(m);
+                const float ms = safe_ref(m);
+                float sw = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sw += softw(z[j], ms, p.c);
+                sw = oct_sum(sw);
+                if (GREEDY) oct_argmax(bv, bi);
+                if ((te & 7) == 0) {
+                    s_part[e & 1][er] = make_float2(m, sw);
+                    if (GREEDY) s_arg[e & 1][er] = bi;
+                }
+            }
+            issue(s + 1, zu);
+            __syncthreads();
+        };
+        for (int s = 0; s < n_stages; s += 2) {
+            stage(zuB, sZ1, s);
+            stage(zuA, sZ0, s + 1);
+        }
+    }
+    stores_done();
 }
 
 // ------------------------------------------------------------ pick
@@ -472,11 +642,10 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
     __shared__ __align__(16) char sB[32 * Ops::RS * Ops::ELEM];
     __shared__ __align__(16) float sZ[32 * ZS];
     __shared__ int s_tok[32];
-    __shared__ float s_red[TILE_THREADS / WAVE];
-    __shared__ int s_ired[TILE_THREADS / WAVE];
-    __shared__ float s_wtot[TILE_THREADS / WAVE];
-    __shared__ int s_cand[TILE_THREADS / WAVE], s_last[TILE_THREADS / WAVE];
-    __shared__ float s_cbefore[TILE_THREADS / WAVE];
+    __shared__ float2 s_mw[TILE_THREADS / WAVE];       // pick: each wave's (max, mass in its own reference)
+    __shared__ int s_lastw[TILE_THREADS / WAVE];       // pick: each wave's last granule of positive mass
+    __shared__ int s_candw[TILE_THREADS / WAVE];       // pick (greedy): each wave's smallest argmax at its max
+    __shared__ __align__(16) float s_w4[FUSED_PER * TILE_THREADS];  // pick: granule weights, wave references
     __shared__ float zrow[GRAN];
     __shared__ int s_prev[FUSED_MAX_R];  // previous token of each request this workgroup picks
 
@@ -632,26 +801,22 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                 float pdx = NAN, sM = NAN, sS = NAN;
                 if (s_prev[j] >= 0) {
                     // q's partials of every granule, polled until all carry
-                    // this position; thread t reads granules 4t .. 4t+3
+                    // this position; thread t reads granules 4t .. 4t+3 (a
+                    // single poll in flight: more polling only adds traffic
+                    // where the partials are being written)
                     const size_t plane = (size_t)R * NG;
                     const uint64_t* rm = opaque(f.part) + (size_t)q * NG;
-                    float gm[FUSED_PER], gs[FUSED_PER];
-                    uint32_t gi[FUSED_PER];
+                    constexpr int NW_ = GREEDY ? 3 : 2;  // words per granule
+                    uint64_t pa[FUSED_PER * NW_];
                     for (int spin = 0;; ++spin) {
                         bool ok = true;
 #pragma unroll
                         for (int i = 0; i < FUSED_PER; ++i) {
-                            const int gg = FUSED_PER * t + i;
-                            gm[i] = -INFINITY;
-                            gs[i] = 0.0f;
-                            gi[i] = 0u;
-                            if (gg < NG) {
-                                const uint64_t a0 = ld_dev(rm + gg), a1 = ld_dev(rm + plane + gg);
-                                const uint64_t a2 = GREEDY ? ld_dev(rm + 2 * plane + gg) : tagged(0u, tag);
-                                ok &= tag_of(a0) == tag && tag_of(a1) == tag && tag_of(a2) == tag;
-                                gm[i] = __uint_as_float((uint32_t)a0);
-                                gs[i] = __uint_as_float((uint32_t)a1);
-                                gi[i] = (uint32_t)a2;
+                            const int gg = min(FUSED_PER * t + i, NG - 1);  // (past NG: a duplicate, not used)
+#pragma unroll
+                            for (int c = 0; c < NW_; ++c) {
+                                pa[i * NW_ + c] = ld_dev(rm + c * plane + gg);
+                                ok &= tag_of(pa[i * NW_ + c]) == tag;
                             }
                         }
                         const bool ab = look_abort(spin) && ld_dev(f.abort_flag) == abort_word(epoch);
@@ -662,42 +827,61 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                         }
                     }
                     if (failed) break;
-                    // three barriers: the maximum M; the wave totals of the
-                    // weights (a running sum in granule order: lanes, then
-                    // waves); the first granule whose running sum passes the
-                    // target
-                    float mloc = -INFINITY;
-#pragma unroll
-                    for (int i = 0; i < FUSED_PER; ++i) mloc = fmaxf(mloc, gm[i]);
-                    mloc = wave_max(mloc);
-                    if (lane == 0) s_red[w] = mloc;
-                    __syncthreads();
-                    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-                    float wv[FUSED_PER], tsum = 0.0f;
+                    float gm[FUSED_PER], gs[FUSED_PER];
+                    int gi[FUSED_PER];
 #pragma unroll
                     for (int i = 0; i < FUSED_PER; ++i) {
-                        wv[i] = gs[i] * softw(gm[i], M, p.c);  // padding: 0 * 0
-                        tsum += wv[i];
+                        const bool in = FUSED_PER * t + i < NG;
+                        const uint64_t* v = pa;
+                        gm[i] = in ? __uint_as_float((uint32_t)v[i * NW_]) : -INFINITY;
+                        gs[i] = in ? __uint_as_float((uint32_t)v[i * NW_ + 1]) : 0.0f;
+                        gi[i] = GREEDY && in ? (int)(uint32_t)v[i * NW_ + (NW_ - 1)] : 0x7fffffff;
                     }
-                    const float incl = wave_incl_scan(tsum);
-                    float exl = __shfl_up(incl, 1, WAVE);
-                    if (lane == 0) exl = 0.0f;
-                    if (lane == WAVE - 1) s_wtot[w] = incl;
+                    // per wave: its maximum m_w, its mass s_w in the 2^(c(z - m_w))
+                    // reference, and each thread's four granule weights in that
+                    // reference (LDS, for the find below)
+                    float mt = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+                    const float mw = wave_max_dpp(mt);
+                    const float mwr = safe_ref(mw);
+                    float wv[FUSED_PER], tsum = 0.0f;
+                    int ilast = -1;
+#pragma unroll
+                    for (int i = 0; i < FUSED_PER; ++i) {
+                        wv[i] = gs[i] * softw(gm[i], mwr, p.c);  // padding: 0 * 0
+                        tsum += wv[i];
+                        if (wv[i] > 0.0f) ilast = i;
+                    }
+                    const float sw = lane63(wave_scan_dpp(tsum));
+                    const int lastw = wave_max_int_dpp(ilast >= 0 ? FUSED_PER * t + ilast : -1);
+                    int candw = 0x7fffffff;
                     if (GREEDY) {
-                        int cand = 0x7fffffff;
 #pragma unroll
                         for (int i = 0; i < FUSED_PER; ++i)
-                            if (FUSED_PER * t + i < NG && gm[i] == M) cand = min(cand, (int)gi[i]);
-                        cand = wave_min(cand);
-                        if (lane == 0) s_ired[w] = cand;
+                            if (gm[i] == mw) candw = min(candw, gi[i]);
+                        candw = wave_min_int_dpp(candw);
+                    } else {
+                        *reinterpret_cast<float4*>(s_w4 + FUSED_PER * t) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+                    }
+                    if (lane == 0) {
+                        s_mw[w] = make_float2(mw, sw);
+                        s_lastw[w] = lastw;
+                        s_candw[w] = candw;
                     }
                     __syncthreads();
-                    float S = 0.0f, woff = 0.0f;
+                    // every wave: M, S and each wave's range of the running sum
+                    // (waves in order, each scaled to the M reference)
+                    float M = -INFINITY;
+#pragma unroll
+                    for (int v = 0; v < TILE_THREADS / WAVE; ++v) M = fmaxf(M, s_mw[v].x);
+                    const float Mr = safe_ref(M);
+                    float sc[TILE_THREADS / WAVE], P[TILE_THREADS / WAVE + 1];
+                    P[0] = 0.0f;
 #pragma unroll
                     for (int v = 0; v < TILE_THREADS / WAVE; ++v) {
-                        if (v == w) woff = S;
-                        S += s_wtot[v];
+                        sc[v] = softw(s_mw[v].x, Mr, p.c);
+                        P[v + 1] = P[v] + s_mw[v].y * sc[v];
                     }
+                    const float S = P[TILE_THREADS / WAVE];
                     sM = M;
                     sS = S;
                     if (!(S > 0.0f)) {
@@ -706,58 +890,67 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                         sM = NAN;
                         sS = NAN;
                     } else if (GREEDY) {
-                        xk = min(min(s_ired[0], s_ired[1]), min(s_ired[2], s_ired[3]));
+                        int cand = 0x7fffffff;
+#pragma unroll
+                        for (int v = 0; v < TILE_THREADS / WAVE; ++v)
+                            if (s_mw[v].x == M) cand = min(cand, s_candw[v]);
+                        xk = cand;
                         pdx = 1.0f / S;
                     } else {
                         const float target = u24f(philox((uint32_t)k, (uint32_t)q, f.round, f.seed).w[0]) * S;
-                        // this thread's share of the running sum is
-                        // [woff + exl, woff + incl): consecutive shares meet
-                        // exactly, so at most one thread holds the target
-                        const float lo = woff + exl, hi = woff + incl;
-                        const bool hit = tsum > 0.0f && lo <= target && target < hi;
-                        int ig = -1, ilast = -1;
-                        float c = lo, cbefore = lo;
-#pragma unroll
-                        for (int i = 0; i < FUSED_PER; ++i) {
-                            if (wv[i] > 0.0f) {
-                                if (ig < 0 && c + wv[i] > target) {
-                                    ig = i;
-                                    cbefore = c;
-                                }
-                                ilast = i;
-                            }
-                            c += wv[i];
-                        }
-                        if (hit && ig < 0) {  // the share's own sum rounded below the target
-                            ig = ilast;
-                            float c2 = lo;
-#pragma unroll
-                            for (int i = 0; i < FUSED_PER; ++i)
-                                if (i < ilast) c2 += wv[i];
-                            cbefore = c2;
-                        }
-                        const unsigned long long hits = __ballot(hit);
-                        const int lastpos = wave_max_int(ilast >= 0 ? FUSED_PER * t + ilast : -1);
-                        if (hits) {
-                            if (lane == __ffsll((long long)hits) - 1) {
-                                s_cand[w] = FUSED_PER * t + ig;
-                                s_cbefore[w] = cbefore;
-                            }
-                        } else if (lane == 0) {
-                            s_cand[w] = -1;
-                        }
-                        if (lane == 0) s_last[w] = lastpos;
-                        __syncthreads();
-                        int gstar = -1;
-                        float before = 0.0f;
+                        // the wave whose range holds the target; every wave replays
+                        // that wave's lane scan from LDS (same inputs, same bits)
+                        int ws = -1;
 #pragma unroll
                         for (int v = TILE_THREADS / WAVE - 1; v >= 0; --v)
-                            if (s_cand[v] >= 0) {
-                                gstar = s_cand[v];
-                                before = s_cbefore[v];
+                            if (s_mw[v].y > 0.0f && P[v] <= target && target < P[v + 1]) ws = v;
+                        int gstar = -1;
+                        float before = 0.0f;
+                        if (ws >= 0) {
+                            const float4 r4 = *reinterpret_cast<const float4*>(s_w4 + FUSED_PER * (ws * WAVE + lane));
+                            const float rv[FUSED_PER] = {r4.x, r4.y, r4.z, r4.w};
+                            const float rt = (rv[0] + rv[1]) + (rv[2] + rv[3]);
+                            float rsum = 0.0f;
+#pragma unroll
+                            for (int i = 0; i < FUSED_PER; ++i) rsum += rv[i];
+                            (void)rt;
+                            const float incl = wave_scan_dpp(rsum);
+                            const float scw = sc[ws];
+                            // the lane's share of the running sum in the M reference;
+                            // consecutive shares meet exactly
+                            const float lo = P[ws] + lane_before(incl) * scw, hi = P[ws] + incl * scw;
+                            const bool hit = rsum > 0.0f && lo <= target && target < hi;
+                            int ig = -1, il = -1;
+                            float c = lo, cbefore = lo;
+#pragma unroll
+                            for (int i = 0; i < FUSED_PER; ++i) {
+                                const float wi = rv[i] * scw;
+                                if (rv[i] > 0.0f) {
+                                    if (ig < 0 && c + wi > target) {
+                                        ig = i;
+                                        cbefore = c;
+                                    }
+                                    il = i;
+                                }
+                                c += wi;
                             }
+                            if (hit && ig < 0) {  // the share's own sum rounded below the target
+                                ig = il;
+                                float c2 = lo;
+#pragma unroll
+                                for (int i = 0; i < FUSED_PER; ++i)
+                                    if (i < il) c2 += rv[i] * scw;
+                                cbefore = c2;
+                            }
+                            const unsigned long long hits = __ballot(hit);
+                            if (hits) {
+                                const int L = __ffsll((long long)hits) - 1;
+                                gstar = FUSED_PER * (ws * WAVE + L) + __builtin_amdgcn_readlane(ig, L);
+                                before = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbefore), L));
+                            }
+                        }
                         const bool fallback = gstar < 0;
-                        if (fallback) gstar = max(max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])), 0);
+                        if (fallback) gstar = max(max(max(s_lastw[0], s_lastw[1]), max(s_lastw[2], s_lastw[3])), 0);
                         // granule gstar for q with the tile's own operands: W2
                         // block, U_k as the starting accumulator, and sB, which
                         // still holds this position's W1 rows (column q)
@@ -774,20 +967,20 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                             if (n == (q & 31)) {
 #pragma unroll
                                 for (int jj = 0; jj < 16; ++jj)
-                                    zrow[32 * w + 8 * (jj >> 2) + 4 * h + (jj & 3)] = softw(acc[jj], M, p.c);
+                                    zrow[32 * w + 8 * (jj >> 2) + 4 * h + (jj & 3)] = softw(acc[jj], Mr, p.c);
                             }
                         }
                         __syncthreads();
                         if (w == 0) {
                             float e;
-                            const int col = granule_pick(zrow[2 * lane], zrow[2 * lane + 1], before, target,
-                                                         fallback, e);
+                            const int col = granule_pick_dpp(zrow[2 * lane], zrow[2 * lane + 1], before, target,
+                                                             fallback, e);
                             xk = gstar * GRAN + col;
                             pdx = e / S;
                         }
                     }
                 }
-                // wave 0 publishes the token (copies in lanes 0..7) and
+                // wave 0 publishes the token (one copy per lane) and
                 // records the outputs
                 if (w == 0) {
                     if (lane < FUSED_TOKEN_COPIES) st_dev(f.words + (size_t)lane * 32 + q, tagged((uint32_t)xk, tag));
@@ -803,7 +996,7 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
             }
             // unconditional, so that the W2 registers are provably free
             // during the picks (32 workgroups re-read 64 KB each)
-            if (!GREEDY) A.load_a(p.W2p, ks, 4 * g + w, 4 * g + w < nblk, lane);
+            A.load_a(p.W2p, ks, 4 * g + w, 4 * g + w < nblk, lane);
         }
     }
     // the call counter advances once every workgroup has read it: workgroup
@@ -869,6 +1062,51 @@ static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* 
     return hipGetLastError();
 }
 
+// Requests above which the per-position path takes the pipelined tile (at
+// fewer, its runs cover too few row blocks per granule to hide the W2
+// reloads).
+constexpr int PIPED_TILE_MIN_R = 96;
+
+// Workgroups of k_draft_tile_ws the current device holds at once; cached
+// per device and variant.
+template <int KS, bool GREEDY>
+static int tile_ws_slots(bool vec4)
+{
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV][2];  // slots + 1; 0 = not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return 256;
+    int v = cache[dev][vec4].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        const hipError_t e = vec4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                        &per_cu, k_draft_tile_ws<KS, true, GREEDY>, 2 * TILE_THREADS, 0)
+                                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                        &per_cu, k_draft_tile_ws<KS, false, GREEDY>, 2 * TILE_THREADS, 0);
+        if (e != hipSuccess || per_cu <= 0) per_cu = 1;
+        v = per_cu * cus + 1;
+        cache[dev][vec4].store(v, std::memory_order_relaxed);
+    }
+    return v - 1;
+}
+
+template <int KS>
+static void launch_tile_ws(const TileArgs& t, bool greedy, int grid, hipStream_t s)
+{
+    if constexpr (KS == 8 || KS == 16 || KS == 32) {
+        const dim3 g(grid), b(2 * TILE_THREADS);
+        if (greedy) {
+            if (t.vec4) hipLaunchKernelGGL((k_draft_tile_ws<KS, true, true>), g, b, 0, s, t);
+            else hipLaunchKernelGGL((k_draft_tile_ws<KS, false, true>), g, b, 0, s, t);
+        } else {
+            if (t.vec4) hipLaunchKernelGGL((k_draft_tile_ws<KS, true, false>), g, b, 0, s, t);
+            else hipLaunchKernelGGL((k_draft_tile_ws<KS, false, false>), g, b, 0, s, t);
+        }
+    }
+}
+
 template <typename WT, int KS>
 static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, float* pd_stats,
                                const ProposeWs& ws, hipStream_t s)
@@ -896,12 +1134,27 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
         }
     }
     const int grid = xcd_grid(n_gran * t.n_chunks);
+    // many requests, bf16 weights filling the k-steps: the pipelined tile
+    const bool piped = std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16 || KS == 32) && a.r == 16 * KS &&
+                       a.R > PIPED_TILE_MIN_R;
+    int pgrid = 0;
+    if constexpr (KS == 8 || KS == 16 || KS == 32) {
+        if (piped) {
+            const long units = (long)n_gran * ((a.R + BLOCK_ROWS - 1) / BLOCK_ROWS);
+            const int slots =
+                a.greedy ? tile_ws_slots<KS, true>(t.vec4 != 0) : tile_ws_slots<KS, false>(t.vec4 != 0);
+            const long n = std::min<long>(slots, units);
+            pgrid = (int)(n >= NUM_XCD ? n / NUM_XCD * NUM_XCD : xcd_grid((int)n));
+        }
+    }
     for (int k = 1; k <= a.gamma; ++k) {
         t.kfix = k - 1;
         pk.k = k;
         {
             ProfScope ps("draft_tile", s);
-            if (a.greedy)
+            if (piped)
+                launch_tile_ws<KS>(t, a.greedy, pgrid, s);
+            else if (a.greedy)
                 hipLaunchKernelGGL((k_draft_tile<WT, KS, true>), dim3(grid), dim3(TILE_THREADS), 0, s, t);
             else
                 hipLaunchKernelGGL((k_draft_tile<WT, KS, false>), dim3(grid), dim3(TILE_THREADS), 0, s, t);

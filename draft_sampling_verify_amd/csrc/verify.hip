@@ -444,62 +444,6 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
     }
 }
 
-// The sweep for bf16 weights whose W1 rows fill the k-steps exactly (r =
-// 128, 256, 512).  The W1 rows of a block are gathered by direct
-// global-to-LDS loads (no registers involved) one block ahead, into the
-// other half of a double-buffered tile, so the gather of block b+1 is in
-// flight during block b's MFMA and epilogue.  A direct load writes 16 bytes
-// per lane at consecutive LDS addresses from a per-wave base, so each load
-// moves one W1 row with half a wave (32 lanes x 16 bytes = 512 bytes at
-// r = 256; longer rows take several loads) and the tile keeps the padded row
-// stride of TileOps (RS elements), which spreads the rows of an operand read
-// over the LDS banks.
-template <int KS>
-struct LdsW1 {
-    using Ops = TileOps<bf16w, KS>;
-    static constexpr int ROW = 32 * KS;                   // bytes per W1 row
-    static constexpr int STRIDE = Ops::RS * Ops::ELEM;    // bytes per LDS row
-    static constexpr int BYTES = 32 * STRIDE;             // one 32-row tile
-    static constexpr int PARTS = ROW / 512;               // 512-byte loads per row
-    static constexpr int PER_WAVE = 32 * PARTS / 4;       // loads per wave per tile
-    static_assert(ROW % 512 == 0 || ROW == 256, "W1 rows of 256, 512 or 1024 bytes");
-
-    // Gather W1[tok[n]] for the 32 rows into buf (tok < 0: row 0, whose
-    // values the caller ignores).  Load j of the workgroup moves part j %
-    // PARTS of row j / PARTS.  At r = 128 (256-byte rows) the half wave
-    // covers two rows: lanes 16-31 write the second row at the padded
-    // stride's offset, which a single contiguous load cannot do, so there
-    // each load takes one row with a quarter wave instead.
-    __device__ static inline void gather(__attribute__((address_space(3))) char* buf, const bf16w* W1,
-                                         const int* tok, int w, int lane)
-    {
-        if constexpr (ROW == 256) {
-            // 8 loads per wave, lanes 0-15 active: 16 x 16 bytes = one row
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = 8 * w + i;
-                const int tk = tok[row];
-                if (lane < 16) {
-                    const uint4* src = reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * 16 + lane;
-                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE, 16, 0, 0);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) {
-                const int j = w * PER_WAVE + i;
-                const int row = j / PARTS, part = j % PARTS;
-                const int tk = tok[row];
-                if (lane < 32) {
-                    const uint4* src =
-                        reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * (2 * KS) + 32 * part + lane;
-                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE + 512 * part, 16, 0, 0);
-                }
-            }
-        }
-    }
-};
-
 // The direct-to-LDS sweep, for the implicit row map (every position of every
 // request verified).  The work is a sequence of units, unit u = (granule
 // u / n_rb, 32-row block u % n_rb); each workgroup takes a contiguous run of
@@ -531,26 +475,15 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
     typedef __attribute__((address_space(3))) char lchar;
     const int nrows = p.max_rows;
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
-    const long NU = (long)p.n_gran * n_rb;
-    // Run rho of the logical order: consecutive runs sit on one XCD.  Even
-    // runs go forward and odd runs backward, so the two runs that share a
-    // boundary granule both take it at their start or both at their end,
-    // and its W2 slice comes from HBM once for the two (the other load hits
-    // the XCD's L2).
-    const int rho = xcd_logical(blockIdx.x, gridDim.x);
-    const int u0 = (int)((long)rho * NU / gridDim.x);
-    const int nu = (int)((long)(rho + 1) * NU / gridDim.x) - u0;
+    const UnitRun run(p.n_gran, n_rb);
+    const int nu = run.nu;
     if (nu <= 0) return;
-    const bool fwd = (rho & 1) == 0;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
     // unit j of this run (j may pass the run's end: such units repeat the
     // last one, only their tokens and row context are loaded, and they are
     // never used)
-    auto unit = [&](int j) {
-        const int jj = min(j, nu - 1);
-        return fwd ? u0 + jj : u0 + nu - 1 - jj;
-    };
+    auto unit = [&](int j) { return run.unit(j); };
     auto ugran = [&](int j) { return unit(j) / n_rb; };
     auto urow = [&](int j, int i) { return (unit(j) % n_rb) * BLOCK_ROWS + i; };
 

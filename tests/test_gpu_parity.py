@@ -44,6 +44,10 @@ SMALL = {
     # per workgroup (its double-buffered gather)
     "lds_r128_odd": Config("lds_r128_odd", 19, 37, 3, 1001, 128, True, 1.0, 2.0, 0.05, 0.5),
     "lds_multi": Config("lds_multi", 20, 40, 7, 40000, 256, True, 1.0, 3.0, 0.02, 1.0),
+    # the pipelined per-position tile (more than 96 requests, bf16, r = 128 /
+    # 256): ragged request count and vocabulary (V % 4 != 0)
+    "piped_tile": Config("piped_tile", 21, 130, 3, 3001, 128, True, 1.0, 2.0, 0.05, 0.5),
+    "piped_tile_v4": Config("piped_tile_v4", 22, 100, 4, 5000, 256, True, 0.8, 3.0, 0.02, 1.0),
 }
 
 
