@@ -673,6 +673,10 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
         for (int j = 0; j < 16; ++j) u[j] = ua[j];
         store_tile(sZ, u, tt / WAVE, tt & (WAVE - 1));
     };
+    // the abort word, loaded with U_1 (no round trip of its own): a call
+    // that is already marked failed (by the host, or by a workgroup that
+    // gave up waiting) ends at once, in every workgroup
+    const uint32_t abort0 = threadIdx.x == 0 ? ld_dev(f.abort_flag) : 0u;
     {
         float ua[16];
         load_u(1, ua);
@@ -706,6 +710,10 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
     };
 
     bool failed = false;
+    if (__syncthreads_or(threadIdx.x == 0 && abort0 == abort_word(epoch))) {
+        if (threadIdx.x == 0) raise_flag(p.status, DEV_WAIT_FAILED);
+        failed = true;
+    }
     for (int k = 1; k <= p.gamma && !failed; ++k) {
         // thread-derived indices are recomputed per position rather than
         // kept live across the loop (register pressure)

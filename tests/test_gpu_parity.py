@@ -598,3 +598,34 @@ def test_reused_workspace_memory_gives_correct_tokens():
     log("  propose", st)
     assert (np_(x) == np_(xp)).mean() > 0.9
     assert spec.spec_device_status(ws2) == 0
+
+
+def test_fused_propose_abort_word_ends_the_call():
+    """The fused propose's failure path, forced from the host: the abort word
+    of the coming call is written into the workspace header before the call
+    (as a workgroup that gave up waiting would write it).  Every workgroup
+    leaves at once, the call returns promptly with SPEC_DEV_WAIT_FAILED
+    raised, and the next call on the same workspace (a new call counter) is
+    correct again."""
+    import time
+    cfg = SMALL["fused_r256"]
+    d = workloads.make(cfg)
+    t = to_dev(d)
+    ws = spec.Workspace(cfg.R, cfg.gamma, cfg.r, cfg.V)
+    run_propose(t, cfg, False, ws=ws)
+    hdr = ws.tensor[:16].view(torch.int32)        # status, call counter, abort word, -
+    epoch = int(hdr[1].item()) & 0x7FFFFFFF
+    hdr[2] = epoch - (1 << 31)                     # the bits of epoch | 0x80000000
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    x, pdx, pds = run_propose(t, cfg, False, ws=ws)
+    el = time.perf_counter() - t0
+    flags = spec.spec_device_status(ws, clear=True)
+    log("  aborted call: %.1f ms, flags %d" % (1e3 * el, flags))
+    assert flags & spec.SPEC_DEV_WAIT_FAILED
+    assert el < 0.5                                # no wait ran to its bound
+    assert int(hdr[1].item()) & 0x7FFFFFFF == (epoch + 1) & 0x7FFFFFFF
+    x, pdx, pds = run_propose(t, cfg, False, rnd=4, ws=ws)
+    assert spec.spec_device_status(ws) == 0
+    log("  next call", check_propose(d, np_(x), np_(pdx), np_(pds), False, rnd=4))
+
