@@ -917,11 +917,9 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
                         if (ws >= 0) {
                             const float4 r4 = *reinterpret_cast<const float4*>(s_w4 + FUSED_PER * (ws * WAVE + lane));
                             const float rv[FUSED_PER] = {r4.x, r4.y, r4.z, r4.w};
-                            const float rt = (rv[0] + rv[1]) + (rv[2] + rv[3]);
                             float rsum = 0.0f;
 #pragma unroll
                             for (int i = 0; i < FUSED_PER; ++i) rsum += rv[i];
-                            (void)rt;
                             const float incl = wave_scan_dpp(rsum);
                             const float scw = sc[ws];
                             // the lane's share of the running sum in the M reference;

@@ -225,8 +225,10 @@ int spec_markov_propose_noalloc(const float* U, const void* W1, const void* W2p,
  * its workgroups need.  Every wait is bounded: after about 2^20 polls (a
  * second or more) the call gives up, its workgroups exit, its outputs are
  * undefined and SPEC_DEV_WAIT_FAILED is raised; the next call on the same
- * workspace is unaffected.  Otherwise: two kernels per position (partials,
- * then the pick), W2 streamed once per position. */
+ * workspace is unaffected; a caller that sees the flag reruns the call with
+ * SPEC_PATH_NO_FUSED_PROPOSE, whose kernels never wait for one another.
+ * Otherwise: two kernels per position (partials, then the pick), W2 streamed
+ * about once per position. */
 int spec_markov_propose_ex(const float* U, const void* W1, const void* W2p, int w_dtype,
                            const int32_t* x0, int R, int gamma, int r, int V, float T,
                            int greedy, uint64_t seed, uint64_t round,
