@@ -429,6 +429,25 @@ __device__ inline int granule_pick(float ea, float eb, float before, float targe
 // Workgroups are dispatched round-robin over the 8 XCDs.  Remap so that
 // consecutive logical ids run on the same XCD (they share W2 columns in its
 // L2).  The grid is launched with xcd_grid(n) blocks; ids >= n must exit.
+// Division by a divisor fixed for a launch: n / d for 0 <= n < 2^31 with one
+// high multiply, an add and a shift (the round-up method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication", PLDI
+// 1994): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (mulhi(n, m) + n) >> l, where the sum stays below 2^32.
+struct FastDiv {
+    uint32_t m;
+    int l;
+    static inline FastDiv make(int d)
+    {
+        FastDiv f;
+        f.l = 0;
+        while ((1u << f.l) < (uint32_t)d) ++f.l;
+        f.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << f.l) - (uint64_t)d)) / (uint64_t)d + 1);
+        return f;
+    }
+    __device__ inline int div(int n) const { return (int)((__umulhi((uint32_t)n, m) + (uint32_t)n) >> l); }
+};
+
 constexpr int NUM_XCD = 8;
 __host__ __device__ inline int xcd_grid(int n) { return (n + NUM_XCD - 1) / NUM_XCD * NUM_XCD; }
 __device__ inline int xcd_logical(int bid, int n)
@@ -513,6 +532,25 @@ struct TileOps<bf16w, KS> {
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
                                                               __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
             }
+        }
+        return acc;
+    }
+    // mfma_acc reading at most LA B fragments ahead of the products that use
+    // them, so that its registers stay bounded (same products, same order)
+    template <int LA>
+    __device__ inline f32x16 mfma_acc_la(const void* sB, int lane, f32x16 acc) const
+    {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(sB) + (lane & 31) * RS + 8 * (lane >> 5);
+        u32x4 bv[LA + 1];
+#pragma unroll
+        for (int s = 0; s < LA; ++s) bv[s] = *reinterpret_cast<const u32x4*>(B + 16 * s);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s + LA < KS) bv[(s + LA) % (LA + 1)] = *reinterpret_cast<const u32x4*>(B + 16 * (s + LA));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                          __builtin_bit_cast(bf16x8, bv[s % (LA + 1)]), acc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         return acc;
     }
@@ -754,6 +792,42 @@ struct W1Gather {
     }
 };
 
+// The W1 rows of a 32-row tile (bf16, r = 16 KS) through registers, for
+// pipelines that load them a stage before they are written to LDS.  The
+// tile's uint4 are taken in row-major order (2 KS per row) and split into
+// PARTS equal parts; thread t of 256 moves uint4 t, t + 256, ... of its
+// part.  A missing token (< 0) loads row 0; the caller ignores that row's
+// results.
+template <int RS, int KS, int PARTS>
+struct W1Regs {
+    // a native vector type: its copies are plain loads and stores, so the
+    // array stays in registers
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    static constexpr int PER_ROW = 2 * KS;
+    static constexpr int PART = 32 * PER_ROW / PARTS;
+    static constexpr int NPT = PART / TILE_THREADS;
+    static_assert(PART % TILE_THREADS == 0, "whole parts");
+    u32x4 v[NPT];
+    __device__ inline void issue(const bf16w* W1, const int* tok, int part, int t)
+    {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int idx = part * PART + t + i * TILE_THREADS;
+            const int tk = tok[idx / PER_ROW];
+            v[i] = reinterpret_cast<const u32x4*>(W1 + (size_t)(tk >= 0 ? tk : 0) * (16 * KS))[idx % PER_ROW];
+        }
+    }
+    __device__ inline void commit(void* sB, int part, int t) const
+    {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int idx = part * PART + t + i * TILE_THREADS;
+            *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sB) + (size_t)(idx / PER_ROW) * RS * 2 +
+                                      16 * (idx % PER_ROW)) = v[i];
+        }
+    }
+};
+
 template <typename WT, int RS, int KS>
 __device__ inline void stage_w1(void* sB, const WT* W1, const int* tok, int r)
 {
@@ -880,6 +954,24 @@ __device__ inline void load16_raw(const float* row, int c0, int V, float (&v)[16
     }
 }
 
+// load16_raw for 8 consecutive floats.
+template <bool VEC4>
+__device__ inline void load8_raw(const float* row, int c0, int V, float (&v)[8])
+{
+    if constexpr (VEC4) {
+        const float4* p4 = reinterpret_cast<const float4*>(row);
+        const int q0 = c0 >> 2, qmax = (V >> 2) - 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float4 a = p4[min(q0 + j, qmax)];
+            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = row[min(c0 + e, V - 1)];
+    }
+}
+
 template <bool VEC4>
 __device__ inline void load16_flat(const float* row, int c0, int V, float (&v)[16])
 {
@@ -914,6 +1006,7 @@ __device__ inline int dpp_i(int v)
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_QUAD_MIRROR = 0x1B, DPP_ROW_ROR8 = 0x128;
 
 __device__ inline float oct_max(float v)
 {
@@ -925,6 +1018,25 @@ __device__ inline float oct_sum(float v)
 {
     v += dpp_f<DPP_XOR1>(v);
     v += dpp_f<DPP_XOR2>(v);
+    return v + dpp_f<DPP_HALF_MIRROR>(v);
+}
+// The sum of a 16-lane group (a DPP row) whose lane l holds the partial sum
+// of ids 8l..8l+7 of a granule: pairs (xor 1), quads (xor 2), halves of 8
+// (half mirror), then the two halves (rotate by 8).  pair_oct_sum gives the
+// same bits when 8 lanes hold two such partials each (lo: lane 2t, hi: lane
+// 2t+1): every level adds the same two operands.
+__device__ inline float hex_sum(float v)
+{
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    return v + dpp_f<DPP_ROW_ROR8>(v);
+}
+__device__ inline float pair_oct_sum(float lo, float hi)
+{
+    float v = lo + hi;
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_QUAD_MIRROR>(v);
     return v + dpp_f<DPP_HALF_MIRROR>(v);
 }
 __device__ inline void oct_argmax(float& v, int& i)

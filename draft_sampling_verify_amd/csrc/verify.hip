@@ -246,6 +246,8 @@ struct SweepArgs {
     float2* vpart;        // [rows, n_gran] (TV mass, residual mass)
     float* vbias;         // [rows] Markov bias at the drafted id x_k
     int staged_only;      // the call asked for the staged sweep (PATH_NO_PIPELINED_SWEEP)
+    FastDiv div_rb;       // by the number of 32-row blocks (the pipelined sweep)
+    FastDiv div_g;        // by gamma
 };
 
 // Verified row f: where its data lives and the normalisers of p_d and p_t.
@@ -424,7 +426,9 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
         __syncthreads();
         if (valid) {
             const float* zr = sZ + er * ZS + ec;
-            float tv = 0.0f, res = 0.0f;
+            // ids 0-7 and 8-15 of the thread's 16 summed apart, then reduced
+            // in the pipelined sweep's order (identical records)
+            float tv[2] = {0.0f, 0.0f}, res[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
@@ -432,47 +436,50 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float d;
-                    res += resid(zu[4 * q + e], bb[e], zt[4 * q + e], rc, p.c, d);
-                    tv += fabsf(d);
+                    res[q >> 1] += resid(zu[4 * q + e], bb[e], zt[4 * q + e], rc, p.c, d);
+                    tv[q >> 1] += fabsf(d);
                 }
             }
-            tv = oct_sum(tv);
-            res = oct_sum(res);
-            if ((t & 7) == 0) p.vpart[(size_t)f * p.n_gran + g] = make_float2(tv, res);
+            const float tvs = pair_oct_sum(tv[0], tv[1]), rs = pair_oct_sum(res[0], res[1]);
+            if ((t & 7) == 0) p.vpart[(size_t)f * p.n_gran + g] = make_float2(tvs, rs);
             if (rc.xk >= cbase && rc.xk < cbase + 16) p.vbias[f] = zr[rc.xk - cbase];
         }
     }
 }
 
-// The direct-to-LDS sweep, for the implicit row map (every position of every
+// The pipelined sweep, for the implicit row map (every position of every
 // request verified).  The work is a sequence of units, unit u = (granule
 // u / n_rb, 32-row block u % n_rb); each workgroup takes a contiguous run of
 // units (runs differ in length by at most one), so the pipeline below fills
 // and drains once per workgroup and W2 is reloaded only where the run
-// crosses into the next granule.  The work of a unit is split between two
-// groups of four waves that run one stage apart:
+// crosses into the next granule.  One workgroup of 12 waves per CU; the
+// work of a unit is split between two groups of waves that run one stage
+// apart:
 //   MFMA waves (0-3)      hold W2's granule slice (the A operand) and, in
-//                         stage s, gather unit s+1's W1 rows into LDS,
-//                         compute unit s's 32 x 128 bias tile into LDS and
-//                         store unit s-2's results;
-//   epilogue waves (4-7)  hold U and target rows of two units in registers
-//                         and, in stage s, finish unit s-1 (p_d, p_t, the TV
-//                         and residual masses, the bias at x_k) into LDS
-//                         while unit s's rows are in flight, then issue
-//                         unit s+1's loads.
-// One barrier per stage.  The epilogue waves issue nothing but their own
-// row loads, so each of their waits is for the older unit only and the
-// newer one stays in flight across the barrier; the MFMA waves wait for all
-// of theirs before it.  Per-row values go through LDS by direct loads, one
-// stage ahead: the raw row context (x_k, the draft's (M, S), the target's
-// (M, S)) and, two units ahead, the token pairs from which the W1 rows are
-// chosen.
+//                         stage s, write unit s+1's W1 rows (loaded into
+//                         registers last stage) into LDS, issue the loads of
+//                         unit s+2's, compute unit s's 32 x 128 bias tile
+//                         into LDS and move the per-row values that arrived
+//                         (tokens, row context) into LDS;
+//   epilogue waves (4-11) hold the U and target rows of three units in
+//                         registers (16 lanes per row, 8 ids each): in
+//                         stage s they finish unit s-1 (p_d, p_t, the TV
+//                         and residual masses, the bias at x_k) while units
+//                         s and s+1 are in flight, store its results, then
+//                         issue unit s+2's loads into the registers just
+//                         freed.
+// One barrier per stage, and no wave waits at it for memory: every value is
+// loaded into registers at least one stage before it is needed (the W1 rows
+// one stage ahead, U and target rows two, the token pairs that choose the W1
+// rows and the row context three stages before they are used), and the
+// results go out as plain stores that stay in flight.  Each group first uses what arrived and only then
+// issues new loads, all without a branch, so every wait the compiler places
+// is for loads of an earlier stage.
 template <int KS, bool VEC4>
-__global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepArgs p)
+__global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepArgs p)
 {
     using Ops = TileOps<bf16w, KS>;
-    using SW = LdsW1<KS>;
-    typedef __attribute__((address_space(3))) char lchar;
+    using GW = W1Regs<Ops::RS, KS, 1>;
     const int nrows = p.max_rows;
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
     const UnitRun run(p.n_gran, n_rb);
@@ -481,132 +488,144 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
     // unit j of this run (j may pass the run's end: such units repeat the
-    // last one, only their tokens and row context are loaded, and they are
-    // never used)
+    // last one; their values are loaded and never used)
     auto unit = [&](int j) { return run.unit(j); };
-    auto ugran = [&](int j) { return unit(j) / n_rb; };
-    auto urow = [&](int j, int i) { return (unit(j) % n_rb) * BLOCK_ROWS + i; };
-
-    // buffers of even and odd units
-    __shared__ __align__(16) char sB0[SW::BYTES], sB1[SW::BYTES];  // W1 tiles
-    __shared__ __align__(16) float sZ0[32 * ZS], sZ1[32 * ZS];     // bias tiles
-    __shared__ int s_tok[4][32];                                    // checked tokens, unit j in j & 3
-    __shared__ int s_tr[2][2][32];                                  // raw (x_{k-1}, x_k)
-    __shared__ int s_xk[2][32];                                     // raw x_k
-    __shared__ float s_cf[2][4][32];                                // raw M_d, S_d, M_t, S_t
-    __shared__ float2 s_part[2][32];                                // results: (TV, residual) mass
-    __shared__ float s_bx[2][32];                                   // results: bias at x_k
-    __shared__ int s_has[2][32];                                    // x_k in this granule
-    __shared__ int s_ok[2][32];                                     // row exists, tokens valid
-    auto L = [](void* q) { return (lchar*)q; };
-
-    // units 0 and 1: tokens (plain loads, needed at once); unit 2: raw
-    // tokens by direct loads.  Rows past the end load row 0's values and are
-    // masked where used.
-    if (t < 64) {
-        const int q = urow(t >> 5, t & 31);
-        s_tok[t >> 5][t & 31] = q < nrows ? tok_check(tok_raw<false>(p, q, nrows), p.V) : -1;
-    }
-    auto load_tokens = [&](int j, int (*tr)[32]) __attribute__((always_inline)) {
-        const int q = urow(j, lane), qc = q < nrows ? q : 0;
-        const int r = qc / p.gamma, kk = qc - r * p.gamma;
-        dma32(kk == 0 ? p.x0 + r : p.x + (qc - 1), L(tr[0]));
-        dma32(p.x + qc, L(tr[1]));
+    auto ugran = [&](int j) { return p.div_rb.div(unit(j)); };
+    auto urow = [&](int j, int i) {
+        const int u = unit(j);
+        return (u - p.div_rb.div(u) * n_rb) * BLOCK_ROWS + i;
     };
-    if (t < 32) load_tokens(2, s_tr[0]);
+
+    __shared__ __align__(16) char sB[2][32 * Ops::RS * Ops::ELEM];  // W1 tiles, unit j in j & 1
+    __shared__ __align__(16) float sZ[2][32 * ZS];                 // bias tiles, unit j in j & 1
+    __shared__ int s_tok[8][32];                                    // checked tokens, unit j in j & 7
+    __shared__ int s_xk[2][32];                                     // x_k
+    __shared__ float s_cf[2][4][32];                                // M_d, S_d, M_t, S_t
+
+    // units 0, 1 and 2: checked tokens.  Rows past the end load row 0's
+    // values and are masked where used.
+    if (t < 96) {
+        const int j = t >> 5, q = urow(j, t & 31);
+        s_tok[j][t & 31] = q < nrows ? tok_check(tok_raw<false>(p, q, nrows), p.V) : -1;
+    }
     // stage s computes unit s's tile (s < nu), finishes unit s-1 and stores
-    // unit s-2's results: stages 0..nu+1, rounded up to an even count (the
-    // loops below take stages in pairs)
-    const int n_stages = (nu + 3) & ~1;
+    // unit s-2's results: stages 0..nu+1, rounded up to a multiple of three
+    // (the epilogue's loop takes stages in threes)
+    const int n_stages = (nu + 2 + 2) / 3 * 3;
+    __syncthreads();
 
     if (w < 4) {
         // ------------------------------------------------ MFMA waves
         const int nblk = (p.V + 31) / 32;
-        // the A operand of unit 0's granule, in flight with the token loads
         int ga = ugran(0);
         Ops A;
         A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
-        stores_done();
-        __syncthreads();
-        SW::gather(L(sB0), W1, s_tok[0], w, lane);
-        stores_done();
-        __syncthreads();
-        auto load_ctx = [&](int j) __attribute__((always_inline)) {
-            const int q = urow(j, lane), qc = q < nrows ? q : 0;
-            const int r = qc / p.gamma, kk = qc - r * p.gamma;
+        // raw per-row values of unit j for row lane & 31 (wave 0: tokens,
+        // wave 1: row context)
+        auto raw_tokens = [&](int j) __attribute__((always_inline)) {
+            const int q = urow(j, lane & 31), qc = q < nrows ? q : 0;
+            const int r = p.div_g.div(qc), kk = qc - r * p.gamma;
+            return make_int2(kk == 0 ? p.x0[r] : p.x[qc - 1], p.x[qc]);
+        };
+        struct Ctx {
+            int xk;
+            float md, sd, mt, st;
+        };
+        auto raw_ctx = [&](int j) __attribute__((always_inline)) {
+            const int q = urow(j, lane & 31), qc = q < nrows ? q : 0;
+            const int r = p.div_g.div(qc), kk = qc - r * p.gamma;
             // target row (r, kk) of the first pass: P rows per request
             const float* ts = reinterpret_cast<const float*>(p.trow) + 2 * ((size_t)r * p.P + kk);
-            dma32(p.x + qc, L(s_xk[j & 1]));
-            dma32(p.dstats + 2 * (size_t)qc, L(s_cf[j & 1][0]));
-            dma32(p.dstats + 2 * (size_t)qc + 1, L(s_cf[j & 1][1]));
-            dma32(ts, L(s_cf[j & 1][2]));
-            dma32(ts + 1, L(s_cf[j & 1][3]));
+            Ctx c;
+            c.xk = p.x[qc];
+            c.md = p.dstats[2 * (size_t)qc];
+            c.sd = p.dstats[2 * (size_t)qc + 1];
+            c.mt = ts[0];
+            c.st = ts[1];
+            return c;
         };
-        // stage s; bcur/zcur hold unit s, bnxt unit s+1 (fixed per call, so
-        // the compiler can tell the MFMA's LDS reads from the direct loads in
-        // flight and does not wait for them)
-        auto stage = [&](char* bcur, char* bnxt, float* zcur, int s) __attribute__((always_inline)) {
+        GW gw;
+        gw.issue(W1, s_tok[0], 0, t);
+        gw.commit(sB[0], 0, t);
+        gw.issue(W1, s_tok[1], 0, t);
+        // the per-row values of stages 0, 1 and 2 in three register sets
+        // (issued after the W1 rows, as in every stage: the waits placed in
+        // the loop hold for its first stage too)
+        int2 trn[3] = {};
+        Ctx cx[3] = {};
+        if (w == 0) {
+            trn[0] = raw_tokens(3);
+            trn[1] = raw_tokens(4);
+            trn[2] = raw_tokens(5);
+        }
+        if (w == 1) {
+            cx[0] = raw_ctx(0);
+            cx[1] = raw_ctx(1);
+            cx[2] = raw_ctx(2);
+        }
+        __syncthreads();
+        // stage s: its own values are in set s % 3, refilled for stage s+3
+        auto stage = [&](int2& tr, Ctx& c, int s) __attribute__((always_inline)) {
+            gw.commit(sB[(s + 1) & 1], 0, t);
             if (t < 32) {
-                // unit s+2's tokens (raw values landed last stage)
-                const int q = urow(s + 2, t);
-                s_tok[(s + 2) & 3][t] =
-                    q < nrows ? tok_check(make_int2(s_tr[s & 1][0][t], s_tr[s & 1][1][t]), p.V) : -1;
-            } else if (w == 2 && lane < 32 && s >= 2 && s - 2 < nu) {
-                // unit s-2's results (finished last stage; its s_tok entry is
-                // being overwritten by wave 0 now)
-                const int e = s - 2, f = urow(e, lane);
-                if (s_ok[e & 1][lane]) {
-                    p.vpart[(size_t)f * p.n_gran + ugran(e)] = s_part[e & 1][lane];
-                    if (s_has[e & 1][lane]) p.vbias[f] = s_bx[e & 1][lane];
-                }
+                // unit s+3's tokens
+                const int q = urow(s + 3, t);
+                s_tok[(s + 3) & 7][t] = q < nrows ? tok_check(tr, p.V) : -1;
+            } else if (w == 1 && lane < 32) {
+                // unit s's row context, read by the epilogue next stage
+                s_xk[s & 1][lane] = c.xk;
+                s_cf[s & 1][0][lane] = c.md;
+                s_cf[s & 1][1][lane] = c.sd;
+                s_cf[s & 1][2][lane] = c.mt;
+                s_cf[s & 1][3][lane] = c.st;
             }
-            if (s + 1 < nu) SW::gather(L(bnxt), W1, s_tok[(s + 1) & 3], w, lane);
-            if (t < 32) load_tokens(s + 3, s_tr[(s + 1) & 1]);
-            else if (w == 1 && lane < 32) load_ctx(s);
+            gw.issue(W1, s_tok[(s + 2) & 7], 0, t);
+            // (one wave each: every vector memory instruction takes a slot in
+            // the CU's queue that the streamed rows also need)
+            if (w == 0) tr = raw_tokens(s + 6);
+            if (w == 1) c = raw_ctx(s + 3);
             if (s < nu) {
-                store_tile(zcur, A.mfma_acc(bcur, lane, f32x16{}), w, lane);
-                // the next unit in another granule: its W2 slice, in flight
-                // until the barrier
+                store_tile(sZ[s & 1], A.mfma_acc(sB[s & 1], lane, f32x16{}), w, lane);
+                // the next unit in another granule: its W2 slice
                 const int gn = ugran(s + 1);
                 if (s + 1 < nu && gn != ga) {
                     ga = gn;
                     A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
                 }
             }
-            stores_done();
             __syncthreads();
         };
-        for (int s = 0; s < n_stages; s += 2) {
-            stage(sB0, sB1, sZ0, s);
-            stage(sB1, sB0, sZ1, s + 1);
+        for (int s = 0; s < n_stages; s += 3) {
+            stage(trn[0], cx[0], s);
+            stage(trn[1], cx[1], s + 1);
+            stage(trn[2], cx[2], s + 2);
         }
     } else {
         // ---------------------------------------------- epilogue waves
+        // 16 lanes per row (a DPP row), 8 ids each
         const int te = t - TILE_THREADS;
-        const int er = te >> 3, ec = (te & 7) * 16;
+        const int er = te >> 4, ec = (te & 15) * 8;
         // issue unit j's U and target rows (j past the run: its last unit
         // again, so the code stays free of branches around loads)
-        auto issue = [&](int j, float (&zu)[16], float (&zt)[16]) __attribute__((always_inline)) {
+        auto issue = [&](int j, float (&zu)[8], float (&zt)[8]) __attribute__((always_inline)) {
             const int jj = min(j, nu - 1);
             const int f = urow(jj, er), fc = f < nrows ? f : 0;
-            const int req = fc / p.gamma, kk = fc - req * p.gamma;
+            const int req = p.div_g.div(fc), kk = fc - req * p.gamma;
             const int cbase = ugran(jj) * GRAN + ec;
-            load16_raw<VEC4>(p.U + (size_t)fc * p.V, cbase, p.V, zu);
-            load16_raw<VEC4>(p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V, cbase, p.V, zt);
+            load8_raw<VEC4>(p.U + (size_t)fc * p.V, cbase, p.V, zu);
+            load8_raw<VEC4>(p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V, cbase, p.V, zt);
         };
-        float zuA[16], ztA[16], zuB[16], ztB[16];  // units of even / odd index
-        // (the first barrier before the loads: the wait before it covers the
-        // prologue's direct loads, and so any load issued ahead of it)
-        __syncthreads();
+        float zuA[8], ztA[8], zuB[8], ztB[8], zuC[8], ztC[8];  // unit j in A, B, C by j % 3
         issue(0, zuA, ztA);
+        issue(1, zuB, ztB);
         __syncthreads();
-        // stage s: finish unit s-1 (rows in zu/zt, tile in zprev) into LDS,
-        // then refill zu/zt with unit s+1
-        auto stage = [&](float (&zu)[16], float (&zt)[16], const float* zprev, int s) __attribute__((always_inline)) {
+        // stage s: finish unit s-1 (rows in zu/zt, tile in sZ) into LDS,
+        // then refill zu/zt with unit s+2
+        auto stage = [&](float (&zu)[8], float (&zt)[8], int s) __attribute__((always_inline)) {
             const int e = s - 1;
             const int ge = ugran(e), cbase = ge * GRAN + ec;
-            const bool ok = urow(e, er) < nrows && s_tok[e & 3][er] >= 0;
-            if (s >= 1 && s <= nu && (te & 7) == 0) s_ok[e & 1][er] = ok;
+            const int f = urow(e, er);
+            const bool ok = f < nrows && s_tok[e & 7][er] >= 0;
             if (s >= 1 && s <= nu && ok) {
                 RowCtx rc;
                 rc.req = 0;
@@ -615,40 +634,53 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_verify_sweep_ws(SweepAr
                 rc.iSd = 1.0f / s_cf[e & 1][1][er];
                 rc.Mt = s_cf[e & 1][2][er];
                 rc.iSt = 1.0f / s_cf[e & 1][3][er];
-                const float* zr = zprev + er * ZS + ec;
+                const float* zr = sZ[e & 1] + er * ZS + ec;
                 float tv = 0.0f, res = 0.0f;
+                if (ge * GRAN + GRAN <= p.V) {
+                    // a whole granule (every one but a ragged last)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
-                    const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+                    for (int q = 0; q < 2; ++q) {
+                        const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
+                        const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        // ids past V as -inf (weight 0 on both sides)
-                        const bool in = cbase + 4 * q + k < p.V;
-                        float d;
-                        res += resid(in ? zu[4 * q + k] : -INFINITY, bb[k], in ? zt[4 * q + k] : -INFINITY, rc, p.c,
-                                     d);
-                        tv += fabsf(d);
+                        for (int k = 0; k < 4; ++k) {
+                            float d;
+                            res += resid(zu[4 * q + k], bb[k], zt[4 * q + k], rc, p.c, d);
+                            tv += fabsf(d);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
+                        const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            // ids past V as -inf (weight 0 on both sides)
+                            const bool in = cbase + 4 * q + k < p.V;
+                            float d;
+                            res += resid(in ? zu[4 * q + k] : -INFINITY, bb[k], in ? zt[4 * q + k] : -INFINITY, rc,
+                                         p.c, d);
+                            tv += fabsf(d);
+                        }
                     }
                 }
-                tv = oct_sum(tv);
-                res = oct_sum(res);
-                if ((te & 7) == 0) {
-                    s_part[e & 1][er] = make_float2(tv, res);
-                    s_has[e & 1][er] = rc.xk >= ge * GRAN && rc.xk < ge * GRAN + GRAN;
-                }
-                if (rc.xk >= cbase && rc.xk < cbase + 16) s_bx[e & 1][er] = zr[rc.xk - cbase];
+                tv = hex_sum(tv);
+                res = hex_sum(res);
+                // the results: stored between this unit's loads and the next
+                // ones, so no later wait is for them
+                if ((te & 15) == 0) p.vpart[(size_t)f * p.n_gran + ge] = make_float2(tv, res);
+                if (rc.xk >= cbase && rc.xk < cbase + 8) p.vbias[f] = zr[rc.xk - cbase];
             }
-            issue(s + 1, zu, zt);
+            issue(s + 2, zu, zt);
             __syncthreads();
         };
-        for (int s = 0; s < n_stages; s += 2) {
-            stage(zuB, ztB, sZ1, s);
-            stage(zuA, ztA, sZ0, s + 1);
+        for (int s = 0; s < n_stages; s += 3) {
+            stage(zuC, ztC, s);
+            stage(zuA, ztA, s + 1);
+            stage(zuB, ztB, s + 2);
         }
     }
-    // direct loads still in flight (units past this run) land before exit
-    stores_done();
 }
 
 // ------------------------------------------------------------- resolve
@@ -1288,6 +1320,8 @@ static SweepArgs make_sweep(const DraftArgs& a, const float* dstats, const float
     s.n_gran = n_granules(a.V);
     s.max_rows = a.R * a.gamma;
     sweep_grid(s.max_rows, s.n_gran, s.bpc, s.n_chunks);
+    s.div_rb = FastDiv::make((s.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
+    s.div_g = FastDiv::make(a.gamma);
     s.vmap = maps ? w.vmap : nullptr;
     s.counts = counts;
     s.trow = w.trow;
@@ -1334,7 +1368,7 @@ static int sweep_ws_slots()
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_verify_sweep_ws<KS, VEC4>, 2 * TILE_THREADS,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_verify_sweep_ws<KS, VEC4>, 3 * TILE_THREADS,
                                                          0) != hipSuccess || per_cu <= 0)
             per_cu = 1;
         v = per_cu * cus + 1;
@@ -1348,11 +1382,13 @@ static void launch_sweep(const SweepArgs& sw, hipStream_t s)
 {
     const dim3 grid(xcd_grid(sw.n_gran * sw.n_chunks));
     const dim3 blk(TILE_THREADS);
-    if constexpr (std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16 || KS == 32)) {
+    // (r = 512 keeps the staged kernel: its W2 slice alone would take 128 of
+    // the pipelined kernel's 170 registers per lane)
+    if constexpr (std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16)) {
         if (sw.r == 16 * KS && !sw.vmap && !sw.staged_only) {
             // as many workgroups as fit at once, each with one run of units
             const long units = (long)sw.n_gran * ((sw.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
-            const dim3 blk2(2 * TILE_THREADS);
+            const dim3 blk2(3 * TILE_THREADS);
             // (a multiple of the XCD count, rounded down unless that is zero)
             auto grid_of = [&](int slots) {
                 const long n = std::min<long>(slots, units);

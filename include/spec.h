@@ -291,7 +291,7 @@ int spec_verify(const float* U, const void* W1, const void* W2p, int w_dtype,
 
 /* spec_verify with an explicit kernel path (SPEC_PATH_* bits).  The sweep
  * recomputes the Markov bias of every verified row in 32-row blocks.  For
- * bf16 weights with r = 128, 256 or 512 and every position verified
+ * bf16 weights with r = 128 or 256 and every position verified
  * (ell == NULL) it runs as a software pipeline: half of each workgroup
  * gathers W1 rows straight into on-chip memory one block ahead and computes
  * the bias tiles on the matrix cores, the other half streams U and target
