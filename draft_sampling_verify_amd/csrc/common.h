@@ -125,15 +125,6 @@ __device__ inline int opaque_v(int v)  // per-lane value
 // Wait until every memory operation this wave issued has completed.
 __device__ inline void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Direct global-to-LDS loads: active lane l of the calling wave writes its
-// 4 (dma32) or 16 (dma16) bytes at dst + 4 l or dst + 16 l; dst is the same
-// for the whole wave.  They count as loads of the issuing wave (a wait for
-// its loads covers them); other waves see the data after that wait and a
-// barrier.
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ inline void dma32(const void* src, lds_void* dst) { __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0); }
-__device__ inline void dma16(const void* src, lds_void* dst) { __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0); }
-
 // ------------------------------------------------------------- arithmetic
 
 // exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
@@ -1032,6 +1023,13 @@ __device__ inline float hex_sum(float v)
     v += dpp_f<DPP_HALF_MIRROR>(v);
     return v + dpp_f<DPP_ROW_ROR8>(v);
 }
+__device__ inline float hex_max(float v)
+{
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    return fmaxf(v, dpp_f<DPP_ROW_ROR8>(v));
+}
 __device__ inline float pair_oct_sum(float lo, float hi)
 {
     float v = lo + hi;
@@ -1044,6 +1042,11 @@ __device__ inline void oct_argmax(float& v, int& i)
     argmax_merge(v, i, dpp_f<DPP_XOR1>(v), dpp_i<DPP_XOR1>(i));
     argmax_merge(v, i, dpp_f<DPP_XOR2>(v), dpp_i<DPP_XOR2>(i));
     argmax_merge(v, i, dpp_f<DPP_HALF_MIRROR>(v), dpp_i<DPP_HALF_MIRROR>(i));
+}
+__device__ inline void hex_argmax(float& v, int& i)
+{
+    oct_argmax(v, i);
+    argmax_merge(v, i, dpp_f<DPP_ROW_ROR8>(v), dpp_i<DPP_ROW_ROR8>(i));
 }
 
 // Whole-wave scans on DPP moves (no LDS round trip): rows of 16 lanes by
@@ -1134,63 +1137,6 @@ __device__ inline int granule_pick_dpp(float ea, float eb, float before, float t
     e_out = leb > 0.0f ? leb : lea;
     return leb > 0.0f ? 2 * L + 1 : 2 * L;
 }
-
-// Direct-to-LDS gather of the W1 rows of a 32-row block, for bf16 weights
-// whose rows fill the k-steps exactly (r = 128, 256, 512).  The pipelined
-// kernels gather a block's W1 rows by direct global-to-LDS loads (no
-// registers involved) one block ahead, into the other half of a
-// double-buffered tile, so the gather of block b+1 is in flight during
-// block b's MFMA and epilogue.  A direct load writes 16 bytes
-// per lane at consecutive LDS addresses from a per-wave base, so each load
-// moves one W1 row with half a wave (32 lanes x 16 bytes = 512 bytes at
-// r = 256; longer rows take several loads) and the tile keeps the padded row
-// stride of TileOps (RS elements), which spreads the rows of an operand read
-// over the LDS banks.
-template <int KS>
-struct LdsW1 {
-    using Ops = TileOps<bf16w, KS>;
-    static constexpr int ROW = 32 * KS;                   // bytes per W1 row
-    static constexpr int STRIDE = Ops::RS * Ops::ELEM;    // bytes per LDS row
-    static constexpr int BYTES = 32 * STRIDE;             // one 32-row tile
-    static constexpr int PARTS = ROW / 512;               // 512-byte loads per row
-    static constexpr int PER_WAVE = 32 * PARTS / 4;       // loads per wave per tile
-    static_assert(ROW % 512 == 0 || ROW == 256, "W1 rows of 256, 512 or 1024 bytes");
-
-    // Gather W1[tok[n]] for the 32 rows into buf (tok < 0: row 0, whose
-    // values the caller ignores).  Load j of the workgroup moves part j %
-    // PARTS of row j / PARTS.  At r = 128 (256-byte rows) the half wave
-    // covers two rows: lanes 16-31 write the second row at the padded
-    // stride's offset, which a single contiguous load cannot do, so there
-    // each load takes one row with a quarter wave instead.
-    __device__ static inline void gather(__attribute__((address_space(3))) char* buf, const bf16w* W1,
-                                         const int* tok, int w, int lane)
-    {
-        if constexpr (ROW == 256) {
-            // 8 loads per wave, lanes 0-15 active: 16 x 16 bytes = one row
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = 8 * w + i;
-                const int tk = tok[row];
-                if (lane < 16) {
-                    const uint4* src = reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * 16 + lane;
-                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE, 16, 0, 0);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) {
-                const int j = w * PER_WAVE + i;
-                const int row = j / PARTS, part = j % PARTS;
-                const int tk = tok[row];
-                if (lane < 32) {
-                    const uint4* src =
-                        reinterpret_cast<const uint4*>(W1) + (size_t)(tk >= 0 ? tk : 0) * (2 * KS) + 32 * part + lane;
-                    __builtin_amdgcn_global_load_lds(src, buf + row * STRIDE + 512 * part, 16, 0, 0);
-                }
-            }
-        }
-    }
-};
 
 // The (granule, 32-row block) units a workgroup of a pipelined kernel takes,
 // unit u = granule u / n_rb, block u % n_rb: run rho of the unit order (runs

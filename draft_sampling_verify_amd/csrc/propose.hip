@@ -113,6 +113,7 @@ struct TileArgs {
     float2* gstat; // [nrows, n_gran]
     int32_t* gidx; // [nrows, n_gran]
     uint32_t* status;
+    FastDiv div_rb; // by the number of 32-row blocks (the pipelined tile)
 };
 
 // Row -> (request, position index kk) and the token whose W1 row biases it.
@@ -201,10 +202,14 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
         }
         m = oct_max(m);
         const float ms = safe_ref(m);
-        float s = 0.0f;
+        // ids 0-7 and 8-15 summed apart, then reduced in the pipelined
+        // tile's order (identical partials)
+        float sl = 0.0f, sh = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s += softw(z[j], ms, p.c);
-        s = oct_sum(s);
+        for (int j = 0; j < 8; ++j) sl += softw(z[j], ms, p.c);
+#pragma unroll
+        for (int j = 8; j < 16; ++j) sh += softw(z[j], ms, p.c);
+        const float s = pair_oct_sum(sl, sh);
         if (GREEDY) oct_argmax(bv, bi);
         if ((t & 7) == 0 && valid) {
             const size_t o = (size_t)erow * p.n_gran + g;
@@ -216,30 +221,33 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 
 // ------------------------------------------------ pipelined draft tile
 //
-// The per-position tile for many requests (bf16 weights, r = 128, 256 or
-// 512), organised as the verify sweep's pipeline: the work is the sequence
-// of (granule, 32-row block) units, unit u = (granule u / n_rb, block u %
+// The per-position tile for many requests (bf16 weights, r = 128 or 256),
+// organised as the pipelined verify sweep: the work is the sequence of
+// (granule, 32-row block) units, unit u = (granule u / n_rb, block u %
 // n_rb); each workgroup takes a contiguous run of units, so W2's granule
 // slice is loaded once per granule a run touches (W2 crosses HBM about
 // once per position instead of once per chunk of row blocks) and the
-// pipeline fills once per workgroup.  Two groups of four waves run one
-// stage apart:
+// pipeline fills once per workgroup.  One workgroup of 12 waves per CU, in
+// two groups that run one stage apart:
 //   MFMA waves (0-3)      hold the granule's W2 slice (A operand); in stage
-//                         s they gather unit s+1's W1 rows into LDS by direct
-//                         loads, compute unit s's 32 x 128 bias tile into LDS
-//                         and store unit s-2's partials;
-//   epilogue waves (4-7)  hold the U rows of two units in registers; in
-//                         stage s they reduce unit s-1 (z = U + bias: the
-//                         granule's max, sum of weights and greedy argmax per
-//                         row) into LDS, then issue unit s+1's U loads.
-// One barrier per stage; the arithmetic per row is the staged tile's
-// (same products, same order), so both give identical partials.
+//                         s they write unit s+1's W1 rows (loaded into
+//                         registers last stage) into LDS, issue the loads of
+//                         unit s+2's, and compute unit s's 32 x 128 bias
+//                         tile into LDS;
+//   epilogue waves (4-11) hold the U rows of three units in registers (16
+//                         lanes per row, 8 ids each); in stage s they reduce
+//                         unit s-1 (z = U + bias: the granule's max, sum of
+//                         weights and greedy argmax per row), store its
+//                         partials, then issue unit s+2's U loads.
+// One barrier per stage and no wait at it for memory (as in the sweep: W1
+// rows one stage ahead, U two, the tokens that choose the W1 rows three).
+// The staged tile sums its 16 ids per thread as two 8-id partials reduced
+// in this kernel's order, so both give identical partials.
 template <int KS, bool VEC4, bool GREEDY>
-__global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_draft_tile_ws(TileArgs p)
+__global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs p)
 {
     using Ops = TileOps<bf16w, KS>;
-    using SW = LdsW1<KS>;
-    typedef __attribute__((address_space(3))) char lchar;
+    using GW = W1Regs<Ops::RS, KS, 1>;
     const int nrows = p.nrows;  // rows are the requests at position kfix + 1
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
     const UnitRun run(p.n_gran, n_rb);
@@ -249,19 +257,17 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_draft_tile_ws(TileArgs 
     const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
     const int kfix = p.kfix;
     auto unit = [&](int j) { return run.unit(j); };
-    auto ugran = [&](int j) { return unit(j) / n_rb; };
-    auto urow = [&](int j, int i) { return (unit(j) % n_rb) * BLOCK_ROWS + i; };
+    auto ugran = [&](int j) { return p.div_rb.div(unit(j)); };
+    auto urow = [&](int j, int i) {
+        const int u = unit(j);
+        return (u - p.div_rb.div(u) * n_rb) * BLOCK_ROWS + i;
+    };
     // the token whose W1 row biases request q at this position
     auto tok_src = [&](int q) { return kfix == 0 ? p.x0 + q : p.x + (size_t)q * p.gamma + kfix - 1; };
 
-    __shared__ __align__(16) char sB0[SW::BYTES], sB1[SW::BYTES];  // W1 tiles of even / odd units
-    __shared__ __align__(16) float sZ0[32 * ZS], sZ1[32 * ZS];     // bias tiles
-    __shared__ int s_tok[4][32];                                    // checked tokens, unit j in j & 3
-    __shared__ int s_tr[2][32];                                     // raw tokens (direct loads)
-    __shared__ float2 s_part[2][32];                                // results: (max, sum of weights)
-    __shared__ int s_arg[2][32];                                    // results: argmax (greedy)
-    __shared__ int s_ok[2][32];                                     // row exists, token valid
-    auto L = [](void* q) { return (lchar*)q; };
+    __shared__ __align__(16) char sB[2][32 * Ops::RS * Ops::ELEM];  // W1 tiles, unit j in j & 1
+    __shared__ __align__(16) float sZ[2][32 * ZS];                 // bias tiles, unit j in j & 1
+    __shared__ int s_tok[8][32];                                    // checked tokens, unit j in j & 7
 
     auto checked = [&](int tk, int q, int j) {
         if (q >= nrows) return -1;
@@ -271,16 +277,14 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_draft_tile_ws(TileArgs 
         }
         return tk;
     };
-    if (t < 64) {
+    if (t < 96) {
         const int j = t >> 5, q = urow(j, t & 31);
         s_tok[j][t & 31] = checked(q < nrows ? *tok_src(q) : -1, q, j);
     }
-    auto load_tokens = [&](int j, int* tr) __attribute__((always_inline)) {
-        const int q = urow(j, lane), qc = q < nrows ? q : 0;
-        dma32(tok_src(qc), L(tr));
-    };
-    if (t < 32) load_tokens(2, s_tr[0]);
-    const int n_stages = (nu + 3) & ~1;
+    // stages 0..nu+1, rounded up to a multiple of three (the loops below
+    // take stages in threes)
+    const int n_stages = (nu + 2 + 2) / 3 * 3;
+    __syncthreads();
 
     if (w < 4) {
         // ------------------------------------------------ MFMA waves
@@ -288,64 +292,69 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_draft_tile_ws(TileArgs 
         int ga = ugran(0);
         Ops A;
         A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
-        stores_done();
+        // raw token of unit j for row lane & 31 (wave 0)
+        auto raw_token = [&](int j) __attribute__((always_inline)) {
+            const int q = urow(j, lane & 31), qc = q < nrows ? q : 0;
+            return *tok_src(qc);
+        };
+        GW gw;
+        gw.issue(W1, s_tok[0], 0, t);
+        gw.commit(sB[0], 0, t);
+        gw.issue(W1, s_tok[1], 0, t);
+
+        // the tokens of stages 0, 1 and 2 in three registers (issued after
+        // the W1 rows, as in every stage)
+        int trn[3] = {};
+        if (w == 0) {
+            trn[0] = raw_token(3);
+            trn[1] = raw_token(4);
+            trn[2] = raw_token(5);
+        }
         __syncthreads();
-        SW::gather(L(sB0), W1, s_tok[0], w, lane);
-        stores_done();
-        __syncthreads();
-        auto stage = [&](char* bcur, char* bnxt, float* zcur, int s) __attribute__((always_inline)) {
-            if (t < 32) {
-                const int q = urow(s + 2, t);
-                s_tok[(s + 2) & 3][t] = checked(s_tr[s & 1][t], q, s + 2);
-            } else if (w == 2 && lane < 32 && s >= 2 && s - 2 < nu) {
-                // unit s-2's partials (reduced last stage)
-                const int e = s - 2, f = urow(e, lane);
-                if (s_ok[e & 1][lane]) {
-                    const size_t o = (size_t)f * p.n_gran + ugran(e);
-                    p.gstat[o] = s_part[e & 1][lane];
-                    if (GREEDY) p.gidx[o] = s_arg[e & 1][lane];
-                }
-            }
-            if (s + 1 < nu) SW::gather(L(bnxt), W1, s_tok[(s + 1) & 3], w, lane);
-            if (t < 32) load_tokens(s + 3, s_tr[(s + 1) & 1]);
+        // stage s: its token is in trn[s % 3], refilled for stage s+3
+        auto stage = [&](int& tr, int s) __attribute__((always_inline)) {
+            gw.commit(sB[(s + 1) & 1], 0, t);
+            if (t < 32) s_tok[(s + 3) & 7][t] = checked(tr, urow(s + 3, t), s + 3);
+            gw.issue(W1, s_tok[(s + 2) & 7], 0, t);
+            if (w == 0) tr = raw_token(s + 6);
             if (s < nu) {
-                store_tile(zcur, A.mfma_acc(bcur, lane, f32x16{}), w, lane);
+                store_tile(sZ[s & 1], A.mfma_acc(sB[s & 1], lane, f32x16{}), w, lane);
                 const int gn = ugran(s + 1);
                 if (s + 1 < nu && gn != ga) {
                     ga = gn;
                     A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
                 }
             }
-            stores_done();
             __syncthreads();
         };
-        for (int s = 0; s < n_stages; s += 2) {
-            stage(sB0, sB1, sZ0, s);
-            stage(sB1, sB0, sZ1, s + 1);
+        for (int s = 0; s < n_stages; s += 3) {
+            stage(trn[0], s);
+            stage(trn[1], s + 1);
+            stage(trn[2], s + 2);
         }
     } else {
         // ---------------------------------------------- epilogue waves
         const int te = t - TILE_THREADS;
-        const int er = te >> 3, ec = (te & 7) * 16;
-        auto issue = [&](int j, float (&zu)[16]) __attribute__((always_inline)) {
+        const int er = te >> 4, ec = (te & 15) * 8;
+        auto issue = [&](int j, float (&zu)[8]) __attribute__((always_inline)) {
             const int jj = min(j, nu - 1);
             const int f = urow(jj, er), fc = f < nrows ? f : 0;
-            load16_raw<VEC4>(p.U + ((size_t)fc * p.gamma + kfix) * p.V, ugran(jj) * GRAN + ec, p.V, zu);
+            load8_raw<VEC4>(p.U + ((size_t)fc * p.gamma + kfix) * p.V, ugran(jj) * GRAN + ec, p.V, zu);
         };
-        float zuA[16], zuB[16];
-        __syncthreads();
+        float zuA[8], zuB[8], zuC[8];  // unit j in A, B, C by j % 3
         issue(0, zuA);
+        issue(1, zuB);
         __syncthreads();
-        auto stage = [&](float (&zu)[16], const float* zprev, int s) __attribute__((always_inline)) {
+        auto stage = [&](float (&zu)[8], int s) __attribute__((always_inline)) {
             const int e = s - 1;
-            const int cbase = ugran(e) * GRAN + ec;
-            const bool ok = urow(e, er) < nrows && s_tok[e & 3][er] >= 0;
-            if (s >= 1 && s <= nu && (te & 7) == 0) s_ok[e & 1][er] = ok;
+            const int ge = ugran(e), cbase = ge * GRAN + ec;
+            const int f = urow(e, er);
+            const bool ok = f < nrows && s_tok[e & 7][er] >= 0;
             if (s >= 1 && s <= nu && ok) {
-                const float* zr = zprev + er * ZS + ec;
-                float z[16];
+                const float* zr = sZ[e & 1] + er * ZS + ec;
+                float z[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < 2; ++q) {
                     const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
                     const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
@@ -355,31 +364,34 @@ __global__ __launch_bounds__(2 * TILE_THREADS, 2) void k_draft_tile_ws(TileArgs 
                 float m = -INFINITY, bv = -INFINITY;
                 int bi = 0x7fffffff;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 0; j < 8; ++j) {
                     m = fmaxf(m, z[j]);
                     if (GREEDY && z[j] > bv) { bv = z[j]; bi = cbase + j; }
                 }
-                m = oct_max(m);
+                m = hex_max(m);
                 const float ms = safe_ref(m);
                 float sw = 0.0f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) sw += softw(z[j], ms, p.c);
-                sw = oct_sum(sw);
-                if (GREEDY) oct_argmax(bv, bi);
-                if ((te & 7) == 0) {
-                    s_part[e & 1][er] = make_float2(m, sw);
-                    if (GREEDY) s_arg[e & 1][er] = bi;
+                for (int j = 0; j < 8; ++j) sw += softw(z[j], ms, p.c);
+                sw = hex_sum(sw);
+                if (GREEDY) hex_argmax(bv, bi);
+                // the partials: stored between this unit's loads and the
+                // next ones, so no later wait is for them
+                if ((te & 15) == 0) {
+                    const size_t o = (size_t)f * p.n_gran + ge;
+                    p.gstat[o] = make_float2(m, sw);
+                    if (GREEDY) p.gidx[o] = bi;
                 }
             }
-            issue(s + 1, zu);
+            issue(s + 2, zu);
             __syncthreads();
         };
-        for (int s = 0; s < n_stages; s += 2) {
-            stage(zuB, sZ1, s);
-            stage(zuA, sZ0, s + 1);
+        for (int s = 0; s < n_stages; s += 3) {
+            stage(zuC, s);
+            stage(zuA, s + 1);
+            stage(zuB, s + 2);
         }
     }
-    stores_done();
 }
 
 // ------------------------------------------------------------ pick
@@ -1088,9 +1100,9 @@ static int tile_ws_slots(bool vec4)
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         const hipError_t e = vec4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                        &per_cu, k_draft_tile_ws<KS, true, GREEDY>, 2 * TILE_THREADS, 0)
+                                        &per_cu, k_draft_tile_ws<KS, true, GREEDY>, 3 * TILE_THREADS, 0)
                                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                        &per_cu, k_draft_tile_ws<KS, false, GREEDY>, 2 * TILE_THREADS, 0);
+                                        &per_cu, k_draft_tile_ws<KS, false, GREEDY>, 3 * TILE_THREADS, 0);
         if (e != hipSuccess || per_cu <= 0) per_cu = 1;
         v = per_cu * cus + 1;
         cache[dev][vec4].store(v, std::memory_order_relaxed);
@@ -1101,8 +1113,8 @@ static int tile_ws_slots(bool vec4)
 template <int KS>
 static void launch_tile_ws(const TileArgs& t, bool greedy, int grid, hipStream_t s)
 {
-    if constexpr (KS == 8 || KS == 16 || KS == 32) {
-        const dim3 g(grid), b(2 * TILE_THREADS);
+    if constexpr (KS == 8 || KS == 16) {
+        const dim3 g(grid), b(3 * TILE_THREADS);
         if (greedy) {
             if (t.vec4) hipLaunchKernelGGL((k_draft_tile_ws<KS, true, true>), g, b, 0, s, t);
             else hipLaunchKernelGGL((k_draft_tile_ws<KS, false, true>), g, b, 0, s, t);
@@ -1141,11 +1153,14 @@ static hipError_t propose_impl(const DraftArgs& a, int32_t* x_out, float* pd_x, 
     }
     const int grid = xcd_grid(n_gran * t.n_chunks);
     // many requests, bf16 weights filling the k-steps: the pipelined tile
-    const bool piped = std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16 || KS == 32) && a.r == 16 * KS &&
+    // (r = 512 keeps the staged tile: its W2 slice alone would take 128 of
+    // the pipelined tile's 170 registers per lane)
+    const bool piped = std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16) && a.r == 16 * KS &&
                        a.R > PIPED_TILE_MIN_R;
     int pgrid = 0;
-    if constexpr (KS == 8 || KS == 16 || KS == 32) {
+    if constexpr (KS == 8 || KS == 16) {
         if (piped) {
+            t.div_rb = FastDiv::make((a.R + BLOCK_ROWS - 1) / BLOCK_ROWS);
             const long units = (long)n_gran * ((a.R + BLOCK_ROWS - 1) / BLOCK_ROWS);
             const int slots =
                 a.greedy ? tile_ws_slots<KS, true>(t.vec4 != 0) : tile_ws_slots<KS, false>(t.vec4 != 0);

@@ -566,6 +566,17 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
         __syncthreads();
         // stage s: its own values are in set s % 3, refilled for stage s+3
         auto stage = [&](int2& tr, Ctx& c, int s) __attribute__((always_inline)) {
+            // unit s's tile first: the W1 rows of unit s+1, loaded last stage,
+            // have until it is done to arrive
+            if (s < nu) {
+                store_tile(sZ[s & 1], A.mfma_acc(sB[s & 1], lane, f32x16{}), w, lane);
+                // the next unit in another granule: its W2 slice
+                const int gn = ugran(s + 1);
+                if (s + 1 < nu && gn != ga) {
+                    ga = gn;
+                    A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
+                }
+            }
             gw.commit(sB[(s + 1) & 1], 0, t);
             if (t < 32) {
                 // unit s+3's tokens
@@ -584,15 +595,6 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
             // the CU's queue that the streamed rows also need)
             if (w == 0) tr = raw_tokens(s + 6);
             if (w == 1) c = raw_ctx(s + 3);
-            if (s < nu) {
-                store_tile(sZ[s & 1], A.mfma_acc(sB[s & 1], lane, f32x16{}), w, lane);
-                // the next unit in another granule: its W2 slice
-                const int gn = ugran(s + 1);
-                if (s + 1 < nu && gn != ga) {
-                    ga = gn;
-                    A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
-                }
-            }
             __syncthreads();
         };
         for (int s = 0; s < n_stages; s += 3) {
