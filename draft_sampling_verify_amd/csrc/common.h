@@ -428,7 +428,7 @@ __device__ inline int granule_pick(float ea, float eb, float before, float targe
 struct FastDiv {
     uint32_t m;
     int l;
-    static inline FastDiv make(int d)
+    __host__ __device__ static inline FastDiv make(int d)
     {
         FastDiv f;
         f.l = 0;

@@ -55,6 +55,8 @@ struct VerifyWs {
     float2* drow;    // confidence only: [VR] draft (M, S)
     double* contrib; // loss only: [VR] weighted loss of each position
     float4* tpart;   // [TR, 16] per-part target row statistics (rows split over workgroups)
+    int4* rtab;      // [VR] scheduled lengths: per verified row (x_{k-1}, x_k, U row, target row)
+    float4* rctab;   // [VR] scheduled lengths: per verified row (M_d, S_d, M_t, S_t)
 };
 
 inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence, size_t* bytes,
@@ -82,6 +84,8 @@ inline VerifyWs carve_verify(void* ws, int R, int gamma, int V, bool confidence,
     }
     if (loss) w.contrib = c.take<double>(VR);
     w.tpart = c.take<float4>(TR * 16);
+    w.rtab = c.take<int4>(VR);
+    w.rctab = c.take<float4>(VR);
     if (bytes) *bytes = c.off;
     return w;
 }

@@ -83,6 +83,25 @@ __global__ __launch_bounds__(TILE_THREADS) void k_plan(const int32_t* ell, int R
     }
 }
 
+// With scheduled lengths: everything the pipelined sweep needs of verified
+// row f in two 16-byte records, so that it reads them with one load each
+// (no load whose address comes from another): the tokens (x_{k-1}, x_k),
+// the U and target rows, and the draft's and target's (M, S).  Runs after
+// the target rows' statistics.
+__global__ __launch_bounds__(TILE_THREADS) void k_row_table(const int4* vmap, const int32_t* counts,
+                                                            const int32_t* x0, const int32_t* x,
+                                                            const float* dstats, const float2* trow, int gamma,
+                                                            int max_rows, int4* rtab, float4* rctab)
+{
+    const int f = blockIdx.x * TILE_THREADS + threadIdx.x;
+    if (f >= max_rows || f >= counts[0]) return;
+    const int4 vi = vmap[f];  // (request, k, compact target row)
+    const int so = vi.x * gamma + vi.y - 1;
+    rtab[f] = make_int4(vi.y == 1 ? x0[vi.x] : x[so - 1], x[so], so, vi.x * (gamma + 1) + vi.y - 1);
+    const float2 ts = trow[vi.z];
+    rctab[f] = make_float4(dstats[2 * (size_t)so], dstats[2 * (size_t)so + 1], ts.x, ts.y);
+}
+
 // ---------------------------------------------------------- target stats
 
 struct TargetArgs {
@@ -246,8 +265,10 @@ struct SweepArgs {
     float2* vpart;        // [rows, n_gran] (TV mass, residual mass)
     float* vbias;         // [rows] Markov bias at the drafted id x_k
     int staged_only;      // the call asked for the staged sweep (PATH_NO_PIPELINED_SWEEP)
-    FastDiv div_rb;       // by the number of 32-row blocks (the pipelined sweep)
+    FastDiv div_rb;       // by the number of 32-row blocks (the pipelined sweep, every row verified)
     FastDiv div_g;        // by gamma
+    const int4* rtab;     // scheduled lengths: per verified row (x_{k-1}, x_k, U row, target row)
+    const float4* rctab;  // scheduled lengths: per verified row (M_d, S_d, M_t, S_t)
 };
 
 // Verified row f: where its data lives and the normalisers of p_d and p_t.
@@ -447,8 +468,8 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
     }
 }
 
-// The pipelined sweep, for the implicit row map (every position of every
-// request verified).  The work is a sequence of units, unit u = (granule
+// The pipelined sweep (every position of every request verified, or the
+// scheduled rows through the row tables).  The work is a sequence of units, unit u = (granule
 // u / n_rb, 32-row block u % n_rb); each workgroup takes a contiguous run of
 // units (runs differ in length by at most one), so the pipeline below fills
 // and drains once per workgroup and W2 is reloaded only where the run
@@ -475,30 +496,46 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
 // results go out as plain stores that stay in flight.  Each group first uses what arrived and only then
 // issues new loads, all without a branch, so every wait the compiler places
 // is for loads of an earlier stage.
-template <int KS, bool VEC4>
+template <int KS, bool VEC4, bool MAPS>
 __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepArgs p)
 {
     using Ops = TileOps<bf16w, KS>;
     using GW = W1Regs<Ops::RS, KS, 1>;
-    const int nrows = p.max_rows;
+    // rows: every position of every request, or the scheduled rows (their
+    // count is known on the device only)
+    const int nrows = MAPS ? p.counts[0] : p.max_rows;
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
+    if (n_rb <= 0) return;
     const UnitRun run(p.n_gran, n_rb);
     const int nu = run.nu;
     if (nu <= 0) return;
+    const FastDiv div_rb = MAPS ? FastDiv::make(n_rb) : p.div_rb;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const bf16w* W1 = reinterpret_cast<const bf16w*>(p.W1);
     // unit j of this run (j may pass the run's end: such units repeat the
     // last one; their values are loaded and never used)
     auto unit = [&](int j) { return run.unit(j); };
-    auto ugran = [&](int j) { return p.div_rb.div(unit(j)); };
+    auto ugran = [&](int j) { return div_rb.div(unit(j)); };
     auto urow = [&](int j, int i) {
         const int u = unit(j);
-        return (u - p.div_rb.div(u) * n_rb) * BLOCK_ROWS + i;
+        return (u - div_rb.div(u) * n_rb) * BLOCK_ROWS + i;
+    };
+    // raw values of verified row q (clamped to row 0 past the end): its
+    // tokens (x_{k-1}, x_k), its U row and its target row
+    auto raw_row = [&](int q) __attribute__((always_inline)) {
+        const int qc = q < nrows ? q : 0;
+        if constexpr (MAPS) {
+            return p.rtab[qc];
+        } else {
+            const int r = p.div_g.div(qc), kk = qc - r * p.gamma;
+            return make_int4(kk == 0 ? p.x0[r] : p.x[qc - 1], p.x[qc], qc, r * (p.gamma + 1) + kk);
+        }
     };
 
     __shared__ __align__(16) char sB[2][32 * Ops::RS * Ops::ELEM];  // W1 tiles, unit j in j & 1
     __shared__ __align__(16) float sZ[2][32 * ZS];                 // bias tiles, unit j in j & 1
     __shared__ int s_tok[8][32];                                    // checked tokens, unit j in j & 7
+    __shared__ int2 s_rows[8][32];                                  // (U row, target row), unit j in j & 7
     __shared__ int s_xk[2][32];                                     // x_k
     __shared__ float s_cf[2][4][32];                                // M_d, S_d, M_t, S_t
 
@@ -506,7 +543,9 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
     // values and are masked where used.
     if (t < 96) {
         const int j = t >> 5, q = urow(j, t & 31);
-        s_tok[j][t & 31] = q < nrows ? tok_check(tok_raw<false>(p, q, nrows), p.V) : -1;
+        const int4 e = raw_row(q);
+        s_tok[j][t & 31] = q < nrows ? tok_check(make_int2(e.x, e.y), p.V) : -1;
+        s_rows[j][t & 31] = make_int2(e.z, e.w);
     }
     // stage s computes unit s's tile (s < nu), finishes unit s-1 and stores
     // unit s-2's results: stages 0..nu+1, rounded up to a multiple of three
@@ -522,26 +561,31 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
         A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
         // raw per-row values of unit j for row lane & 31 (wave 0: tokens,
         // wave 1: row context)
-        auto raw_tokens = [&](int j) __attribute__((always_inline)) {
-            const int q = urow(j, lane & 31), qc = q < nrows ? q : 0;
-            const int r = p.div_g.div(qc), kk = qc - r * p.gamma;
-            return make_int2(kk == 0 ? p.x0[r] : p.x[qc - 1], p.x[qc]);
-        };
+        auto raw_tokens = [&](int j) __attribute__((always_inline)) { return raw_row(urow(j, lane & 31)); };
         struct Ctx {
             int xk;
             float md, sd, mt, st;
         };
         auto raw_ctx = [&](int j) __attribute__((always_inline)) {
             const int q = urow(j, lane & 31), qc = q < nrows ? q : 0;
-            const int r = p.div_g.div(qc), kk = qc - r * p.gamma;
-            // target row (r, kk) of the first pass: P rows per request
-            const float* ts = reinterpret_cast<const float*>(p.trow) + 2 * ((size_t)r * p.P + kk);
             Ctx c;
-            c.xk = p.x[qc];
-            c.md = p.dstats[2 * (size_t)qc];
-            c.sd = p.dstats[2 * (size_t)qc + 1];
-            c.mt = ts[0];
-            c.st = ts[1];
+            if constexpr (MAPS) {
+                const float4 v = p.rctab[qc];
+                c.xk = p.rtab[qc].y;
+                c.md = v.x;
+                c.sd = v.y;
+                c.mt = v.z;
+                c.st = v.w;
+            } else {
+                const int r = p.div_g.div(qc), kk = qc - r * p.gamma;
+                // target row (r, kk) of the first pass: P rows per request
+                const float* ts = reinterpret_cast<const float*>(p.trow) + 2 * ((size_t)r * p.P + kk);
+                c.xk = p.x[qc];
+                c.md = p.dstats[2 * (size_t)qc];
+                c.sd = p.dstats[2 * (size_t)qc + 1];
+                c.mt = ts[0];
+                c.st = ts[1];
+            }
             return c;
         };
         GW gw;
@@ -551,7 +595,7 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
         // the per-row values of stages 0, 1 and 2 in three register sets
         // (issued after the W1 rows, as in every stage: the waits placed in
         // the loop hold for its first stage too)
-        int2 trn[3] = {};
+        int4 trn[3] = {};
         Ctx cx[3] = {};
         if (w == 0) {
             trn[0] = raw_tokens(3);
@@ -565,7 +609,7 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
         }
         __syncthreads();
         // stage s: its own values are in set s % 3, refilled for stage s+3
-        auto stage = [&](int2& tr, Ctx& c, int s) __attribute__((always_inline)) {
+        auto stage = [&](int4& tr, Ctx& c, int s) __attribute__((always_inline)) {
             // unit s's tile first: the W1 rows of unit s+1, loaded last stage,
             // have until it is done to arrive
             if (s < nu) {
@@ -579,9 +623,10 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
             }
             gw.commit(sB[(s + 1) & 1], 0, t);
             if (t < 32) {
-                // unit s+3's tokens
+                // unit s+3's tokens and rows
                 const int q = urow(s + 3, t);
-                s_tok[(s + 3) & 7][t] = q < nrows ? tok_check(tr, p.V) : -1;
+                s_tok[(s + 3) & 7][t] = q < nrows ? tok_check(make_int2(tr.x, tr.y), p.V) : -1;
+                s_rows[(s + 3) & 7][t] = make_int2(tr.z, tr.w);
             } else if (w == 1 && lane < 32) {
                 // unit s's row context, read by the epilogue next stage
                 s_xk[s & 1][lane] = c.xk;
@@ -610,12 +655,10 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
         // issue unit j's U and target rows (j past the run: its last unit
         // again, so the code stays free of branches around loads)
         auto issue = [&](int j, float (&zu)[8], float (&zt)[8]) __attribute__((always_inline)) {
-            const int jj = min(j, nu - 1);
-            const int f = urow(jj, er), fc = f < nrows ? f : 0;
-            const int req = p.div_g.div(fc), kk = fc - req * p.gamma;
-            const int cbase = ugran(jj) * GRAN + ec;
-            load8_raw<VEC4>(p.U + (size_t)fc * p.V, cbase, p.V, zu);
-            load8_raw<VEC4>(p.Lt + ((size_t)req * (p.gamma + 1) + kk) * p.V, cbase, p.V, zt);
+            const int2 rows = s_rows[j & 7][er];  // (units past the run: its last unit's rows)
+            const int cbase = ugran(min(j, nu - 1)) * GRAN + ec;
+            load8_raw<VEC4>(p.U + (size_t)rows.x * p.V, cbase, p.V, zu);
+            load8_raw<VEC4>(p.Lt + (size_t)rows.y * p.V, cbase, p.V, zt);
         };
         float zuA[8], ztA[8], zuB[8], ztB[8], zuC[8], ztC[8];  // unit j in A, B, C by j % 3
         issue(0, zuA, ztA);
@@ -1324,6 +1367,8 @@ static SweepArgs make_sweep(const DraftArgs& a, const float* dstats, const float
     sweep_grid(s.max_rows, s.n_gran, s.bpc, s.n_chunks);
     s.div_rb = FastDiv::make((s.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
     s.div_g = FastDiv::make(a.gamma);
+    s.rtab = w.rtab;
+    s.rctab = w.rctab;
     s.vmap = maps ? w.vmap : nullptr;
     s.counts = counts;
     s.trow = w.trow;
@@ -1370,8 +1415,8 @@ static int sweep_ws_slots()
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_verify_sweep_ws<KS, VEC4>, 3 * TILE_THREADS,
-                                                         0) != hipSuccess || per_cu <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_verify_sweep_ws<KS, VEC4, false>,
+                                                         3 * TILE_THREADS, 0) != hipSuccess || per_cu <= 0)
             per_cu = 1;
         v = per_cu * cus + 1;
         cache[dev].store(v, std::memory_order_relaxed);
@@ -1387,7 +1432,13 @@ static void launch_sweep(const SweepArgs& sw, hipStream_t s)
     // (r = 512 keeps the staged kernel: its W2 slice alone would take 128 of
     // the pipelined kernel's 170 registers per lane)
     if constexpr (std::is_same<WT, bf16w>::value && (KS == 8 || KS == 16)) {
-        if (sw.r == 16 * KS && !sw.vmap && !sw.staged_only) {
+        if (sw.r == 16 * KS && !sw.staged_only) {
+            if (sw.vmap) {
+                // the scheduled rows' records, after the target rows' statistics
+                hipLaunchKernelGGL(k_row_table, dim3((sw.max_rows + TILE_THREADS - 1) / TILE_THREADS),
+                                   dim3(TILE_THREADS), 0, s, sw.vmap, sw.counts, sw.x0, sw.x, sw.dstats, sw.trow,
+                                   sw.gamma, sw.max_rows, const_cast<int4*>(sw.rtab), const_cast<float4*>(sw.rctab));
+            }
             // as many workgroups as fit at once, each with one run of units
             const long units = (long)sw.n_gran * ((sw.max_rows + BLOCK_ROWS - 1) / BLOCK_ROWS);
             const dim3 blk2(3 * TILE_THREADS);
@@ -1396,12 +1447,13 @@ static void launch_sweep(const SweepArgs& sw, hipStream_t s)
                 const long n = std::min<long>(slots, units);
                 return (unsigned)(n >= NUM_XCD ? n / NUM_XCD * NUM_XCD : xcd_grid((int)n));
             };
-            if (sw.vec4) {
-                hipLaunchKernelGGL((k_verify_sweep_ws<KS, true>), dim3(grid_of(sweep_ws_slots<KS, true>())), blk2, 0,
-                                   s, sw);
+            const dim3 g2(grid_of(sw.vec4 ? sweep_ws_slots<KS, true>() : sweep_ws_slots<KS, false>()));
+            if (sw.vmap) {
+                if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep_ws<KS, true, true>), g2, blk2, 0, s, sw);
+                else hipLaunchKernelGGL((k_verify_sweep_ws<KS, false, true>), g2, blk2, 0, s, sw);
             } else {
-                hipLaunchKernelGGL((k_verify_sweep_ws<KS, false>), dim3(grid_of(sweep_ws_slots<KS, false>())), blk2,
-                                   0, s, sw);
+                if (sw.vec4) hipLaunchKernelGGL((k_verify_sweep_ws<KS, true, false>), g2, blk2, 0, s, sw);
+                else hipLaunchKernelGGL((k_verify_sweep_ws<KS, false, false>), g2, blk2, 0, s, sw);
             }
             return;
         }

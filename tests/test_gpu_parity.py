@@ -39,9 +39,8 @@ SMALL = {
     # k-steps, R <= 32; a ragged request count; more requests than granules
     "fused_r256": Config("fused_r256", 17, 29, 7, 5000, 256, True, 1.0, 3.0, 0.02, 1.0),
     "fused_many_req": Config("fused_many_req", 18, 30, 4, 300, 64, True, 1.0, 2.0, 0.1, 0.7),
-    # the verify sweep that gathers W1 straight into LDS (bf16, r = 128 /
-    # 256 / 512): V % 4 != 0 with a ragged last block; several 32-row blocks
-    # per workgroup (its double-buffered gather)
+    # the pipelined verify sweep (bf16, r = 128 / 256): V % 4 != 0 with a
+    # ragged last block; several 32-row blocks per workgroup
     "lds_r128_odd": Config("lds_r128_odd", 19, 37, 3, 1001, 128, True, 1.0, 2.0, 0.05, 0.5),
     "lds_multi": Config("lds_multi", 20, 40, 7, 40000, 256, True, 1.0, 3.0, 0.02, 1.0),
     # the pipelined per-position tile (more than 96 requests, bf16, r = 128 /
@@ -172,9 +171,9 @@ def test_propose_paths_agree_with_oracle(name):
 
 @pytest.mark.parametrize("name", ["lds_multi", "rank512", "lds_r128_odd"])
 def test_verify_sweep_paths_identical(name):
-    """The sweep that gathers W1 rows straight into LDS and the one that
-    stages them through registers compute the same products in the same
-    order: verify (fixed and scheduled lengths, sampled and greedy) and
+    """The pipelined sweep and the staged one compute the same products and
+    sum them in the same order: verify (fixed lengths, scheduled lengths
+    through the row tables, and every length zero; sampled and greedy) and
     confidence outputs are bit-identical, and match the oracle."""
     cfg = SMALL[name]
     d = workloads.make(cfg)
@@ -183,18 +182,18 @@ def test_verify_sweep_paths_identical(name):
     x, pdx, pds = run_propose(t, cfg, False, ws=ws)
     rng = np.random.default_rng(cfg.index + 100)
     ell = rng.integers(0, cfg.gamma + 1, cfg.R).astype(np.int32)
-    ell_d = torch.from_numpy(ell).cuda()
+    lens_cases = {"fixed": None, "scheduled": ell, "zero": np.zeros(cfg.R, np.int32)}
     outs = {}
     for lds in (True, False):
         path = 0 if lds else STAGED
         for greedy in (False, True):
-            for lens in (None, ell):
-                res = run_verify(t, cfg, x, pds, greedy, ell=None if lens is None else ell_d, ws=ws, path=path)
+            for kind, lens in lens_cases.items():
+                ell_d = None if lens is None else torch.from_numpy(lens).cuda()
+                res = run_verify(t, cfg, x, pds, greedy, ell=ell_d, ws=ws, path=path)
                 res = [np_(v) for v in res]
                 st = check_verify(d, np_(x), lens, *res, greedy)
-                log("  %s %s %s" % ("lds" if lds else "staged", "greedy" if greedy else "sampled",
-                                    "fixed" if lens is None else "scheduled"), st)
-                outs[lds, greedy, lens is None] = res
+                log("  %s %s %s" % ("pipelined" if lds else "staged", "greedy" if greedy else "sampled", kind), st)
+                outs[lds, greedy, kind] = res
         cs, a = spec.spec_confidence(t["U"], t["W1"], t["W2p"], t["x0"], x, t["Lt"], cfg.T, pd_stats=pds, ws=ws,
                                      path=path)
         torch.cuda.synchronize()
