@@ -277,7 +277,7 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
         }
         return tk;
     };
-    if (t < 96) {
+    if (t < 128) {
         const int j = t >> 5, q = urow(j, t & 31);
         s_tok[j][t & 31] = checked(q < nrows ? *tok_src(q) : -1, q, j);
     }
@@ -292,45 +292,51 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
         int ga = ugran(0);
         Ops A;
         A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
-        // raw token of unit j for row lane & 31 (wave 0)
+        // raw token of unit j for row lane & 31
         auto raw_token = [&](int j) __attribute__((always_inline)) {
             const int q = urow(j, lane & 31), qc = q < nrows ? q : 0;
             return *tok_src(qc);
         };
-        GW gw;
-        gw.issue(W1, s_tok[0], 0, t);
-        gw.commit(sB[0], 0, t);
-        gw.issue(W1, s_tok[1], 0, t);
-
-        // the tokens of stages 0, 1 and 2 in three registers (issued after
-        // the W1 rows, as in every stage)
-        int trn[3] = {};
-        if (w == 0) {
-            trn[0] = raw_token(3);
-            trn[1] = raw_token(4);
-            trn[2] = raw_token(5);
-        }
+        // unit j's W1 rows are loaded into g[j % 3], two stages before they
+        // are written to LDS; the tokens of units 4, 5 and 6 into three
+        // registers.  The loads go out in the order of every stage (W1 rows,
+        // then a token), so the waits of the first stages are the loop's.
+        // Every MFMA wave loads the tokens (wave 0 uses them): the count of
+        // loads in flight is then the same in every wave, and a wait for W1
+        // rows is never a wait for younger loads.
+        GW g0, g1, g2;
+        int trn[3];
+        trn[0] = raw_token(4);
+        g0.issue(W1, s_tok[0], 0, t);
+        g0.commit(sB[0], 0, t);
+        g1.issue(W1, s_tok[1], 0, t);
+        trn[1] = raw_token(5);
+        g2.issue(W1, s_tok[2], 0, t);
+        trn[2] = raw_token(6);
         __syncthreads();
-        // stage s: its token is in trn[s % 3], refilled for stage s+3
-        auto stage = [&](int& tr, int s) __attribute__((always_inline)) {
-            gw.commit(sB[(s + 1) & 1], 0, t);
-            if (t < 32) s_tok[(s + 3) & 7][t] = checked(tr, urow(s + 3, t), s + 3);
-            gw.issue(W1, s_tok[(s + 2) & 7], 0, t);
-            if (w == 0) tr = raw_token(s + 6);
+        // stage s: unit s+4's token is in trn[s % 3], refilled for unit s+7.
+        // The next granule's W2 slice is loaded before this stage's W1 rows
+        // and token: a wait for the slice (in the next stage, on either
+        // path of the granule test) is then never a wait for them.
+        auto stage = [&](int& tr, GW& gc, GW& gi, int s) __attribute__((always_inline)) {
+            gc.commit(sB[(s + 1) & 1], 0, t);
+            if (t < 32) s_tok[(s + 4) & 7][t] = checked(tr, urow(s + 4, t), s + 4);
             if (s < nu) {
-                store_tile(sZ[s & 1], A.mfma_acc(sB[s & 1], lane, f32x16{}), w, lane);
+                store_tile(sZ[s & 1], A.template mfma_acc_la<6>(sB[s & 1], lane, f32x16{}), w, lane);
                 const int gn = ugran(s + 1);
                 if (s + 1 < nu && gn != ga) {
                     ga = gn;
                     A.load_a(p.W2p, KS, 4 * ga + w, 4 * ga + w < nblk, lane);
                 }
             }
+            gi.issue(W1, s_tok[(s + 3) & 7], 0, t);
+            tr = raw_token(s + 7);
             __syncthreads();
         };
         for (int s = 0; s < n_stages; s += 3) {
-            stage(trn[0], s);
-            stage(trn[1], s + 1);
-            stage(trn[2], s + 2);
+            stage(trn[0], g1, g0, s);
+            stage(trn[1], g2, g1, s + 1);
+            stage(trn[2], g0, g2, s + 2);
         }
     } else {
         // ---------------------------------------------- epilogue waves

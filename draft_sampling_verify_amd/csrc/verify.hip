@@ -613,7 +613,7 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
             // unit s's tile first: the W1 rows of unit s+1, loaded last stage,
             // have until it is done to arrive
             if (s < nu) {
-                store_tile(sZ[s & 1], A.mfma_acc(sB[s & 1], lane, f32x16{}), w, lane);
+                store_tile(sZ[s & 1], A.template mfma_acc_la<KS >= 16 ? 3 : 6>(sB[s & 1], lane, f32x16{}), w, lane);
                 // the next unit in another granule: its W2 slice
                 const int gn = ugran(s + 1);
                 if (s + 1 < nu && gn != ga) {
