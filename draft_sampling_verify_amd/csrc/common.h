@@ -328,61 +328,6 @@ __device__ inline int wave_granule_find(WF wf, int g0, int g1, double excl, doub
     return lp < 0 ? 0 : lp;
 }
 
-// Register-cached inverse CDF over at most 64 NR granule masses, one wave.
-// Lane l holds w[i] = mass of granule l + 64 i (0 past the end): the caller
-// loads all of them at once (coalesced, one memory round trip).  Round i
-// covers granules 64 i .. 64 i + 63 in lane order, so the rounds in order
-// are the granules in vocabulary order.  Returns the first granule of
-// positive mass whose running sum exceeds u * total, the running sum before
-// it and the total, identical in every lane; if rounding leaves none, the
-// last granule with positive mass (fallback set).
-template <int NR>
-__device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& total, float& before, bool& fallback)
-{
-    const int lane = threadIdx.x & (WAVE - 1);
-    float T[NR];
-    float Z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        T[i] = wave_sum(w[i]);
-        Z += T[i];
-    }
-    total = Z;
-    const float target = u * Z;
-    float pre = 0.0f, rbase = 0.0f;
-    int rstar = -1;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        if (rstar < 0 && T[i] > 0.0f && pre + T[i] > target) {
-            rstar = i;
-            rbase = pre;
-        }
-        pre += T[i];
-    }
-    float wr = 0.0f;
-    int lastpos = -1;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        if (i == rstar) wr = w[i];
-        if (w[i] > 0.0f) lastpos = lane + WAVE * i;
-    }
-    const float incl = wave_incl_scan(wr);
-    float ex = __shfl_up(incl, 1, WAVE);
-    if (lane == 0) ex = 0.0f;
-    const float run0 = rbase + ex;
-    const unsigned long long hit = __ballot(rstar >= 0 && wr > 0.0f && run0 + wr > target);
-    if (hit) {
-        const int L = __ffsll((long long)hit) - 1;
-        fallback = false;
-        before = __shfl(run0, L, WAVE);
-        return L + WAVE * rstar;
-    }
-    fallback = true;
-    before = 0.0f;
-    const int lp = -wave_min(-lastpos);
-    return lp < 0 ? 0 : lp;
-}
-
 // Inside one granule, run by a single full wave: lane l holds the weights of
 // ids 2l and 2l+1 of the granule.  Picks the first id whose running sum
 // (from `before`) exceeds target; if none (rounding, or `fallback`), the
@@ -1084,6 +1029,17 @@ __device__ inline float wave_scan_dpp(float v)
 // The previous lane's value (0 in lane 0).
 __device__ inline float lane_before(float v) { return dpp_z<DPP_WAVE_SHR1, 0xF>(v); }
 __device__ inline float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+// Sum over the wave, the same bits in every lane: the 16-lane row sums on
+// DPP (hex_sum), then (row 0 + row 1) + (row 2 + row 3) from scalar reads.
+__device__ inline float wave_total_dpp(float v)
+{
+    v = hex_sum(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
 // Maximum over the wave, in every lane.
 __device__ inline float wave_max_dpp(float v)
 {
@@ -1098,6 +1054,60 @@ __device__ inline float wave_max_dpp(float v)
                                                             0xC, 0xF, false)));
     return lane63(v);
 }
+// Register-cached inverse CDF over at most 64 NR granule masses, one wave.
+// Lane l holds w[i] = mass of granule l + 64 i (0 past the end): the caller
+// loads all of them at once (coalesced, one memory round trip).  Round i
+// covers granules 64 i .. 64 i + 63 in lane order, so the rounds in order
+// are the granules in vocabulary order.  Returns the first granule of
+// positive mass whose running sum exceeds u * total, the running sum before
+// it and the total, identical in every lane; if rounding leaves none, the
+// last granule with positive mass (fallback set).  The round totals and the
+// scan inside the chosen round run on DPP (no LDS round trips).
+template <int NR>
+__device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& total, float& before, bool& fallback)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    float T[NR];
+    float Z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        T[i] = wave_total_dpp(w[i]);
+        Z += T[i];
+    }
+    total = Z;
+    const float target = u * Z;
+    float pre = 0.0f, rbase = 0.0f;
+    int rstar = -1;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        if (rstar < 0 && T[i] > 0.0f && pre + T[i] > target) {
+            rstar = i;
+            rbase = pre;
+        }
+        pre += T[i];
+    }
+    float wr = 0.0f;
+    int lastpos = -1;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        if (i == rstar) wr = w[i];
+        if (w[i] > 0.0f) lastpos = lane + WAVE * i;
+    }
+    const float ex = lane_before(wave_scan_dpp(wr));
+    const float run0 = rbase + ex;
+    const unsigned long long hit = __ballot(rstar >= 0 && wr > 0.0f && run0 + wr > target);
+    if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        fallback = false;
+        before = __shfl(run0, L, WAVE);
+        return L + WAVE * rstar;
+    }
+    fallback = true;
+    before = 0.0f;
+    const int lp = -wave_min(-lastpos);
+    return lp < 0 ? 0 : lp;
+}
+
 __device__ inline int wave_max_int_dpp(int v)
 {
     v = max(v, dpp_i<DPP_XOR1>(v));

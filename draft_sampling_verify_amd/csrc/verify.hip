@@ -869,11 +869,15 @@ __device__ inline int draw_target_row(const ResolveArgs& a, int trow, int req, i
     const int ca = gstar * GRAN + 2 * lane, cb = ca + 1;
     const float za = ca < p.V ? L[ca] : -INFINITY, zb = cb < p.V ? L[cb] : -INFINITY;
     float e;
-    return gstar * GRAN + granule_pick(softw(za, M, c), softw(zb, M, c), before, target, fallback, e);
+    return gstar * GRAN + granule_pick_dpp(softw(za, M, c), softw(zb, M, c), before, target, fallback, e);
 }
 
-constexpr int RES_THREADS = 512;
-constexpr int RES_WAVES = RES_THREADS / WAVE;
+// Resolve workgroups of eight waves (the granule rescan needs up to 256
+// VGPRs): RES_SEARCH waves for the per-position c* and residual search, the
+// last one for the accept tests.
+constexpr int RES_WAVES = 8;
+constexpr int RES_SEARCH = RES_WAVES - 1;
+constexpr int RES_THREADS = RES_WAVES * WAVE;
 
 // The draft side of the resolve, for drafts of the Markov head: p_d(x) from
 // U, the bias the sweep recorded at x and propose's (M, S); the residual
@@ -1002,9 +1006,10 @@ struct ClusterDraft {
 
 // One workgroup of eight waves per request.
 // Phase 1 does everything that does not depend on which position is rejected
-// first, in parallel: the accept test of every verified position (one thread
-// each, fp64 on the drafted id), c* of every position and the residual
-// granule search of every position (one wave each), and the bonus draw.
+// first, in parallel: the accept test of every verified position (one lane
+// each of the last wave, fp64 on the drafted id), c* of every position and
+// the residual granule search of every position (position k on wave
+// (k - 1) % RES_SEARCH), and the bonus draw (the last wave again).
 // Phase 2 rescans one granule of the first rejected position's residual
 // (the draft side's waves).
 template <class D, bool GREEDY>
@@ -1030,36 +1035,37 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
     const int toff = a.toff ? a.toff[r] : r * p.P;
     bool bad = bad_len || dr.bad_anchor(a, r);
 
-    // ---- phase 1a: accept tests, one thread per verified position
-    if (t < L) {
-        const int xk = p.x[(size_t)r * G + t];
+    // ---- phase 1a: accept tests, one lane of wave RES_SEARCH per position
+    const int ia = t - RES_SEARCH * WAVE;  // the position (0-based) of this lane
+    if (ia >= 0 && ia < L) {
+        const int xk = p.x[(size_t)r * G + ia];
         if (xk < 0 || xk >= p.V) {
             bad = true;
         } else {
-            const int tr = toff + t;
+            const int tr = toff + ia;
             const float2 ts = p.trow[tr];
-            const double zt = (double)p.Lt[((size_t)r * (G + 1) + t) * p.V + xk];
+            const double zt = (double)p.Lt[((size_t)r * (G + 1) + ia) * p.V + xk];
             const double pt = exp2((zt - (double)ts.x) * (double)p.c) / (double)ts.y;
             int acc;
             if (GREEDY) {
                 acc = xk == a.targ[tr];
             } else {
-                const double pd = dr.pd_at(a, r, t, xk, voff);
+                const double pd = dr.pd_at(a, r, ia, xk, voff);
                 double ratio;
                 if (pd > 0.0) ratio = pt / pd;
                 else ratio = pt > 0.0 ? INFINITY : 0.0;
-                const double u1 = u24d(philox((uint32_t)(t + 1), (uint32_t)r, a.round, a.seed).w[1]);
+                const double u1 = u24d(philox((uint32_t)(ia + 1), (uint32_t)r, a.round, a.seed).w[1]);
                 acc = u1 < ratio;
             }
-            s_acc[t] = acc;
-            if (a.pt_x) a.pt_x[(size_t)r * G + t] = (float)pt;
+            s_acc[ia] = acc;
+            if (a.pt_x) a.pt_x[(size_t)r * G + ia] = (float)pt;
         }
-    } else if (t < G) {
-        if (a.pt_x) a.pt_x[(size_t)r * G + t] = NAN;
-        if (a.c_star) a.c_star[(size_t)r * G + t] = NAN;
+    } else if (ia >= L && ia < G) {
+        if (a.pt_x) a.pt_x[(size_t)r * G + ia] = NAN;
+        if (a.c_star) a.c_star[(size_t)r * G + ia] = NAN;
     }
     // ---- phase 1b: per position, one wave: c* and the residual granule search
-    for (int k = w + 1; k <= L; k += RES_WAVES) {
+    for (int k = w + 1; w < RES_SEARCH && k <= L; k += RES_SEARCH) {
         const float2* vp = p.vpart + (size_t)(voff + k - 1) * p.n_gran;
         const float u2 = u24f(philox((uint32_t)k, (uint32_t)r, a.round, a.seed).w[2]);
         float Z, before, tv;
@@ -1073,8 +1079,9 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
             s_Z[k - 1] = Z;
         }
     }
-    // ---- phase 1c: the bonus draw after a full accept (wave L % 8)
-    if (w == L % RES_WAVES) {
+    // ---- phase 1c: the bonus draw after a full accept (the last wave, after
+    // its accept tests)
+    if (w == RES_SEARCH) {
         int yb;
         if (GREEDY) {
             yb = a.targ[toff + L];
@@ -1111,7 +1118,7 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
         __syncthreads();
         if (w == 0) {
             float e;
-            const int y = gstar * GRAN + granule_pick(zrow[2 * lane], zrow[2 * lane + 1], s_before[kstar - 1],
+            const int y = gstar * GRAN + granule_pick_dpp(zrow[2 * lane], zrow[2 * lane + 1], s_before[kstar - 1],
                                                       s_Z[kstar - 1] * u24f(philox((uint32_t)kstar, (uint32_t)r,
                                                                                    a.round, a.seed).w[2]),
                                                       s_fb[kstar - 1], e);
