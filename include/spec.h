@@ -291,14 +291,14 @@ int spec_verify(const float* U, const void* W1, const void* W2p, int w_dtype,
 
 /* spec_verify with an explicit kernel path (SPEC_PATH_* bits).  The sweep
  * recomputes the Markov bias of every verified row in 32-row blocks.  For
- * bf16 weights with r = 128 or 256 and every position verified
- * (ell == NULL) it runs as a software pipeline: half of each workgroup
- * gathers W1 rows straight into on-chip memory one block ahead and computes
- * the bias tiles on the matrix cores, the other half streams U and target
- * rows two blocks ahead and finishes each block.  Otherwise (or with
- * SPEC_PATH_NO_PIPELINED_SWEEP) the W1 rows are staged through registers and
- * one workgroup does each block start to end.  Both compute the same
- * products in the same order (identical results). */
+ * bf16 weights with r = 128 or 256 (every position verified, or lengths
+ * ell) it runs as a software pipeline, one workgroup per compute unit: a
+ * third of each workgroup computes the bias tiles on the matrix cores, with
+ * the W1 rows of the next block loaded through registers one block ahead;
+ * the rest streams U and target rows two blocks ahead and finishes each
+ * block.  Otherwise (r = 512, fp32 weights, or with
+ * SPEC_PATH_NO_PIPELINED_SWEEP) one workgroup does each block start to end.
+ * Both compute the same products in the same order (identical results). */
 int spec_verify_ex(const float* U, const void* W1, const void* W2p, int w_dtype,
                    const int32_t* x0, const int32_t* x, const float* pd_stats,
                    const float* Lt, const int32_t* ell,
