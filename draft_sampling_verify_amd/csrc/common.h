@@ -1125,7 +1125,6 @@ __device__ inline int wave_min_int_dpp(int v) { return -wave_max_int_dpp(-v); }
 // target, else (rounding, or `fallback`) the last id of positive weight.
 __device__ inline int granule_pick_dpp(float ea, float eb, float before, float target, bool fallback, float& e_out)
 {
-    const int lane = threadIdx.x & (WAVE - 1);
     const float incl = wave_scan_dpp(ea + eb);
     const float ex = lane_before(incl);
     const float ca = (before + ex) + ea;

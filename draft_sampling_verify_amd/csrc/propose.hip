@@ -231,16 +231,17 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 // two groups that run one stage apart:
 //   MFMA waves (0-3)      hold the granule's W2 slice (A operand); in stage
 //                         s they write unit s+1's W1 rows (loaded into
-//                         registers last stage) into LDS, issue the loads of
-//                         unit s+2's, and compute unit s's 32 x 128 bias
-//                         tile into LDS;
+//                         registers two stages before) into LDS, check and
+//                         write unit s+4's tokens (loaded three stages
+//                         before), compute unit s's 32 x 128 bias tile into
+//                         LDS, and issue the loads of unit s+3's W1 rows
+//                         and unit s+7's tokens;
 //   epilogue waves (4-11) hold the U rows of three units in registers (16
-//                         lanes per row, 8 ids each); in stage s they reduce
-//                         unit s-1 (z = U + bias: the granule's max, sum of
-//                         weights and greedy argmax per row), store its
-//                         partials, then issue unit s+2's U loads.
-// One barrier per stage and no wait at it for memory (as in the sweep: W1
-// rows one stage ahead, U two, the tokens that choose the W1 rows three).
+//                         lanes per row, 8 ids each); in stage s they
+//                         reduce unit s-1 (z = U + bias: the granule's max,
+//                         sum of weights and greedy argmax per row), store
+//                         its partials, then issue unit s+2's U loads.
+// One barrier per stage and no wait at it for memory.
 // The staged tile sums its 16 ids per thread as two 8-id partials reduced
 // in this kernel's order, so both give identical partials.
 template <int KS, bool VEC4, bool GREEDY>
@@ -351,6 +352,7 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
         issue(0, zuA);
         issue(1, zuB);
         __syncthreads();
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
         auto stage = [&](float (&zu)[8], int s) __attribute__((always_inline)) {
             const int e = s - 1;
             const int ge = ugran(e), cbase = ge * GRAN + ec;
@@ -358,14 +360,16 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
             const bool ok = f < nrows && s_tok[e & 7][er] >= 0;
             if (s >= 1 && s <= nu && ok) {
                 const float* zr = sZ[e & 1] + er * ZS + ec;
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(zr), b1 = *reinterpret_cast<const f32x4*>(zr + 4);
+                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
                 float z[8];
+                if ((ge + 1) * GRAN <= p.V) {
+                    // a whole granule: no id past V
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const float4 bq = *reinterpret_cast<const float4*>(zr + 4 * q);
-                    const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+                    for (int k = 0; k < 8; ++k) z[k] = zu[k] + bb[k];
+                } else {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        z[4 * q + k] = cbase + 4 * q + k < p.V ? zu[4 * q + k] + bb[k] : -INFINITY;
+                    for (int k = 0; k < 8; ++k) z[k] = cbase + k < p.V ? zu[k] + bb[k] : -INFINITY;
                 }
                 float m = -INFINITY, bv = -INFINITY;
                 int bi = 0x7fffffff;
