@@ -239,11 +239,19 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 //   epilogue waves (4-11) hold the U rows of three units in registers (16
 //                         lanes per row, 8 ids each); in stage s they
 //                         reduce unit s-1 (z = U + bias: the granule's max,
-//                         sum of weights and greedy argmax per row), store
-//                         its partials, then issue unit s+2's U loads.
+//                         sum of weights and greedy argmax per row), keep
+//                         its partials in LDS, then issue unit s+2's U
+//                         loads; the partials are written out in bursts
+//                         (stores mixed into the streamed reads cost more
+//                         than the same bytes written together).
 // One barrier per stage and no wait at it for memory.
 // The staged tile sums its 16 ids per thread as two 8-id partials reduced
 // in this kernel's order, so both give identical partials.
+
+// Units whose (row, granule) partials the pipelined tile holds in LDS before
+// writing them out (a run of more units writes them in chunks).
+constexpr int TILE_REC_UNITS = 160;
+
 template <int KS, bool VEC4, bool GREEDY>
 __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs p)
 {
@@ -269,6 +277,8 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
     __shared__ __align__(16) char sB[2][32 * Ops::RS * Ops::ELEM];  // W1 tiles, unit j in j & 1
     __shared__ __align__(16) float sZ[2][32 * ZS];                 // bias tiles, unit j in j & 1
     __shared__ int s_tok[8][32];                                    // checked tokens, unit j in j & 7
+    __shared__ float2 s_rec[TILE_REC_UNITS * 32];                   // partials of unit j in slot j % TILE_REC_UNITS
+    __shared__ int s_ridx[GREEDY ? TILE_REC_UNITS * 32 : 1];        // greedy: argmax of unit j
 
     auto checked = [&](int tk, int q, int j) {
         if (q >= nrows) return -1;
@@ -353,11 +363,32 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
         issue(1, zuB);
         __syncthreads();
         typedef float f32x4 __attribute__((ext_vector_type(4)));
+        // The partials of units [j0, j1) (their slots in s_rec) into gstat
+        // and gidx.  Each wave writes the four rows whose partials it wrote
+        // itself, so no barrier is needed; rows past the end are skipped.
+        const int ew = te / WAVE, el = te & (WAVE - 1);
+        auto flush = [&](int j0, int j1) __attribute__((always_inline)) {
+            for (int idx = el; idx < 4 * (j1 - j0); idx += WAVE) {
+                const int j = j0 + (idx >> 2), i = 4 * ew + (idx & 3);
+                const int f = urow(j, i);
+                if (f < nrows) {
+                    const int sl = (j % TILE_REC_UNITS) * 32 + i;
+                    const size_t o = (size_t)f * p.n_gran + ugran(j);
+                    p.gstat[o] = s_rec[sl];
+                    if (GREEDY) p.gidx[o] = s_ridx[sl];
+                }
+            }
+        };
         auto stage = [&](float (&zu)[8], int s) __attribute__((always_inline)) {
             const int e = s - 1;
             const int ge = ugran(e), cbase = ge * GRAN + ec;
             const int f = urow(e, er);
             const bool ok = f < nrows && s_tok[e & 7][er] >= 0;
+            if (s >= 1 && s <= nu && !ok && (te & 15) == 0) {
+                // a row without a valid token: no mass (its request drafts -1)
+                s_rec[(e % TILE_REC_UNITS) * 32 + er] = make_float2(-INFINITY, 0.0f);
+                if (GREEDY) s_ridx[(e % TILE_REC_UNITS) * 32 + er] = 0x7fffffff;
+            }
             if (s >= 1 && s <= nu && ok) {
                 const float* zr = sZ[e & 1] + er * ZS + ec;
                 const f32x4 b0 = *reinterpret_cast<const f32x4*>(zr), b1 = *reinterpret_cast<const f32x4*>(zr + 4);
@@ -385,15 +416,18 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
                 for (int j = 0; j < 8; ++j) sw += softw(z[j], ms, p.c);
                 sw = hex_sum(sw);
                 if (GREEDY) hex_argmax(bv, bi);
-                // the partials: stored between this unit's loads and the
-                // next ones, so no later wait is for them
+                // the partials wait in LDS: stores mixed into the streamed
+                // reads cost far more than the same bytes written in a burst
                 if ((te & 15) == 0) {
-                    const size_t o = (size_t)f * p.n_gran + ge;
-                    p.gstat[o] = make_float2(m, sw);
-                    if (GREEDY) p.gidx[o] = bi;
+                    const int sl = (e % TILE_REC_UNITS) * 32 + er;
+                    s_rec[sl] = make_float2(m, sw);
+                    if (GREEDY) s_ridx[sl] = bi;
                 }
             }
             issue(s + 2, zu);
+            // a full chunk of partials, or the run's last unit: write them out
+            if (s >= 1 && s <= nu && (e % TILE_REC_UNITS == TILE_REC_UNITS - 1 || e == nu - 1))
+                flush(e - e % TILE_REC_UNITS, e + 1);
             __syncthreads();
         };
         for (int s = 0; s < n_stages; s += 3) {

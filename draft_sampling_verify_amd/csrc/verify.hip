@@ -486,16 +486,24 @@ __global__ __launch_bounds__(TILE_THREADS, 3) void k_verify_sweep(SweepArgs p)
 //                         registers (16 lanes per row, 8 ids each): in
 //                         stage s they finish unit s-1 (p_d, p_t, the TV
 //                         and residual masses, the bias at x_k) while units
-//                         s and s+1 are in flight, store its results, then
-//                         issue unit s+2's loads into the registers just
-//                         freed.
+//                         s and s+1 are in flight, keep its records in LDS,
+//                         then issue unit s+2's loads into the registers
+//                         just freed.
 // One barrier per stage, and no wave waits at it for memory: every value is
 // loaded into registers at least one stage before it is needed (the W1 rows
 // one stage ahead, U and target rows two, the token pairs that choose the W1
-// rows and the row context three stages before they are used), and the
-// results go out as plain stores that stay in flight.  Each group first uses what arrived and only then
-// issues new loads, all without a branch, so every wait the compiler places
-// is for loads of an earlier stage.
+// rows and the row context three stages before they are used).  The
+// (row, granule) records are written out at the end of the run (or of each
+// chunk of SWEEP_REC_UNITS units): one 8-byte store per row and unit mixed
+// into the streamed reads cost about a fifth of the read rate, the same
+// bytes written in one burst almost nothing.  Each group first uses what
+// arrived and only then issues new loads, all without a branch, so every
+// wait the compiler places is for loads of an earlier stage.
+
+// Units whose (row, granule) records the pipelined sweep holds in LDS before
+// writing them out (80 KB; a run of more units writes them in chunks).
+constexpr int SWEEP_REC_UNITS = 320;
+
 template <int KS, bool VEC4, bool MAPS>
 __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepArgs p)
 {
@@ -538,6 +546,7 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
     __shared__ int2 s_rows[8][32];                                  // (U row, target row), unit j in j & 7
     __shared__ int s_xk[2][32];                                     // x_k
     __shared__ float s_cf[2][4][32];                                // M_d, S_d, M_t, S_t
+    __shared__ float2 s_rec[SWEEP_REC_UNITS * 32];                  // records of unit j in slot j % SWEEP_REC_UNITS
 
     // units 0, 1 and 2: checked tokens.  Rows past the end load row 0's
     // values and are masked where used.
@@ -664,6 +673,17 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
         issue(0, zuA, ztA);
         issue(1, zuB, ztB);
         __syncthreads();
+        // The records of units [j0, j1) (their slots in s_rec) into vpart.
+        // Each wave writes the four rows whose records it wrote itself, so
+        // no barrier is needed; rows past the end are skipped.
+        const int ew = te / WAVE, el = te & (WAVE - 1);
+        auto flush = [&](int j0, int j1) __attribute__((always_inline)) {
+            for (int idx = el; idx < 4 * (j1 - j0); idx += WAVE) {
+                const int j = j0 + (idx >> 2), i = 4 * ew + (idx & 3);
+                const int f = urow(j, i);
+                if (f < nrows) p.vpart[(size_t)f * p.n_gran + ugran(j)] = s_rec[(j % SWEEP_REC_UNITS) * 32 + i];
+            }
+        };
         // stage s: finish unit s-1 (rows in zu/zt, tile in sZ) into LDS,
         // then refill zu/zt with unit s+2
         auto stage = [&](float (&zu)[8], float (&zt)[8], int s) __attribute__((always_inline)) {
@@ -671,6 +691,9 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
             const int ge = ugran(e), cbase = ge * GRAN + ec;
             const int f = urow(e, er);
             const bool ok = f < nrows && s_tok[e & 7][er] >= 0;
+            // a row without a valid token keeps a record of zeros (its
+            // request's outputs are blanked by the resolve)
+            if (s >= 1 && s <= nu && !ok && (te & 15) == 0) s_rec[(e % SWEEP_REC_UNITS) * 32 + er] = make_float2(0.0f, 0.0f);
             if (s >= 1 && s <= nu && ok) {
                 RowCtx rc;
                 rc.req = 0;
@@ -712,12 +735,15 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_verify_sweep_ws(SweepAr
                 }
                 tv = hex_sum(tv);
                 res = hex_sum(res);
-                // the results: stored between this unit's loads and the next
-                // ones, so no later wait is for them
-                if ((te & 15) == 0) p.vpart[(size_t)f * p.n_gran + ge] = make_float2(tv, res);
+                // the records wait in LDS: stores mixed into the streamed
+                // reads cost far more than the same bytes written in a burst
+                if ((te & 15) == 0) s_rec[(e % SWEEP_REC_UNITS) * 32 + er] = make_float2(tv, res);
                 if (rc.xk >= cbase && rc.xk < cbase + 8) p.vbias[f] = zr[rc.xk - cbase];
             }
             issue(s + 2, zu, zt);
+            // a full chunk of records, or the run's last unit: write them out
+            if (s >= 1 && s <= nu && (e % SWEEP_REC_UNITS == SWEEP_REC_UNITS - 1 || e == nu - 1))
+                flush(e - e % SWEEP_REC_UNITS, e + 1);
             __syncthreads();
         };
         for (int s = 0; s < n_stages; s += 3) {
