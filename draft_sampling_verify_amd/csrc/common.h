@@ -807,77 +807,6 @@ __device__ inline void stage_w1_exact(void* sB, const WT* W1, const int* tok)
     }
 }
 
-// stage_w1_exact in two steps: issue() starts the row loads into registers,
-// commit() writes them (missing tokens as zero rows) into the LDS tile, so
-// that loads issued in between are not waited for by the commit.
-template <typename WT, int RS, int KS>
-struct W1Exact {
-    static constexpr int ELEM = (int)sizeof(WT);
-    static constexpr int PER_ROW = 2 * KS;               // uint4 per W1 row
-    static constexpr int R_ELEMS = PER_ROW * 16 / ELEM;  // r
-    static constexpr int TOTAL = 32 * PER_ROW;
-    static constexpr int NPT = (TOTAL + TILE_THREADS - 1) / TILE_THREADS;
-    uint4 v[NPT];
-    uint32_t keep[NPT];
-    __device__ static inline int index(int i)
-    {
-        int idx = opaque_v(threadIdx.x) + i * TILE_THREADS;
-        if (TOTAL % TILE_THREADS != 0) idx = min(idx, TOTAL - 1);  // duplicates store the same value
-        return idx;
-    }
-    __device__ inline void issue(const WT* W1, const int* tok)
-    {
-#pragma unroll
-        for (int i = 0; i < NPT; ++i) {
-            const int idx = index(i);
-            const int tk = tok[idx / PER_ROW];
-            keep[i] = tk >= 0 ? ~0u : 0u;
-            // unconditional load (row 0 for a missing token), masked to zero below
-            v[i] = reinterpret_cast<const uint4*>(W1 + (size_t)(tk >= 0 ? tk : 0) * R_ELEMS)[idx % PER_ROW];
-        }
-    }
-    __device__ inline void commit(void* sB) const
-    {
-#pragma unroll
-        for (int i = 0; i < NPT; ++i) {
-            const int idx = index(i);
-            const uint4 m = make_uint4(v[i].x & keep[i], v[i].y & keep[i], v[i].z & keep[i], v[i].w & keep[i]);
-            *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sB) + (size_t)(idx / PER_ROW) * RS * ELEM +
-                                      16 * (idx % PER_ROW)) = m;
-        }
-    }
-};
-
-// load_acc16 without branches around the loads (so that a later wait for an
-// earlier load does not also wait for these): indices clamped into the row,
-// ids past V masked to -inf.  vec4 requires V % 4 == 0.
-__device__ inline void load_acc16_flat(const float* row, int c0, int h, int V, bool vec4, float (&v)[16])
-{
-    if (vec4) {
-        const float4* p4 = reinterpret_cast<const float4*>(row);
-        const int qmax = (V >> 2) - 1;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = c0 + 8 * q + 4 * h;
-            const float4 t = p4[min(c >> 2, qmax)];
-            const bool in = c < V;
-            v[4 * q + 0] = in ? t.x : -INFINITY;
-            v[4 * q + 1] = in ? t.y : -INFINITY;
-            v[4 * q + 2] = in ? t.z : -INFINITY;
-            v[4 * q + 3] = in ? t.w : -INFINITY;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = c0 + 8 * q + 4 * h + e;
-                const float t = row[min(c, V - 1)];
-                v[4 * q + e] = c < V ? t : -INFINITY;
-            }
-    }
-}
-
 // Read back what store_tile wrote for this lane (its own 16 entries).
 __device__ inline void load_tile_own(const float* sZ, f32x16& acc, int w, int lane)
 {

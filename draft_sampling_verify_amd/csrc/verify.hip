@@ -130,6 +130,7 @@ constexpr int TROW_THREADS = 1024;
 constexpr int TROW_GRANS = TROW_THREADS / 8;  // granules per step
 constexpr int TROW_MAX_SPLIT = 16;            // workgroups per row at most
 constexpr int TROW_TARGET_WGS = 256;          // rows are split while fewer than this (more is slower)
+constexpr int TROW_STAGE_GRANS = 4096;        // granule statistics held in LDS per workgroup (48 KB)
 
 // With few rows a row is split over nsplit workgroups (consecutive runs of
 // steps); each writes its part's (max, sum, argmax) and k_target_merge folds
@@ -144,6 +145,11 @@ __global__ __launch_bounds__(TROW_THREADS) void k_target_rows(TargetArgs p)
     const int t = threadIdx.x, gi = t >> 3, l8 = t & 7;
     const int steps_all = (p.n_gran + TROW_GRANS - 1) / TROW_GRANS;
     const int st0 = part * steps_all / p.nsplit, steps = (part + 1) * steps_all / p.nsplit;
+    // this part's granule statistics wait in LDS until the row is read:
+    // stores mixed into the streamed reads cost far more than their bytes
+    __shared__ float2 s_tg[TROW_STAGE_GRANS];
+    __shared__ int s_ti[TROW_STAGE_GRANS];
+    const int g_first = st0 * TROW_GRANS;
     float rm = -INFINITY, rs = 0.0f;
     int rbi = 0x7fffffff;
     float cur[16], nxt[16];
@@ -168,9 +174,15 @@ __global__ __launch_bounds__(TROW_THREADS) void k_target_rows(TargetArgs p)
         oct_argmax(bv, bi);
         if (g < p.n_gran) {
             if (l8 == 0) {
-                const size_t o = (size_t)row * p.n_gran + g;
-                p.tgran[o] = make_float2(m, sm);
-                p.tgidx[o] = bi;
+                const int sg = g - g_first;
+                if (sg < TROW_STAGE_GRANS) {
+                    s_tg[sg] = make_float2(m, sm);
+                    s_ti[sg] = bi;
+                } else {
+                    const size_t o = (size_t)row * p.n_gran + g;
+                    p.tgran[o] = make_float2(m, sm);
+                    p.tgidx[o] = bi;
+                }
             }
             // fold into the group's running row statistics (granules ascend)
             if (m > rm) {
@@ -189,6 +201,16 @@ __global__ __launch_bounds__(TROW_THREADS) void k_target_rows(TargetArgs p)
     // merge the 64 groups: lanes 0, 8, ..., 56 of each wave, then the waves
     __shared__ float s_m[TROW_THREADS / WAVE], s_s[TROW_THREADS / WAVE];
     __shared__ int s_i[TROW_THREADS / WAVE];
+    __syncthreads();
+    {
+        // the staged granule statistics of this part, in one burst
+        const int g_end = min(min(steps * TROW_GRANS, p.n_gran), g_first + TROW_STAGE_GRANS);
+        for (int g = g_first + t; g < g_end; g += TROW_THREADS) {
+            const size_t o = (size_t)row * p.n_gran + g;
+            p.tgran[o] = s_tg[g - g_first];
+            p.tgidx[o] = s_ti[g - g_first];
+        }
+    }
 #pragma unroll
     for (int o = 8; o < WAVE; o <<= 1) {
         const float m2 = shfl_xor(rm, o), s2 = shfl_xor(rs, o);
