@@ -102,6 +102,7 @@ struct ProposeWs {
     int32_t* gidx;    // [R, n_gran]
     uint64_t* part;   // [FUSED_PART_WORDS][R][n_gran] fused: tagged partials (R <= FUSED_MAX_R), else null
     uint64_t* words;  // [FUSED_TOKEN_COPIES, 32] fused: tagged token words
+    uint64_t* exitw;  // [n_gran] fused: tagged exit word of each workgroup
 };
 
 // Propose regions start at `start` bytes (the header by default; after the
@@ -118,6 +119,7 @@ inline ProposeWs carve_propose(void* ws, int R, int V, size_t* bytes, size_t sta
     if (R <= FUSED_MAX_R) {
         w.part = c.take<uint64_t>((size_t)R * ng * FUSED_PART_WORDS);
         w.words = c.take<uint64_t>((size_t)FUSED_TOKEN_COPIES * 32);
+        w.exitw = c.take<uint64_t>(ng);
     }
     if (bytes) *bytes = c.off;
     return w;

@@ -636,6 +636,7 @@ struct FusedArgs {
     float* pd_stats;       // [R, gamma, 2]
     uint64_t* part;        // [FUSED_PART_WORDS][R][n_gran] tagged partials: max, sum, argmax
     uint64_t* words;       // [FUSED_TOKEN_COPIES, 32] tagged token words
+    uint64_t* exitw;       // [n_gran] tagged exit word of each workgroup
     uint32_t* epoch;       // calls so far on this workspace
     uint32_t* abort_flag;  // abort_word(epoch) of a call that gave up waiting
 };
@@ -1061,9 +1062,25 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_propose_fused(FusedArgs f)
             A.load_a(p.W2p, ks, 4 * g + w, 4 * g + w < nblk, lane);
         }
     }
-    // the call counter advances once every workgroup has read it: workgroup
-    // 0's last pick needed the partials of all of them
-    if (g == 0 && threadIdx.x == 0) st_dev(f.epoch, (epoch + 1) & 0x7FFFFFFFu);
+    // The call counter advances once every workgroup has read it.  After a
+    // complete call that holds when workgroup 0 ends (its last pick needed
+    // the partials of all of them).  After a failed call workgroup 0 may end
+    // first, so it waits (boundedly) for every workgroup's exit word of this
+    // call: a workgroup that started late then still read this call's
+    // counter, and saw its abort word.
+    const uint32_t done_tag = call_tag(epoch, 0);  // (positions use k >= 1)
+    if (threadIdx.x == 0) st_dev(f.exitw + g, tagged(1u, done_tag));
+    if (g == 0) {
+        if (failed) {
+            for (int spin = 0;; ++spin) {
+                bool ok = true;
+                for (int i = threadIdx.x; i < NG; i += TILE_THREADS) ok &= tag_of(ld_dev(f.exitw + i)) == done_tag;
+                if (__syncthreads_and(ok) || spin >= SPIN_LIMIT) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        if (threadIdx.x == 0) st_dev(f.epoch, (epoch + 1) & 0x7FFFFFFFu);
+    }
 }
 
 // ------------------------------------------------------------ launchers
@@ -1112,6 +1129,7 @@ static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* 
     f.x = x_out; f.pd_x = pd_x; f.pd_stats = pd_stats;
     f.part = ws.part;
     f.words = ws.words;
+    f.exitw = ws.exitw;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(a.status);
     f.epoch = &hdr->epoch;
     f.abort_flag = &hdr->abort;

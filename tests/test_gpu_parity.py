@@ -47,6 +47,10 @@ SMALL = {
     # 256): ragged request count and vocabulary (V % 4 != 0)
     "piped_tile": Config("piped_tile", 21, 130, 3, 3001, 128, True, 1.0, 2.0, 0.05, 0.5),
     "piped_tile_v4": Config("piped_tile_v4", 22, 100, 4, 5000, 256, True, 0.8, 3.0, 0.02, 1.0),
+    # more than one 32-row block of requests with fewer than 96 of them
+    # (the per-position propose with the staged tile): a ragged last block,
+    # V % 4 != 0, r = 128
+    "multi_block": Config("multi_block", 23, 70, 3, 9001, 128, True, 1.0, 2.0, 0.05, 0.5),
 }
 
 
