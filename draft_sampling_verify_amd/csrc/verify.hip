@@ -938,6 +938,8 @@ struct MarkovDraft {
         const int x0r = a.s.x0[r];
         return x0r < 0 || x0r >= a.s.V;
     }
+    // the token before position 1 (the rescan of a rejection there needs its W1 row)
+    __device__ inline int anchor(const ResolveArgs& a, int r) const { return a.s.x0[r]; }
     __device__ inline double pd_at(const ResolveArgs& a, int r, int t, int xk, int voff) const
     {
         const SweepArgs& p = a.s;
@@ -946,8 +948,9 @@ struct MarkovDraft {
         return exp2((zd - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
     }
     // zrow[i] = residual weight of id 128 gstar + i at position kstar.
-    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, float* zrow,
-                                            int w, int lane) const
+    // xp: the token before position kstar (the anchor for kstar = 1)
+    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, int xp,
+                                            float* zrow, int w, int lane) const
     {
         const SweepArgs& p = a.s;
         if (w >= 4) return;
@@ -960,7 +963,6 @@ struct MarkovDraft {
         const int b = 4 * gstar + w;
         const int c0 = gstar * GRAN + 32 * w;
         const bool v4 = (p.V % 4) == 0;
-        const int xp = kstar == 1 ? p.x0[r] : p.x[(size_t)r * G + kstar - 2];
         typename TileOps<WT, KS>::BRow brow;
         brow.load(reinterpret_cast<const WT*>(p.W1), p.r, n == nf ? xp : -1, ks, lane);
         float uu[16], ll[16];
@@ -1001,6 +1003,7 @@ struct ClusterDraft {
     const float* zf;
     int N_c, K_c, max_cl;
     __device__ inline bool bad_anchor(const ResolveArgs&, int) const { return false; }
+    __device__ inline int anchor(const ResolveArgs&, int) const { return -1; }  // (no anchor: not read)
     __device__ inline float logit(int f, int v, bool& in) const
     {
         in = false;
@@ -1028,8 +1031,8 @@ struct ClusterDraft {
         const size_t so = (size_t)r * p.gamma + t;
         return exp2(((double)z - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
     }
-    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, float* zrow,
-                                            int w, int lane) const
+    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, int,
+                                            float* zrow, int w, int lane) const
     {
         const SweepArgs& p = a.s;
         if (w >= 2) return;
@@ -1074,6 +1077,7 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
     __shared__ float s_Z[65];
     __shared__ int s_bonus;
     __shared__ int s_y;
+    __shared__ int s_x[65];        // the anchor, then the drafted tokens (read by the accept tests)
     __shared__ float zrow[GRAN];
 
     const int Lr = a.ell ? a.ell[r] : G;
@@ -1085,8 +1089,10 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
 
     // ---- phase 1a: accept tests, one lane of wave RES_SEARCH per position
     const int ia = t - RES_SEARCH * WAVE;  // the position (0-based) of this lane
+    if (t == 0) s_x[0] = dr.anchor(a, r);
     if (ia >= 0 && ia < L) {
         const int xk = p.x[(size_t)r * G + ia];
+        s_x[ia + 1] = xk;  // (the rescan's previous token, without a second load)
         if (xk < 0 || xk >= p.V) {
             bad = true;
         } else {
@@ -1162,7 +1168,7 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
         if (t == 0) s_y = a.targ[toff + kstar - 1];
     } else if (s_Z[kstar - 1] > 0.0f) {
         const int gstar = s_g[kstar - 1];
-        dr.residual_granule(a, r, kstar, gstar, voff, zrow, w, lane);
+        dr.residual_granule(a, r, kstar, gstar, voff, s_x[kstar - 1], zrow, w, lane);
         __syncthreads();
         if (w == 0) {
             float e;
