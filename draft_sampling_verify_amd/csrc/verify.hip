@@ -299,25 +299,6 @@ struct RowCtx {
     float Md, iSd, Mt, iSt;
 };
 
-__device__ inline RowCtx row_ctx(const SweepArgs& p, int f, int nrows)
-{
-    RowCtx rc{};
-    rc.req = -1;
-    if (f >= nrows) return rc;
-    const int4 vi = vrow_info(p.vmap, f, p.gamma, p.P);
-    rc.req = vi.x;
-    rc.k = vi.y;
-    rc.trow = vi.z;
-    rc.xk = p.x[(size_t)vi.x * p.gamma + vi.y - 1];
-    const size_t so = (size_t)vi.x * p.gamma + vi.y - 1;
-    rc.Md = p.dstats[2 * so];
-    rc.iSd = 1.0f / p.dstats[2 * so + 1];
-    const float2 ts = p.trow[vi.z];
-    rc.Mt = ts.x;
-    rc.iSt = 1.0f / ts.y;
-    return rc;
-}
-
 // Token whose W1 row biases verified row f (x_{k-1}), or -1 when the row does
 // not exist or its tokens are out of range.
 __device__ inline int row_tok(const SweepArgs& p, int f, int nrows)
@@ -374,7 +355,7 @@ __device__ inline RowRaw row_raw(const SweepArgs& p, int f, int nrows)
     return w;
 }
 
-// The same RowCtx as row_ctx() computes.
+// The verified row's context from its loaded values (req = -1 past the end).
 __device__ inline RowCtx row_finish(const RowRaw& w)
 {
     RowCtx rc;
@@ -948,29 +929,38 @@ struct MarkovDraft {
         return exp2((zd - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
     }
     // zrow[i] = residual weight of id 128 gstar + i at position kstar.
-    // xp: the token before position kstar (the anchor for kstar = 1)
-    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, int xp,
-                                            float* zrow, int w, int lane) const
+    // xp: the token before position kstar (the anchor for kstar = 1); toff:
+    // the request's first target row.  The row's softmax statistics are read
+    // at addresses known here (not through the verified-row map), so that the
+    // W1 row, U, Lt, statistics and W2 loads all go out before any is waited on.
+    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, int toff,
+                                            int xp, float* zrow, int w, int lane) const
     {
         const SweepArgs& p = a.s;
         if (w >= 4) return;
         const int G = p.gamma;
         const int f = voff + kstar - 1;
-        const int nrows = p.vmap ? p.counts[0] : p.max_rows;
         const int n = lane & 31, h = lane >> 5;
         const int nf = f & (BLOCK_ROWS - 1);
         const int ks = k_steps<WT>(p.r);
         const int b = 4 * gstar + w;
         const int c0 = gstar * GRAN + 32 * w;
         const bool v4 = (p.V % 4) == 0;
+        const size_t so = (size_t)r * G + kstar - 1;
         typename TileOps<WT, KS>::BRow brow;
         brow.load(reinterpret_cast<const WT*>(p.W1), p.r, n == nf ? xp : -1, ks, lane);
         float uu[16], ll[16];
-        load_acc16(p.U + ((size_t)r * G + kstar - 1) * p.V, c0, h, p.V, v4, uu);
+        load_acc16(p.U + so * p.V, c0, h, p.V, v4, uu);
         load_acc16(p.Lt + ((size_t)r * (G + 1) + kstar - 1) * p.V, c0, h, p.V, v4, ll);
-        const RowCtx rc = row_ctx(p, f, nrows);
+        const float md = p.dstats[2 * so], sd = p.dstats[2 * so + 1];
+        const float2 ts = p.trow[toff + kstar - 1];
         TileOps<WT, KS> A;
         A.load_a(p.W2p, ks, b, b < (p.V + 31) / 32, lane);
+        RowCtx rc{};
+        rc.Md = md;
+        rc.iSd = 1.0f / sd;
+        rc.Mt = ts.x;
+        rc.iSt = 1.0f / ts.y;
         const f32x16 acc = A.mfma_row(brow, ks);
         if (n == nf) {
 #pragma unroll
@@ -1031,13 +1021,12 @@ struct ClusterDraft {
         const size_t so = (size_t)r * p.gamma + t;
         return exp2(((double)z - (double)p.dstats[2 * so]) * (double)p.c) / (double)p.dstats[2 * so + 1];
     }
-    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, int,
-                                            float* zrow, int w, int lane) const
+    __device__ inline void residual_granule(const ResolveArgs& a, int r, int kstar, int gstar, int voff, int toff,
+                                            int, float* zrow, int w, int lane) const
     {
         const SweepArgs& p = a.s;
         if (w >= 2) return;
         const int f = voff + kstar - 1;
-        const int toff = a.toff ? a.toff[r] : r * p.P;
         const float2 ts = p.trow[toff + kstar - 1];
         const size_t so = (size_t)r * p.gamma + kstar - 1;
         const float Md = p.dstats[2 * so], iSd = 1.0f / p.dstats[2 * so + 1];
@@ -1089,6 +1078,7 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
 
     // ---- phase 1a: accept tests, one lane of wave RES_SEARCH per position
     const int ia = t - RES_SEARCH * WAVE;  // the position (0-based) of this lane
+    bool rej = false;                      // this lane's position was rejected
     if (t == 0) s_x[0] = dr.anchor(a, r);
     if (ia >= 0 && ia < L) {
         const int xk = p.x[(size_t)r * G + ia];
@@ -1112,6 +1102,7 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
                 acc = u1 < ratio;
             }
             s_acc[ia] = acc;
+            rej = !acc;
             if (a.pt_x) a.pt_x[(size_t)r * G + ia] = (float)pt;
         }
     } else if (ia >= L && ia < G) {
@@ -1134,8 +1125,9 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
         }
     }
     // ---- phase 1c: the bonus draw after a full accept (the last wave, after
-    // its accept tests)
-    if (w == RES_SEARCH) {
+    // its accept tests; skipped once one of them has rejected, as the bonus
+    // is then not emitted)
+    if (w == RES_SEARCH && __ballot(rej) == 0) {
         int yb;
         if (GREEDY) {
             yb = a.targ[toff + L];
@@ -1168,7 +1160,7 @@ __device__ inline void resolve_body(const ResolveArgs& a, const D& dr)
         if (t == 0) s_y = a.targ[toff + kstar - 1];
     } else if (s_Z[kstar - 1] > 0.0f) {
         const int gstar = s_g[kstar - 1];
-        dr.residual_granule(a, r, kstar, gstar, voff, s_x[kstar - 1], zrow, w, lane);
+        dr.residual_granule(a, r, kstar, gstar, voff, toff, s_x[kstar - 1], zrow, w, lane);
         __syncthreads();
         if (w == 0) {
             float e;
