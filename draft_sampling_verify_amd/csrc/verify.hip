@@ -1431,6 +1431,28 @@ static SweepArgs make_sweep(const DraftArgs& a, const float* dstats, const float
     return s;
 }
 
+// Workgroups of k_target_rows the current device holds at once; cached per
+// device.
+static int trow_slots()
+{
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV];  // slots + 1; 0 = not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return 512;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_target_rows, TROW_THREADS, 0) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        v = per_cu * cus + 1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v - 1;
+}
+
 static hipError_t target_pass(const DraftArgs& a, const float* Lt, int P, int max_rows,
                               const VerifyWs& w, const int32_t* counts, bool maps, hipStream_t s)
 {
@@ -1442,9 +1464,23 @@ static hipError_t target_pass(const DraftArgs& a, const float* Lt, int P, int ma
     t.counts = counts;
     t.tgran = w.tgran; t.tgidx = w.tgidx; t.trow = w.trow; t.targ = w.targ;
     // split rows over several workgroups while there are fewer than about
-    // 256 of them
+    // 256 of them; with more rows than the device holds workgroups at once,
+    // into as many parts (1, 2 or 4) as make the last round of workgroups
+    // least ragged (rounds per part, fewest parts on a tie)
     const int steps = (t.n_gran + TROW_GRANS - 1) / TROW_GRANS;
     t.nsplit = std::max(1, std::min(std::min(TROW_TARGET_WGS / std::max(max_rows, 1), steps), TROW_MAX_SPLIT));
+    const int slots = trow_slots();
+    if (max_rows > slots) {
+        long best_num = -1, best_den = 1;
+        for (int n = 1; n <= 4 && n <= steps; n *= 2) {
+            const long rounds = ((long)max_rows * n + slots - 1) / slots;
+            if (best_num < 0 || rounds * best_den < best_num * n) {
+                best_num = rounds;
+                best_den = n;
+                t.nsplit = n;
+            }
+        }
+    }
     t.tpart = w.tpart;
     {
         ProfScope ps("target_rows", s);
