@@ -334,9 +334,13 @@ def _kernel_table(spec, run, n, cfg, K):
     return kernels
 
 
-def measure_config(spec, workloads, name, dev, stream, steps, warmup=3):
+def measure_config(spec, workloads, name, dev, stream, steps, warmup=3, min_warm_s=0.3, min_timed_s=0.5):
     """One more workload, timed with the headline's protocol (warm-up, then
-    `steps` steps bracketed by device synchronisation; round = step index).
+    timed steps bracketed by device synchronisation; round = step index).
+    The warm-up runs at least `warmup` steps and `min_warm_s` seconds, and
+    the timed region at least `steps` steps and `min_timed_s` seconds: the
+    clocks settle over some hundred milliseconds of back-to-back steps, and
+    a short window after the host-side input generation reads high.
     c1: latency of one propose + verify step.  c3, c5: propose + verify of
     every position.  c4: the serving pipeline propose -> schedule(c) ->
     verify(l) with c* fused; verified draft tokens = K* of the schedule."""
@@ -368,16 +372,27 @@ def measure_config(spec, workloads, name, dev, stream, steps, warmup=3):
                          ell=ell if sched else None, n_acc=n_acc, y=y, pt_x=pt_x, c_star=c_star, ws=ws,
                          stream=stream)
 
-    for i in range(warmup):
-        step(i)
+    n_warm = 0
+    tw = time.perf_counter()
+    while n_warm < warmup or time.perf_counter() - tw < min_warm_s:
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # the timed step count: at least `steps`, and enough for min_timed_s at
+    # the warm-up's rate
+    per_step = (time.perf_counter() - tw) / n_warm
+    n_table = steps  # the kernel table (HIP events around every launch) keeps the requested count
+    steps = max(steps, int(min_timed_s / max(per_step, 1e-6)) + 1)
     t0 = time.perf_counter()
     for i in range(steps):
-        step(warmup + i)
+        step(n_warm + i)
     torch.cuda.synchronize()
     el = (time.perf_counter() - t0) / steps
+    warmup = n_warm
     K = int(K_star.item()) if sched else R * g
-    kernels = _kernel_table(spec, lambda i: step(warmup + i), steps, cfg, K)
+    kernels = _kernel_table(spec, lambda i: step(warmup + i), n_table, cfg, K)
     sb = step_algorithmic_bytes(cfg, K) + (4.0 * R * g + 4.0 * cfg.sps_len if sched else 0.0)
     out = {"workload": "%s: R=%d, gamma=%d, V=%d, r=%d, %s weights, sampled, T=%g%s" % (
                cfg.name if name != "c1" else "c1 (tiny)", R, g, V, cfg.r, "bf16" if cfg.bf16 else "fp32", cfg.T,
