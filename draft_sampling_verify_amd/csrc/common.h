@@ -1054,6 +1054,61 @@ __device__ inline float wave_max_dpp(float v)
                                                             0xC, 0xF, false)));
     return lane63(v);
 }
+// Totals of NR rounds of granule masses (lane l holds w[i], the mass of
+// granule l + 64 i) by a transposing butterfly: at each exchange a lane
+// keeps one half of its values, the half its partner lane gives away, and
+// adds the partner's copy of it, so NR values per lane become one after
+// log2 NR exchanges of halving size (NR - 1 shuffles in all instead of NR
+// separate wave reductions); the lanes that still share a round are then
+// summed.  Lane l ends with the total of round l >> (6 - log2 NR), the same
+// bits in every lane of that group.
+template <int NR>
+__device__ inline float wave_round_totals(const float (&w)[NR])
+{
+    static_assert(NR == 16 || NR == 32, "16 or 32 rounds");
+    constexpr int LOG = NR == 16 ? 4 : 5;
+    const int lane = threadIdx.x & (WAVE - 1);
+    float v[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) v[i] = w[i];
+#pragma unroll
+    for (int k = 0; k < LOG; ++k) {
+        const int d = 32 >> k, half = (NR >> k) >> 1;
+        const bool up = (lane & d) != 0;
+#pragma unroll
+        for (int j = 0; j < half; ++j) {
+            const float keep = up ? v[j + half] : v[j];
+            const float give = up ? v[j] : v[j + half];
+            v[j] = keep + shfl_xor(give, d);
+        }
+    }
+    float t = v[0];
+#pragma unroll
+    for (int d = 32 >> LOG; d >= 1; d >>= 1) t += shfl_xor(t, d);
+    return t;
+}
+
+// The running totals of the rounds in order: lane l's inclusive sum over the
+// rounds up to its own (only the first lane of each round's group
+// contributes), on DPP.
+template <int NR>
+__device__ inline float wave_rounds_scan(const float (&w)[NR], float& T, bool& lead)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    T = wave_round_totals(w);
+    lead = lane % (WAVE / NR) == 0;
+    return wave_scan_dpp(lead ? T : 0.0f);
+}
+
+// The total of all rounds, with the bits wave_rounds_pick reports.
+template <int NR>
+__device__ inline float wave_rounds_sum(const float (&w)[NR])
+{
+    float T;
+    bool lead;
+    return lane63(wave_rounds_scan(w, T, lead));
+}
+
 // Register-cached inverse CDF over at most 64 NR granule masses, one wave.
 // Lane l holds w[i] = mass of granule l + 64 i (0 past the end): the caller
 // loads all of them at once (coalesced, one memory round trip).  Round i
@@ -1061,30 +1116,27 @@ __device__ inline float wave_max_dpp(float v)
 // are the granules in vocabulary order.  Returns the first granule of
 // positive mass whose running sum exceeds u * total, the running sum before
 // it and the total, identical in every lane; if rounding leaves none, the
-// last granule with positive mass (fallback set).  The round totals and the
-// scan inside the chosen round run on DPP (no LDS round trips).
+// last granule with positive mass (fallback set).  The round totals, their
+// running sums and the scan inside the chosen round stay in registers (no
+// LDS round trips).
 template <int NR>
 __device__ inline int wave_rounds_pick(const float (&w)[NR], float u, float& total, float& before, bool& fallback)
 {
     const int lane = threadIdx.x & (WAVE - 1);
-    float T[NR];
-    float Z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        T[i] = wave_total_dpp(w[i]);
-        Z += T[i];
-    }
+    float T;
+    bool lead;
+    const float incl = wave_rounds_scan(w, T, lead);
+    const float Z = lane63(incl);
     total = Z;
     const float target = u * Z;
-    float pre = 0.0f, rbase = 0.0f;
+    // the first round of positive mass whose running total passes the target
+    const unsigned long long hr = __ballot(lead && T > 0.0f && incl > target);
     int rstar = -1;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        if (rstar < 0 && T[i] > 0.0f && pre + T[i] > target) {
-            rstar = i;
-            rbase = pre;
-        }
-        pre += T[i];
+    float rbase = 0.0f;
+    if (hr) {
+        const int Lr = __ffsll((long long)hr) - 1;
+        rstar = Lr / (WAVE / NR);
+        rbase = __shfl(lane_before(incl), Lr, WAVE);  // the rounds before it
     }
     float wr = 0.0f;
     int lastpos = -1;

@@ -462,10 +462,16 @@ struct PickArgs {
 // W1 row, its granule partials); every wave then merges the partials and
 // locates the granule (identical results), wave w recomputes column block w
 // of that granule on MFMA with U added, and wave 0 picks the id.
-constexpr int PICK_CACHE = 32;  // granule partials held in registers per lane
+// Rows of at most 64 NR granules (NR = 16, 32) are read lane-strided (lane l
+// holds granules l + 64 i: every load instruction reads 64 consecutive
+// records) and merged in fp32 on DPP: per 64-granule round its total, the
+// round whose running total passes the target, then a scan inside it
+// (vocabulary order throughout).  Longer rows (NR = 0) give each lane a
+// contiguous run of granules and sum in fp64 (up to 2048 terms a lane).
+constexpr int PICK_CACHE = 32;  // granule partials held in registers per lane (fp64 path)
 
-template <typename WT, int KS, bool GREEDY>
-__global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
+template <typename WT, int KS, bool GREEDY, int NR>
+__device__ inline void pick_body(const PickArgs& p)
 {
     const int q = blockIdx.x;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
@@ -477,11 +483,19 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
 
     // independent loads first
     const float2* gs = p.gstat + (size_t)q * p.n_gran;
+    constexpr int NC = NR > 0 ? NR : PICK_CACHE;
     const int per = (p.n_gran + WAVE - 1) / WAVE;
-    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);
-    float2 gc[PICK_CACHE];
+    const int g0 = min(lane * per, p.n_gran), g1 = min(g0 + per, p.n_gran);  // (fp64 path)
+    float2 gc[NC];
 #pragma unroll
-    for (int i = 0; i < PICK_CACHE; ++i) gc[i] = (g0 + i < g1) ? gs[g0 + i] : make_float2(-INFINITY, 0.0f);
+    for (int i = 0; i < NC; ++i) {
+        if constexpr (NR > 0) {
+            const int g = lane + WAVE * i;
+            gc[i] = g < p.n_gran ? gs[g] : make_float2(-INFINITY, 0.0f);
+        } else {
+            gc[i] = (g0 + i < g1) ? gs[g0 + i] : make_float2(-INFINITY, 0.0f);
+        }
+    }
     const int tok = p.k == 1 ? p.x0[q] : p.x[(size_t)q * p.gamma + p.k - 2];
     const bool ok = tok >= 0 && tok < p.V;
     // B operand: only this request's W1 row (column n == q's slot); a matrix
@@ -499,34 +513,56 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         }
         return;
     }
-    // merge the granule partials: M = max, w_g = S_g 2^((M_g - M) c); the
-    // first PICK_CACHE granules of each lane come from registers
+    // merge the granule partials: M = max, w_g = S_g 2^((M_g - M) c)
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PICK_CACHE; ++i) m = fmaxf(m, gc[i].x);
-    for (int g = g0 + PICK_CACHE; g < g1; ++g) m = fmaxf(m, gs[g].x);
+    for (int i = 0; i < NC; ++i) m = fmaxf(m, gc[i].x);
+    if constexpr (NR == 0)
+        for (int g = g0 + PICK_CACHE; g < g1; ++g) m = fmaxf(m, gs[g].x);
     const float M = wave_max(m);
     const float c = p.c;
-    // sums across granules in fp64 (a lane owns up to 2048 granules)
-    float wv[PICK_CACHE];
-    double tsum = 0.0;
+    float wv[NC];
 #pragma unroll
-    for (int i = 0; i < PICK_CACHE; ++i) {
-        wv[i] = gc[i].y * softw(gc[i].x, M, c);  // padding: 0 * 0
-        tsum += (double)wv[i];
+    for (int i = 0; i < NC; ++i) wv[i] = gc[i].y * softw(gc[i].x, M, c);  // padding: 0 * 0
+    float S;
+    double Sd = 0.0, excl = 0.0;  // (fp64 path)
+    const float u = u24f(philox((uint32_t)p.k, (uint32_t)q, p.round, p.seed).w[0]);
+    float target = 0.0f, before = 0.0f;
+    bool fallback = true;
+    int gstar = 0;
+    if constexpr (NR > 0) {
+        // the total with the bits of the draw's own (which needs it first)
+        if (GREEDY) S = wave_rounds_sum(wv);
+        else {
+            gstar = wave_rounds_pick(wv, u, S, before, fallback);
+            target = u * S;
+        }
+    } else {
+        double tsum = 0.0;
+#pragma unroll
+        for (int i = 0; i < PICK_CACHE; ++i) tsum += (double)wv[i];
+        for (int g = g0 + PICK_CACHE; g < g1; ++g) tsum += (double)(gs[g].y * softw(gs[g].x, M, c));
+        const double incl = wave_incl_scan(tsum);
+        excl = __shfl_up(incl, 1, WAVE);
+        if (lane == 0) excl = 0.0;
+        Sd = __shfl(incl, WAVE - 1, WAVE);
+        S = (float)Sd;
     }
-    for (int g = g0 + PICK_CACHE; g < g1; ++g) tsum += (double)(gs[g].y * softw(gs[g].x, M, c));
-    const double incl = wave_incl_scan(tsum);
-    double excl = __shfl_up(incl, 1, WAVE);
-    if (lane == 0) excl = 0.0;
-    const double Sd = __shfl(incl, WAVE - 1, WAVE);
-    const float S = (float)Sd;
 
     if (GREEDY) {
         if (w != 0) return;
+        // the smallest argmax among the granules whose maximum is M
         int cand = 0x7fffffff;
-        for (int g = g0; g < g1; ++g)
-            if (gs[g].x == M) { cand = p.gidx[(size_t)q * p.n_gran + g]; break; }
+        if constexpr (NR > 0) {
+            int gfirst = -1;
+#pragma unroll
+            for (int i = NR - 1; i >= 0; --i)
+                if (gc[i].x == M) gfirst = lane + WAVE * i;
+            if (gfirst >= 0) cand = p.gidx[(size_t)q * p.n_gran + gfirst];
+        } else {
+            for (int g = g0; g < g1; ++g)
+                if (gs[g].x == M) { cand = p.gidx[(size_t)q * p.n_gran + g]; break; }
+        }
         const int best = wave_min(cand);
         if (lane == 0) {
             const bool mass = S > 0.0f && best != 0x7fffffff;  // a row of -inf logits has no argmax
@@ -547,44 +583,42 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         return;
     }
 
-    const float u = u24f(philox((uint32_t)p.k, (uint32_t)q, p.round, p.seed).w[0]);
-    const double target_d = (double)u * Sd;
-    const float target = (float)target_d;
-    // first granule of positive mass whose running sum exceeds target
-    double run = excl, prev = excl;
-    int pick = -1, lastpos = -1;
+    if constexpr (NR == 0) {
+        const double target_d = (double)u * Sd;
+        target = (float)target_d;
+        // first granule of positive mass whose running sum exceeds target
+        double run = excl, prev = excl;
+        int pick = -1, lastpos = -1;
 #pragma unroll
-    for (int i = 0; i < PICK_CACHE; ++i) {
-        if (wv[i] > 0.0f) lastpos = g0 + i;
-        if (pick < 0) {
-            prev = run;
-            run += (double)wv[i];
-            if (run > target_d && wv[i] > 0.0f) pick = g0 + i;
+        for (int i = 0; i < PICK_CACHE; ++i) {
+            if (wv[i] > 0.0f) lastpos = g0 + i;
+            if (pick < 0) {
+                prev = run;
+                run += (double)wv[i];
+                if (run > target_d && wv[i] > 0.0f) pick = g0 + i;
+            }
         }
-    }
-    for (int g = g0 + PICK_CACHE; g < g1; ++g) {
-        const float wg = gs[g].y * softw(gs[g].x, M, c);
-        if (wg > 0.0f) lastpos = g;
-        if (pick < 0) {
-            prev = run;
-            run += (double)wg;
-            if (run > target_d && wg > 0.0f) pick = g;
+        for (int g = g0 + PICK_CACHE; g < g1; ++g) {
+            const float wg = gs[g].y * softw(gs[g].x, M, c);
+            if (wg > 0.0f) lastpos = g;
+            if (pick < 0) {
+                prev = run;
+                run += (double)wg;
+                if (run > target_d && wg > 0.0f) pick = g;
+            }
         }
-    }
-    const unsigned long long hit = __ballot(pick >= 0);
-    bool fallback;
-    float before;
-    int gstar;
-    if (hit) {
-        const int L = __ffsll((long long)hit) - 1;
-        fallback = false;
-        before = (float)__shfl(prev, L, WAVE);
-        gstar = __shfl(pick, L, WAVE);
-    } else {
-        fallback = true;
-        before = 0.0f;
-        const int lp = -wave_min(-lastpos);
-        gstar = lp < 0 ? 0 : lp;
+        const unsigned long long hit = __ballot(pick >= 0);
+        if (hit) {
+            const int L = __ffsll((long long)hit) - 1;
+            fallback = false;
+            before = (float)__shfl(prev, L, WAVE);
+            gstar = __shfl(pick, L, WAVE);
+        } else {
+            fallback = true;
+            before = 0.0f;
+            const int lp = -wave_min(-lastpos);
+            gstar = lp < 0 ? 0 : lp;
+        }
     }
 
     // column block w of granule gstar for q's row (same operands as the tile)
@@ -607,6 +641,14 @@ __global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
         p.pd_stats[2 * o] = M;
         p.pd_stats[2 * o + 1] = S;
     }
+}
+
+template <typename WT, int KS, bool GREEDY>
+__global__ __launch_bounds__(TILE_THREADS) void k_propose_pick(PickArgs p)
+{
+    if (p.n_gran <= 16 * WAVE) pick_body<WT, KS, GREEDY, 16>(p);
+    else if (p.n_gran <= 32 * WAVE) pick_body<WT, KS, GREEDY, 32>(p);
+    else pick_body<WT, KS, GREEDY, 0>(p);
 }
 
 // ------------------------------------------------------------ fused propose
