@@ -764,6 +764,32 @@ struct W1Regs {
     }
 };
 
+// The second half of a 32-row W1 tile (rows 16..31, bf16, r = 16 KS)
+// through the registers of 512 threads, one uint4 each: for KS = 8 the half
+// has 256 uint4 and threads past it load and store the half's last one again
+// (the same value), so that every thread issues exactly one load.
+template <int RS, int KS>
+struct W1HalfRegs {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    static constexpr int PER_ROW = 2 * KS;
+    static constexpr int HALF = 16 * PER_ROW;
+    static_assert(HALF <= 2 * TILE_THREADS, "one uint4 per thread");
+    u32x4 v;
+    __device__ static inline int index(int te) { return HALF + min(te, HALF - 1); }
+    __device__ inline void issue(const bf16w* W1, const int* tok, int te)
+    {
+        const int idx = index(te);
+        const int tk = tok[idx / PER_ROW];
+        v = reinterpret_cast<const u32x4*>(W1 + (size_t)(tk >= 0 ? tk : 0) * (16 * KS))[idx % PER_ROW];
+    }
+    __device__ inline void commit(void* sB, int te) const
+    {
+        const int idx = index(te);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sB) + (size_t)(idx / PER_ROW) * RS * 2 +
+                                  16 * (idx % PER_ROW)) = v;
+    }
+};
+
 template <typename WT, int RS, int KS>
 __device__ inline void stage_w1(void* sB, const WT* W1, const int* tok, int r)
 {

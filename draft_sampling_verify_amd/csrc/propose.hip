@@ -230,20 +230,24 @@ __global__ __launch_bounds__(TILE_THREADS, 4) void k_draft_tile(TileArgs p)
 // pipeline fills once per workgroup.  One workgroup of 12 waves per CU, in
 // two groups that run one stage apart:
 //   MFMA waves (0-3)      hold the granule's W2 slice (A operand); in stage
-//                         s they write unit s+1's W1 rows (loaded into
-//                         registers two stages before) into LDS, check and
-//                         write unit s+4's tokens (loaded three stages
-//                         before), compute unit s's 32 x 128 bias tile into
-//                         LDS, and issue the loads of unit s+3's W1 rows
-//                         and unit s+7's tokens;
+//                         s they write rows 0..15 of unit s+1's W1 tile
+//                         (loaded into registers two stages before) into
+//                         LDS, check and write unit s+4's tokens (loaded
+//                         three stages before), compute unit s's 32 x 128
+//                         bias tile into LDS, and issue the loads of unit
+//                         s+3's W1 rows 0..15 and unit s+7's tokens;
 //   epilogue waves (4-11) hold the U rows of three units in registers (16
-//                         lanes per row, 8 ids each); in stage s they
-//                         reduce unit s-1 (z = U + bias: the granule's max,
-//                         sum of weights and greedy argmax per row), keep
-//                         its partials in LDS, then issue unit s+2's U
-//                         loads; the partials are written out in bursts
-//                         (stores mixed into the streamed reads cost more
-//                         than the same bytes written together).
+//                         lanes per row, 8 ids each); in stage s they write
+//                         rows 16..31 of unit s+1's W1 tile, reduce unit s-1
+//                         (z = U + bias: the granule's max, sum of weights
+//                         and greedy argmax per row), keep its partials in
+//                         LDS, then issue the loads of unit s+3's W1 rows
+//                         16..31 and unit s+2's U; the partials are written
+//                         out in bursts (stores mixed into the streamed
+//                         reads cost more than the same bytes written
+//                         together).  The W1 tile is split between the
+//                         groups because the MFMA waves' stage is the
+//                         longer one.
 // One barrier per stage and no wait at it for memory.
 // The staged tile sums its 16 ids per thread as two 8-id partials reduced
 // in this kernel's order, so both give identical partials.
@@ -256,7 +260,8 @@ template <int KS, bool VEC4, bool GREEDY>
 __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs p)
 {
     using Ops = TileOps<bf16w, KS>;
-    using GW = W1Regs<Ops::RS, KS, 1>;
+    using GW = W1Regs<Ops::RS, KS, 2>;  // MFMA waves: rows 0..15 of a unit's W1 tile (part 0 of 2)
+    using GE = W1HalfRegs<Ops::RS, KS>;  // epilogue waves: rows 16..31
     const int nrows = p.nrows;  // rows are the requests at position kfix + 1
     const int n_rb = (nrows + BLOCK_ROWS - 1) / BLOCK_ROWS;
     const UnitRun run(p.n_gran, n_rb);
@@ -308,8 +313,9 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
             const int q = urow(j, lane & 31), qc = q < nrows ? q : 0;
             return *tok_src(qc);
         };
-        // unit j's W1 rows are loaded into g[j % 3], two stages before they
-        // are written to LDS; the tokens of units 4, 5 and 6 into three
+        // unit j's W1 rows 0..15 are loaded into g[j % 3], two stages before
+        // they are written to LDS (the epilogue waves move rows 16..31 on the
+        // same schedule); the tokens of units 4, 5 and 6 into three
         // registers.  The loads go out in the order of every stage (W1 rows,
         // then a token), so the waits of the first stages are the loop's.
         // Every MFMA wave loads the tokens (wave 0 uses them): the count of
@@ -359,7 +365,14 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
             load8_raw<VEC4>(p.U + ((size_t)fc * p.gamma + kfix) * p.V, ugran(jj) * GRAN + ec, p.V, zu);
         };
         float zuA[8], zuB[8], zuC[8];  // unit j in A, B, C by j % 3
+        // rows 16..31 of unit j's W1 tile in h[j % 3], loaded two stages
+        // before they are written to LDS (the MFMA waves move rows 0..15)
+        GE h0, h1, h2;
+        h0.issue(W1, s_tok[0], te);
+        h0.commit(sB[0], te);
+        h1.issue(W1, s_tok[1], te);
         issue(0, zuA);
+        h2.issue(W1, s_tok[2], te);
         issue(1, zuB);
         __syncthreads();
         typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -379,7 +392,11 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
                 }
             }
         };
-        auto stage = [&](float (&zu)[8], int s) __attribute__((always_inline)) {
+        // stage s: commit unit s+1's rows 16..31 (hc), reduce unit s-1, then
+        // issue unit s+3's W1 rows (hi) and, after them, unit s+2's U: a wait
+        // for W1 rows is then never a wait for the younger U loads
+        auto stage = [&](float (&zu)[8], GE& hc, GE& hi, int s) __attribute__((always_inline)) {
+            hc.commit(sB[(s + 1) & 1], te);
             const int e = s - 1;
             const int ge = ugran(e), cbase = ge * GRAN + ec;
             const int f = urow(e, er);
@@ -424,6 +441,7 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
                     if (GREEDY) s_ridx[sl] = bi;
                 }
             }
+            hi.issue(W1, s_tok[(s + 3) & 7], te);
             issue(s + 2, zu);
             // a full chunk of partials, or the run's last unit: write them out
             if (s >= 1 && s <= nu && (e % TILE_REC_UNITS == TILE_REC_UNITS - 1 || e == nu - 1))
@@ -431,9 +449,9 @@ __global__ __launch_bounds__(3 * TILE_THREADS, 1) void k_draft_tile_ws(TileArgs 
             __syncthreads();
         };
         for (int s = 0; s < n_stages; s += 3) {
-            stage(zuC, s);
-            stage(zuA, s + 1);
-            stage(zuB, s + 2);
+            stage(zuC, h1, h0, s);
+            stage(zuA, h2, h1, s + 1);
+            stage(zuB, h0, h2, s + 2);
         }
     }
 }
