@@ -1202,10 +1202,11 @@ static hipError_t propose_fused(const DraftArgs& a, const TileArgs& t, int32_t* 
     return hipGetLastError();
 }
 
-// Requests above which the per-position path takes the pipelined tile (at
-// fewer, its runs cover too few row blocks per granule to hide the W2
-// reloads).
-constexpr int PIPED_TILE_MIN_R = 96;
+// Requests above which the per-position path takes the pipelined tile: from
+// two 32-row blocks per granule up it is the faster one (R = 64 over 2048
+// granules: 34 against 39 us a position); with one block, every unit would
+// start a granule and wait for its W2 slice.
+constexpr int PIPED_TILE_MIN_R = 32;
 
 // Workgroups of k_draft_tile_ws the current device holds at once; cached
 // per device and variant.

@@ -43,14 +43,16 @@ SMALL = {
     # ragged last block; several 32-row blocks per workgroup
     "lds_r128_odd": Config("lds_r128_odd", 19, 37, 3, 1001, 128, True, 1.0, 2.0, 0.05, 0.5),
     "lds_multi": Config("lds_multi", 20, 40, 7, 40000, 256, True, 1.0, 3.0, 0.02, 1.0),
-    # the pipelined per-position tile (more than 96 requests, bf16, r = 128 /
+    # the pipelined per-position tile (more than 32 requests, bf16, r = 128 /
     # 256): ragged request count and vocabulary (V % 4 != 0)
     "piped_tile": Config("piped_tile", 21, 130, 3, 3001, 128, True, 1.0, 2.0, 0.05, 0.5),
     "piped_tile_v4": Config("piped_tile_v4", 22, 100, 4, 5000, 256, True, 0.8, 3.0, 0.02, 1.0),
-    # more than one 32-row block of requests with fewer than 96 of them
-    # (the per-position propose with the staged tile): a ragged last block,
-    # V % 4 != 0, r = 128
+    # the pipelined tile with three 32-row blocks per granule (the last
+    # ragged), V % 4 != 0, r = 128
     "multi_block": Config("multi_block", 23, 70, 3, 9001, 128, True, 1.0, 2.0, 0.05, 0.5),
+    # several 32-row blocks through the staged tile (r = 64 has too few
+    # k-steps for the pipelined one): a ragged last block, V % 4 != 0
+    "multi_block_staged": Config("multi_block_staged", 24, 70, 3, 9001, 64, True, 1.0, 2.0, 0.05, 0.5),
 }
 
 
